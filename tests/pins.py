@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle: checks against facts the pages and mathematics fix.
+
+Each pin takes the oracle module as an argument so that ``test_oracle_mutations`` can run the
+same pin against a deliberately broken copy of the oracle and see it fail.  A pin raises
+``AssertionError`` when the oracle disagrees with the fact it encodes.
+
+[VDN] = "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models" (openvdn.github.io).
+"""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import scipy.linalg
+
+from oracle import bruteforce
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def frame_objective(s, s_bar, keys, vals, beta):
+    """The frame objective of [VDN] "From independent token updates to one frame-wise solve":
+    beta-weighted squared read errors plus the proximity term, each with a factor 1/2."""
+    err = keys @ s.T - vals                      # row u: S k_u - v_u
+    return 0.5 * float(np.sum(beta[:, None] * err * err)) + 0.5 * float(np.sum((s - s_bar) ** 2))
+
+
+# --------------------------------------------------------------------------------------------
+# VDA frame update pins
+# --------------------------------------------------------------------------------------------
+
+def pin_objective_minimum(orc, seed=0):
+    """P1: the update minimises the frame objective: zero directional derivatives (central
+    differences), no random perturbation decreases it, and a generic least-squares solve of the
+    stacked system gives the same state."""
+    rng = _rng(seed)
+    U, d = 12, 8
+    keys = _unit(rng.standard_normal((U, d)))
+    vals = rng.standard_normal((U, d))
+    beta = rng.random(U)
+    s_bar = rng.standard_normal((d, d))
+    a, b = orc.frame_stats(keys, vals, beta)
+    s = orc.frame_update(s_bar, a, b)
+    j0 = frame_objective(s, s_bar, keys, vals, beta)
+    eps = 1e-5
+    scale = 0.0
+    for _ in range(8):
+        delta = rng.standard_normal((d, d))
+        g = (frame_objective(s + eps * delta, s_bar, keys, vals, beta)
+             - frame_objective(s - eps * delta, s_bar, keys, vals, beta)) / (2 * eps)
+        g_bar = (frame_objective(s_bar + eps * delta, s_bar, keys, vals, beta)
+                 - frame_objective(s_bar - eps * delta, s_bar, keys, vals, beta)) / (2 * eps)
+        scale = max(scale, abs(g_bar))
+        assert abs(g) < 1e-6 * max(1.0, scale), f"directional derivative {g} not zero"
+        assert frame_objective(s + 1e-3 * delta, s_bar, keys, vals, beta) > j0
+    ref = bruteforce.lstsq_update(s_bar, keys, vals, beta)
+    assert np.allclose(s, ref, rtol=1e-10, atol=1e-10), "closed form differs from least squares"
+
+
+def pin_sherman_morrison(orc, seed=1):
+    """P2: one token (U=1) reduces to the classical delta-rule step with the effective rate
+    beta/(1 + beta ||k||^2) (Sherman-Morrison on I + beta k k^T); [VDN] "Video Delta Attention"."""
+    rng = _rng(seed)
+    d = 6
+    for trial in range(4):
+        k = rng.standard_normal(d) * (1.0 if trial % 2 else 1.7)   # also non-unit keys
+        v = rng.standard_normal(d)
+        beta = float(rng.random()) * 1.5
+        s_bar = rng.standard_normal((d, d))
+        a, b = orc.frame_stats(k[None], v[None], np.array([beta]))
+        s = orc.frame_update(s_bar, a, b)
+        c = beta / (1.0 + beta * float(k @ k))
+        expect = s_bar - c * np.outer(s_bar @ k - v, k)
+        assert np.allclose(s, expect, rtol=1e-12, atol=1e-12)
+
+
+def pin_repeated_keys(orc, seed=2):
+    """P3: every token of the frame uses the same unit key with a shared rate: the state's read on
+    that key becomes (S_bar k + U beta v_mean) / (1 + U beta) -- repeated evidence accumulates."""
+    rng = _rng(seed)
+    U, d = 9, 7
+    k = _unit(rng.standard_normal(d))
+    vals = rng.standard_normal((U, d))
+    beta = 0.35
+    s_bar = rng.standard_normal((d, d))
+    a, b = orc.frame_stats(np.tile(k, (U, 1)), vals, np.full(U, beta))
+    s = orc.frame_update(s_bar, a, b)
+    vmean = vals.mean(axis=0)
+    assert np.allclose(s @ k, (s_bar @ k + U * beta * vmean) / (1 + U * beta), atol=1e-12)
+    z = rng.standard_normal(d)
+    z -= (z @ k) * k                                   # a direction no token addressed
+    assert np.allclose(s @ z, s_bar @ z, atol=1e-12)
+
+
+def pin_orthonormal_keys(orc, seed=3):
+    """P4: orthonormal keys: each token's read becomes (S_bar k_u + beta v_u)/(1 + beta), with no
+    penalty from the other tokens."""
+    rng = _rng(seed)
+    d, U = 8, 5
+    qmat, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    keys = qmat[:, :U].T
+    vals = rng.standard_normal((U, d))
+    beta = 0.6
+    s_bar = rng.standard_normal((d, d))
+    a, b = orc.frame_stats(keys, vals, np.full(U, beta))
+    s = orc.frame_update(s_bar, a, b)
+    for u in range(U):
+        assert np.allclose(s @ keys[u], (s_bar @ keys[u] + beta * vals[u]) / (1 + beta), atol=1e-12)
+
+
+def _transition_matrix(orc, a):
+    """Matrix of the linear map S_bar -> S_bar (I + A)^-1 (the frame update with B = 0): its
+    image of the identity."""
+    d = a.shape[0]
+    return orc.frame_update(np.eye(d), a, np.zeros((d, d)))
+
+
+def pin_spectrum(orc, seed=4):
+    """P5: the inherited-state transition has eigenvalues 1/(1 + lambda_i(A)) in (0, 1] and
+    operator norm at most one, for any A >= 0 ([VDN] "Stability of the Inherited State")."""
+    rng = _rng(seed)
+    d, U = 6, 40
+    keys = _unit(rng.standard_normal((1, d)) + 0.05 * rng.standard_normal((U, d)))  # crowded
+    a, _ = orc.frame_stats(keys, np.zeros((U, d)), rng.random(U))
+    lam = np.linalg.eigvalsh(a)
+    assert lam.max() > 2.0                          # the additive rule would expand here
+    m = _transition_matrix(orc, a)
+    ev = np.sort(np.linalg.eigvals(m).real)
+    assert np.allclose(ev, np.sort(1.0 / (1.0 + lam)), atol=1e-10)
+    assert np.linalg.norm(m, 2) <= 1.0 + 1e-12
+
+
+def pin_contraction(orc, seed=5):
+    """P6: the frame update is non-expansive: ||f(X) - f(Y)||_F <= ||X - Y||_F."""
+    rng = _rng(seed)
+    d, U = 8, 64
+    for crowd in (0.02, 1.0):
+        keys = _unit(rng.standard_normal((1, d)) + crowd * rng.standard_normal((U, d)))
+        vals = rng.standard_normal((U, d))
+        a, b = orc.frame_stats(keys, vals, rng.random(U))
+        for _ in range(5):
+            x, y = rng.standard_normal((2, d, d)) * 3
+            fx, fy = orc.frame_update(x, a, b), orc.frame_update(y, a, b)
+            assert np.linalg.norm(fx - fy) <= np.linalg.norm(x - y) * (1 + 1e-12)
+
+
+def pin_neumann(orc, seed=6):
+    """P7: for a Gram matrix of spectral radius < 1 the update equals the Neumann-series form
+    (S_bar + B)(I - A + A^2 - ...) ([VDN] "Correlation-Aware Frame Updates")."""
+    rng = _rng(seed)
+    d, U = 6, 4
+    keys = _unit(rng.standard_normal((U, d)))
+    vals = rng.standard_normal((U, d))
+    beta = 0.2 * rng.random(U)
+    s_bar = rng.standard_normal((d, d))
+    a, b = orc.frame_stats(keys, vals, beta)
+    assert max(abs(np.linalg.eigvalsh(a))) < 0.5
+    series = np.zeros((d, d))
+    term = np.eye(d)
+    for _ in range(80):
+        series += term
+        term = -term @ a
+    assert np.allclose(orc.frame_update(s_bar, a, b), (s_bar + b) @ series, atol=1e-12)
+
+
+def pin_cho_solve(orc, seed=7):
+    """P9: the update agrees with a Cholesky-based solve from another library routine."""
+    rng = _rng(seed)
+    d, U = 16, 100
+    keys = _unit(rng.standard_normal((U, d)))
+    vals = rng.standard_normal((U, d))
+    beta = rng.random(U)
+    s_bar = rng.standard_normal((d, d))
+    a, b = orc.frame_stats(keys, vals, beta)
+    fac = scipy.linalg.cho_factor(np.eye(d) + a)
+    ref = scipy.linalg.cho_solve(fac, (s_bar + b).T).T
+    assert np.allclose(orc.frame_update(s_bar, a, b), ref, rtol=1e-11, atol=1e-11)
+
+
+# --------------------------------------------------------------------------------------------
+# Frame-set and state-bookkeeping pins
+# --------------------------------------------------------------------------------------------
+
+def _parse_set(tok):
+    tok = tok.strip()
+    if tok == "-":
+        return []
+    out = []
+    for part in tok.split(","):
+        if "-" in part:
+            lo, hi = part.split("-")
+            out.extend(range(int(lo), int(hi) + 1))
+        else:
+            out.append(int(part))
+    return out
+
+
+def golden_frame_sets():
+    rows = {}
+    with open(os.path.join(GOLDEN, "frame_sets_T16_C2.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = line.split("|")
+            rows[int(parts[0])] = tuple(_parse_set(p) for p in parts[1:])
+    return rows
+
+
+def pin_golden_frame_sets(orc):
+    """The hand-derived frame sets of the 16-frame, chunk-2 visualisation workload."""
+    gold = golden_frame_sets()
+    assert len(gold) == 16
+    for t, (w, anc, f, r) in gold.items():
+        got = orc.frame_sets(t, 16, 2, True)
+        assert [list(x) for x in got] == [w, anc, f, r], (t, got)
+
+
+def pin_partition(orc):
+    """P10: W, Anc, F and R partition all frames for every query frame (the two linear regions
+    are disjoint and exclude window and boundary frames, so no frame is counted twice)."""
+    for anchors in (True, False):
+        for C in (1, 2, 3, 5):
+            for T in list(range(1, 26)) + [37, 59]:
+                for t in range(T):
+                    w, anc, f, r = orc.frame_sets(t, T, C, anchors)
+                    allf = sorted(w + anc + f + r)
+                    assert allf == list(range(T)), (T, C, anchors, t)
+                    if anchors:
+                        assert not ({0, T - 1} & set(f + r))
+                        assert {0, T - 1} <= set(w + anc)
+
+
+def pin_uniform_keys_visibility(orc):
+    """With identical keys the softmax is uniform over the visible keys, so a frame-indicator value
+    per key reveals each query's visible set; it must match the golden frame sets (text plus
+    window plus anchors)."""
+    T, N, C, H, d = 16, 3, 2, 1, 20
+    n_text = 2
+    q = np.zeros((T * N, H, d), np.float32)
+    q[..., 0] = 1
+    k = np.zeros_like(q)
+    k[..., 0] = 1
+    v = np.zeros_like(q)
+    for f in range(T):
+        v[f * N:(f + 1) * N, 0, f] = 1.0
+    tk = np.zeros((n_text, H, d), np.float32)
+    tk[..., 0] = 1
+    tv = np.zeros((n_text, H, d), np.float32)
+    tv[..., 16] = 1.0
+    o = orc.softmax_branch(q, k, v, tk, tv, T, N, C, True)
+    gold = golden_frame_sets()
+    for t in range(T):
+        w, anc, _, _ = gold[t]
+        vis = sorted(w + anc)
+        nkeys = n_text + N * len(vis)
+        expect = np.zeros(d)
+        expect[vis] = N / nkeys
+        expect[16] = n_text / nkeys
+        for n in range(N):
+            assert np.allclose(o[t * N + n, 0], expect, atol=1e-6), t
+
+
+def pin_beta_zero(orc, seed=8):
+    """P8: with every video write strength zero the states keep the text state: o_l = 2 S0 q."""
+    rng = _rng(seed)
+    T, N, C, H, d, n_text = 11, 3, 2, 2, 5, 4
+    q = rng.standard_normal((T * N, H, d))
+    k = _unit(rng.standard_normal((T * N, H, d)))
+    v = rng.standard_normal((T * N, H, d))
+    tk = _unit(rng.standard_normal((n_text, H, d)))
+    tv = rng.standard_normal((n_text, H, d))
+    beta = rng.random((n_text + T * N, H))
+    beta[n_text:] = 0.0
+    o_l = orc.linear_branch(q, k, v, beta, tk, tv, T, N, C, True)
+    for h in range(H):
+        s0 = bruteforce.lstsq_update(np.zeros((d, d)), tk[:, h], tv[:, h], 0.5 * beta[:n_text, h])
+        assert np.allclose(o_l[:, h], q[:, h] @ (2 * s0).T, atol=1e-10)
+
+
+def pin_text_once(orc, seed=9):
+    """P11: text enters only through the initial states, each at half strength, so that in the
+    small-beta limit the two readouts together carry the text write B_text exactly once."""
+    rng = _rng(seed)
+    n_text, d = 6, 5
+    tk = _unit(rng.standard_normal((n_text, d)))
+    tv = rng.standard_normal((n_text, d))
+    tb = rng.random(n_text)
+    b_text = (tv * tb[:, None]).T @ tk
+    for eps in (1e-4, 1e-6):
+        s0 = orc.text_state(tk, tv, eps * tb)
+        assert np.allclose((s0 + s0) / eps, b_text, atol=10 * eps * np.abs(b_text).max() * n_text)
+    # no text -> zero initial state
+    assert np.allclose(orc.text_state(tk[:0], tv[:0], tb[:0]), 0)
+
+
+def pin_boundary_text_only(orc, seed=10):
+    """Boundary query frames see every frame through the softmax, so their linear readout holds
+    only the text: o_l = 2 S0 q for frames 0 and T-1."""
+    rng = _rng(seed)
+    T, N, C, H, d, n_text = 9, 2, 2, 1, 4, 3
+    q = rng.standard_normal((T * N, H, d))
+    k = _unit(rng.standard_normal((T * N, H, d)))
+    v = rng.standard_normal((T * N, H, d))
+    tk = _unit(rng.standard_normal((n_text, H, d)))
+    tv = rng.standard_normal((n_text, H, d))
+    beta = rng.random((n_text + T * N, H))
+    o_l = orc.linear_branch(q, k, v, beta, tk, tv, T, N, C, True)
+    s0 = bruteforce.lstsq_update(np.zeros((d, d)), tk[:, 0], tv[:, 0], 0.5 * beta[:n_text, 0])
+    for t in (0, T - 1):
+        for n in range(N):
+            i = t * N + n
+            assert np.allclose(o_l[i, 0], 2 * s0 @ q[i, 0], atol=1e-10)
+
+
+# --------------------------------------------------------------------------------------------
+# Merge pins ([VDN] "Gating the Softmax and Linear Branch Outputs")
+# --------------------------------------------------------------------------------------------
+
+def pin_gate_closed_forms(orc, seed=11):
+    """P14: zero gate weights give gates of 1/2; identity projections then give
+    out = o_s/2 + RMSNorm(o_l)/2; a single non-zero gate weight w at [i][j] gates output channel j
+    by sigmoid(w q_i) (weights are [in][out]); a single non-zero projection weight moves channel i
+    to channel j."""
+    rng = _rng(seed)
+    M, d = 7, 6
+    q = rng.standard_normal((M, d))
+    o_s = rng.standard_normal((M, d))
+    o_l = rng.standard_normal((M, d)) * 3
+    gw = np.zeros((2, d, d))
+    pw = np.stack([np.eye(d), np.eye(d)])
+    rms = np.sqrt(np.mean(o_l ** 2, axis=-1, keepdims=True) + 1e-6)
+    assert np.allclose(orc.merge(q, o_s, o_l, gw, pw), 0.5 * o_s + 0.5 * o_l / rms, atol=1e-12)
+    # orientation of the gate weights: softmax gate only, one entry
+    gw1 = np.zeros((2, d, d))
+    gw1[0, 1, 4] = 2.5
+    pw_s = np.stack([np.eye(d), np.zeros((d, d))])
+    out = orc.merge(q, o_s, o_l, gw1, pw_s)
+    g = np.full((M, d), 0.5)
+    g[:, 4] = 1 / (1 + np.exp(-2.5 * q[:, 1]))
+    assert np.allclose(out, g * o_s, atol=1e-12)
+    # linear gate, one entry; projection moves channel 2 to channel 5
+    gw2 = np.zeros((2, d, d))
+    gw2[1, 3, 2] = -1.5
+    pw2 = np.zeros((2, d, d))
+    pw2[1, 2, 5] = 2.0
+    out = orc.merge(q, o_s, o_l, gw2, pw2)
+    expect = np.zeros((M, d))
+    expect[:, 5] = 2.0 * (1 / (1 + np.exp(1.5 * q[:, 3]))) * (o_l / rms)[:, 2]
+    assert np.allclose(out, expect, atol=1e-12)
+    # RMSNorm: scale invariance of the linear branch
+    a = orc.merge(q, o_s, o_l, gw2, pw2)
+    b = orc.merge(q, o_s, 1e3 * o_l, gw2, pw2)
+    assert np.allclose(a, b, rtol=1e-6, atol=1e-9)
+
+
+# --------------------------------------------------------------------------------------------
+# Whole-layer pins
+# --------------------------------------------------------------------------------------------
+
+def tiny_inputs(T, N, n_text, H, d, seed, dtype=np.float32):
+    rng = _rng(seed)
+    return dict(
+        q=_unit(rng.standard_normal((T * N, H, d))).astype(dtype),
+        k=_unit(rng.standard_normal((T * N, H, d))).astype(dtype),
+        v=rng.standard_normal((T * N, H, d)).astype(dtype),
+        text_k=_unit(rng.standard_normal((n_text, H, d))).astype(dtype),
+        text_v=rng.standard_normal((n_text, H, d)).astype(dtype),
+        beta=rng.random((n_text + T * N, H)).astype(dtype),
+        gate_w=(rng.standard_normal((2, d, d)) / math.sqrt(d)).astype(dtype),
+        proj_w=(rng.standard_normal((2, d, d)) / math.sqrt(d)).astype(dtype),
+    )
+
+
+BRUTE_CASES = [
+    # T, N, C, n_text, H, d, anchors
+    (16, 2, 2, 1, 1, 8, True),
+    (7, 3, 2, 2, 2, 4, True),
+    (7, 3, 2, 2, 1, 4, False),
+    (1, 4, 5, 3, 1, 4, True),
+    (2, 3, 1, 1, 1, 4, True),
+    (3, 2, 5, 2, 1, 4, False),
+    (11, 2, 3, 0, 1, 6, True),
+    (13, 2, 1, 2, 2, 5, True),
+    (10, 3, 5, 4, 1, 8, True),
+]
+
+
+def pin_bruteforce(orc, cases=BRUTE_CASES, seed=12):
+    """P12: the structured oracle equals the brute-force oracle (dense mask, least-squares frame
+    updates, per-frame rebuilt states) on tiny shapes, including T not divisible by C, T <= 3C,
+    T = 1 and 2, no text, and anchors off."""
+    for ci, (T, N, C, n_text, H, d, anchors) in enumerate(cases):
+        inp = tiny_inputs(T, N, n_text, H, d, seed + ci)
+        out_s, mids = orc.vdn_forward(inp, T, N, C, anchors, with_intermediates=True)
+        out_b, os_b, ol_b = bruteforce.layer_dense(inp, T, N, C, anchors)
+        assert np.allclose(mids["o_s"], os_b, rtol=1e-5, atol=1e-6), ("o_s", ci)
+        assert np.allclose(mids["o_l"], ol_b, rtol=1e-9, atol=1e-9), ("o_l", ci)
+        assert np.allclose(out_s, out_b, rtol=1e-5, atol=1e-5), ("out", ci)

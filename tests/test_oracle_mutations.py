@@ -1,0 +1,182 @@
+"""Planted mistakes in a private copy of the CPU oracle must each fail a pin.
+
+Every mutant is a fresh copy of the oracle module with one function replaced by a plausible
+wrong version (a dropped term, a wrong sign, a transposed operand, an off-by-one window, a wrong
+scan order, ...).  The named pin must reject it; otherwise the pins would not guard the oracle.
+All of this runs on the CPU.
+"""
+
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import pins
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "vdn_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("vdn_oracle_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def m_drop_sbar(o):
+    def frame_update(s_bar, a, b):
+        d = a.shape[0]
+        return np.linalg.solve((np.eye(d) + a).T, b.T).T
+    o.frame_update = frame_update
+
+
+def m_minus_gram(o):
+    def frame_update(s_bar, a, b):
+        d = a.shape[0]
+        return np.linalg.solve((np.eye(d) - a).T, (s_bar + b).T).T
+    o.frame_update = frame_update
+
+
+def m_write_transposed(o):
+    orig = o.frame_stats
+
+    def frame_stats(kf, vf, bf):
+        a, b = orig(kf, vf, bf)
+        return a, b.T
+    o.frame_stats = frame_stats
+
+
+def m_gram_unweighted(o):
+    orig = o.frame_stats
+
+    def frame_stats(kf, vf, bf):
+        _, b = orig(kf, vf, bf)
+        kf = np.asarray(kf, np.float64)
+        return kf.T @ kf, b
+    o.frame_stats = frame_stats
+
+
+def m_forward_window_off_by_one(o):
+    orig = o.frame_sets
+
+    def frame_sets(t, T, C, anchors):
+        w, anc, f, r = orig(t, T, C, anchors)
+        bset = o.boundary_set(T, anchors)
+        if t not in bset:
+            c = t // C
+            f = [x for x in range(T) if x not in bset and x // C <= c - 1]
+        return w, anc, f, r
+    o.frame_sets = frame_sets
+
+
+def m_reverse_scan_increasing(o):
+    def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half_beta"):
+        n_text = text_k.shape[0]
+        s0 = o.text_state(text_k[:, h], text_v[:, h], beta[:n_text, h], text_mode)
+        order = o.scan_order(T, anchors)
+        stats = {f: o.frame_stats(k[f * N:(f + 1) * N, h], v[f * N:(f + 1) * N, h],
+                                  beta[n_text + f * N:n_text + (f + 1) * N, h]) for f in order}
+        fwd = [s0]
+        for f in order:
+            fwd.append(o.frame_update(fwd[-1], *stats[f]))
+        per = []
+        for t in range(T):
+            _, _, ff, rr = o.frame_sets(t, T, C, anchors)
+            s = s0
+            for f in rr:                                # wrong: farthest frame written last
+                s = o.frame_update(s, *stats[f])
+            per.append((fwd[len(ff)], s))
+        return s0, per
+    o.head_states = head_states
+
+
+def m_text_full_beta(o):
+    def text_state(tk, tv, tb, text_mode="half_beta"):
+        d = tk.shape[-1]
+        if tk.shape[0] == 0:
+            return np.zeros((d, d))
+        return o.frame_update(np.zeros((d, d)), *o.frame_stats(tk, tv, tb))
+    o.text_state = text_state
+
+
+def m_gate_transposed(o):
+    def merge(q, o_s, o_l, gate_w, proj_w, eps=o.RMS_EPS):
+        gw = np.asarray(gate_w, np.float64)
+        pw = np.asarray(proj_w, np.float64)
+        q = np.asarray(q, np.float64)
+        g_s = o.sigmoid(q @ gw[0].T)
+        g_l = o.sigmoid(q @ gw[1].T)
+        return (g_s * o_s) @ pw[0] + (g_l * o.rms_norm(np.asarray(o_l, np.float64), eps)) @ pw[1]
+    o.merge = merge
+
+
+def m_no_rmsnorm(o):
+    def merge(q, o_s, o_l, gate_w, proj_w, eps=o.RMS_EPS):
+        gw = np.asarray(gate_w, np.float64)
+        pw = np.asarray(proj_w, np.float64)
+        q = np.asarray(q, np.float64)
+        return (o.sigmoid(q @ gw[0]) * o_s) @ pw[0] + (o.sigmoid(q @ gw[1]) * o_l) @ pw[1]
+    o.merge = merge
+
+
+def m_softmax_ignores_anchors(o):
+    def key_frames(t, T, C, anchors):
+        return sorted(o.frame_sets(t, T, C, anchors)[0])
+    o.key_frames = key_frames
+
+
+def m_softmax_scale(o):
+    def softmax_rows(qr, keys, vals):
+        s = (qr.astype(np.float32) @ keys.astype(np.float32).T) / np.float32(qr.shape[-1])
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        return (p @ vals.astype(np.float32)) / p.sum(axis=1, keepdims=True)
+    o.softmax_rows = softmax_rows
+
+
+def m_softmax_no_text(o):
+    orig = o.softmax_branch
+
+    def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None):
+        return orig(q, k, v, text_k[:0], text_v[:0], T, N, C, anchors, rows)
+    o.softmax_branch = softmax_branch
+
+
+def m_boundary_reads_states(o):
+    orig = o.frame_sets
+
+    def frame_sets(t, T, C, anchors):
+        w, anc, f, r = orig(t, T, C, anchors)
+        if anchors and t in (0, T - 1):
+            c = t // C
+            bset = o.boundary_set(T, anchors)
+            f = [x for x in range(T) if x not in bset and x // C <= c - 2]
+            r = [x for x in range(T) if x not in bset and x // C >= c + 2]
+        return w, anc, f, r
+    o.frame_sets = frame_sets
+
+
+MUTANTS = [
+    (m_drop_sbar, pins.pin_objective_minimum),
+    (m_minus_gram, pins.pin_spectrum),
+    (m_write_transposed, pins.pin_sherman_morrison),
+    (m_gram_unweighted, pins.pin_objective_minimum),
+    (m_forward_window_off_by_one, pins.pin_golden_frame_sets),
+    (m_reverse_scan_increasing, pins.pin_bruteforce),
+    (m_text_full_beta, pins.pin_text_once),
+    (m_gate_transposed, pins.pin_gate_closed_forms),
+    (m_no_rmsnorm, pins.pin_gate_closed_forms),
+    (m_softmax_ignores_anchors, pins.pin_uniform_keys_visibility),
+    (m_softmax_scale, pins.pin_bruteforce),
+    (m_softmax_no_text, pins.pin_uniform_keys_visibility),
+    (m_boundary_reads_states, pins.pin_partition),
+]
+
+
+@pytest.mark.parametrize("mutate,pin", MUTANTS, ids=[m.__name__ for m, _ in MUTANTS])
+def test_mutant_is_caught(mutate, pin):
+    o = fresh_oracle()
+    pin(o)                       # the unmodified copy passes
+    mutate(o)
+    with pytest.raises(AssertionError):
+        pin(o)
