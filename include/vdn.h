@@ -1,0 +1,140 @@
+/*
+ * vdn.h -- C ABI of the MI355X (gfx950) forward pass of the Video DeltaNet (VDN) hybrid
+ * video-video attention layer.
+ *
+ * Source of every operation below: "Video DeltaNet: Near-Lossless Hybrid Attention for Video
+ * Models" (openvdn.github.io), cited as [VDN] with the section name, and "Faster Than It Plays:
+ * Video DeltaNet Generates 14 Seconds of 768p Video in 11 Seconds" (ai-blog.deepmagic.app),
+ * cited as [FTP], whose section "Two branches instead of one" prints the frame update in text.
+ *
+ * The layer, per head h, for video query token i in latent frame t (chunk c = t / C):
+ *
+ *   softmax branch  ([VDN] "Local Softmax and Long-Range Linear Memory")
+ *     o_s = softmax(q_i K^T / sqrt(d)) V over the text keys, the keys of every frame whose chunk is
+ *     within one chunk of c (the bidirectional sliding window), and the boundary anchors: frames 0
+ *     and T-1 for every query frame, every frame for query frames 0 and T-1.  One normaliser.
+ *
+ *   linear branch   ([VDN] "Video Delta Attention: A Frame-Wise Solution", [FTP])
+ *     per frame f: A_f = sum_u beta_u k_u k_u^T, B_f = sum_u beta_u v_u k_u^T over the frame's N
+ *     tokens; the frame update is S <- (S + B_f)(I + A_f)^-1.  The text is written first, as one
+ *     joint update from S = 0 with every text weight halved (beta/2), giving S0 for both
+ *     directions.  The forward state of query frame t has then absorbed, in increasing order, the
+ *     non-boundary frames of chunks <= c-2; the reverse state, in decreasing order, those of
+ *     chunks >= c+2.  o_l = (S_fwd + S_rev) q_i; boundary query frames read 2 S0 q_i.
+ *
+ *   merge           ([VDN] "Gating the Softmax and Linear Branch Outputs")
+ *     r = o_l / sqrt(mean(o_l^2) + 1e-6); g_s = sigmoid(q_i Wg[0]); g_l = sigmoid(q_i Wg[1]);
+ *     out_i = (g_s * o_s) Wp[0] + (g_l * r) Wp[1].   The residual add is the caller's.
+ *
+ * With anchors off there are no boundary frames: no anchor keys, and frames 0 and T-1 are
+ * written into the states like any other frame.
+ *
+ * Layouts (row-major, token-major, head inside the token; every pointer is a DEVICE pointer):
+ *   q, k, v, out : [T*N][H][d]         element type = the plan's dtype
+ *   beta         : [n_text + T*N][H]    float32, text rows first; beta >= 0
+ *   text_kv      : [2][n_text][H][d]    keys then values, plan dtype (may be NULL if n_text == 0)
+ *   gate_w       : [2][d][d]            [in][out] (y = x W); [0] softmax gate, [1] linear gate
+ *   proj_w       : [2][d][d]            [in][out]; [0] softmax projection, [1] linear projection
+ * The weights are shared by all heads.  q, k and text keys are expected L2-normalised per
+ * (token, head); the layer does not renormalise.
+ *
+ * Ownership: the caller owns every tensor; the library reads inputs and writes `out` inside the
+ * stream-ordered call and keeps no reference afterwards.  `out` must not alias an input.  The plan
+ * owns a device workspace allocated at create time on the device current then, plus one side
+ * stream and two events; a plan is used from that device only.  Calls on one plan must not
+ * overlap (they share the workspace): serialise them on one stream, or use one plan per stream.
+ *
+ * Errors: no call aborts or throws.  Argument errors are detected on the host before anything is
+ * enqueued.  Faults inside kernels surface at the caller's next synchronisation of `stream`.
+ */
+#ifndef VDN_H
+#define VDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct vdn_plan vdn_plan;
+
+typedef enum {
+  VDN_OK = 0,
+  VDN_ERR_INVALID_ARG = -1,   /* NULL pointer, dimension <= 0, anchors not 0/1, misalignment */
+  VDN_ERR_UNSUPPORTED = -2,   /* d not in {16, 32, 64, 128}, unknown dtype, size overflow      */
+  VDN_ERR_OUT_OF_MEMORY = -3, /* workspace allocation failed                                   */
+  VDN_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed                    */
+} vdn_status;
+
+typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype;
+
+/* Build a plan for one layer shape.  T frames of N tokens, chunks of C frames, n_text text tokens
+ * (may be 0), H heads of size d, anchors 0/1, element type dtype.  Computes the per-frame key
+ * ranges of the softmax branch and the scan order of the linear branch, allocates the workspace
+ * and the side stream.  On success *plan_out owns them; on failure *plan_out is set to NULL. */
+vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int anchors,
+                           vdn_dtype dtype, vdn_plan **plan_out);
+
+/* As vdn_plan_create, with flags: VDN_FLAG_GENERIC_KERNELS selects the generic (SIMT) kernel of
+ * every stage even where an MFMA kernel exists (used to cross-check the two kernel families). */
+enum { VDN_FLAG_GENERIC_KERNELS = 1 };
+vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,
+                              vdn_dtype dtype, unsigned flags, vdn_plan **plan_out);
+
+/* Enqueue the whole layer forward on `stream` (a hipStream_t; NULL = the null stream).  Returns
+ * after enqueueing.  Every pointer must be 16-byte aligned.  See the layouts above. */
+vdn_status vdn_forward(const vdn_plan *plan, const void *q, const void *k, const void *v,
+                       const float *beta, const void *text_kv, const void *gate_w,
+                       const void *proj_w, void *out, void *stream);
+
+/* Free the plan's workspace, stream and events.  The caller must have synchronised the streams
+ * the plan was used on.  NULL is a no-op. */
+void vdn_plan_destroy(vdn_plan *plan);
+
+/* Static description of a status code. */
+const char *vdn_status_str(vdn_status s);
+
+/* Bytes of device workspace the plan holds (informational). */
+size_t vdn_plan_workspace_bytes(const vdn_plan *plan);
+
+/* Host only, no GPU needed.  Key ranges of the softmax branch for query frame t, in the key index
+ * space of one head: text key j is index j; video token j (= f*N + n) is index text_pad + j where
+ * text_pad = n_text rounded up to a multiple of 64.  Writes up to max_ranges [start, end) pairs
+ * into ranges[2*r], ranges[2*r+1] in ascending order and returns their number, or -1 on an
+ * invalid argument.  Empty ranges are omitted. */
+int vdn_key_ranges(int T, int N, int C, int n_text, int anchors, int t, int64_t *ranges,
+                   int max_ranges);
+
+/* Host only.  Frames absorbed by the forward (dir = 0) or reverse (dir = 1) state of query frame
+ * t, in the order they are written; returns their count (<= max_frames written) or -1. */
+int vdn_scan_frames(int T, int C, int anchors, int t, int dir, int *frames, int max_frames);
+
+/* Intermediate buffers of the last vdn_forward on this plan, for checking; stream-ordered copy of
+ * `bytes` bytes (must equal the buffer's size) into the device buffer dst:
+ *   VDN_BUF_OS     o_s     [T*N][H][d]          plan dtype
+ *   VDN_BUF_STATES S_fwd, S_rev: [2][Nc+1][H][d][d] float32; slot Nc holds S0 (boundary frames)
+ *   VDN_BUF_MINV   M_f = (I + A_f)^-1: [T+1][H][d][d] float32, slot 0 for the text (beta/2),
+ *                  slot 1+f for frame f (boundary frames' slots are not written when anchors on)
+ */
+enum { VDN_BUF_OS = 0, VDN_BUF_STATES = 1, VDN_BUF_MINV = 2 };
+vdn_status vdn_debug_buffer_bytes(const vdn_plan *plan, int which, size_t *bytes);
+vdn_status vdn_debug_copy(const vdn_plan *plan, int which, void *dst, size_t bytes, void *stream);
+
+/* Kernel timing.  vdn_profile_enable(plan, n) makes the next n forwards record HIP events around
+ * each stage on the stream it runs on; vdn_profile_read sums the recorded times (milliseconds,
+ * synchronising the events) into ms[VDN_STAGE_*] for n_stages entries and reports the number of
+ * forwards recorded.  Stages: */
+enum { VDN_STAGE_SOFTMAX = 0, VDN_STAGE_PREP = 1, VDN_STAGE_VDA_STATS = 2, VDN_STAGE_VDA_SCAN = 3,
+       VDN_STAGE_EPILOGUE = 4, VDN_STAGE_TOTAL = 5, VDN_NUM_STAGES = 6 };
+vdn_status vdn_profile_enable(vdn_plan *plan, int max_calls);
+vdn_status vdn_profile_read(vdn_plan *plan, float *ms, int n_stages, int *calls);
+
+/* Which kernel family a plan selected for each stage (0 = generic SIMT kernel, 1 = MFMA kernel). */
+vdn_status vdn_plan_kernel_kind(const vdn_plan *plan, int stage, int *kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_H */

@@ -1,0 +1,275 @@
+// C ABI of the VDN layer forward: argument validation, plan ownership, stream fork/join and stage
+// timing.  The kernels themselves live in the .hip files; see include/vdn.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "vdn_internal.h"
+
+struct vdn_plan {
+  vdn::Shape s;
+  vdn::Layout lay;
+  vdn::Kinds kinds;
+  int device = -1;
+  char* ws = nullptr;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // stage timing (mutable: recording events does not change the plan's meaning)
+  mutable int prof_max = 0, prof_count = 0;
+  mutable std::vector<hipEvent_t> prof_events;   // [prof_max][VDN_NUM_STAGES][2]
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+vdn::Buffers buffers_of(const vdn_plan* p) {
+  vdn::Buffers b{};
+  char* ws = p->ws;
+  b.os = ws + p->lay.os;
+  b.kp = p->kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.kp) : nullptr;
+  b.vt = p->kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.vt) : nullptr;
+  b.minv = reinterpret_cast<float*>(ws + p->lay.minv);
+  b.bw = reinterpret_cast<float*>(ws + p->lay.bw);
+  b.states = reinterpret_cast<float*>(ws + p->lay.states);
+  b.ranges = reinterpret_cast<const int*>(ws + p->lay.ranges);
+  b.nranges = b.ranges + (size_t)p->s.T * 2 * vdn::kMaxRanges;
+  return b;
+}
+
+void free_plan(vdn_plan* p) {
+  if (!p) return;
+  if (p->device >= 0) (void)hipSetDevice(p->device);
+  for (hipEvent_t e : p->prof_events) if (e) (void)hipEventDestroy(e);
+  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+  if (p->ev_join) (void)hipEventDestroy(p->ev_join);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  if (p->ws) (void)hipFree(p->ws);
+  delete p;
+}
+
+bool shape_ok(int T, int N, int C, int n_text, int H, int d, int anchors) {
+  return T > 0 && N > 0 && C > 0 && n_text >= 0 && H > 0 && d > 0 && (anchors == 0 || anchors == 1);
+}
+
+vdn::Shape make_shape(int T, int N, int C, int n_text, int H, int d, int anchors, vdn_dtype dt) {
+  vdn::Shape s{};
+  s.T = T; s.N = N; s.C = C; s.n_text = n_text; s.H = H; s.d = d; s.anchors = anchors; s.dtype = dt;
+  s.Nc = (T + C - 1) / C;
+  s.text_pad = (int)vdn::round_up(n_text, vdn::kTextPad);
+  s.Lk = (int64_t)s.text_pad + (int64_t)T * N;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vdn_status_str(vdn_status s) {
+  switch (s) {
+    case VDN_OK: return "ok";
+    case VDN_ERR_INVALID_ARG: return "invalid argument";
+    case VDN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VDN_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case VDN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int vdn_key_ranges(int T, int N, int C, int n_text, int anchors, int t, int64_t* ranges, int max_ranges) {
+  if (!shape_ok(T, N, C, n_text, 1, 1, anchors) || t < 0 || t >= T || (max_ranges > 0 && !ranges) || max_ranges < 0)
+    return -1;
+  vdn::Shape s = make_shape(T, N, C, n_text, 1, 1, anchors, VDN_F32);
+  return vdn::key_ranges(s, t, ranges, max_ranges);
+}
+
+int vdn_scan_frames(int T, int C, int anchors, int t, int dir, int* frames, int max_frames) {
+  if (!shape_ok(T, 1, C, 0, 1, 1, anchors) || t < 0 || t >= T || (dir != 0 && dir != 1) ||
+      (max_frames > 0 && !frames) || max_frames < 0)
+    return -1;
+  vdn::Shape s = make_shape(T, 1, C, 0, 1, 1, anchors, VDN_F32);
+  return vdn::scan_frames(s, t, dir, frames, max_frames);
+}
+
+vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int anchors, vdn_dtype dtype,
+                           vdn_plan** plan_out) {
+  return vdn_plan_create_ex(T, N, C, n_text, H, d, anchors, dtype, 0u, plan_out);
+}
+
+vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors, vdn_dtype dtype,
+                              unsigned flags, vdn_plan** plan_out) {
+  if (!plan_out) return VDN_ERR_INVALID_ARG;
+  *plan_out = nullptr;
+  if (!shape_ok(T, N, C, n_text, H, d, anchors)) return VDN_ERR_INVALID_ARG;
+  if (dtype != VDN_F32 && dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return VDN_ERR_UNSUPPORTED;
+  // keep every index well inside 63 bits and grid dimensions inside their limits
+  const int64_t tokens = (int64_t)T * N;
+  if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || (int64_t)n_text * H * d > (int64_t(1) << 40))
+    return VDN_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)VDN_FLAG_GENERIC_KERNELS) return VDN_ERR_INVALID_ARG;
+  if ((int64_t)vdn::round_up(n_text, vdn::kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
+
+  vdn_plan* p = new (std::nothrow) vdn_plan();
+  if (!p) return VDN_ERR_OUT_OF_MEMORY;
+  p->s = make_shape(T, N, C, n_text, H, d, anchors, dtype);
+  p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
+  p->lay = vdn::make_layout(p->s, p->kinds.softmax_mfma);
+  if (hipGetDevice(&p->device) != hipSuccess) { free_plan(p); return VDN_ERR_HIP; }
+  if (hipMalloc(&p->ws, p->lay.total) != hipSuccess) {
+    (void)hipGetLastError();
+    p->ws = nullptr;
+    free_plan(p);
+    return VDN_ERR_OUT_OF_MEMORY;
+  }
+  // per-frame key-range table
+  std::vector<int> tab((size_t)T * (2 * vdn::kMaxRanges + 1), 0);
+  for (int t = 0; t < T; ++t) {
+    int64_t r[2 * vdn::kMaxRanges];
+    int n = vdn::key_ranges(p->s, t, r, vdn::kMaxRanges);
+    for (int i = 0; i < 2 * n; ++i) tab[(size_t)t * 2 * vdn::kMaxRanges + i] = (int)r[i];
+    tab[(size_t)T * 2 * vdn::kMaxRanges + t] = n;
+  }
+  if (hipMemcpy(p->ws + p->lay.ranges, tab.data(), tab.size() * sizeof(int), hipMemcpyHostToDevice) != hipSuccess ||
+      hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming) != hipSuccess) {
+    free_plan(p);
+    return VDN_ERR_HIP;
+  }
+  *plan_out = p;
+  return VDN_OK;
+}
+
+void vdn_plan_destroy(vdn_plan* plan) { free_plan(plan); }
+
+size_t vdn_plan_workspace_bytes(const vdn_plan* plan) { return plan ? plan->lay.total : 0; }
+
+vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
+  if (!plan || !kind) return VDN_ERR_INVALID_ARG;
+  switch (stage) {
+    case VDN_STAGE_SOFTMAX: *kind = plan->kinds.softmax_mfma; break;
+    case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma; break;
+    case VDN_STAGE_VDA_STATS: *kind = plan->kinds.stats_mfma; break;
+    case VDN_STAGE_VDA_SCAN: *kind = plan->kinds.scan_mfma; break;
+    case VDN_STAGE_EPILOGUE: *kind = plan->kinds.epilogue_mfma; break;
+    default: return VDN_ERR_INVALID_ARG;
+  }
+  return VDN_OK;
+}
+
+vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                       const void* text_kv, const void* gate_w, const void* proj_w, void* out, void* stream) {
+  if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !out) return VDN_ERR_INVALID_ARG;
+  if (plan->s.n_text > 0 && !text_kv) return VDN_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, out};
+  for (const void* ptr : ptrs) if (!aligned16(ptr)) return VDN_ERR_INVALID_ARG;
+  if (text_kv && !aligned16(text_kv)) return VDN_ERR_INVALID_ARG;
+  if (out == q || out == k || out == v || out == text_kv) return VDN_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
+  if (dev != plan->device) return VDN_ERR_INVALID_ARG;
+
+  const vdn::Shape& s = plan->s;
+  hipStream_t main = reinterpret_cast<hipStream_t>(stream);
+  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out};
+  vdn::Buffers b = buffers_of(plan);
+
+  hipEvent_t* ev = nullptr;
+  if (plan->prof_count < plan->prof_max) {
+    ev = &plan->prof_events[(size_t)plan->prof_count * VDN_NUM_STAGES * 2];
+    ++plan->prof_count;
+  }
+  auto mark = [&](int stage, int end, hipStream_t st) {
+    if (ev) (void)hipEventRecord(ev[stage * 2 + end], st);
+  };
+#define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
+
+  mark(VDN_STAGE_TOTAL, 0, main);
+  // linear branch on the side stream, forked from the caller's stream
+  VDN_TRY(hipEventRecord(plan->ev_fork, main));
+  VDN_TRY(hipStreamWaitEvent(plan->side, plan->ev_fork, 0));
+  mark(VDN_STAGE_VDA_STATS, 0, plan->side);
+  VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, plan->side));
+  mark(VDN_STAGE_VDA_STATS, 1, plan->side);
+  mark(VDN_STAGE_VDA_SCAN, 0, plan->side);
+  VDN_TRY(vdn::launch_vda_scan(s, b, plan->side));
+  mark(VDN_STAGE_VDA_SCAN, 1, plan->side);
+  VDN_TRY(hipEventRecord(plan->ev_join, plan->side));
+  // softmax branch on the caller's stream
+  mark(VDN_STAGE_PREP, 0, main);
+  if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
+  mark(VDN_STAGE_PREP, 1, main);
+  mark(VDN_STAGE_SOFTMAX, 0, main);
+  if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
+  else VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
+  mark(VDN_STAGE_SOFTMAX, 1, main);
+  // join, then readout + gates + projections
+  VDN_TRY(hipStreamWaitEvent(main, plan->ev_join, 0));
+  mark(VDN_STAGE_EPILOGUE, 0, main);
+  VDN_TRY(vdn::launch_epilogue(s, in, b, plan->kinds.epilogue_mfma, main));
+  mark(VDN_STAGE_EPILOGUE, 1, main);
+  mark(VDN_STAGE_TOTAL, 1, main);
+#undef VDN_TRY
+  return VDN_OK;
+}
+
+vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes) {
+  if (!plan || !bytes) return VDN_ERR_INVALID_ARG;
+  const vdn::Shape& s = plan->s;
+  const size_t dd = (size_t)s.d * s.d;
+  switch (which) {
+    case VDN_BUF_OS: *bytes = (size_t)s.T * s.N * s.H * s.d * (s.dtype == VDN_BF16 ? 2 : 4); break;
+    case VDN_BUF_STATES: *bytes = (size_t)2 * (s.Nc + 1) * s.H * dd * 4; break;
+    case VDN_BUF_MINV: *bytes = (size_t)(s.T + 1) * s.H * dd * 4; break;
+    default: return VDN_ERR_INVALID_ARG;
+  }
+  return VDN_OK;
+}
+
+vdn_status vdn_debug_copy(const vdn_plan* plan, int which, void* dst, size_t bytes, void* stream) {
+  size_t want = 0;
+  vdn_status st = vdn_debug_buffer_bytes(plan, which, &want);
+  if (st != VDN_OK) return st;
+  if (!dst || bytes != want) return VDN_ERR_INVALID_ARG;
+  size_t off = which == VDN_BUF_OS ? plan->lay.os : which == VDN_BUF_STATES ? plan->lay.states : plan->lay.minv;
+  if (hipMemcpyAsync(dst, plan->ws + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return VDN_ERR_HIP;
+  }
+  return VDN_OK;
+}
+
+vdn_status vdn_profile_enable(vdn_plan* plan, int max_calls) {
+  if (!plan || max_calls < 0 || max_calls > 100000) return VDN_ERR_INVALID_ARG;
+  for (hipEvent_t e : plan->prof_events) if (e) (void)hipEventDestroy(e);
+  plan->prof_events.assign((size_t)max_calls * VDN_NUM_STAGES * 2, nullptr);
+  plan->prof_max = 0;
+  plan->prof_count = 0;
+  for (auto& e : plan->prof_events)
+    if (hipEventCreate(&e) != hipSuccess) { e = nullptr; return VDN_ERR_HIP; }
+  plan->prof_max = max_calls;
+  return VDN_OK;
+}
+
+vdn_status vdn_profile_read(vdn_plan* plan, float* ms, int n_stages, int* calls) {
+  if (!plan || !ms || n_stages < 0 || n_stages > VDN_NUM_STAGES) return VDN_ERR_INVALID_ARG;
+  for (int st = 0; st < n_stages; ++st) ms[st] = 0.f;
+  for (int c = 0; c < plan->prof_count; ++c) {
+    for (int st = 0; st < n_stages; ++st) {
+      hipEvent_t a = plan->prof_events[((size_t)c * VDN_NUM_STAGES + st) * 2];
+      hipEvent_t z = plan->prof_events[((size_t)c * VDN_NUM_STAGES + st) * 2 + 1];
+      if (hipEventSynchronize(z) != hipSuccess) return VDN_ERR_HIP;
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, a, z) != hipSuccess) return VDN_ERR_HIP;
+      ms[st] += t;
+    }
+  }
+  if (calls) *calls = plan->prof_count;
+  return VDN_OK;
+}
+
+}  // extern "C"

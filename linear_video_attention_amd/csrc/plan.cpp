@@ -1,0 +1,81 @@
+// Host-side plan logic of the VDN layer: key ranges of the softmax branch, scan order of the
+// linear branch, workspace layout and kernel selection.  No GPU calls.
+//
+// Frame rules from "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section
+// "Local Softmax and Long-Range Linear Memory": chunks of C consecutive frames; a chunk attends to
+// itself and its two neighbours; the first and last frames are anchors seen by every frame and
+// seeing every frame; the forward state covers the frames before the window and the reverse state
+// those after it, neither covering window or boundary frames.
+#include "vdn_internal.h"
+
+#include <algorithm>
+
+namespace vdn {
+
+bool is_boundary(const Shape& s, int t) { return s.anchors && (t == 0 || t == s.T - 1); }
+
+int key_ranges(const Shape& s, int t, int64_t* r, int max_ranges) {
+  int64_t tmp[2 * kMaxRanges];
+  int n = 0;
+  auto add = [&](int64_t a, int64_t b) {
+    if (b > a) { tmp[2 * n] = a; tmp[2 * n + 1] = b; ++n; }
+  };
+  const int64_t base = s.text_pad, N = s.N;
+  add(0, s.n_text);
+  if (is_boundary(s, t)) {
+    add(base, base + (int64_t)s.T * N);
+  } else {
+    const int c = t / s.C;
+    const int lo = std::max(0, (c - 1) * s.C);
+    const int hi = std::min(s.T, (c + 2) * s.C);
+    if (s.anchors && lo > 0) add(base, base + N);                        // frame 0
+    add(base + lo * N, base + hi * N);                                   // window
+    if (s.anchors && s.T - 1 >= hi) add(base + (int64_t)(s.T - 1) * N, base + (int64_t)s.T * N);  // frame T-1
+  }
+  for (int i = 0; i < n && i < max_ranges; ++i) { r[2 * i] = tmp[2 * i]; r[2 * i + 1] = tmp[2 * i + 1]; }
+  return n;
+}
+
+int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames) {
+  int n = 0;
+  if (is_boundary(s, t)) return 0;
+  const int c = t / s.C;
+  if (dir == 0) {
+    for (int f = 0; f < s.T; ++f)
+      if (!is_boundary(s, f) && f / s.C <= c - 2) { if (n < max_frames) frames[n] = f; ++n; }
+  } else {
+    for (int f = s.T - 1; f >= 0; --f)
+      if (!is_boundary(s, f) && f / s.C >= c + 2) { if (n < max_frames) frames[n] = f; ++n; }
+  }
+  return n;
+}
+
+Layout make_layout(const Shape& s, bool mfma_softmax) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += (size_t)round_up((int64_t)bytes, 256); return o; };
+  const size_t elt = s.dtype == VDN_BF16 ? 2 : 4;
+  const size_t tok = (size_t)s.T * s.N * s.H * s.d;
+  const size_t dd = (size_t)s.d * s.d;
+  L.os = take(tok * elt);
+  L.kp = mfma_softmax ? take((size_t)s.H * s.Lk * s.d * 2) : 0;
+  L.vt = mfma_softmax ? take((size_t)s.H * s.Lk * s.d * 2) : 0;
+  L.minv = take((size_t)(s.T + 1) * s.H * dd * 4);
+  L.bw = take((size_t)(s.T + 1) * s.H * dd * 4);
+  L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
+  L.ranges = take((size_t)s.T * (2 * kMaxRanges + 1) * 4);
+  L.total = off;
+  return L;
+}
+
+Kinds choose_kinds(const Shape& s) {
+  Kinds k{};
+  const bool bf16 = s.dtype == VDN_BF16;
+  k.softmax_mfma = bf16 && (s.d == 64 || s.d == 128) && s.N % 8 == 0;
+  k.stats_mfma = false;
+  k.scan_mfma = false;
+  k.epilogue_mfma = false;
+  return k;
+}
+
+}  // namespace vdn

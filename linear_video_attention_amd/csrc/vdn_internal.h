@@ -1,0 +1,82 @@
+// Internal declarations shared by the host code and the kernel launchers of the VDN layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/vdn.h"
+
+namespace vdn {
+
+constexpr int kTextPad = 64;        // text keys occupy [0, round_up(n_text, 64)) of a head's key space
+constexpr int kMaxRanges = 4;       // text, window, frame 0, frame T-1
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Host-side description of the layer shape plus everything derived from it.
+struct Shape {
+  int T, N, C, n_text, H, d, anchors;
+  vdn_dtype dtype;
+  int Nc;            // number of chunks
+  int text_pad;      // n_text rounded up to kTextPad
+  int64_t Lk;        // key-space length per head: text_pad + T*N
+};
+
+// Key ranges of query frame t in a head's key space (see vdn_key_ranges); returns the count.
+int key_ranges(const Shape& s, int t, int64_t* ranges, int max_ranges);
+// Frames written into the forward (dir 0) / reverse (dir 1) state of query frame t, in order.
+int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames);
+bool is_boundary(const Shape& s, int t);
+
+// Device workspace layout (byte offsets from the workspace base).
+struct Layout {
+  size_t os;        // o_s [T*N][H][d] plan dtype
+  size_t kp;        // packed keys  [H][Lk][d] bf16          (MFMA softmax path only)
+  size_t vt;        // packed values, transposed [H][d][Lk] bf16
+  size_t minv;      // M = (I+A)^-1  [T+1][H][d][d] f32
+  size_t bw;        // B             [T+1][H][d][d] f32
+  size_t states;    // S_fwd, S_rev  [2][Nc+1][H][d][d] f32
+  size_t ranges;    // int32 [T][2*kMaxRanges] + int32 [T] counts
+  size_t total;
+};
+Layout make_layout(const Shape& s, bool mfma_softmax);
+
+// Kernel selection per stage.
+struct Kinds {
+  bool softmax_mfma;
+  bool stats_mfma;
+  bool scan_mfma;
+  bool epilogue_mfma;
+};
+Kinds choose_kinds(const Shape& s);
+
+struct Buffers {
+  void* os;
+  uint16_t* kp;
+  uint16_t* vt;
+  float* minv;
+  float* bw;
+  float* states;
+  const int* ranges;   // [T][2*kMaxRanges]
+  const int* nranges;  // [T]
+};
+
+struct Inputs {
+  const void *q, *k, *v;
+  const float* beta;
+  const void* text_kv;
+  const void *gate_w, *proj_w;
+  void* out;
+};
+
+// Launchers (each returns hipGetLastError() after its launches).
+hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
+hipError_t launch_vda_scan(const Shape& s, const Buffers& b, hipStream_t st);
+hipError_t launch_epilogue(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
+
+}  // namespace vdn

@@ -1,0 +1,210 @@
+"""Thin ctypes binding of the VDN layer C ABI (``include/vdn.h``).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and contiguity, and their
+device pointers are handed to the library; every step of the layer runs in the library's HIP
+kernels.  There is no fallback: if ``libvdn.so`` is missing or no GPU is visible, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvdn.so")
+
+VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_OUT_OF_MEMORY, VDN_ERR_HIP = 0, -1, -2, -3, -4
+VDN_F32, VDN_BF16 = 0, 1
+VDN_FLAG_GENERIC_KERNELS = 1
+VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV = 0, 1, 2
+STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total")
+
+# every symbol include/vdn.h declares: (name, restype, argtypes)
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = [
+    ("vdn_plan_create", _c_int, [_c_int] * 7 + [_c_int, ctypes.POINTER(_vp)]),
+    ("vdn_plan_create_ex", _c_int, [_c_int] * 7 + [_c_int, ctypes.c_uint, ctypes.POINTER(_vp)]),
+    ("vdn_forward", _c_int, [_vp] * 10),
+    ("vdn_plan_destroy", None, [_vp]),
+    ("vdn_status_str", ctypes.c_char_p, [_c_int]),
+    ("vdn_plan_workspace_bytes", _c_size, [_vp]),
+    ("vdn_key_ranges", _c_int, [_c_int] * 6 + [ctypes.POINTER(ctypes.c_int64), _c_int]),
+    ("vdn_scan_frames", _c_int, [_c_int] * 5 + [ctypes.POINTER(_c_int), _c_int]),
+    ("vdn_debug_buffer_bytes", _c_int, [_vp, _c_int, ctypes.POINTER(_c_size)]),
+    ("vdn_debug_copy", _c_int, [_vp, _c_int, _vp, _c_size, _vp]),
+    ("vdn_profile_enable", _c_int, [_vp, _c_int]),
+    ("vdn_profile_read", _c_int, [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]),
+    ("vdn_plan_kernel_kind", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)]),
+]
+
+_lib = None
+
+
+class VdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libvdn.so`` (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().vdn_status_str(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != VDN_OK:
+        raise VdnError(status, what)
+
+
+# ---- host-only helpers ----
+
+def vdn_key_ranges(T, N, C, n_text, anchors, t, max_ranges=4):
+    buf = (ctypes.c_int64 * (2 * max_ranges))()
+    n = lib().vdn_key_ranges(T, N, C, n_text, int(anchors), t, buf, max_ranges)
+    if n < 0:
+        raise ValueError("invalid arguments")
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(min(n, max_ranges))]
+
+
+def vdn_scan_frames(T, C, anchors, t, direction):
+    buf = (ctypes.c_int * max(T, 1))()
+    n = lib().vdn_scan_frames(T, C, int(anchors), t, direction, buf, T)
+    if n < 0:
+        raise ValueError("invalid arguments")
+    return [buf[i] for i in range(n)]
+
+
+# ---- plan ----
+
+def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False):
+    """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"."""
+    dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
+    h = _vp()
+    flags = VDN_FLAG_GENERIC_KERNELS if generic else 0
+    _check(lib().vdn_plan_create_ex(T, N, C, n_text, H, d, int(anchors), dt, flags, ctypes.byref(h)),
+           "vdn_plan_create")
+    return h.value
+
+
+def vdn_plan_destroy(plan):
+    lib().vdn_plan_destroy(plan)
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def vdn_forward(plan, q, k, v, beta, text_kv, gate_w, proj_w, out, stream=None):
+    """Enqueue the layer forward on ``stream`` (default: torch's current stream).  All arguments
+    are device tensors laid out as in ``include/vdn.h``; ``out`` is written."""
+    ptr = lambda x: None if x is None else x.data_ptr()
+    _check(lib().vdn_forward(plan, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(text_kv), ptr(gate_w),
+                             ptr(proj_w), ptr(out), _stream_ptr(stream)), "vdn_forward")
+
+
+class Plan:
+    """Owning wrapper of a plan with argument checks on torch tensors."""
+
+    def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("no GPU visible: the VDN layer runs only on the GPU")
+        self.T, self.N, self.C, self.n_text, self.H, self.d = T, N, C, n_text, H, d
+        self.anchors = bool(anchors)
+        self.dtype = dtype
+        self.torch_dtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+        self.Nc = (T + C - 1) // C
+        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic)
+
+    def close(self):
+        if self.handle:
+            vdn_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _expect(self, name, x, shape, dtype):
+        import torch
+        if x is None or not isinstance(x, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+        if not x.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+        if x.dtype != dtype:
+            raise ValueError(f"{name} has dtype {x.dtype}, expected {dtype}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def forward(self, q, k, v, beta, text_kv, gate_w, proj_w, out=None, stream=None):
+        import torch
+        TN, H, d = self.T * self.N, self.H, self.d
+        dt = self.torch_dtype
+        for name, x in (("q", q), ("k", k), ("v", v)):
+            self._expect(name, x, (TN, H, d), dt)
+        self._expect("beta", beta, (self.n_text + TN, H), torch.float32)
+        if self.n_text > 0:
+            self._expect("text_kv", text_kv, (2, self.n_text, H, d), dt)
+        self._expect("gate_w", gate_w, (2, d, d), dt)
+        self._expect("proj_w", proj_w, (2, d, d), dt)
+        if out is None:
+            out = torch.empty((TN, H, d), dtype=dt, device=q.device)
+        self._expect("out", out, (TN, H, d), dt)
+        vdn_forward(self.handle, q, k, v, beta, text_kv if self.n_text > 0 else None, gate_w, proj_w, out,
+                    stream)
+        return out
+
+    def debug_buffer(self, which, stream=None):
+        """Copy an intermediate buffer of the last forward into a new device tensor."""
+        import torch
+        nbytes = ctypes.c_size_t()
+        _check(lib().vdn_debug_buffer_bytes(self.handle, which, ctypes.byref(nbytes)), "vdn_debug_buffer_bytes")
+        if which == VDN_BUF_OS:
+            dst = torch.empty((self.T * self.N, self.H, self.d), dtype=self.torch_dtype, device="cuda")
+        elif which == VDN_BUF_STATES:
+            dst = torch.empty((2, self.Nc + 1, self.H, self.d, self.d), dtype=torch.float32, device="cuda")
+        else:
+            dst = torch.empty((self.T + 1, self.H, self.d, self.d), dtype=torch.float32, device="cuda")
+        assert dst.numel() * dst.element_size() == nbytes.value
+        _check(lib().vdn_debug_copy(self.handle, which, dst.data_ptr(), nbytes.value, _stream_ptr(stream)),
+               "vdn_debug_copy")
+        return dst
+
+    def workspace_bytes(self):
+        return lib().vdn_plan_workspace_bytes(self.handle)
+
+    def kernel_kind(self, stage):
+        kind = ctypes.c_int()
+        _check(lib().vdn_plan_kernel_kind(self.handle, stage, ctypes.byref(kind)), "vdn_plan_kernel_kind")
+        return kind.value
+
+    def profile_enable(self, max_calls):
+        _check(lib().vdn_profile_enable(self.handle, max_calls), "vdn_profile_enable")
+
+    def profile_read(self):
+        """Summed milliseconds per stage over the recorded forwards, and their count."""
+        ms = (ctypes.c_float * len(STAGES))()
+        calls = ctypes.c_int()
+        _check(lib().vdn_profile_read(self.handle, ms, len(STAGES), ctypes.byref(calls)), "vdn_profile_read")
+        return {name: ms[i] for i, name in enumerate(STAGES)}, calls.value

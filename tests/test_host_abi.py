@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI library (no GPU): it loads, exports every symbol the header
+declares, rejects invalid plans before touching the GPU, and its key ranges and scan order equal
+the oracle's frame sets."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import vdn_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def vdn():
+    from linear_video_attention_amd import vdn as binding
+    return binding
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "vdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vdn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(vdn):
+    names = declared_functions()
+    assert len(names) >= 10
+    handle = ctypes.CDLL(vdn.LIB_PATH)
+    for name in names:
+        assert hasattr(handle, name), name
+    bound = {n for n, _, _ in vdn.SIGNATURES}
+    assert set(names) == bound, set(names) ^ bound
+
+
+def test_status_strings(vdn):
+    for s in (0, -1, -2, -3, -4):
+        assert vdn.status_str(s)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 16, 2, 1, 1, 16, 1, 0), -1),      # T = 0
+    ((4, 0, 2, 1, 1, 16, 1, 0), -1),       # N = 0
+    ((4, 16, 0, 1, 1, 16, 1, 0), -1),      # C = 0
+    ((4, 16, 2, -1, 1, 16, 1, 0), -1),     # n_text < 0
+    ((4, 16, 2, 1, 0, 16, 1, 0), -1),      # H = 0
+    ((4, 16, 2, 1, 1, 16, 2, 0), -1),      # anchors not 0/1
+    ((4, 16, 2, 1, 1, 48, 1, 0), -2),      # unsupported d
+    ((4, 16, 2, 1, 1, 16, 1, 7), -2),      # unknown dtype
+    ((1 << 20, 1 << 12, 2, 1, 1, 16, 1, 1), -2),   # too many tokens
+])
+def test_invalid_plans_rejected_on_host(vdn, args, status):
+    h = ctypes.c_void_p(1234)
+    st = vdn.lib().vdn_plan_create(*args, ctypes.byref(h))
+    assert st == status
+    assert h.value is None
+
+
+def test_null_arguments_rejected(vdn):
+    L = vdn.lib()
+    assert L.vdn_plan_create(4, 16, 2, 1, 1, 16, 1, 0, None) == -1
+    assert L.vdn_forward(None, *([None] * 9)) == -1
+    L.vdn_plan_destroy(None)                       # no-op
+    assert L.vdn_plan_workspace_bytes(None) == 0
+    assert L.vdn_profile_enable(None, 4) == -1
+    assert vdn.lib().vdn_key_ranges(4, 16, 2, 1, 1, 9, None, 0) == -1
+
+
+SHAPES = [(T, C, anchors) for T in (1, 2, 3, 5, 7, 16, 20, 31) for C in (1, 2, 3, 5) for anchors in (True, False)]
+
+
+@pytest.mark.parametrize("T,C,anchors", SHAPES)
+def test_key_ranges_match_oracle(vdn, T, C, anchors):
+    N, n_text = 3, 5
+    text_pad = 64
+    for t in range(T):
+        ranges = vdn.vdn_key_ranges(T, N, C, n_text, anchors, t)
+        keys = []
+        for a, b in ranges:
+            assert a < b
+            keys.extend(range(a, b))
+        assert keys == sorted(keys) and len(set(keys)) == len(keys)
+        expect = list(range(n_text)) + [text_pad + f * N + n for f in orc.key_frames(t, T, C, anchors) for n in range(N)]
+        assert keys == expect, (t, ranges)
+
+
+@pytest.mark.parametrize("T,C,anchors", SHAPES)
+def test_scan_frames_match_oracle(vdn, T, C, anchors):
+    for t in range(T):
+        _, _, fwd, rev = orc.frame_sets(t, T, C, anchors)
+        assert vdn.vdn_scan_frames(T, C, anchors, t, 0) == fwd
+        assert vdn.vdn_scan_frames(T, C, anchors, t, 1) == rev[::-1]
+
+
+def test_key_ranges_at_768p_workload(vdn):
+    # interior query frame: text + window (15 frames) + both anchors = 26 624 keys
+    ranges = vdn.vdn_key_ranges(75, 1536, 5, 512, True, 37)
+    assert sum(b - a for a, b in ranges) == 512 + 17 * 1536
+    # boundary query frame: text + every frame
+    ranges = vdn.vdn_key_ranges(75, 1536, 5, 512, True, 74)
+    assert sum(b - a for a, b in ranges) == 512 + 75 * 1536
+

@@ -1,0 +1,142 @@
+"""Parity of the HIP layer (through the C ABI) with the CPU oracle, element by element.
+
+Tolerance: max |gpu - oracle| <= 1e-4 * RMS(oracle) for fp32 workloads and <= 2e-2 * RMS(oracle)
+for bf16 workloads (inputs are the same bf16-rounded values on both sides).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import bruteforce
+from oracle import vdn_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import TOL, combined_states, make_plan, rel_err, run_layer, softmax_out, to_device  # noqa: E402
+
+
+def check_full(w, generic=False, seed=0, stress=False):
+    inp = synth.make_inputs(w, seed=seed, stress=stress)
+    plan = make_plan(w, generic=generic)
+    dev = to_device(inp, w.dtype)
+    out = run_layer(plan, dev).float().cpu().numpy()
+    ref, mids = orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors, with_intermediates=True)
+    tol = TOL[w.dtype]
+    e_out = rel_err(out, ref)
+    e_os = rel_err(softmax_out(plan), mids["o_s"])
+    e_st = rel_err(combined_states(plan), orc.chunk_states(inp, w.T, w.N, w.C, w.anchors))
+    print(f"{w} generic={generic}: out {e_out:.2e}  o_s {e_os:.2e}  states {e_st:.2e}", flush=True)
+    assert e_os <= tol, ("o_s", e_os)
+    assert e_st <= tol, ("states", e_st)
+    assert e_out <= tol, ("out", e_out)
+    plan.close()
+    return inp, out
+
+
+def test_tiny_fp32_matches_oracle_and_bruteforce():
+    w = synth.WORKLOADS["tiny"]
+    inp, out = check_full(w)
+    ref, _, _ = bruteforce.layer_dense(inp, w.T, w.N, w.C, w.anchors)
+    assert rel_err(out, ref) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_small_bf16_matches_oracle(generic):
+    check_full(synth.WORKLOADS["small"], generic=generic)
+
+
+RAGGED = [
+    # n_text, T, N, C, H, d, dtype, anchors
+    (37, 13, 200, 3, 3, 64, "bf16", True),       # partial query tile, odd text, T % C != 0
+    (0, 7, 72, 2, 2, 128, "bf16", True),         # no text, N not a multiple of 64
+    (5, 9, 136, 5, 2, 128, "bf16", False),       # anchors off
+    (1, 1, 264, 5, 1, 64, "bf16", True),         # a single (boundary) frame
+    (3, 2, 64, 1, 2, 128, "bf16", True),         # two frames, both boundary
+    (64, 11, 320, 4, 2, 128, "bf16", True),      # several 256-query tiles + tail
+    (7, 12, 24, 3, 2, 32, "bf16", True),         # d = 32 (generic kernels)
+    (2, 10, 20, 3, 2, 16, "bf16", True),         # d = 16, N % 8 != 0 (generic kernels)
+    (9, 11, 37, 3, 2, 64, "fp32", True),         # fp32, ragged everything
+    (1, 6, 5, 2, 1, 128, "fp32", False),         # fp32, d = 128, anchors off
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "x".join(str(x) for x in c))
+def test_ragged_shapes_match_oracle(case):
+    n_text, T, N, C, H, d, dtype, anchors = case
+    w = synth.custom(n_text, T, N, C, H, d, dtype, "sigmoid", anchors)
+    check_full(w, seed=3)
+
+
+def test_stress_keys_crowded_gram():
+    """Keys of each frame crowd one direction (lambda_max(A) near sum beta): exercises the fp32
+    inverse of I + A at a condition number in the hundreds."""
+    w = synth.custom(16, 12, 256, 3, 2, 128, "bf16", "sigmoid", True)
+    check_full(w, seed=5, stress=True)
+
+
+@pytest.mark.parametrize("name", ["medium", "768p", "long"])
+def test_full_size_sampled_rows(name):
+    """Full-size workloads in the launch configuration the benchmark times: every frame's first
+    and last token plus two random tokens per frame, all heads, against the oracle."""
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w, seed=0)
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
+    out = run_layer(plan, dev)
+    rows = synth.sample_rows(w)
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    del dev, out
+    ref = orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors, rows=rows)
+    e = rel_err(got, ref)
+    print(f"{name}: sampled {len(rows)} rows, out err {e:.2e}", flush=True)
+    assert e <= TOL[w.dtype]
+    plan.close()
+
+
+def test_two_runs_bit_identical():
+    w = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(w, seed=1)
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
+    a = run_layer(plan, dev).clone()
+    b = run_layer(plan, dev)
+    assert torch.equal(a, b)
+    plan.close()
+
+
+def test_generic_and_mfma_kernels_agree():
+    w = synth.custom(32, 10, 256, 5, 2, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, seed=2)
+    dev = to_device(inp, w.dtype)
+    fast, slow = make_plan(w), make_plan(w, generic=True)
+    assert fast.kernel_kind(0) == 1 and slow.kernel_kind(0) == 0
+    a = run_layer(fast, dev).float().cpu().numpy()
+    b = run_layer(slow, dev).float().cpu().numpy()
+    assert rel_err(a, b) <= TOL["bf16"]
+    fast.close()
+    slow.close()
+
+
+def test_forward_argument_errors():
+    from linear_video_attention_amd import vdn
+    w = synth.custom(4, 4, 64, 2, 1, 64, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w)
+    dev = to_device(inp, w.dtype)
+    plan = make_plan(w)
+    out = torch.empty_like(dev["q"])
+    L = vdn.lib()
+    ptr = lambda x: x.data_ptr()
+    args = [ptr(dev[k]) for k in ("q", "k", "v", "beta", "text_kv", "gate_w", "proj_w")]
+    stream = torch.cuda.current_stream().cuda_stream
+    assert L.vdn_forward(plan.handle, *args, ptr(out), stream) == 0
+    bad = list(args)
+    bad[0] += 2                                               # misaligned q
+    assert L.vdn_forward(plan.handle, *bad, ptr(out), stream) == -1
+    assert L.vdn_forward(plan.handle, *args, args[0], stream) == -1   # out aliases q
+    nul = list(args)
+    nul[4] = None                                             # text_kv missing with n_text > 0
+    assert L.vdn_forward(plan.handle, *nul, ptr(out), stream) == -1
+    torch.cuda.synchronize()
+    plan.close()
