@@ -24,6 +24,7 @@ SOURCES = [
     "softmax_mfma.hip",
     "vda.hip",
     "epilogue_simt.hip",
+    "epilogue_mfma.hip",
 ]
 
 ARCH = "gfx950"

@@ -35,6 +35,10 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.minv = reinterpret_cast<float*>(ws + p->lay.minv);
   b.bw = reinterpret_cast<float*>(ws + p->lay.bw);
   b.states = reinterpret_cast<float*>(ws + p->lay.states);
+  b.wt = p->kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.wt) : nullptr;
+  b.kmax_part = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax_part) : nullptr;
+  b.kmax = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax) : nullptr;
+  b.flags = p->kinds.softmax_mfma ? reinterpret_cast<int*>(ws + p->lay.flags) : nullptr;
   b.ranges = reinterpret_cast<const int*>(ws + p->lay.ranges);
   b.nranges = b.ranges + (size_t)p->s.T * 2 * vdn::kMaxRanges;
   return b;
@@ -61,6 +65,7 @@ vdn::Shape make_shape(int T, int N, int C, int n_text, int H, int d, int anchors
   s.Nc = (T + C - 1) / C;
   s.text_pad = (int)vdn::round_up(n_text, vdn::kTextPad);
   s.Lk = (int64_t)s.text_pad + (int64_t)T * N;
+  s.Ls = s.Lk + 64;
   return s;
 }
 
@@ -117,7 +122,7 @@ vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int
   if (!p) return VDN_ERR_OUT_OF_MEMORY;
   p->s = make_shape(T, N, C, n_text, H, d, anchors, dtype);
   p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
-  p->lay = vdn::make_layout(p->s, p->kinds.softmax_mfma);
+  p->lay = vdn::make_layout(p->s, p->kinds.softmax_mfma, p->kinds.epilogue_mfma);
   if (hipGetDevice(&p->device) != hipSuccess) { free_plan(p); return VDN_ERR_HIP; }
   if (hipMalloc(&p->ws, p->lay.total) != hipSuccess) {
     (void)hipGetLastError();
@@ -133,7 +138,11 @@ vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int
     for (int i = 0; i < 2 * n; ++i) tab[(size_t)t * 2 * vdn::kMaxRanges + i] = (int)r[i];
     tab[(size_t)T * 2 * vdn::kMaxRanges + t] = n;
   }
-  if (hipMemcpy(p->ws + p->lay.ranges, tab.data(), tab.size() * sizeof(int), hipMemcpyHostToDevice) != hipSuccess ||
+  // the packed K/V padding tile must hold finite values (zero); the packing pass never writes it
+  if ((p->kinds.softmax_mfma &&
+       (hipMemset(p->ws + p->lay.kp, 0, (size_t)p->s.H * p->s.Ls * d * 2) != hipSuccess ||
+        hipMemset(p->ws + p->lay.vt, 0, (size_t)p->s.H * p->s.Ls * d * 2) != hipSuccess)) ||
+      hipMemcpy(p->ws + p->lay.ranges, tab.data(), tab.size() * sizeof(int), hipMemcpyHostToDevice) != hipSuccess ||
       hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming) != hipSuccess) {
@@ -152,7 +161,7 @@ vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
   if (!plan || !kind) return VDN_ERR_INVALID_ARG;
   switch (stage) {
     case VDN_STAGE_SOFTMAX: *kind = plan->kinds.softmax_mfma; break;
-    case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma; break;
+    case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma || plan->kinds.epilogue_mfma; break;
     case VDN_STAGE_VDA_STATS: *kind = plan->kinds.stats_mfma; break;
     case VDN_STAGE_VDA_SCAN: *kind = plan->kinds.scan_mfma; break;
     case VDN_STAGE_EPILOGUE: *kind = plan->kinds.epilogue_mfma; break;
@@ -202,6 +211,7 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   // softmax branch on the caller's stream
   mark(VDN_STAGE_PREP, 0, main);
   if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
+  if (plan->kinds.epilogue_mfma) VDN_TRY(vdn::launch_prep_weights(s, in, b, main));
   mark(VDN_STAGE_PREP, 1, main);
   mark(VDN_STAGE_SOFTMAX, 0, main);
   if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
@@ -210,7 +220,8 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   // join, then readout + gates + projections
   VDN_TRY(hipStreamWaitEvent(main, plan->ev_join, 0));
   mark(VDN_STAGE_EPILOGUE, 0, main);
-  VDN_TRY(vdn::launch_epilogue(s, in, b, plan->kinds.epilogue_mfma, main));
+  if (plan->kinds.epilogue_mfma) VDN_TRY(vdn::launch_epilogue_mfma(s, in, b, main));
+  else VDN_TRY(vdn::launch_epilogue(s, in, b, false, main));
   mark(VDN_STAGE_EPILOGUE, 1, main);
   mark(VDN_STAGE_TOTAL, 1, main);
 #undef VDN_TRY

@@ -50,7 +50,7 @@ int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames) {
   return n;
 }
 
-Layout make_layout(const Shape& s, bool mfma_softmax) {
+Layout make_layout(const Shape& s, bool mfma_softmax, bool mfma_epilogue) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (size_t)round_up((int64_t)bytes, 256); return o; };
@@ -58,11 +58,15 @@ Layout make_layout(const Shape& s, bool mfma_softmax) {
   const size_t tok = (size_t)s.T * s.N * s.H * s.d;
   const size_t dd = (size_t)s.d * s.d;
   L.os = take(tok * elt);
-  L.kp = mfma_softmax ? take((size_t)s.H * s.Lk * s.d * 2) : 0;
-  L.vt = mfma_softmax ? take((size_t)s.H * s.Lk * s.d * 2) : 0;
+  L.kp = mfma_softmax ? take((size_t)s.H * s.Ls * s.d * 2) : 0;
+  L.vt = mfma_softmax ? take((size_t)s.H * s.Ls * s.d * 2) : 0;
   L.minv = take((size_t)(s.T + 1) * s.H * dd * 4);
   L.bw = take((size_t)(s.T + 1) * s.H * dd * 4);
   L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
+  L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
+  L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;
+  L.kmax = mfma_softmax ? take((size_t)s.H * 4) : 0;
+  L.flags = mfma_softmax ? take((size_t)softmax_grid(s) * 4) : 0;
   L.ranges = take((size_t)s.T * (2 * kMaxRanges + 1) * 4);
   L.total = off;
   return L;
@@ -71,10 +75,11 @@ Layout make_layout(const Shape& s, bool mfma_softmax) {
 Kinds choose_kinds(const Shape& s) {
   Kinds k{};
   const bool bf16 = s.dtype == VDN_BF16;
-  k.softmax_mfma = bf16 && (s.d == 64 || s.d == 128) && s.N % 8 == 0;
+  // lane offsets into one head's packed V^T are 32-bit: d * Ls * 2 bytes must stay below 2^31
+  k.softmax_mfma = bf16 && (s.d == 64 || s.d == 128) && s.N % 8 == 0 && (int64_t)s.d * s.Ls * 2 < (int64_t(1) << 31);
   k.stats_mfma = false;
   k.scan_mfma = false;
-  k.epilogue_mfma = false;
+  k.epilogue_mfma = bf16 && (s.d == 64 || s.d == 128);
   return k;
 }
 

@@ -15,10 +15,13 @@
 //     lane ends up holding 16 consecutive keys of one query -- the row permutation used when the
 //     K fragments are read makes those keys contiguous;  O^T += V^T P^T with the same instruction,
 //     P taken straight from the S^T registers (no LDS round trip);
-//   * online softmax in base 2 with a lazy rescale: the running reference max only moves when a
-//     tile's max exceeds it by more than 8 (a factor 256), so the O rescale (128 values per lane)
-//     is skipped for almost every tile; exactness is unaffected since the final division uses the
-//     same reference;
+//   * exponent reference: softmax is invariant to the offset subtracted from the scores, and
+//     |q.k| <= |q| max|k| bounds every score of the query, so p = 2^(s c - |q| kmax c) never
+//     exceeds 1 and needs no running maximum and no rescaling of the accumulator (kmax = largest
+//     key norm of the head, from the packing pass).  When that bound is so loose that the largest
+//     term could underflow (|q| kmax c > 48 in log2 units -- far outside unit-normalised inputs)
+//     the workgroup flags itself and a second launch of the same kernel with the classic online
+//     maximum (running max, rescale of the accumulator) redoes just those workgroups;
 //   * workgroup order: the long boundary-frame workgroups first (longest job first), then the
 //     interior ones remapped so that consecutive query tiles -- which share their key window --
 //     land on the same XCD (workgroups are dispatched round-robin over the 8 XCDs).
@@ -31,13 +34,17 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kBK = 64;        // keys per tile
 constexpr int kWaves = 4;
 constexpr int kQW = 64;        // queries per wave
 constexpr int kBQ = kWaves * kQW;
-constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr float kMaxRef = 48.0f;            // log2 units; beyond it the fallback kernel runs
+constexpr float kRescaleThreshold = 8.0f;   // fallback: log2 units of growth before a rescale
 constexpr float kMasked = -1.0e30f;
+constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
 
 // LDS chunk swizzles (16-byte chunks).  K rows are read 16 rows per 16 lanes in the order
 // {0-3,16-19,4-7,20-23} (+8 for the next 16 lanes); V^T rows 16 consecutive rows per 16 lanes.
@@ -58,42 +65,63 @@ struct Smem {
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-typedef __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-constexpr int kVmcntZero = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
+struct Params {
+  const bf16_t* q;
+  const bf16_t* kp;
+  const bf16_t* vt;
+  bf16_t* o_s;
+  const int* ranges;
+  const int* nranges;
+  const float* kmax;
+  int* flags;
+  int T, N, H;
+  int64_t Ls;
+  int QT, n_bnd_wg, n_int_frames, first_int_frame, per_xcd, n_int_wg;
+  float c_log2;
+};
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vt,
-    bf16_t* __restrict__ o_s, const int* __restrict__ ranges, const int* __restrict__ nranges, int T, int N, int H,
-    int64_t Lk, int QT, int n_bnd_wg, int n_int_frames, int first_int_frame, int per_xcd, int n_int_wg,
-    float c_log2) {
+// FALLBACK = false: fixed exponent reference, writes its workgroup's flag (1 = redo).
+// FALLBACK = true : online maximum; runs only the workgroups flagged by the first launch.
+template <int D, bool FALLBACK>
+__global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
   using SM = Smem<D>;
   constexpr int KS = D / 16;          // k-steps of the QK^T contraction
   constexpr int DT = D / 32;          // 32-row d tiles of O^T
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int unsafe_any;
 
-  // ---- workgroup -> (head, frame, query tile) ----
   const int w = blockIdx.x;
+  if constexpr (FALLBACK) {
+    if (P.flags[w] == 0) return;
+  }
+  // ---- workgroup -> (head, frame, query tile) ----
   int h, t, qt;
-  if (w < n_bnd_wg) {
-    qt = w % QT;
-    const int rest = w / QT;
-    const int nb = n_bnd_wg / (QT * H);
+  if (w < P.n_bnd_wg) {
+    qt = w % P.QT;
+    const int rest = w / P.QT;
+    const int nb = P.n_bnd_wg / (P.QT * P.H);
     const int bi = rest % nb;
     h = rest / nb;
-    t = bi == 0 ? 0 : T - 1;
+    t = bi == 0 ? 0 : P.T - 1;
   } else {
-    const int wp = w - n_bnd_wg;
-    const int x = w & 7;
-    const int L = x * per_xcd + (wp >> 3);
-    if (L >= n_int_wg) return;
-    qt = L % QT;
-    const int rest = L / QT;
-    t = first_int_frame + rest % n_int_frames;
-    h = rest / n_int_frames;
+    const int wp = w - P.n_bnd_wg;
+    const int L = (w & 7) * P.per_xcd + (wp >> 3);
+    if (L >= P.n_int_wg) {
+      if constexpr (!FALLBACK) {
+        if (threadIdx.x == 0) P.flags[w] = 0;
+      }
+      return;
+    }
+    qt = L % P.QT;
+    const int rest = L / P.QT;
+    t = P.first_int_frame + rest % P.n_int_frames;
+    h = rest / P.n_int_frames;
   }
+  const int N = P.N, H = P.H;
+  const int64_t Ls = P.Ls;
+  const float c_log2 = P.c_log2;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -101,6 +129,7 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
 
   // ---- Q fragments (B operand of S^T = K Q^T): query = l32 (+32 qs), d = ks*16 + hl*8 .. +8 ----
   bf16x8 qf[2][KS];
+  float qn2[2] = {0.f, 0.f};
   const int n_base = qt * kBQ + wave * kQW;
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
@@ -108,66 +137,105 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 val = {0, 0, 0, 0};
-      if (n < N) val = *reinterpret_cast<const u32x4*>(q + (((int64_t)t * N + n) * H + h) * D + ks * 16 + hl * 8);
+      if (n < N) val = *reinterpret_cast<const u32x4*>(P.q + (((int64_t)t * N + n) * H + h) * D + ks * 16 + hl * 8);
       qf[qs][ks] = as_bf16x8(val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qn2[qs] += (float)qf[qs][ks][e] * (float)qf[qs][ks][e];
     }
   }
 
-  // ---- key tiles: flatten the range list ----
-  const int nr = nranges[t];
-  int rs[kMaxRanges], re[kMaxRanges], rtiles[kMaxRanges];
-  int ntiles = 0;
+  // ---- exponent reference (fixed path) or running maximum (fallback) ----
+  float mref[2];
+  {
+    const float kmax = P.kmax[h];
+    bool unsafe = false;
 #pragma unroll
-  for (int r = 0; r < kMaxRanges; ++r) {
-    rs[r] = r < nr ? ranges[t * 2 * kMaxRanges + 2 * r] : 0;
-    re[r] = r < nr ? ranges[t * 2 * kMaxRanges + 2 * r + 1] : 0;
-    rtiles[r] = r < nr ? (re[r] - rs[r] + kBK - 1) / kBK : 0;
-    ntiles += rtiles[r];
+    for (int qs = 0; qs < 2; ++qs) {
+      const float qn = sqrtf(qn2[qs] + __shfl_xor(qn2[qs], 32));
+      mref[qs] = qn * kmax * c_log2;
+      unsafe |= !(mref[qs] <= kMaxRef);
+    }
+    if constexpr (!FALLBACK) {
+      if (tid == 0) unsafe_any = 0;
+      __syncthreads();
+      if (__builtin_amdgcn_ballot_w64(unsafe) && lane == 0) atomicOr(&unsafe_any, 1);
+      __syncthreads();
+      const int bad = unsafe_any;
+      if (tid == 0) P.flags[w] = bad;
+      if (bad) return;
+    } else {
+      mref[0] = -INFINITY;
+      mref[1] = -INFINITY;
+    }
   }
+
+  // ---- key tiles (all workgroup-uniform scalars).  Full 64-key tiles of every range come first,
+  // then the partial last tile of each range whose length is not a multiple of 64: the main loop
+  // is then straight-line code and only the short second loop masks keys. ----
+  const int* rg = P.ranges + t * 2 * kMaxRanges;
+  const int nr = uniform(P.nranges[t]);
+  const int rs0 = uniform(rg[0]), rl0 = uniform(rg[1]) - rs0;
+  const int rs1 = nr > 1 ? uniform(rg[2]) : 0, rl1 = nr > 1 ? uniform(rg[3]) - rs1 : 0;
+  const int rs2 = nr > 2 ? uniform(rg[4]) : 0, rl2 = nr > 2 ? uniform(rg[5]) - rs2 : 0;
+  const int rs3 = nr > 3 ? uniform(rg[6]) : 0, rl3 = nr > 3 ? uniform(rg[7]) - rs3 : 0;
+  const int nf0 = rl0 / kBK, nf1 = rl1 / kBK, nf2 = rl2 / kBK, nf3 = rl3 / kBK;
+  const int nfull = nf0 + nf1 + nf2 + nf3;
+  const int pp0 = (rl0 % kBK) != 0, pp1 = (rl1 % kBK) != 0, pp2 = (rl2 % kBK) != 0, pp3 = (rl3 % kBK) != 0;
+  const int ntiles = nfull + pp0 + pp1 + pp2 + pp3;
   auto tile_at = [&](int it, int& key0, int& valid) {
-    int r = 0;
-#pragma unroll
-    for (int rr = 0; rr < kMaxRanges - 1; ++rr)
-      if (r == rr && it >= rtiles[rr]) { it -= rtiles[rr]; r = rr + 1; }
-    int s0 = rs[0], e0 = re[0];
-#pragma unroll
-    for (int rr = 1; rr < kMaxRanges; ++rr)
-      if (r == rr) { s0 = rs[rr]; e0 = re[rr]; }
-    key0 = s0 + it * kBK;
-    valid = min(kBK, e0 - key0);
+    if (it < nfull) {
+      valid = kBK;
+      if (it < nf0) { key0 = rs0 + it * kBK; return; }
+      it -= nf0;
+      if (it < nf1) { key0 = rs1 + it * kBK; return; }
+      it -= nf1;
+      if (it < nf2) { key0 = rs2 + it * kBK; return; }
+      it -= nf2;
+      key0 = rs3 + it * kBK;
+      return;
+    }
+    it -= nfull;                              // it-th range that has a partial tile
+    if (pp0 && it-- == 0) { key0 = rs0 + nf0 * kBK; valid = rl0 - nf0 * kBK; return; }
+    if (pp1 && it-- == 0) { key0 = rs1 + nf1 * kBK; valid = rl1 - nf1 * kBK; return; }
+    if (pp2 && it-- == 0) { key0 = rs2 + nf2 * kBK; valid = rl2 - nf2 * kBK; return; }
+    key0 = rs3 + nf3 * kBK;
+    valid = rl3 - nf3 * kBK;
   };
 
-  const bf16_t* kh = kp + (int64_t)h * Lk * D;
-  const bf16_t* vh = vt + (int64_t)h * D * Lk;
+  const unsigned char* kh = reinterpret_cast<const unsigned char*>(P.kp + (int64_t)h * Ls * D);
+  const unsigned char* vh = reinterpret_cast<const unsigned char*>(P.vt + (int64_t)h * D * Ls);
 
   // Direct global -> LDS tile loads (global_load_lds_dwordx4): one instruction of a wave fills 1 KB
   // of LDS, lane l writing bytes [16 l, 16 l + 16).  Each lane therefore fetches the global chunk
-  // whose swizzled LDS position is its own.  Keys past the key space are clamped to its last
-  // chunk (finite data; such keys are masked).
-  constexpr int K_INSTR = Smem<D>::K_BYTES / 1024 / kWaves;     // per wave
-  constexpr int V_INSTR = Smem<D>::V_BYTES / 1024 / kWaves;
+  // whose swizzled LDS position is its own: a workgroup-uniform tile base plus a fixed 32-bit lane
+  // offset.  The packed key space ends with a zero tile, so no load leaves the buffer.
+  constexpr int K_INSTR = SM::K_BYTES / 1024 / kWaves;     // per wave
+  constexpr int V_INSTR = SM::V_BYTES / 1024 / kWaves;
   constexpr int K_ROWS_PER_KB = 1024 / (D * 2);
+  uint32_t koff[K_INSTR], voff[V_INSTR];
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) {
+    const int row = (i * kWaves + wave) * K_ROWS_PER_KB + lane / SM::KCH;
+    const int c = (lane % SM::KCH) ^ k_swz<D>(row);
+    koff[i] = (uint32_t)(row * D + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) {
+    const int row = (i * kWaves + wave) * 8 + lane / 8;
+    const int c = (lane % 8) ^ v_swz(row);
+    voff[i] = (uint32_t)((int64_t)row * Ls + c * 8) * 2u;
+  }
   auto issue_tile = [&](int key0, int stage) {
     unsigned char* kb = smem + stage * SM::STAGE;
     unsigned char* vb = kb + SM::K_BYTES;
+    const unsigned char* kt0 = kh + (int64_t)key0 * D * 2;
+    const unsigned char* vt0 = vh + (int64_t)key0 * 2;
 #pragma unroll
-    for (int i = 0; i < K_INSTR; ++i) {
-      const int blk = i * kWaves + wave;
-      const int row = blk * K_ROWS_PER_KB + lane / SM::KCH;
-      const int c = (lane % SM::KCH) ^ k_swz<D>(row);
-      int64_t j = key0 + row;
-      j = j < Lk ? j : Lk - 1;
-      __builtin_amdgcn_global_load_lds((gptr_t)(kh + j * D + c * 8), (lptr_t)(kb + blk * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < K_INSTR; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(kt0 + koff[i]), (lptr_t)(kb + (i * kWaves + wave) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < V_INSTR; ++i) {
-      const int blk = i * kWaves + wave;
-      const int row = blk * 8 + lane / 8;
-      const int c = (lane % 8) ^ v_swz(row);
-      int64_t j = key0 + c * 8;
-      j = j + 8 <= Lk ? j : Lk - 8;
-      __builtin_amdgcn_global_load_lds((gptr_t)(vh + (int64_t)row * Lk + j), (lptr_t)(vb + blk * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < V_INSTR; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(vt0 + voff[i]), (lptr_t)(vb + (i * kWaves + wave) * 1024), 16, 0, 0);
   };
 
   f32x16 oacc[2][DT];
@@ -177,11 +245,90 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[qs][dt][i] = 0.f;
-  float mref[2] = {-INFINITY, -INFINITY};
   float lsum[2] = {0.f, 0.f};
 
   // row of the K tile that this lane feeds as MFMA row l32 (see header): key 16*h + 4*a + b
   const int krow = ((l32 >> 2) & 1) * 16 + (l32 >> 3) * 4 + (l32 & 3);
+
+  // S^T for one 32-key half: 2 query subtiles
+  auto scores = [&](const unsigned char* kb, int kt, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[qs][i] = 0.f;
+    const int row = kt * 32 + krow;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 2 + hl;
+      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)));
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+        sacc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qs][ks], sacc[qs], 0, 0, 0);
+    }
+  };
+  auto mask = [&](int kt, int valid, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kl = kt * 32 + hl * 16 + i;
+      if (kl >= valid) { sacc[0][i] = kMasked; sacc[1][i] = kMasked; }
+    }
+  };
+  // running maximum with lazy rescale (fallback kernel only)
+  auto online_max = [&](f32x16 (&sacc)[2]) {
+    float mxc[2];
+    bool need = false;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float mx = sacc[qs][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qs][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mxc[qs] = mx * c_log2;
+      need |= mxc[qs] > mref[qs] + kRescaleThreshold;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float mnew = fmaxf(mref[qs], mxc[qs]);
+        const float alpha = exp2f(mref[qs] - mnew);
+        mref[qs] = mnew;
+        lsum[qs] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[qs][dt][i] *= alpha;
+      }
+    }
+  };
+  auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pf)[2][2]) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // raw v_exp_f32: results below 2^-126 flush to zero, harmless since the largest term of
+        // every query is >= 2^-96 (fixed reference) or 1 (online maximum)
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c_log2, -mref[qs]));
+        ls += p;
+        pf[qs][i >> 3][i & 7] = (__bf16)p;
+      }
+      lsum[qs] += ls;
+    }
+  };
+  auto accumulate = [&](const unsigned char* vb, int kt, const bf16x8 (&pf)[2][2]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int vrow = dt * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = kt * 4 + hl * 2 + s;
+        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + vrow * (kBK * 2) + ((c ^ v_swz(vrow)) * 16)));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          oacc[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qs][s], oacc[qs][dt], 0, 0, 0);
+      }
+    }
+  };
 
   {
     int key0, valid;
@@ -191,97 +338,71 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int stage = it & 1;
-    int key0, valid;
-    tile_at(it, key0, valid);
+  auto next_tile = [&](int it) {
     if (it + 1 < ntiles) {
       int nkey0, nvalid;
       tile_at(it + 1, nkey0, nvalid);
-      issue_tile(nkey0, stage ^ 1);
+      issue_tile(nkey0, (it + 1) & 1);
     }
-    const unsigned char* kb = smem + stage * SM::STAGE;
-    const unsigned char* vb = kb + SM::K_BYTES;
+  };
 
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {       // two 32-key halves of the tile
-      // ---- S^T = K Q^T for 32 keys x 64 queries ----
-      f32x16 sacc[2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[qs][i] = 0.f;
-      const int row = kt * 32 + krow;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int c = ks * 2 + hl;
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)));
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-          sacc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qs][ks], sacc[qs], 0, 0, 0);
-      }
-      // ---- mask the tail of a partial tile ----
-      if (valid < kBK) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = kt * 32 + hl * 16 + i;
-          if (kl >= valid) { sacc[0][i] = kMasked; sacc[1][i] = kMasked; }
-        }
-      }
-      // ---- online softmax: this lane holds 16 keys of 2 queries; the other 16 are in lane ^ 32 ----
-      float mxc[2];
-      bool need = false;
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float mx = sacc[qs][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qs][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mxc[qs] = mx * c_log2;
-        need |= mxc[qs] > mref[qs] + kRescaleThreshold;
-      }
-      if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          const float mnew = fmaxf(mref[qs], mxc[qs]);
-          const float alpha = exp2f(mref[qs] - mnew);
-          mref[qs] = mnew;
-          lsum[qs] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[qs][dt][i] *= alpha;
-        }
-      }
-      bf16x8 pf[2][2];     // [qs][k-step]
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float ls = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(fmaf(sacc[qs][i], c_log2, -mref[qs]));
-          ls += p;
-          pf[qs][i >> 3][i & 7] = (__bf16)p;
-        }
-        lsum[qs] += ls;
-      }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int vrow = dt * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int c = kt * 4 + hl * 2 + s;
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + vrow * (kBK * 2) + ((c ^ v_swz(vrow)) * 16)));
-#pragma unroll
-          for (int qs = 0; qs < 2; ++qs)
-            oacc[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qs][s], oacc[qs][dt], 0, 0, 0);
-        }
-      }
+  if constexpr (!FALLBACK) {
+    // full tiles: straight-line body; the second half's scores can overlap the first half's
+    // exponentials
+    for (int it = 0; it < nfull; ++it) {
+      next_tile(it);
+      const unsigned char* kb = smem + (it & 1) * SM::STAGE;
+      const unsigned char* vb = kb + SM::K_BYTES;
+      f32x16 s0[2], s1[2];
+      bf16x8 p0[2][2], p1[2][2];
+      scores(kb, 0, s0);
+      scores(kb, 1, s1);
+      probs(s0, p0);
+      accumulate(vb, 0, p0);
+      probs(s1, p1);
+      accumulate(vb, 1, p1);
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      __syncthreads();
     }
-
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
+    // partial tiles (at most one per range)
+    for (int it = nfull; it < ntiles; ++it) {
+      next_tile(it);
+      int key0, valid;
+      tile_at(it, key0, valid);
+      const unsigned char* kb = smem + (it & 1) * SM::STAGE;
+      const unsigned char* vb = kb + SM::K_BYTES;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 sacc[2];
+        bf16x8 pf[2][2];
+        scores(kb, kt, sacc);
+        mask(kt, valid, sacc);
+        probs(sacc, pf);
+        accumulate(vb, kt, pf);
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      __syncthreads();
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) {
+      next_tile(it);
+      int key0, valid;
+      tile_at(it, key0, valid);
+      const unsigned char* kb = smem + (it & 1) * SM::STAGE;
+      const unsigned char* vb = kb + SM::K_BYTES;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 sacc[2];
+        bf16x8 pf[2][2];
+        scores(kb, kt, sacc);
+        if (valid < kBK) mask(kt, valid, sacc);
+        online_max(sacc);
+        probs(sacc, pf);
+        accumulate(vb, kt, pf);
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      __syncthreads();
+    }
   }
 
   // ---- normalise and store o_s (bf16) ----
@@ -291,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
     const float inv = 1.0f / tot;
     const int n = n_base + qs * 32 + l32;
     if (n < N) {
-      bf16_t* op = o_s + (((int64_t)t * N + n) * H + h) * D;
+      bf16_t* op = P.o_s + (((int64_t)t * N + n) * H + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -307,34 +428,51 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(
 
 template <int D>
 void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
-  const int QT = (s.N + kBQ - 1) / kBQ;
+  Params P{};
+  P.q = (const bf16_t*)in.q;
+  P.kp = b.kp;
+  P.vt = b.vt;
+  P.o_s = (bf16_t*)b.os;
+  P.ranges = b.ranges;
+  P.nranges = b.nranges;
+  P.kmax = b.kmax;
+  P.flags = b.flags;
+  P.T = s.T;
+  P.N = s.N;
+  P.H = s.H;
+  P.Ls = s.Ls;
+  P.QT = (s.N + kBQ - 1) / kBQ;
   const bool two_bnd = s.anchors && s.T > 1;
   const int nb = s.anchors ? (two_bnd ? 2 : 1) : 0;
-  const int n_int_frames = s.T - nb;
-  const int first_int = s.anchors ? 1 : 0;
-  const int n_bnd_wg = nb * QT * s.H;
-  const int n_int_wg = n_int_frames * QT * s.H;
-  const int per_xcd = (n_int_wg + 7) / 8;
-  const int grid = n_bnd_wg + 8 * per_xcd;
+  P.n_int_frames = s.T - nb;
+  P.first_int_frame = s.anchors ? 1 : 0;
+  P.n_bnd_wg = nb * P.QT * s.H;
+  P.n_int_wg = P.n_int_frames * P.QT * s.H;
+  P.per_xcd = (P.n_int_wg + 7) / 8;
+  P.c_log2 = 1.4426950408889634f / sqrtf((float)D);
+  const int grid = softmax_grid(s);
   const size_t smem = 2 * Smem<D>::STAGE;
-  const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(softmax_mfma_kernel<D>, dim3(grid), dim3(256), smem, st, (const bf16_t*)in.q, b.kp, b.vt,
-                     (bf16_t*)b.os, b.ranges, b.nranges, s.T, s.N, s.H, s.Lk, QT, n_bnd_wg, n_int_frames, first_int,
-                     per_xcd, n_int_wg, c_log2);
+  (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+  (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+  hipLaunchKernelGGL((softmax_mfma_kernel<D, false>), dim3(grid), dim3(256), smem, st, P);
+  hipLaunchKernelGGL((softmax_mfma_kernel<D, true>), dim3(grid), dim3(256), smem, st, P);
 }
 
 }  // namespace
 
+int softmax_grid(const Shape& s) {
+  const int QT = (s.N + kBQ - 1) / kBQ;
+  const int nb = s.anchors ? (s.T > 1 ? 2 : 1) : 0;
+  const int n_bnd_wg = nb * QT * s.H;
+  const int n_int_wg = (s.T - nb) * QT * s.H;
+  return n_bnd_wg + 8 * ((n_int_wg + 7) / 8);
+}
+
 hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
-  if (s.d == 128) {
-    (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              2 * Smem<128>::STAGE);
-    launch_t<128>(s, in, b, st);
-  } else {
-    (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              2 * Smem<64>::STAGE);
-    launch_t<64>(s, in, b, st);
-  }
+  if (s.d == 128) launch_t<128>(s, in, b, st);
+  else launch_t<64>(s, in, b, st);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct Shape {
   int Nc;            // number of chunks
   int text_pad;      // n_text rounded up to kTextPad
   int64_t Lk;        // key-space length per head: text_pad + T*N
+  int64_t Ls;        // allocated key stride of the packed K/V: Lk + one zero tile of padding
 };
 
 // Key ranges of query frame t in a head's key space (see vdn_key_ranges); returns the count.
@@ -33,15 +34,19 @@ bool is_boundary(const Shape& s, int t);
 // Device workspace layout (byte offsets from the workspace base).
 struct Layout {
   size_t os;        // o_s [T*N][H][d] plan dtype
-  size_t kp;        // packed keys  [H][Lk][d] bf16          (MFMA softmax path only)
-  size_t vt;        // packed values, transposed [H][d][Lk] bf16
+  size_t kp;        // packed keys  [H][Ls][d] bf16          (MFMA softmax path only)
+  size_t vt;        // packed values, transposed [H][d][Ls] bf16
   size_t minv;      // M = (I+A)^-1  [T+1][H][d][d] f32
   size_t bw;        // B             [T+1][H][d][d] f32
   size_t states;    // S_fwd, S_rev  [2][Nc+1][H][d][d] f32
+  size_t wt;        // transposed weights [4][d][d] bf16: Wg0^T, Wg1^T, Wp0^T, Wp1^T (MFMA epilogue)
+  size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
+  size_t kmax;      // largest key norm per head [H] f32
+  size_t flags;     // per-workgroup fallback flags of the MFMA softmax [softmax_grid] int32
   size_t ranges;    // int32 [T][2*kMaxRanges] + int32 [T] counts
   size_t total;
 };
-Layout make_layout(const Shape& s, bool mfma_softmax);
+Layout make_layout(const Shape& s, bool mfma_softmax, bool mfma_epilogue);
 
 // Kernel selection per stage.
 struct Kinds {
@@ -59,6 +64,10 @@ struct Buffers {
   float* minv;
   float* bw;
   float* states;
+  uint16_t* wt;
+  float* kmax_part;
+  float* kmax;
+  int* flags;
   const int* ranges;   // [T][2*kMaxRanges]
   const int* nranges;  // [T]
 };
@@ -71,6 +80,9 @@ struct Inputs {
   void* out;
 };
 
+// Number of workgroups of the MFMA softmax launch.
+int softmax_grid(const Shape& s);
+
 // Launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
@@ -78,5 +90,7 @@ hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& 
 hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_vda_scan(const Shape& s, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
+hipError_t launch_prep_weights(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 
 }  // namespace vdn
