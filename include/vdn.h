@@ -116,8 +116,9 @@ int vdn_scan_frames(int T, int C, int anchors, int t, int dir, int *frames, int 
  *   VDN_BUF_STATES S_fwd, S_rev: [2][Nc+1][H][d][d] float32; slot Nc holds S0 (boundary frames)
  *   VDN_BUF_MINV   M_f = (I + A_f)^-1: [T+1][H][d][d] float32, slot 0 for the text (beta/2),
  *                  slot 1+f for frame f (boundary frames' slots are not written when anchors on)
+ *   VDN_BUF_BW     B_f = sum_u beta_u v_u k_u^T: [T+1][H][d][d] float32, same slots as VDN_BUF_MINV
  */
-enum { VDN_BUF_OS = 0, VDN_BUF_STATES = 1, VDN_BUF_MINV = 2 };
+enum { VDN_BUF_OS = 0, VDN_BUF_STATES = 1, VDN_BUF_MINV = 2, VDN_BUF_BW = 3 };
 vdn_status vdn_debug_buffer_bytes(const vdn_plan *plan, int which, size_t *bytes);
 vdn_status vdn_debug_copy(const vdn_plan *plan, int which, void *dst, size_t bytes, void *stream);
 

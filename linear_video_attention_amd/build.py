@@ -23,6 +23,8 @@ SOURCES = [
     "softmax_simt.hip",
     "softmax_mfma.hip",
     "vda.hip",
+    "vda_stats_mfma.hip",
+    "vda_scan_mfma.hip",
     "epilogue_simt.hip",
     "epilogue_mfma.hip",
 ]
@@ -43,9 +45,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, out_dir: str, extra: list) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-x", "hip", *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,19 +56,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, lib_path: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile every source and link ``lib_path`` (default: the in-tree libvdn.so)."""
+    out_dir = OUT_DIR if lib_path == LIB_PATH else lib_path + ".objs"
+    os.makedirs(out_dir, exist_ok=True)
+    extra = list(extra_flags)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, out_dir, extra), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -205,7 +205,7 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, plan->side));
   mark(VDN_STAGE_VDA_STATS, 1, plan->side);
   mark(VDN_STAGE_VDA_SCAN, 0, plan->side);
-  VDN_TRY(vdn::launch_vda_scan(s, b, plan->side));
+  VDN_TRY(vdn::launch_vda_scan(s, b, plan->kinds.scan_mfma, plan->side));
   mark(VDN_STAGE_VDA_SCAN, 1, plan->side);
   VDN_TRY(hipEventRecord(plan->ev_join, plan->side));
   // softmax branch on the caller's stream
@@ -236,6 +236,7 @@ vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes
     case VDN_BUF_OS: *bytes = (size_t)s.T * s.N * s.H * s.d * (s.dtype == VDN_BF16 ? 2 : 4); break;
     case VDN_BUF_STATES: *bytes = (size_t)2 * (s.Nc + 1) * s.H * dd * 4; break;
     case VDN_BUF_MINV: *bytes = (size_t)(s.T + 1) * s.H * dd * 4; break;
+    case VDN_BUF_BW: *bytes = (size_t)(s.T + 1) * s.H * dd * 4; break;
     default: return VDN_ERR_INVALID_ARG;
   }
   return VDN_OK;
@@ -246,7 +247,10 @@ vdn_status vdn_debug_copy(const vdn_plan* plan, int which, void* dst, size_t byt
   vdn_status st = vdn_debug_buffer_bytes(plan, which, &want);
   if (st != VDN_OK) return st;
   if (!dst || bytes != want) return VDN_ERR_INVALID_ARG;
-  size_t off = which == VDN_BUF_OS ? plan->lay.os : which == VDN_BUF_STATES ? plan->lay.states : plan->lay.minv;
+  size_t off = which == VDN_BUF_OS ? plan->lay.os
+               : which == VDN_BUF_STATES ? plan->lay.states
+               : which == VDN_BUF_MINV ? plan->lay.minv
+                                       : plan->lay.bw;
   if (hipMemcpyAsync(dst, plan->ws + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipGetLastError();
     return VDN_ERR_HIP;

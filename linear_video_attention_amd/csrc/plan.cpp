@@ -77,8 +77,8 @@ Kinds choose_kinds(const Shape& s) {
   const bool bf16 = s.dtype == VDN_BF16;
   // lane offsets into one head's packed V^T are 32-bit: d * Ls * 2 bytes must stay below 2^31
   k.softmax_mfma = bf16 && (s.d == 64 || s.d == 128) && s.N % 8 == 0 && (int64_t)s.d * s.Ls * 2 < (int64_t(1) << 31);
-  k.stats_mfma = false;
-  k.scan_mfma = false;
+  k.stats_mfma = bf16 && (s.d == 64 || s.d == 128);
+  k.scan_mfma = bf16 && (s.d == 64 || s.d == 128);
   k.epilogue_mfma = bf16 && (s.d == 64 || s.d == 128);
   return k;
 }

@@ -7,7 +7,10 @@
 // key space (built on the host), so the kernel is a flash-style attention over a range list.
 //
 // Work decomposition
-//   * one workgroup = 256 queries of one frame and one head; 4 waves x 64 queries;
+//   * one workgroup = 256 queries of one frame and one head; 8 waves x 32 queries, two waves per
+//     SIMD so one wave's exponentials overlap the other's MFMAs (measured faster on gfx950 than
+//     4 waves x 64 queries at one wave per SIMD, which halves the LDS reads per MFMA but leaves
+//     every LDS and MFMA latency exposed);
 //   * key tiles of 64 keys are loaded straight from global memory into LDS (global_load_lds,
 //     double buffered; K as [key][d], V transposed as [d][key], both XOR-swizzled so the 16-byte
 //     fragment reads are bank-conflict free) and processed as two 32-key halves;
@@ -38,9 +41,14 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kBK = 64;        // keys per tile
-constexpr int kWaves = 4;
-constexpr int kQW = 64;        // queries per wave
-constexpr int kBQ = kWaves * kQW;
+constexpr int kBQ = 256;       // queries per workgroup
+// Wave shape: QSUB 32-query column tiles per wave, kBQ / (32 QSUB) waves per workgroup.
+#ifndef VDN_SOFTMAX_QSUB
+#define VDN_SOFTMAX_QSUB 1
+#endif
+constexpr int kQSub = VDN_SOFTMAX_QSUB;
+constexpr int kWaves = kBQ / (32 * kQSub);
+constexpr int kQW = 32 * kQSub;        // queries per wave
 constexpr float kMaxRef = 48.0f;            // log2 units; beyond it the fallback kernel runs
 constexpr float kRescaleThreshold = 8.0f;   // fallback: log2 units of growth before a rescale
 constexpr float kMasked = -1.0e30f;
@@ -85,7 +93,7 @@ struct Params {
 // FALLBACK = false: fixed exponent reference, writes its workgroup's flag (1 = redo).
 // FALLBACK = true : online maximum; runs only the workgroups flagged by the first launch.
 template <int D, bool FALLBACK>
-__global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
+__global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) {
   using SM = Smem<D>;
   constexpr int KS = D / 16;          // k-steps of the QK^T contraction
   constexpr int DT = D / 32;          // 32-row d tiles of O^T
@@ -128,11 +136,13 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
   const int l32 = lane & 31, hl = lane >> 5;
 
   // ---- Q fragments (B operand of S^T = K Q^T): query = l32 (+32 qs), d = ks*16 + hl*8 .. +8 ----
-  bf16x8 qf[2][KS];
-  float qn2[2] = {0.f, 0.f};
+  bf16x8 qf[kQSub][KS];
+  float qn2[kQSub];
+#pragma unroll
+  for (int qs = 0; qs < kQSub; ++qs) qn2[qs] = 0.f;
   const int n_base = qt * kBQ + wave * kQW;
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < kQSub; ++qs) {
     const int n = n_base + qs * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -145,12 +155,12 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
   }
 
   // ---- exponent reference (fixed path) or running maximum (fallback) ----
-  float mref[2];
+  float mref[kQSub];
   {
     const float kmax = P.kmax[h];
     bool unsafe = false;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < kQSub; ++qs) {
       const float qn = sqrtf(qn2[qs] + __shfl_xor(qn2[qs], 32));
       mref[qs] = qn * kmax * c_log2;
       unsafe |= !(mref[qs] <= kMaxRef);
@@ -164,8 +174,8 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       if (tid == 0) P.flags[w] = bad;
       if (bad) return;
     } else {
-      mref[0] = -INFINITY;
-      mref[1] = -INFINITY;
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs) mref[qs] = -INFINITY;
     }
   }
 
@@ -238,47 +248,56 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       __builtin_amdgcn_global_load_lds((gptr_t)(vt0 + voff[i]), (lptr_t)(vb + (i * kWaves + wave) * 1024), 16, 0, 0);
   };
 
-  f32x16 oacc[2][DT];
+  f32x16 oacc[kQSub][DT];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+  for (int qs = 0; qs < kQSub; ++qs)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[qs][dt][i] = 0.f;
-  float lsum[2] = {0.f, 0.f};
+  float lsum[kQSub];
+#pragma unroll
+  for (int qs = 0; qs < kQSub; ++qs) lsum[qs] = 0.f;
 
   // row of the K tile that this lane feeds as MFMA row l32 (see header): key 16*h + 4*a + b
   const int krow = ((l32 >> 2) & 1) * 16 + (l32 >> 3) * 4 + (l32 & 3);
 
-  // S^T for one 32-key half: 2 query subtiles
-  auto scores = [&](const unsigned char* kb, int kt, f32x16 (&sacc)[2]) {
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[qs][i] = 0.f;
+  // S^T for one 32-key half: 2 query subtiles.  All K fragments of the half are read before the
+  // first MFMA so the LDS latency is paid once per half, not once per fragment.
+  auto scores = [&](const unsigned char* kb, int kt, f32x16 (&sacc)[kQSub]) {
     const int row = kt * 32 + krow;
+    bf16x8 kf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = ks * 2 + hl;
-      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)));
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-        sacc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qs][ks], sacc[qs], 0, 0, 0);
+      kf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)));
     }
+#pragma unroll
+    for (int qs = 0; qs < kQSub; ++qs)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[qs][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs)
+        sacc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qs][ks], sacc[qs], 0, 0, 0);
   };
-  auto mask = [&](int kt, int valid, f32x16 (&sacc)[2]) {
+  auto mask = [&](int kt, int valid, f32x16 (&sacc)[kQSub]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kl = kt * 32 + hl * 16 + i;
-      if (kl >= valid) { sacc[0][i] = kMasked; sacc[1][i] = kMasked; }
+      if (kl >= valid) {
+#pragma unroll
+        for (int qs = 0; qs < kQSub; ++qs) sacc[qs][i] = kMasked;
+      }
     }
   };
   // running maximum with lazy rescale (fallback kernel only)
-  auto online_max = [&](f32x16 (&sacc)[2]) {
-    float mxc[2];
+  auto online_max = [&](f32x16 (&sacc)[kQSub]) {
+    float mxc[kQSub];
     bool need = false;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < kQSub; ++qs) {
       float mx = sacc[qs][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qs][i]);
@@ -288,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
     }
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
+      for (int qs = 0; qs < kQSub; ++qs) {
         const float mnew = fmaxf(mref[qs], mxc[qs]);
         const float alpha = exp2f(mref[qs] - mnew);
         mref[qs] = mnew;
@@ -300,9 +319,9 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       }
     }
   };
-  auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pf)[2][2]) {
+  auto probs = [&](const f32x16 (&sacc)[kQSub], bf16x8 (&pf)[kQSub][2]) {
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < kQSub; ++qs) {
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -315,19 +334,24 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       lsum[qs] += ls;
     }
   };
-  auto accumulate = [&](const unsigned char* vb, int kt, const bf16x8 (&pf)[2][2]) {
+  auto accumulate = [&](const unsigned char* vb, int kt, const bf16x8 (&pf)[kQSub][2]) {
+    bf16x8 vf[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int vrow = dt * 32 + l32;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int c = kt * 4 + hl * 2 + s;
-        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + vrow * (kBK * 2) + ((c ^ v_swz(vrow)) * 16)));
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-          oacc[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qs][s], oacc[qs][dt], 0, 0, 0);
+        vf[dt][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + vrow * (kBK * 2) + ((c ^ v_swz(vrow)) * 16)));
       }
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int qs = 0; qs < kQSub; ++qs)
+          oacc[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][s], pf[qs][s], oacc[qs][dt], 0, 0, 0);
   };
 
   {
@@ -353,8 +377,8 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       next_tile(it);
       const unsigned char* kb = smem + (it & 1) * SM::STAGE;
       const unsigned char* vb = kb + SM::K_BYTES;
-      f32x16 s0[2], s1[2];
-      bf16x8 p0[2][2], p1[2][2];
+      f32x16 s0[kQSub], s1[kQSub];
+      bf16x8 p0[kQSub][2], p1[kQSub][2];
       scores(kb, 0, s0);
       scores(kb, 1, s1);
       probs(s0, p0);
@@ -373,8 +397,8 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       const unsigned char* vb = kb + SM::K_BYTES;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc[2];
-        bf16x8 pf[2][2];
+        f32x16 sacc[kQSub];
+        bf16x8 pf[kQSub][2];
         scores(kb, kt, sacc);
         mask(kt, valid, sacc);
         probs(sacc, pf);
@@ -392,8 +416,8 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
       const unsigned char* vb = kb + SM::K_BYTES;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc[2];
-        bf16x8 pf[2][2];
+        f32x16 sacc[kQSub];
+        bf16x8 pf[kQSub][2];
         scores(kb, kt, sacc);
         if (valid < kBK) mask(kt, valid, sacc);
         online_max(sacc);
@@ -407,7 +431,7 @@ __global__ __launch_bounds__(256, 1) void softmax_mfma_kernel(Params P) {
 
   // ---- normalise and store o_s (bf16) ----
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < kQSub; ++qs) {
     const float tot = lsum[qs] + __shfl_xor(lsum[qs], 32);
     const float inv = 1.0f / tot;
     const int n = n_base + qs * 32 + l32;
@@ -456,8 +480,8 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
                             (int)smem);
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
-  hipLaunchKernelGGL((softmax_mfma_kernel<D, false>), dim3(grid), dim3(256), smem, st, P);
-  hipLaunchKernelGGL((softmax_mfma_kernel<D, true>), dim3(grid), dim3(256), smem, st, P);
+  hipLaunchKernelGGL((softmax_mfma_kernel<D, false>), dim3(grid), dim3(kWaves * 64), smem, st, P);
+  hipLaunchKernelGGL((softmax_mfma_kernel<D, true>), dim3(grid), dim3(kWaves * 64), smem, st, P);
 }
 
 }  // namespace

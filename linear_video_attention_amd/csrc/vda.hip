@@ -18,53 +18,13 @@
 // direction) and walks the frames in order, x = s + B_f, s = x M_f, storing the state at every
 // chunk boundary.  Slot Nc of each direction holds S0, read by boundary query frames.
 #include "dev_common.h"
+#include "vda_common.h"
 #include "vdn_internal.h"
 
 namespace vdn {
 namespace {
 
 constexpr int kTileU = 32;   // tokens staged per iteration
-
-// Gauss-Jordan in-place inverse of the D x D matrix held as R x R register blocks by a 16 x 16
-// thread grid (thread (ty, tx) owns rows ty*R.., cols tx*R..).  rowbuf/colbuf: [2][D] shared.
-template <int D>
-__device__ __forceinline__ void gauss_jordan_inverse(float (&a)[D / 16][D / 16], float* rowbuf, float* colbuf,
-                                                     int ty, int tx) {
-  constexpr int R = D / 16;
-  for (int p = 0; p < D; ++p) {
-    float* rb = rowbuf + (p & 1) * D;
-    float* cb = colbuf + (p & 1) * D;
-    const int pb = p / R, pr = p % R;
-    if (ty == pb) {
-#pragma unroll
-      for (int jj = 0; jj < R; ++jj) rb[tx * R + jj] = a[pr][jj];
-    }
-    if (tx == pb) {
-#pragma unroll
-      for (int ii = 0; ii < R; ++ii) cb[ty * R + ii] = a[ii][pr];
-    }
-    __syncthreads();
-    const float inv = 1.0f / rb[p];
-    float rj[R], fi[R];
-#pragma unroll
-    for (int jj = 0; jj < R; ++jj) {
-      const int j = tx * R + jj;
-      rj[jj] = (j == p) ? inv : rb[j] * inv;
-    }
-#pragma unroll
-    for (int ii = 0; ii < R; ++ii) fi[ii] = cb[ty * R + ii];
-#pragma unroll
-    for (int ii = 0; ii < R; ++ii) {
-      const int i = ty * R + ii;
-#pragma unroll
-      for (int jj = 0; jj < R; ++jj) {
-        const int j = tx * R + jj;
-        if (i == p) a[ii][jj] = rj[jj];
-        else a[ii][jj] = ((j == p) ? 0.f : a[ii][jj]) - fi[ii] * rj[jj];
-      }
-    }
-  }
-}
 
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) void vda_stats_simt_kernel(
@@ -251,13 +211,15 @@ void scan_t(const Shape& s, const Buffers& b, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool /*mfma*/, hipStream_t st) {
+hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st) {
+  if (mfma) return launch_vda_stats_mfma(s, in, b, st);
   if (s.dtype == VDN_BF16) stats_d<bf16_t>(s, in, b, st);
   else stats_d<float>(s, in, b, st);
   return hipGetLastError();
 }
 
-hipError_t launch_vda_scan(const Shape& s, const Buffers& b, hipStream_t st) {
+hipError_t launch_vda_scan(const Shape& s, const Buffers& b, bool mfma, hipStream_t st) {
+  if (mfma) return launch_vda_scan_mfma(s, b, st);
   switch (s.d) {
     case 16: scan_t<16>(s, b, st); break;
     case 32: scan_t<32>(s, b, st); break;

@@ -88,7 +88,9 @@ hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hi
 hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
-hipError_t launch_vda_scan(const Shape& s, const Buffers& b, hipStream_t st);
+hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_vda_scan(const Shape& s, const Buffers& b, bool mfma, hipStream_t st);
+hipError_t launch_vda_scan_mfma(const Shape& s, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_prep_weights(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);

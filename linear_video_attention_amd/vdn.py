@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libvdn.so")
 VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_OUT_OF_MEMORY, VDN_ERR_HIP = 0, -1, -2, -3, -4
 VDN_F32, VDN_BF16 = 0, 1
 VDN_FLAG_GENERIC_KERNELS = 1
-VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV = 0, 1, 2
+VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV, VDN_BUF_BW = 0, 1, 2, 3
 STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total")
 
 # every symbol include/vdn.h declares: (name, restype, argtypes)

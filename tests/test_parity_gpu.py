@@ -142,14 +142,21 @@ def test_forward_argument_errors():
     plan.close()
 
 
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place of |x| (8 significant bits)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 1e-30)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
 def test_softmax_fallback_for_large_scores():
     """Queries scaled far beyond unit norm make the fixed exponent reference unsafe; those
     workgroups must be redone by the online-maximum kernel and still match the oracle.
 
-    The softmax is then nearly one-hot, so o_s is close to single value rows (max |o_s| ~ 4 RMS)
-    and storing o_s in bf16 alone costs up to 2^-8 * 4 RMS = 1.6e-2 RMS; the comparison is made
-    against the oracle's o_s rounded to bf16, which leaves the kernel's own error (bf16 P, fp32
-    sums) against the 2e-2 RMS bar."""
+    The softmax is then nearly one-hot: o_s is close to single value rows, max|o_s| / RMS ~ 7.6,
+    so rounding the stored o_s to bf16 alone moves an element by up to 2^-8 |o_s| ~ 2.8e-2 RMS.
+    The bar is therefore applied to the error beyond that half-ulp storage rounding of each
+    element: max(|gpu - oracle| - half_ulp_bf16(oracle)) <= 2e-2 RMS."""
     import torch as _t
     w = synth.custom(8, 6, 256, 2, 2, 128, "bf16", "sigmoid", True)
     inp = synth.make_inputs(w, seed=4)
@@ -158,9 +165,9 @@ def test_softmax_fallback_for_large_scores():
     dev = to_device(inp, w.dtype)
     run_layer(plan, dev)
     ref = orc.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], w.T, w.N, w.C, w.anchors)
-    ref_b = _t.from_numpy(ref).to(_t.bfloat16).float().numpy()
-    e = rel_err(softmax_out(plan), ref_b)
-    print(f"fallback o_s err vs bf16-rounded oracle {e:.2e} (vs unrounded {rel_err(softmax_out(plan), ref):.2e})",
-          flush=True)
-    assert e <= TOL["bf16"]
+    got = softmax_out(plan).astype(np.float64)
+    rms = np.sqrt(np.mean(ref.astype(np.float64) ** 2))
+    excess = np.max(np.abs(got - ref) - bf16_half_ulp(ref)) / rms
+    print(f"fallback o_s: plain err {rel_err(got, ref):.2e}, beyond bf16 storage rounding {excess:.2e}", flush=True)
+    assert excess <= TOL["bf16"]
     plan.close()
