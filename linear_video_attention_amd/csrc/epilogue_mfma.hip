@@ -13,10 +13,11 @@
 //     channels [16w, 16w + 16) and holds rows [16w, 16w+16) of S (as bf16 hi + lo parts, so the
 //     readout keeps ~16 mantissa bits) and of Wg0^T, Wg1^T, Wp0^T, Wp1^T (pre-transposed once per
 //     forward by prep_weights_kernel);
-//   * tokens stream through LDS in tiles of 32: q^T is the shared B operand of the readout and of
-//     both gates; the per-token RMS needs all channels, so each wave's partial sum of squares is
-//     exchanged through LDS; the gated branches x_s, x_l are exchanged through LDS as the B
-//     operand of the two projections.
+//   * tokens stream through LDS in tiles of 64 whose global operands (q, the o_s slice) are fetched
+//     two tiles ahead: q^T is the shared B operand of the readout and of both gates; the per-token
+//     RMS needs all channels, so each wave's partial sum of squares is exchanged through LDS; the
+//     gated branches x_s, x_l are exchanged through LDS, as bf16 hi + lo parts, as the B operand
+//     of the two projections.
 #include "dev_common.h"
 #include "vdn_internal.h"
 
@@ -27,7 +28,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int kTileTok = 32;
+constexpr int kTileTok = 64;
 constexpr int kTokPerWG = 512;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -53,8 +54,10 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
   constexpr int KS = D / 32;              // k-steps of 32
   constexpr int NT = kTileTok / 16;       // 16-token column tiles per tile
   constexpr int NTHR = NW * 64;
+  constexpr int QCH = kTileTok * D / 8;   // 16-byte chunks of a q tile
+  constexpr int QPT = (QCH + NTHR - 1) / NTHR;
   __shared__ __attribute__((aligned(16))) bf16_t qtile[kTileTok][D + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t xtile[2][kTileTok][D + 8];
+  __shared__ __attribute__((aligned(16))) bf16_t xtile[4][kTileTok][D + 8];   // x_s hi, x_s lo, x_l hi, x_l lo
   __shared__ float part[NW][kTileTok];
 
   const int wg = blockIdx.x;
@@ -93,11 +96,14 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
     wp1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 3 * DD + (int64_t)j * D + i0));
   }
 
-  // q tile loader: kTileTok * D / 8 chunks of 16 bytes
-  constexpr int QCH = kTileTok * D / 8;
-  auto load_q = [&](int tok0, u32x4* regs) {
+  // Global operands of a tile (q tile chunks, this lane's o_s slice), fetched two tiles ahead.
+  struct Pre {
+    u32x4 q[QPT];
+    uint2 os[NT];
+  };
+  auto fetch = [&](int tok0, Pre& pr) {
 #pragma unroll
-    for (int c = 0; c < (QCH + NTHR - 1) / NTHR; ++c) {
+    for (int c = 0; c < QPT; ++c) {
       const int e = c * NTHR + tid;
       u32x4 val = {0, 0, 0, 0};
       if (e < QCH) {
@@ -105,37 +111,27 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
         const int n = tok0 + r;
         if (n < tok_end) val = *reinterpret_cast<const u32x4*>(q + (((int64_t)t * N + n) * H + h) * D + cc * 8);
       }
-      regs[c] = val;
+      pr.q[c] = val;
     }
-  };
-  auto store_q = [&](const u32x4* regs) {
-#pragma unroll
-    for (int c = 0; c < (QCH + NTHR - 1) / NTHR; ++c) {
-      const int e = c * NTHR + tid;
-      if (e < QCH) {
-        const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<u32x4*>(&qtile[r][cc * 8]) = regs[c];
-      }
-    }
-  };
-
-  u32x4 qreg[(QCH + NTHR - 1) / NTHR];
-  load_q(tok_begin, qreg);
-  for (int tok0 = tok_begin; tok0 < tok_end; tok0 += kTileTok) {
-    store_q(qreg);
-    // o_s slice of this wave's channels for its two tokens (prefetch before the barrier)
-    uint2 osv[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = tok0 + nt * 16 + l16;
-      osv[nt] = n < tok_end ? *reinterpret_cast<const uint2*>(o_s + (((int64_t)t * N + n) * H + h) * D + j0 + lg * 4)
-                            : make_uint2(0, 0);
+      pr.os[nt] = n < tok_end ? *reinterpret_cast<const uint2*>(o_s + (((int64_t)t * N + n) * H + h) * D + j0 + lg * 4)
+                              : make_uint2(0, 0);
     }
-    __syncthreads();                                         // q tile ready (all reads of the
-                                                             // previous tiles ended before the
-                                                             // previous iteration's 2nd/3rd barrier)
-    if (tok0 + kTileTok < tok_end) load_q(tok0 + kTileTok, qreg);
+  };
 
+  auto process = [&](int tok0, const Pre& pr) {
+#pragma unroll
+    for (int c = 0; c < QPT; ++c) {
+      const int e = c * NTHR + tid;
+      if (e < QCH) {
+        const int r = e / (D / 8), cc = e % (D / 8);
+        *reinterpret_cast<u32x4*>(&qtile[r][cc * 8]) = pr.q[c];
+      }
+    }
+    __syncthreads();                                         // q tile ready (previous tile's readers
+                                                             // passed the previous 2nd and 3rd barrier)
     f32x4 ol[NT], gs[NT], gl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -160,21 +156,32 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
       if (lg == 0) part[wave][nt * 16 + l16] = ss;
     }
     __syncthreads();                                         // partial sums ready
+    // gated branches, as bf16 hi + lo parts (the projection weights are exact bf16, so the two
+    // projections keep ~fp32 accuracy)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float ss = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) ss += part[ww][nt * 16 + l16];
       const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + 1e-6f);
-      const bf16_t* ob = reinterpret_cast<const bf16_t*>(&osv[nt]);
-      __bf16 xs[4], xl[4];
+      __bf16 xsh[4], xsl[4], xlh[4], xll[4];
+      const uint32_t o01 = pr.os[nt].x, o23 = pr.os[nt].y;
+      const float osv[4] = {__uint_as_float(o01 << 16), __uint_as_float(o01 & 0xFFFF0000u),
+                            __uint_as_float(o23 << 16), __uint_as_float(o23 & 0xFFFF0000u)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        xs[e] = (__bf16)(sigmoidf_(gs[nt][e]) * to_f32(ob[e]));
-        xl[e] = (__bf16)(sigmoidf_(gl[nt][e]) * ol[nt][e] * rinv);
+        const float xs = sigmoidf_(gs[nt][e]) * osv[e];
+        const float xl = sigmoidf_(gl[nt][e]) * ol[nt][e] * rinv;
+        xsh[e] = (__bf16)xs;
+        xsl[e] = (__bf16)(xs - (float)xsh[e]);
+        xlh[e] = (__bf16)xl;
+        xll[e] = (__bf16)(xl - (float)xlh[e]);
       }
-      *reinterpret_cast<uint2*>(&xtile[0][nt * 16 + l16][j0 + lg * 4]) = __builtin_bit_cast(uint2, xs);
-      *reinterpret_cast<uint2*>(&xtile[1][nt * 16 + l16][j0 + lg * 4]) = __builtin_bit_cast(uint2, xl);
+      const int row = nt * 16 + l16, c0 = j0 + lg * 4;
+      *reinterpret_cast<uint2*>(&xtile[0][row][c0]) = __builtin_bit_cast(uint2, xsh);
+      *reinterpret_cast<uint2*>(&xtile[1][row][c0]) = __builtin_bit_cast(uint2, xsl);
+      *reinterpret_cast<uint2*>(&xtile[2][row][c0]) = __builtin_bit_cast(uint2, xlh);
+      *reinterpret_cast<uint2*>(&xtile[3][row][c0]) = __builtin_bit_cast(uint2, xll);
     }
     __syncthreads();                                         // gated branches ready
 #pragma unroll
@@ -182,10 +189,15 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
       f32x4 o = {0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 xs = as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[0][nt * 16 + l16][ks * 32 + lg * 8]));
-        const bf16x8 xl = as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[1][nt * 16 + l16][ks * 32 + lg * 8]));
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp0[ks], xs, o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ks], xl, o, 0, 0, 0);
+        const int row = nt * 16 + l16, k0 = ks * 32 + lg * 8;
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wp0[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[0][row][k0])), o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wp0[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[1][row][k0])), o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wp1[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[2][row][k0])), o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            wp1[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[3][row][k0])), o, 0, 0, 0);
       }
       const int n = tok0 + nt * 16 + l16;
       if (n < tok_end) {
@@ -194,6 +206,19 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)o[e];
         *reinterpret_cast<uint2*>(out + (((int64_t)t * N + n) * H + h) * D + j0 + lg * 4) = __builtin_bit_cast(uint2, ov);
       }
+    }
+  };
+
+  // two register sets, fetched two tiles ahead of their use
+  Pre pa, pb;
+  fetch(tok_begin, pa);
+  fetch(tok_begin + kTileTok, pb);
+  for (int tok0 = tok_begin; tok0 < tok_end; tok0 += 2 * kTileTok) {
+    process(tok0, pa);
+    if (tok0 + 2 * kTileTok < tok_end) fetch(tok0 + 2 * kTileTok, pa);
+    if (tok0 + kTileTok < tok_end) {
+      process(tok0 + kTileTok, pb);
+      if (tok0 + 3 * kTileTok < tok_end) fetch(tok0 + 3 * kTileTok, pb);
     }
   }
 }

@@ -222,6 +222,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) 
   constexpr int K_INSTR = SM::K_BYTES / 1024 / kWaves;     // per wave
   constexpr int V_INSTR = SM::V_BYTES / 1024 / kWaves;
   constexpr int K_ROWS_PER_KB = 1024 / (D * 2);
+  static_assert(K_INSTR + V_INSTR < 16, "vmcnt field");
+  constexpr int kVmcntTile = 0x0F70 | (K_INSTR + V_INSTR);   // s_waitcnt vmcnt(loads of one tile)
   uint32_t koff[K_INSTR], voff[V_INSTR];
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
@@ -371,41 +373,71 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) 
   };
 
   if constexpr (!FALLBACK) {
-    // full tiles: straight-line body; the second half's scores can overlap the first half's
-    // exponentials
-    for (int it = 0; it < nfull; ++it) {
-      next_tile(it);
-      const unsigned char* kb = smem + (it & 1) * SM::STAGE;
-      const unsigned char* vb = kb + SM::K_BYTES;
-      f32x16 s0[kQSub], s1[kQSub];
-      bf16x8 p0[kQSub][2], p1[kQSub][2];
-      scores(kb, 0, s0);
-      scores(kb, 1, s1);
-      probs(s0, p0);
-      accumulate(vb, 0, p0);
-      probs(s1, p1);
-      accumulate(vb, 1, p1);
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      __syncthreads();
+    // Software-pipelined over tiles with three LDS stages: iteration i computes the scores of
+    // tile i+1 (MFMA) while it turns the scores of tile i into probabilities (VALU), then
+    // accumulates P.V of tile i.  The two streams are independent inside the iteration, so one
+    // wave keeps the matrix pipe and the vector ALU busy at the same time.  Full tiles come before
+    // partial ones (tile_at), so masking is a uniform branch outside the overlapped block.
+    f32x16 sc0[kQSub], sc1[kQSub];          // scores of the tile being finished
+    {
+      int key0, valid;
+      tile_at(0, key0, valid);
+      issue_tile(key0, 0);
+      if (ntiles > 1) {
+        tile_at(1, key0, valid);
+        issue_tile(key0, 1);
+        __builtin_amdgcn_s_waitcnt(kVmcntTile);      // tile 0 landed, tile 1 may still be in flight
+      } else {
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      }
     }
-    // partial tiles (at most one per range)
-    for (int it = nfull; it < ntiles; ++it) {
-      next_tile(it);
+    __syncthreads();
+    scores(smem, 0, sc0);
+    scores(smem, 1, sc1);
+    for (int it = 0; it + 1 < ntiles; ++it) {
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);       // tile it+1 landed
+      __syncthreads();                              // ... for every wave; stage (it+2)%3 is free
+      if (it + 2 < ntiles) {
+        int nkey0, nvalid;
+        tile_at(it + 2, nkey0, nvalid);
+        issue_tile(nkey0, (it + 2) % 3);
+      }
       int key0, valid;
       tile_at(it, key0, valid);
-      const unsigned char* kb = smem + (it & 1) * SM::STAGE;
-      const unsigned char* vb = kb + SM::K_BYTES;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc[kQSub];
-        bf16x8 pf[kQSub][2];
-        scores(kb, kt, sacc);
-        mask(kt, valid, sacc);
-        probs(sacc, pf);
-        accumulate(vb, kt, pf);
+      if (valid < kBK) {
+        mask(0, valid, sc0);
+        mask(1, valid, sc1);
       }
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      __syncthreads();
+      const unsigned char* kn = smem + ((it + 1) % 3) * SM::STAGE;
+      const unsigned char* vb = smem + (it % 3) * SM::STAGE + SM::K_BYTES;
+      f32x16 sn0[kQSub], sn1[kQSub];
+      bf16x8 p0[kQSub][2], p1[kQSub][2];
+      scores(kn, 0, sn0);
+      probs(sc0, p0);
+      scores(kn, 1, sn1);
+      probs(sc1, p1);
+      accumulate(vb, 0, p0);
+      accumulate(vb, 1, p1);
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs) {
+        sc0[qs] = sn0[qs];
+        sc1[qs] = sn1[qs];
+      }
+    }
+    {
+      const int it = ntiles - 1;
+      int key0, valid;
+      tile_at(it, key0, valid);
+      if (valid < kBK) {
+        mask(0, valid, sc0);
+        mask(1, valid, sc1);
+      }
+      const unsigned char* vb = smem + (it % 3) * SM::STAGE + SM::K_BYTES;
+      bf16x8 p0[kQSub][2], p1[kQSub][2];
+      probs(sc0, p0);
+      probs(sc1, p1);
+      accumulate(vb, 0, p0);
+      accumulate(vb, 1, p1);
     }
   } else {
     for (int it = 0; it < ntiles; ++it) {
@@ -475,7 +507,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   P.per_xcd = (P.n_int_wg + 7) / 8;
   P.c_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int grid = softmax_grid(s);
-  const size_t smem = 2 * Smem<D>::STAGE;
+  const size_t smem = 3 * Smem<D>::STAGE;
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
