@@ -51,6 +51,41 @@ def vda_bytes(w) -> float:
     return w.H * ((scanned * w.N + w.n_text) * (2 * w.d * s + 4)) + 2 * nc * w.d * w.d * 4 * w.H
 
 
+def stage_rooflines(w, ms):
+    """Standalone per-stage rooflines from per-stage milliseconds of a serial plan."""
+    s = 2 if w.dtype == "bf16" else 4
+    tok = w.T * w.N * w.H * w.d
+    lk = (w.n_text + 63) // 64 * 64 + w.T * w.N
+    out = {}
+    def hbm(name, nbytes, t):
+        if t > 0:
+            out[name] = {"bound": "hbm", "ms": t, "algorithmic_GB": nbytes / 1e9,
+                         "achieved_GBs": nbytes / (t * 1e-3) / 1e9, "frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    t = ms["softmax"]
+    out["softmax"] = {"bound": "mfma", "ms": t, "achieved_TFLOPs": softmax_flops(w) / (t * 1e-3) / 1e12,
+                      "frac": softmax_flops(w) / (t * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    hbm("prep", 2 * tok * s + 2 * w.n_text * w.H * w.d * s + 2 * w.H * lk * w.d * 2, ms["prep"])
+    hbm("vda_stats+scan", vda_bytes(w), ms["vda_stats"] + ms["vda_scan"])
+    hbm("epilogue", 3 * tok * s, ms["epilogue"])
+    return out
+
+
+def recorded_traffic():
+    """HBM bytes per softmax launch from the committed rocprofv3 byte-counter summary, if it was
+    taken on the current source of the softmax kernel (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "softmax_mfma_768p_traffic.txt")
+    src = os.path.join(ROOT, "linear_video_attention_amd", "csrc", "softmax_mfma.hip")
+    try:
+        rec = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256", "").strip() != sha:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, inp, budget_rows=256):
     """Time the CPU oracle on a bounded sample of the workload and scale it to video tokens/s.
 
@@ -166,14 +201,30 @@ def main():
                    "n_text": w.n_text, "T": w.T, "N": w.N, "C": w.C, "H": w.H, "d": w.d},
         "roofline": {"bound": "mfma", "kernel": "softmax_mfma_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "algorithmic_tflop_per_launch": flops / 1e12, "avg_launch_ms": sm_ms},
+                     "traffic": recorded_traffic(), "algorithmic_tflop_per_launch": flops / 1e12,
+                     "avg_launch_ms": sm_ms},
         "stages_ms": {k: v / calls for k, v in stage_ms.items()},
         "vda": {"ms": vda_ms, "algorithmic_bytes": vda_bytes(w),
                 "achieved_GBs": vda_bytes(w) / (vda_ms * 1e-3) / 1e9,
                 "frac_hbm": vda_bytes(w) / (vda_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     plan.close()
-    del dev, beta, text_kv, out
+    # the same forward with every stage serialised on one stream: standalone per-stage rooflines
+    splan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, serial=True)
+    sref = out.clone()
+    for _ in range(2):
+        splan.forward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"], dev["proj_w"], out)
+    torch.cuda.synchronize()
+    n_solo = max(3, min(args.steps, 10))
+    splan.profile_enable(n_solo)
+    for _ in range(n_solo):
+        splan.forward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"], dev["proj_w"], out)
+    torch.cuda.synchronize()
+    solo_ms, solo_calls = splan.profile_read()
+    splan.close()
+    result["standalone_stages"] = stage_rooflines(w, {k: v / solo_calls for k, v in solo_ms.items()})
+    result["standalone_stages"]["serial_and_overlapped_outputs_identical"] = bool(torch.equal(out, sref))
+    del dev, beta, text_kv, out, sref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)

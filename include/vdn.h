@@ -77,8 +77,10 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
                            vdn_dtype dtype, vdn_plan **plan_out);
 
 /* As vdn_plan_create, with flags: VDN_FLAG_GENERIC_KERNELS selects the generic (SIMT) kernel of
- * every stage even where an MFMA kernel exists (used to cross-check the two kernel families). */
-enum { VDN_FLAG_GENERIC_KERNELS = 1 };
+ * every stage even where an MFMA kernel exists (used to cross-check the two kernel families);
+ * VDN_FLAG_SERIAL runs every stage one after the other on the caller's stream (no side stream),
+ * so that per-stage timings measure each stage alone.  Results are identical either way. */
+enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2 };
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,
                               vdn_dtype dtype, unsigned flags, vdn_plan **plan_out);
 

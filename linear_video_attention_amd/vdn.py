@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libvdn.so")
 VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_OUT_OF_MEMORY, VDN_ERR_HIP = 0, -1, -2, -3, -4
 VDN_F32, VDN_BF16 = 0, 1
 VDN_FLAG_GENERIC_KERNELS = 1
+VDN_FLAG_SERIAL = 2
 VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV, VDN_BUF_BW = 0, 1, 2, 3
 STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total")
 
@@ -90,11 +91,11 @@ def vdn_scan_frames(T, C, anchors, t, direction):
 
 # ---- plan ----
 
-def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False):
+def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False):
     """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"."""
     dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
     h = _vp()
-    flags = VDN_FLAG_GENERIC_KERNELS if generic else 0
+    flags = (VDN_FLAG_GENERIC_KERNELS if generic else 0) | (VDN_FLAG_SERIAL if serial else 0)
     _check(lib().vdn_plan_create_ex(T, N, C, n_text, H, d, int(anchors), dt, flags, ctypes.byref(h)),
            "vdn_plan_create")
     return h.value
@@ -122,7 +123,7 @@ def vdn_forward(plan, q, k, v, beta, text_kv, gate_w, proj_w, out, stream=None):
 class Plan:
     """Owning wrapper of a plan with argument checks on torch tensors."""
 
-    def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False):
+    def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("no GPU visible: the VDN layer runs only on the GPU")
@@ -131,7 +132,7 @@ class Plan:
         self.dtype = dtype
         self.torch_dtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         self.Nc = (T + C - 1) // C
-        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic)
+        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial)
 
     def close(self):
         if self.handle:
