@@ -35,6 +35,7 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.vt = p->kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.vt) : nullptr;
   b.minv = reinterpret_cast<float*>(ws + p->lay.minv);
   b.bw = reinterpret_cast<float*>(ws + p->lay.bw);
+  b.cw = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.cw) : nullptr;
   b.states = reinterpret_cast<float*>(ws + p->lay.states);
   b.wt = p->kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.wt) : nullptr;
   b.kmax_part = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax_part) : nullptr;
@@ -124,7 +125,7 @@ vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int
   p->s = make_shape(T, N, C, n_text, H, d, anchors, dtype);
   p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
   p->serial = (flags & VDN_FLAG_SERIAL) != 0;
-  p->lay = vdn::make_layout(p->s, p->kinds.softmax_mfma, p->kinds.epilogue_mfma);
+  p->lay = vdn::make_layout(p->s, p->kinds);
   if (hipGetDevice(&p->device) != hipSuccess) { free_plan(p); return VDN_ERR_HIP; }
   if (hipMalloc(&p->ws, p->lay.total) != hipSuccess) {
     (void)hipGetLastError();

@@ -21,4 +21,10 @@ __device__ __forceinline__ void store_elt(bf16_t* p, float x) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Sigmoid from the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of
+// the IEEE-exact division sequence; large |x| saturate to 0 or 1.
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
 }  // namespace vdn

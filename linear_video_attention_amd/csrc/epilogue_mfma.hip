@@ -29,7 +29,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kTileTok = 64;
-constexpr int kTokPerWG = 512;
+#ifndef VDN_EPI_TOK
+#define VDN_EPI_TOK 512
+#endif
+constexpr int kTokPerWG = VDN_EPI_TOK;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -163,15 +166,15 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
       float ss = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) ss += part[ww][nt * 16 + l16];
-      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + 1e-6f);
+      const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + 1e-6f);
       __bf16 xsh[4], xsl[4], xlh[4], xll[4];
       const uint32_t o01 = pr.os[nt].x, o23 = pr.os[nt].y;
       const float osv[4] = {__uint_as_float(o01 << 16), __uint_as_float(o01 & 0xFFFF0000u),
                             __uint_as_float(o23 << 16), __uint_as_float(o23 & 0xFFFF0000u)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float xs = sigmoidf_(gs[nt][e]) * osv[e];
-        const float xl = sigmoidf_(gl[nt][e]) * ol[nt][e] * rinv;
+        const float xs = fast_sigmoid(gs[nt][e]) * osv[e];
+        const float xl = fast_sigmoid(gl[nt][e]) * ol[nt][e] * rinv;
         xsh[e] = (__bf16)xs;
         xsl[e] = (__bf16)(xs - (float)xsh[e]);
         xlh[e] = (__bf16)xl;

@@ -50,7 +50,8 @@ int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames) {
   return n;
 }
 
-Layout make_layout(const Shape& s, bool mfma_softmax, bool mfma_epilogue) {
+Layout make_layout(const Shape& s, const Kinds& k) {
+  const bool mfma_softmax = k.softmax_mfma, mfma_epilogue = k.epilogue_mfma;
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (size_t)round_up((int64_t)bytes, 256); return o; };
@@ -62,6 +63,7 @@ Layout make_layout(const Shape& s, bool mfma_softmax, bool mfma_epilogue) {
   L.vt = mfma_softmax ? take((size_t)s.H * s.Ls * s.d * 2) : 0;
   L.minv = take((size_t)(s.T + 1) * s.H * dd * 4);
   L.bw = take((size_t)(s.T + 1) * s.H * dd * 4);
+  L.cw = k.scan_mfma ? take((size_t)(s.T + 1) * s.H * dd * 4) : 0;
   L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
   L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
   L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;

@@ -38,6 +38,7 @@ struct Layout {
   size_t vt;        // packed values, transposed [H][d][Ls] bf16
   size_t minv;      // M = (I+A)^-1  [T+1][H][d][d] f32
   size_t bw;        // B             [T+1][H][d][d] f32
+  size_t cw;        // C = B M       [T+1][H][d][d] f32      (MFMA scan only)
   size_t states;    // S_fwd, S_rev  [2][Nc+1][H][d][d] f32
   size_t wt;        // transposed weights [4][d][d] bf16: Wg0^T, Wg1^T, Wp0^T, Wp1^T (MFMA epilogue)
   size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
@@ -46,8 +47,6 @@ struct Layout {
   size_t ranges;    // int32 [T][2*kMaxRanges] + int32 [T] counts
   size_t total;
 };
-Layout make_layout(const Shape& s, bool mfma_softmax, bool mfma_epilogue);
-
 // Kernel selection per stage.
 struct Kinds {
   bool softmax_mfma;
@@ -56,6 +55,7 @@ struct Kinds {
   bool epilogue_mfma;
 };
 Kinds choose_kinds(const Shape& s);
+Layout make_layout(const Shape& s, const Kinds& k);
 
 struct Buffers {
   void* os;
@@ -63,6 +63,7 @@ struct Buffers {
   uint16_t* vt;
   float* minv;
   float* bw;
+  float* cw;
   float* states;
   uint16_t* wt;
   float* kmax_part;
