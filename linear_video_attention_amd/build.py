@@ -24,6 +24,7 @@ SOURCES = [
     "softmax_mfma.hip",
     "vda.hip",
     "vda_stats_mfma.hip",
+    "vda_invert_mfma.hip",
     "vda_scan_mfma.hip",
     "epilogue_simt.hip",
     "epilogue_mfma.hip",

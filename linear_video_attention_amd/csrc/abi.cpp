@@ -35,7 +35,9 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.vt = p->kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.vt) : nullptr;
   b.minv = reinterpret_cast<float*>(ws + p->lay.minv);
   b.bw = reinterpret_cast<float*>(ws + p->lay.bw);
+  b.mhl = p->kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.mhl) : nullptr;
   b.cw = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.cw) : nullptr;
+  b.sink = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.sink) : nullptr;
   b.states = reinterpret_cast<float*>(ws + p->lay.states);
   b.wt = p->kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.wt) : nullptr;
   b.kmax_part = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax_part) : nullptr;

@@ -63,7 +63,9 @@ Layout make_layout(const Shape& s, const Kinds& k) {
   L.vt = mfma_softmax ? take((size_t)s.H * s.Ls * s.d * 2) : 0;
   L.minv = take((size_t)(s.T + 1) * s.H * dd * 4);
   L.bw = take((size_t)(s.T + 1) * s.H * dd * 4);
+  L.mhl = k.scan_mfma ? take((size_t)(s.T + 1) * s.H * dd * 4) : 0;
   L.cw = k.scan_mfma ? take((size_t)(s.T + 1) * s.H * dd * 4) : 0;
+  L.sink = k.scan_mfma ? take(dd * 4) : 0;
   L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
   L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
   L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;
@@ -80,7 +82,7 @@ Kinds choose_kinds(const Shape& s) {
   // lane offsets into one head's packed V^T are 32-bit: d * Ls * 2 bytes must stay below 2^31
   k.softmax_mfma = bf16 && (s.d == 64 || s.d == 128) && s.N % 8 == 0 && (int64_t)s.d * s.Ls * 2 < (int64_t(1) << 31);
   k.stats_mfma = bf16 && (s.d == 64 || s.d == 128);
-  k.scan_mfma = bf16 && (s.d == 64 || s.d == 128);
+  k.scan_mfma = k.stats_mfma;     // the MFMA statistics stage writes the MFMA scan's operands
   k.epilogue_mfma = bf16 && (s.d == 64 || s.d == 128);
   return k;
 }

@@ -1,6 +1,6 @@
 // MFMA statistics of Video Delta Attention (bf16 plans, d in {64, 128}): per (frame or text, head)
 // the weighted key Gram A = sum_u beta_u k_u k_u^T and write matrix B = sum_u beta_u v_u k_u^T,
-// then M = (I + A)^-1 by in-register Gauss-Jordan elimination.
+// written as I + A (inverted in place by the next kernel) and B.
 //
 // "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Video Delta
 // Attention: A Frame-Wise Solution": a frame's tokens jointly update the state as
@@ -18,7 +18,6 @@
 // order is free, and the mapping is undone when the result is written.  4 waves: waves 0-1 own the
 // rows of A, waves 2-3 those of B.  HBM-bound: every K/V/beta byte of the frame is read once.
 #include "dev_common.h"
-#include "vda_common.h"
 #include "vdn_internal.h"
 
 namespace vdn {
@@ -41,7 +40,7 @@ struct GramSmem {
   static constexpr int A_BYTES = D * (D + 1) * 4;
   static constexpr int TILE_BYTES = X_BYTES + Y_BYTES;
   static constexpr int MAIN = TILE_BYTES > A_BYTES ? TILE_BYTES : A_BYTES;
-  static constexpr int TOTAL = MAIN + 4 * D * 4;       // + Gauss-Jordan row/column buffers
+  static constexpr int TOTAL = MAIN;
 };
 
 template <int D>
@@ -158,8 +157,6 @@ __global__ __launch_bounds__(256) void vda_gram_mfma_kernel(const bf16_t* __rest
   __syncthreads();                          // tiles no longer needed: the LDS now holds I + A
 
   float* af = reinterpret_cast<float*>(smem);           // [D][D + 1]
-  float* rowbuf = reinterpret_cast<float*>(smem + SM::MAIN);
-  float* colbuf = rowbuf + 2 * D;
   const int64_t DD = (int64_t)D * D;
   const int64_t mbase = ((int64_t)slot * H + h) * DD;
 #pragma unroll
@@ -179,18 +176,7 @@ __global__ __launch_bounds__(256) void vda_gram_mfma_kernel(const bf16_t* __rest
         }
       }
   __syncthreads();
-  constexpr int R = D / 16;
-  const int ty = tid / 16, tx = tid % 16;
-  float g[R][R];
-#pragma unroll
-  for (int ii = 0; ii < R; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < R; ++jj) g[ii][jj] = af[(ty * R + ii) * (D + 1) + tx * R + jj];
-  gauss_jordan_inverse<D>(g, rowbuf, colbuf, ty, tx);
-#pragma unroll
-  for (int ii = 0; ii < R; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < R; ++jj) minv[mbase + (int64_t)(ty * R + ii) * D + tx * R + jj] = g[ii][jj];
+  for (int e = tid; e < D * D; e += 256) minv[mbase + e] = af[(e / D) * (D + 1) + e % D];   // I + A, inverted later
 }
 
 template <int D>
@@ -208,7 +194,8 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
 hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   if (s.d == 128) launch_t<128>(s, in, b, st);
   else launch_t<64>(s, in, b, st);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_vda_invert_mfma(s, b, st);
 }
 
 }  // namespace vdn

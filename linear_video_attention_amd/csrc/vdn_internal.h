@@ -37,8 +37,10 @@ struct Layout {
   size_t kp;        // packed keys  [H][Ls][d] bf16          (MFMA softmax path only)
   size_t vt;        // packed values, transposed [H][d][Ls] bf16
   size_t minv;      // M = (I+A)^-1  [T+1][H][d][d] f32
+  size_t mhl;       // M as bf16 high and low planes [T+1][H][2][d][d] (MFMA scan only)
   size_t bw;        // B             [T+1][H][d][d] f32
-  size_t cw;        // C = B M       [T+1][H][d][d] f32      (MFMA scan only)
+  size_t cw;        // C = B M       [T+1][H][d][d] f32 (MFMA scan only)
+  size_t sink;      // [d][d] f32: target of the MFMA scan's stores that keep nothing (never read)
   size_t states;    // S_fwd, S_rev  [2][Nc+1][H][d][d] f32
   size_t wt;        // transposed weights [4][d][d] bf16: Wg0^T, Wg1^T, Wp0^T, Wp1^T (MFMA epilogue)
   size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
@@ -62,8 +64,10 @@ struct Buffers {
   uint16_t* kp;
   uint16_t* vt;
   float* minv;
+  uint16_t* mhl;
   float* bw;
   float* cw;
+  float* sink;
   float* states;
   uint16_t* wt;
   float* kmax_part;
@@ -90,6 +94,7 @@ hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& 
 hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_vda_invert_mfma(const Shape& s, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_scan(const Shape& s, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_vda_scan_mfma(const Shape& s, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
