@@ -37,7 +37,8 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.bw = reinterpret_cast<float*>(ws + p->lay.bw);
   b.mhl = p->kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.mhl) : nullptr;
   b.cw = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.cw) : nullptr;
-  b.sink = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.sink) : nullptr;
+  b.pp = p->kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.pp) : nullptr;
+  b.qq = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.qq) : nullptr;
   b.states = reinterpret_cast<float*>(ws + p->lay.states);
   b.wt = p->kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.wt) : nullptr;
   b.kmax_part = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax_part) : nullptr;

@@ -65,7 +65,8 @@ Layout make_layout(const Shape& s, const Kinds& k) {
   L.bw = take((size_t)(s.T + 1) * s.H * dd * 4);
   L.mhl = k.scan_mfma ? take((size_t)(s.T + 1) * s.H * dd * 4) : 0;
   L.cw = k.scan_mfma ? take((size_t)(s.T + 1) * s.H * dd * 4) : 0;
-  L.sink = k.scan_mfma ? take(dd * 4) : 0;
+  L.pp = k.scan_mfma ? take((size_t)s.Nc * s.H * 4 * dd * 2) : 0;
+  L.qq = k.scan_mfma ? take((size_t)2 * s.Nc * s.H * dd * 4) : 0;
   L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
   L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
   L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;

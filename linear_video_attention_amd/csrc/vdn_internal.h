@@ -40,7 +40,8 @@ struct Layout {
   size_t mhl;       // M as bf16 high and low planes [T+1][H][2][d][d] (MFMA scan only)
   size_t bw;        // B             [T+1][H][d][d] f32
   size_t cw;        // C = B M       [T+1][H][d][d] f32 (MFMA scan only)
-  size_t sink;      // [d][d] f32: target of the MFMA scan's stores that keep nothing (never read)
+  size_t pp;        // chunk maps P, P^T as bf16 hi/lo planes [Nc][H][2][2][d][d] (MFMA scan only)
+  size_t qq;        // chunk maps Q_fwd, Q_rev [2][Nc][H][d][d] f32 (MFMA scan only)
   size_t states;    // S_fwd, S_rev  [2][Nc+1][H][d][d] f32
   size_t wt;        // transposed weights [4][d][d] bf16: Wg0^T, Wg1^T, Wp0^T, Wp1^T (MFMA epilogue)
   size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
@@ -67,7 +68,8 @@ struct Buffers {
   uint16_t* mhl;
   float* bw;
   float* cw;
-  float* sink;
+  uint16_t* pp;
+  float* qq;
   float* states;
   uint16_t* wt;
   float* kmax_part;
