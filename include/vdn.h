@@ -40,8 +40,8 @@
  *
  * Ownership: the caller owns every tensor; the library reads inputs and writes `out` inside the
  * stream-ordered call and keeps no reference afterwards.  `out` must not alias an input.  The plan
- * owns a device workspace allocated at create time on the device current then, plus one side
- * stream and two events; a plan is used from that device only.  Calls on one plan must not
+ * owns a device workspace allocated at create time on the device current then (plus one side
+ * stream and two events when created with VDN_FLAG_OVERLAP); a plan is used from that device only.  Calls on one plan must not
  * overlap (they share the workspace): serialise them on one stream, or use one plan per stream.
  *
  * Errors: no call aborts or throws.  Argument errors are detected on the host before anything is
@@ -71,16 +71,20 @@ typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype;
 
 /* Build a plan for one layer shape.  T frames of N tokens, chunks of C frames, n_text text tokens
  * (may be 0), H heads of size d, anchors 0/1, element type dtype.  Computes the per-frame key
- * ranges of the softmax branch and the scan order of the linear branch, allocates the workspace
- * and the side stream.  On success *plan_out owns them; on failure *plan_out is set to NULL. */
+ * ranges of the softmax branch and the scan order of the linear branch, and allocates the
+ * workspace.  Every stage runs in order on the caller's stream.  On success *plan_out owns the
+ * plan; on failure *plan_out is set to NULL. */
 vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int anchors,
                            vdn_dtype dtype, vdn_plan **plan_out);
 
 /* As vdn_plan_create, with flags: VDN_FLAG_GENERIC_KERNELS selects the generic (SIMT) kernel of
  * every stage even where an MFMA kernel exists (used to cross-check the two kernel families);
- * VDN_FLAG_SERIAL runs every stage one after the other on the caller's stream (no side stream),
- * so that per-stage timings measure each stage alone.  Results are identical either way. */
-enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2 };
+ * VDN_FLAG_SERIAL requests the default order (every stage one after the other on the caller's
+ * stream); VDN_FLAG_OVERLAP instead runs the linear branch on a side stream of the plan, forked
+ * from and joined back into the caller's stream, concurrently with the softmax branch (on MI355X
+ * this is slower at the 768p shape: the two branches compete for the compute units).  SERIAL and
+ * OVERLAP together are an argument error.  Results are identical in every case. */
+enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4 };
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,
                               vdn_dtype dtype, unsigned flags, vdn_plan **plan_out);
 
@@ -135,6 +139,14 @@ vdn_status vdn_profile_read(vdn_plan *plan, float *ms, int n_stages, int *calls)
 
 /* Which kernel family a plan selected for each stage (0 = generic SIMT kernel, 1 = MFMA kernel). */
 vdn_status vdn_plan_kernel_kind(const vdn_plan *plan, int stage, int *kind);
+
+/* On-box reference rates for rooflines (measurement helpers; synchronous, on the current device's
+ * null stream; no layer stage uses them).  vdn_measure_mfma_bf16_tflops runs a tight loop of
+ * independent v_mfma_f32_32x32x16_bf16 on every compute unit for `iters` iterations and reports
+ * dense bf16 TFLOP/s; vdn_measure_copy_gbs copies `bytes` device to device (hipMemcpyAsync) and
+ * reports GB/s counting the read and the write.  Both allocate and free their own buffers. */
+vdn_status vdn_measure_mfma_bf16_tflops(int iters, double *tflops);
+vdn_status vdn_measure_copy_gbs(size_t bytes, double *gbs);
 
 #ifdef __cplusplus
 }

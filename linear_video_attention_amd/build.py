@@ -28,6 +28,7 @@ SOURCES = [
     "vda_scan_mfma.hip",
     "epilogue_simt.hip",
     "epilogue_mfma.hip",
+    "calibrate.hip",
 ]
 
 ARCH = "gfx950"

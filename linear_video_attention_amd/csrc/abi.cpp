@@ -18,7 +18,7 @@ struct vdn_plan {
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // stage timing (mutable: recording events does not change the plan's meaning)
-  bool serial = false;                           // every stage on the caller's stream
+  bool overlap = false;                          // linear branch on the side stream
   mutable int prof_max = 0, prof_count = 0;
   mutable std::vector<hipEvent_t> prof_events;   // [prof_max][VDN_NUM_STAGES][2]
 };
@@ -120,14 +120,15 @@ vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int
   const int64_t tokens = (int64_t)T * N;
   if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || (int64_t)n_text * H * d > (int64_t(1) << 40))
     return VDN_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL)) return VDN_ERR_INVALID_ARG;
+  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
+  if ((flags & VDN_FLAG_SERIAL) && (flags & VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
   if ((int64_t)vdn::round_up(n_text, vdn::kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
 
   vdn_plan* p = new (std::nothrow) vdn_plan();
   if (!p) return VDN_ERR_OUT_OF_MEMORY;
   p->s = make_shape(T, N, C, n_text, H, d, anchors, dtype);
   p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
-  p->serial = (flags & VDN_FLAG_SERIAL) != 0;
+  p->overlap = (flags & VDN_FLAG_OVERLAP) != 0;
   p->lay = vdn::make_layout(p->s, p->kinds);
   if (hipGetDevice(&p->device) != hipSuccess) { free_plan(p); return VDN_ERR_HIP; }
   if (hipMalloc(&p->ws, p->lay.total) != hipSuccess) {
@@ -149,9 +150,9 @@ vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int
        (hipMemset(p->ws + p->lay.kp, 0, (size_t)p->s.H * p->s.Ls * d * 2) != hipSuccess ||
         hipMemset(p->ws + p->lay.vt, 0, (size_t)p->s.H * p->s.Ls * d * 2) != hipSuccess)) ||
       hipMemcpy(p->ws + p->lay.ranges, tab.data(), tab.size() * sizeof(int), hipMemcpyHostToDevice) != hipSuccess ||
-      hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming) != hipSuccess) {
+      (p->overlap && (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
+                      hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming) != hipSuccess ||
+                      hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming) != hipSuccess))) {
     free_plan(p);
     return VDN_ERR_HIP;
   }
@@ -204,10 +205,10 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
 #define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
 
   mark(VDN_STAGE_TOTAL, 0, main);
-  // linear branch: on the side stream, forked from the caller's stream (or on the caller's stream
-  // itself for serial plans)
-  hipStream_t lin = plan->serial ? main : plan->side;
-  if (!plan->serial) {
+  // linear branch: on the caller's stream, or for overlapped plans on the side stream, forked from
+  // the caller's stream
+  hipStream_t lin = plan->overlap ? plan->side : main;
+  if (plan->overlap) {
     VDN_TRY(hipEventRecord(plan->ev_fork, main));
     VDN_TRY(hipStreamWaitEvent(plan->side, plan->ev_fork, 0));
   }
@@ -217,7 +218,7 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   mark(VDN_STAGE_VDA_SCAN, 0, lin);
   VDN_TRY(vdn::launch_vda_scan(s, b, plan->kinds.scan_mfma, lin));
   mark(VDN_STAGE_VDA_SCAN, 1, lin);
-  if (!plan->serial) VDN_TRY(hipEventRecord(plan->ev_join, plan->side));
+  if (plan->overlap) VDN_TRY(hipEventRecord(plan->ev_join, plan->side));
   // softmax branch on the caller's stream
   mark(VDN_STAGE_PREP, 0, main);
   if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
@@ -228,7 +229,7 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   else VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
   mark(VDN_STAGE_SOFTMAX, 1, main);
   // join, then readout + gates + projections
-  if (!plan->serial) VDN_TRY(hipStreamWaitEvent(main, plan->ev_join, 0));
+  if (plan->overlap) VDN_TRY(hipStreamWaitEvent(main, plan->ev_join, 0));
   mark(VDN_STAGE_EPILOGUE, 0, main);
   if (plan->kinds.epilogue_mfma) VDN_TRY(vdn::launch_epilogue_mfma(s, in, b, main));
   else VDN_TRY(vdn::launch_epilogue(s, in, b, false, main));

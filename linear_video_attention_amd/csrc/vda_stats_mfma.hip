@@ -7,16 +7,19 @@
 // S <- (S + B)(I + A)^-1.  Section "Local Softmax and Long-Range Linear Memory": the text enters
 // once, at half strength in each direction (weights beta/2), as one joint update from S = 0.
 //
-// [A; B] = [K V]^T Diag(beta) K is one (2d x d) product with the frame's tokens as the reduction
-// dimension.  Tokens stream through LDS 64 at a time, written transposed (feature rows, token
-// columns) so both MFMA operands are read as token-contiguous 16-byte fragments:
-//   X^T = [K V]^T (2d rows, exact: the inputs are bf16), Y^T = (Diag(beta) K)^T held as two bf16
-//   parts hi + lo (beta * k = hi + lo to ~2^-16), so A and B keep near-fp32 accuracy and A stays
-//   symmetric (the scan reads M = (I + A)^-1 by rows using M^T = M).
-// Feature f = 8c + e of a 16-byte chunk c is stored at row e * (d/8) + c, so the eight 2-byte
-// LDS writes of one chunk land in different banks for neighbouring chunks; the MFMA row and column
-// order is free, and the mapping is undone when the result is written.  4 waves: waves 0-1 own the
-// rows of A, waves 2-3 those of B.  HBM-bound: every K/V/beta byte of the frame is read once.
+// [A; B] = [K V]^T Diag(beta) K is one (2d x d) product with the tokens as the reduction
+// dimension, run on v_mfma_f32_32x32x16_bf16:
+//   * tokens stream through LDS 64 at a time, copied straight from global memory in their natural
+//     token-major layout (global_load_lds, three stages: two tiles in flight while one is used),
+//     16-byte chunks XOR-swizzled per row; beta comes along the same way;
+//   * Y = Diag(beta) K is formed once per tile in LDS as two bf16 parts, beta k = Yh + Yl to
+//     ~2^-16, so A and B keep near-fp32 accuracy (X = [K V] is exact: the inputs are bf16);
+//   * both MFMA operands need eight consecutive tokens of one feature per lane: they are read
+//     with ds_read_b64_tr_b16, which hands lane j of each 16-lane group the 4 values at column j
+//     of the 4 x 16 block that the group's 16 addresses describe (two reads per fragment);
+//   * 8 waves: wave w owns X rows [32 MT (w % 4), +32 MT) (K features for w % 4 < 2, V features
+//     otherwise) and Y columns [32 NT (w / 4), +32 NT), MT = NT = d / 64.
+// Every K/V/beta byte of the frame is read once.
 #include "dev_common.h"
 #include "vdn_internal.h"
 
@@ -24,52 +27,65 @@ namespace vdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
 
 constexpr int kTU = 64;             // tokens per tile
-constexpr int kLDT = kTU + 8;       // token stride of the transposed tiles (bf16 elements)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+// 16-byte chunk c of token row r sits at chunk position c ^ swz(r).  The transposed reads of one
+// half-wave cover 4 consecutive rows x 64 bytes; the swizzle spreads them over all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3);
+  else return 4 * ((r >> 1) & 1);
+}
+
+constexpr int kStages = 3;
 
 template <int D>
 struct GramSmem {
-  static constexpr int CH = D / 8;
-  static constexpr int X_BYTES = 2 * D * kLDT * 2;
-  static constexpr int Y_BYTES = 2 * D * kLDT * 2;       // hi and lo parts
-  static constexpr int A_BYTES = D * (D + 1) * 4;
-  static constexpr int TILE_BYTES = X_BYTES + Y_BYTES;
-  static constexpr int MAIN = TILE_BYTES > A_BYTES ? TILE_BYTES : A_BYTES;
-  static constexpr int TOTAL = MAIN;
+  static constexpr int ROW = 2 * D;                    // bytes per token row
+  static constexpr int TILE = kTU * ROW;               // one matrix, one tile
+  static constexpr int BETA = 2 * TILE;                // beta: wave w's 256 bytes hold tokens 8w..8w+7
+  static constexpr int STAGE = BETA + kWaves * 256;    // K, V, beta
+  static constexpr int Y_OFF = kStages * STAGE;
+  static constexpr int TOTAL = Y_OFF + 2 * TILE;       // Yh, Yl
 };
 
-template <int D>
-__device__ __forceinline__ int feat_of_row(int p) {   // inverse of row(f) = (f % 8) * (D/8) + f / 8
-  constexpr int CH = D / 8;
-  return (p % CH) * 8 + p / CH;
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                        (__attribute__((address_space(3))) lds_bf16x4*)(p)));
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void vda_gram_mfma_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                                                            const float* __restrict__ beta,
-                                                            const bf16_t* __restrict__ text_kv,
-                                                            float* __restrict__ minv, float* __restrict__ bw, int T,
-                                                            int N, int H, int n_text, int anchors) {
+__global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* __restrict__ k,
+                                                                 const bf16_t* __restrict__ v,
+                                                                 const float* __restrict__ beta,
+                                                                 const bf16_t* __restrict__ text_kv,
+                                                                 float* __restrict__ minv, float* __restrict__ bw,
+                                                                 int T, int N, int H, int n_text, int anchors) {
   using SM = GramSmem<D>;
-  constexpr int CH = SM::CH;
-  constexpr int MT = 2 * D / 32 / 4;        // M tiles (32 rows of X^T) per wave
-  constexpr int NT = D / 32;                // N tiles (32 rows of Y^T)
-  constexpr int CHUNKS = kTU * CH;          // 16-byte chunks per matrix per tile
-  constexpr int CPT = 2 * CHUNKS / 256;     // chunks per thread (K and V)
+  constexpr int CH = D / 8;                 // 16-byte chunks per token row
+  constexpr int ROWS_PER_KB = 1024 / SM::ROW;
+  constexpr int DMA = SM::TILE / 1024 / kWaves;   // DMA instructions per wave per matrix and tile
+  constexpr int YCH = kTU * CH / kThreads;        // Y chunks per thread per tile
+  constexpr int MT = D / 64, NT = D / 64;
+  constexpr int kVmcntTile = 0x0F70 | (2 * DMA + 1);   // s_waitcnt vmcnt(one tile's loads of a wave)
+  static_assert(2 * DMA + 1 < 16, "vmcnt field");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16_t* xt = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* yt = reinterpret_cast<bf16_t*>(smem + SM::X_BYTES);          // hi part
-  bf16_t* yl = yt + D * kLDT;                                           // lo part
 
   const int slot = blockIdx.x, h = blockIdx.y;
   if (slot > 0 && anchors && (slot - 1 == 0 || slot - 1 == T - 1)) return;   // boundary frames are never written
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hl = lane >> 5;
 
   const int U = slot == 0 ? n_text : N;
   const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
@@ -77,106 +93,130 @@ __global__ __launch_bounds__(256) void vda_gram_mfma_kernel(const bf16_t* __rest
   const bf16_t* vbase = slot == 0 ? text_kv + (int64_t)n_text * H * D : v;
   const float wscale = slot == 0 ? 0.5f : 1.0f;
   const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
+  const int ntiles = (U + kTU - 1) / kTU;
 
-  u32x4 reg[CPT];
-  float wreg[CPT];
-  auto load = [&](int u0) {
+  // DMA: instruction i of wave w fills token rows (i*kWaves + w)*ROWS_PER_KB + lane / CH; lane
+  // writes chunk position lane % CH, so it fetches chunk (lane % CH) ^ swz(row).  Rows past the
+  // last token re-read the last token; beta is read for tokens 8w + lane % 8 (clamped the same
+  // way) and zeroed past the last token when Y is formed.  Every wave issues 2 DMA + 1 loads per
+  // tile and nothing else, so one explicit vmcnt per tile covers them.
+  auto issue_tile = [&](int u0, int stage) {
+    unsigned char* kb = smem + stage * SM::STAGE;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int e = i * 256 + tid;
-      const int m = e / CHUNKS, rem = e % CHUNKS;     // m: 0 = K, 1 = V
-      const int tok = rem / CH, c = rem % CH;
-      const int u = u0 + tok;
-      u32x4 val = {0, 0, 0, 0};
-      float wv = 0.f;
-      if (u < U) {
-        const int64_t off = ((tok0 + u) * H + h) * D + c * 8;
-        val = *reinterpret_cast<const u32x4*>((m == 0 ? kbase : vbase) + off);
-        if (m == 0) wv = wscale * beta[(brow0 + u) * H + h];
-      }
-      reg[i] = val;
-      wreg[i] = wv;
+    for (int i = 0; i < DMA; ++i) {
+      const int blk = i * kWaves + wave;
+      const int row = blk * ROWS_PER_KB + lane / CH;
+      const int u = min(u0 + row, U - 1);
+      const int c = (lane % CH) ^ swz<D>(row);
+      const int64_t off = ((tok0 + u) * H + h) * D + c * 8;
+      __builtin_amdgcn_global_load_lds((gptr_t)(kbase + off), (lptr_t)(kb + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(vbase + off), (lptr_t)(kb + SM::TILE + blk * 1024), 16, 0, 0);
     }
+    const int ub = min(u0 + 8 * wave + (lane & 7), U - 1);
+    __builtin_amdgcn_global_load_lds((gptr_t)(beta + (brow0 + ub) * H + h), (lptr_t)(kb + SM::BETA + wave * 256), 4,
+                                     0, 0);
   };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int e = i * 256 + tid;
-      const int m = e / CHUNKS, rem = e % CHUNKS;
-      const int tok = rem / CH, c = rem % CH;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int row = q * CH + c;
-        const bf16_t el = (bf16_t)((q & 1) ? (reg[i][q >> 1] >> 16) : (reg[i][q >> 1] & 0xFFFFu));
-        xt[(m * D + row) * kLDT + tok] = el;
-        if (m == 0) {
-          const float wk = wreg[i] * to_f32(el);
-          const __bf16 wh = (__bf16)wk;
-          const __bf16 wl = (__bf16)(wk - (float)wh);
-          yt[row * kLDT + tok] = __builtin_bit_cast(bf16_t, wh);
-          yl[row * kLDT + tok] = __builtin_bit_cast(bf16_t, wl);
-        }
-      }
-    }
+
+  // transposed-read lane offsets: lane (g = lane / 16, i = lane % 16) addresses token
+  // 8 (g / 2) + (i / 4) (+ 4 for the second read) and feature 16 (g % 2) + 4 (i % 4) of a
+  // 16-token x 32-feature fragment block
+  const int g = lane >> 4, li = lane & 15;
+  const int tr_tok = 8 * (g >> 1) + (li >> 2);
+  const int tr_feat = 16 * (g & 1) + 4 * (li & 3);
+  auto tr_off = [&](int f0) {                         // byte offset for feature block f0, token 0
+    const int f = f0 + tr_feat;
+    return tr_tok * SM::ROW + (((f >> 3) ^ swz<D>(tr_tok)) << 4) + (f & 7) * 2;
   };
+  const int xg = wave & 3, yh = wave >> 2;
+  int xoff[MT], yoff[NT];
+  bool xv[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int xr = (xg * MT + mt) * 32;                 // X row = K feature (< D) or D + V feature
+    xv[mt] = xr >= D;
+    xoff[mt] = tr_off(xv[mt] ? xr - D : xr);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) yoff[nt] = tr_off((yh * NT + nt) * 32);
 
   f32x16 acc[MT][NT];
 #pragma unroll
-  for (int a = 0; a < MT; ++a)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int b = 0; b < NT; ++b)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
-  if (U > 0) load(0);
-  for (int u0 = 0; u0 < U; u0 += kTU) {
-    __syncthreads();                        // previous tile fully consumed
-    store();
-    __syncthreads();
-    if (u0 + kTU < U) load(u0 + kTU);
+  if (ntiles > 0) issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(kTU, 1);
+  unsigned char* yb = smem + SM::Y_OFF;
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntTile);   // tile it landed, it+1 in flight
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+    __syncthreads();                       // ... for every wave; Y and stage (it+2)%3 (tile it-1) are free
+    if (it + 2 < ntiles) issue_tile((it + 2) * kTU, (it + 2) % kStages);
+    const unsigned char* kb = smem + (it % kStages) * SM::STAGE;
+    // Y = beta k as hi + lo, same chunk positions as K (chunk e = tid + s * kThreads, token e / CH)
+#pragma unroll
+    for (int s = 0; s < YCH; ++s) {
+      const int e = tid + s * kThreads;
+      const int tok = e / CH;
+      const float bt = it * kTU + tok < U ? wscale * *reinterpret_cast<const float*>(
+                                                          kb + SM::BETA + (tok >> 3) * 256 + (tok & 7) * 4)
+                                          : 0.f;
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kb + e * 16);
+      bf16x8 yhv, ylv;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float y = bt * (float)kv[q];
+        const __bf16 hi = (__bf16)y;
+        yhv[q] = hi;
+        ylv[q] = (__bf16)(y - (float)hi);
+      }
+      *reinterpret_cast<bf16x8*>(yb + e * 16) = yhv;
+      *reinterpret_cast<bf16x8*>(yb + SM::TILE + e * 16) = ylv;
+    }
+    __syncthreads();                                  // Y ready
 #pragma unroll
     for (int ks = 0; ks < kTU / 16; ++ks) {
-      bf16x8 bfr[NT], bfl[NT];
+      const int kbyte = ks * 16 * SM::ROW;
+      bf16x8 yf[NT][2];
 #pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        bfr[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(yt + (b * 32 + l32) * kLDT + ks * 16 + hl * 8));
-        bfl[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(yl + (b * 32 + l32) * kLDT + ks * 16 + hl * 8));
-      }
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int a = 0; a < MT; ++a) {
-        const int xrow = (wave * MT + a) * 32 + l32;
-        const bf16x8 afr = as_bf16x8(*reinterpret_cast<const u32x4*>(xt + xrow * kLDT + ks * 16 + hl * 8));
+        for (int p = 0; p < 2; ++p) {
+          const unsigned char* base = yb + p * SM::TILE + kbyte + yoff[nt];
+          yf[nt][p] = cat(tr_read(base), tr_read(base + 4 * SM::ROW));
+        }
 #pragma unroll
-        for (int b = 0; b < NT; ++b) {
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[b], acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfl[b], acc[a][b], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        const unsigned char* base = kb + (xv[mt] ? SM::TILE : 0) + kbyte + xoff[mt];
+        const bf16x8 xf = cat(tr_read(base), tr_read(base + 4 * SM::ROW));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, yf[nt][0], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, yf[nt][1], acc[mt][nt], 0, 0, 0);
         }
       }
     }
   }
-  __syncthreads();                          // tiles no longer needed: the LDS now holds I + A
 
-  float* af = reinterpret_cast<float*>(smem);           // [D][D + 1]
+  // acc[mt][nt][r]: X row 32 (xg MT + mt) + 8 (r / 4) + 4 (lane / 32) + r % 4, Y column
+  // 32 (yh NT + nt) + lane % 32
   const int64_t DD = (int64_t)D * D;
   const int64_t mbase = ((int64_t)slot * H + h) * DD;
+  const int l32 = lane & 31, hl = lane >> 5;
 #pragma unroll
-  for (int a = 0; a < MT; ++a)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int b = 0; b < NT; ++b)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int prow = (wave * MT + a) * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-        const int j = feat_of_row<D>(b * 32 + l32);
-        if (prow < D) {
-          const int i = feat_of_row<D>(prow);
-          af[i * (D + 1) + j] = acc[a][b][r] + (i == j ? 1.0f : 0.0f);
-        } else {
-          const int i = feat_of_row<D>(prow - D);
-          bw[mbase + (int64_t)i * D + j] = acc[a][b][r];
-        }
+        const int xr = (xg * MT + mt) * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+        const int j = (yh * NT + nt) * 32 + l32;
+        if (xr < D) minv[mbase + (int64_t)xr * D + j] = acc[mt][nt][r] + (xr == j ? 1.0f : 0.0f);   // I + A
+        else bw[mbase + (int64_t)(xr - D) * D + j] = acc[mt][nt][r];
       }
-  __syncthreads();
-  for (int e = tid; e < D * D; e += 256) minv[mbase + e] = af[(e / D) * (D + 1) + e % D];   // I + A, inverted later
 }
 
 template <int D>
@@ -184,7 +224,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   const size_t smem = GramSmem<D>::TOTAL;
   (void)hipFuncSetAttribute((const void*)vda_gram_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
-  hipLaunchKernelGGL(vda_gram_mfma_kernel<D>, dim3(s.T + 1, s.H), dim3(256), smem, st, (const bf16_t*)in.k,
+  hipLaunchKernelGGL(vda_gram_mfma_kernel<D>, dim3(s.T + 1, s.H), dim3(kThreads), smem, st, (const bf16_t*)in.k,
                      (const bf16_t*)in.v, in.beta, (const bf16_t*)in.text_kv, b.minv, b.bw, s.T, s.N, s.H, s.n_text,
                      s.anchors);
 }

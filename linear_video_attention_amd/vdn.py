@@ -17,6 +17,7 @@ VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_OUT_OF_MEMORY, VDN_ERR
 VDN_F32, VDN_BF16 = 0, 1
 VDN_FLAG_GENERIC_KERNELS = 1
 VDN_FLAG_SERIAL = 2
+VDN_FLAG_OVERLAP = 4
 VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV, VDN_BUF_BW = 0, 1, 2, 3
 STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total")
 
@@ -36,6 +37,8 @@ SIGNATURES = [
     ("vdn_profile_enable", _c_int, [_vp, _c_int]),
     ("vdn_profile_read", _c_int, [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]),
     ("vdn_plan_kernel_kind", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)]),
+    ("vdn_measure_mfma_bf16_tflops", _c_int, [_c_int, ctypes.POINTER(ctypes.c_double)]),
+    ("vdn_measure_copy_gbs", _c_int, [_c_size, ctypes.POINTER(ctypes.c_double)]),
 ]
 
 _lib = None
@@ -89,13 +92,29 @@ def vdn_scan_frames(T, C, anchors, t, direction):
     return [buf[i] for i in range(n)]
 
 
+def measure_mfma_bf16_tflops(iters=20000):
+    """Dense bf16 TFLOP/s of a tight MFMA loop on this GPU (on-box roofline reference)."""
+    x = ctypes.c_double()
+    _check(lib().vdn_measure_mfma_bf16_tflops(iters, ctypes.byref(x)), "vdn_measure_mfma_bf16_tflops")
+    return x.value
+
+
+def measure_copy_gbs(nbytes=1 << 30):
+    """Device-to-device copy GB/s (read + write) over ``nbytes`` (on-box HBM reference)."""
+    x = ctypes.c_double()
+    _check(lib().vdn_measure_copy_gbs(nbytes, ctypes.byref(x)), "vdn_measure_copy_gbs")
+    return x.value
+
+
 # ---- plan ----
 
-def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False):
+def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
+                    overlap=False):
     """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"."""
     dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
     h = _vp()
-    flags = (VDN_FLAG_GENERIC_KERNELS if generic else 0) | (VDN_FLAG_SERIAL if serial else 0)
+    flags = ((VDN_FLAG_GENERIC_KERNELS if generic else 0) | (VDN_FLAG_SERIAL if serial else 0)
+             | (VDN_FLAG_OVERLAP if overlap else 0))
     _check(lib().vdn_plan_create_ex(T, N, C, n_text, H, d, int(anchors), dt, flags, ctypes.byref(h)),
            "vdn_plan_create")
     return h.value
@@ -123,7 +142,8 @@ def vdn_forward(plan, q, k, v, beta, text_kv, gate_w, proj_w, out, stream=None):
 class Plan:
     """Owning wrapper of a plan with argument checks on torch tensors."""
 
-    def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False):
+    def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
+                 overlap=False):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("no GPU visible: the VDN layer runs only on the GPU")
@@ -132,7 +152,7 @@ class Plan:
         self.dtype = dtype
         self.torch_dtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         self.Nc = (T + C - 1) // C
-        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial)
+        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap)
 
     def close(self):
         if self.handle:

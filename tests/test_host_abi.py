@@ -23,7 +23,7 @@ def vdn():
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "vdn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(vdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol(vdn):
@@ -57,6 +57,22 @@ def test_invalid_plans_rejected_on_host(vdn, args, status):
     st = vdn.lib().vdn_plan_create(*args, ctypes.byref(h))
     assert st == status
     assert h.value is None
+
+
+@pytest.mark.parametrize("flags", [2 | 4, 8, 1 << 31])
+def test_invalid_plan_flags_rejected_on_host(vdn, flags):
+    """Serial and overlapped order together, or an unknown flag bit, are argument errors."""
+    h = ctypes.c_void_p(1234)
+    assert vdn.lib().vdn_plan_create_ex(4, 16, 2, 1, 1, 16, 1, 0, flags, ctypes.byref(h)) == -1
+    assert h.value is None
+
+
+def test_measurement_helpers_reject_bad_arguments(vdn):
+    x = ctypes.c_double()
+    assert vdn.lib().vdn_measure_mfma_bf16_tflops(0, ctypes.byref(x)) == -1
+    assert vdn.lib().vdn_measure_mfma_bf16_tflops(10, None) == -1
+    assert vdn.lib().vdn_measure_copy_gbs(0, ctypes.byref(x)) == -1
+    assert vdn.lib().vdn_measure_copy_gbs(1 << 20, None) == -1
 
 
 def test_null_arguments_rejected(vdn):
