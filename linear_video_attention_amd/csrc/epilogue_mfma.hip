@@ -6,18 +6,21 @@
 // Outputs": out = (sigmoid(q Wg0) * o_s) Wp0 + (sigmoid(q Wg1) * RMSNorm(o_l)) Wp1 (gate input q,
 // weights [in][out] shared by the heads, RMSNorm eps 1e-6 with unit weight).
 //
-// All products are computed transposed (channels x tokens) with v_mfma_f32_16x16x32_bf16, so the
-// small operand that is the same for every token of the workgroup -- the combined state S of the
-// frame's chunk and the four weight matrices -- is the A operand and stays in registers:
-//   * one workgroup = up to 512 tokens of one frame and one head, D/16 waves; wave w owns output
-//     channels [16w, 16w + 16) and holds rows [16w, 16w+16) of S (as bf16 hi + lo parts, so the
-//     readout keeps ~16 mantissa bits) and of Wg0^T, Wg1^T, Wp0^T, Wp1^T (pre-transposed once per
-//     forward by prep_weights_kernel);
-//   * tokens stream through LDS in tiles of 64 whose global operands (q, the o_s slice) are fetched
-//     two tiles ahead: q^T is the shared B operand of the readout and of both gates; the per-token
-//     RMS needs all channels, so each wave's partial sum of squares is exchanged through LDS; the
-//     gated branches x_s, x_l are exchanged through LDS, as bf16 hi + lo parts, as the B operand
-//     of the two projections.
+// RMSNorm scales each token's o_l by one number r = 1/sqrt(mean(o_l^2) + eps), and that scalar
+// commutes with the projection: (g_l * o_l * r) Wp1 = r ((g_l * o_l) Wp1).  So the work splits into
+// two stages that never wait for each other inside a tile:
+//   * readout waves (0-3): per 64-token tile, o_l^T, (q Wg0)^T, (q Wg1)^T = [S; Wg0^T; Wg1^T] q^T,
+//     then x_s = sigmoid(q Wg0) * o_s and z_l = sigmoid(q Wg1) * o_l, written to LDS (z_l as bf16
+//     hi + lo parts), plus each wave's partial sum of o_l^2 per token;
+//   * projection waves (4-7): one tile behind, out^T = Wp0^T x_s^T + r (Wp1^T z_l^T), with r from
+//     the four partial sums, stored as bf16.
+// One barrier per tile hands the tile over (double-buffered x planes and partials).  Every product
+// is computed transposed (channels x tokens) with v_mfma_f32_16x16x32_bf16 so that the matrix
+// shared by all tokens -- S (as bf16 hi + lo, since the readout needs ~16 mantissa bits) and the
+// pre-transposed weights -- is the A operand and stays in registers: each wave owns 16 CT
+// channels.  q tiles are copied straight into LDS (global_load_lds, three buffers, issued two
+// tiles ahead by the readout waves, which are their only readers); all LDS tiles are token rows
+// with 16-byte chunks XOR-swizzled so the 16-lane fragment reads are bank-conflict free.
 #include "dev_common.h"
 #include "vdn_internal.h"
 
@@ -25,16 +28,34 @@ namespace vdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kTileTok = 64;
-#ifndef VDN_EPI_TOK
-#define VDN_EPI_TOK 512
-#endif
-constexpr int kTokPerWG = VDN_EPI_TOK;
+constexpr int kSub = kTileTok / 16;      // 16-token column tiles per tile
+constexpr int kTokPerWG = 768;
+constexpr int kQBufs = 3;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+// 16-byte chunk c of token row r sits at chunk position c ^ swz(r): the 16 rows read by one
+// 16-lane fragment load then cover all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r >> 1) & 7;
+}
+
+template <int D>
+struct EpiSmem {
+  static constexpr int ROW = 2 * D;                          // bytes per token row
+  static constexpr int PLANE = kTileTok * ROW;
+  static constexpr int Q_OFF = 0;                            // kQBufs q tiles
+  static constexpr int X_OFF = kQBufs * PLANE;               // [2][3] planes: x_s, z_l hi, z_l lo
+  static constexpr int P_OFF = X_OFF + 6 * PLANE;            // [2][4 waves][kTileTok] floats
+  static constexpr int TOTAL = P_OFF + 2 * 4 * kTileTok * 4;
+};
 
 // W^T for gate_w[0], gate_w[1], proj_w[0], proj_w[1]: wt[m][j][i] = W_m[i][j]
 __global__ __launch_bounds__(256) void prep_weights_kernel(const bf16_t* __restrict__ gate_w,
@@ -48,180 +69,213 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(const bf16_t* __restr
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ o_s, const float* __restrict__ states,
-    const bf16_t* __restrict__ wt, bf16_t* __restrict__ out, int T, int N, int H, int C, int Nc, int anchors,
-    int wg_per_frame) {
-  constexpr int NW = D / 16;              // waves
-  constexpr int KS = D / 32;              // k-steps of 32
-  constexpr int NT = kTileTok / 16;       // 16-token column tiles per tile
-  constexpr int NTHR = NW * 64;
-  constexpr int QCH = kTileTok * D / 8;   // 16-byte chunks of a q tile
-  constexpr int QPT = (QCH + NTHR - 1) / NTHR;
-  __shared__ __attribute__((aligned(16))) bf16_t qtile[kTileTok][D + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t xtile[4][kTileTok][D + 8];   // x_s hi, x_s lo, x_l hi, x_l lo
-  __shared__ float part[NW][kTileTok];
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-  const int wg = blockIdx.x;
-  const int h = blockIdx.y;
+template <int D>
+__global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __restrict__ q,
+                                                            const bf16_t* __restrict__ o_s,
+                                                            const float* __restrict__ states,
+                                                            const bf16_t* __restrict__ wt, bf16_t* __restrict__ out,
+                                                            int T, int N, int H, int C, int Nc, int anchors,
+                                                            int wg_per_frame) {
+  using SM = EpiSmem<D>;
+  constexpr int CT = D / 64;              // 16-channel tiles per wave (4 waves per stage cover D)
+  constexpr int KS = D / 32;              // k-steps of 32
+  constexpr int CH = D / 8;               // 16-byte chunks per token row
+  constexpr int ROWS_PER_KB = 1024 / SM::ROW;
+  constexpr int QDMA = SM::PLANE / 1024 / 4;      // q DMA instructions per readout wave per tile
+  constexpr int kVmcntTile = 0x0F70 | QDMA;       // s_waitcnt vmcnt(one tile's q loads of a wave)
+  static_assert(QDMA < 16, "vmcnt field");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int wg = blockIdx.x, h = blockIdx.y;
   const int t = wg / wg_per_frame;
   const int tok_begin = (wg % wg_per_frame) * kTokPerWG;
   const int tok_end = min(N, tok_begin + kTokPerWG);
+  const int ntiles = (tok_end - tok_begin + kTileTok - 1) / kTileTok;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, lg = lane >> 4;         // lane group 0..3
-  const int j0 = wave * 16;
-
-  const bool bnd = anchors && (t == 0 || t == T - 1);
-  const int slot = bnd ? Nc : t / C;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const bool readout = wave < 4;
+  const int sw = wave & 3;                 // wave index within its stage
   const int64_t DD = (int64_t)D * D;
-  const float* sf = states + ((int64_t)slot * H + h) * DD;
-  const float* sr = states + (((int64_t)(Nc + 1) + slot) * H + h) * DD;
+  auto tok_row = [&](int n) { return ((int64_t)t * N + n) * H + h; };
 
-  // ---- A fragments: row j0 + l16, k = ks*32 + lg*8 .. +8 ----
-  bf16x8 s_hi[KS], s_lo[KS], wg0[KS], wg1[KS], wp0[KS], wp1[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int j = j0 + l16, i0 = ks * 32 + lg * 8;
-    const f32x4* a = reinterpret_cast<const f32x4*>(sf + (int64_t)j * D + i0);
-    const f32x4* b = reinterpret_cast<const f32x4*>(sr + (int64_t)j * D + i0);
-    const f32x4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float sv = e < 4 ? a0[e] + b0[e] : a1[e - 4] + b1[e - 4];
-      const __bf16 hi = (__bf16)sv;
-      s_hi[ks][e] = hi;
-      s_lo[ks][e] = (__bf16)(sv - (float)hi);
-    }
-    wg0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 0 * DD + (int64_t)j * D + i0));
-    wg1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 1 * DD + (int64_t)j * D + i0));
-    wp0[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 2 * DD + (int64_t)j * D + i0));
-    wp1[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 3 * DD + (int64_t)j * D + i0));
-  }
+  // fragment byte offset of (token row r, channels k0 .. k0+7) in a swizzled tile
+  auto frag_off = [&](int r, int k0) { return r * SM::ROW + (((k0 >> 3) ^ swz<D>(r)) << 4); };
 
-  // Global operands of a tile (q tile chunks, this lane's o_s slice), fetched two tiles ahead.
-  struct Pre {
-    u32x4 q[QPT];
-    uint2 os[NT];
-  };
-  auto fetch = [&](int tok0, Pre& pr) {
+  // q DMA (readout waves): instruction i of stage wave sw fills token rows
+  // (i*4 + sw)*ROWS_PER_KB + lane / CH; the lane fetches chunk (lane % CH) ^ swz(row).  Rows past the
+  // last token re-read the last token (their results are never stored).
+  auto issue_q = [&](int it) {
+    unsigned char* qb = smem + SM::Q_OFF + (it % kQBufs) * SM::PLANE;
+    const int tok0 = tok_begin + it * kTileTok;
 #pragma unroll
-    for (int c = 0; c < QPT; ++c) {
-      const int e = c * NTHR + tid;
-      u32x4 val = {0, 0, 0, 0};
-      if (e < QCH) {
-        const int r = e / (D / 8), cc = e % (D / 8);
-        const int n = tok0 + r;
-        if (n < tok_end) val = *reinterpret_cast<const u32x4*>(q + (((int64_t)t * N + n) * H + h) * D + cc * 8);
-      }
-      pr.q[c] = val;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = tok0 + nt * 16 + l16;
-      pr.os[nt] = n < tok_end ? *reinterpret_cast<const uint2*>(o_s + (((int64_t)t * N + n) * H + h) * D + j0 + lg * 4)
-                              : make_uint2(0, 0);
+    for (int i = 0; i < QDMA; ++i) {
+      const int blk = i * 4 + sw;
+      const int row = blk * ROWS_PER_KB + lane / CH;
+      const int n = min(tok0 + row, tok_end - 1);
+      const int c = (lane % CH) ^ swz<D>(row);
+      __builtin_amdgcn_global_load_lds((gptr_t)(q + tok_row(n) * D + c * 8), (lptr_t)(qb + blk * 1024), 16, 0, 0);
     }
   };
 
-  auto process = [&](int tok0, const Pre& pr) {
+  if (readout) {
+    // ---- readout waves: channels [16 CT sw, +16 CT) ----
+    // o_s of this lane's outputs of a tile: channels 16 (sw CT + ct) + 4 lg .. +4, token 16 sub + l16
+    auto fetch_os = [&](int it, uint2 (&os)[CT][kSub]) {
+      const int tok0 = tok_begin + it * kTileTok;
 #pragma unroll
-    for (int c = 0; c < QPT; ++c) {
-      const int e = c * NTHR + tid;
-      if (e < QCH) {
-        const int r = e / (D / 8), cc = e % (D / 8);
-        *reinterpret_cast<u32x4*>(&qtile[r][cc * 8]) = pr.q[c];
-      }
-    }
-    __syncthreads();                                         // q tile ready (previous tile's readers
-                                                             // passed the previous 2nd and 3rd barrier)
-    f32x4 ol[NT], gs[NT], gl[NT];
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      ol[nt] = f32x4{0, 0, 0, 0};
-      gs[nt] = f32x4{0, 0, 0, 0};
-      gl[nt] = f32x4{0, 0, 0, 0};
+        for (int sub = 0; sub < kSub; ++sub) {
+          const int n = min(tok0 + sub * 16 + l16, tok_end - 1);
+          os[ct][sub] = *reinterpret_cast<const uint2*>(o_s + tok_row(n) * D + (sw * CT + ct) * 16 + lg * 4);
+        }
+    };
+    // the first tiles' loads go out before the (once per workgroup) state and weight loads
+    uint2 osa[CT][kSub], osb[CT][kSub];
+    issue_q(0);
+    fetch_os(0, osa);
+    if (ntiles > 1) issue_q(1);
+    const bool bnd = anchors && (t == 0 || t == T - 1);
+    const int slot = bnd ? Nc : t / C;
+    const float* sf = states + ((int64_t)slot * H + h) * DD;
+    const float* sr = states + (((int64_t)(Nc + 1) + slot) * H + h) * DD;
+    bf16x8 s_hi[CT][KS], s_lo[CT][KS], wg0[CT][KS], wg1[CT][KS];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qb = as_bf16x8(*reinterpret_cast<const u32x4*>(&qtile[nt * 16 + l16][ks * 32 + lg * 8]));
-        ol[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_hi[ks], qb, ol[nt], 0, 0, 0);
-        ol[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_lo[ks], qb, ol[nt], 0, 0, 0);
-        gs[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg0[ks], qb, gs[nt], 0, 0, 0);
-        gl[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg1[ks], qb, gl[nt], 0, 0, 0);
+        const int j = (sw * CT + ct) * 16 + l16, i0 = ks * 32 + lg * 8;
+        const f32x4* a = reinterpret_cast<const f32x4*>(sf + (int64_t)j * D + i0);
+        const f32x4* b = reinterpret_cast<const f32x4*>(sr + (int64_t)j * D + i0);
+        const f32x4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = e < 4 ? a0[e] + b0[e] : a1[e - 4] + b1[e - 4];
+          const __bf16 hi = (__bf16)sv;
+          s_hi[ct][ks][e] = hi;
+          s_lo[ct][ks][e] = (__bf16)(sv - (float)hi);
+        }
+        wg0[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 0 * DD + (int64_t)j * D + i0));
+        wg1[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 1 * DD + (int64_t)j * D + i0));
       }
-    }
-    // partial sums of squares of o_l over this wave's 16 channels, per token
+    // Issue order per tile: the o_s loads of the next tile, then the q DMA of the tile after; the
+    // wait for those o_s loads (before their registers are used) then leaves the DMA in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // q tiles 0 (and 1) landed
+    __syncthreads();                                   // q tile 0 complete for every wave
+    for (int it = 0; it <= ntiles; ++it) {
+      if (it < ntiles) {
+        if (it + 1 < ntiles) fetch_os(it + 1, osb);
+        if (it + 2 < ntiles) issue_q(it + 2);          // its buffer held tile it-1, read in the last iteration
+        const unsigned char* qb = smem + SM::Q_OFF + (it % kQBufs) * SM::PLANE;
+        unsigned char* xb = smem + SM::X_OFF + (it & 1) * 3 * SM::PLANE;
+        float* part = reinterpret_cast<float*>(smem + SM::P_OFF) + (it & 1) * 4 * kTileTok + sw * kTileTok;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float ss = ol[nt][0] * ol[nt][0] + ol[nt][1] * ol[nt][1] + ol[nt][2] * ol[nt][2] + ol[nt][3] * ol[nt][3];
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      if (lg == 0) part[wave][nt * 16 + l16] = ss;
-    }
-    __syncthreads();                                         // partial sums ready
-    // gated branches, as bf16 hi + lo parts (the projection weights are exact bf16, so the two
-    // projections keep ~fp32 accuracy)
+        for (int sub = 0; sub < kSub; ++sub) {
+          const int r = sub * 16 + l16;
+          f32x4 ol[CT], gs[CT], gl[CT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float ss = 0.f;
+          for (int ct = 0; ct < CT; ++ct) ol[ct] = gs[ct] = gl[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) ss += part[ww][nt * 16 + l16];
-      const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + 1e-6f);
-      __bf16 xsh[4], xsl[4], xlh[4], xll[4];
-      const uint32_t o01 = pr.os[nt].x, o23 = pr.os[nt].y;
-      const float osv[4] = {__uint_as_float(o01 << 16), __uint_as_float(o01 & 0xFFFF0000u),
-                            __uint_as_float(o23 << 16), __uint_as_float(o23 & 0xFFFF0000u)};
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qb + frag_off(r, ks * 32 + lg * 8));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xs = fast_sigmoid(gs[nt][e]) * osv[e];
-        const float xl = fast_sigmoid(gl[nt][e]) * ol[nt][e] * rinv;
-        xsh[e] = (__bf16)xs;
-        xsl[e] = (__bf16)(xs - (float)xsh[e]);
-        xlh[e] = (__bf16)xl;
-        xll[e] = (__bf16)(xl - (float)xlh[e]);
+            for (int ct = 0; ct < CT; ++ct) {
+              ol[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_hi[ct][ks], qf, ol[ct], 0, 0, 0);
+              ol[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_lo[ct][ks], qf, ol[ct], 0, 0, 0);
+              gs[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg0[ct][ks], qf, gs[ct], 0, 0, 0);
+              gl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg1[ct][ks], qf, gl[ct], 0, 0, 0);
+            }
+          }
+          // outputs: channel 16 (sw CT + ct) + 4 lg + e, token row r
+          float ss = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const uint32_t o01 = osa[ct][sub].x, o23 = osa[ct][sub].y;
+            const float osv[4] = {__uint_as_float(o01 << 16), __uint_as_float(o01 & 0xFFFF0000u),
+                                  __uint_as_float(o23 << 16), __uint_as_float(o23 & 0xFFFF0000u)};
+            bf16x4 xs, zh, zl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ss += ol[ct][e] * ol[ct][e];
+              const float xsv = fast_sigmoid(gs[ct][e]) * osv[e];
+              const float zlv = fast_sigmoid(gl[ct][e]) * ol[ct][e];
+              xs[e] = (__bf16)xsv;
+              zh[e] = (__bf16)zlv;
+              zl[e] = (__bf16)(zlv - (float)zh[e]);
+            }
+            const int ch = (sw * CT + ct) * 16 + lg * 4;
+            const int off = frag_off(r, ch) + (ch & 4) * 2;
+            *reinterpret_cast<bf16x4*>(xb + off) = xs;
+            *reinterpret_cast<bf16x4*>(xb + SM::PLANE + off) = zh;
+            *reinterpret_cast<bf16x4*>(xb + 2 * SM::PLANE + off) = zl;
+          }
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          if (lg == 0) part[r] = ss;
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int sub = 0; sub < kSub; ++sub) osa[ct][sub] = osb[ct][sub];
       }
-      const int row = nt * 16 + l16, c0 = j0 + lg * 4;
-      *reinterpret_cast<uint2*>(&xtile[0][row][c0]) = __builtin_bit_cast(uint2, xsh);
-      *reinterpret_cast<uint2*>(&xtile[1][row][c0]) = __builtin_bit_cast(uint2, xsl);
-      *reinterpret_cast<uint2*>(&xtile[2][row][c0]) = __builtin_bit_cast(uint2, xlh);
-      *reinterpret_cast<uint2*>(&xtile[3][row][c0]) = __builtin_bit_cast(uint2, xll);
+      if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntTile);   // q tile it+1 landed
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();                                 // tile it handed over; q tile it+1 complete
     }
-    __syncthreads();                                         // gated branches ready
+  } else {
+    // ---- projection waves: channels [16 CT sw, +16 CT) ----
+    bf16x8 wp0[CT][KS], wp1[CT][KS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 o = {0, 0, 0, 0};
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int row = nt * 16 + l16, k0 = ks * 32 + lg * 8;
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            wp0[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[0][row][k0])), o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            wp0[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[1][row][k0])), o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            wp1[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[2][row][k0])), o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            wp1[ks], as_bf16x8(*reinterpret_cast<const u32x4*>(&xtile[3][row][k0])), o, 0, 0, 0);
+        const int j = (sw * CT + ct) * 16 + l16, i0 = ks * 32 + lg * 8;
+        wp0[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 2 * DD + (int64_t)j * D + i0));
+        wp1[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 3 * DD + (int64_t)j * D + i0));
       }
-      const int n = tok0 + nt * 16 + l16;
-      if (n < tok_end) {
-        __bf16 ov[4];
+    __syncthreads();
+    for (int it = 0; it <= ntiles; ++it) {
+      if (it >= 1) {
+        const int pt = it - 1;                         // the tile handed over at the last barrier
+        const unsigned char* xb = smem + SM::X_OFF + (pt & 1) * 3 * SM::PLANE;
+        const float* part = reinterpret_cast<const float*>(smem + SM::P_OFF) + (pt & 1) * 4 * kTileTok;
+        const int tok0 = tok_begin + pt * kTileTok;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)o[e];
-        *reinterpret_cast<uint2*>(out + (((int64_t)t * N + n) * H + h) * D + j0 + lg * 4) = __builtin_bit_cast(uint2, ov);
+        for (int sub = 0; sub < kSub; ++sub) {
+          const int r = sub * 16 + l16;
+          f32x4 as[CT], al[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) as[ct] = al[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int off = frag_off(r, ks * 32 + lg * 8);
+            const bf16x8 xs = *reinterpret_cast<const bf16x8*>(xb + off);
+            const bf16x8 zh = *reinterpret_cast<const bf16x8*>(xb + SM::PLANE + off);
+            const bf16x8 zl = *reinterpret_cast<const bf16x8*>(xb + 2 * SM::PLANE + off);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              as[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp0[ct][ks], xs, as[ct], 0, 0, 0);
+              al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ct][ks], zh, al[ct], 0, 0, 0);
+              al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ct][ks], zl, al[ct], 0, 0, 0);
+            }
+          }
+          const float ss = part[r] + part[kTileTok + r] + part[2 * kTileTok + r] + part[3 * kTileTok + r];
+          const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + 1e-6f);
+          const int n = tok0 + r;
+          if (n < tok_end) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              bf16x4 ov;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(as[ct][e] + rinv * al[ct][e]);
+              *reinterpret_cast<bf16x4*>(out + tok_row(n) * D + (sw * CT + ct) * 16 + lg * 4) = ov;
+            }
+          }
+        }
       }
-    }
-  };
-
-  // two register sets, fetched two tiles ahead of their use
-  Pre pa, pb;
-  fetch(tok_begin, pa);
-  fetch(tok_begin + kTileTok, pb);
-  for (int tok0 = tok_begin; tok0 < tok_end; tok0 += 2 * kTileTok) {
-    process(tok0, pa);
-    if (tok0 + 2 * kTileTok < tok_end) fetch(tok0 + 2 * kTileTok, pa);
-    if (tok0 + kTileTok < tok_end) {
-      process(tok0 + kTileTok, pb);
-      if (tok0 + 3 * kTileTok < tok_end) fetch(tok0 + 3 * kTileTok, pb);
+      __syncthreads();
     }
   }
 }
@@ -229,10 +283,12 @@ __global__ __launch_bounds__(D * 4) void epilogue_mfma_kernel(
 template <int D>
 void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   const int wg_per_frame = (s.N + kTokPerWG - 1) / kTokPerWG;
-  dim3 grid(s.T * wg_per_frame, s.H);
-  epilogue_mfma_kernel<D><<<grid, D * 4, 0, st>>>((const bf16_t*)in.q, (const bf16_t*)b.os, b.states, b.wt,
-                                                  (bf16_t*)in.out, s.T, s.N, s.H, s.C, s.Nc, s.anchors,
-                                                  wg_per_frame);
+  const size_t smem = EpiSmem<D>::TOTAL;
+  (void)hipFuncSetAttribute((const void*)epilogue_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+  hipLaunchKernelGGL(epilogue_mfma_kernel<D>, dim3(s.T * wg_per_frame, s.H), dim3(512), smem, st,
+                     (const bf16_t*)in.q, (const bf16_t*)b.os, b.states, b.wt, (bf16_t*)in.out, s.T, s.N, s.H, s.C,
+                     s.Nc, s.anchors, wg_per_frame);
 }
 
 }  // namespace

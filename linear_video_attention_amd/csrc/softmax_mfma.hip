@@ -41,7 +41,15 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kBK = 64;        // keys per tile
-constexpr int kBQ = 256;       // queries per workgroup
+#ifndef VDN_SOFTMAX_BQ
+#define VDN_SOFTMAX_BQ 256
+#endif
+#ifndef VDN_SOFTMAX_SIMPLE
+#define VDN_SOFTMAX_SIMPLE 0
+#endif
+constexpr int kBQ = VDN_SOFTMAX_BQ;   // queries per workgroup
+constexpr bool kSimpleLoop = VDN_SOFTMAX_SIMPLE != 0;
+constexpr int kStages = kSimpleLoop ? 2 : 3;
 // Wave shape: QSUB 32-query column tiles per wave, kBQ / (32 QSUB) waves per workgroup.
 #ifndef VDN_SOFTMAX_QSUB
 #define VDN_SOFTMAX_QSUB 1
@@ -93,7 +101,7 @@ struct Params {
 // FALLBACK = false: fixed exponent reference, writes its workgroup's flag (1 = redo).
 // FALLBACK = true : online maximum; runs only the workgroups flagged by the first launch.
 template <int D, bool FALLBACK>
-__global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) {
+__global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(Params P) {
   using SM = Smem<D>;
   constexpr int KS = D / 16;          // k-steps of the QK^T contraction
   constexpr int DT = D / 32;          // 32-row d tiles of O^T
@@ -356,14 +364,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) 
           oacc[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][s], pf[qs][s], oacc[qs][dt], 0, 0, 0);
   };
 
-  {
-    int key0, valid;
-    tile_at(0, key0, valid);
-    issue_tile(key0, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  __syncthreads();
-
   auto next_tile = [&](int it) {
     if (it + 1 < ntiles) {
       int nkey0, nvalid;
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) 
     }
   };
 
-  if constexpr (!FALLBACK) {
+  if constexpr (!FALLBACK && !kSimpleLoop) {
     // Software-pipelined over tiles with three LDS stages: iteration i computes the scores of
     // tile i+1 (MFMA) while it turns the scores of tile i into probabilities (VALU), then
     // accumulates P.V of tile i.  The two streams are independent inside the iteration, so one
@@ -440,6 +440,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) 
       accumulate(vb, 1, p1);
     }
   } else {
+    {
+      int key0, valid;
+      tile_at(0, key0, valid);
+      issue_tile(key0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       next_tile(it);
       int key0, valid;
@@ -452,7 +459,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_mfma_kernel(Params P) 
         bf16x8 pf[kQSub][2];
         scores(kb, kt, sacc);
         if (valid < kBK) mask(kt, valid, sacc);
-        online_max(sacc);
+        if constexpr (FALLBACK) online_max(sacc);
         probs(sacc, pf);
         accumulate(vb, kt, pf);
       }
@@ -507,7 +514,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   P.per_xcd = (P.n_int_wg + 7) / 8;
   P.c_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int grid = softmax_grid(s);
-  const size_t smem = 3 * Smem<D>::STAGE;
+  const size_t smem = kStages * Smem<D>::STAGE;
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -57,6 +57,10 @@ RAGGED = [
     (64, 11, 320, 4, 2, 128, "bf16", True),      # several 256-query tiles + tail
     (7, 12, 24, 3, 2, 32, "bf16", True),         # d = 32 (generic kernels)
     (2, 10, 20, 3, 2, 16, "bf16", True),         # d = 16, N % 8 != 0 (generic kernels)
+    (16, 9, 64, 1, 2, 128, "bf16", True),        # one frame per chunk: boundary chunks map to identity
+    (8, 4, 96, 8, 1, 128, "bf16", True),         # a single chunk: no chunk-scan step
+    (0, 15, 64, 7, 1, 64, "bf16", False),        # C = 7, anchors off, no text
+    (4, 3, 800, 2, 1, 128, "bf16", True),        # two epilogue workgroups per frame, short last one
     (9, 11, 37, 3, 2, 64, "fp32", True),         # fp32, ragged everything
     (1, 6, 5, 2, 1, 128, "fp32", False),         # fp32, d = 128, anchors off
 ]
