@@ -11,9 +11,10 @@
 //     SIMD so one wave's exponentials overlap the other's MFMAs (measured faster on gfx950 than
 //     4 waves x 64 queries at one wave per SIMD, which halves the LDS reads per MFMA but leaves
 //     every LDS and MFMA latency exposed);
-//   * key tiles of 64 keys are loaded straight from global memory into LDS (global_load_lds,
-//     double buffered; K as [key][d], V transposed as [d][key], both XOR-swizzled so the 16-byte
-//     fragment reads are bank-conflict free) and processed as two 32-key halves;
+//   * key tiles of 64 keys are loaded straight from global memory into LDS (global_load_lds, four
+//     stages: up to three tiles in flight; K as [key][d], V transposed as [d][key], both
+//     XOR-swizzled so the 16-byte fragment reads are bank-conflict free) and processed as two
+//     32-key halves;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as rows, queries as columns) so that each
 //     lane ends up holding 16 consecutive keys of one query -- the row permutation used when the
 //     K fragments are read makes those keys contiguous;  O^T += V^T P^T with the same instruction,
@@ -48,8 +49,13 @@ constexpr int kBK = 64;        // keys per tile
 #define VDN_SOFTMAX_SIMPLE 0
 #endif
 constexpr int kBQ = VDN_SOFTMAX_BQ;   // queries per workgroup
+#ifndef VDN_SOFTMAX_STAGES
+#define VDN_SOFTMAX_STAGES 4
+#endif
 constexpr bool kSimpleLoop = VDN_SOFTMAX_SIMPLE != 0;
-constexpr int kStages = kSimpleLoop ? 2 : 3;
+constexpr int kPipeStages = VDN_SOFTMAX_STAGES;     // LDS stages of the pipelined loop (3 or 4)
+constexpr int kStages = kSimpleLoop ? 2 : kPipeStages;
+static_assert(kPipeStages == 3 || kPipeStages == 4, "pipeline stages");
 // Wave shape: QSUB 32-query column tiles per wave, kBQ / (32 QSUB) waves per workgroup.
 #ifndef VDN_SOFTMAX_QSUB
 #define VDN_SOFTMAX_QSUB 1
@@ -232,6 +238,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   constexpr int K_ROWS_PER_KB = 1024 / (D * 2);
   static_assert(K_INSTR + V_INSTR < 16, "vmcnt field");
   constexpr int kVmcntTile = 0x0F70 | (K_INSTR + V_INSTR);   // s_waitcnt vmcnt(loads of one tile)
+  constexpr int kVmcntTile2 = 0x0F70 | (2 * (K_INSTR + V_INSTR));   // ... of two tiles
+  static_assert(2 * (K_INSTR + V_INSTR) < 16, "vmcnt field");
   uint32_t koff[K_INSTR], voff[V_INSTR];
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
@@ -373,34 +381,35 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   };
 
   if constexpr (!FALLBACK && !kSimpleLoop) {
-    // Software-pipelined over tiles with three LDS stages: iteration i computes the scores of
+    // Software-pipelined over tiles with kPipeStages LDS stages: iteration i computes the scores of
     // tile i+1 (MFMA) while it turns the scores of tile i into probabilities (VALU), then
     // accumulates P.V of tile i.  The two streams are independent inside the iteration, so one
     // wave keeps the matrix pipe and the vector ALU busy at the same time.  Full tiles come before
     // partial ones (tile_at), so masking is a uniform branch outside the overlapped block.
+    // Tiles are loaded kPipeStages - 1 ahead of the one whose scores are computed.
+    constexpr int S = kPipeStages;
+    auto wait_younger = [&](int younger) {          // wait until at most `younger` tiles are in flight
+      if (younger >= 2) __builtin_amdgcn_s_waitcnt(kVmcntTile2);
+      else if (younger == 1) __builtin_amdgcn_s_waitcnt(kVmcntTile);
+      else __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    };
     f32x16 sc0[kQSub], sc1[kQSub];          // scores of the tile being finished
-    {
+    for (int i = 0; i < S - 1 && i < ntiles; ++i) {
       int key0, valid;
-      tile_at(0, key0, valid);
-      issue_tile(key0, 0);
-      if (ntiles > 1) {
-        tile_at(1, key0, valid);
-        issue_tile(key0, 1);
-        __builtin_amdgcn_s_waitcnt(kVmcntTile);      // tile 0 landed, tile 1 may still be in flight
-      } else {
-        __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      }
+      tile_at(i, key0, valid);
+      issue_tile(key0, i);
     }
+    wait_younger(min(ntiles, S - 1) - 1);           // tile 0 landed
     __syncthreads();
     scores(smem, 0, sc0);
     scores(smem, 1, sc1);
     for (int it = 0; it + 1 < ntiles; ++it) {
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);       // tile it+1 landed
-      __syncthreads();                              // ... for every wave; stage (it+2)%3 is free
-      if (it + 2 < ntiles) {
+      wait_younger(min(ntiles - 1, it + S - 2) - (it + 1));   // tile it+1 landed
+      __syncthreads();                              // ... for every wave; stage (it-1)%S is free
+      if (it + S - 1 < ntiles) {
         int nkey0, nvalid;
-        tile_at(it + 2, nkey0, nvalid);
-        issue_tile(nkey0, (it + 2) % 3);
+        tile_at(it + S - 1, nkey0, nvalid);
+        issue_tile(nkey0, (it + S - 1) % S);
       }
       int key0, valid;
       tile_at(it, key0, valid);
@@ -408,8 +417,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
         mask(0, valid, sc0);
         mask(1, valid, sc1);
       }
-      const unsigned char* kn = smem + ((it + 1) % 3) * SM::STAGE;
-      const unsigned char* vb = smem + (it % 3) * SM::STAGE + SM::K_BYTES;
+      const unsigned char* kn = smem + ((it + 1) % S) * SM::STAGE;
+      const unsigned char* vb = smem + (it % S) * SM::STAGE + SM::K_BYTES;
       f32x16 sn0[kQSub], sn1[kQSub];
       bf16x8 p0[kQSub][2], p1[kQSub][2];
       scores(kn, 0, sn0);
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
         mask(0, valid, sc0);
         mask(1, valid, sc1);
       }
-      const unsigned char* vb = smem + (it % 3) * SM::STAGE + SM::K_BYTES;
+      const unsigned char* vb = smem + (it % S) * SM::STAGE + SM::K_BYTES;
       bf16x8 p0[kQSub][2], p1[kQSub][2];
       probs(sc0, p0);
       probs(sc1, p1);
