@@ -13,7 +13,9 @@ It is written independently of ``vdn_oracle`` so the two can check each other:
   S k_u ~ v_u plus the proximity term ||S - S_bar||_F^2 -- with a generic least-squares routine on
   the stacked system, never through the closed form;
 * each query frame's forward and reverse states are rebuilt from the text state in fresh loops
-  over the frames the rule assigns to it (no reuse between query frames).
+  over the frames the rule assigns to it (no reuse between query frames);
+* with a decay gate alpha ``[T, H, d]`` the proximity target of frame f is the inherited state
+  times the diagonal matrix of alpha_f (a matrix product here).
 
 [VDN] = "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models" (openvdn.github.io).
 """
@@ -72,8 +74,10 @@ def lstsq_update(s_bar, keys, vals, weights):
     return sol.T
 
 
-def linear_dense(q, k, v, beta, text_k, text_v, T, N, C, anchors):
+def linear_dense(q, k, v, beta, text_k, text_v, T, N, C, anchors, alpha=None):
     TN, H, d = q.shape
+    def inherited(s, f, h):
+        return s if alpha is None else s @ np.diag(np.asarray(alpha[f, h], np.float64))
     n_text = text_k.shape[0]
     out = np.zeros(q.shape)
     bset = (0, T - 1) if anchors else ()
@@ -87,11 +91,13 @@ def linear_dense(q, k, v, beta, text_k, text_v, T, N, C, anchors):
                 for f in range(T):                       # frames before the window, nearest last
                     if f not in bset and f // C < c - 1:
                         sl = slice(f * N, (f + 1) * N)
-                        fwd = lstsq_update(fwd, k[sl, h], v[sl, h], beta[n_text + f * N:n_text + (f + 1) * N, h])
+                        fwd = lstsq_update(inherited(fwd, f, h), k[sl, h], v[sl, h],
+                                           beta[n_text + f * N:n_text + (f + 1) * N, h])
                 for f in range(T - 1, -1, -1):           # frames after the window, nearest last
                     if f not in bset and f // C > c + 1:
                         sl = slice(f * N, (f + 1) * N)
-                        rev = lstsq_update(rev, k[sl, h], v[sl, h], beta[n_text + f * N:n_text + (f + 1) * N, h])
+                        rev = lstsq_update(inherited(rev, f, h), k[sl, h], v[sl, h],
+                                           beta[n_text + f * N:n_text + (f + 1) * N, h])
             for n in range(N):
                 i = t * N + n
                 out[i, h] = fwd @ q[i, h] + rev @ q[i, h]
@@ -101,7 +107,8 @@ def linear_dense(q, k, v, beta, text_k, text_v, T, N, C, anchors):
 def layer_dense(inp, T, N, C, anchors=True, eps=1e-6):
     q = inp["q"]
     o_s = softmax_dense(q, inp["k"], inp["v"], inp["text_k"], inp["text_v"], T, N, C, anchors)
-    o_l = linear_dense(q, inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"], T, N, C, anchors)
+    o_l = linear_dense(q, inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"], T, N, C, anchors,
+                       inp.get("alpha"))
     q64 = q.astype(np.float64)
     gw = inp["gate_w"].astype(np.float64)
     pw = inp["proj_w"].astype(np.float64)

@@ -10,7 +10,8 @@ Sources (cited by page title and section; no other document is used):
 * [VDN] "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models" (openvdn.github.io).
   Sections: "Local Softmax and Long-Range Linear Memory", "Gating the Softmax and Linear Branch
   Outputs", "Video Delta Attention: A Frame-Wise Solution" with its sub-part "From independent
-  token updates to one frame-wise solve", "Stability of the Inherited State".
+  token updates to one frame-wise solve" (and the review of the token-wise rule before it, which
+  defines the channel-wise decay of the inherited state), "Stability of the Inherited State".
 * [FTP] "Faster Than It Plays: Video DeltaNet Generates 14 Seconds of 768p Video in 11 Seconds"
   (ai-blog.deepmagic.app), section "Two branches instead of one", which prints the closed-form
   frame update S_t = (S_bar + B)(I + A)^-1 in text.
@@ -32,7 +33,10 @@ Readings of points the pages leave open (each one is also listed in the design n
   (solve at full beta, then halve the state) is kept as ``text_mode="half_state"``;
 * boundary query frames read only the text part of the linear memory (both scans empty), so no
   video frame reaches them twice;
-* decay alpha == 1 (the inherited state is the previous state);
+* decay: none by default (alpha == 1, the inherited state is the previous state); with an alpha
+  argument ``[T, H, d]``, writing frame f first decays the inherited state channel-wise,
+  S_bar = S Diag(alpha_f), in either scan direction (the same alpha_f for both); the text
+  initialisation starts from the zero state and is unaffected;
 * the linear-branch output is RMS-normalised over d with eps = 1e-6 and unit weight, gated by
   sigmoid(q @ W_gate[1]); the softmax branch is gated by sigmoid(q @ W_gate[0]); each gated
   branch goes through its own projection and the two are summed (no residual).
@@ -140,6 +144,14 @@ def frame_stats(kf: np.ndarray, vf: np.ndarray, bf: np.ndarray):
     return a, b
 
 
+def decay(s: np.ndarray, alpha_f) -> np.ndarray:
+    """The inherited state S_bar = S Diag(alpha_f): key channel j (column j) scaled by alpha_f[j]
+    ([VDN] "Video Delta Attention: A Frame-Wise Solution", the channel-wise decay gate)."""
+    if alpha_f is None:
+        return s
+    return s * np.asarray(alpha_f, np.float64)[None, :]
+
+
 def frame_update(s_bar: np.ndarray, a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """Closed-form frame update S = (S_bar + B)(I + A)^-1, via a linear solve (no inverse)."""
     d = a.shape[0]
@@ -174,12 +186,14 @@ def scan_order(T: int, anchors: bool) -> list[int]:
     return [f for f in range(T) if f not in bset]
 
 
-def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half_beta"):
+def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half_beta", alpha=None):
     """For one head: S0 and, for every query frame t, (S_fwd(t), S_rev(t)) in fp64.
 
     S_fwd(t) is the forward state after exactly the frames F(t) in increasing order; S_rev(t) is
-    the reverse state after exactly R(t) in decreasing order (nearest frame written last).
+    the reverse state after exactly R(t) in decreasing order (nearest frame written last).  With
+    ``alpha`` ([T, H, d]), writing frame f updates decay(S, alpha[f, h]) instead of S.
     """
+    alpha_of = (lambda f: None) if alpha is None else (lambda f: alpha[f, h])
     n_text = text_k.shape[0]
     s0 = text_state(text_k[:, h], text_v[:, h], beta[:n_text, h], text_mode)
     order = scan_order(T, anchors)
@@ -190,10 +204,10 @@ def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half
     # prefix states of the forward scan and of the reverse scan
     fwd_prefix = [s0]
     for f in order:
-        fwd_prefix.append(frame_update(fwd_prefix[-1], *stats[f]))
+        fwd_prefix.append(frame_update(decay(fwd_prefix[-1], alpha_of(f)), *stats[f]))
     rev_prefix = [s0]
     for f in reversed(order):
-        rev_prefix.append(frame_update(rev_prefix[-1], *stats[f]))
+        rev_prefix.append(frame_update(decay(rev_prefix[-1], alpha_of(f)), *stats[f]))
     per_frame = []
     for t in range(T):
         _, _, fwd, rev = frame_sets(t, T, C, anchors)
@@ -204,14 +218,14 @@ def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half
 
 
 def linear_branch(q, k, v, beta, text_k, text_v, T, N, C, anchors, rows=None,
-                  text_mode="half_beta", return_states=False):
+                  text_mode="half_beta", return_states=False, alpha=None):
     """o_l = (S_fwd(t) + S_rev(t)) q for each video token; fp64."""
     TN, H, d = q.shape
     rows = np.arange(TN) if rows is None else np.asarray(rows)
     o_l = np.zeros((len(rows), H, d))
     states = []
     for h in range(H):
-        s0, per_frame = head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode)
+        s0, per_frame = head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode, alpha)
         states.append((s0, per_frame))
         for j, i in enumerate(rows):
             sf, sr = per_frame[i // N]
@@ -253,14 +267,16 @@ def vdn_forward(inp: dict, T, N, C, anchors=True, rows=None, text_mode="half_bet
                 with_intermediates=False):
     """Layer output ``out`` [len(rows) or T*N, H, d] (fp64) from the inputs dict.
 
-    ``inp`` holds float32 arrays: q, k, v, text_k, text_v, beta, gate_w, proj_w.
+    ``inp`` holds float32 arrays: q, k, v, text_k, text_v, beta, gate_w, proj_w, and optionally
+    alpha ``[T, H, d]`` (the decay gate; absent = no decay).
     """
     q, k, v = inp["q"], inp["k"], inp["v"]
     tk, tv = inp["text_k"], inp["text_v"]
     beta = inp["beta"]
     rows_arr = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     o_s = softmax_branch(q, k, v, tk, tv, T, N, C, anchors, rows_arr)
-    o_l = linear_branch(q, k, v, beta, tk, tv, T, N, C, anchors, rows_arr, text_mode)
+    o_l = linear_branch(q, k, v, beta, tk, tv, T, N, C, anchors, rows_arr, text_mode,
+                        alpha=inp.get("alpha"))
     out = merge(q[rows_arr], o_s, o_l, inp["gate_w"], inp["proj_w"])
     if with_intermediates:
         return out, {"o_s": o_s, "o_l": o_l}
@@ -274,7 +290,7 @@ def chunk_states(inp: dict, T, N, C, anchors=True, text_mode="half_beta"):
     res = np.zeros((T, H, d, d))
     for h in range(H):
         _, per_frame = head_states(inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"],
-                                   h, T, N, C, anchors, text_mode)
+                                   h, T, N, C, anchors, text_mode, inp.get("alpha"))
         for t in range(T):
             res[t, h] = per_frame[t][0] + per_frame[t][1]
     return res

@@ -64,11 +64,13 @@ def _round_bf16(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(torch.float32).numpy()
 
 
-def make_inputs(w: Workload, seed: int = 0, stress: bool = False) -> dict:
+def make_inputs(w: Workload, seed: int = 0, stress: bool = False, decay: bool = False) -> dict:
     """float32 numpy inputs (bf16-rounded for bf16 workloads).
 
     ``stress=True`` replaces each frame's keys by normalise(shared + 0.1 * noise) so that one
     direction of the per-frame key Gram matrix is crowded (large top eigenvalue).
+    ``decay=True`` adds ``alpha`` ``[T, H, d]`` float32 ~ U(0.5, 1), a per-frame channel-wise decay
+    gate, drawn after every other input (so the other inputs do not change).
     """
     rng = np.random.default_rng(seed)
     TN, H, d = w.T * w.N, w.H, w.d
@@ -93,6 +95,8 @@ def make_inputs(w: Workload, seed: int = 0, stress: bool = False) -> dict:
     k = _l2n(k)
     text_k = _l2n(text_k)
     out = dict(q=q, k=k, v=v, text_k=text_k, text_v=text_v, beta=beta, gate_w=gate_w, proj_w=proj_w)
+    if decay:
+        out["alpha"] = (0.5 + 0.5 * rng.random((w.T, H, d), dtype=f32)).astype(f32)
     if w.dtype == "bf16":
         for key in ("q", "k", "v", "text_k", "text_v", "gate_w", "proj_w"):
             out[key] = _round_bf16(out[key])

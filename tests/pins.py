@@ -364,6 +364,118 @@ def pin_gate_closed_forms(orc, seed=11):
 
 
 # --------------------------------------------------------------------------------------------
+# Decay gate pins ([VDN] "Video Delta Attention: A Frame-Wise Solution": the inherited state is
+# decayed channel-wise, S_bar = S Diag(alpha); "Stability of the Inherited State": the decayed
+# transition Diag(alpha)(I + A)^-1 has operator norm at most one)
+# --------------------------------------------------------------------------------------------
+
+def _frame_sums(k, v, beta, n_text, N, f, h):
+    """A_f and B_f by explicit sums over the frame's tokens (independent of the oracle)."""
+    d = k.shape[-1]
+    a = np.zeros((d, d))
+    b = np.zeros((d, d))
+    for u in range(f * N, (f + 1) * N):
+        ku = np.asarray(k[u, h], np.float64)
+        w = float(beta[n_text + u, h])
+        a += w * np.outer(ku, ku)
+        b += w * np.outer(np.asarray(v[u, h], np.float64), ku)
+    return a, b
+
+
+def pin_decay_one(orc, seed=13):
+    """P15: alpha = 1 everywhere is exactly the undecayed layer."""
+    T, N, C, n_text, H, d = 9, 3, 2, 2, 2, 4
+    inp = tiny_inputs(T, N, n_text, H, d, seed)
+    ref = orc.chunk_states(inp, T, N, C, True)
+    inp["alpha"] = np.ones((T, H, d), np.float32)
+    assert np.array_equal(orc.chunk_states(inp, T, N, C, True), ref)
+
+
+def pin_decay_zero(orc, seed=14):
+    """P16: alpha = 0 forgets everything before the frame being written: every scanned state is
+    that frame's own solve from zero, B_f (I + A_f)^-1 (computed here with an explicit inverse)."""
+    T, N, C, n_text, H, d = 8, 3, 1, 2, 1, 4
+    inp = tiny_inputs(T, N, n_text, H, d, seed)
+    inp["alpha"] = np.zeros((T, H, d), np.float32)
+    st = orc.chunk_states(inp, T, N, C, False)
+    for t in range(T):
+        # anchors off, C = 1: forward region = frames <= t-2, reverse region = frames >= t+2
+        want = np.zeros((d, d))
+        for f in ([t - 2] if t >= 2 else []) + ([t + 2] if t + 2 < T else []):
+            a, b = _frame_sums(inp["k"], inp["v"], inp["beta"], n_text, N, f, 0)
+            want += b @ np.linalg.inv(np.eye(d) + a)
+        if t < 2 or t + 2 >= T:                          # an empty region keeps the text state
+            a, b = _frame_sums(inp["text_k"], inp["text_v"], np.concatenate(
+                [0.5 * inp["beta"][:n_text], inp["beta"][n_text:]]), 0, n_text, 0, 0)
+            s0 = b @ np.linalg.inv(np.eye(d) + a)
+            want += s0 * ((t < 2) + (t + 2 >= T))
+        assert np.allclose(st[t, 0], want, rtol=1e-9, atol=1e-10), t
+
+
+def pin_decay_columns(orc, seed=15):
+    """P17: writing frame f solves S_f (I + A_f) = S_prev Diag(alpha_f) + B_f, with the decay on
+    the key channels (columns) of the inherited state and alpha of the frame being written, in
+    both scan directions (checked on consecutive prefix states, anchors off, one frame per chunk)."""
+    rng = _rng(seed)
+    T, N, C, n_text, H, d = 9, 4, 1, 1, 1, 5
+    inp = tiny_inputs(T, N, n_text, H, d, seed)
+    inp["alpha"] = rng.random((T, H, d)).astype(np.float32)
+    _, per_frame = orc.head_states(inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"], 0,
+                                   T, N, C, False, alpha=inp["alpha"])
+    fwd = [per_frame[t][0] for t in range(2, T)]        # after frames 0..t-2
+    rev = [per_frame[t][1] for t in range(T - 3, -1, -1)]   # after frames T-1 .. t+2
+    for i in range(1, len(fwd)):
+        f = i                                            # fwd[i] has written frames 0..i
+        a, b = _frame_sums(inp["k"], inp["v"], inp["beta"], n_text, N, f, 0)
+        lhs = fwd[i] @ (np.eye(d) + a) - b
+        assert np.allclose(lhs, fwd[i - 1] * inp["alpha"][f, 0].astype(np.float64)[None, :],
+                           rtol=1e-8, atol=1e-10), ("forward", f)
+    for i in range(1, len(rev)):
+        f = T - 1 - i                                    # rev[i] has written frames T-1 .. f
+        a, b = _frame_sums(inp["k"], inp["v"], inp["beta"], n_text, N, f, 0)
+        lhs = rev[i] @ (np.eye(d) + a) - b
+        assert np.allclose(lhs, rev[i - 1] * inp["alpha"][f, 0].astype(np.float64)[None, :],
+                           rtol=1e-8, atol=1e-10), ("reverse", f)
+
+
+def pin_decay_nonexpansive(orc, seed=16):
+    """P18: with 0 <= alpha <= 1 the decayed update is non-expansive in the inherited state:
+    ||f(X) - f(Y)||_F <= ||X - Y||_F for f(S) = update(decay(S))."""
+    rng = _rng(seed)
+    d, U = 8, 40
+    for trial in range(20):
+        k = _unit(rng.standard_normal((U, d)))
+        if trial % 2:
+            k = _unit(k[:1] + 0.05 * rng.standard_normal((U, d)))   # crowded keys
+        a, b = orc.frame_stats(k, rng.standard_normal((U, d)), rng.random(U))
+        alpha = rng.random(d)
+        x, y = rng.standard_normal((d, d)), rng.standard_normal((d, d))
+        fx = orc.frame_update(orc.decay(x, alpha), a, b)
+        fy = orc.frame_update(orc.decay(y, alpha), a, b)
+        assert np.linalg.norm(fx - fy) <= np.linalg.norm(x - y) * (1 + 1e-12)
+
+
+BRUTE_DECAY_CASES = [
+    # T, N, C, n_text, H, d, anchors
+    (7, 3, 2, 2, 2, 4, True),
+    (9, 2, 1, 1, 1, 4, False),
+    (10, 3, 3, 2, 1, 6, True),
+]
+
+
+def pin_bruteforce_decay(orc, seed=17):
+    """P19: with a decay gate, the structured oracle equals the brute-force oracle (least-squares
+    updates whose proximity target is the inherited state times the diagonal of alpha)."""
+    for ci, (T, N, C, n_text, H, d, anchors) in enumerate(BRUTE_DECAY_CASES):
+        inp = tiny_inputs(T, N, n_text, H, d, seed + ci)
+        inp["alpha"] = _rng(seed + 100 + ci).random((T, H, d)).astype(np.float32)
+        out_s, mids = orc.vdn_forward(inp, T, N, C, anchors, with_intermediates=True)
+        out_b, _, ol_b = bruteforce.layer_dense(inp, T, N, C, anchors)
+        assert np.allclose(mids["o_l"], ol_b, rtol=1e-9, atol=1e-9), ("o_l", ci)
+        assert np.allclose(out_s, out_b, rtol=1e-5, atol=1e-5), ("out", ci)
+
+
+# --------------------------------------------------------------------------------------------
 # Whole-layer pins
 # --------------------------------------------------------------------------------------------
 

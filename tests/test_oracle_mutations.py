@@ -71,7 +71,7 @@ def m_forward_window_off_by_one(o):
 
 
 def m_reverse_scan_increasing(o):
-    def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half_beta"):
+    def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half_beta", alpha=None):
         n_text = text_k.shape[0]
         s0 = o.text_state(text_k[:, h], text_v[:, h], beta[:n_text, h], text_mode)
         order = o.scan_order(T, anchors)
@@ -156,6 +156,48 @@ def m_boundary_reads_states(o):
     o.frame_sets = frame_sets
 
 
+def m_decay_dropped(o):
+    o.decay = lambda s, alpha_f: s
+
+
+def m_decay_on_rows(o):
+    def decay(s, alpha_f):
+        if alpha_f is None:
+            return s
+        return np.asarray(alpha_f, np.float64)[:, None] * s
+    o.decay = decay
+
+
+def m_decay_after_solve(o):
+    orig_update = o.frame_update
+    pending = {}
+
+    def decay(s, alpha_f):
+        pending["alpha"] = alpha_f           # remember it; apply it to the solved state instead
+        return s
+
+    def frame_update(s_bar, a, b):
+        out = orig_update(s_bar, a, b)
+        alpha_f = pending.pop("alpha", None)
+        return out if alpha_f is None else out * np.asarray(alpha_f, np.float64)[None, :]
+    o.decay = decay
+    o.frame_update = frame_update
+
+
+def m_decay_reverse_uses_next_frame(o):
+    orig = o.head_states
+
+    def head_states(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode="half_beta", alpha=None):
+        if alpha is None:
+            return orig(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode)
+        # forward pass unchanged, reverse pass with alpha shifted by one frame
+        s0, fwd_only = orig(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode, alpha)
+        shifted = np.concatenate([alpha[1:], alpha[-1:]])
+        _, rev_only = orig(k, v, beta, text_k, text_v, h, T, N, C, anchors, text_mode, shifted)
+        return s0, [(fwd_only[t][0], rev_only[t][1]) for t in range(T)]
+    o.head_states = head_states
+
+
 MUTANTS = [
     (m_drop_sbar, pins.pin_objective_minimum),
     (m_minus_gram, pins.pin_spectrum),
@@ -170,6 +212,10 @@ MUTANTS = [
     (m_softmax_scale, pins.pin_bruteforce),
     (m_softmax_no_text, pins.pin_uniform_keys_visibility),
     (m_boundary_reads_states, pins.pin_partition),
+    (m_decay_dropped, pins.pin_decay_zero),
+    (m_decay_on_rows, pins.pin_decay_columns),
+    (m_decay_after_solve, pins.pin_decay_columns),
+    (m_decay_reverse_uses_next_frame, pins.pin_decay_columns),
 ]
 
 

@@ -14,6 +14,8 @@ from oracle import vdn_oracle as orc
     pins.pin_cho_solve, pins.pin_golden_frame_sets, pins.pin_partition,
     pins.pin_uniform_keys_visibility, pins.pin_beta_zero, pins.pin_text_once,
     pins.pin_boundary_text_only, pins.pin_gate_closed_forms, pins.pin_bruteforce,
+    pins.pin_decay_one, pins.pin_decay_zero, pins.pin_decay_columns, pins.pin_decay_nonexpansive,
+    pins.pin_bruteforce_decay,
 ], ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(orc)
