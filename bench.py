@@ -171,16 +171,17 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
-    inp = synth.make_inputs(w, seed=0)
+    inp = synth.make_inputs(w, seed=0, decay=True)      # alpha is drawn last: other inputs as without it
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = {k: torch.from_numpy(inp[k]).to("cuda").to(tdt).contiguous() for k in ("q", "k", "v", "gate_w", "proj_w")}
     beta = torch.from_numpy(inp["beta"]).to("cuda").contiguous()
     text_kv = torch.from_numpy(np.stack([inp["text_k"], inp["text_v"]])).to("cuda").to(tdt).contiguous()
+    alpha = torch.from_numpy(inp["alpha"]).to("cuda").contiguous()
     out = torch.empty_like(dev["q"])
     plan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype)
 
-    def forward(p):
-        p.forward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"], dev["proj_w"], out)
+    def forward(p, gate=None):
+        p.forward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"], dev["proj_w"], out, alpha=gate)
 
     for _ in range(args.warmup):
         forward(plan)
@@ -213,6 +214,16 @@ def main():
     cold_ms, cold_calls = plan.profile_read()
     del flush
     vda_cold_ms = (cold_ms["vda_stats"] + cold_ms["vda_scan"]) / cold_calls
+
+    # the same layer with the channel-wise decay gate on the linear branch (context)
+    n_dec = max(3, min(args.steps, 10))
+    forward(plan, alpha)
+    torch.cuda.synchronize()
+    plan.profile_enable(n_dec)
+    dec = timed_steps(lambda: forward(plan, alpha), n_dec)
+    dec_ms, dec_calls = plan.profile_read()
+    decay = {"ms_per_step_median": float(np.median(dec)),
+             "vda_ms": (dec_ms["vda_stats"] + dec_ms["vda_scan"]) / dec_calls}
     plan.close()
 
     overlapped = None
@@ -256,9 +267,11 @@ def main():
                 "frac_onbox_copy": vb / (vda_ms * 1e-3) / 1e9 / copy_onbox},
         "onbox": {"mfma_bf16_tflops": mfma_onbox, "copy_gbs": copy_onbox},
     }
+    decay["vda_frac_hbm"] = (vb + 4 * w.T * w.H * w.d) / (decay["vda_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    result["decay_gate"] = decay
     if overlapped is not None:
         result["overlapped_branches"] = overlapped
-    del dev, beta, text_kv, out, ref
+    del dev, beta, text_kv, alpha, out, ref
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)

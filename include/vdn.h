@@ -94,6 +94,19 @@ vdn_status vdn_forward(const vdn_plan *plan, const void *q, const void *k, const
                        const float *beta, const void *text_kv, const void *gate_w,
                        const void *proj_w, void *out, void *stream);
 
+/* As vdn_forward, with the channel-wise decay gate of the linear branch ("Video DeltaNet:
+ * Near-Lossless Hybrid Attention for Video Models", section "Video Delta Attention: A Frame-Wise
+ * Solution"): before frame f is absorbed, each scan direction's inherited state is scaled per key
+ * channel, S <- S Diag(alpha_f), then updated as usual.  alpha is fp32 [T][H][d] (frame-major,
+ * d contiguous), device memory owned by the caller and only read; the text initialisation uses
+ * no gate, and boundary frames' entries are unused.  alpha = 1 everywhere gives vdn_forward's
+ * result.  alpha must be non-NULL, 16-byte aligned and not alias out (else
+ * VDN_ERR_INVALID_ARG); values in [0, 1] keep the state non-expansive.  Every other argument and
+ * error as vdn_forward. */
+vdn_status vdn_forward_decay(const vdn_plan *plan, const void *q, const void *k, const void *v,
+                             const float *beta, const void *text_kv, const float *alpha,
+                             const void *gate_w, const void *proj_w, void *out, void *stream);
+
 /* Free the plan's workspace, stream and events.  The caller must have synchronised the streams
  * the plan was used on.  NULL is a no-op. */
 void vdn_plan_destroy(vdn_plan *plan);

@@ -177,8 +177,11 @@ vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
   return VDN_OK;
 }
 
-vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
-                       const void* text_kv, const void* gate_w, const void* proj_w, void* out, void* stream) {
+namespace {
+
+vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                        const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w, void* out,
+                        void* stream) {
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !out) return VDN_ERR_INVALID_ARG;
   if (plan->s.n_text > 0 && !text_kv) return VDN_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, out};
@@ -191,7 +194,7 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
 
   const vdn::Shape& s = plan->s;
   hipStream_t main = reinterpret_cast<hipStream_t>(stream);
-  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out};
+  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out, alpha};
   vdn::Buffers b = buffers_of(plan);
 
   hipEvent_t* ev = nullptr;
@@ -216,7 +219,7 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, lin));
   mark(VDN_STAGE_VDA_STATS, 1, lin);
   mark(VDN_STAGE_VDA_SCAN, 0, lin);
-  VDN_TRY(vdn::launch_vda_scan(s, b, plan->kinds.scan_mfma, lin));
+  VDN_TRY(vdn::launch_vda_scan(s, in, b, plan->kinds.scan_mfma, lin));
   mark(VDN_STAGE_VDA_SCAN, 1, lin);
   if (plan->overlap) VDN_TRY(hipEventRecord(plan->ev_join, plan->side));
   // softmax branch on the caller's stream
@@ -237,6 +240,20 @@ vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const
   mark(VDN_STAGE_TOTAL, 1, main);
 #undef VDN_TRY
   return VDN_OK;
+}
+
+}  // namespace
+
+vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                       const void* text_kv, const void* gate_w, const void* proj_w, void* out, void* stream) {
+  return forward_impl(plan, q, k, v, beta, text_kv, nullptr, gate_w, proj_w, out, stream);
+}
+
+vdn_status vdn_forward_decay(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                             const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
+                             void* out, void* stream) {
+  if (!alpha || !aligned16(alpha) || alpha == out) return VDN_ERR_INVALID_ARG;
+  return forward_impl(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, out, stream);
 }
 
 vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes) {

@@ -15,8 +15,9 @@
 // positive definite with every pivot >= 1, so no pivot is small).  Writes M = (I + A)^-1 and B.
 // Stage 2 (scan): the update acts on each row of S independently (row r of the new state only
 // needs row r of the old state and of B), so one block owns 16 rows of S for one (head,
-// direction) and walks the frames in order, x = s + B_f, s = x M_f, storing the state at every
-// chunk boundary.  Slot Nc of each direction holds S0, read by boundary query frames.
+// direction) and walks the frames in order, x = s Diag(alpha_f) + B_f (the decay gate, when given,
+// on the key channels of the inherited state), s = x M_f, storing the state at every chunk
+// boundary.  Slot Nc of each direction holds S0, read by boundary query frames.
 #include "dev_common.h"
 #include "vda_common.h"
 #include "vdn_internal.h"
@@ -110,12 +111,17 @@ __global__ __launch_bounds__(256) void vda_stats_simt_kernel(
 
 constexpr int kScanRows = 16;
 
+// s <- (s Diag(alpha) + B) M for the block's rows; alpha == nullptr means no decay
 template <int D>
 __device__ __forceinline__ void scan_apply(float (&s)[D / 16], float (*x)[D], const float* __restrict__ bslot,
-                                           const float* __restrict__ mslot, int row0, int r, int jc) {
+                                           const float* __restrict__ mslot, const float* __restrict__ aslot,
+                                           int row0, int r, int jc) {
   constexpr int CPT = D / 16;
 #pragma unroll
-  for (int cc = 0; cc < CPT; ++cc) x[r][jc * CPT + cc] = s[cc] + bslot[(int64_t)(row0 + r) * D + jc * CPT + cc];
+  for (int cc = 0; cc < CPT; ++cc) {
+    const int col = jc * CPT + cc;
+    x[r][col] = (aslot ? s[cc] * aslot[col] : s[cc]) + bslot[(int64_t)(row0 + r) * D + col];
+  }
   __syncthreads();
   float o[CPT];
 #pragma unroll
@@ -133,8 +139,10 @@ __device__ __forceinline__ void scan_apply(float (&s)[D / 16], float (*x)[D], co
 
 template <int D>
 __global__ __launch_bounds__(256) void vda_scan_simt_kernel(const float* __restrict__ minv,
-                                                            const float* __restrict__ bw, float* __restrict__ states,
-                                                            int T, int C, int Nc, int H, int anchors) {
+                                                            const float* __restrict__ bw,
+                                                            const float* __restrict__ alpha,
+                                                            float* __restrict__ states, int T, int C, int Nc, int H,
+                                                            int anchors) {
   constexpr int CPT = D / 16;
   constexpr int ROWS = D < kScanRows ? D : kScanRows;
   const int rblk = blockIdx.x, dir = blockIdx.y, h = blockIdx.z;
@@ -148,10 +156,11 @@ __global__ __launch_bounds__(256) void vda_scan_simt_kernel(const float* __restr
   for (int cc = 0; cc < CPT; ++cc) s[cc] = 0.f;
   const int rr = active ? r : 0;
 
-  auto apply = [&](int slot) {
+  auto apply = [&](int slot) {                       // slot 0: the text; slot 1 + f: frame f
     const float* bslot = bw + ((int64_t)slot * H + h) * DD;
     const float* mslot = minv + ((int64_t)slot * H + h) * DD;
-    scan_apply<D>(s, x, bslot, mslot, row0, rr, jc);
+    const float* aslot = (alpha && slot > 0) ? alpha + ((int64_t)(slot - 1) * H + h) * D : nullptr;
+    scan_apply<D>(s, x, bslot, mslot, aslot, row0, rr, jc);
   };
   auto store = [&](int cslot) {
     if (!active) return;
@@ -203,10 +212,10 @@ void stats_d(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st)
 }
 
 template <int D>
-void scan_t(const Shape& s, const Buffers& b, hipStream_t st) {
+void scan_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   constexpr int ROWS = D < kScanRows ? D : kScanRows;
   dim3 grid(D / ROWS, 2, s.H);
-  vda_scan_simt_kernel<D><<<grid, 256, 0, st>>>(b.minv, b.bw, b.states, s.T, s.C, s.Nc, s.H, s.anchors);
+  vda_scan_simt_kernel<D><<<grid, 256, 0, st>>>(b.minv, b.bw, in.alpha, b.states, s.T, s.C, s.Nc, s.H, s.anchors);
 }
 
 }  // namespace
@@ -218,13 +227,13 @@ hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, 
   return hipGetLastError();
 }
 
-hipError_t launch_vda_scan(const Shape& s, const Buffers& b, bool mfma, hipStream_t st) {
-  if (mfma) return launch_vda_scan_mfma(s, b, st);
+hipError_t launch_vda_scan(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st) {
+  if (mfma) return launch_vda_scan_mfma(s, in, b, st);
   switch (s.d) {
-    case 16: scan_t<16>(s, b, st); break;
-    case 32: scan_t<32>(s, b, st); break;
-    case 64: scan_t<64>(s, b, st); break;
-    default: scan_t<128>(s, b, st); break;
+    case 16: scan_t<16>(s, in, b, st); break;
+    case 32: scan_t<32>(s, in, b, st); break;
+    case 64: scan_t<64>(s, in, b, st); break;
+    default: scan_t<128>(s, in, b, st); break;
   }
   return hipGetLastError();
 }

@@ -5,10 +5,13 @@
 // S M + C with M = (I + A)^-1 and C = B M.  Per (frame or text, head) one workgroup
 //   1. inverts I + A (written by the statistics kernel into the M buffer) in place by Gauss-Jordan
 //      elimination in registers (16 x 16 threads, R x R elements each);
-//   2. keeps M in LDS as two bf16 planes, M = Mh + Ml to ~2^-16, and writes them out for the scan
-//      (row-major; M is symmetric, so row n of a plane is also its column n);
+//   2. keeps M in LDS as two bf16 planes, M = Mh + Ml to ~2^-16;
 //   3. forms C = B M on v_mfma_f32_16x16x32_bf16 with B split the same way,
-//      B M ~ Bh Mh + Bh Ml + Bl Mh, and writes C (fp32).
+//      B M ~ Bh Mh + Bh Ml + Bl Mh, and writes C (fp32);
+//   4. writes the frame's step matrix for the scans as two bf16 planes holding its transpose row
+//      by row: the step is S <- S G + C with G = Diag(alpha_f) M (the decay gate on the inherited
+//      state's key channels; alpha = 1 without it), and G^T = M Diag(alpha_f), so plane row n is
+//      row n of M with column k scaled by alpha_f[k] (row n of M itself when there is no decay).
 // Boundary frames are never written into a state and are skipped.
 #include "dev_common.h"
 #include "vda_common.h"
@@ -33,8 +36,8 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 
 template <int D>
 __global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ minv, const float* __restrict__ bw,
-                                                         float* __restrict__ cw, bf16_t* __restrict__ mhl, int T,
-                                                         int H, int anchors) {
+                                                         const float* __restrict__ alpha, float* __restrict__ cw,
+                                                         bf16_t* __restrict__ mhl, int T, int H, int anchors) {
   constexpr int R = D / 16;
   constexpr int LDM = D + 8;                 // bf16 row stride of the M planes in LDS
   constexpr int KS = D / 32;                 // k-steps of the 16x16x32 products
@@ -62,6 +65,7 @@ __global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ min
   gauss_jordan_inverse<D>(g, rowbuf, colbuf, ty, tx);
 
   // 2. M (fp32) out, M planes into LDS
+  const float* af = (alpha && slot > 0) ? alpha + ((int64_t)(slot - 1) * H + h) * D + tx * R : nullptr;
 #pragma unroll
   for (int ii = 0; ii < R; ++ii) {
 #pragma unroll
@@ -80,12 +84,15 @@ __global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ min
   }
   __syncthreads();
   bf16_t* mout = mhl + ((int64_t)slot * H + h) * 2 * DD;
-  for (int e = tid; e < 2 * D * D / 8; e += 256) {
-    const int plane = e / (D * D / 8), rem = e % (D * D / 8);
-    const int row = rem / (D / 8), c8 = rem % (D / 8);
-    *reinterpret_cast<u32x4*>(mout + plane * DD + (int64_t)row * D + c8 * 8) =
-        *reinterpret_cast<const u32x4*>(&mp[plane][row][c8 * 8]);
-  }
+  auto write_planes = [&]() {
+    for (int e = tid; e < 2 * D * D / 8; e += 256) {
+      const int plane = e / (D * D / 8), rem = e % (D * D / 8);
+      const int row = rem / (D / 8), c8 = rem % (D / 8);
+      *reinterpret_cast<u32x4*>(mout + plane * DD + (int64_t)row * D + c8 * 8) =
+          *reinterpret_cast<const u32x4*>(&mp[plane][row][c8 * 8]);
+    }
+  };
+  if (!af) write_planes();                 // step planes = M planes
 
   // 3. C = B M: wave w owns rows [RT*16*w, RT*16*(w+1)), all columns
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -124,16 +131,35 @@ __global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ min
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cout[(int64_t)(16 * rt + i) * D + 16 * ct] = acc[rt][ct][i];
+
+  // 4. with a decay gate: step planes = M Diag(alpha_f), rebuilt in LDS once C no longer needs M
+  if (af) {
+    float a[R];
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) a[jj] = af[jj];
+    __syncthreads();                       // every wave is done reading the M planes
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < R; ++jj) {
+        const float gv = g[ii][jj] * a[jj];
+        const __bf16 xh = (__bf16)gv;
+        mp[0][ty * R + ii][tx * R + jj] = __builtin_bit_cast(bf16_t, xh);
+        mp[1][ty * R + ii][tx * R + jj] = __builtin_bit_cast(bf16_t, (__bf16)(gv - (float)xh));
+      }
+    __syncthreads();
+    write_planes();
+  }
 }
 
 }  // namespace
 
-hipError_t launch_vda_invert_mfma(const Shape& s, const Buffers& b, hipStream_t st) {
+hipError_t launch_vda_invert_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   const dim3 grid(s.T + 1, s.H);
   if (s.d == 128)
-    vda_invert_kernel<128><<<grid, 256, 0, st>>>(b.minv, b.bw, b.cw, b.mhl, s.T, s.H, s.anchors);
+    vda_invert_kernel<128><<<grid, 256, 0, st>>>(b.minv, b.bw, in.alpha, b.cw, b.mhl, s.T, s.H, s.anchors);
   else
-    vda_invert_kernel<64><<<grid, 256, 0, st>>>(b.minv, b.bw, b.cw, b.mhl, s.T, s.H, s.anchors);
+    vda_invert_kernel<64><<<grid, 256, 0, st>>>(b.minv, b.bw, in.alpha, b.cw, b.mhl, s.T, s.H, s.anchors);
   return hipGetLastError();
 }
 

@@ -1,17 +1,20 @@
 // Chunk maps and chunk-level state scans of Video Delta Attention (bf16 plans, d in {64, 128}).
 //
 // "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Video Delta
-// Attention: A Frame-Wise Solution": each frame updates the state as S <- (S + B_f) M_f =
-// S M_f + C_f (M_f = (I + A_f)^-1 symmetric, C_f = B_f M_f).  Section "Local Softmax and Long-Range
-// Linear Memory": both directions start from the text state S0 = C_0; the forward state of a
-// query frame in chunk c has absorbed, in increasing order, the non-boundary frames of chunks
-// <= c-2, the reverse state, in decreasing order, those of chunks >= c+2.  Only whole chunks ever
-// enter a state, so the frames of a chunk compose into one affine map S -> S P + Q:
-//   forward  (increasing frames f1 < ... < fm):  P = M_f1 ... M_fm,  Q> = (..(C_f1 M_f2 + C_f2) ..) + C_fm
-//   reverse  (decreasing frames):                P^T (the M_f are symmetric),  Q< likewise from C_fm down
-// and the states follow from a scan over chunks:
-//   S>_0 = S>_1 = S0,  S>_c = S>_{c-1} P_{c-2} + Q>_{c-2};   S<_{Nc-1} = S<_{Nc-2} = S0,
-//   S<_c = S<_{c+1} P_{c+2}^T + Q<_{c+2}.
+// Attention: A Frame-Wise Solution": each frame updates the state as
+// S <- (S Diag(alpha_f) + B_f) M_f = S G_f + C_f with G_f = Diag(alpha_f) M_f (the decay gate on
+// the inherited state; alpha = 1 without it), M_f = (I + A_f)^-1 symmetric, C_f = B_f M_f.
+// Section "Local Softmax and Long-Range Linear Memory": both directions start from the text state
+// S0 = C_0; the forward state of a query frame in chunk c has absorbed, in increasing order, the
+// non-boundary frames of chunks <= c-2, the reverse state, in decreasing order, those of chunks
+// >= c+2.  Only whole chunks ever enter a state, so the frames of a chunk compose into one affine
+// map S -> S P + Q:
+//   forward  (increasing frames f1 < ... < fm):  P> = G_f1 ... G_fm,  Q> = (..(C_f1 G_f2 + C_f2) ..) + C_fm
+//   reverse  (decreasing frames):                P< = G_fm ... G_f1,  Q< likewise from C_fm down
+// (without decay P< = P>^T, the M_f being symmetric, so P< needs no chain of its own), and the
+// states follow from a scan over chunks:
+//   S>_0 = S>_1 = S0,  S>_c = S>_{c-1} P>_{c-2} + Q>_{c-2};   S<_{Nc-1} = S<_{Nc-2} = S0,
+//   S<_c = S<_{c+1} P<_{c+2} + Q<_{c+2}.
 //
 // Two kernels, both built on the same row-chain step: row r of X M + Q depends only on row r of X,
 // so a workgroup owns 16 RT rows and walks its steps; each of its D/16 waves produces 16 output
@@ -20,8 +23,9 @@
 // bf16 planes holding its transpose row by row, so a lane's k-run is contiguous); the running rows
 // are kept in LDS as their two bf16 planes (double buffered: one barrier per step) and the fp32
 // accumulator is what gets stored.
-//   * vda_compose_kernel: every (chunk, head, map part) in parallel: P (written as P and P^T
-//     planes), Q> and Q< (fp32).  At most C-1 steps each.
+//   * vda_compose_kernel: every (chunk, head, map part) in parallel: P>, Q>, Q< (fp32), and P<
+//     with a decay gate; the maps are written as the planes of their transposes (the scan's
+//     operand layout), P> also as its own planes (= P<^T) without decay.  At most C-1 steps each.
 //   * vda_chunk_scan_kernel: one workgroup per (head, direction, 16 rows) walks the Nc-2 chunk
 //     steps with the operands of the next two steps in flight, storing one state slot per step.
 //     Slot Nc of each direction receives S0 (read by boundary query frames).
@@ -105,13 +109,15 @@ __device__ __forceinline__ void step_product(const RowPlanes<D, RT>& s, int buf,
 
 constexpr int kComposeRT = 2;      // 32 rows per compose workgroup
 
-// blockIdx.x = part * RB + rb (part 0: P, 1: Q>, 2: Q<), blockIdx.y = chunk, blockIdx.z = head.
+// blockIdx.x = part * RB + rb (part 0: P>, 1: Q>, 2: Q<, 3: P< (decay only)), blockIdx.y = chunk,
+// blockIdx.z = head.  mhl holds each frame's step planes (G_f^T by rows, see the inverse kernel).
 template <int D>
 __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restrict__ minv,
                                                             const bf16_t* __restrict__ mhl,
-                                                            const float* __restrict__ cw, bf16_t* __restrict__ pp,
-                                                            float* __restrict__ qq, int T, int C, int Nc, int H,
-                                                            int anchors) {
+                                                            const float* __restrict__ cw,
+                                                            const float* __restrict__ alpha,
+                                                            bf16_t* __restrict__ pp, float* __restrict__ qq, int T,
+                                                            int C, int Nc, int H, int anchors) {
   constexpr int RT = kComposeRT;
   constexpr int RB = D / (16 * RT);
   __shared__ __attribute__((aligned(16))) RowPlanes<D, RT> s;
@@ -121,13 +127,15 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
   const int col = wave * 16 + l16;
   const int64_t DD = (int64_t)D * D;
 
-  // the chunk's scanned frames, in this part's order (forward parts increasing, Q< decreasing)
+  const bool is_p = part == 0 || part == 3;
+  const bool decreasing = part >= 2;
+  // the chunk's scanned frames, in this part's order (P>, Q> increasing; Q<, P< decreasing)
   const int f_lo = j * C, f_hi = min(f_lo + C, T);
   int m = 0;
   for (int f = f_lo; f < f_hi; ++f) m += is_bnd(f, T, anchors) ? 0 : 1;
   auto frame_at = [&](int a) {                       // a-th scanned frame of the chunk in this order
-    int f = part == 2 ? f_hi - 1 : f_lo;
-    const int step = part == 2 ? -1 : 1;
+    int f = decreasing ? f_hi - 1 : f_lo;
+    const int step = decreasing ? -1 : 1;
     for (int seen = 0;; f += step)
       if (!is_bnd(f, T, anchors) && seen++ == a) return f;
   };
@@ -137,13 +145,19 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rt][i] = (part == 0 && row0 + 16 * rt + 4 * lg + i == col) ? 1.f : 0.f;
+      for (int i = 0; i < 4; ++i) acc[rt][i] = (is_p && row0 + 16 * rt + 4 * lg + i == col) ? 1.f : 0.f;
   } else {
-    const float* x0 = (part == 0 ? minv : cw) + ((int64_t)(1 + frame_at(0)) * H + h) * DD;
+    // first frame's map: rows of G = Diag(alpha) M (row r of M times alpha[r]) or of C
+    const int f1 = frame_at(0);
+    const float* x0 = (is_p ? minv : cw) + ((int64_t)(1 + f1) * H + h) * DD;
+    const float* a1 = (is_p && alpha) ? alpha + ((int64_t)f1 * H + h) * D : nullptr;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rt][i] = x0[(int64_t)(row0 + 16 * rt + 4 * lg + i) * D + col];
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + 16 * rt + 4 * lg + i;
+        acc[rt][i] = x0[(int64_t)r * D + col] * (a1 ? a1[r] : 1.f);
+      }
   }
   int buf = 0;
   put_rows<D, RT>(s, buf, acc, col, lg);
@@ -151,7 +165,7 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
     StepOps<D, RT> op;
     const int64_t slot = (int64_t)(1 + frame_at(a)) * H + h;
     load_mat<D, RT>(op, mhl + slot * 2 * DD, col, lg);
-    if (part == 0) {
+    if (is_p) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) op.c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
@@ -164,8 +178,9 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
   }
 
   const int64_t ph = (int64_t)j * H + h;
-  if (part == 0) {
-    // P and P^T, each as hi and lo planes: pp[chunk][head][layout][plane][D][D]
+  if (is_p) {
+    // pp[chunk][head][layout][plane][D][D]: layout 1 = P>^T (operand of the forward scan),
+    // layout 0 = P<^T (reverse scan); without decay P<^T = P>, written by the P> chain directly
     bf16_t* p = pp + ph * 4 * DD;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -175,10 +190,13 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
         const __bf16 xh = (__bf16)acc[rt][i];
         const bf16_t hb = __builtin_bit_cast(bf16_t, xh);
         const bf16_t lb = __builtin_bit_cast(bf16_t, (__bf16)(acc[rt][i] - (float)xh));
-        p[(int64_t)r * D + col] = hb;
-        p[DD + (int64_t)r * D + col] = lb;
-        p[2 * DD + (int64_t)col * D + r] = hb;
-        p[3 * DD + (int64_t)col * D + r] = lb;
+        if (part == 0 && !alpha) {
+          p[(int64_t)r * D + col] = hb;
+          p[DD + (int64_t)r * D + col] = lb;
+        }
+        bf16_t* t = p + (part == 0 ? 2 * DD : 0);      // transposed planes of this map
+        t[(int64_t)col * D + r] = hb;
+        t[DD + (int64_t)col * D + r] = lb;
       }
   } else {
     float* q = qq + ((int64_t)(part - 1) * Nc * H + ph) * DD;
@@ -219,7 +237,7 @@ __global__ __launch_bounds__(D * 4) void vda_chunk_scan_kernel(const float* __re
     const int kk = k < n_steps ? k : 0;
     const int j = dir == 0 ? kk : Nc - 1 - kk;
     const int64_t ph = (int64_t)j * H + h;
-    // forward applies P (planes of P^T give its columns), reverse applies P^T (planes of P)
+    // forward applies P> (planes of P>^T give its columns), reverse applies P< (planes of P<^T)
     load_mat<D, 1>(op, pp + ph * 4 * DD + (dir == 0 ? 2 * DD : 0), col, lg);
     load_add<D, 1>(op, qq + ((int64_t)dir * Nc * H + ph) * DD, row0, col, lg);
   };
@@ -275,10 +293,11 @@ __global__ __launch_bounds__(D * 4) void vda_chunk_scan_kernel(const float* __re
 }
 
 template <int D>
-void launch_t(const Shape& s, const Buffers& b, hipStream_t st) {
+void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   constexpr int RB = D / (16 * kComposeRT);
-  vda_compose_kernel<D><<<dim3(3 * RB, s.Nc, s.H), D * 4, 0, st>>>(b.minv, b.mhl, b.cw, b.pp, b.qq, s.T, s.C, s.Nc,
-                                                                  s.H, s.anchors);
+  const int parts = in.alpha ? 4 : 3;
+  vda_compose_kernel<D><<<dim3(parts * RB, s.Nc, s.H), D * 4, 0, st>>>(b.minv, b.mhl, b.cw, in.alpha, b.pp, b.qq, s.T,
+                                                                      s.C, s.Nc, s.H, s.anchors);
   // the row blocks of one (head, direction) stay on one XCD: per_xcd is a multiple of D / 16
   const int n_chains = 2 * s.H;
   const int per_xcd = (n_chains + 7) / 8 * (D / 16);
@@ -287,9 +306,9 @@ void launch_t(const Shape& s, const Buffers& b, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_vda_scan_mfma(const Shape& s, const Buffers& b, hipStream_t st) {
-  if (s.d == 128) launch_t<128>(s, b, st);
-  else launch_t<64>(s, b, st);
+hipError_t launch_vda_scan_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
+  if (s.d == 128) launch_t<128>(s, in, b, st);
+  else launch_t<64>(s, in, b, st);
   return hipGetLastError();
 }
 

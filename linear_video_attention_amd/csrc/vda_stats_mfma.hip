@@ -235,7 +235,7 @@ hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers
   if (s.d == 128) launch_t<128>(s, in, b, st);
   else launch_t<64>(s, in, b, st);
   const hipError_t e = hipGetLastError();
-  return e != hipSuccess ? e : launch_vda_invert_mfma(s, b, st);
+  return e != hipSuccess ? e : launch_vda_invert_mfma(s, in, b, st);
 }
 
 }  // namespace vdn

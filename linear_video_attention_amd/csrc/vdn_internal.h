@@ -85,6 +85,7 @@ struct Inputs {
   const void* text_kv;
   const void *gate_w, *proj_w;
   void* out;
+  const float* alpha;  // [T][H][d] channel-wise decay gate of the inherited state, or nullptr (none)
 };
 
 // Number of workgroups of the MFMA softmax launch.
@@ -96,9 +97,9 @@ hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& 
 hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
-hipError_t launch_vda_invert_mfma(const Shape& s, const Buffers& b, hipStream_t st);
-hipError_t launch_vda_scan(const Shape& s, const Buffers& b, bool mfma, hipStream_t st);
-hipError_t launch_vda_scan_mfma(const Shape& s, const Buffers& b, hipStream_t st);
+hipError_t launch_vda_invert_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_vda_scan(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
+hipError_t launch_vda_scan_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_prep_weights(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);

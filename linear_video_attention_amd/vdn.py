@@ -27,6 +27,7 @@ SIGNATURES = [
     ("vdn_plan_create", _c_int, [_c_int] * 7 + [_c_int, ctypes.POINTER(_vp)]),
     ("vdn_plan_create_ex", _c_int, [_c_int] * 7 + [_c_int, ctypes.c_uint, ctypes.POINTER(_vp)]),
     ("vdn_forward", _c_int, [_vp] * 10),
+    ("vdn_forward_decay", _c_int, [_vp] * 11),
     ("vdn_plan_destroy", None, [_vp]),
     ("vdn_status_str", ctypes.c_char_p, [_c_int]),
     ("vdn_plan_workspace_bytes", _c_size, [_vp]),
@@ -139,6 +140,15 @@ def vdn_forward(plan, q, k, v, beta, text_kv, gate_w, proj_w, out, stream=None):
                              ptr(proj_w), ptr(out), _stream_ptr(stream)), "vdn_forward")
 
 
+def vdn_forward_decay(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, out, stream=None):
+    """As ``vdn_forward`` with the channel-wise decay gate ``alpha`` (fp32 [T][H][d] device tensor)
+    on the linear branch's inherited state."""
+    ptr = lambda x: None if x is None else x.data_ptr()
+    _check(lib().vdn_forward_decay(plan, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(text_kv), ptr(alpha),
+                                   ptr(gate_w), ptr(proj_w), ptr(out), _stream_ptr(stream)),
+           "vdn_forward_decay")
+
+
 class Plan:
     """Owning wrapper of a plan with argument checks on torch tensors."""
 
@@ -178,7 +188,8 @@ class Plan:
         if not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
 
-    def forward(self, q, k, v, beta, text_kv, gate_w, proj_w, out=None, stream=None):
+    def forward(self, q, k, v, beta, text_kv, gate_w, proj_w, out=None, stream=None, alpha=None):
+        """The layer forward; with ``alpha`` ([T, H, d] fp32) the linear branch's decay gate."""
         import torch
         TN, H, d = self.T * self.N, self.H, self.d
         dt = self.torch_dtype
@@ -192,8 +203,12 @@ class Plan:
         if out is None:
             out = torch.empty((TN, H, d), dtype=dt, device=q.device)
         self._expect("out", out, (TN, H, d), dt)
-        vdn_forward(self.handle, q, k, v, beta, text_kv if self.n_text > 0 else None, gate_w, proj_w, out,
-                    stream)
+        tkv = text_kv if self.n_text > 0 else None
+        if alpha is None:
+            vdn_forward(self.handle, q, k, v, beta, tkv, gate_w, proj_w, out, stream)
+        else:
+            self._expect("alpha", alpha, (self.T, H, d), torch.float32)
+            vdn_forward_decay(self.handle, q, k, v, beta, tkv, alpha, gate_w, proj_w, out, stream)
         return out
 
     def debug_buffer(self, which, stream=None):

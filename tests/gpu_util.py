@@ -21,6 +21,9 @@ def to_device(inp: dict, dtype: str) -> dict:
         dev["text_kv"] = torch.from_numpy(np.ascontiguousarray(tkv)).to("cuda").to(tdt).contiguous()
     else:
         dev["text_kv"] = None
+    dev["alpha"] = None
+    if inp.get("alpha") is not None:
+        dev["alpha"] = torch.from_numpy(np.ascontiguousarray(inp["alpha"])).to("cuda").float().contiguous()
     return dev
 
 
@@ -29,7 +32,8 @@ def make_plan(w, generic=False) -> Plan:
 
 
 def run_layer(plan: Plan, dev: dict, out=None):
-    out = plan.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"], out)
+    out = plan.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"], out,
+                       alpha=dev.get("alpha"))
     torch.cuda.synchronize()
     return out
 

@@ -79,6 +79,7 @@ def test_null_arguments_rejected(vdn):
     L = vdn.lib()
     assert L.vdn_plan_create(4, 16, 2, 1, 1, 16, 1, 0, None) == -1
     assert L.vdn_forward(None, *([None] * 9)) == -1
+    assert L.vdn_forward_decay(None, *([None] * 10)) == -1
     L.vdn_plan_destroy(None)                       # no-op
     assert L.vdn_plan_workspace_bytes(None) == 0
     assert L.vdn_profile_enable(None, 4) == -1

@@ -17,8 +17,8 @@ pytestmark = pytest.mark.gpu
 from gpu_util import TOL, combined_states, make_plan, rel_err, run_layer, softmax_out, to_device  # noqa: E402
 
 
-def check_full(w, generic=False, seed=0, stress=False):
-    inp = synth.make_inputs(w, seed=seed, stress=stress)
+def check_full(w, generic=False, seed=0, stress=False, decay=False):
+    inp = synth.make_inputs(w, seed=seed, stress=stress, decay=decay)
     plan = make_plan(w, generic=generic)
     dev = to_device(inp, w.dtype)
     out = run_layer(plan, dev).float().cpu().numpy()
@@ -27,7 +27,7 @@ def check_full(w, generic=False, seed=0, stress=False):
     e_out = rel_err(out, ref)
     e_os = rel_err(softmax_out(plan), mids["o_s"])
     e_st = rel_err(combined_states(plan), orc.chunk_states(inp, w.T, w.N, w.C, w.anchors))
-    print(f"{w} generic={generic}: out {e_out:.2e}  o_s {e_os:.2e}  states {e_st:.2e}", flush=True)
+    print(f"{w} generic={generic} decay={decay}: out {e_out:.2e}  o_s {e_os:.2e}  states {e_st:.2e}", flush=True)
     assert e_os <= tol, ("o_s", e_os)
     assert e_st <= tol, ("states", e_st)
     assert e_out <= tol, ("out", e_out)
@@ -174,4 +174,96 @@ def test_softmax_fallback_for_large_scores():
     excess = np.max(np.abs(got - ref) - bf16_half_ulp(ref)) / rms
     print(f"fallback o_s: plain err {rel_err(got, ref):.2e}, beyond bf16 storage rounding {excess:.2e}", flush=True)
     assert excess <= TOL["bf16"]
+    plan.close()
+
+
+# --- channel-wise decay gate of the linear branch (vdn_forward_decay) ---
+
+def test_decay_tiny_fp32_matches_oracle_and_bruteforce():
+    w = synth.WORKLOADS["tiny"]
+    inp, out = check_full(w, decay=True)
+    ref, _, _ = bruteforce.layer_dense(inp, w.T, w.N, w.C, w.anchors)
+    assert rel_err(out, ref) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_decay_small_bf16_matches_oracle(generic):
+    check_full(synth.WORKLOADS["small"], generic=generic, decay=True)
+
+
+DECAY_RAGGED = [
+    # n_text, T, N, C, H, d, dtype, anchors
+    (37, 13, 200, 3, 3, 64, "bf16", True),
+    (5, 9, 136, 5, 2, 128, "bf16", False),
+    (16, 9, 64, 1, 2, 128, "bf16", True),        # one frame per chunk
+    (8, 4, 96, 8, 1, 128, "bf16", True),         # a single chunk
+    (0, 15, 64, 7, 1, 64, "bf16", False),
+    (7, 12, 24, 3, 2, 32, "bf16", True),         # generic kernels
+    (9, 11, 37, 3, 2, 64, "fp32", True),
+    (1, 6, 5, 2, 1, 128, "fp32", False),
+]
+
+
+@pytest.mark.parametrize("case", DECAY_RAGGED, ids=lambda c: "x".join(str(x) for x in c))
+def test_decay_ragged_shapes_match_oracle(case):
+    n_text, T, N, C, H, d, dtype, anchors = case
+    w = synth.custom(n_text, T, N, C, H, d, dtype, "sigmoid", anchors)
+    check_full(w, seed=6, decay=True)
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_decay_of_one_is_the_plain_layer(generic):
+    """alpha = 1 reduces the gated update to the plain one: the generic kernels give the same bits,
+    the chunk-map kernels (which then compose the reverse map by its own chain) the same values
+    to within the tolerance."""
+    w = synth.custom(12, 11, 128, 3, 2, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, seed=7)
+    plan = make_plan(w, generic=generic)
+    dev = to_device(inp, w.dtype)
+    plain = run_layer(plan, dev).clone()
+    dev["alpha"] = torch.ones((w.T, w.H, w.d), dtype=torch.float32, device="cuda")
+    gated = run_layer(plan, dev)
+    if generic:
+        assert torch.equal(plain, gated)
+    else:
+        assert rel_err(gated.float().cpu().numpy(), plain.float().cpu().numpy()) <= TOL["bf16"]
+    plan.close()
+
+
+def test_decay_768p_sampled_rows():
+    """The 768p workload with a decay gate, in the benchmark's launch configuration, on sampled
+    rows against the oracle."""
+    w = synth.WORKLOADS["768p"]
+    inp = synth.make_inputs(w, seed=0, decay=True)
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
+    out = run_layer(plan, dev)
+    rows = synth.sample_rows(w)
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    del dev, out
+    ref = orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors, rows=rows)
+    e = rel_err(got, ref)
+    print(f"768p decay: sampled {len(rows)} rows, out err {e:.2e}", flush=True)
+    assert e <= TOL[w.dtype]
+    plan.close()
+
+
+def test_decay_argument_errors():
+    from linear_video_attention_amd import vdn
+    w = synth.custom(4, 4, 64, 2, 1, 64, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, decay=True)
+    dev = to_device(inp, w.dtype)
+    plan = make_plan(w)
+    out = torch.empty_like(dev["q"])
+    L = vdn.lib()
+    ptr = lambda x: x.data_ptr()
+    head = [ptr(dev[k]) for k in ("q", "k", "v", "beta", "text_kv")]
+    tail = [ptr(dev["gate_w"]), ptr(dev["proj_w"])]
+    stream = torch.cuda.current_stream().cuda_stream
+    a = ptr(dev["alpha"])
+    assert L.vdn_forward_decay(plan.handle, *head, a, *tail, ptr(out), stream) == 0
+    assert L.vdn_forward_decay(plan.handle, *head, None, *tail, ptr(out), stream) == -1     # no gate
+    assert L.vdn_forward_decay(plan.handle, *head, a + 4, *tail, ptr(out), stream) == -1    # misaligned
+    assert L.vdn_forward_decay(plan.handle, *head, ptr(out), *tail, ptr(out), stream) == -1  # aliases out
+    torch.cuda.synchronize()
     plan.close()
