@@ -15,7 +15,12 @@ It is written independently of ``vdn_oracle`` so the two can check each other:
 * each query frame's forward and reverse states are rebuilt from the text state in fresh loops
   over the frames the rule assigns to it (no reuse between query frames);
 * with a decay gate alpha ``[T, H, d]`` the proximity target of frame f is the inherited state
-  times the diagonal matrix of alpha_f (a matrix product here).
+  times the diagonal matrix of alpha_f (a matrix product here);
+* with audio tokens and text/audio query rows ([GLN] "Video DeltaNet speeds MiniMax H3 video
+  generation 14.5x": every interaction involving text or audio stays softmax attention), the
+  whole sequence [text, audio, video] gets one dense mask built entry by entry from a per-token
+  kind: a text or audio query sees every token, a text or audio key is seen by every query,
+  video-video pairs follow the frame rule; audio never enters the linear memory.
 
 [VDN] = "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models" (openvdn.github.io).
 """
@@ -43,6 +48,52 @@ def dense_mask(T, N, n_text, C, anchors) -> np.ndarray:
         for j in range(T * N):
             m[i, n_text + j] = visible(i // N, j // N, T, C, anchors)
     return m
+
+
+def token_kinds(n_text, n_audio, T, N):
+    """Kind and frame of every token of the joint sequence [text, audio, video]."""
+    kinds = ["text"] * n_text + ["audio"] * n_audio + ["video"] * (T * N)
+    frames = [-1] * (n_text + n_audio) + [j // N for j in range(T * N)]
+    return kinds, frames
+
+
+def joint_mask(n_text, n_audio, T, N, C, anchors) -> np.ndarray:
+    """Softmax visibility over the joint sequence, query x key."""
+    kinds, frames = token_kinds(n_text, n_audio, T, N)
+    L = len(kinds)
+    m = np.zeros((L, L), bool)
+    for i in range(L):
+        for j in range(L):
+            if kinds[i] != "video" or kinds[j] != "video":
+                m[i, j] = True
+            else:
+                m[i, j] = visible(frames[i], frames[j], T, C, anchors)
+    return m
+
+
+def joint_softmax_dense(inp, T, N, C, anchors):
+    """Softmax output of every token of the joint sequence [text, audio, video] under joint_mask;
+    the text and audio queries are ``inp["ctx_q"]`` (text rows first)."""
+    n_text = inp["text_k"].shape[0]
+    has_audio = inp.get("audio_k") is not None
+    n_audio = inp["audio_k"].shape[0] if has_audio else 0
+    def seq(text, audio, video):
+        return np.concatenate([inp[text]] + ([inp[audio]] if has_audio else []) + [inp[video]], axis=0)
+    ctx_q = inp.get("ctx_q")
+    if ctx_q is None:                                  # no context rows wanted: placeholder queries
+        ctx_q = np.zeros((n_text + n_audio,) + inp["q"].shape[1:], np.float32)
+    qs = np.concatenate([ctx_q, inp["q"]], axis=0)
+    ks = seq("text_k", "audio_k", "k")
+    vs = seq("text_v", "audio_v", "v")
+    mask = joint_mask(n_text, n_audio, T, N, C, anchors)
+    d = qs.shape[-1]
+    out = np.zeros(qs.shape, np.float32)
+    for h in range(qs.shape[1]):
+        s = (qs[:, h].astype(np.float32) @ ks[:, h].astype(np.float32).T) / np.float32(math.sqrt(d))
+        s = np.where(mask, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h] = (p @ vs[:, h].astype(np.float32)) / p.sum(axis=1, keepdims=True)
+    return out
 
 
 def softmax_dense(q, k, v, text_k, text_v, T, N, C, anchors) -> np.ndarray:
@@ -104,9 +155,17 @@ def linear_dense(q, k, v, beta, text_k, text_v, T, N, C, anchors, alpha=None):
     return out
 
 
+def context_dense(inp, T, N, C, anchors=True):
+    """The text and audio query rows of the joint softmax, ``[n_text + n_audio, H, d]``."""
+    return joint_softmax_dense(inp, T, N, C, anchors)[:inp["ctx_q"].shape[0]]
+
+
 def layer_dense(inp, T, N, C, anchors=True, eps=1e-6):
     q = inp["q"]
-    o_s = softmax_dense(q, inp["k"], inp["v"], inp["text_k"], inp["text_v"], T, N, C, anchors)
+    if inp.get("audio_k") is not None:
+        o_s = joint_softmax_dense(inp, T, N, C, anchors)[-q.shape[0]:]
+    else:
+        o_s = softmax_dense(q, inp["k"], inp["v"], inp["text_k"], inp["text_v"], T, N, C, anchors)
     o_l = linear_dense(q, inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"], T, N, C, anchors,
                        inp.get("alpha"))
     q64 = q.astype(np.float64)

@@ -15,6 +15,9 @@ Sources (cited by page title and section; no other document is used):
 * [FTP] "Faster Than It Plays: Video DeltaNet Generates 14 Seconds of 768p Video in 11 Seconds"
   (ai-blog.deepmagic.app), section "Two branches instead of one", which prints the closed-form
   frame update S_t = (S_bar + B)(I + A)^-1 in text.
+* [GLN] "Video DeltaNet speeds MiniMax H3 video generation 14.5x" (glonce.com), its summary and
+  key facts: the hybrid attention replaces only video-to-video interactions; every interaction
+  with a text or audio token keeps the model's full softmax attention.
 
 Precision: the softmax branch is computed in float32 with float32 accumulation; the text
 initialisation, the per-frame solves, the two state scans, the readout and the merge are computed
@@ -39,7 +42,14 @@ Readings of points the pages leave open (each one is also listed in the design n
   initialisation starts from the zero state and is unaffected;
 * the linear-branch output is RMS-normalised over d with eps = 1e-6 and unit weight, gated by
   sigmoid(q @ W_gate[1]); the softmax branch is gated by sigmoid(q @ W_gate[0]); each gated
-  branch goes through its own projection and the two are summed (no residual).
+  branch goes through its own projection and the two are summed (no residual);
+* audio tokens (optional ``audio_k``, ``audio_v`` ``[n_audio, H, d]``): global keys of the
+  softmax branch exactly like the text keys (same normaliser), never written into the linear
+  memory (only the text prompt initialises it);
+* text and audio query rows (optional ``ctx_q`` ``[n_text + n_audio, H, d]``, text rows first):
+  one plain softmax over every token (text, audio and all video tokens), fp32; the result is the
+  attention output before any projection (the model's own output projection applies to it, as
+  it did before the hybrid layer).
 """
 
 from __future__ import annotations
@@ -105,11 +115,17 @@ def key_frames(t: int, T: int, C: int, anchors: bool) -> list[int]:
     return sorted(window + anc)
 
 
-def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None) -> np.ndarray:
+def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None,
+                   audio_v=None) -> np.ndarray:
     """o_s for every video token (``rows=None``) or for the given token indices; float32.
 
-    Returns an array shaped like ``q`` (``rows=None``) or ``[len(rows), H, d]``.
+    Global keys are the text tokens and, when given, the audio tokens ([GLN]: interactions with
+    audio stay in the softmax).  Returns an array shaped like ``q`` (``rows=None``) or
+    ``[len(rows), H, d]``.
     """
+    if audio_k is not None:
+        text_k = np.concatenate([text_k, audio_k], axis=0)
+        text_v = np.concatenate([text_v, audio_v], axis=0)
     TN, H, d = q.shape
     assert TN == T * N
     rows = np.arange(TN) if rows is None else np.asarray(rows)
@@ -268,18 +284,40 @@ def vdn_forward(inp: dict, T, N, C, anchors=True, rows=None, text_mode="half_bet
     """Layer output ``out`` [len(rows) or T*N, H, d] (fp64) from the inputs dict.
 
     ``inp`` holds float32 arrays: q, k, v, text_k, text_v, beta, gate_w, proj_w, and optionally
-    alpha ``[T, H, d]`` (the decay gate; absent = no decay).
+    alpha ``[T, H, d]`` (the decay gate; absent = no decay) and audio_k, audio_v
+    ``[n_audio, H, d]`` (global softmax keys; absent = none).  Video query rows only; the text
+    and audio query rows are ``context_rows``.
     """
     q, k, v = inp["q"], inp["k"], inp["v"]
     tk, tv = inp["text_k"], inp["text_v"]
     beta = inp["beta"]
     rows_arr = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
-    o_s = softmax_branch(q, k, v, tk, tv, T, N, C, anchors, rows_arr)
+    o_s = softmax_branch(q, k, v, tk, tv, T, N, C, anchors, rows_arr, inp.get("audio_k"), inp.get("audio_v"))
     o_l = linear_branch(q, k, v, beta, tk, tv, T, N, C, anchors, rows_arr, text_mode,
                         alpha=inp.get("alpha"))
     out = merge(q[rows_arr], o_s, o_l, inp["gate_w"], inp["proj_w"])
     if with_intermediates:
         return out, {"o_s": o_s, "o_l": o_l}
+    return out
+
+
+def context_rows(inp: dict, T, N) -> np.ndarray:
+    """Text and audio query rows ``[n_text + n_audio, H, d]`` (float32).
+
+    [GLN]: interactions that involve a text or audio token keep the full softmax attention, so a
+    text or audio query attends to every token of the sequence (text, audio and every video
+    frame) under one softmax, with the layer's scale 1/sqrt(d).
+    """
+    cq = inp["ctx_q"]
+    H = cq.shape[1]
+    parts_k = [inp["text_k"]] + ([inp["audio_k"]] if inp.get("audio_k") is not None else []) + [inp["k"]]
+    parts_v = [inp["text_v"]] + ([inp["audio_v"]] if inp.get("audio_v") is not None else []) + [inp["v"]]
+    assert inp["k"].shape[0] == T * N
+    out = np.zeros(cq.shape, np.float32)
+    for h in range(H):
+        keys = np.concatenate([p[:, h] for p in parts_k], axis=0)
+        vals = np.concatenate([p[:, h] for p in parts_v], axis=0)
+        out[:, h] = softmax_rows(cq[:, h], keys, vals)
     return out
 
 

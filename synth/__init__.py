@@ -64,13 +64,18 @@ def _round_bf16(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(torch.float32).numpy()
 
 
-def make_inputs(w: Workload, seed: int = 0, stress: bool = False, decay: bool = False) -> dict:
+def make_inputs(w: Workload, seed: int = 0, stress: bool = False, decay: bool = False, n_audio: int = 0,
+                ctx_rows: bool = False) -> dict:
     """float32 numpy inputs (bf16-rounded for bf16 workloads).
 
     ``stress=True`` replaces each frame's keys by normalise(shared + 0.1 * noise) so that one
     direction of the per-frame key Gram matrix is crowded (large top eigenvalue).
     ``decay=True`` adds ``alpha`` ``[T, H, d]`` float32 ~ U(0.5, 1), a per-frame channel-wise decay
     gate, drawn after every other input (so the other inputs do not change).
+    ``n_audio > 0`` adds audio tokens ``audio_k`` (L2-normalised N(0,1)) and ``audio_v`` (N(0,1)),
+    ``[n_audio, H, d]``; ``ctx_rows=True`` adds the text and audio query rows ``ctx_q``
+    ``[n_text + n_audio, H, d]`` (L2-normalised N(0,1)).  Both come from a second generator,
+    ``default_rng([seed, 1])``, drawn in that order, so the other inputs do not change.
     """
     rng = np.random.default_rng(seed)
     TN, H, d = w.T * w.N, w.H, w.d
@@ -97,9 +102,17 @@ def make_inputs(w: Workload, seed: int = 0, stress: bool = False, decay: bool = 
     out = dict(q=q, k=k, v=v, text_k=text_k, text_v=text_v, beta=beta, gate_w=gate_w, proj_w=proj_w)
     if decay:
         out["alpha"] = (0.5 + 0.5 * rng.random((w.T, H, d), dtype=f32)).astype(f32)
+    if n_audio > 0 or ctx_rows:
+        rng2 = np.random.default_rng([seed, 1])
+        if n_audio > 0:
+            out["audio_k"] = _l2n(rng2.standard_normal((n_audio, H, d), dtype=f32))
+            out["audio_v"] = rng2.standard_normal((n_audio, H, d), dtype=f32)
+        if ctx_rows:
+            out["ctx_q"] = _l2n(rng2.standard_normal((w.n_text + n_audio, H, d), dtype=f32))
     if w.dtype == "bf16":
-        for key in ("q", "k", "v", "text_k", "text_v", "gate_w", "proj_w"):
-            out[key] = _round_bf16(out[key])
+        for key in ("q", "k", "v", "text_k", "text_v", "gate_w", "proj_w", "audio_k", "audio_v", "ctx_q"):
+            if key in out:
+                out[key] = _round_bf16(out[key])
     return out
 
 

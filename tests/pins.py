@@ -518,3 +518,136 @@ def pin_bruteforce(orc, cases=BRUTE_CASES, seed=12):
         assert np.allclose(mids["o_s"], os_b, rtol=1e-5, atol=1e-6), ("o_s", ci)
         assert np.allclose(mids["o_l"], ol_b, rtol=1e-9, atol=1e-9), ("o_l", ci)
         assert np.allclose(out_s, out_b, rtol=1e-5, atol=1e-5), ("out", ci)
+
+
+# --------------------------------------------------------------------------------------------
+# Text and audio tokens in the joint sequence.  [GLN] = "Video DeltaNet speeds MiniMax H3 video
+# generation 14.5x" (glonce.com): the hybrid attention covers only video-to-video interactions;
+# any interaction with a text or audio token keeps the full softmax attention.
+# --------------------------------------------------------------------------------------------
+
+def joint_inputs(T, N, n_text, n_audio, H, d, seed):
+    """tiny_inputs plus audio tokens and the text/audio query rows."""
+    rng = _rng(seed + 1000)
+    inp = tiny_inputs(T, N, n_text, H, d, seed)
+    inp["audio_k"] = _unit(rng.standard_normal((n_audio, H, d))).astype(np.float32)
+    inp["audio_v"] = rng.standard_normal((n_audio, H, d)).astype(np.float32)
+    inp["ctx_q"] = _unit(rng.standard_normal((n_text + n_audio, H, d))).astype(np.float32)
+    return inp
+
+
+def golden_attention_map():
+    rows = {}
+    with open(os.path.join(GOLDEN, "attention_map_T16_C2_text1_audio1.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            label, entries = line.split("|")
+            rows[label.strip()] = entries.split()
+    return rows
+
+
+def pin_golden_attention_map(orc):
+    """The hand-derived branch map of the visualisation workload (1 text, 1 audio token, 16 frames,
+    chunks of 2).  Softmax visibility is read off the oracle's outputs with identical keys and a
+    one-hot value per key (a uniform softmax over the visible keys), for the video rows and for
+    the text/audio rows; 'B' and 'L' entries are read off the linear branch: changing a frame's
+    or the text's values moves o_l exactly when the map says the key reaches the linear memory."""
+    gold = golden_attention_map()
+    T, N, C, H, d = 16, 1, 2, 1, 18
+    labels = ["text", "audio"] + [f"f{t}" for t in range(T)]
+    assert list(gold) == labels
+    # column j of the sequence [text, audio, f0..f15] carries value e_j
+    e = np.eye(d, dtype=np.float32)
+    q = np.zeros((T, H, d), np.float32)
+    q[..., 0] = 1
+    inp = dict(q=q, k=np.array(q), v=e[2:][:, None, :].copy(),
+               text_k=np.array(q[:1]), text_v=e[0][None, None, :].copy(),
+               audio_k=np.array(q[:1]), audio_v=e[1][None, None, :].copy(),
+               ctx_q=np.array(q[:2]))
+    o_s = orc.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], T, N, C, True,
+                             audio_k=inp["audio_k"], audio_v=inp["audio_v"])
+    o_c = orc.context_rows(inp, T, N)
+    seen = np.concatenate([o_c[:, 0], o_s[:, 0]]) > 1e-6          # [query][key]
+    soft = np.array([[x in ("S", "B") for x in gold[lab]] for lab in labels])
+    assert (seen == soft).all(), np.argwhere(seen != soft)
+    assert (bruteforce.joint_mask(1, 1, T, N, C, True) == soft).all()
+    # linear memory: perturb one key's value and see which video rows' o_l move
+    rng = _rng(30)
+    base = tiny_inputs(T, N, 1, H, 6, 31)
+    base["audio_k"] = _unit(rng.standard_normal((1, H, 6))).astype(np.float32)
+    base["audio_v"] = rng.standard_normal((1, H, 6)).astype(np.float32)
+    ref = orc.vdn_forward(base, T, N, C, True, with_intermediates=True)[1]["o_l"]
+    for j, lab in enumerate(labels):
+        pert = {key: np.array(val) for key, val in base.items()}
+        if j == 0:
+            pert["text_v"] += 1.0
+        elif j == 1:
+            pert["audio_v"] += 1.0
+        else:
+            pert["v"][j - 2] += 1.0
+        o_l = orc.vdn_forward(pert, T, N, C, True, with_intermediates=True)[1]["o_l"]
+        moved = np.abs(o_l - ref).max(axis=(1, 2)) > 1e-9
+        expect = np.array([gold[f"f{t}"][j] in ("B", "L") for t in range(T)])
+        assert (moved == expect).all(), (lab, np.nonzero(moved != expect))
+
+
+def pin_context_rows_sdpa(orc, seed=32):
+    """Text and audio query rows are plain softmax attention over the whole sequence: torch's CPU
+    scaled_dot_product_attention in float64 on the concatenated keys and values."""
+    import torch
+    for ci, (T, N, n_text, n_audio, H, d) in enumerate([(5, 3, 2, 3, 2, 8), (3, 4, 0, 2, 1, 16),
+                                                         (4, 2, 3, 0, 2, 4)]):
+        inp = joint_inputs(T, N, n_text, n_audio, H, d, seed + ci)
+        got = orc.context_rows(inp, T, N)
+        assert got.shape == (n_text + n_audio, H, d)
+        for h in range(H):
+            kk = np.concatenate([inp["text_k"][:, h], inp["audio_k"][:, h], inp["k"][:, h]]).astype(np.float64)
+            vv = np.concatenate([inp["text_v"][:, h], inp["audio_v"][:, h], inp["v"][:, h]]).astype(np.float64)
+            qq = inp["ctx_q"][:, h].astype(np.float64)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qq)[None, None], torch.from_numpy(kk)[None, None],
+                torch.from_numpy(vv)[None, None])[0, 0].numpy()
+            assert np.allclose(got[:, h], ref, atol=2e-6), (ci, h)
+
+
+def pin_audio_softmax_only(orc, seed=33):
+    """Audio tokens are softmax keys only: changing them moves o_s of every video row and leaves
+    o_l bit for bit unchanged (the linear memory is initialised from the text alone)."""
+    T, N, C, n_text, n_audio, H, d = 9, 2, 2, 2, 3, 2, 6
+    inp = joint_inputs(T, N, n_text, n_audio, H, d, seed)
+    _, a = orc.vdn_forward(inp, T, N, C, True, with_intermediates=True)
+    pert = dict(inp)
+    pert["audio_k"] = _unit(inp["audio_k"] + 0.5).astype(np.float32)
+    pert["audio_v"] = inp["audio_v"] + 1.0
+    _, b = orc.vdn_forward(pert, T, N, C, True, with_intermediates=True)
+    assert np.array_equal(a["o_l"], b["o_l"])
+    assert (np.abs(a["o_s"] - b["o_s"]).max(axis=(1, 2)) > 1e-4).all()
+
+
+JOINT_CASES = [
+    # T, N, C, n_text, n_audio, H, d, anchors
+    (16, 1, 2, 1, 1, 1, 8, True),
+    (7, 3, 2, 2, 3, 2, 4, True),
+    (6, 2, 1, 0, 2, 1, 4, False),
+    (1, 4, 5, 3, 1, 1, 4, True),
+    (10, 2, 3, 2, 0, 2, 6, True),
+]
+
+
+def pin_bruteforce_joint(orc, seed=34):
+    """The structured oracle with audio keys and text/audio query rows equals the brute-force
+    oracle, whose single dense mask over [text, audio, video] is built entry by entry from the
+    token kinds."""
+    for ci, (T, N, C, n_text, n_audio, H, d, anchors) in enumerate(JOINT_CASES):
+        inp = joint_inputs(T, N, n_text, n_audio, H, d, seed + ci)
+        if n_audio == 0:
+            inp.pop("audio_k")
+            inp.pop("audio_v")
+        out_s, mids = orc.vdn_forward(inp, T, N, C, anchors, with_intermediates=True)
+        out_b, os_b, ol_b = bruteforce.layer_dense(inp, T, N, C, anchors)
+        assert np.allclose(mids["o_s"], os_b, rtol=1e-5, atol=1e-6), ("o_s", ci)
+        assert np.allclose(mids["o_l"], ol_b, rtol=1e-9, atol=1e-9), ("o_l", ci)
+        assert np.allclose(out_s, out_b, rtol=1e-5, atol=1e-5), ("out", ci)
+        ctx = orc.context_rows(inp, T, N)
+        assert np.allclose(ctx, bruteforce.context_dense(inp, T, N, C, anchors), rtol=1e-5, atol=1e-6), ("ctx", ci)

@@ -198,6 +198,55 @@ def m_decay_reverse_uses_next_frame(o):
     o.head_states = head_states
 
 
+def m_audio_written_to_linear(o):
+    """Audio tokens treated as more prompt: appended to the text for both branches, so they are
+    also written into the linear memory at initialisation (unit write strength)."""
+    orig = o.vdn_forward
+
+    def vdn_forward(inp, T, N, C, anchors=True, rows=None, text_mode="half_beta", with_intermediates=False):
+        if inp.get("audio_k") is None:
+            return orig(inp, T, N, C, anchors, rows, text_mode, with_intermediates)
+        n_text, n_audio, H = inp["text_k"].shape[0], inp["audio_k"].shape[0], inp["q"].shape[1]
+        mod = {key: val for key, val in inp.items() if key not in ("audio_k", "audio_v")}
+        mod["text_k"] = np.concatenate([inp["text_k"], inp["audio_k"]])
+        mod["text_v"] = np.concatenate([inp["text_v"], inp["audio_v"]])
+        mod["beta"] = np.concatenate([inp["beta"][:n_text], np.ones((n_audio, H), np.float32), inp["beta"][n_text:]])
+        return orig(mod, T, N, C, anchors, rows, text_mode, with_intermediates)
+    o.vdn_forward = vdn_forward
+
+
+def m_audio_dropped_from_softmax(o):
+    orig = o.softmax_branch
+
+    def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None):
+        return orig(q, k, v, text_k, text_v, T, N, C, anchors, rows)
+    o.softmax_branch = softmax_branch
+
+
+def m_context_rows_context_only(o):
+    """Text and audio queries attend only to the text and audio tokens."""
+    def context_rows(inp, T, N):
+        cq = inp["ctx_q"]
+        out = np.zeros(cq.shape, np.float32)
+        for h in range(cq.shape[1]):
+            keys = np.concatenate([inp["text_k"][:, h], inp["audio_k"][:, h]])
+            vals = np.concatenate([inp["text_v"][:, h], inp["audio_v"][:, h]])
+            out[:, h] = o.softmax_rows(cq[:, h], keys, vals)
+        return out
+    o.context_rows = context_rows
+
+
+def m_context_rows_unscaled(o):
+    """The 1/sqrt(d) score scale forgotten on the text and audio query rows."""
+    orig = o.context_rows
+
+    def context_rows(inp, T, N):
+        mod = dict(inp)
+        mod["ctx_q"] = inp["ctx_q"] * np.float32(np.sqrt(inp["ctx_q"].shape[-1]))
+        return orig(mod, T, N)
+    o.context_rows = context_rows
+
+
 MUTANTS = [
     (m_drop_sbar, pins.pin_objective_minimum),
     (m_minus_gram, pins.pin_spectrum),
@@ -216,6 +265,10 @@ MUTANTS = [
     (m_decay_on_rows, pins.pin_decay_columns),
     (m_decay_after_solve, pins.pin_decay_columns),
     (m_decay_reverse_uses_next_frame, pins.pin_decay_columns),
+    (m_audio_written_to_linear, pins.pin_audio_softmax_only),
+    (m_audio_dropped_from_softmax, pins.pin_golden_attention_map),
+    (m_context_rows_context_only, pins.pin_context_rows_sdpa),
+    (m_context_rows_unscaled, pins.pin_context_rows_sdpa),
 ]
 
 

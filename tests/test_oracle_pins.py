@@ -15,7 +15,8 @@ from oracle import vdn_oracle as orc
     pins.pin_uniform_keys_visibility, pins.pin_beta_zero, pins.pin_text_once,
     pins.pin_boundary_text_only, pins.pin_gate_closed_forms, pins.pin_bruteforce,
     pins.pin_decay_one, pins.pin_decay_zero, pins.pin_decay_columns, pins.pin_decay_nonexpansive,
-    pins.pin_bruteforce_decay,
+    pins.pin_bruteforce_decay, pins.pin_golden_attention_map, pins.pin_context_rows_sdpa,
+    pins.pin_audio_softmax_only, pins.pin_bruteforce_joint,
 ], ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(orc)
