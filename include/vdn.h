@@ -29,10 +29,22 @@
  * With anchors off there are no boundary frames: no anchor keys, and frames 0 and T-1 are
  * written into the states like any other frame.
  *
+ * Text and audio tokens ("Video DeltaNet speeds MiniMax H3 video generation 14.5x" (glonce.com),
+ * summary and key facts: only video-to-video interactions become hybrid; every interaction with a
+ * text or audio token keeps the full softmax attention).  A plan may carry n_audio audio tokens
+ * after the n_text text tokens (the n_ctx = n_text + n_audio context tokens): audio keys are
+ * global keys of the softmax branch exactly like the text keys, and are never written into the
+ * linear memory.  The text and audio query rows (vdn_forward_joint) get one plain softmax over
+ * every token, o_c = softmax(q_c K^T / sqrt(d)) V over the context and all T*N video tokens,
+ * returned before any projection (the model's own output projection applies to those rows).
+ *
  * Layouts (row-major, token-major, head inside the token; every pointer is a DEVICE pointer):
  *   q, k, v, out : [T*N][H][d]         element type = the plan's dtype
  *   beta         : [n_text + T*N][H]    float32, text rows first; beta >= 0
- *   text_kv      : [2][n_text][H][d]    keys then values, plan dtype (may be NULL if n_text == 0)
+ *   text_kv      : [2][n_ctx][H][d]     keys then values of the context tokens, text rows first,
+ *                                       then audio (n_ctx = n_text for plans without audio), plan
+ *                                       dtype (may be NULL if n_ctx == 0)
+ *   ctx_q, ctx_out : [n_ctx][H][d]      context query rows and their output (vdn_forward_joint)
  *   gate_w       : [2][d][d]            [in][out] (y = x W); [0] softmax gate, [1] linear gate
  *   proj_w       : [2][d][d]            [in][out]; [0] softmax projection, [1] linear projection
  * The weights are shared by all heads.  q, k and text keys are expected L2-normalised per
@@ -88,6 +100,13 @@ enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4 }
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,
                               vdn_dtype dtype, unsigned flags, vdn_plan **plan_out);
 
+/* As vdn_plan_create_ex, for a sequence with n_audio >= 0 audio tokens after the n_text text
+ * tokens (see "Text and audio tokens" above).  n_audio = 0 is vdn_plan_create_ex.  Every forward
+ * entry point then takes text_kv as [2][n_text + n_audio][H][d]. */
+vdn_status vdn_plan_create_joint(int T, int N, int C, int n_text, int n_audio, int H, int d,
+                                 int anchors, vdn_dtype dtype, unsigned flags,
+                                 vdn_plan **plan_out);
+
 /* Enqueue the whole layer forward on `stream` (a hipStream_t; NULL = the null stream).  Returns
  * after enqueueing.  Every pointer must be 16-byte aligned.  See the layouts above. */
 vdn_status vdn_forward(const vdn_plan *plan, const void *q, const void *k, const void *v,
@@ -107,6 +126,20 @@ vdn_status vdn_forward_decay(const vdn_plan *plan, const void *q, const void *k,
                              const float *beta, const void *text_kv, const float *alpha,
                              const void *gate_w, const void *proj_w, void *out, void *stream);
 
+/* The whole joint sequence: vdn_forward (alpha NULL) or vdn_forward_decay (alpha non-NULL) for
+ * the video rows, plus, when ctx_q and ctx_out are both non-NULL, the context (text and audio)
+ * query rows: ctx_out[j] = softmax over every key of the plan's sequence for query ctx_q[j]
+ * ("Video DeltaNet speeds MiniMax H3 video generation 14.5x", summary: text and audio
+ * interactions keep the full softmax attention).  ctx_q and ctx_out are [n_ctx][H][d] in the
+ * plan's dtype, device memory owned by the caller, 16-byte aligned; ctx_out must not alias any
+ * other argument.  ctx_q and ctx_out both NULL computes no context rows; exactly one NULL is
+ * VDN_ERR_INVALID_ARG.  With n_ctx = 0 they are ignored.  Other arguments and errors as
+ * vdn_forward_decay, except that alpha may be NULL (no decay). */
+vdn_status vdn_forward_joint(const vdn_plan *plan, const void *q, const void *k, const void *v,
+                             const float *beta, const void *ctx_q, const void *ctx_kv,
+                             const float *alpha, const void *gate_w, const void *proj_w,
+                             void *out, void *ctx_out, void *stream);
+
 /* Free the plan's workspace, stream and events.  The caller must have synchronised the streams
  * the plan was used on.  NULL is a no-op. */
 void vdn_plan_destroy(vdn_plan *plan);
@@ -118,8 +151,9 @@ const char *vdn_status_str(vdn_status s);
 size_t vdn_plan_workspace_bytes(const vdn_plan *plan);
 
 /* Host only, no GPU needed.  Key ranges of the softmax branch for query frame t, in the key index
- * space of one head: text key j is index j; video token j (= f*N + n) is index text_pad + j where
- * text_pad = n_text rounded up to a multiple of 64.  Writes up to max_ranges [start, end) pairs
+ * space of one head: global (text, then audio) key j is index j; video token j (= f*N + n) is
+ * index text_pad + j where text_pad = n_text rounded up to a multiple of 64.  Here n_text counts
+ * every global key (n_text + n_audio of a joint plan).  Writes up to max_ranges [start, end) pairs
  * into ranges[2*r], ranges[2*r+1] in ascending order and returns their number, or -1 on an
  * invalid argument.  Empty ranges are omitted. */
 int vdn_key_ranges(int T, int N, int C, int n_text, int anchors, int t, int64_t *ranges,

@@ -45,7 +45,7 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.kmax = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax) : nullptr;
   b.flags = p->kinds.softmax_mfma ? reinterpret_cast<int*>(ws + p->lay.flags) : nullptr;
   b.ranges = reinterpret_cast<const int*>(ws + p->lay.ranges);
-  b.nranges = b.ranges + (size_t)p->s.T * 2 * vdn::kMaxRanges;
+  b.nranges = b.ranges + (size_t)(p->s.T + 1) * 2 * vdn::kMaxRanges;
   return b;
 }
 
@@ -64,12 +64,14 @@ bool shape_ok(int T, int N, int C, int n_text, int H, int d, int anchors) {
   return T > 0 && N > 0 && C > 0 && n_text >= 0 && H > 0 && d > 0 && (anchors == 0 || anchors == 1);
 }
 
-vdn::Shape make_shape(int T, int N, int C, int n_text, int H, int d, int anchors, vdn_dtype dt) {
+vdn::Shape make_shape(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors, vdn_dtype dt) {
   vdn::Shape s{};
   s.T = T; s.N = N; s.C = C; s.n_text = n_text; s.H = H; s.d = d; s.anchors = anchors; s.dtype = dt;
+  s.n_audio = n_audio;
+  s.n_ctx = n_text + n_audio;
   s.Nc = (T + C - 1) / C;
-  s.text_pad = (int)vdn::round_up(n_text, vdn::kTextPad);
-  s.Lk = (int64_t)s.text_pad + (int64_t)T * N;
+  s.ctx_pad = (int)vdn::round_up(s.n_ctx, vdn::kTextPad);
+  s.Lk = (int64_t)s.ctx_pad + (int64_t)T * N;
   s.Ls = s.Lk + 64;
   return s;
 }
@@ -92,7 +94,7 @@ const char* vdn_status_str(vdn_status s) {
 int vdn_key_ranges(int T, int N, int C, int n_text, int anchors, int t, int64_t* ranges, int max_ranges) {
   if (!shape_ok(T, N, C, n_text, 1, 1, anchors) || t < 0 || t >= T || (max_ranges > 0 && !ranges) || max_ranges < 0)
     return -1;
-  vdn::Shape s = make_shape(T, N, C, n_text, 1, 1, anchors, VDN_F32);
+  vdn::Shape s = make_shape(T, N, C, n_text, 0, 1, 1, anchors, VDN_F32);
   return vdn::key_ranges(s, t, ranges, max_ranges);
 }
 
@@ -100,7 +102,7 @@ int vdn_scan_frames(int T, int C, int anchors, int t, int dir, int* frames, int 
   if (!shape_ok(T, 1, C, 0, 1, 1, anchors) || t < 0 || t >= T || (dir != 0 && dir != 1) ||
       (max_frames > 0 && !frames) || max_frames < 0)
     return -1;
-  vdn::Shape s = make_shape(T, 1, C, 0, 1, 1, anchors, VDN_F32);
+  vdn::Shape s = make_shape(T, 1, C, 0, 0, 1, 1, anchors, VDN_F32);
   return vdn::scan_frames(s, t, dir, frames, max_frames);
 }
 
@@ -111,22 +113,28 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
 
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors, vdn_dtype dtype,
                               unsigned flags, vdn_plan** plan_out) {
+  return vdn_plan_create_joint(T, N, C, n_text, 0, H, d, anchors, dtype, flags, plan_out);
+}
+
+vdn_status vdn_plan_create_joint(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors,
+                                 vdn_dtype dtype, unsigned flags, vdn_plan** plan_out) {
   if (!plan_out) return VDN_ERR_INVALID_ARG;
   *plan_out = nullptr;
-  if (!shape_ok(T, N, C, n_text, H, d, anchors)) return VDN_ERR_INVALID_ARG;
+  if (!shape_ok(T, N, C, n_text, H, d, anchors) || n_audio < 0) return VDN_ERR_INVALID_ARG;
+  const int64_t n_ctx = (int64_t)n_text + n_audio;
   if (dtype != VDN_F32 && dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (d != 16 && d != 32 && d != 64 && d != 128) return VDN_ERR_UNSUPPORTED;
   // keep every index well inside 63 bits and grid dimensions inside their limits
   const int64_t tokens = (int64_t)T * N;
-  if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || (int64_t)n_text * H * d > (int64_t(1) << 40))
+  if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || n_ctx * H * d > (int64_t(1) << 40))
     return VDN_ERR_UNSUPPORTED;
   if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
   if ((flags & VDN_FLAG_SERIAL) && (flags & VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
-  if ((int64_t)vdn::round_up(n_text, vdn::kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
+  if (vdn::round_up(n_ctx, vdn::kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
 
   vdn_plan* p = new (std::nothrow) vdn_plan();
   if (!p) return VDN_ERR_OUT_OF_MEMORY;
-  p->s = make_shape(T, N, C, n_text, H, d, anchors, dtype);
+  p->s = make_shape(T, N, C, n_text, n_audio, H, d, anchors, dtype);
   p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
   p->overlap = (flags & VDN_FLAG_OVERLAP) != 0;
   p->lay = vdn::make_layout(p->s, p->kinds);
@@ -137,13 +145,13 @@ vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int
     free_plan(p);
     return VDN_ERR_OUT_OF_MEMORY;
   }
-  // per-frame key-range table
-  std::vector<int> tab((size_t)T * (2 * vdn::kMaxRanges + 1), 0);
-  for (int t = 0; t < T; ++t) {
+  // key-range table: one row per query frame, then one for the context (text and audio) rows
+  std::vector<int> tab((size_t)(T + 1) * (2 * vdn::kMaxRanges + 1), 0);
+  for (int t = 0; t <= T; ++t) {
     int64_t r[2 * vdn::kMaxRanges];
     int n = vdn::key_ranges(p->s, t, r, vdn::kMaxRanges);
     for (int i = 0; i < 2 * n; ++i) tab[(size_t)t * 2 * vdn::kMaxRanges + i] = (int)r[i];
-    tab[(size_t)T * 2 * vdn::kMaxRanges + t] = n;
+    tab[(size_t)(T + 1) * 2 * vdn::kMaxRanges + t] = n;
   }
   // the packed K/V padding tile must hold finite values (zero); the packing pass never writes it
   if ((p->kinds.softmax_mfma &&
@@ -180,21 +188,30 @@ vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
 namespace {
 
 vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
-                        const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w, void* out,
-                        void* stream) {
+                        const void* ctx_q, const void* text_kv, const float* alpha, const void* gate_w,
+                        const void* proj_w, void* out, void* ctx_out, void* stream) {
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !out) return VDN_ERR_INVALID_ARG;
-  if (plan->s.n_text > 0 && !text_kv) return VDN_ERR_INVALID_ARG;
+  if (plan->s.n_ctx > 0 && !text_kv) return VDN_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, out};
   for (const void* ptr : ptrs) if (!aligned16(ptr)) return VDN_ERR_INVALID_ARG;
   if (text_kv && !aligned16(text_kv)) return VDN_ERR_INVALID_ARG;
   if (out == q || out == k || out == v || out == text_kv) return VDN_ERR_INVALID_ARG;
+  if (alpha && (!aligned16(alpha) || alpha == out)) return VDN_ERR_INVALID_ARG;
+  if (!ctx_q != !ctx_out) return VDN_ERR_INVALID_ARG;          // context rows: both or neither
+  if (plan->s.n_ctx == 0) ctx_q = ctx_out = nullptr;
+  if (ctx_out) {
+    if (!aligned16(ctx_q) || !aligned16(ctx_out)) return VDN_ERR_INVALID_ARG;
+    const void* inputs[] = {q, k, v, beta, ctx_q, text_kv, alpha, gate_w, proj_w};
+    for (const void* ptr : inputs) if (ctx_out == ptr) return VDN_ERR_INVALID_ARG;
+    if (ctx_out == out) return VDN_ERR_INVALID_ARG;
+  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
   if (dev != plan->device) return VDN_ERR_INVALID_ARG;
 
   const vdn::Shape& s = plan->s;
   hipStream_t main = reinterpret_cast<hipStream_t>(stream);
-  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out, alpha};
+  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out, alpha, ctx_q, ctx_out};
   vdn::Buffers b = buffers_of(plan);
 
   hipEvent_t* ev = nullptr;
@@ -246,14 +263,20 @@ vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, cons
 
 vdn_status vdn_forward(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
                        const void* text_kv, const void* gate_w, const void* proj_w, void* out, void* stream) {
-  return forward_impl(plan, q, k, v, beta, text_kv, nullptr, gate_w, proj_w, out, stream);
+  return forward_impl(plan, q, k, v, beta, nullptr, text_kv, nullptr, gate_w, proj_w, out, nullptr, stream);
 }
 
 vdn_status vdn_forward_decay(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
                              const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
                              void* out, void* stream) {
-  if (!alpha || !aligned16(alpha) || alpha == out) return VDN_ERR_INVALID_ARG;
-  return forward_impl(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, out, stream);
+  if (!alpha) return VDN_ERR_INVALID_ARG;
+  return forward_impl(plan, q, k, v, beta, nullptr, text_kv, alpha, gate_w, proj_w, out, nullptr, stream);
+}
+
+vdn_status vdn_forward_joint(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                             const void* ctx_q, const void* ctx_kv, const float* alpha, const void* gate_w,
+                             const void* proj_w, void* out, void* ctx_out, void* stream) {
+  return forward_impl(plan, q, k, v, beta, ctx_q, ctx_kv, alpha, gate_w, proj_w, out, ctx_out, stream);
 }
 
 vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes) {

@@ -20,9 +20,9 @@ int key_ranges(const Shape& s, int t, int64_t* r, int max_ranges) {
   auto add = [&](int64_t a, int64_t b) {
     if (b > a) { tmp[2 * n] = a; tmp[2 * n + 1] = b; ++n; }
   };
-  const int64_t base = s.text_pad, N = s.N;
-  add(0, s.n_text);
-  if (is_boundary(s, t)) {
+  const int64_t base = s.ctx_pad, N = s.N;
+  add(0, s.n_ctx);
+  if (t == s.T || is_boundary(s, t)) {                                  // context rows, boundary frames
     add(base, base + (int64_t)s.T * N);
   } else {
     const int c = t / s.C;
@@ -71,8 +71,8 @@ Layout make_layout(const Shape& s, const Kinds& k) {
   L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
   L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;
   L.kmax = mfma_softmax ? take((size_t)s.H * 4) : 0;
-  L.flags = mfma_softmax ? take((size_t)softmax_grid(s) * 4) : 0;
-  L.ranges = take((size_t)s.T * (2 * kMaxRanges + 1) * 4);
+  L.flags = mfma_softmax ? take((size_t)softmax_grid(s, true) * 4) : 0;
+  L.ranges = take((size_t)(s.T + 1) * (2 * kMaxRanges + 1) * 4);
   L.total = off;
   return L;
 }

@@ -1,13 +1,14 @@
 // Packing of keys and values for the MFMA softmax kernel.
 //
 // The softmax branch reads, for every query chunk, a few contiguous ranges of keys of one head
-// (text, window, anchors).  Packing once per forward gives every head one contiguous key space
-// [text (padded to 64) | video tokens] so each key tile is one dense 64 x d block:
+// (global keys, window, anchors).  Packing once per forward gives every head one contiguous key
+// space [text, audio (padded together to 64) | video tokens] so each key tile is one dense 64 x d
+// block:
 //   Kp [H][Ls][d]   keys, bf16, row per key
 //   Vt [H][d][Ls]   values transposed, bf16, so that the P.V contraction (over keys) reads
 //                   key-contiguous 16-byte fragments
 // Ls = Lk + 64: one tile of zero keys past the end (zeroed at plan creation, never written here)
-// so that a tile load never leaves the buffer.  Padding keys (n_text <= j < text_pad) are zero;
+// so that a tile load never leaves the buffer.  Padding keys (n_ctx <= j < ctx_pad) are zero;
 // the softmax kernel masks them.
 // The same pass records the largest key norm of each 64-key block; a second tiny kernel reduces
 // them to the largest key norm of each head, which bounds every score of the head
@@ -22,9 +23,9 @@ namespace vdn {
 namespace {
 
 __global__ __launch_bounds__(256) void prep_kv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                                                      const bf16_t* __restrict__ text_kv, bf16_t* __restrict__ kp,
+                                                      const bf16_t* __restrict__ ctx_kv, bf16_t* __restrict__ kp,
                                                       bf16_t* __restrict__ vt, float* __restrict__ kmax_part, int H,
-                                                      int D, int n_text, int text_pad, int64_t Lk, int64_t Ls) {
+                                                      int D, int n_ctx, int ctx_pad, int64_t Lk, int64_t Ls) {
   const int64_t key0 = (int64_t)blockIdx.x * 64;
   const int h = blockIdx.y;
   __shared__ bf16_t tile[64][64 + 2];
@@ -38,12 +39,12 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const bf16_t* __restrict__
       const int64_t j = key0 + r;
       uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
       if (j < Lk) {
-        if (j < n_text) {
+        if (j < n_ctx) {
           const int64_t off = (j * H + h) * D + d0 + c * 8;
-          kk = *reinterpret_cast<const uint4*>(text_kv + off);
-          vv = *reinterpret_cast<const uint4*>(text_kv + (int64_t)n_text * H * D + off);
-        } else if (j >= text_pad) {
-          const int64_t off = ((j - text_pad) * H + h) * D + d0 + c * 8;
+          kk = *reinterpret_cast<const uint4*>(ctx_kv + off);
+          vv = *reinterpret_cast<const uint4*>(ctx_kv + (int64_t)n_ctx * H * D + off);
+        } else if (j >= ctx_pad) {
+          const int64_t off = ((j - ctx_pad) * H + h) * D + d0 + c * 8;
           kk = *reinterpret_cast<const uint4*>(k + off);
           vv = *reinterpret_cast<const uint4*>(v + off);
         }
@@ -107,7 +108,7 @@ hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hi
   const int nblk = (int)((s.Lk + 63) / 64);
   prep_kv_kernel<<<dim3(nblk, s.H), 256, 0, st>>>((const bf16_t*)in.k, (const bf16_t*)in.v,
                                                   (const bf16_t*)in.text_kv, b.kp, b.vt, b.kmax_part, s.H, s.d,
-                                                  s.n_text, s.text_pad, s.Lk, s.Ls);
+                                                  s.n_ctx, s.ctx_pad, s.Lk, s.Ls);
   kmax_reduce_kernel<<<s.H, 256, 0, st>>>(b.kmax_part, b.kmax, nblk);
   return hipGetLastError();
 }

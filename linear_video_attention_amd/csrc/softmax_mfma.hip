@@ -91,16 +91,18 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 struct Params {
   const bf16_t* q;
+  const bf16_t* qc;         // context (text, audio) query rows [n_ctx][H][D], or unused
   const bf16_t* kp;
   const bf16_t* vt;
   bf16_t* o_s;
+  bf16_t* oc;               // their output [n_ctx][H][D]
   const int* ranges;
   const int* nranges;
   const float* kmax;
   int* flags;
-  int T, N, H;
+  int T, N, H, n_ctx;
   int64_t Ls;
-  int QT, n_bnd_wg, n_int_frames, first_int_frame, per_xcd, n_int_wg;
+  int QT, QTc, n_ctx_wg, n_bnd_wg, n_int_frames, first_int_frame, per_xcd, n_int_wg;
   float c_log2;
 };
 
@@ -118,17 +120,23 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   if constexpr (FALLBACK) {
     if (P.flags[w] == 0) return;
   }
-  // ---- workgroup -> (head, frame, query tile) ----
+  // ---- workgroup -> (head, frame, query tile); the context rows (every key) come first as
+  // pseudo-frame T, then the boundary frames, then the interior frames ----
   int h, t, qt;
-  if (w < P.n_bnd_wg) {
-    qt = w % P.QT;
-    const int rest = w / P.QT;
+  if (w < P.n_ctx_wg) {
+    qt = w % P.QTc;
+    h = w / P.QTc;
+    t = P.T;
+  } else if (w - P.n_ctx_wg < P.n_bnd_wg) {
+    const int wb = w - P.n_ctx_wg;
+    qt = wb % P.QT;
+    const int rest = wb / P.QT;
     const int nb = P.n_bnd_wg / (P.QT * P.H);
     const int bi = rest % nb;
     h = rest / nb;
     t = bi == 0 ? 0 : P.T - 1;
   } else {
-    const int wp = w - P.n_bnd_wg;
+    const int wp = w - P.n_ctx_wg - P.n_bnd_wg;
     const int L = (w & 7) * P.per_xcd + (wp >> 3);
     if (L >= P.n_int_wg) {
       if constexpr (!FALLBACK) {
@@ -141,8 +149,13 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
     t = P.first_int_frame + rest % P.n_int_frames;
     h = rest / P.n_int_frames;
   }
-  const int N = P.N, H = P.H;
+  const int H = P.H;
   const int64_t Ls = P.Ls;
+  // this workgroup's query rows: nrows rows of stride H*D from qsrc, results to odst
+  const bool ctx = t == P.T;
+  const int nrows = ctx ? P.n_ctx : P.N;
+  const bf16_t* qsrc = ctx ? P.qc + (int64_t)h * D : P.q + ((int64_t)t * P.N * H + h) * D;
+  bf16_t* odst = ctx ? P.oc + (int64_t)h * D : P.o_s + ((int64_t)t * P.N * H + h) * D;
   const float c_log2 = P.c_log2;
 
   const int tid = threadIdx.x;
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 val = {0, 0, 0, 0};
-      if (n < N) val = *reinterpret_cast<const u32x4*>(P.q + (((int64_t)t * N + n) * H + h) * D + ks * 16 + hl * 8);
+      if (n < nrows) val = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)n * H * D + ks * 16 + hl * 8);
       qf[qs][ks] = as_bf16x8(val);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qn2[qs] += (float)qf[qs][ks][e] * (float)qf[qs][ks][e];
@@ -483,8 +496,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
     const float tot = lsum[qs] + __shfl_xor(lsum[qs], 32);
     const float inv = 1.0f / tot;
     const int n = n_base + qs * 32 + l32;
-    if (n < N) {
-      bf16_t* op = P.o_s + (((int64_t)t * N + n) * H + h) * D;
+    if (n < nrows) {
+      bf16_t* op = odst + (int64_t)n * H * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -502,9 +515,11 @@ template <int D>
 void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   Params P{};
   P.q = (const bf16_t*)in.q;
+  P.qc = (const bf16_t*)in.ctx_q;
   P.kp = b.kp;
   P.vt = b.vt;
   P.o_s = (bf16_t*)b.os;
+  P.oc = (bf16_t*)in.ctx_out;
   P.ranges = b.ranges;
   P.nranges = b.nranges;
   P.kmax = b.kmax;
@@ -512,8 +527,11 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   P.T = s.T;
   P.N = s.N;
   P.H = s.H;
+  P.n_ctx = s.n_ctx;
   P.Ls = s.Ls;
   P.QT = (s.N + kBQ - 1) / kBQ;
+  P.QTc = (s.n_ctx + kBQ - 1) / kBQ;
+  P.n_ctx_wg = in.ctx_out ? P.QTc * s.H : 0;
   const bool two_bnd = s.anchors && s.T > 1;
   const int nb = s.anchors ? (two_bnd ? 2 : 1) : 0;
   P.n_int_frames = s.T - nb;
@@ -522,7 +540,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   P.n_int_wg = P.n_int_frames * P.QT * s.H;
   P.per_xcd = (P.n_int_wg + 7) / 8;
   P.c_log2 = 1.4426950408889634f / sqrtf((float)D);
-  const int grid = softmax_grid(s);
+  const int grid = softmax_grid(s, in.ctx_out != nullptr);
   const size_t smem = kStages * Smem<D>::STAGE;
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
@@ -534,12 +552,13 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
 
 }  // namespace
 
-int softmax_grid(const Shape& s) {
+int softmax_grid(const Shape& s, bool with_ctx) {
   const int QT = (s.N + kBQ - 1) / kBQ;
   const int nb = s.anchors ? (s.T > 1 ? 2 : 1) : 0;
+  const int n_ctx_wg = with_ctx ? (s.n_ctx + kBQ - 1) / kBQ * s.H : 0;
   const int n_bnd_wg = nb * QT * s.H;
   const int n_int_wg = (s.T - nb) * QT * s.H;
-  return n_bnd_wg + 8 * ((n_int_wg + 7) / 8);
+  return n_ctx_wg + n_bnd_wg + 8 * ((n_int_wg + 7) / 8);
 }
 
 hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {

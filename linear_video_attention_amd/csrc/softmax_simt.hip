@@ -3,7 +3,10 @@
 // "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Local Softmax and
 // Long-Range Linear Memory": each video query attends, under one softmax with scale 1/sqrt(d), to
 // the text keys, the keys of its chunk and of the two neighbouring chunks, and the boundary anchor
-// frames.  The key set of a query frame is a short list of contiguous ranges (built on the host).
+// frames.  "Video DeltaNet speeds MiniMax H3 video generation 14.5x" (summary): interactions with
+// text or audio stay full softmax attention, so audio keys join the text keys, and the text and
+// audio query rows attend to every token.  The key set of a row group is a short list of
+// contiguous ranges (built on the host) in the key space [text, audio (padded) | video tokens].
 //
 // One thread per query token: the 64 threads of a block are 64 consecutive tokens of one frame
 // and one head, so they walk the same keys in lock step and every key/value load is a broadcast.
@@ -14,31 +17,33 @@
 namespace vdn {
 namespace {
 
+// Row group g = blockIdx.y holds nq query rows (q and o are [groups][nq][H][D]) and uses key-range
+// row t0 + g: video frames (t0 = 0, nq = N) or the context rows (t0 = T, nq = n_ctx, one group).
 template <typename Tin, int D>
 __global__ __launch_bounds__(64) void softmax_simt_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const Tin* __restrict__ text_kv, Tin* __restrict__ o_s, const int* __restrict__ ranges,
-    const int* __restrict__ nranges, int N, int H, int n_text, int text_pad, float scale_log2) {
-  const int t = blockIdx.y, h = blockIdx.z;
+    const Tin* __restrict__ ctx_kv, Tin* __restrict__ o, const int* __restrict__ ranges,
+    const int* __restrict__ nranges, int nq, int t0, int H, int n_ctx, int ctx_pad, float scale_log2) {
+  const int t = t0 + blockIdx.y, h = blockIdx.z;
   const int n = blockIdx.x * 64 + threadIdx.x;
-  if (n >= N) return;
-  const int64_t tok = (int64_t)t * N + n;
+  if (n >= nq) return;
+  const int64_t tok = (int64_t)blockIdx.y * nq + n;
   const Tin* qp = q + (tok * H + h) * D;
   float qr[D], acc[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) { qr[i] = to_f32(qp[i]) * scale_log2; acc[i] = 0.f; }
   float m = -INFINITY, l = 0.f;
-  const Tin* text_v = text_kv + (int64_t)n_text * H * D;
+  const Tin* ctx_v = ctx_kv + (int64_t)n_ctx * H * D;
   const int nr = nranges[t];
   for (int r = 0; r < nr; ++r) {
     const int a = ranges[t * 2 * kMaxRanges + 2 * r], b = ranges[t * 2 * kMaxRanges + 2 * r + 1];
     for (int j = a; j < b; ++j) {
       const Tin *kp, *vp;
-      if (j < text_pad) {
-        kp = text_kv + ((int64_t)j * H + h) * D;
-        vp = text_v + ((int64_t)j * H + h) * D;
+      if (j < ctx_pad) {
+        kp = ctx_kv + ((int64_t)j * H + h) * D;
+        vp = ctx_v + ((int64_t)j * H + h) * D;
       } else {
-        const int64_t vt = j - text_pad;
+        const int64_t vt = j - ctx_pad;
         kp = k + (vt * H + h) * D;
         vp = v + (vt * H + h) * D;
       }
@@ -59,18 +64,21 @@ __global__ __launch_bounds__(64) void softmax_simt_kernel(
     }
   }
   const float inv = 1.f / l;
-  Tin* op = o_s + (tok * H + h) * D;
+  Tin* op = o + (tok * H + h) * D;
 #pragma unroll
   for (int i = 0; i < D; ++i) store_elt(op + i, acc[i] * inv);
 }
 
 template <typename Tin, int D>
 void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
-  dim3 grid((s.N + 63) / 64, s.T, s.H);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  softmax_simt_kernel<Tin, D><<<grid, 64, 0, st>>>(
+  softmax_simt_kernel<Tin, D><<<dim3((s.N + 63) / 64, s.T, s.H), 64, 0, st>>>(
       (const Tin*)in.q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, (Tin*)b.os, b.ranges,
-      b.nranges, s.N, s.H, s.n_text, s.text_pad, scale_log2);
+      b.nranges, s.N, 0, s.H, s.n_ctx, s.ctx_pad, scale_log2);
+  if (in.ctx_out)
+    softmax_simt_kernel<Tin, D><<<dim3((s.n_ctx + 63) / 64, 1, s.H), 64, 0, st>>>(
+        (const Tin*)in.ctx_q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, (Tin*)in.ctx_out,
+        b.ranges, b.nranges, s.n_ctx, s.T, s.H, s.n_ctx, s.ctx_pad, scale_log2);
 }
 
 template <typename Tin>

@@ -31,7 +31,7 @@ template <typename Tin, int D>
 __global__ __launch_bounds__(256) void vda_stats_simt_kernel(
     const Tin* __restrict__ k, const Tin* __restrict__ v, const float* __restrict__ beta,
     const Tin* __restrict__ text_kv, float* __restrict__ minv, float* __restrict__ bw, int T, int N, int H,
-    int n_text, int anchors) {
+    int n_text, int n_ctx, int anchors) {
   constexpr int R = D / 16;
   const int slot = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void vda_stats_simt_kernel(
   const int U = slot == 0 ? n_text : N;
   const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
   const Tin* kbase = slot == 0 ? text_kv : k;
-  const Tin* vbase = slot == 0 ? text_kv + (int64_t)n_text * H * D : v;
+  const Tin* vbase = slot == 0 ? text_kv + (int64_t)n_ctx * H * D : v;   // V half of [2][n_ctx][H][d]
   const float wscale = slot == 0 ? 0.5f : 1.0f;
   const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
 
@@ -198,7 +198,7 @@ void stats_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st)
   dim3 grid(s.T + 1, s.H);
   vda_stats_simt_kernel<Tin, D><<<grid, 256, 0, st>>>((const Tin*)in.k, (const Tin*)in.v, in.beta,
                                                       (const Tin*)in.text_kv, b.minv, b.bw, s.T, s.N, s.H,
-                                                      s.n_text, s.anchors);
+                                                      s.n_text, s.n_ctx, s.anchors);
 }
 
 template <typename Tin>

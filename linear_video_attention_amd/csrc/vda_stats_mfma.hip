@@ -72,7 +72,8 @@ __global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* _
                                                                  const float* __restrict__ beta,
                                                                  const bf16_t* __restrict__ text_kv,
                                                                  float* __restrict__ minv, float* __restrict__ bw,
-                                                                 int T, int N, int H, int n_text, int anchors) {
+                                                                 int T, int N, int H, int n_text, int n_ctx,
+                                                                 int anchors) {
   using SM = GramSmem<D>;
   constexpr int CH = D / 8;                 // 16-byte chunks per token row
   constexpr int ROWS_PER_KB = 1024 / SM::ROW;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* _
   const int U = slot == 0 ? n_text : N;
   const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
   const bf16_t* kbase = slot == 0 ? text_kv : k;
-  const bf16_t* vbase = slot == 0 ? text_kv + (int64_t)n_text * H * D : v;
+  const bf16_t* vbase = slot == 0 ? text_kv + (int64_t)n_ctx * H * D : v;   // V half of [2][n_ctx][H][d]
   const float wscale = slot == 0 ? 0.5f : 1.0f;
   const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
   const int ntiles = (U + kTU - 1) / kTU;
@@ -226,7 +227,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
                             (int)smem);
   hipLaunchKernelGGL(vda_gram_mfma_kernel<D>, dim3(s.T + 1, s.H), dim3(kThreads), smem, st, (const bf16_t*)in.k,
                      (const bf16_t*)in.v, in.beta, (const bf16_t*)in.text_kv, b.minv, b.bw, s.T, s.N, s.H, s.n_text,
-                     s.anchors);
+                     s.n_ctx, s.anchors);
 }
 
 }  // namespace

@@ -10,7 +10,7 @@
 
 namespace vdn {
 
-constexpr int kTextPad = 64;        // text keys occupy [0, round_up(n_text, 64)) of a head's key space
+constexpr int kTextPad = 64;        // global (text, then audio) keys occupy [0, round_up(n_ctx, 64)) of a head's key space
 constexpr int kMaxRanges = 4;       // text, window, frame 0, frame T-1
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -19,13 +19,16 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 struct Shape {
   int T, N, C, n_text, H, d, anchors;
   vdn_dtype dtype;
+  int n_audio;       // audio tokens: global softmax keys after the text, never written to the linear memory
+  int n_ctx;         // n_text + n_audio: the global (context) tokens
   int Nc;            // number of chunks
-  int text_pad;      // n_text rounded up to kTextPad
-  int64_t Lk;        // key-space length per head: text_pad + T*N
+  int ctx_pad;       // n_ctx rounded up to kTextPad
+  int64_t Lk;        // key-space length per head: ctx_pad + T*N
   int64_t Ls;        // allocated key stride of the packed K/V: Lk + one zero tile of padding
 };
 
-// Key ranges of query frame t in a head's key space (see vdn_key_ranges); returns the count.
+// Key ranges of query frame t in a head's key space (see vdn_key_ranges); t == T gives the ranges
+// of the context (text and audio) query rows: every key.  Returns the count.
 int key_ranges(const Shape& s, int t, int64_t* ranges, int max_ranges);
 // Frames written into the forward (dir 0) / reverse (dir 1) state of query frame t, in order.
 int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames);
@@ -47,7 +50,7 @@ struct Layout {
   size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
   size_t kmax;      // largest key norm per head [H] f32
   size_t flags;     // per-workgroup fallback flags of the MFMA softmax [softmax_grid] int32
-  size_t ranges;    // int32 [T][2*kMaxRanges] + int32 [T] counts
+  size_t ranges;    // int32 [T+1][2*kMaxRanges] + int32 [T+1] counts (row T: context query rows)
   size_t total;
 };
 // Kernel selection per stage.
@@ -75,8 +78,8 @@ struct Buffers {
   float* kmax_part;
   float* kmax;
   int* flags;
-  const int* ranges;   // [T][2*kMaxRanges]
-  const int* nranges;  // [T]
+  const int* ranges;   // [T+1][2*kMaxRanges]
+  const int* nranges;  // [T+1]
 };
 
 struct Inputs {
@@ -86,10 +89,13 @@ struct Inputs {
   const void *gate_w, *proj_w;
   void* out;
   const float* alpha;  // [T][H][d] channel-wise decay gate of the inherited state, or nullptr (none)
+  const void* ctx_q;   // [n_ctx][H][d] text and audio query rows, or nullptr (not computed)
+  void* ctx_out;       // [n_ctx][H][d] their attention output (with ctx_q)
 };
 
 // Number of workgroups of the MFMA softmax launch.
-int softmax_grid(const Shape& s);
+// with_ctx: including the workgroups of the context query rows.
+int softmax_grid(const Shape& s, bool with_ctx);
 
 // Launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);

@@ -26,8 +26,10 @@ _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 SIGNATURES = [
     ("vdn_plan_create", _c_int, [_c_int] * 7 + [_c_int, ctypes.POINTER(_vp)]),
     ("vdn_plan_create_ex", _c_int, [_c_int] * 7 + [_c_int, ctypes.c_uint, ctypes.POINTER(_vp)]),
+    ("vdn_plan_create_joint", _c_int, [_c_int] * 8 + [_c_int, ctypes.c_uint, ctypes.POINTER(_vp)]),
     ("vdn_forward", _c_int, [_vp] * 10),
     ("vdn_forward_decay", _c_int, [_vp] * 11),
+    ("vdn_forward_joint", _c_int, [_vp] * 13),
     ("vdn_plan_destroy", None, [_vp]),
     ("vdn_status_str", ctypes.c_char_p, [_c_int]),
     ("vdn_plan_workspace_bytes", _c_size, [_vp]),
@@ -110,14 +112,19 @@ def measure_copy_gbs(nbytes=1 << 30):
 # ---- plan ----
 
 def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
-                    overlap=False):
-    """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"."""
+                    overlap=False, n_audio=0):
+    """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"; ``n_audio``
+    audio tokens follow the text tokens (a joint plan)."""
     dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
     h = _vp()
     flags = ((VDN_FLAG_GENERIC_KERNELS if generic else 0) | (VDN_FLAG_SERIAL if serial else 0)
              | (VDN_FLAG_OVERLAP if overlap else 0))
-    _check(lib().vdn_plan_create_ex(T, N, C, n_text, H, d, int(anchors), dt, flags, ctypes.byref(h)),
-           "vdn_plan_create")
+    if n_audio:
+        _check(lib().vdn_plan_create_joint(T, N, C, n_text, n_audio, H, d, int(anchors), dt, flags,
+                                           ctypes.byref(h)), "vdn_plan_create_joint")
+    else:
+        _check(lib().vdn_plan_create_ex(T, N, C, n_text, H, d, int(anchors), dt, flags, ctypes.byref(h)),
+               "vdn_plan_create")
     return h.value
 
 
@@ -149,20 +156,31 @@ def vdn_forward_decay(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, out, 
            "vdn_forward_decay")
 
 
+def vdn_forward_joint(plan, q, k, v, beta, ctx_q, ctx_kv, alpha, gate_w, proj_w, out, ctx_out, stream=None):
+    """The joint sequence: the video rows as ``vdn_forward`` / ``vdn_forward_decay`` (``alpha`` may
+    be None) and, with ``ctx_q`` and ``ctx_out``, the text and audio query rows."""
+    ptr = lambda x: None if x is None else x.data_ptr()
+    _check(lib().vdn_forward_joint(plan, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(ctx_q), ptr(ctx_kv),
+                                   ptr(alpha), ptr(gate_w), ptr(proj_w), ptr(out), ptr(ctx_out),
+                                   _stream_ptr(stream)), "vdn_forward_joint")
+
+
 class Plan:
     """Owning wrapper of a plan with argument checks on torch tensors."""
 
     def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
-                 overlap=False):
+                 overlap=False, n_audio=0):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("no GPU visible: the VDN layer runs only on the GPU")
         self.T, self.N, self.C, self.n_text, self.H, self.d = T, N, C, n_text, H, d
+        self.n_audio = n_audio
+        self.n_ctx = n_text + n_audio
         self.anchors = bool(anchors)
         self.dtype = dtype
         self.torch_dtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         self.Nc = (T + C - 1) // C
-        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap)
+        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap, n_audio)
 
     def close(self):
         if self.handle:
@@ -188,26 +206,38 @@ class Plan:
         if not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
 
-    def forward(self, q, k, v, beta, text_kv, gate_w, proj_w, out=None, stream=None, alpha=None):
-        """The layer forward; with ``alpha`` ([T, H, d] fp32) the linear branch's decay gate."""
+    def forward(self, q, k, v, beta, text_kv, gate_w, proj_w, out=None, stream=None, alpha=None,
+                ctx_q=None, ctx_out=None):
+        """The layer forward; with ``alpha`` ([T, H, d] fp32) the linear branch's decay gate.
+        ``text_kv`` holds the context tokens ([2, n_text + n_audio, H, d]).  With ``ctx_q``
+        ([n_ctx, H, d]) the text and audio query rows are computed too, into ``ctx_out`` (a new
+        tensor when None); the call then returns ``(out, ctx_out)``."""
         import torch
         TN, H, d = self.T * self.N, self.H, self.d
         dt = self.torch_dtype
         for name, x in (("q", q), ("k", k), ("v", v)):
             self._expect(name, x, (TN, H, d), dt)
         self._expect("beta", beta, (self.n_text + TN, H), torch.float32)
-        if self.n_text > 0:
-            self._expect("text_kv", text_kv, (2, self.n_text, H, d), dt)
+        if self.n_ctx > 0:
+            self._expect("text_kv", text_kv, (2, self.n_ctx, H, d), dt)
         self._expect("gate_w", gate_w, (2, d, d), dt)
         self._expect("proj_w", proj_w, (2, d, d), dt)
         if out is None:
             out = torch.empty((TN, H, d), dtype=dt, device=q.device)
         self._expect("out", out, (TN, H, d), dt)
-        tkv = text_kv if self.n_text > 0 else None
+        if alpha is not None:
+            self._expect("alpha", alpha, (self.T, H, d), torch.float32)
+        tkv = text_kv if self.n_ctx > 0 else None
+        if ctx_q is not None:
+            self._expect("ctx_q", ctx_q, (self.n_ctx, H, d), dt)
+            if ctx_out is None:
+                ctx_out = torch.empty((self.n_ctx, H, d), dtype=dt, device=q.device)
+            self._expect("ctx_out", ctx_out, (self.n_ctx, H, d), dt)
+            vdn_forward_joint(self.handle, q, k, v, beta, ctx_q, tkv, alpha, gate_w, proj_w, out, ctx_out, stream)
+            return out, ctx_out
         if alpha is None:
             vdn_forward(self.handle, q, k, v, beta, tkv, gate_w, proj_w, out, stream)
         else:
-            self._expect("alpha", alpha, (self.T, H, d), torch.float32)
             vdn_forward_decay(self.handle, q, k, v, beta, tkv, alpha, gate_w, proj_w, out, stream)
         return out
 

@@ -16,19 +16,34 @@ def to_device(inp: dict, dtype: str) -> dict:
     for key in ("q", "k", "v", "gate_w", "proj_w"):
         dev[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to("cuda").to(tdt).contiguous()
     dev["beta"] = torch.from_numpy(np.ascontiguousarray(inp["beta"])).to("cuda").float().contiguous()
-    if inp["text_k"].shape[0] > 0:
-        tkv = np.stack([inp["text_k"], inp["text_v"]])
+    ck, cv = inp["text_k"], inp["text_v"]
+    if inp.get("audio_k") is not None:                  # context tokens: text rows, then audio
+        ck = np.concatenate([ck, inp["audio_k"]])
+        cv = np.concatenate([cv, inp["audio_v"]])
+    if ck.shape[0] > 0:
+        tkv = np.stack([ck, cv])
         dev["text_kv"] = torch.from_numpy(np.ascontiguousarray(tkv)).to("cuda").to(tdt).contiguous()
     else:
         dev["text_kv"] = None
+    dev["ctx_q"] = None
+    if inp.get("ctx_q") is not None:
+        dev["ctx_q"] = torch.from_numpy(np.ascontiguousarray(inp["ctx_q"])).to("cuda").to(tdt).contiguous()
     dev["alpha"] = None
     if inp.get("alpha") is not None:
         dev["alpha"] = torch.from_numpy(np.ascontiguousarray(inp["alpha"])).to("cuda").float().contiguous()
     return dev
 
 
-def make_plan(w, generic=False) -> Plan:
-    return Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, generic=generic)
+def make_plan(w, generic=False, n_audio=0) -> Plan:
+    return Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, generic=generic, n_audio=n_audio)
+
+
+def run_joint(plan: Plan, dev: dict):
+    """The joint forward: (video rows out, context rows out)."""
+    out, ctx = plan.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"],
+                            dev["proj_w"], alpha=dev.get("alpha"), ctx_q=dev["ctx_q"])
+    torch.cuda.synchronize()
+    return out, ctx
 
 
 def run_layer(plan: Plan, dev: dict, out=None):

@@ -67,6 +67,19 @@ def test_invalid_plan_flags_rejected_on_host(vdn, flags):
     assert h.value is None
 
 
+def test_joint_plan_argument_errors(vdn):
+    """A negative audio count is an argument error; an audio count that pushes the context key
+    space past the supported size is unsupported."""
+    h = ctypes.c_void_p(1234)
+    L = vdn.lib()
+    assert L.vdn_plan_create_joint(4, 16, 2, 1, -1, 1, 16, 1, 0, 0, ctypes.byref(h)) == -1
+    assert h.value is None
+    assert L.vdn_plan_create_joint(4, 16, 2, 1, 1, 1, 48, 1, 0, 0, ctypes.byref(h)) == -2
+    assert L.vdn_plan_create_joint(4, 16, 2, 1, (1 << 31) - 2, 1, 16, 1, 0, 0, ctypes.byref(h)) == -2
+    assert L.vdn_plan_create_joint(4, 16, 2, 1, 0, 1, 16, 1, 0, 0, None) == -1
+    assert L.vdn_forward_joint(None, *([None] * 12)) == -1
+
+
 def test_measurement_helpers_reject_bad_arguments(vdn):
     x = ctypes.c_double()
     assert vdn.lib().vdn_measure_mfma_bf16_tflops(0, ctypes.byref(x)) == -1

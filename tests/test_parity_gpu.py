@@ -14,7 +14,7 @@ from oracle import vdn_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import TOL, combined_states, make_plan, rel_err, run_layer, softmax_out, to_device  # noqa: E402
+from gpu_util import TOL, combined_states, make_plan, rel_err, run_joint, run_layer, softmax_out, to_device  # noqa: E402
 
 
 def check_full(w, generic=False, seed=0, stress=False, decay=False):
@@ -265,5 +265,117 @@ def test_decay_argument_errors():
     assert L.vdn_forward_decay(plan.handle, *head, None, *tail, ptr(out), stream) == -1     # no gate
     assert L.vdn_forward_decay(plan.handle, *head, a + 4, *tail, ptr(out), stream) == -1    # misaligned
     assert L.vdn_forward_decay(plan.handle, *head, ptr(out), *tail, ptr(out), stream) == -1  # aliases out
+    torch.cuda.synchronize()
+    plan.close()
+
+
+# --- text and audio tokens: audio keys and the context query rows (vdn_forward_joint) ---
+
+def check_joint(w, n_audio, generic=False, seed=0, decay=False, ctx_rows=True):
+    inp = synth.make_inputs(w, seed=seed, decay=decay, n_audio=n_audio, ctx_rows=ctx_rows)
+    plan = make_plan(w, generic=generic, n_audio=n_audio)
+    dev = to_device(inp, w.dtype)
+    if ctx_rows:
+        out, ctx = run_joint(plan, dev)
+    else:
+        out, ctx = run_layer(plan, dev), None
+    ref, mids = orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors, with_intermediates=True)
+    tol = TOL[w.dtype]
+    e_out = rel_err(out.float().cpu().numpy(), ref)
+    e_os = rel_err(softmax_out(plan), mids["o_s"])
+    e_st = rel_err(combined_states(plan), orc.chunk_states(inp, w.T, w.N, w.C, w.anchors))
+    msg = f"{w} n_audio={n_audio} generic={generic} decay={decay}: out {e_out:.2e}  o_s {e_os:.2e}  states {e_st:.2e}"
+    e_ctx = 0.0
+    if ctx_rows and w.n_text + n_audio > 0:
+        e_ctx = rel_err(ctx.float().cpu().numpy(), orc.context_rows(inp, w.T, w.N))
+        msg += f"  ctx {e_ctx:.2e}"
+    print(msg, flush=True)
+    assert e_os <= tol and e_st <= tol and e_out <= tol and e_ctx <= tol, msg
+    plan.close()
+    return inp, out, ctx
+
+
+def test_joint_tiny_fp32_matches_oracle_and_bruteforce():
+    w = synth.WORKLOADS["tiny"]
+    inp, out, ctx = check_joint(w, n_audio=1)
+    ref, _, _ = bruteforce.layer_dense(inp, w.T, w.N, w.C, w.anchors)
+    assert rel_err(out.cpu().numpy(), ref) <= TOL["fp32"]
+    assert rel_err(ctx.cpu().numpy(), bruteforce.context_dense(inp, w.T, w.N, w.C, w.anchors)) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_joint_small_bf16_matches_oracle(generic):
+    check_joint(synth.WORKLOADS["small"], n_audio=40, generic=generic)
+
+
+JOINT_RAGGED = [
+    # n_text, n_audio, T, N, C, H, d, dtype, anchors, decay
+    (0, 7, 9, 136, 3, 2, 128, "bf16", True, False),      # audio only, no text
+    (37, 300, 13, 200, 3, 3, 64, "bf16", True, True),    # two context query tiles, with decay
+    (64, 64, 7, 72, 2, 2, 128, "bf16", False, False),    # context exactly one key tile, anchors off
+    (5, 3, 6, 24, 2, 2, 32, "bf16", True, False),        # generic kernels (d = 32)
+    (9, 4, 11, 37, 3, 2, 64, "fp32", True, True),        # fp32
+    (1, 0, 5, 64, 2, 1, 64, "bf16", True, False),        # context rows without audio
+]
+
+
+@pytest.mark.parametrize("case", JOINT_RAGGED, ids=lambda c: "x".join(str(x) for x in c))
+def test_joint_ragged_shapes_match_oracle(case):
+    n_text, n_audio, T, N, C, H, d, dtype, anchors, decay = case
+    w = synth.custom(n_text, T, N, C, H, d, dtype, "sigmoid", anchors)
+    check_joint(w, n_audio, seed=8, decay=decay)
+
+
+def test_joint_plan_without_context_rows():
+    """A plan with audio tokens called through vdn_forward: the video rows see the audio keys."""
+    w = synth.custom(16, 10, 128, 3, 2, 128, "bf16", "sigmoid", True)
+    check_joint(w, n_audio=24, ctx_rows=False)
+
+
+def test_joint_768p_sampled():
+    """768p with 576 audio tokens (14.4 s at 40 audio latents per second) and the context rows,
+    in the benchmark's launch configuration: sampled video rows and every 16th context row."""
+    w = synth.WORKLOADS["768p"]
+    n_audio = 576
+    inp = synth.make_inputs(w, seed=0, n_audio=n_audio, ctx_rows=True)
+    plan = make_plan(w, n_audio=n_audio)
+    dev = to_device(inp, w.dtype)
+    out, ctx = run_joint(plan, dev)
+    rows = synth.sample_rows(w)
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    crow = np.arange(0, w.n_text + n_audio, 16)
+    got_c = ctx[torch.from_numpy(crow).cuda()].float().cpu().numpy()
+    del dev, out, ctx
+    ref = orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors, rows=rows)
+    sub = dict(inp)
+    sub["ctx_q"] = inp["ctx_q"][crow]
+    ref_c = orc.context_rows(sub, w.T, w.N)
+    e, ec = rel_err(got, ref), rel_err(got_c, ref_c)
+    print(f"768p joint: out err {e:.2e} ({len(rows)} rows), ctx err {ec:.2e} ({len(crow)} rows)", flush=True)
+    assert e <= TOL[w.dtype] and ec <= TOL[w.dtype]
+    plan.close()
+
+
+def test_joint_argument_errors():
+    from linear_video_attention_amd import vdn
+    w = synth.custom(4, 4, 64, 2, 1, 64, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, n_audio=3, ctx_rows=True)
+    dev = to_device(inp, w.dtype)
+    plan = make_plan(w, n_audio=3)
+    out = torch.empty_like(dev["q"])
+    ctx = torch.empty_like(dev["ctx_q"])
+    L = vdn.lib()
+    ptr = lambda x: x.data_ptr()
+    head = [ptr(dev[k]) for k in ("q", "k", "v", "beta")]
+    cq, ckv = ptr(dev["ctx_q"]), ptr(dev["text_kv"])
+    tail = [ptr(dev["gate_w"]), ptr(dev["proj_w"])]
+    stream = torch.cuda.current_stream().cuda_stream
+    assert L.vdn_forward_joint(plan.handle, *head, cq, ckv, None, *tail, ptr(out), ptr(ctx), stream) == 0
+    assert L.vdn_forward_joint(plan.handle, *head, cq, ckv, None, *tail, ptr(out), None, stream) == -1
+    assert L.vdn_forward_joint(plan.handle, *head, None, ckv, None, *tail, ptr(out), ptr(ctx), stream) == -1
+    assert L.vdn_forward_joint(plan.handle, *head, cq, ckv, None, *tail, ptr(out), ptr(out), stream) == -1
+    assert L.vdn_forward_joint(plan.handle, *head, cq, ckv, None, *tail, ptr(out), cq, stream) == -1
+    assert L.vdn_forward_joint(plan.handle, *head, cq, ckv, None, *tail, ptr(out), ptr(ctx) + 8, stream) == -1
+    assert L.vdn_forward_joint(plan.handle, *head, cq, None, None, *tail, ptr(out), ptr(ctx), stream) == -1
     torch.cuda.synchronize()
     plan.close()
