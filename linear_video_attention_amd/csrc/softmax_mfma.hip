@@ -1,33 +1,34 @@
 // Block-sparse window softmax of the VDN layer on CDNA4 matrix cores (bf16 in, fp32 accumulate).
 //
 // "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Local Softmax and
-// Long-Range Linear Memory": a video query in chunk c attends, with one softmax, to the text keys,
-// the keys of chunks c-1, c, c+1 and the two boundary anchor frames (boundary query frames attend
-// to every frame).  The key set of a query frame is at most four contiguous ranges of the packed
-// key space (built on the host), so the kernel is a flash-style attention over a range list.
+// Long-Range Linear Memory": a video query in chunk c attends, with one softmax, to the global
+// (text, audio) keys, the keys of chunks c-1, c, c+1 and the two boundary anchor frames (boundary
+// query frames attend to every frame).  "Video DeltaNet speeds MiniMax H3 video generation 14.5x"
+// (summary): the text and audio query rows attend to every key.  The key set of a row group is at
+// most four contiguous ranges of the packed key space (built on the host).
 //
 // Work decomposition
-//   * one workgroup = 256 queries of one frame and one head; 8 waves x 32 queries, two waves per
-//     SIMD so one wave's exponentials overlap the other's MFMAs (measured faster on gfx950 than
-//     4 waves x 64 queries at one wave per SIMD, which halves the LDS reads per MFMA but leaves
-//     every LDS and MFMA latency exposed);
-//   * key tiles of 64 keys are loaded straight from global memory into LDS (global_load_lds, four
-//     stages: up to three tiles in flight; K as [key][d], V transposed as [d][key], both
-//     XOR-swizzled so the 16-byte fragment reads are bank-conflict free) and processed as two
-//     32-key halves;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as rows, queries as columns) so that each
-//     lane ends up holding 16 consecutive keys of one query -- the row permutation used when the
-//     K fragments are read makes those keys contiguous;  O^T += V^T P^T with the same instruction,
-//     P taken straight from the S^T registers (no LDS round trip);
+//   * one workgroup = 384 queries of one frame and one head; 8 waves x 48 queries (three 16-query
+//     column tiles), two waves per SIMD.  Every K or V^T fragment a wave reads from LDS feeds three
+//     v_mfma_f32_16x16x32_bf16 (one per query tile), so a flop costs 2/3 of the LDS bytes of a
+//     32-query wave on 32 x 32 tiles (measured 7 % faster than that layout, whose LDS reads ran
+//     level with its MFMAs) while the registers (O^T 96, Q 48, S^T 24 per 32-key half) still fit
+//     two waves per SIMD, whose interleaving hides each other's exponentials and LDS latency;
+//   * key tiles of 64 keys are loaded straight from global memory into LDS (global_load_lds,
+//     two stages by default: the next tile in flight; K as [key][d], V transposed as [d][key], both
+//     XOR-swizzled so that every group of eight lanes of a 16-byte fragment read hits distinct
+//     banks) and processed as two 32-key halves;
+//   * S^T = K Q^T with keys as rows: the K fragment rows of 16-key tile t are the keys
+//     8 (r / 4) + 4 t + (r % 4) of the half, so that a lane's four scores of tile 0 and four of
+//     tile 1 are 8 consecutive keys -- exactly the B operand of O^T += V^T P^T, which is thus
+//     taken straight from the score registers;
 //   * exponent reference: softmax is invariant to the offset subtracted from the scores, and
 //     |q.k| <= |q| max|k| bounds every score of the query, so p = 2^(s c - |q| kmax c) never
-//     exceeds 1 and needs no running maximum and no rescaling of the accumulator (kmax = largest
-//     key norm of the head, from the packing pass).  When that bound is so loose that the largest
-//     term could underflow (|q| kmax c > 48 in log2 units -- far outside unit-normalised inputs)
-//     the workgroup flags itself and a second launch of the same kernel with the classic online
-//     maximum (running max, rescale of the accumulator) redoes just those workgroups;
-//   * workgroup order: the long boundary-frame workgroups first (longest job first), then the
-//     interior ones remapped so that consecutive query tiles -- which share their key window --
+//     exceeds 1 and needs no running maximum or accumulator rescale.  Workgroups whose bound could
+//     underflow (|q| kmax c > 48 in log2 units) flag themselves and a second launch of the same
+//     kernel with the classic online maximum redoes just those;
+//   * workgroup order: context query rows (every key) first, then the boundary frames, then the
+//     interior frames remapped so that consecutive query tiles -- which share their key window --
 //     land on the same XCD (workgroups are dispatched round-robin over the 8 XCDs).
 #include "dev_common.h"
 #include "vdn_internal.h"
@@ -36,47 +37,45 @@ namespace vdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-constexpr int kBK = 64;        // keys per tile
-#ifndef VDN_SOFTMAX_BQ
-#define VDN_SOFTMAX_BQ 256
+constexpr int kBK = 64;             // keys per tile
+// Build parameters (defaults measured best at 768p; the alternatives are kept for measurement):
+//   VDN_SOFTMAX_WAVES   waves per workgroup (8; 4 gives two 192-query workgroups per CU, ~4 % slower)
+//   VDN_SOFTMAX_STAGES  LDS stages of the tile pipeline (2; 3 and 4 keep more tiles in flight,
+//                       1-2 % slower since the key tiles mostly hit in L2 / Infinity Cache)
+//   VDN_SOFTMAX_SCHED   1: order each half as K reads, score MFMAs | V reads, exponentials, P.V
+//                       MFMAs (about 3 % faster than the compiler's own interleaving)
+#ifndef VDN_SOFTMAX_WAVES
+#define VDN_SOFTMAX_WAVES 8
 #endif
-#ifndef VDN_SOFTMAX_SIMPLE
-#define VDN_SOFTMAX_SIMPLE 0
-#endif
-constexpr int kBQ = VDN_SOFTMAX_BQ;   // queries per workgroup
 #ifndef VDN_SOFTMAX_STAGES
-#define VDN_SOFTMAX_STAGES 4
+#define VDN_SOFTMAX_STAGES 2
 #endif
-constexpr bool kSimpleLoop = VDN_SOFTMAX_SIMPLE != 0;
-constexpr int kPipeStages = VDN_SOFTMAX_STAGES;     // LDS stages of the pipelined loop (3 or 4)
-constexpr int kStages = kSimpleLoop ? 2 : kPipeStages;
-static_assert(kPipeStages == 3 || kPipeStages == 4, "pipeline stages");
-// Wave shape: QSUB 32-query column tiles per wave, kBQ / (32 QSUB) waves per workgroup.
-#ifndef VDN_SOFTMAX_QSUB
-#define VDN_SOFTMAX_QSUB 1
+#ifndef VDN_SOFTMAX_SCHED
+#define VDN_SOFTMAX_SCHED 1
 #endif
-constexpr int kQSub = VDN_SOFTMAX_QSUB;
-constexpr int kWaves = kBQ / (32 * kQSub);
-constexpr int kQW = 32 * kQSub;        // queries per wave
+constexpr int kWaves = VDN_SOFTMAX_WAVES;       // waves per workgroup; 8 / kWaves workgroups per CU
+constexpr int kQT = 3;              // 16-query column tiles per wave
+constexpr int kQW = 16 * kQT;       // queries per wave
+constexpr int kBQ = kWaves * kQW;   // queries per workgroup
+constexpr int kStages = VDN_SOFTMAX_STAGES;     // LDS stages: up to kStages - 1 tiles in flight
+static_assert(kStages >= 2 && kStages <= 4, "LDS stages");
 constexpr float kMaxRef = 48.0f;            // log2 units; beyond it the fallback kernel runs
 constexpr float kRescaleThreshold = 8.0f;   // fallback: log2 units of growth before a rescale
 constexpr float kMasked = -1.0e30f;
 constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
+// s_waitcnt immediate for vmcnt(n), n < 64 (low four bits in [3:0], high two in [15:14])
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// LDS chunk swizzles (16-byte chunks).  K rows are read 16 rows per 16 lanes in the order
-// {0-3,16-19,4-7,20-23} (+8 for the next 16 lanes); V^T rows 16 consecutive rows per 16 lanes.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  const int r = row & 31;
-  if constexpr (D == 128) return (r & 7) | ((r >> 1) & 8);
-  else return ((r >> 1) & 3) | ((r >> 2) & 4);
-}
-__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
+// LDS chunk swizzles (16-byte chunks).  One fragment read serves eight lanes per LDS cycle: lanes
+// 8j .. 8j+7 read K rows {8a + b : a in {0,1}, b in 0..3} + const (same chunk) and V^T rows
+// 8 consecutive rows (same chunk); the swizzles give those rows eight distinct chunk positions.
+__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int v_swz(int row) { return row & 7; }
 
 template <int D>
 struct Smem {
@@ -111,8 +110,8 @@ struct Params {
 template <int D, bool FALLBACK>
 __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(Params P) {
   using SM = Smem<D>;
-  constexpr int KS = D / 16;          // k-steps of the QK^T contraction
-  constexpr int DT = D / 32;          // 32-row d tiles of O^T
+  constexpr int KS = D / 32;          // k-steps of the QK^T contraction
+  constexpr int DT = D / 16;          // 16-row d tiles of O^T
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int unsafe_any;
 
@@ -120,8 +119,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   if constexpr (FALLBACK) {
     if (P.flags[w] == 0) return;
   }
-  // ---- workgroup -> (head, frame, query tile); the context rows (every key) come first as
-  // pseudo-frame T, then the boundary frames, then the interior frames ----
+  // ---- workgroup -> (head, frame, query tile); context rows are pseudo-frame T ----
   int h, t, qt;
   if (w < P.n_ctx_wg) {
     qt = w % P.QTc;
@@ -151,7 +149,6 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   }
   const int H = P.H;
   const int64_t Ls = P.Ls;
-  // this workgroup's query rows: nrows rows of stride H*D from qsrc, results to odst
   const bool ctx = t == P.T;
   const int nrows = ctx ? P.n_ctx : P.N;
   const bf16_t* qsrc = ctx ? P.qc + (int64_t)h * D : P.q + ((int64_t)t * P.N * H + h) * D;
@@ -160,37 +157,37 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hl = lane >> 5;
+  const int l16 = lane & 15, g = lane >> 4;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): query = l32 (+32 qs), d = ks*16 + hl*8 .. +8 ----
-  bf16x8 qf[kQSub][KS];
-  float qn2[kQSub];
-#pragma unroll
-  for (int qs = 0; qs < kQSub; ++qs) qn2[qs] = 0.f;
+  // ---- Q fragments (B operand of S^T = K Q^T): query l16 of column tile j, d = 32 ks + 8 g .. +8 ----
+  bf16x8 qf[kQT][KS];
+  float qn2[kQT];
   const int n_base = qt * kBQ + wave * kQW;
 #pragma unroll
-  for (int qs = 0; qs < kQSub; ++qs) {
-    const int n = n_base + qs * 32 + l32;
+  for (int j = 0; j < kQT; ++j) {
+    qn2[j] = 0.f;
+    const int n = n_base + 16 * j + l16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 val = {0, 0, 0, 0};
-      if (n < nrows) val = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)n * H * D + ks * 16 + hl * 8);
-      qf[qs][ks] = as_bf16x8(val);
+      if (n < nrows) val = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)n * H * D + ks * 32 + g * 8);
+      qf[j][ks] = as_bf16x8(val);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qn2[qs] += (float)qf[qs][ks][e] * (float)qf[qs][ks][e];
+      for (int e = 0; e < 8; ++e) qn2[j] += (float)qf[j][ks][e] * (float)qf[j][ks][e];
     }
   }
 
   // ---- exponent reference (fixed path) or running maximum (fallback) ----
-  float mref[kQSub];
+  float mref[kQT];
   {
     const float kmax = P.kmax[h];
     bool unsafe = false;
 #pragma unroll
-    for (int qs = 0; qs < kQSub; ++qs) {
-      const float qn = sqrtf(qn2[qs] + __shfl_xor(qn2[qs], 32));
-      mref[qs] = qn * kmax * c_log2;
-      unsafe |= !(mref[qs] <= kMaxRef);
+    for (int j = 0; j < kQT; ++j) {
+      float s2 = qn2[j] + __shfl_xor(qn2[j], 16);
+      s2 += __shfl_xor(s2, 32);
+      mref[j] = sqrtf(s2) * kmax * c_log2;
+      unsafe |= !(mref[j] <= kMaxRef);
     }
     if constexpr (!FALLBACK) {
       if (tid == 0) unsafe_any = 0;
@@ -202,13 +199,11 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
       if (bad) return;
     } else {
 #pragma unroll
-      for (int qs = 0; qs < kQSub; ++qs) mref[qs] = -INFINITY;
+      for (int j = 0; j < kQT; ++j) mref[j] = -INFINITY;
     }
   }
 
-  // ---- key tiles (all workgroup-uniform scalars).  Full 64-key tiles of every range come first,
-  // then the partial last tile of each range whose length is not a multiple of 64: the main loop
-  // is then straight-line code and only the short second loop masks keys. ----
+  // ---- key tiles: full 64-key tiles of every range first, then each range's partial last tile ----
   const int* rg = P.ranges + t * 2 * kMaxRanges;
   const int nr = uniform(P.nranges[t]);
   const int rs0 = uniform(rg[0]), rl0 = uniform(rg[1]) - rs0;
@@ -242,22 +237,20 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   const unsigned char* kh = reinterpret_cast<const unsigned char*>(P.kp + (int64_t)h * Ls * D);
   const unsigned char* vh = reinterpret_cast<const unsigned char*>(P.vt + (int64_t)h * D * Ls);
 
-  // Direct global -> LDS tile loads (global_load_lds_dwordx4): one instruction of a wave fills 1 KB
-  // of LDS, lane l writing bytes [16 l, 16 l + 16).  Each lane therefore fetches the global chunk
-  // whose swizzled LDS position is its own: a workgroup-uniform tile base plus a fixed 32-bit lane
-  // offset.  The packed key space ends with a zero tile, so no load leaves the buffer.
+  // Direct global -> LDS tile loads: one instruction of a wave fills 1 KB of LDS, lane l writing
+  // bytes [16 l, 16 l + 16), so each lane fetches the global chunk whose swizzled LDS position is
+  // its own.  The packed key space ends with a zero tile, so no load leaves the buffer.
   constexpr int K_INSTR = SM::K_BYTES / 1024 / kWaves;     // per wave
   constexpr int V_INSTR = SM::V_BYTES / 1024 / kWaves;
   constexpr int K_ROWS_PER_KB = 1024 / (D * 2);
-  static_assert(K_INSTR + V_INSTR < 16, "vmcnt field");
-  constexpr int kVmcntTile = 0x0F70 | (K_INSTR + V_INSTR);   // s_waitcnt vmcnt(loads of one tile)
-  constexpr int kVmcntTile2 = 0x0F70 | (2 * (K_INSTR + V_INSTR));   // ... of two tiles
-  static_assert(2 * (K_INSTR + V_INSTR) < 16, "vmcnt field");
+  constexpr int kVmcntTile = vmcnt_wait(K_INSTR + V_INSTR);          // loads of one tile
+  constexpr int kVmcntTile2 = vmcnt_wait(2 * (K_INSTR + V_INSTR));   // ... of two tiles
+  static_assert(2 * (K_INSTR + V_INSTR) < 64, "vmcnt field");
   uint32_t koff[K_INSTR], voff[V_INSTR];
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
     const int row = (i * kWaves + wave) * K_ROWS_PER_KB + lane / SM::KCH;
-    const int c = (lane % SM::KCH) ^ k_swz<D>(row);
+    const int c = (lane % SM::KCH) ^ k_swz(row);
     koff[i] = (uint32_t)(row * D + c * 8) * 2u;
   }
 #pragma unroll
@@ -279,234 +272,179 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
       __builtin_amdgcn_global_load_lds((gptr_t)(vt0 + voff[i]), (lptr_t)(vb + (i * kWaves + wave) * 1024), 16, 0, 0);
   };
 
-  f32x16 oacc[kQSub][DT];
+  f32x4 oacc[DT][kQT];
 #pragma unroll
-  for (int qs = 0; qs < kQSub; ++qs)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int j = 0; j < kQT; ++j) oacc[dt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum[kQT];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[qs][dt][i] = 0.f;
-  float lsum[kQSub];
-#pragma unroll
-  for (int qs = 0; qs < kQSub; ++qs) lsum[qs] = 0.f;
+  for (int j = 0; j < kQT; ++j) lsum[j] = 0.f;
 
-  // row of the K tile that this lane feeds as MFMA row l32 (see header): key 16*h + 4*a + b
-  const int krow = ((l32 >> 2) & 1) * 16 + (l32 >> 3) * 4 + (l32 & 3);
+  // K row read by this lane for 16-key tile u of a half (see header): key 8 (l16 / 4) + 4 u + l16 % 4
+  const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
 
-  // S^T for one 32-key half: 2 query subtiles.  All K fragments of the half are read before the
-  // first MFMA so the LDS latency is paid once per half, not once per fragment.
-  auto scores = [&](const unsigned char* kb, int kt, f32x16 (&sacc)[kQSub]) {
-    const int row = kt * 32 + krow;
-    bf16x8 kf[KS];
+  // S^T of one 32-key half: two 16-key row tiles x kQT query tiles.  All K fragments of the half
+  // are read before the first MFMA so the LDS latency is paid once per half.
+  auto scores = [&](const unsigned char* kb, int half, f32x4 (&sacc)[2][kQT]) {
+    bf16x8 kf[2][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c = ks * 2 + hl;
-      kf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)));
+    for (int u = 0; u < 2; ++u) {
+      const int row = half * 32 + krow0 + 4 * u;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks * 4 + g;
+        kf[u][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz(row)) * 16)));
+      }
     }
 #pragma unroll
-    for (int qs = 0; qs < kQSub; ++qs)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[qs][i] = 0.f;
+      for (int j = 0; j < kQT; ++j) sacc[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int qs = 0; qs < kQSub; ++qs)
-        sacc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qs][ks], sacc[qs], 0, 0, 0);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < kQT; ++j)
+          sacc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[j][ks], sacc[u][j], 0, 0, 0);
+#if VDN_SOFTMAX_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);         // the K fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS * kQT, 0);   // then the score MFMAs
+#endif
   };
-  auto mask = [&](int kt, int valid, f32x16 (&sacc)[kQSub]) {
+  // lane's score i of row tile u is key half*32 + 8 g + 4 u + i
+  auto mask = [&](int half, int valid, f32x4 (&sacc)[2][kQT]) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kl = kt * 32 + hl * 16 + i;
-      if (kl >= valid) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int qs = 0; qs < kQSub; ++qs) sacc[qs][i] = kMasked;
+      for (int i = 0; i < 4; ++i) {
+        if (half * 32 + 8 * g + 4 * u + i >= valid) {
+#pragma unroll
+          for (int j = 0; j < kQT; ++j) sacc[u][j][i] = kMasked;
+        }
       }
-    }
   };
-  // running maximum with lazy rescale (fallback kernel only)
-  auto online_max = [&](f32x16 (&sacc)[kQSub]) {
-    float mxc[kQSub];
+  // running maximum with lazy rescale (fallback kernel only); a query's 32 scores of the half are
+  // spread over the four lane groups g
+  auto online_max = [&](f32x4 (&sacc)[2][kQT]) {
+    float mxc[kQT];
     bool need = false;
 #pragma unroll
-    for (int qs = 0; qs < kQSub; ++qs) {
-      float mx = sacc[qs][0];
+    for (int j = 0; j < kQT; ++j) {
+      float mx = sacc[0][j][0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[qs][i]);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[u][j][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mxc[qs] = mx * c_log2;
-      need |= mxc[qs] > mref[qs] + kRescaleThreshold;
+      mxc[j] = mx * c_log2;
+      need |= mxc[j] > mref[j] + kRescaleThreshold;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int qs = 0; qs < kQSub; ++qs) {
-        const float mnew = fmaxf(mref[qs], mxc[qs]);
-        const float alpha = exp2f(mref[qs] - mnew);
-        mref[qs] = mnew;
-        lsum[qs] *= alpha;
+      for (int j = 0; j < kQT; ++j) {
+        const float mnew = fmaxf(mref[j], mxc[j]);
+        const float alpha = exp2f(mref[j] - mnew);
+        mref[j] = mnew;
+        lsum[j] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qs][dt][i] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][j] *= alpha;
       }
     }
   };
-  auto probs = [&](const f32x16 (&sacc)[kQSub], bf16x8 (&pf)[kQSub][2]) {
+  // P^T fragment of query tile j: keys 8 g .. 8 g + 7 of the half (row tile 0 then row tile 1)
+  auto probs = [&](const f32x4 (&sacc)[2][kQT], bf16x8 (&pf)[kQT]) {
 #pragma unroll
-    for (int qs = 0; qs < kQSub; ++qs) {
+    for (int j = 0; j < kQT; ++j) {
       float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // raw v_exp_f32: results below 2^-126 flush to zero, harmless since the largest term of
-        // every query is >= 2^-96 (fixed reference) or 1 (online maximum)
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qs][i], c_log2, -mref[qs]));
-        ls += p;
-        pf[qs][i >> 3][i & 7] = (__bf16)p;
-      }
-      lsum[qs] += ls;
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // raw v_exp_f32: results below 2^-126 flush to zero, harmless since the largest term of
+          // every query is >= 2^-96 (fixed reference) or 1 (online maximum)
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][j][i], c_log2, -mref[j]));
+          ls += p;
+          pf[j][4 * u + i] = (__bf16)p;
+        }
+      lsum[j] += ls;
     }
   };
-  auto accumulate = [&](const unsigned char* vb, int kt, const bf16x8 (&pf)[kQSub][2]) {
-    bf16x8 vf[DT][2];
+  auto accumulate = [&](const unsigned char* vb, int half, const bf16x8 (&pf)[kQT]) {
+    bf16x8 vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int vrow = dt * 32 + l32;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int c = kt * 4 + hl * 2 + s;
-        vf[dt][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + vrow * (kBK * 2) + ((c ^ v_swz(vrow)) * 16)));
-      }
+      const int vrow = dt * 16 + l16;
+      const int c = half * 4 + g;
+      vf[dt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + vrow * (kBK * 2) + ((c ^ v_swz(vrow)) * 16)));
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int qs = 0; qs < kQSub; ++qs)
-          oacc[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][s], pf[qs][s], oacc[qs][dt], 0, 0, 0);
+      for (int j = 0; j < kQT; ++j)
+        oacc[dt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[j], oacc[dt][j], 0, 0, 0);
+#if VDN_SOFTMAX_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);        // V fragment reads first,
+    __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);       // then the probabilities (VALU),
+    __builtin_amdgcn_sched_group_barrier(0x008, DT * kQT, 0);  // then the P.V MFMAs
+#endif
   };
 
-  auto next_tile = [&](int it) {
-    if (it + 1 < ntiles) {
+  // Tiles are loaded kStages - 1 ahead of the one being computed; iteration it waits for tile it,
+  // synchronises (after which the stage of tile it-1 is free in every wave), refills that stage
+  // and computes tile it as two 32-key halves.
+  auto wait_younger = [&](int younger) {          // wait until at most `younger` tiles are in flight
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(kVmcntTile2);
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(kVmcntTile);
+    else __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  };
+  for (int i = 0; i < kStages - 1 && i < ntiles; ++i) {
+    int key0, valid;
+    tile_at(i, key0, valid);
+    issue_tile(key0, i);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    wait_younger(min(ntiles - 1, it + kStages - 2) - it);    // tile it landed
+    __syncthreads();
+    if (it + kStages - 1 < ntiles) {
       int nkey0, nvalid;
-      tile_at(it + 1, nkey0, nvalid);
-      issue_tile(nkey0, (it + 1) & 1);
+      tile_at(it + kStages - 1, nkey0, nvalid);
+      issue_tile(nkey0, (it + kStages - 1) % kStages);
     }
-  };
-
-  if constexpr (!FALLBACK && !kSimpleLoop) {
-    // Software-pipelined over tiles with kPipeStages LDS stages: iteration i computes the scores of
-    // tile i+1 (MFMA) while it turns the scores of tile i into probabilities (VALU), then
-    // accumulates P.V of tile i.  The two streams are independent inside the iteration, so one
-    // wave keeps the matrix pipe and the vector ALU busy at the same time.  Full tiles come before
-    // partial ones (tile_at), so masking is a uniform branch outside the overlapped block.
-    // Tiles are loaded kPipeStages - 1 ahead of the one whose scores are computed.
-    constexpr int S = kPipeStages;
-    auto wait_younger = [&](int younger) {          // wait until at most `younger` tiles are in flight
-      if (younger >= 2) __builtin_amdgcn_s_waitcnt(kVmcntTile2);
-      else if (younger == 1) __builtin_amdgcn_s_waitcnt(kVmcntTile);
-      else __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    };
-    f32x16 sc0[kQSub], sc1[kQSub];          // scores of the tile being finished
-    for (int i = 0; i < S - 1 && i < ntiles; ++i) {
-      int key0, valid;
-      tile_at(i, key0, valid);
-      issue_tile(key0, i);
-    }
-    wait_younger(min(ntiles, S - 1) - 1);           // tile 0 landed
-    __syncthreads();
-    scores(smem, 0, sc0);
-    scores(smem, 1, sc1);
-    for (int it = 0; it + 1 < ntiles; ++it) {
-      wait_younger(min(ntiles - 1, it + S - 2) - (it + 1));   // tile it+1 landed
-      __syncthreads();                              // ... for every wave; stage (it-1)%S is free
-      if (it + S - 1 < ntiles) {
-        int nkey0, nvalid;
-        tile_at(it + S - 1, nkey0, nvalid);
-        issue_tile(nkey0, (it + S - 1) % S);
-      }
-      int key0, valid;
-      tile_at(it, key0, valid);
-      if (valid < kBK) {
-        mask(0, valid, sc0);
-        mask(1, valid, sc1);
-      }
-      const unsigned char* kn = smem + ((it + 1) % S) * SM::STAGE;
-      const unsigned char* vb = smem + (it % S) * SM::STAGE + SM::K_BYTES;
-      f32x16 sn0[kQSub], sn1[kQSub];
-      bf16x8 p0[kQSub][2], p1[kQSub][2];
-      scores(kn, 0, sn0);
-      probs(sc0, p0);
-      scores(kn, 1, sn1);
-      probs(sc1, p1);
-      accumulate(vb, 0, p0);
-      accumulate(vb, 1, p1);
+    int key0, valid;
+    tile_at(it, key0, valid);
+    const unsigned char* kb = smem + (it % kStages) * SM::STAGE;
+    const unsigned char* vb = kb + SM::K_BYTES;
 #pragma unroll
-      for (int qs = 0; qs < kQSub; ++qs) {
-        sc0[qs] = sn0[qs];
-        sc1[qs] = sn1[qs];
-      }
-    }
-    {
-      const int it = ntiles - 1;
-      int key0, valid;
-      tile_at(it, key0, valid);
-      if (valid < kBK) {
-        mask(0, valid, sc0);
-        mask(1, valid, sc1);
-      }
-      const unsigned char* vb = smem + (it % S) * SM::STAGE + SM::K_BYTES;
-      bf16x8 p0[kQSub][2], p1[kQSub][2];
-      probs(sc0, p0);
-      probs(sc1, p1);
-      accumulate(vb, 0, p0);
-      accumulate(vb, 1, p1);
-    }
-  } else {
-    {
-      int key0, valid;
-      tile_at(0, key0, valid);
-      issue_tile(key0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      next_tile(it);
-      int key0, valid;
-      tile_at(it, key0, valid);
-      const unsigned char* kb = smem + (it & 1) * SM::STAGE;
-      const unsigned char* vb = kb + SM::K_BYTES;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc[kQSub];
-        bf16x8 pf[kQSub][2];
-        scores(kb, kt, sacc);
-        if (valid < kBK) mask(kt, valid, sacc);
-        if constexpr (FALLBACK) online_max(sacc);
-        probs(sacc, pf);
-        accumulate(vb, kt, pf);
-      }
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      __syncthreads();
+    for (int half = 0; half < 2; ++half) {
+      f32x4 sacc[2][kQT];
+      bf16x8 pf[kQT];
+      scores(kb, half, sacc);
+      if (valid < kBK) mask(half, valid, sacc);
+      if constexpr (FALLBACK) online_max(sacc);
+      probs(sacc, pf);
+      accumulate(vb, half, pf);
     }
   }
 
-  // ---- normalise and store o_s (bf16) ----
+  // ---- normalise and store (bf16): lane holds d rows 16 dt + 4 g + i of query l16 of tile j ----
 #pragma unroll
-  for (int qs = 0; qs < kQSub; ++qs) {
-    const float tot = lsum[qs] + __shfl_xor(lsum[qs], 32);
+  for (int j = 0; j < kQT; ++j) {
+    float tot = lsum[j] + __shfl_xor(lsum[j], 16);
+    tot += __shfl_xor(tot, 32);
     const float inv = 1.0f / tot;
-    const int n = n_base + qs * 32 + l32;
+    const int n = n_base + 16 * j + l16;
     if (n < nrows) {
       bf16_t* op = odst + (int64_t)n * H * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) {
+        __bf16 b4[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          __bf16 b4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) b4[e] = (__bf16)(oacc[qs][dt][g * 4 + e] * inv);
-          *reinterpret_cast<uint2*>(op + dt * 32 + g * 8 + hl * 4) = __builtin_bit_cast(uint2, b4);
-        }
+        for (int i = 0; i < 4; ++i) b4[i] = (__bf16)(oacc[dt][j][i] * inv);
+        *reinterpret_cast<uint2*>(op + dt * 16 + g * 4) = __builtin_bit_cast(uint2, b4);
+      }
     }
   }
 }
@@ -542,10 +480,10 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   P.c_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int grid = softmax_grid(s, in.ctx_out != nullptr);
   const size_t smem = kStages * Smem<D>::STAGE;
-  (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
-  (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
+  (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipLaunchKernelGGL((softmax_mfma_kernel<D, false>), dim3(grid), dim3(kWaves * 64), smem, st, P);
   hipLaunchKernelGGL((softmax_mfma_kernel<D, true>), dim3(grid), dim3(kWaves * 64), smem, st, P);
 }

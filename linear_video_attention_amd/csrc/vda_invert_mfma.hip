@@ -35,7 +35,7 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ minv, const float* __restrict__ bw,
+__global__ __launch_bounds__(256, 2) void vda_invert_kernel(float* __restrict__ minv, const float* __restrict__ bw,
                                                          const float* __restrict__ alpha, float* __restrict__ cw,
                                                          bf16_t* __restrict__ mhl, int T, int H, int anchors) {
   constexpr int R = D / 16;
@@ -132,7 +132,9 @@ __global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ min
 #pragma unroll
       for (int i = 0; i < 4; ++i) cout[(int64_t)(16 * rt + i) * D + 16 * ct] = acc[rt][ct][i];
 
-  // 4. with a decay gate: step planes = M Diag(alpha_f), rebuilt in LDS once C no longer needs M
+  // 4. with a decay gate: step planes = M Diag(alpha_f), rebuilt in LDS once C no longer needs M.
+  // Each thread reads back the fp32 elements of M it wrote in step 2 (its own writes, so no fence
+  // is needed), which keeps M out of registers across step 3.
   if (af) {
     float a[R];
 #pragma unroll
@@ -141,11 +143,16 @@ __global__ __launch_bounds__(256) void vda_invert_kernel(float* __restrict__ min
 #pragma unroll
     for (int ii = 0; ii < R; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < R; ++jj) {
-        const float gv = g[ii][jj] * a[jj];
-        const __bf16 xh = (__bf16)gv;
-        mp[0][ty * R + ii][tx * R + jj] = __builtin_bit_cast(bf16_t, xh);
-        mp[1][ty * R + ii][tx * R + jj] = __builtin_bit_cast(bf16_t, (__bf16)(gv - (float)xh));
+      for (int j4 = 0; j4 < R / 4; ++j4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(minv + mbase + (int64_t)(ty * R + ii) * D + tx * R + 4 * j4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 4 * j4 + e;
+          const float gv = x[e] * a[jj];
+          const __bf16 xh = (__bf16)gv;
+          mp[0][ty * R + ii][tx * R + jj] = __builtin_bit_cast(bf16_t, xh);
+          mp[1][ty * R + ii][tx * R + jj] = __builtin_bit_cast(bf16_t, (__bf16)(gv - (float)xh));
+        }
       }
     __syncthreads();
     write_planes();
