@@ -100,14 +100,15 @@ def frame_sets(t: int, T: int, C: int, anchors: bool):
 # every frame; the softmax attends to text, window and anchor keys.  Exact softmax, fp32.
 # ----------------------------------------------------------------------------------------------
 
-def softmax_rows(qr: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
-    """Exact softmax attention of query rows ``qr`` [m, d] over keys/values [n, d], fp32."""
+def softmax_rows(qr: np.ndarray, keys: np.ndarray, vals: np.ndarray, dtype=np.float32) -> np.ndarray:
+    """Exact softmax attention of query rows ``qr`` [m, d] over keys/values [n, d], in ``dtype``
+    (fp32 by default; fp64 for derivative checks)."""
     d = qr.shape[-1]
-    tau = np.float32(1.0 / math.sqrt(d))
-    s = (qr.astype(np.float32) @ keys.astype(np.float32).T) * tau
+    tau = dtype(1.0 / math.sqrt(d))
+    s = (qr.astype(dtype) @ keys.astype(dtype).T) * tau
     s = s - s.max(axis=1, keepdims=True)
-    p = np.exp(s, dtype=np.float32)
-    return (p @ vals.astype(np.float32)) / p.sum(axis=1, keepdims=True, dtype=np.float32)
+    p = np.exp(s, dtype=dtype)
+    return (p @ vals.astype(dtype)) / p.sum(axis=1, keepdims=True, dtype=dtype)
 
 
 def key_frames(t: int, T: int, C: int, anchors: bool) -> list[int]:
@@ -116,7 +117,7 @@ def key_frames(t: int, T: int, C: int, anchors: bool) -> list[int]:
 
 
 def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None,
-                   audio_v=None) -> np.ndarray:
+                   audio_v=None, dtype=np.float32) -> np.ndarray:
     """o_s for every video token (``rows=None``) or for the given token indices; float32.
 
     Global keys are the text tokens and, when given, the audio tokens ([GLN]: interactions with
@@ -129,7 +130,7 @@ def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k
     TN, H, d = q.shape
     assert TN == T * N
     rows = np.arange(TN) if rows is None else np.asarray(rows)
-    out = np.zeros((len(rows), H, d), np.float32)
+    out = np.zeros((len(rows), H, d), dtype)
     frames_of_rows = rows // N
     for t in np.unique(frames_of_rows):
         sel = np.nonzero(frames_of_rows == t)[0]
@@ -138,7 +139,7 @@ def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k
         for h in range(H):
             keys = np.concatenate([text_k[:, h], k[idx, h]], axis=0)
             vals = np.concatenate([text_v[:, h], v[idx, h]], axis=0)
-            out[sel, h] = softmax_rows(q[rows[sel], h], keys, vals)
+            out[sel, h] = softmax_rows(q[rows[sel], h], keys, vals, dtype)
     return out
 
 
@@ -280,7 +281,7 @@ def merge(q, o_s, o_l, gate_w, proj_w, eps=RMS_EPS):
 # ----------------------------------------------------------------------------------------------
 
 def vdn_forward(inp: dict, T, N, C, anchors=True, rows=None, text_mode="half_beta",
-                with_intermediates=False):
+                with_intermediates=False, softmax_dtype=np.float32):
     """Layer output ``out`` [len(rows) or T*N, H, d] (fp64) from the inputs dict.
 
     ``inp`` holds float32 arrays: q, k, v, text_k, text_v, beta, gate_w, proj_w, and optionally
@@ -292,7 +293,8 @@ def vdn_forward(inp: dict, T, N, C, anchors=True, rows=None, text_mode="half_bet
     tk, tv = inp["text_k"], inp["text_v"]
     beta = inp["beta"]
     rows_arr = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
-    o_s = softmax_branch(q, k, v, tk, tv, T, N, C, anchors, rows_arr, inp.get("audio_k"), inp.get("audio_v"))
+    o_s = softmax_branch(q, k, v, tk, tv, T, N, C, anchors, rows_arr, inp.get("audio_k"), inp.get("audio_v"),
+                         softmax_dtype)
     o_l = linear_branch(q, k, v, beta, tk, tv, T, N, C, anchors, rows_arr, text_mode,
                         alpha=inp.get("alpha"))
     out = merge(q[rows_arr], o_s, o_l, inp["gate_w"], inp["proj_w"])

@@ -651,3 +651,119 @@ def pin_bruteforce_joint(orc, seed=34):
         assert np.allclose(out_s, out_b, rtol=1e-5, atol=1e-5), ("out", ci)
         ctx = orc.context_rows(inp, T, N)
         assert np.allclose(ctx, bruteforce.context_dense(inp, T, N, C, anchors), rtol=1e-5, atol=1e-6), ("ctx", ci)
+
+
+# --------------------------------------------------------------------------------------------
+# Backward pass.  The reverse-mode oracle (oracle/vdn_backward.py) against (a) torch autograd on an
+# independent dense float64 forward written here from the same rules, and (b) central finite
+# differences of the numpy forward oracle (softmax in float64) along random directions.
+# --------------------------------------------------------------------------------------------
+
+BWD_INPUTS = ("q", "k", "v", "beta", "text_k", "text_v", "gate_w", "proj_w")
+
+
+def torch_layer_forward(x, T, N, C, anchors, eps=1e-6):
+    """Dense float64 forward in torch: one mask over [text, video] keys built from the frame rule,
+    every query frame's states rebuilt from the text state by repeated solves."""
+    import torch
+    q, k, v, beta = x["q"], x["k"], x["v"], x["beta"]
+    tk, tv = x["text_k"], x["text_v"]
+    alpha = x.get("alpha")
+    TN, H, d = q.shape
+    n_text = tk.shape[0]
+    bset = (0, T - 1) if anchors else ()
+    tau = 1.0 / math.sqrt(d)
+    mask = torch.tensor(bruteforce.dense_mask(T, N, n_text, C, anchors))
+    eye = torch.eye(d, dtype=torch.float64)
+    outs = []
+    for h in range(H):
+        keys = torch.cat([tk[:, h], k[:, h]])
+        vals = torch.cat([tv[:, h], v[:, h]])
+        s = (q[:, h] @ keys.T) * tau
+        s = s.masked_fill(~mask, float("-inf"))
+        o_s = torch.softmax(s, dim=1) @ vals
+
+        def step(z, kf, vf, bf, a=None):
+            zbar = z if a is None else z * a[None, :]
+            amat = (kf * bf[:, None]).T @ kf
+            bmat = (vf * bf[:, None]).T @ kf
+            return torch.linalg.solve((eye + amat).T, (zbar + bmat).T).T
+        s0 = step(torch.zeros(d, d, dtype=torch.float64), tk[:, h], tv[:, h], 0.5 * beta[:n_text, h])
+        rows = []
+        for t in range(T):
+            c = t // C
+            zf, zr = s0, s0
+            if t not in bset:
+                for f in range(T):
+                    if f not in bset and f // C < c - 1:
+                        sl = slice(f * N, (f + 1) * N)
+                        zf = step(zf, k[sl, h], v[sl, h], beta[n_text + f * N:n_text + (f + 1) * N, h],
+                                  None if alpha is None else alpha[f, h])
+                for f in range(T - 1, -1, -1):
+                    if f not in bset and f // C > c + 1:
+                        sl = slice(f * N, (f + 1) * N)
+                        zr = step(zr, k[sl, h], v[sl, h], beta[n_text + f * N:n_text + (f + 1) * N, h],
+                                  None if alpha is None else alpha[f, h])
+            rows.append(q[t * N:(t + 1) * N, h] @ (zf + zr).T)
+        o_l = torch.cat(rows)
+        gs = torch.sigmoid(q[:, h] @ x["gate_w"][0])
+        gl = torch.sigmoid(q[:, h] @ x["gate_w"][1])
+        r = o_l / torch.sqrt(torch.mean(o_l * o_l, dim=1, keepdim=True) + eps)
+        outs.append((gs * o_s) @ x["proj_w"][0] + (gl * r) @ x["proj_w"][1])
+    return torch.stack(outs, dim=1)
+
+
+BWD_CASES = [
+    # T, N, C, n_text, H, d, anchors, decay
+    (7, 3, 2, 2, 2, 4, True, False),
+    (6, 2, 1, 3, 1, 5, False, False),
+    (9, 2, 2, 1, 1, 4, True, True),
+    (5, 3, 5, 0, 1, 4, True, False),
+]
+
+
+def _bwd_inputs(T, N, n_text, H, d, decay, seed):
+    inp = {key: val.astype(np.float64) for key, val in tiny_inputs(T, N, n_text, H, d, seed).items()}
+    if decay:
+        inp["alpha"] = 0.5 + 0.5 * _rng(seed + 7).random((T, H, d))
+    return inp
+
+
+def pin_backward_autograd(bwd, seed=40):
+    """The reverse-mode oracle equals torch autograd through an independent dense forward."""
+    import torch
+    for ci, (T, N, C, n_text, H, d, anchors, decay) in enumerate(BWD_CASES):
+        inp = _bwd_inputs(T, N, n_text, H, d, decay, seed + ci)
+        dout = _rng(seed + 100 + ci).standard_normal((T * N, H, d))
+        x = {key: torch.tensor(val, requires_grad=True) for key, val in inp.items()}
+        out = torch_layer_forward(x, T, N, C, anchors)
+        loss = torch.sum(out * torch.tensor(dout))
+        names = [key for key in x if key != "alpha" or decay]
+        auto = dict(zip(names, torch.autograd.grad(loss, [x[n] for n in names])))
+        got = bwd.vdn_backward(inp, dout, T, N, C, anchors)
+        for name in names:
+            ref = auto[name].numpy()
+            scale = max(1.0, float(np.abs(ref).max())) if ref.size else 1.0
+            assert np.allclose(got[name], ref, rtol=1e-8, atol=1e-9 * scale), (ci, name, np.abs(got[name] - ref).max())
+
+
+def pin_backward_finite_differences(bwd, seed=50):
+    """Directional derivatives of <dout, out> by central differences of the numpy forward oracle
+    (float64 softmax) equal <gradient, direction> for every input, one random direction each."""
+    from oracle import vdn_oracle as orc
+    for ci, (T, N, C, n_text, H, d, anchors, decay) in enumerate(BWD_CASES[:3]):
+        inp = _bwd_inputs(T, N, n_text, H, d, decay, seed + ci)
+        dout = _rng(seed + 200 + ci).standard_normal((T * N, H, d))
+        got = bwd.vdn_backward(inp, dout, T, N, C, anchors)
+        loss = lambda x: float(np.sum(dout * orc.vdn_forward(x, T, N, C, anchors, softmax_dtype=np.float64)))
+        rng = _rng(seed + 300 + ci)
+        for name in got:
+            delta = rng.standard_normal(inp[name].shape)
+            eps = 1e-5
+            plus = dict(inp)
+            minus = dict(inp)
+            plus[name] = inp[name] + eps * delta
+            minus[name] = inp[name] - eps * delta
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = float(np.sum(got[name] * delta))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (ci, name, fd, an)

@@ -1,0 +1,102 @@
+"""The backward-pass oracle against autograd and finite differences (no GPU)."""
+
+import pytest
+
+import pins
+from oracle import vdn_backward as bwd
+
+
+@pytest.mark.parametrize("pin", [pins.pin_backward_autograd, pins.pin_backward_finite_differences],
+                         ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(bwd)
+
+
+import importlib.util
+import os
+
+import numpy as np
+
+BWD_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "vdn_backward.py")
+
+
+def fresh_backward():
+    spec = importlib.util.spec_from_file_location("vdn_backward_mutant", BWD_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def m_softmax_no_rowsum(b):
+    """The rowsum(P dP) term of the softmax Jacobian dropped."""
+    orig_exp = np.exp
+
+    def softmax_backward(q, k, v, text_k, text_v, T, N, C, anchors, do_s):
+        import math
+        TN, H, d = q.shape
+        tau = 1.0 / math.sqrt(d)
+        n_text = text_k.shape[0]
+        dq = np.zeros((TN, H, d)); dk = np.zeros((TN, H, d)); dv = np.zeros((TN, H, d))
+        dtk = np.zeros((n_text, H, d)); dtv = np.zeros((n_text, H, d))
+        for t in range(T):
+            rows = np.arange(t * N, (t + 1) * N)
+            kf = b.orc.key_frames(t, T, C, anchors)
+            idx = np.concatenate([np.arange(f * N, (f + 1) * N) for f in kf])
+            for h in range(H):
+                qh = q[rows, h].astype(np.float64)
+                keys = np.concatenate([text_k[:, h], k[idx, h]]).astype(np.float64)
+                vals = np.concatenate([text_v[:, h], v[idx, h]]).astype(np.float64)
+                s = tau * (qh @ keys.T)
+                p = orig_exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                do = do_s[rows, h].astype(np.float64)
+                ds = p * (do @ vals.T)
+                dq[rows, h] += tau * (ds @ keys)
+                dkeys, dvals = tau * (ds.T @ qh), p.T @ do
+                dtk[:, h] += dkeys[:n_text]; dtv[:, h] += dvals[:n_text]
+                dk[idx, h] += dkeys[n_text:]; dv[idx, h] += dvals[n_text:]
+        return dq, dk, dv, dtk, dtv
+    b.softmax_backward = softmax_backward
+
+
+def m_text_full_weight(b):
+    """Text token gradients taken at full write strength instead of beta/2."""
+    orig = b.frame_stats_backward
+    b.frame_stats_backward = lambda kf, vf, bf, da, db, weight_scale=1.0: orig(kf, vf, bf, da, db, 1.0)
+
+
+def m_gram_gradient_sign(b):
+    """dA taken as +M dM M (the inverse's derivative with the wrong sign)."""
+    orig = b.frame_stats_backward
+    b.frame_stats_backward = lambda kf, vf, bf, da, db, weight_scale=1.0: orig(kf, vf, bf, -da, db, weight_scale)
+
+
+def m_rms_no_projection(b):
+    """The RMSNorm Jacobian reduced to 1/rho (its projection term dropped)."""
+    orig = b.merge_backward
+
+    def merge_backward(q, o_s, o_l, gate_w, proj_w, dout, eps=b.orc.RMS_EPS):
+        dq, do_s, do_l, dgate, dproj = orig(q, o_s, o_l, gate_w, proj_w, dout, eps)
+        o_l = np.asarray(o_l, np.float64)
+        rho = np.sqrt(np.mean(o_l * o_l, axis=-1, keepdims=True) + eps)
+        r = o_l / rho
+        dr = do_l * rho + r * np.mean(r * (do_l * rho), axis=-1, keepdims=True)  # undo, then drop
+        return dq, do_s, dr / rho, dgate, dproj
+    b.merge_backward = merge_backward
+
+
+BWD_MUTANTS = [
+    (m_softmax_no_rowsum, pins.pin_backward_autograd),
+    (m_text_full_weight, pins.pin_backward_autograd),
+    (m_gram_gradient_sign, pins.pin_backward_finite_differences),
+    (m_rms_no_projection, pins.pin_backward_finite_differences),
+]
+
+
+@pytest.mark.parametrize("mutate,pin", BWD_MUTANTS, ids=[m.__name__ for m, _ in BWD_MUTANTS])
+def test_backward_mutant_is_caught(mutate, pin):
+    b = fresh_backward()
+    pin(b)
+    mutate(b)
+    with pytest.raises(AssertionError):
+        pin(b)

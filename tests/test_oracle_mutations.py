@@ -127,7 +127,7 @@ def m_softmax_ignores_anchors(o):
 
 
 def m_softmax_scale(o):
-    def softmax_rows(qr, keys, vals):
+    def softmax_rows(qr, keys, vals, dtype=np.float32):
         s = (qr.astype(np.float32) @ keys.astype(np.float32).T) / np.float32(qr.shape[-1])
         p = np.exp(s - s.max(axis=1, keepdims=True))
         return (p @ vals.astype(np.float32)) / p.sum(axis=1, keepdims=True)
@@ -137,8 +137,9 @@ def m_softmax_scale(o):
 def m_softmax_no_text(o):
     orig = o.softmax_branch
 
-    def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None):
-        return orig(q, k, v, text_k[:0], text_v[:0], T, N, C, anchors, rows)
+    def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None,
+                       dtype=np.float32):
+        return orig(q, k, v, text_k[:0], text_v[:0], T, N, C, anchors, rows, audio_k, audio_v, dtype)
     o.softmax_branch = softmax_branch
 
 
@@ -218,8 +219,9 @@ def m_audio_written_to_linear(o):
 def m_audio_dropped_from_softmax(o):
     orig = o.softmax_branch
 
-    def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None):
-        return orig(q, k, v, text_k, text_v, T, N, C, anchors, rows)
+    def softmax_branch(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None,
+                       dtype=np.float32):
+        return orig(q, k, v, text_k, text_v, T, N, C, anchors, rows, dtype=dtype)
     o.softmax_branch = softmax_branch
 
 
