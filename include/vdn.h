@@ -140,6 +140,24 @@ vdn_status vdn_forward_joint(const vdn_plan *plan, const void *q, const void *k,
                              const float *alpha, const void *gate_w, const void *proj_w,
                              void *out, void *ctx_out, void *stream);
 
+/* Backward pass (reverse mode) of the layer for the output gradient dout ([T*N][H][d], plan dtype):
+ * the transposes of every step of the forward definition above -- the merge ("Gating the Softmax
+ * and Linear Branch Outputs"), the softmax branch ("Local Softmax and Long-Range Linear Memory") and
+ * both frame scans with the text initialisation and, when alpha is given, the decay gate ("Video
+ * Delta Attention: A Frame-Wise Solution").  Inputs as vdn_forward / vdn_forward_decay (alpha may
+ * be NULL: no decay).  Outputs, all float32 device buffers owned by the caller and overwritten:
+ * dq, dk, dv [T*N][H][d]; dbeta [n_text + T*N][H]; dtext_kv [2][n_text][H][d] (NULL iff
+ * n_text == 0); dgate_w, dproj_w [2][d][d]; dalpha [T][H][d] or NULL (requires alpha).  The call
+ * recomputes the forward quantities it needs on `stream`.  The first call on a plan allocates a
+ * backward workspace (about 6 T N H d float32 plus per-frame d x d matrices) that the plan keeps.
+ * Plans with audio tokens are VDN_ERR_UNSUPPORTED; other errors as vdn_forward, plus
+ * VDN_ERR_INVALID_ARG when an output aliases an input. */
+vdn_status vdn_backward(vdn_plan *plan, const void *q, const void *k, const void *v,
+                        const float *beta, const void *text_kv, const float *alpha,
+                        const void *gate_w, const void *proj_w, const void *dout, float *dq,
+                        float *dk, float *dv, float *dbeta, float *dtext_kv, float *dgate_w,
+                        float *dproj_w, float *dalpha, void *stream);
+
 /* Free the plan's workspace, stream and events.  The caller must have synchronised the streams
  * the plan was used on.  NULL is a no-op. */
 void vdn_plan_destroy(vdn_plan *plan);

@@ -29,6 +29,7 @@ SOURCES = [
     "epilogue_simt.hip",
     "epilogue_mfma.hip",
     "calibrate.hip",
+    "backward.hip",
 ]
 
 ARCH = "gfx950"

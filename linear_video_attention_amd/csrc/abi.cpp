@@ -2,6 +2,7 @@
 // timing.  The kernels themselves live in the .hip files; see include/vdn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -21,6 +22,9 @@ struct vdn_plan {
   bool overlap = false;                          // linear branch on the side stream
   mutable int prof_max = 0, prof_count = 0;
   mutable std::vector<hipEvent_t> prof_events;   // [prof_max][VDN_NUM_STAGES][2]
+  // backward workspace and tables, allocated by the first vdn_backward call
+  char* bws = nullptr;
+  vdn::BwdBuffers bw{};
 };
 
 namespace {
@@ -57,6 +61,7 @@ void free_plan(vdn_plan* p) {
   if (p->ev_join) (void)hipEventDestroy(p->ev_join);
   if (p->side) (void)hipStreamDestroy(p->side);
   if (p->ws) (void)hipFree(p->ws);
+  if (p->bws) (void)hipFree(p->bws);
   delete p;
 }
 
@@ -277,6 +282,186 @@ vdn_status vdn_forward_joint(const vdn_plan* plan, const void* q, const void* k,
                              const void* ctx_q, const void* ctx_kv, const float* alpha, const void* gate_w,
                              const void* proj_w, void* out, void* ctx_out, void* stream) {
   return forward_impl(plan, q, k, v, beta, ctx_q, ctx_kv, alpha, gate_w, proj_w, out, ctx_out, stream);
+}
+
+namespace {
+
+// Backward workspace: buffers and host-built tables (scan order, readout slots, query ranges per
+// key slot, row segments), allocated once per plan.
+vdn_status ensure_backward(vdn_plan* p) {
+  if (p->bws) return VDN_OK;
+  const vdn::Shape& s = p->s;
+  const int T = s.T, N = s.N, H = s.H, d = s.d, Nc = s.Nc, C = s.C;
+  const int64_t rows = (int64_t)T * N * H;
+  const int64_t dd = (int64_t)d * d;
+  // scan order and readout slots
+  std::vector<int> order;
+  for (int f = 0; f < T; ++f)
+    if (!vdn::is_boundary(s, f)) order.push_back(f);
+  const int nslots = Nc + 2;
+  std::vector<int> mslot(2 * nslots, 0);
+  for (int c = 0; c < Nc; ++c) {
+    int mf = 0, mr = 0;
+    for (int f : order) {
+      if (f / C <= c - 2) ++mf;
+      if (f / C >= c + 2) ++mr;
+    }
+    mslot[c] = mf;
+    mslot[nslots + c] = mr;
+  }
+  // query-frame ranges for each key slot (0 = text: every frame; 1 + f = frame f)
+  std::vector<int> qr((size_t)(T + 1) * 2 * vdn::kMaxRanges, 0), nqr(T + 1, 0);
+  for (int slot = 0; slot <= T; ++slot) {
+    int n = 0, start = -1;
+    for (int t = 0; t <= T; ++t) {
+      bool sees = false;
+      if (t < T) {
+        if (slot == 0) sees = true;
+        else {
+          const int f = slot - 1;
+          int64_t r[2 * vdn::kMaxRanges];
+          const int nr = vdn::key_ranges(s, t, r, vdn::kMaxRanges);
+          const int64_t key = (int64_t)s.ctx_pad + (int64_t)f * N;
+          for (int i = 0; i < nr; ++i) sees |= (r[2 * i] <= key && key < r[2 * i + 1]);
+        }
+      }
+      if (sees && start < 0) start = t;
+      if (!sees && start >= 0) {
+        if (n >= vdn::kMaxRanges) return VDN_ERR_UNSUPPORTED;
+        qr[(size_t)slot * 2 * vdn::kMaxRanges + 2 * n] = start;
+        qr[(size_t)slot * 2 * vdn::kMaxRanges + 2 * n + 1] = t;
+        ++n;
+        start = -1;
+      }
+    }
+    nqr[slot] = n;
+  }
+  // row segments: all rows of all heads; each chunk's non-boundary frames and each boundary
+  // frame, per head
+  std::vector<vdn::Segment> seg_all{{0, T * N, -1}}, seg_read;
+  for (int c = 0; c < nslots; ++c)
+    for (int h = 0; h < H; ++h) {
+      int f0 = 0, f1 = 0;
+      if (c < Nc) {
+        f0 = c * C;
+        f1 = std::min(T, (c + 1) * C);
+        while (f0 < f1 && vdn::is_boundary(s, f0)) ++f0;
+        while (f1 > f0 && vdn::is_boundary(s, f1 - 1)) --f1;
+      } else if (s.anchors) {
+        f0 = c == Nc ? 0 : T - 1;
+        f1 = f0 + 1;
+        if (c == Nc + 1 && T == 1) f1 = f0;          // a single frame is one boundary frame
+      }
+      seg_read.push_back({(int64_t)f0 * N, (f1 - f0) * N, h});
+    }
+  const int splits_all = 512, splits_read = 8;
+  // layout
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += (size_t)vdn::round_up((int64_t)bytes, 256); return o; };
+  const size_t o_rows6 = take((size_t)6 * rows * d * 4);
+  const size_t o_dsum = take((size_t)rows * 4), o_lse = take((size_t)rows * 4);
+  const size_t o_part = take((size_t)std::max<int64_t>(splits_all, (int64_t)nslots * H * splits_read) * dd * 4);
+  const size_t o_dread = take((size_t)nslots * H * dd * 4);
+  const size_t o_z = take((size_t)3 * 2 * T * H * dd * 4);
+  const size_t o_dal = take((size_t)2 * T * H * d * 4);
+  const size_t o_ds0 = take((size_t)2 * H * dd * 4);
+  const size_t o_order = take(std::max<size_t>(1, order.size()) * 4), o_ms = take(mslot.size() * 4);
+  const size_t o_qr = take(qr.size() * 4), o_nqr = take(nqr.size() * 4);
+  const size_t o_sa = take(seg_all.size() * sizeof(vdn::Segment)), o_sr = take(seg_read.size() * sizeof(vdn::Segment));
+  char* ws = nullptr;
+  if (hipMalloc(&ws, off) != hipSuccess) {
+    (void)hipGetLastError();
+    return VDN_ERR_OUT_OF_MEMORY;
+  }
+  auto up = [&](size_t o, const void* src, size_t bytes) {
+    return bytes == 0 || hipMemcpy(ws + o, src, bytes, hipMemcpyHostToDevice) == hipSuccess;
+  };
+  if (!up(o_order, order.data(), order.size() * 4) || !up(o_ms, mslot.data(), mslot.size() * 4) ||
+      !up(o_qr, qr.data(), qr.size() * 4) || !up(o_nqr, nqr.data(), nqr.size() * 4) ||
+      !up(o_sa, seg_all.data(), seg_all.size() * sizeof(vdn::Segment)) ||
+      !up(o_sr, seg_read.data(), seg_read.size() * sizeof(vdn::Segment))) {
+    (void)hipFree(ws);
+    return VDN_ERR_HIP;
+  }
+  vdn::BwdBuffers& w = p->bw;
+  float* r6 = reinterpret_cast<float*>(ws + o_rows6);
+  w.do_s = r6;
+  w.do_l = r6 + rows * d;
+  w.x_s = r6 + 2 * rows * d;
+  w.x_l = r6 + 3 * rows * d;
+  w.dz_s = r6 + 4 * rows * d;
+  w.dz_l = r6 + 5 * rows * d;
+  w.dsum = reinterpret_cast<float*>(ws + o_dsum);
+  w.lse = reinterpret_cast<float*>(ws + o_lse);
+  w.partial = reinterpret_cast<float*>(ws + o_part);
+  w.dread = reinterpret_cast<float*>(ws + o_dread);
+  float* z = reinterpret_cast<float*>(ws + o_z);
+  w.zin = z;
+  w.dmf = z + 2 * (int64_t)T * H * dd;
+  w.dbf = z + 4 * (int64_t)T * H * dd;
+  w.dalf = reinterpret_cast<float*>(ws + o_dal);
+  w.ds0 = reinterpret_cast<float*>(ws + o_ds0);
+  w.order = reinterpret_cast<const int*>(ws + o_order);
+  w.mslot = reinterpret_cast<const int*>(ws + o_ms);
+  w.qranges = reinterpret_cast<const int*>(ws + o_qr);
+  w.nqranges = reinterpret_cast<const int*>(ws + o_nqr);
+  w.seg_all = reinterpret_cast<const vdn::Segment*>(ws + o_sa);
+  w.seg_read = reinterpret_cast<const vdn::Segment*>(ws + o_sr);
+  w.splits_all = splits_all;
+  w.splits_read = splits_read;
+  w.nscan = (int)order.size();
+  p->bws = ws;
+  return VDN_OK;
+}
+
+}  // namespace
+
+vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                        const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
+                        const void* dout, float* dq, float* dk, float* dv, float* dbeta, float* dtext_kv,
+                        float* dgate_w, float* dproj_w, float* dalpha, void* stream) {
+  if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !dout || !dq || !dk || !dv || !dbeta || !dgate_w ||
+      !dproj_w)
+    return VDN_ERR_INVALID_ARG;
+  if (plan->s.n_audio > 0) return VDN_ERR_UNSUPPORTED;
+  if (plan->s.n_text > 0 && (!text_kv || !dtext_kv)) return VDN_ERR_INVALID_ARG;
+  if (dalpha && !alpha) return VDN_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, dout, dq, dk, dv, dbeta, dgate_w, dproj_w};
+  for (const void* ptr : ptrs) if (!aligned16(ptr)) return VDN_ERR_INVALID_ARG;
+  const void* opt[] = {text_kv, dtext_kv, alpha, dalpha};
+  for (const void* ptr : opt) if (ptr && !aligned16(ptr)) return VDN_ERR_INVALID_ARG;
+  const void* outs[] = {dq, dk, dv, dbeta, dtext_kv, dgate_w, dproj_w, dalpha};
+  const void* ins[] = {q, k, v, beta, text_kv, alpha, gate_w, proj_w, dout};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o && o == i) return VDN_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
+  if (dev != plan->device) return VDN_ERR_INVALID_ARG;
+  vdn_status st = ensure_backward(plan);
+  if (st != VDN_OK) return st;
+
+  const vdn::Shape& s = plan->s;
+  hipStream_t main = reinterpret_cast<hipStream_t>(stream);
+  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, nullptr, alpha, nullptr, nullptr};
+  vdn::Buffers b = buffers_of(plan);
+  b.lse = plan->bw.lse;
+  vdn::BwdBuffers w = plan->bw;
+  w.dout = dout;
+  vdn::BwdOutputs o{dq, dk, dv, dbeta, dtext_kv, dgate_w, dproj_w, dalpha};
+#define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
+  // forward recomputation: linear-branch states, softmax output and its normalisers
+  VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, main));
+  VDN_TRY(vdn::launch_vda_scan(s, in, b, plan->kinds.scan_mfma, main));
+  if (plan->kinds.softmax_mfma) {
+    VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
+    VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
+  } else {
+    VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
+  }
+  VDN_TRY(vdn::launch_backward(s, in, b, w, o, main));
+#undef VDN_TRY
+  return VDN_OK;
 }
 
 vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes) {

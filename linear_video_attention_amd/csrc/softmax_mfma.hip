@@ -95,6 +95,7 @@ struct Params {
   const bf16_t* vt;
   bf16_t* o_s;
   bf16_t* oc;               // their output [n_ctx][H][D]
+  float* lse;               // video rows: log2 of the normaliser in scaled-score units, or nullptr
   const int* ranges;
   const int* nranges;
   const float* kmax;
@@ -436,6 +437,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
     tot += __shfl_xor(tot, 32);
     const float inv = 1.0f / tot;
     const int n = n_base + 16 * j + l16;
+    if (P.lse && !ctx && n < nrows && g == 0) P.lse[((int64_t)t * P.N + n) * H + h] = mref[j] + __log2f(tot);
     if (n < nrows) {
       bf16_t* op = odst + (int64_t)n * H * D;
 #pragma unroll
@@ -458,6 +460,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   P.vt = b.vt;
   P.o_s = (bf16_t*)b.os;
   P.oc = (bf16_t*)in.ctx_out;
+  P.lse = b.lse;
   P.ranges = b.ranges;
   P.nranges = b.nranges;
   P.kmax = b.kmax;

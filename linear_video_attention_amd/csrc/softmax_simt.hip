@@ -23,7 +23,8 @@ template <typename Tin, int D>
 __global__ __launch_bounds__(64) void softmax_simt_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ ctx_kv, Tin* __restrict__ o, const int* __restrict__ ranges,
-    const int* __restrict__ nranges, int nq, int t0, int H, int n_ctx, int ctx_pad, float scale_log2) {
+    const int* __restrict__ nranges, int nq, int t0, int H, int n_ctx, int ctx_pad, float scale_log2,
+    float* __restrict__ lse) {
   const int t = t0 + blockIdx.y, h = blockIdx.z;
   const int n = blockIdx.x * 64 + threadIdx.x;
   if (n >= nq) return;
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(64) void softmax_simt_kernel(
     }
   }
   const float inv = 1.f / l;
+  if (lse) lse[tok * H + h] = m + __log2f(l);         // scores are in base-2 units here
   Tin* op = o + (tok * H + h) * D;
 #pragma unroll
   for (int i = 0; i < D; ++i) store_elt(op + i, acc[i] * inv);
@@ -74,11 +76,11 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   softmax_simt_kernel<Tin, D><<<dim3((s.N + 63) / 64, s.T, s.H), 64, 0, st>>>(
       (const Tin*)in.q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, (Tin*)b.os, b.ranges,
-      b.nranges, s.N, 0, s.H, s.n_ctx, s.ctx_pad, scale_log2);
+      b.nranges, s.N, 0, s.H, s.n_ctx, s.ctx_pad, scale_log2, b.lse);
   if (in.ctx_out)
     softmax_simt_kernel<Tin, D><<<dim3((s.n_ctx + 63) / 64, 1, s.H), 64, 0, st>>>(
         (const Tin*)in.ctx_q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, (Tin*)in.ctx_out,
-        b.ranges, b.nranges, s.n_ctx, s.T, s.H, s.n_ctx, s.ctx_pad, scale_log2);
+        b.ranges, b.nranges, s.n_ctx, s.T, s.H, s.n_ctx, s.ctx_pad, scale_log2, nullptr);
 }
 
 template <typename Tin>

@@ -80,6 +80,7 @@ struct Buffers {
   int* flags;
   const int* ranges;   // [T+1][2*kMaxRanges]
   const int* nranges;  // [T+1]
+  float* lse;          // [T*N][H] base-2 log of each video row's softmax normaliser, or nullptr
 };
 
 struct Inputs {
@@ -92,6 +93,36 @@ struct Inputs {
   const void* ctx_q;   // [n_ctx][H][d] text and audio query rows, or nullptr (not computed)
   void* ctx_out;       // [n_ctx][H][d] their attention output (with ctx_q)
 };
+
+// Backward pass.  Row segment for X^T Y reductions: rows [row0, row0 + nrows) of head `head`
+// (head < 0: every head) of [rows][H][d] arrays.
+struct Segment {
+  int64_t row0;
+  int nrows;
+  int head;
+};
+// Backward workspace (device) and host-built tables.
+struct BwdBuffers {
+  const void* dout;                     // [T*N][H][d] plan dtype (the caller's)
+  float *do_s, *do_l, *x_s, *x_l, *dz_s, *dz_l;   // [T*N][H][d]
+  float *dsum, *lse;                    // [T*N][H]
+  float* partial;                       // [segments][splits][d][d]
+  float* dread;                         // [Nc+2][H][d][d] readout adjoints (slots Nc, Nc+1: frames 0, T-1)
+  float *zin, *dmf, *dbf;               // [2][T][H][d][d]
+  float* dalf;                          // [2][T][H][d]
+  float* ds0;                           // [2][H][d][d]
+  const int* order;                     // [T] scanned frames, forward order
+  const int* mslot;                     // [2][Nc+2] state index each readout slot reads
+  const int* qranges;                   // [T+1][2*kMaxRanges] query-frame ranges per key slot
+  const int* nqranges;                  // [T+1]
+  const Segment *seg_all, *seg_read;    // 1 and (Nc+2)*H segments
+  int splits_all, splits_read, nscan;
+};
+struct BwdOutputs {
+  float *dq, *dk, *dv, *dbeta, *dtext_kv, *dgate_w, *dproj_w, *dalpha;
+};
+hipError_t launch_backward(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
+                           const BwdOutputs& o, hipStream_t st);
 
 // Number of workgroups of the MFMA softmax launch.
 // with_ctx: including the workgroups of the context query rows.

@@ -30,6 +30,7 @@ SIGNATURES = [
     ("vdn_forward", _c_int, [_vp] * 10),
     ("vdn_forward_decay", _c_int, [_vp] * 11),
     ("vdn_forward_joint", _c_int, [_vp] * 13),
+    ("vdn_backward", _c_int, [_vp] * 19),
     ("vdn_plan_destroy", None, [_vp]),
     ("vdn_status_str", ctypes.c_char_p, [_c_int]),
     ("vdn_plan_workspace_bytes", _c_size, [_vp]),
@@ -240,6 +241,35 @@ class Plan:
         else:
             vdn_forward_decay(self.handle, q, k, v, beta, tkv, alpha, gate_w, proj_w, out, stream)
         return out
+
+    def backward(self, q, k, v, beta, text_kv, gate_w, proj_w, dout, alpha=None, stream=None):
+        """Input gradients of the layer for the output gradient ``dout``; returns a dict of float32
+        device tensors (q, k, v, beta, text_kv, gate_w, proj_w and, with ``alpha``, alpha)."""
+        import torch
+        TN, H, d = self.T * self.N, self.H, self.d
+        dt = self.torch_dtype
+        for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+            self._expect(name, x, (TN, H, d), dt)
+        self._expect("beta", beta, (self.n_text + TN, H), torch.float32)
+        if self.n_text > 0:
+            self._expect("text_kv", text_kv, (2, self.n_text, H, d), dt)
+        self._expect("gate_w", gate_w, (2, d, d), dt)
+        self._expect("proj_w", proj_w, (2, d, d), dt)
+        if alpha is not None:
+            self._expect("alpha", alpha, (self.T, H, d), torch.float32)
+        f32 = dict(dtype=torch.float32, device=q.device)
+        g = dict(q=torch.empty((TN, H, d), **f32), k=torch.empty((TN, H, d), **f32),
+                 v=torch.empty((TN, H, d), **f32), beta=torch.empty((self.n_text + TN, H), **f32),
+                 text_kv=torch.empty((2, self.n_text, H, d), **f32) if self.n_text > 0 else None,
+                 gate_w=torch.empty((2, d, d), **f32), proj_w=torch.empty((2, d, d), **f32),
+                 alpha=torch.empty((self.T, H, d), **f32) if alpha is not None else None)
+        ptr = lambda x: None if x is None else x.data_ptr()
+        _check(lib().vdn_backward(self.handle, ptr(q), ptr(k), ptr(v), ptr(beta),
+                                  ptr(text_kv if self.n_text > 0 else None), ptr(alpha), ptr(gate_w),
+                                  ptr(proj_w), ptr(dout), ptr(g["q"]), ptr(g["k"]), ptr(g["v"]),
+                                  ptr(g["beta"]), ptr(g["text_kv"]), ptr(g["gate_w"]), ptr(g["proj_w"]),
+                                  ptr(g["alpha"]), _stream_ptr(stream)), "vdn_backward")
+        return {key: val for key, val in g.items() if val is not None}
 
     def debug_buffer(self, which, stream=None):
         """Copy an intermediate buffer of the last forward into a new device tensor."""

@@ -1,0 +1,72 @@
+"""Parity of the HIP backward pass (vdn_backward through the C ABI) with the reverse-mode oracle,
+gradient by gradient.  Bar as for the forward: max |gpu - oracle| <= 1e-4 * RMS(oracle) for fp32
+workloads and <= 2e-2 * RMS(oracle) for bf16 workloads (bf16 workloads store o_s in bf16 and run
+the forward's linear branch on split-bf16 MFMA operands, both inside that bar)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import vdn_backward as bwd
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import TOL, make_plan, rel_err, to_device  # noqa: E402
+
+
+def check_backward(w, seed=0, decay=False, generic=False, names=None):
+    inp = synth.make_inputs(w, seed=seed, decay=decay)
+    dout = np.random.default_rng(seed + 99).standard_normal((w.T * w.N, w.H, w.d)).astype(np.float32)
+    if w.dtype == "bf16":
+        dout = torch.from_numpy(dout).to(torch.bfloat16).float().numpy()
+    plan = make_plan(w, generic=generic)
+    dev = to_device(inp, w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = plan.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
+                      torch.from_numpy(dout).cuda().to(tdt), alpha=dev["alpha"])
+    torch.cuda.synchronize()
+    ref = bwd.vdn_backward({k: np.asarray(v, np.float64) if isinstance(v, np.ndarray) else v for k, v in inp.items()},
+                           dout.astype(np.float64), w.T, w.N, w.C, w.anchors)
+    got = {k: v.cpu().numpy() for k, v in g.items()}
+    if "text_kv" in got:
+        got["text_k"], got["text_v"] = got.pop("text_kv")
+    tol = TOL[w.dtype]
+    errs = {}
+    for name in (names or ref):
+        if ref[name].size == 0:
+            continue
+        errs[name] = rel_err(got[name], ref[name])
+    print(f"{w} decay={decay} generic={generic}: " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= tol, (name, e)
+    plan.close()
+
+
+def test_backward_tiny_fp32():
+    check_backward(synth.WORKLOADS["tiny"])
+
+
+def test_backward_tiny_fp32_decay():
+    check_backward(synth.WORKLOADS["tiny"], decay=True)
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_backward_small_bf16(generic):
+    check_backward(synth.WORKLOADS["small"], generic=generic)
+
+
+BWD_RAGGED = [
+    # n_text, T, N, C, H, d, dtype, anchors, decay
+    (5, 9, 40, 2, 2, 64, "fp32", True, False),
+    (0, 7, 24, 3, 1, 32, "fp32", False, False),
+    (3, 1, 16, 5, 1, 64, "fp32", True, False),
+    (7, 11, 72, 3, 2, 128, "bf16", True, True),
+    (2, 6, 64, 1, 1, 128, "bf16", False, False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_RAGGED, ids=lambda c: "x".join(str(x) for x in c))
+def test_backward_ragged(case):
+    n_text, T, N, C, H, d, dtype, anchors, decay = case
+    check_backward(synth.custom(n_text, T, N, C, H, d, dtype, "sigmoid", anchors), seed=4, decay=decay)
