@@ -30,6 +30,7 @@ SOURCES = [
     "epilogue_mfma.hip",
     "calibrate.hip",
     "backward.hip",
+    "backward_mfma.hip",
 ]
 
 ARCH = "gfx950"

@@ -354,6 +354,20 @@ vdn_status ensure_backward(vdn_plan* p) {
       }
       seg_read.push_back({(int64_t)f0 * N, (f1 - f0) * N, h});
     }
+  // dK/dV workgroups of the MFMA softmax backward: 128 keys of one slot each, the slots seen by
+  // every query frame (text, boundary frames) first
+  std::vector<int2> kblocks;
+  auto add_slot = [&](int slot) {
+    const int U = slot == 0 ? s.n_text : N;
+    for (int k0 = 0; k0 < U; k0 += 128) kblocks.push_back(make_int2(slot, k0));
+  };
+  if (s.n_text > 0) add_slot(0);
+  for (int f = 0; f < T; ++f)
+    if (vdn::is_boundary(s, f)) add_slot(1 + f);
+  for (int f = 0; f < T; ++f)
+    if (!vdn::is_boundary(s, f)) add_slot(1 + f);
+  const bool mfma_bwd = p->kinds.softmax_mfma;
+  const int64_t Lq = (int64_t)T * N + 64;
   const int splits_all = 512, splits_read = 8;
   // layout
   size_t off = 0;
@@ -368,6 +382,9 @@ vdn_status ensure_backward(vdn_plan* p) {
   const size_t o_order = take(std::max<size_t>(1, order.size()) * 4), o_ms = take(mslot.size() * 4);
   const size_t o_qr = take(qr.size() * 4), o_nqr = take(nqr.size() * 4);
   const size_t o_sa = take(seg_all.size() * sizeof(vdn::Segment)), o_sr = take(seg_read.size() * sizeof(vdn::Segment));
+  const size_t o_kb = take(std::max<size_t>(1, kblocks.size()) * sizeof(int2));
+  const size_t pack_bytes = mfma_bwd ? (size_t)H * d * 2 * (2 * Lq + 2 * s.Ls) + (size_t)rows * d * 2 : 0;
+  const size_t o_pack = take(pack_bytes);
   char* ws = nullptr;
   if (hipMalloc(&ws, off) != hipSuccess) {
     (void)hipGetLastError();
@@ -379,7 +396,9 @@ vdn_status ensure_backward(vdn_plan* p) {
   if (!up(o_order, order.data(), order.size() * 4) || !up(o_ms, mslot.data(), mslot.size() * 4) ||
       !up(o_qr, qr.data(), qr.size() * 4) || !up(o_nqr, nqr.data(), nqr.size() * 4) ||
       !up(o_sa, seg_all.data(), seg_all.size() * sizeof(vdn::Segment)) ||
-      !up(o_sr, seg_read.data(), seg_read.size() * sizeof(vdn::Segment))) {
+      !up(o_sr, seg_read.data(), seg_read.size() * sizeof(vdn::Segment)) ||
+      !up(o_kb, kblocks.data(), kblocks.size() * sizeof(int2)) ||
+      (pack_bytes && hipMemset(ws + o_pack, 0, pack_bytes) != hipSuccess)) {
     (void)hipFree(ws);
     return VDN_ERR_HIP;
   }
@@ -410,6 +429,17 @@ vdn_status ensure_backward(vdn_plan* p) {
   w.splits_all = splits_all;
   w.splits_read = splits_read;
   w.nscan = (int)order.size();
+  w.kblocks = reinterpret_cast<const int2*>(ws + o_kb);
+  w.nkblocks = (int)kblocks.size();
+  w.Lq = Lq;
+  if (mfma_bwd) {
+    uint16_t* pk = reinterpret_cast<uint16_t*>(ws + o_pack);
+    w.qt = pk;
+    w.dot = pk + (int64_t)H * d * Lq;
+    w.kt = pk + 2 * (int64_t)H * d * Lq;
+    w.vp = w.kt + (int64_t)H * d * s.Ls;
+    w.dos16 = w.vp + (int64_t)H * d * s.Ls;
+  }
   p->bws = ws;
   return VDN_OK;
 }
@@ -459,7 +489,7 @@ vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void
   } else {
     VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
   }
-  VDN_TRY(vdn::launch_backward(s, in, b, w, o, main));
+  VDN_TRY(vdn::launch_backward(s, in, b, w, o, plan->kinds.softmax_mfma, main));
 #undef VDN_TRY
   return VDN_OK;
 }

@@ -288,15 +288,16 @@ __global__ __launch_bounds__(kThreads) void xty_partial_kernel(const TX* __restr
     for (int jj = 0; jj < R; ++jj) out[(int64_t)(ty * R + ii) * D + tx * R + jj] = c[ii][jj];
 }
 
+// grid (segments, D*D / 256): one thread per output element, summing the splits in order
 template <int D>
 __global__ __launch_bounds__(kThreads) void xty_reduce_kernel(const float* __restrict__ partial, int splits,
                                                               float* __restrict__ out, float scale) {
   const int s = blockIdx.x;
-  for (int e = threadIdx.x; e < D * D; e += kThreads) {
-    float acc = 0.f;
-    for (int k = 0; k < splits; ++k) acc += partial[((int64_t)s * splits + k) * D * D + e];
-    out[(int64_t)s * D * D + e] = acc * scale;
-  }
+  const int e = blockIdx.y * kThreads + threadIdx.x;
+  if (e >= D * D) return;
+  float acc = 0.f;
+  for (int k = 0; k < splits; ++k) acc += partial[((int64_t)s * splits + k) * D * D + e];
+  out[(int64_t)s * D * D + e] = acc * scale;
 }
 
 // ---- 3. states entering every scanned frame, per (head, direction) ----
@@ -656,7 +657,7 @@ size_t merge_smem() { return sizeof(MergeSmem<D>); }
 
 template <typename Tin, int D>
 hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w, const BwdOutputs& o,
-                 hipStream_t st) {
+                 bool mfma_softmax, hipStream_t st) {
   const int T = s.T, N = s.N, H = s.H, Nc = s.Nc;
   const int64_t DD = (int64_t)D * D;
   const float tau = 1.0f / sqrtf((float)D);
@@ -682,7 +683,8 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
       using TX = std::remove_cv_t<std::remove_pointer_t<decltype(x)>>;
       using TY = std::remove_cv_t<std::remove_pointer_t<decltype(y)>>;
       xty_partial_kernel<D, TX, TY><<<dim3(nseg, splits), kThreads, 0, st>>>(x, y, segs, H, splits, w.partial);
-      xty_reduce_kernel<D><<<nseg, kThreads, 0, st>>>(w.partial, splits, out, 1.f);
+      xty_reduce_kernel<D><<<dim3(nseg, (D * D + kThreads - 1) / kThreads), kThreads, 0, st>>>(w.partial, splits, out,
+                                                                                               1.f);
     };
     const Tin* q = (const Tin*)in.q;
     const Tin* dout = (const Tin*)w.dout;
@@ -708,12 +710,19 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
                                                          w.nscan, T, H, Nc, w.dmf, w.dbf, w.dalf, w.ds0);
   }
   // 6.-7. softmax branch (dq adds to the merge part, dk/dv/dtext start from zero)
+  if (mfma_softmax) {
+    if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128)) {
+      const hipError_t e = launch_softmax_backward_mfma(s, in, b, w, o, st);
+      if (e != hipSuccess) return e;
+    }
+  } else {
   softmax_dq_kernel<Tin, D><<<dim3((N + 63) / 64, T, H), 64, 0, st>>>(
       (const Tin*)in.q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, w.do_s, w.lse, w.dsum, b.ranges,
       b.nranges, N, H, s.n_text, s.ctx_pad, tau, o.dq);
   softmax_dkv_kernel<Tin, D><<<dim3((max(N, s.n_text) + 63) / 64, T + 1, H), 64, 0, st>>>(
       (const Tin*)in.q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, w.do_s, w.lse, w.dsum,
       w.qranges, w.nqranges, T, N, H, s.n_text, tau, o.dk, o.dv, o.dtext_kv);
+  }
   {
     const size_t sm3 = (size_t)2 * D * (D + 1) * 4;
     (void)hipFuncSetAttribute((const void*)frame_grads_kernel<Tin, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -733,13 +742,14 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
 }  // namespace
 
 hipError_t launch_backward(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
-                           const BwdOutputs& o, hipStream_t st) {
+                           const BwdOutputs& o, bool mfma_softmax, hipStream_t st) {
   const bool bf = s.dtype == VDN_BF16;
+  const bool mf = mfma_softmax && bf && (s.d == 64 || s.d == 128);
   switch (s.d) {
-    case 16: return bf ? run_t<bf16_t, 16>(s, in, b, w, o, st) : run_t<float, 16>(s, in, b, w, o, st);
-    case 32: return bf ? run_t<bf16_t, 32>(s, in, b, w, o, st) : run_t<float, 32>(s, in, b, w, o, st);
-    case 64: return bf ? run_t<bf16_t, 64>(s, in, b, w, o, st) : run_t<float, 64>(s, in, b, w, o, st);
-    default: return bf ? run_t<bf16_t, 128>(s, in, b, w, o, st) : run_t<float, 128>(s, in, b, w, o, st);
+    case 16: return bf ? run_t<bf16_t, 16>(s, in, b, w, o, false, st) : run_t<float, 16>(s, in, b, w, o, false, st);
+    case 32: return bf ? run_t<bf16_t, 32>(s, in, b, w, o, false, st) : run_t<float, 32>(s, in, b, w, o, false, st);
+    case 64: return bf ? run_t<bf16_t, 64>(s, in, b, w, o, mf, st) : run_t<float, 64>(s, in, b, w, o, false, st);
+    default: return bf ? run_t<bf16_t, 128>(s, in, b, w, o, mf, st) : run_t<float, 128>(s, in, b, w, o, false, st);
   }
 }
 

@@ -117,12 +117,21 @@ struct BwdBuffers {
   const int* nqranges;                  // [T+1]
   const Segment *seg_all, *seg_read;    // 1 and (Nc+2)*H segments
   int splits_all, splits_read, nscan;
+  // MFMA softmax backward (bf16 plans, d in {64, 128})
+  uint16_t* dos16;                      // [T*N][H][d] do_s in bf16
+  uint16_t *qt, *dot;                   // [H][d][Lq] transposed q, do_s (bf16); pad columns zero
+  uint16_t *kt, *vp;                    // [H][d][Ls] transposed keys, [H][Ls][d] key-major values
+  int64_t Lq;                           // T*N + 64
+  const int2* kblocks;                  // dK/dV workgroups: (key slot, first key)
+  int nkblocks;
 };
 struct BwdOutputs {
   float *dq, *dk, *dv, *dbeta, *dtext_kv, *dgate_w, *dproj_w, *dalpha;
 };
 hipError_t launch_backward(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
-                           const BwdOutputs& o, hipStream_t st);
+                           const BwdOutputs& o, bool mfma_softmax, hipStream_t st);
+hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
+                                        const BwdOutputs& o, hipStream_t st);
 
 // Number of workgroups of the MFMA softmax launch.
 // with_ctx: including the workgroups of the context query rows.

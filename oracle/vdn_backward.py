@@ -214,3 +214,36 @@ def vdn_backward(inp: dict, dout, T, N, C, anchors=True):
     if alpha is not None:
         grads["alpha"] = dalpha
     return grads
+
+
+def dq_rows(inp: dict, dout, T, N, C, anchors, rows):
+    """dq of the given video rows only (float64 [len(rows), H, d]): the merge, softmax and readout
+    parts of ``vdn_backward``'s dq, evaluated row by row (each needs only its own key set and the
+    two states of its frame), so that it stays cheap at full size."""
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    tk, tv, beta = inp["text_k"], inp["text_v"], inp["beta"]
+    TN, H, d = q.shape
+    tau = 1.0 / math.sqrt(d)
+    rows = np.asarray(rows)
+    out = np.zeros((len(rows), H, d))
+    for h in range(H):
+        _, per_frame = orc.head_states(k, v, beta, tk, tv, h, T, N, C, anchors, alpha=inp.get("alpha"))
+        for j, i in enumerate(rows):
+            t = int(i) // N
+            kf = orc.key_frames(t, T, C, anchors)
+            idx = np.concatenate([np.arange(f * N, (f + 1) * N) for f in kf])
+            keys = np.concatenate([tk[:, h], k[idx, h]]).astype(np.float64)
+            vals = np.concatenate([tv[:, h], v[idx, h]]).astype(np.float64)
+            qi = np.asarray(q[i, h], np.float64)
+            s = tau * (keys @ qi)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o_s = p @ vals
+            zsum = per_frame[t][0] + per_frame[t][1]
+            o_l = zsum @ qi
+            dq_m, do_s, do_l, _, _ = merge_backward(qi[None], o_s[None], o_l[None], inp["gate_w"], inp["proj_w"],
+                                                    np.asarray(dout[i, h], np.float64)[None])
+            dp = vals @ do_s[0]
+            ds = p * (dp - np.sum(p * dp))
+            out[j, h] = dq_m[0] + tau * (ds @ keys) + do_l[0] @ zsum
+    return out

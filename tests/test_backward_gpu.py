@@ -70,3 +70,28 @@ BWD_RAGGED = [
 def test_backward_ragged(case):
     n_text, T, N, C, H, d, dtype, anchors, decay = case
     check_backward(synth.custom(n_text, T, N, C, H, d, dtype, "sigmoid", anchors), seed=4, decay=decay)
+
+
+def test_backward_768p_sampled_dq():
+    """768p in the benchmark's configuration: dq of sampled rows (every frame's first and last
+    token plus two random tokens per frame, all heads) against the row-wise oracle; every other
+    gradient is checked for finiteness here and against the full oracle at the smaller shapes."""
+    w = synth.WORKLOADS["768p"]
+    inp = synth.make_inputs(w, seed=0)
+    dout = np.random.default_rng(7).standard_normal((w.T * w.N, w.H, w.d)).astype(np.float32)
+    dout = torch.from_numpy(dout).to(torch.bfloat16).float().numpy()
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
+    g = plan.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
+                      torch.from_numpy(dout).cuda().to(torch.bfloat16))
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w)
+    got = g["q"][torch.from_numpy(rows).cuda()].cpu().numpy()
+    finite = all(bool(torch.isfinite(x).all()) for x in g.values())
+    del dev, g
+    ref = bwd.dq_rows(inp, dout.astype(np.float64), w.T, w.N, w.C, w.anchors, rows)
+    e = rel_err(got, ref)
+    print(f"768p backward: dq of {len(rows)} sampled rows, err {e:.2e}", flush=True)
+    assert finite
+    assert e <= TOL[w.dtype]
+    plan.close()

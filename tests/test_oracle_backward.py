@@ -100,3 +100,14 @@ def test_backward_mutant_is_caught(mutate, pin):
     mutate(b)
     with pytest.raises(AssertionError):
         pin(b)
+
+
+def test_dq_rows_equals_full_backward():
+    """The row-wise dq (used for full-size sampled checks) equals the full reverse-mode dq."""
+    rng = np.random.default_rng(60)
+    T, N, C, n_text, H, d = 9, 3, 2, 2, 2, 6
+    inp = pins._bwd_inputs(T, N, n_text, H, d, False, 61)
+    dout = rng.standard_normal((T * N, H, d))
+    full = bwd.vdn_backward(inp, dout, T, N, C, True)["q"]
+    rows = np.array([0, 4, 13, T * N - 1])
+    assert np.allclose(bwd.dq_rows(inp, dout, T, N, C, True, rows), full[rows], rtol=1e-10, atol=1e-12)
