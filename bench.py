@@ -224,6 +224,20 @@ def main():
     dec_ms, dec_calls = plan.profile_read()
     decay = {"ms_per_step_median": float(np.median(dec)),
              "vda_ms": (dec_ms["vda_stats"] + dec_ms["vda_scan"]) / dec_calls}
+
+    # the backward pass for a seeded output gradient (context): one call recomputes the forward
+    # quantities it needs, then runs every transposed stage
+    dout = torch.from_numpy(np.random.default_rng(7).standard_normal(out.shape, dtype=np.float32)).to("cuda").to(tdt)
+    backward = lambda: plan.backward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"], dev["proj_w"], dout)
+    backward()
+    torch.cuda.synchronize()
+    n_bwd = max(2, min(args.steps, 5))
+    bwd_ms = timed_steps(backward, n_bwd)
+    bwd_med = float(np.median(bwd_ms))
+    backward_info = {"ms_per_call_median": bwd_med, "calls": n_bwd,
+                     "train_step_tokens_per_s": tokens / ((float(np.median(per_step)) + bwd_med) * 1e-3),
+                     "softmax_backward_algorithmic_tflop": 3.5 * flops / 1e12}
+    del dout
     plan.close()
 
     overlapped = None
@@ -269,6 +283,7 @@ def main():
     }
     decay["vda_frac_hbm"] = (vb + 4 * w.T * w.H * w.d) / (decay["vda_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
     result["decay_gate"] = decay
+    result["backward"] = backward_info
     if overlapped is not None:
         result["overlapped_branches"] = overlapped
     del dev, beta, text_kv, alpha, out, ref

@@ -59,30 +59,41 @@ __device__ __forceinline__ void mm_block(FA a, FB b, float (&c)[D / 16][D / 16],
 // kRows/16) x 16 (column groups of D/16).
 constexpr int kRows = 64;
 
+constexpr int kWChunk = 16;            // rows of the right-hand matrix staged in LDS at a time
+
 template <int D>
 struct MergeSmem {
   float q[kRows][D + 1], dout[kRows][D + 1], t1[kRows][D + 1], t2[kRows][D + 1];
+  float w[kWChunk][D];
 };
 
-// out[r][j] = sum_k x[r][k] w(k, j) for the thread's rows and columns
+// out[r][j] = sum_k x[r][k] w(k, j) for the thread's rows and columns; w is staged through LDS in
+// chunks of kWChunk rows (every thread of the block must call it)
 template <int D, class FW>
-__device__ __forceinline__ void rows_mm(const float (*x)[D + 1], FW w, float (&out)[kRows / 16][D / 16], int ty,
-                                        int tx) {
+__device__ __forceinline__ void rows_mm(const float (*x)[D + 1], FW w, float (*wst)[D], float (&out)[kRows / 16][D / 16],
+                                        int ty, int tx) {
   constexpr int RR = kRows / 16, RC = D / 16;
+  const int tid = ty * 16 + tx;
 #pragma unroll
   for (int i = 0; i < RR; ++i)
 #pragma unroll
     for (int j = 0; j < RC; ++j) out[i][j] = 0.f;
-  for (int k = 0; k < D; ++k) {
-    float xv[RR], wv[RC];
+  for (int k0 = 0; k0 < D; k0 += kWChunk) {
+    __syncthreads();                                  // the previous chunk has been consumed
+    for (int e = tid; e < kWChunk * D; e += kThreads) wst[e / D][e % D] = w(k0 + e / D, e % D);
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kWChunk; ++kk) {
+      float xv[RR], wv[RC];
 #pragma unroll
-    for (int i = 0; i < RR; ++i) xv[i] = x[ty * RR + i][k];
+      for (int i = 0; i < RR; ++i) xv[i] = x[ty * RR + i][k0 + kk];
 #pragma unroll
-    for (int j = 0; j < RC; ++j) wv[j] = w(k, tx * RC + j);
+      for (int j = 0; j < RC; ++j) wv[j] = wst[kk][tx * RC + j];
 #pragma unroll
-    for (int i = 0; i < RR; ++i)
+      for (int i = 0; i < RR; ++i)
 #pragma unroll
-      for (int j = 0; j < RC; ++j) out[i][j] = fmaf(xv[i], wv[j], out[i][j]);
+        for (int j = 0; j < RC; ++j) out[i][j] = fmaf(xv[i], wv[j], out[i][j]);
+    }
   }
 }
 
@@ -116,11 +127,11 @@ __global__ __launch_bounds__(kThreads) void merge_bwd_kernel(
   auto wmat_t = [&](const Tin* w) { return [w](int k, int j) { return to_f32(w[(int64_t)j * D + k]); }; };
   // o_l = S q  (row form: q S^T),  S = S_fwd + S_rev
   float ol[RR][RC], zs[RR][RC], zl[RR][RC], dxs[RR][RC], dxl[RR][RC];
-  rows_mm<D>(S.q, [&](int k, int j) { return sf[(int64_t)j * D + k] + sr[(int64_t)j * D + k]; }, ol, ty, tx);
-  rows_mm<D>(S.q, wmat(gate_w), zs, ty, tx);
-  rows_mm<D>(S.q, wmat(gate_w + DD), zl, ty, tx);
-  rows_mm<D>(S.dout, wmat_t(proj_w), dxs, ty, tx);
-  rows_mm<D>(S.dout, wmat_t(proj_w + DD), dxl, ty, tx);
+  rows_mm<D>(S.q, [&](int k, int j) { return sf[(int64_t)j * D + k] + sr[(int64_t)j * D + k]; }, S.w, ol, ty, tx);
+  rows_mm<D>(S.q, wmat(gate_w), S.w, zs, ty, tx);
+  rows_mm<D>(S.q, wmat(gate_w + DD), S.w, zl, ty, tx);
+  rows_mm<D>(S.dout, wmat_t(proj_w), S.w, dxs, ty, tx);
+  rows_mm<D>(S.dout, wmat_t(proj_w + DD), S.w, dxl, ty, tx);
   // per-row RMS of o_l (row sums across the 16 column-group threads of the row group)
   float* red = &S.t1[0][0];                     // scratch [kRows][16]
   float* red2 = &S.t2[0][0];
@@ -217,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void merge_bwd_kernel(
   __syncthreads();
   // dq = dz_s Wg0^T + dz_l Wg1^T + do_l S
   float a1[RR][RC], a2[RR][RC], a3[RR][RC];
-  rows_mm<D>(S.t2, wmat_t(gate_w), a1, ty, tx);
-  rows_mm<D>(S.dout, wmat_t(gate_w + DD), a2, ty, tx);
-  rows_mm<D>(S.t1, [&](int k, int j) { return sf[(int64_t)k * D + j] + sr[(int64_t)k * D + j]; }, a3, ty, tx);
+  rows_mm<D>(S.t2, wmat_t(gate_w), S.w, a1, ty, tx);
+  rows_mm<D>(S.dout, wmat_t(gate_w + DD), S.w, a2, ty, tx);
+  rows_mm<D>(S.t1, [&](int k, int j) { return sf[(int64_t)k * D + j] + sr[(int64_t)k * D + j]; }, S.w, a3, ty, tx);
 #pragma unroll
   for (int i = 0; i < RR; ++i) {
     const int r = ty * RR + i;
