@@ -1,0 +1,148 @@
+"""CPU oracle of the FP8 variant of the VDN softmax branch.
+
+TEST INFRASTRUCTURE ONLY (same rules as ``vdn_oracle``: only the test suite, the smoke check and
+the benchmark's CPU-baseline leg may import it; it shares nothing with the GPU path).
+
+The pages run the layer with FP8 arithmetic in production ([VDN] "Adapting the Pretrained H3
+backbone": optimized kernels plus FP8 cut the per-block latency further) but do not say which
+roundings the FP8 path makes.  This module is the definition used here, written so that every
+rounding is a stated, deterministic step; the window, anchors, global keys and the one softmax per
+query are those of the exact branch ([VDN] "Local Softmax and Long-Range Linear Memory";
+``vdn_oracle.softmax_branch``).
+
+Number format: OCP FP8 E4M3 (one sign bit, four exponent bits with bias 7, three mantissa bits,
+no infinities; largest finite value 448, subnormal spacing 2^-9), rounding to nearest with ties to
+even; values beyond 448 saturate (the scales below keep every operand inside the range).
+
+Definition, per head h, for a video query row q with key set J (global keys, window, anchors):
+
+* power-of-two scales: scale(m) = 2^(8 - e) for a largest magnitude m = f 2^e, f in [0.5, 1)
+  (scale(0) = 1), so the scaled values stay below 256.  s_k = scale(max |k|) and s_v =
+  scale(max |v|) over every key and value of the head (global and video), s_q = scale(max |q|)
+  per query row;
+* K8 = e4m3(s_k k), V8 = e4m3(s_v v), Q8 = e4m3(s_q q);
+* scores x_j = <Q8, K8_j> / (s_q s_k) (exact);
+* exponent offset: with c = log2(e) / sqrt(d) and the bound b = c |q| kmax (kmax the largest key
+  norm of the head, |q| the query's norm), m = b when b <= 4, else m = c max_{j in J} x_j.  (Any
+  offset gives the exact softmax; after rounding it matters, so it is part of the definition.
+  With b <= 4 every row's largest term 2^(8 + c x - m) is at least 1.)
+* P8_j = e4m3(2^(8 + c x_j - m));
+* o = sum_j P8_j V8_j / (s_v sum_j P8_j).
+
+The normaliser sums the same rounded weights that multiply the values, so o is a convex
+combination of the dequantised values.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import vdn_oracle as orc
+
+E4M3_MAX = 448.0
+OFFSET_BOUND_LIMIT = 4.0      # log2 units: larger bounds use the row maximum as the offset
+P_SHIFT = 8.0                 # the weights are rounded as 2^8 p
+
+
+def e4m3(x) -> np.ndarray:
+    """Round to the nearest OCP E4M3 value (ties to even), saturating at +-448; float64 result."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                        # a = f 2^ex with f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                 # binade of a; below 2^-6 the subnormal spacing
+    step = np.ldexp(1.0, (e - 3).astype(np.int64))  # three mantissa bits
+    r = np.round(a / step) * step              # numpy rounds halves to even
+    r = np.minimum(r, E4M3_MAX)
+    return np.where(np.isnan(x), np.nan, np.copysign(r, x))
+
+
+def pow2_scale(max_abs: float) -> float:
+    """2^(8 - e) for max_abs = f 2^e, f in [0.5, 1); 1 for zero."""
+    if max_abs == 0.0:
+        return 1.0
+    _, e = math.frexp(float(max_abs))
+    return math.ldexp(1.0, 8 - e)
+
+
+def head_scales(keys_all: np.ndarray, vals_all: np.ndarray):
+    """(s_k, s_v, kmax) of one head from all of its keys and values [n, d]."""
+    keys_all = np.asarray(keys_all, np.float64)
+    vals_all = np.asarray(vals_all, np.float64)
+    s_k = pow2_scale(np.abs(keys_all).max()) if keys_all.size else 1.0
+    s_v = pow2_scale(np.abs(vals_all).max()) if vals_all.size else 1.0
+    kmax = float(np.sqrt((keys_all ** 2).sum(axis=1)).max()) if keys_all.size else 0.0
+    return s_k, s_v, kmax
+
+
+def softmax_rows_fp8(qr, keys, vals, s_k, s_v, kmax) -> np.ndarray:
+    """FP8 softmax attention of query rows ``qr`` [m, d] over ``keys``, ``vals`` [n, d] with the
+    head's scales; float64 result."""
+    qr = np.asarray(qr, np.float64)
+    d = qr.shape[-1]
+    c = math.log2(math.e) / math.sqrt(d)
+    k8 = e4m3(s_k * np.asarray(keys, np.float64))
+    v8 = e4m3(s_v * np.asarray(vals, np.float64))
+    out = np.zeros(qr.shape)
+    for i, q in enumerate(qr):
+        s_q = pow2_scale(np.abs(q).max())
+        x = (k8 @ e4m3(s_q * q)) / (s_q * s_k)
+        b = c * math.sqrt(float(q @ q)) * kmax
+        m = b if b <= OFFSET_BOUND_LIMIT else c * x.max()
+        p8 = e4m3(np.exp2(P_SHIFT + c * x - m))
+        out[i] = (p8 @ v8) / (s_v * p8.sum())
+    return out
+
+
+def softmax_branch_fp8(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None):
+    """o_s of the FP8 variant for every video token (``rows=None``) or the given token indices."""
+    if audio_k is not None:
+        text_k = np.concatenate([text_k, audio_k], axis=0)
+        text_v = np.concatenate([text_v, audio_v], axis=0)
+    TN, H, d = q.shape
+    assert TN == T * N
+    rows = np.arange(TN) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows), H, d))
+    scales = [head_scales(np.concatenate([text_k[:, h], k[:, h]]), np.concatenate([text_v[:, h], v[:, h]]))
+              for h in range(H)]
+    frames_of_rows = rows // N
+    for t in np.unique(frames_of_rows):
+        sel = np.nonzero(frames_of_rows == t)[0]
+        kf = orc.key_frames(int(t), T, C, anchors)
+        idx = np.concatenate([np.arange(f * N, (f + 1) * N) for f in kf])
+        for h in range(H):
+            keys = np.concatenate([text_k[:, h], k[idx, h]], axis=0)
+            vals = np.concatenate([text_v[:, h], v[idx, h]], axis=0)
+            out[sel, h] = softmax_rows_fp8(q[rows[sel], h], keys, vals, *scales[h])
+    return out
+
+
+def context_rows_fp8(inp: dict, T, N) -> np.ndarray:
+    """Text and audio query rows of the FP8 variant: every key of the sequence, one softmax."""
+    cq = inp["ctx_q"]
+    H = cq.shape[1]
+    parts_k = [inp["text_k"]] + ([inp["audio_k"]] if inp.get("audio_k") is not None else []) + [inp["k"]]
+    parts_v = [inp["text_v"]] + ([inp["audio_v"]] if inp.get("audio_v") is not None else []) + [inp["v"]]
+    assert inp["k"].shape[0] == T * N
+    out = np.zeros(cq.shape)
+    for h in range(H):
+        keys = np.concatenate([p[:, h] for p in parts_k], axis=0)
+        vals = np.concatenate([p[:, h] for p in parts_v], axis=0)
+        out[:, h] = softmax_rows_fp8(cq[:, h], keys, vals, *head_scales(keys, vals))
+    return out
+
+
+def vdn_forward_fp8(inp: dict, T, N, C, anchors=True, rows=None, with_intermediates=False):
+    """The layer with the FP8 softmax branch; the linear branch and the merge are the exact ones
+    of ``vdn_oracle`` (float64)."""
+    q = inp["q"]
+    rows_arr = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    o_s = softmax_branch_fp8(q, inp["k"], inp["v"], inp["text_k"], inp["text_v"], T, N, C, anchors, rows_arr,
+                             inp.get("audio_k"), inp.get("audio_v"))
+    o_l = orc.linear_branch(q, inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"], T, N, C, anchors,
+                            rows_arr, alpha=inp.get("alpha"))
+    out = orc.merge(q[rows_arr], o_s, o_l, inp["gate_w"], inp["proj_w"])
+    if with_intermediates:
+        return out, {"o_s": o_s, "o_l": o_l}
+    return out

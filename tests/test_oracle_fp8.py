@@ -1,0 +1,264 @@
+"""Pins of the FP8 softmax oracle (``oracle/fp8_softmax.py``), all on the CPU.
+
+* the E4M3 rounding against torch's float8_e4m3fn conversion (a library routine) on random values
+  over the whole range, on every representable value and on every midpoint between neighbours
+  (ties to even);
+* two hand-derived cases of the definition (one on the bound offset, one on the row-maximum offset
+  with a weight in the subnormal range), whose rounded weights are worked out in the comments;
+* uniform attention: identical keys give every visible key the same weight, so a frame-indicator
+  value reveals each query's key set (text, window, anchors), exactly;
+* closeness to the exact softmax within the error the rounding allows;
+* planted mistakes, each caught by one of the pins above.
+"""
+
+import importlib.util
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import pins
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fp8_softmax.py")
+
+
+def fresh():
+    spec = importlib.util.spec_from_file_location("fp8_softmax_mutant", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _torch_e4m3(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_e4m3_library(f8, seed=0):
+    """Rounding agrees with torch's conversion wherever the result is finite (|x| < 464)."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-5, 2.6, 200000)).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    vals = np.unique(codes[np.isfinite(codes)])
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)   # exact in float32
+    for arr in (x, vals.astype(np.float32), mids, -mids):
+        assert np.array_equal(f8.e4m3(arr), _torch_e4m3(arr))
+
+
+def _two_key_case():
+    d = 16
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    keys = np.zeros((2, d))
+    keys[0, 0] = 0.5
+    keys[1, 0] = -1.0
+    vals = np.zeros((2, d))
+    vals[0, 0] = 1.0
+    vals[1, 1] = 1.0
+    return q, keys, vals
+
+
+def pin_hand_bound_offset(f8):
+    """d = 16, c = log2(e)/4 = 0.3607; q = e1, k1 = e1/2, k2 = -e1, v1 = e1, v2 = e2.
+    Scales: s_q = s_k = 2^(8-1) = 128 (max |.| = 1 = 0.5 * 2^1), s_v = 128; all operands exact, so
+    x = (0.5, -1).  kmax = 1, bound b = c <= 4 is the offset.  Weights: 2^(8 - c/2) = 225.92 lies
+    in [128, 256) where E4M3 steps by 16 -> 224; 2^(8 - 2c) = 155.27 -> 160.  o = (224, 160) / 384
+    in the first two channels."""
+    q, keys, vals = _two_key_case()
+    o = f8.softmax_rows_fp8(q, keys, vals, *f8.head_scales(keys, vals))[0]
+    expect = np.zeros(16)
+    expect[0], expect[1] = 224 / 384, 160 / 384
+    assert np.allclose(o, expect, rtol=0, atol=1e-12), o[:2]
+
+
+def pin_hand_rowmax_offset(f8):
+    """As above with q = 20 e1: s_q = 2^(8-5) = 8, q8 = 160 exact, x = (10, -20); the bound
+    c * 20 = 7.21 > 4, so the offset is c * max x = 10 c.  Weights: 2^8 = 256 (exact) and
+    2^(8 - 30 c) = 2^-2.82 = 0.1416, in [2^-3, 2^-2) where E4M3 steps by 2^-6 -> 9/64.
+    o = (256, 9/64) / (256 + 9/64)."""
+    q, keys, vals = _two_key_case()
+    q = q * 20.0
+    o = f8.softmax_rows_fp8(q, keys, vals, *f8.head_scales(keys, vals))[0]
+    tot = 256 + 9 / 64
+    assert math.isclose(o[0], 256 / tot, rel_tol=0, abs_tol=1e-12), o[0]
+    assert math.isclose(o[1], (9 / 64) / tot, rel_tol=0, abs_tol=1e-15), o[1]
+
+
+def pin_uniform_visibility_fp8(f8):
+    """Identical keys: every visible key gets the same rounded weight, so with one-hot frame values
+    (exact in E4M3) o is each frame's share of the visible keys, exactly; the visible sets are the
+    hand-derived golden frame sets of the 16-frame, chunk-2 workload."""
+    T, N, C, H, d, n_text = 16, 3, 2, 1, 20, 2
+    q = np.zeros((T * N, H, d))
+    q[..., 0] = 1
+    k = np.zeros_like(q)
+    k[..., 0] = 1
+    v = np.zeros_like(q)
+    for f in range(T):
+        v[f * N:(f + 1) * N, 0, f] = 1.0
+    tk = np.zeros((n_text, H, d))
+    tk[..., 0] = 1
+    tv = np.zeros((n_text, H, d))
+    tv[..., 16] = 1.0
+    o = f8.softmax_branch_fp8(q, k, v, tk, tv, T, N, C, True)
+    gold = pins.golden_frame_sets()
+    for t in range(T):
+        w, anc, _, _ = gold[t]
+        vis = sorted(w + anc)
+        nkeys = n_text + N * len(vis)
+        expect = np.zeros(d)
+        expect[vis] = N / nkeys
+        expect[16] = n_text / nkeys
+        for n in range(N):
+            assert np.allclose(o[t * N + n, 0], expect, rtol=0, atol=1e-12), t
+
+
+def pin_close_to_exact(f8, seed=3):
+    """Against the exact softmax (float64) on unit-norm q, k and N(0,1) v: each E4M3 rounding
+    moves a weight or a value by at most 2^-4 of itself (RMS 2^-4/sqrt(3) = 3.6 %), and o averages
+    those moves, so the RMS error stays near 5 % of RMS(o); allowed: 6 % RMS, 30 % at the worst
+    element."""
+    rng = np.random.default_rng(seed)
+    for d, n, qscale in ((128, 3000, 1.0), (64, 2000, 8.0)):
+        q = pins._unit(rng.standard_normal((48, d))) * qscale
+        k = pins._unit(rng.standard_normal((n, d)))
+        v = rng.standard_normal((n, d))
+        s = (q @ k.T) / math.sqrt(d)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        exact = (p @ v) / p.sum(axis=1, keepdims=True)
+        o = f8.softmax_rows_fp8(q, k, v, *f8.head_scales(k, v))
+        rms = np.sqrt((exact ** 2).mean())
+        err = o - exact
+        assert np.sqrt((err ** 2).mean()) <= 0.06 * rms
+        assert np.abs(err).max() <= 0.30 * rms
+
+
+PINS = [pin_e4m3_library, pin_hand_bound_offset, pin_hand_rowmax_offset, pin_uniform_visibility_fp8,
+        pin_close_to_exact]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(fresh())
+
+
+# ---- planted mistakes ----
+
+def m_truncating_round(f8):
+    def e4m3(x):
+        x = np.asarray(x, np.float64)
+        a = np.abs(x)
+        _, ex = np.frexp(a)
+        step = np.ldexp(1.0, (np.maximum(ex - 1, -6) - 3).astype(np.int64))
+        return np.copysign(np.minimum(np.floor(a / step) * step, 448.0), x)
+    f8.e4m3 = e4m3
+
+
+def m_ties_away(f8):
+    def e4m3(x):
+        x = np.asarray(x, np.float64)
+        a = np.abs(x)
+        _, ex = np.frexp(a)
+        step = np.ldexp(1.0, (np.maximum(ex - 1, -6) - 3).astype(np.int64))
+        return np.copysign(np.minimum(np.floor(a / step + 0.5) * step, 448.0), x)
+    f8.e4m3 = e4m3
+
+
+def m_no_subnormals(f8):
+    orig = f8.e4m3
+
+    def e4m3(x):
+        r = orig(x)
+        return np.where(np.abs(r) < 2.0 ** -6, 0.0, r)
+    f8.e4m3 = e4m3
+
+
+def m_unrounded_denominator(f8):
+    def softmax_rows_fp8(qr, keys, vals, s_k, s_v, kmax):
+        qr = np.asarray(qr, np.float64)
+        c = math.log2(math.e) / math.sqrt(qr.shape[-1])
+        k8, v8 = f8.e4m3(s_k * keys), f8.e4m3(s_v * vals)
+        out = np.zeros(qr.shape)
+        for i, q in enumerate(qr):
+            s_q = f8.pow2_scale(np.abs(q).max())
+            x = (k8 @ f8.e4m3(s_q * q)) / (s_q * s_k)
+            b = c * math.sqrt(float(q @ q)) * kmax
+            m = b if b <= 4 else c * x.max()
+            p = np.exp2(8 + c * x - m)
+            out[i] = (f8.e4m3(p) @ v8) / (s_v * p.sum())
+        return out
+    f8.softmax_rows_fp8 = softmax_rows_fp8
+
+
+def m_always_rowmax(f8):
+    f8.OFFSET_BOUND_LIMIT = -1.0
+
+
+def m_no_shift(f8):
+    f8.P_SHIFT = 0.0
+
+
+def m_value_scale_kept(f8):
+    orig = f8.softmax_rows_fp8
+
+    def softmax_rows_fp8(qr, keys, vals, s_k, s_v, kmax):
+        return orig(qr, keys, vals, s_k, s_v, kmax) * s_v
+    f8.softmax_rows_fp8 = softmax_rows_fp8
+
+
+def m_query_scale_dropped(f8):
+    orig = f8.pow2_scale
+
+    def softmax_rows_fp8(qr, keys, vals, s_k, s_v, kmax):
+        qr = np.asarray(qr, np.float64)
+        c = math.log2(math.e) / math.sqrt(qr.shape[-1])
+        k8, v8 = f8.e4m3(s_k * keys), f8.e4m3(s_v * vals)
+        out = np.zeros(qr.shape)
+        for i, q in enumerate(qr):
+            s_q = orig(np.abs(q).max())
+            x = (k8 @ f8.e4m3(s_q * q)) / s_k                 # wrong: s_q not divided out
+            b = c * math.sqrt(float(q @ q)) * kmax
+            m = b if b <= 4 else c * x.max()
+            p8 = f8.e4m3(np.exp2(8 + c * x - m))
+            out[i] = (p8 @ v8) / (s_v * p8.sum())
+        return out
+    f8.softmax_rows_fp8 = softmax_rows_fp8
+
+
+def m_window_without_anchors(f8):
+    orc = f8.orc
+    orig = orc.key_frames
+
+    class Shim:
+        def __getattr__(self, name):
+            return getattr(orc, name)
+
+        @staticmethod
+        def key_frames(t, T, C, anchors):
+            return sorted(orc.frame_sets(t, T, C, anchors)[0])
+    f8.orc = Shim()
+    assert orig is orc.key_frames
+
+
+MUTANTS = [
+    (m_truncating_round, pin_e4m3_library),
+    (m_ties_away, pin_e4m3_library),
+    (m_no_subnormals, pin_e4m3_library),
+    (m_unrounded_denominator, pin_hand_bound_offset),
+    (m_always_rowmax, pin_hand_bound_offset),
+    (m_no_shift, pin_hand_rowmax_offset),
+    (m_value_scale_kept, pin_hand_bound_offset),
+    (m_query_scale_dropped, pin_hand_bound_offset),
+    (m_window_without_anchors, pin_uniform_visibility_fp8),
+]
+
+
+@pytest.mark.parametrize("mutate,pin", MUTANTS, ids=[m.__name__ for m, _ in MUTANTS])
+def test_mutant_is_caught(mutate, pin):
+    f8 = fresh()
+    pin(f8)
+    mutate(f8)
+    with pytest.raises(AssertionError):
+        pin(f8)
