@@ -95,8 +95,21 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
  * stream); VDN_FLAG_OVERLAP instead runs the linear branch on a side stream of the plan, forked
  * from and joined back into the caller's stream, concurrently with the softmax branch (on MI355X
  * this is slower at the 768p shape: the two branches compete for the compute units).  SERIAL and
- * OVERLAP together are an argument error.  Results are identical in every case. */
-enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4 };
+ * OVERLAP together are an argument error.  Results are identical in every case.
+ *
+ * VDN_FLAG_FP8_SOFTMAX runs the softmax branch of the video rows and of the context rows in FP8
+ * (OCP E4M3) on the matrix cores.  "Video DeltaNet: Near-Lossless Hybrid Attention for Video
+ * Models", section "Adapting the Pretrained H3 backbone", reports the production layer with FP8
+ * arithmetic but not its roundings; the ones made here are: power-of-two scales 2^(8 - e) (e the
+ * binary exponent of the largest magnitude) for the keys and for the values of each head and for
+ * each query row; operands rounded to E4M3 (nearest, ties to even); scores from the rounded
+ * operands in fp32; weights P8 = e4m3(2^(8 + c x - m)) with c = log2(e)/sqrt(d) and the offset
+ * m = c |q| max|k| when that is <= 4, else the row's exact maximum c max x; o = sum P8 V8 /
+ * (s_v sum P8).  Inputs and outputs are unchanged (bf16); the linear branch and the merge are the
+ * bf16 plan's.  Requires VDN_BF16, d = 128 and N a multiple of 16 (else VDN_ERR_UNSUPPORTED);
+ * with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward rejects such plans
+ * (VDN_ERR_UNSUPPORTED). */
+enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4, VDN_FLAG_FP8_SOFTMAX = 8 };
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,
                               vdn_dtype dtype, unsigned flags, vdn_plan **plan_out);
 
@@ -188,8 +201,13 @@ int vdn_scan_frames(int T, int C, int anchors, int t, int dir, int *frames, int 
  *   VDN_BUF_MINV   M_f = (I + A_f)^-1: [T+1][H][d][d] float32, slot 0 for the text (beta/2),
  *                  slot 1+f for frame f (boundary frames' slots are not written when anchors on)
  *   VDN_BUF_BW     B_f = sum_u beta_u v_u k_u^T: [T+1][H][d][d] float32, same slots as VDN_BUF_MINV
+ *   VDN_BUF_K8     FP8 plans: keys e4m3(s_k k) [H][Ls8][d] bytes, Ls8 = round_up(n_ctx, 64) + T*N + 128,
+ *                  key j of a head at row j (global keys, then video token j - round_up(n_ctx, 64))
+ *   VDN_BUF_V8     FP8 plans: values e4m3(s_v v) transposed, [H][d][Ls8] bytes
+ *   VDN_BUF_SCALES8 FP8 plans: [H][2] float32 (s_k, s_v)
  */
-enum { VDN_BUF_OS = 0, VDN_BUF_STATES = 1, VDN_BUF_MINV = 2, VDN_BUF_BW = 3 };
+enum { VDN_BUF_OS = 0, VDN_BUF_STATES = 1, VDN_BUF_MINV = 2, VDN_BUF_BW = 3, VDN_BUF_K8 = 4, VDN_BUF_V8 = 5,
+       VDN_BUF_SCALES8 = 6 };
 vdn_status vdn_debug_buffer_bytes(const vdn_plan *plan, int which, size_t *bytes);
 vdn_status vdn_debug_copy(const vdn_plan *plan, int which, void *dst, size_t bytes, void *stream);
 
@@ -202,7 +220,8 @@ enum { VDN_STAGE_SOFTMAX = 0, VDN_STAGE_PREP = 1, VDN_STAGE_VDA_STATS = 2, VDN_S
 vdn_status vdn_profile_enable(vdn_plan *plan, int max_calls);
 vdn_status vdn_profile_read(vdn_plan *plan, float *ms, int n_stages, int *calls);
 
-/* Which kernel family a plan selected for each stage (0 = generic SIMT kernel, 1 = MFMA kernel). */
+/* Which kernel family a plan selected for each stage (0 = generic SIMT kernel, 1 = MFMA kernel,
+ * 2 = FP8 MFMA kernel: the softmax stage of VDN_FLAG_FP8_SOFTMAX plans). */
 vdn_status vdn_plan_kernel_kind(const vdn_plan *plan, int stage, int *kind);
 
 /* On-box reference rates for rooflines (measurement helpers; synchronous, on the current device's

@@ -22,6 +22,8 @@ SOURCES = [
     "prep_kv.hip",
     "softmax_simt.hip",
     "softmax_mfma.hip",
+    "prep_fp8.hip",
+    "softmax_fp8.hip",
     "vda.hip",
     "vda_stats_mfma.hip",
     "vda_invert_mfma.hip",

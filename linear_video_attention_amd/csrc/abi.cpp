@@ -45,9 +45,14 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.qq = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.qq) : nullptr;
   b.states = reinterpret_cast<float*>(ws + p->lay.states);
   b.wt = p->kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.wt) : nullptr;
+  const bool packed = p->kinds.softmax_mfma || p->kinds.softmax_fp8;
   b.kmax_part = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax_part) : nullptr;
-  b.kmax = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax) : nullptr;
-  b.flags = p->kinds.softmax_mfma ? reinterpret_cast<int*>(ws + p->lay.flags) : nullptr;
+  b.kmax = packed ? reinterpret_cast<float*>(ws + p->lay.kmax) : nullptr;
+  b.flags = packed ? reinterpret_cast<int*>(ws + p->lay.flags) : nullptr;
+  b.k8 = p->kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + p->lay.k8) : nullptr;
+  b.v8 = p->kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + p->lay.v8) : nullptr;
+  b.part8 = p->kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + p->lay.part8) : nullptr;
+  b.scale8 = p->kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + p->lay.scale8) : nullptr;
   b.ranges = reinterpret_cast<const int*>(ws + p->lay.ranges);
   b.nranges = b.ranges + (size_t)(p->s.T + 1) * 2 * vdn::kMaxRanges;
   return b;
@@ -78,6 +83,7 @@ vdn::Shape make_shape(int T, int N, int C, int n_text, int n_audio, int H, int d
   s.ctx_pad = (int)vdn::round_up(s.n_ctx, vdn::kTextPad);
   s.Lk = (int64_t)s.ctx_pad + (int64_t)T * N;
   s.Ls = s.Lk + 64;
+  s.Ls8 = s.Lk + 128;
   return s;
 }
 
@@ -133,14 +139,25 @@ vdn_status vdn_plan_create_joint(int T, int N, int C, int n_text, int n_audio, i
   const int64_t tokens = (int64_t)T * N;
   if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || n_ctx * H * d > (int64_t(1) << 40))
     return VDN_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
+  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP | VDN_FLAG_FP8_SOFTMAX))
+    return VDN_ERR_INVALID_ARG;
   if ((flags & VDN_FLAG_SERIAL) && (flags & VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
+  const bool fp8 = (flags & VDN_FLAG_FP8_SOFTMAX) != 0;
+  if (fp8 && (flags & VDN_FLAG_GENERIC_KERNELS)) return VDN_ERR_INVALID_ARG;
+  // FP8 softmax: bf16 inputs, d = 128, key tiles 16-key aligned, 32-bit lane offsets into V8
+  if (fp8 && (dtype != VDN_BF16 || d != 128 || N % 16 != 0 ||
+              (int64_t)d * (vdn::round_up(n_ctx, vdn::kTextPad) + tokens + 128) >= (int64_t(1) << 31)))
+    return VDN_ERR_UNSUPPORTED;
   if (vdn::round_up(n_ctx, vdn::kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
 
   vdn_plan* p = new (std::nothrow) vdn_plan();
   if (!p) return VDN_ERR_OUT_OF_MEMORY;
   p->s = make_shape(T, N, C, n_text, n_audio, H, d, anchors, dtype);
   p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
+  if (fp8) {
+    p->kinds.softmax_mfma = false;
+    p->kinds.softmax_fp8 = true;
+  }
   p->overlap = (flags & VDN_FLAG_OVERLAP) != 0;
   p->lay = vdn::make_layout(p->s, p->kinds);
   if (hipGetDevice(&p->device) != hipSuccess) { free_plan(p); return VDN_ERR_HIP; }
@@ -162,6 +179,9 @@ vdn_status vdn_plan_create_joint(int T, int N, int C, int n_text, int n_audio, i
   if ((p->kinds.softmax_mfma &&
        (hipMemset(p->ws + p->lay.kp, 0, (size_t)p->s.H * p->s.Ls * d * 2) != hipSuccess ||
         hipMemset(p->ws + p->lay.vt, 0, (size_t)p->s.H * p->s.Ls * d * 2) != hipSuccess)) ||
+      (p->kinds.softmax_fp8 &&
+       (hipMemset(p->ws + p->lay.k8, 0, (size_t)p->s.H * p->s.Ls8 * d) != hipSuccess ||
+        hipMemset(p->ws + p->lay.v8, 0, (size_t)p->s.H * p->s.Ls8 * d) != hipSuccess)) ||
       hipMemcpy(p->ws + p->lay.ranges, tab.data(), tab.size() * sizeof(int), hipMemcpyHostToDevice) != hipSuccess ||
       (p->overlap && (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess ||
                       hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming) != hipSuccess ||
@@ -180,8 +200,8 @@ size_t vdn_plan_workspace_bytes(const vdn_plan* plan) { return plan ? plan->lay.
 vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
   if (!plan || !kind) return VDN_ERR_INVALID_ARG;
   switch (stage) {
-    case VDN_STAGE_SOFTMAX: *kind = plan->kinds.softmax_mfma; break;
-    case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma || plan->kinds.epilogue_mfma; break;
+    case VDN_STAGE_SOFTMAX: *kind = plan->kinds.softmax_fp8 ? 2 : plan->kinds.softmax_mfma; break;
+    case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma || plan->kinds.softmax_fp8 || plan->kinds.epilogue_mfma; break;
     case VDN_STAGE_VDA_STATS: *kind = plan->kinds.stats_mfma; break;
     case VDN_STAGE_VDA_SCAN: *kind = plan->kinds.scan_mfma; break;
     case VDN_STAGE_EPILOGUE: *kind = plan->kinds.epilogue_mfma; break;
@@ -247,10 +267,12 @@ vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, cons
   // softmax branch on the caller's stream
   mark(VDN_STAGE_PREP, 0, main);
   if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
+  if (plan->kinds.softmax_fp8) VDN_TRY(vdn::launch_prep_fp8(s, in, b, main));
   if (plan->kinds.epilogue_mfma) VDN_TRY(vdn::launch_prep_weights(s, in, b, main));
   mark(VDN_STAGE_PREP, 1, main);
   mark(VDN_STAGE_SOFTMAX, 0, main);
-  if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
+  if (plan->kinds.softmax_fp8) VDN_TRY(vdn::launch_softmax_fp8(s, in, b, main));
+  else if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
   else VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
   mark(VDN_STAGE_SOFTMAX, 1, main);
   // join, then readout + gates + projections
@@ -453,7 +475,7 @@ vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !dout || !dq || !dk || !dv || !dbeta || !dgate_w ||
       !dproj_w)
     return VDN_ERR_INVALID_ARG;
-  if (plan->s.n_audio > 0) return VDN_ERR_UNSUPPORTED;
+  if (plan->s.n_audio > 0 || plan->kinds.softmax_fp8) return VDN_ERR_UNSUPPORTED;
   if (plan->s.n_text > 0 && (!text_kv || !dtext_kv)) return VDN_ERR_INVALID_ARG;
   if (dalpha && !alpha) return VDN_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, dout, dq, dk, dv, dbeta, dgate_w, dproj_w};
@@ -503,6 +525,15 @@ vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes
     case VDN_BUF_STATES: *bytes = (size_t)2 * (s.Nc + 1) * s.H * dd * 4; break;
     case VDN_BUF_MINV: *bytes = (size_t)(s.T + 1) * s.H * dd * 4; break;
     case VDN_BUF_BW: *bytes = (size_t)(s.T + 1) * s.H * dd * 4; break;
+    case VDN_BUF_K8:
+    case VDN_BUF_V8:
+      if (!plan->kinds.softmax_fp8) return VDN_ERR_INVALID_ARG;
+      *bytes = (size_t)s.H * s.Ls8 * s.d;
+      break;
+    case VDN_BUF_SCALES8:
+      if (!plan->kinds.softmax_fp8) return VDN_ERR_INVALID_ARG;
+      *bytes = (size_t)s.H * 2 * 4;
+      break;
     default: return VDN_ERR_INVALID_ARG;
   }
   return VDN_OK;
@@ -516,7 +547,10 @@ vdn_status vdn_debug_copy(const vdn_plan* plan, int which, void* dst, size_t byt
   size_t off = which == VDN_BUF_OS ? plan->lay.os
                : which == VDN_BUF_STATES ? plan->lay.states
                : which == VDN_BUF_MINV ? plan->lay.minv
-                                       : plan->lay.bw;
+               : which == VDN_BUF_BW ? plan->lay.bw
+               : which == VDN_BUF_K8 ? plan->lay.k8
+               : which == VDN_BUF_V8 ? plan->lay.v8
+                                     : plan->lay.scale8;
   if (hipMemcpyAsync(dst, plan->ws + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipGetLastError();
     return VDN_ERR_HIP;

@@ -70,8 +70,12 @@ Layout make_layout(const Shape& s, const Kinds& k) {
   L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
   L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
   L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;
-  L.kmax = mfma_softmax ? take((size_t)s.H * 4) : 0;
-  L.flags = mfma_softmax ? take((size_t)softmax_grid(s, true) * 4) : 0;
+  L.kmax = (mfma_softmax || k.softmax_fp8) ? take((size_t)s.H * 4) : 0;
+  L.flags = mfma_softmax ? take((size_t)softmax_grid(s, true) * 4) : k.softmax_fp8 ? take((size_t)softmax_fp8_grid(s, true) * 4) : 0;
+  L.k8 = k.softmax_fp8 ? take((size_t)s.H * s.Ls8 * s.d) : 0;
+  L.v8 = k.softmax_fp8 ? take((size_t)s.H * s.Ls8 * s.d) : 0;
+  L.part8 = k.softmax_fp8 ? take((size_t)s.H * ((s.Lk + 63) / 64) * 3 * 4) : 0;
+  L.scale8 = k.softmax_fp8 ? take((size_t)s.H * 2 * 4) : 0;
   L.ranges = take((size_t)(s.T + 1) * (2 * kMaxRanges + 1) * 4);
   L.total = off;
   return L;

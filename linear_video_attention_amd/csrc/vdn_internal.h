@@ -25,6 +25,7 @@ struct Shape {
   int ctx_pad;       // n_ctx rounded up to kTextPad
   int64_t Lk;        // key-space length per head: ctx_pad + T*N
   int64_t Ls;        // allocated key stride of the packed K/V: Lk + one zero tile of padding
+  int64_t Ls8;       // key stride of the FP8 packed K/V: Lk + one zero 128-key tile
 };
 
 // Key ranges of query frame t in a head's key space (see vdn_key_ranges); t == T gives the ranges
@@ -50,12 +51,17 @@ struct Layout {
   size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
   size_t kmax;      // largest key norm per head [H] f32
   size_t flags;     // per-workgroup fallback flags of the MFMA softmax [softmax_grid] int32
+  size_t k8;        // FP8 softmax: keys E4M3 [H][Ls8][d], values E4M3 transposed [H][d][Ls8]
+  size_t v8;
+  size_t part8;     // FP8 softmax: per 64-key block and head max |k|, max |v|, max key norm [H][Lk/64][3] f32
+  size_t scale8;    // FP8 softmax: per head key and value scales [H][2] f32
   size_t ranges;    // int32 [T+1][2*kMaxRanges] + int32 [T+1] counts (row T: context query rows)
   size_t total;
 };
 // Kernel selection per stage.
 struct Kinds {
   bool softmax_mfma;
+  bool softmax_fp8;   // FP8 (E4M3) softmax branch instead of the bf16 one
   bool stats_mfma;
   bool scan_mfma;
   bool epilogue_mfma;
@@ -80,6 +86,10 @@ struct Buffers {
   int* flags;
   const int* ranges;   // [T+1][2*kMaxRanges]
   const int* nranges;  // [T+1]
+  uint8_t* k8;
+  uint8_t* v8;
+  float* part8;
+  float* scale8;
   float* lse;          // [T*N][H] base-2 log of each video row's softmax normaliser, or nullptr
 };
 
@@ -136,11 +146,14 @@ hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const 
 // Number of workgroups of the MFMA softmax launch.
 // with_ctx: including the workgroups of the context query rows.
 int softmax_grid(const Shape& s, bool with_ctx);
+int softmax_fp8_grid(const Shape& s, bool with_ctx);
 
 // Launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_prep_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_softmax_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_invert_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);

@@ -18,7 +18,9 @@ VDN_F32, VDN_BF16 = 0, 1
 VDN_FLAG_GENERIC_KERNELS = 1
 VDN_FLAG_SERIAL = 2
 VDN_FLAG_OVERLAP = 4
+VDN_FLAG_FP8_SOFTMAX = 8
 VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV, VDN_BUF_BW = 0, 1, 2, 3
+VDN_BUF_K8, VDN_BUF_V8, VDN_BUF_SCALES8 = 4, 5, 6
 STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total")
 
 # every symbol include/vdn.h declares: (name, restype, argtypes)
@@ -113,13 +115,13 @@ def measure_copy_gbs(nbytes=1 << 30):
 # ---- plan ----
 
 def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
-                    overlap=False, n_audio=0):
+                    overlap=False, n_audio=0, fp8=False):
     """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"; ``n_audio``
-    audio tokens follow the text tokens (a joint plan)."""
+    audio tokens follow the text tokens (a joint plan); ``fp8`` selects the FP8 softmax branch."""
     dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
     h = _vp()
     flags = ((VDN_FLAG_GENERIC_KERNELS if generic else 0) | (VDN_FLAG_SERIAL if serial else 0)
-             | (VDN_FLAG_OVERLAP if overlap else 0))
+             | (VDN_FLAG_OVERLAP if overlap else 0) | (VDN_FLAG_FP8_SOFTMAX if fp8 else 0))
     if n_audio:
         _check(lib().vdn_plan_create_joint(T, N, C, n_text, n_audio, H, d, int(anchors), dt, flags,
                                            ctypes.byref(h)), "vdn_plan_create_joint")
@@ -170,7 +172,7 @@ class Plan:
     """Owning wrapper of a plan with argument checks on torch tensors."""
 
     def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
-                 overlap=False, n_audio=0):
+                 overlap=False, n_audio=0, fp8=False):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("no GPU visible: the VDN layer runs only on the GPU")
@@ -181,7 +183,9 @@ class Plan:
         self.dtype = dtype
         self.torch_dtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
         self.Nc = (T + C - 1) // C
-        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap, n_audio)
+        self.fp8 = bool(fp8)
+        self.Ls8 = (self.n_ctx + 63) // 64 * 64 + T * N + 128
+        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap, n_audio, fp8)
 
     def close(self):
         if self.handle:
@@ -280,6 +284,12 @@ class Plan:
             dst = torch.empty((self.T * self.N, self.H, self.d), dtype=self.torch_dtype, device="cuda")
         elif which == VDN_BUF_STATES:
             dst = torch.empty((2, self.Nc + 1, self.H, self.d, self.d), dtype=torch.float32, device="cuda")
+        elif which == VDN_BUF_K8:
+            dst = torch.empty((self.H, self.Ls8, self.d), dtype=torch.uint8, device="cuda")
+        elif which == VDN_BUF_V8:
+            dst = torch.empty((self.H, self.d, self.Ls8), dtype=torch.uint8, device="cuda")
+        elif which == VDN_BUF_SCALES8:
+            dst = torch.empty((self.H, 2), dtype=torch.float32, device="cuda")
         else:
             dst = torch.empty((self.T + 1, self.H, self.d, self.d), dtype=torch.float32, device="cuda")
         assert dst.numel() * dst.element_size() == nbytes.value

@@ -79,11 +79,15 @@ def head_scales(keys_all: np.ndarray, vals_all: np.ndarray):
 def softmax_rows_fp8(qr, keys, vals, s_k, s_v, kmax) -> np.ndarray:
     """FP8 softmax attention of query rows ``qr`` [m, d] over ``keys``, ``vals`` [n, d] with the
     head's scales; float64 result."""
+    return softmax_rows_rounded(qr, e4m3(s_k * np.asarray(keys, np.float64)),
+                                e4m3(s_v * np.asarray(vals, np.float64)), s_k, s_v, kmax)
+
+
+def softmax_rows_rounded(qr, k8, v8, s_k, s_v, kmax) -> np.ndarray:
+    """As ``softmax_rows_fp8`` for keys and values already rounded (k8 = e4m3(s_k k), v8 likewise)."""
     qr = np.asarray(qr, np.float64)
     d = qr.shape[-1]
     c = math.log2(math.e) / math.sqrt(d)
-    k8 = e4m3(s_k * np.asarray(keys, np.float64))
-    v8 = e4m3(s_v * np.asarray(vals, np.float64))
     out = np.zeros(qr.shape)
     for i, q in enumerate(qr):
         s_q = pow2_scale(np.abs(q).max())
@@ -95,6 +99,42 @@ def softmax_rows_fp8(qr, keys, vals, s_k, s_v, kmax) -> np.ndarray:
     return out
 
 
+def ambiguous_rounding_effect(qr, keys, vals, s_k, s_v, kmax, rel_score_err=2.0 ** -16) -> np.ndarray:
+    """Per query row, how far o may move when the scores carry a relative error: a weight P8_j can
+    round to the other side of an E4M3 midpoint only if its exponent 8 + c x_j - m lies within
+    delta_j = c rel_score_err sum_i |Q8_i K8_ji| / (s_q s_k) (+ a float32 rounding of the
+    exponent) of the midpoint's exponent; each such weight moves o by at most one E4M3 step times
+    max |V8_j / s_v - o| / sum P8.  Returns the sum over those weights (zero for most rows).  Used
+    to compare with hardware whose fp32 score sums are not exact."""
+    qr = np.asarray(qr, np.float64)
+    d = qr.shape[-1]
+    c = math.log2(math.e) / math.sqrt(d)
+    k8 = e4m3(s_k * np.asarray(keys, np.float64))
+    v8 = e4m3(s_v * np.asarray(vals, np.float64)) / s_v
+    res = np.zeros(len(qr))
+    for i, q in enumerate(qr):
+        s_q = pow2_scale(np.abs(q).max())
+        q8 = e4m3(s_q * q)
+        x = (k8 @ q8) / (s_q * s_k)
+        b = c * math.sqrt(float(q @ q)) * kmax
+        m = b if b <= OFFSET_BOUND_LIMIT else c * x.max()
+        arg = P_SHIFT + c * x - m
+        p8 = e4m3(np.exp2(arg))
+        o = (p8 @ v8) / p8.sum()
+        delta = c * rel_score_err * (np.abs(k8) @ np.abs(q8)) / (s_q * s_k) + 2.0 ** -20 * (np.abs(arg) + P_SHIFT)
+        if m != b:
+            delta = delta + c * rel_score_err * np.max(np.abs(k8) @ np.abs(q8)) / (s_q * s_k)  # the row maximum too
+        p = np.exp2(arg)
+        _, ex = np.frexp(p)
+        e = np.maximum(ex - 1, -6)
+        step = np.ldexp(1.0, e - 3)
+        mid = (np.floor(p / step) + 0.5) * step                   # midpoint above the value's floor
+        near = np.minimum(np.abs(np.log2(p / mid)), np.abs(np.log2(p / np.maximum(mid - step, 2.0 ** -12))))
+        amb = near < delta
+        res[i] = np.sum(2 * step[amb] * np.abs(v8[amb] - o).max(axis=1)) / p8.sum()
+    return res
+
+
 def softmax_branch_fp8(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None):
     """o_s of the FP8 variant for every video token (``rows=None``) or the given token indices."""
     if audio_k is not None:
@@ -102,19 +142,20 @@ def softmax_branch_fp8(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, aud
         text_v = np.concatenate([text_v, audio_v], axis=0)
     TN, H, d = q.shape
     assert TN == T * N
+    n_g = text_k.shape[0]
     rows = np.arange(TN) if rows is None else np.asarray(rows)
     out = np.zeros((len(rows), H, d))
-    scales = [head_scales(np.concatenate([text_k[:, h], k[:, h]]), np.concatenate([text_v[:, h], v[:, h]]))
-              for h in range(H)]
     frames_of_rows = rows // N
-    for t in np.unique(frames_of_rows):
-        sel = np.nonzero(frames_of_rows == t)[0]
-        kf = orc.key_frames(int(t), T, C, anchors)
-        idx = np.concatenate([np.arange(f * N, (f + 1) * N) for f in kf])
-        for h in range(H):
-            keys = np.concatenate([text_k[:, h], k[idx, h]], axis=0)
-            vals = np.concatenate([text_v[:, h], v[idx, h]], axis=0)
-            out[sel, h] = softmax_rows_fp8(q[rows[sel], h], keys, vals, *scales[h])
+    for h in range(H):
+        keys_all = np.concatenate([text_k[:, h], k[:, h]]).astype(np.float64)
+        vals_all = np.concatenate([text_v[:, h], v[:, h]]).astype(np.float64)
+        s_k, s_v, kmax = head_scales(keys_all, vals_all)
+        k8, v8 = e4m3(s_k * keys_all), e4m3(s_v * vals_all)       # every key rounded once
+        for t in np.unique(frames_of_rows):
+            sel = np.nonzero(frames_of_rows == t)[0]
+            kf = orc.key_frames(int(t), T, C, anchors)
+            idx = np.concatenate([np.arange(n_g)] + [n_g + np.arange(f * N, (f + 1) * N) for f in kf])
+            out[sel, h] = softmax_rows_rounded(q[rows[sel], h], k8[idx], v8[idx], s_k, s_v, kmax)
     return out
 
 

@@ -1,0 +1,217 @@
+"""Parity of the FP8 softmax variant (plans created with VDN_FLAG_FP8_SOFTMAX) with its CPU oracle
+(``oracle/fp8_softmax.py``), through the C ABI.
+
+* the packed E4M3 keys and values and the per-head scales are compared byte for byte with the
+  oracle's rounding of the same inputs (integer work: bit-exact);
+* o_s, out and the context rows are held to the bf16 bar, max |gpu - oracle| <= 2e-2 * RMS(oracle),
+  against the FP8 oracle (the GPU stores o_s in bf16, inside that bar; the two sides round the same
+  values, and a weight whose exponent lands within an fp32 rounding of an E4M3 midpoint may round
+  the other way, which moves o_s by far less than the bar);
+* the FP8 layer stays within the FP8 rounding error of the exact layer (a loose sanity bound);
+* the row-maximum offset (rows whose bound exceeds the limit), ragged tiles, no text, anchors off,
+  one frame, decay, audio keys and context rows, and 768p on sampled rows in the bench's launch
+  configuration.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import TOL, rel_err, softmax_out, to_device
+from linear_video_attention_amd.vdn import VDN_BUF_K8, VDN_BUF_SCALES8, VDN_BUF_V8, Plan
+from oracle import fp8_softmax as f8
+from oracle import vdn_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def fp8_plan(w, n_audio=0):
+    return Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, n_audio=n_audio, fp8=True)
+
+
+def forward(plan, dev, ctx=False):
+    res = plan.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
+                       alpha=dev.get("alpha"), ctx_q=dev["ctx_q"] if ctx else None)
+    torch.cuda.synchronize()
+    return res
+
+
+def ctx_keys_values(inp):
+    ck, cv = inp["text_k"], inp["text_v"]
+    if inp.get("audio_k") is not None:
+        ck = np.concatenate([ck, inp["audio_k"]])
+        cv = np.concatenate([cv, inp["audio_v"]])
+    return ck, cv
+
+
+def check_fp8(w, seed=0, decay=False, n_audio=0, ctx_rows=False, q_scale=None):
+    inp = synth.make_inputs(w, seed=seed, decay=decay, n_audio=n_audio, ctx_rows=ctx_rows)
+    if q_scale is not None:          # the oracle must see the bf16 values the device holds
+        q = torch.from_numpy((inp["q"] * q_scale[:, None, None]).astype(np.float32))
+        inp["q"] = q.to(torch.bfloat16).float().numpy()
+    plan = fp8_plan(w, n_audio=n_audio)
+    dev = to_device(inp, w.dtype)
+    res = forward(plan, dev, ctx=ctx_rows)
+    out, ctx = res if ctx_rows else (res, None)
+    got_os = softmax_out(plan)
+    got_out = out.float().cpu().numpy()
+    ref_out, inter = f8.vdn_forward_fp8(inp, w.T, w.N, w.C, w.anchors, with_intermediates=True)
+    e_os, e_out = rel_err(got_os, inter["o_s"]), rel_err(got_out, ref_out)
+    msg = f"{w} decay={decay} audio={n_audio}: o_s {e_os:.2e} out {e_out:.2e}"
+    if ctx_rows:
+        ref_c = f8.context_rows_fp8(inp, w.T, w.N)
+        e_c = rel_err(ctx.float().cpu().numpy(), ref_c)
+        msg += f" ctx {e_c:.2e}"
+        assert e_c <= TOL["bf16"]
+    print(msg, flush=True)
+    assert e_os <= TOL["bf16"] and e_out <= TOL["bf16"]
+    plan.close()
+    return inp, got_os, got_out
+
+
+def test_fp8_packing_is_bit_exact():
+    w = synth.custom(20, 5, 48, 2, 2, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, seed=1, n_audio=7)
+    plan = fp8_plan(w, n_audio=7)
+    dev = to_device(inp, w.dtype)
+    forward(plan, dev)
+    k8 = plan.debug_buffer(VDN_BUF_K8).cpu()
+    v8 = plan.debug_buffer(VDN_BUF_V8).cpu()
+    sc = plan.debug_buffer(VDN_BUF_SCALES8).cpu().numpy()
+    ck, cv = ctx_keys_values(inp)
+    n_ctx = ck.shape[0]
+    pad = (n_ctx + 63) // 64 * 64
+    for h in range(w.H):
+        keys = np.concatenate([ck[:, h], inp["k"][:, h]])
+        vals = np.concatenate([cv[:, h], inp["v"][:, h]])
+        s_k, s_v, _ = f8.head_scales(keys, vals)
+        assert sc[h, 0] == s_k and sc[h, 1] == s_v, (h, sc[h], s_k, s_v)
+        # decode the device bytes as E4M3 and compare with the oracle's rounding, key by key
+        gk = k8[h].view(torch.float8_e4m3fn).double().numpy()
+        gv = v8[h].view(torch.float8_e4m3fn).double().numpy()
+        want_k = np.zeros_like(gk)
+        want_v = np.zeros_like(gv)
+        want_k[:n_ctx] = f8.e4m3(s_k * ck[:, h])
+        want_k[pad:pad + w.T * w.N] = f8.e4m3(s_k * inp["k"][:, h])
+        want_v[:, :n_ctx] = f8.e4m3(s_v * cv[:, h]).T
+        want_v[:, pad:pad + w.T * w.N] = f8.e4m3(s_v * inp["v"][:, h]).T
+        assert np.array_equal(gk, want_k), h
+        assert np.array_equal(gv, want_v), h
+    plan.close()
+
+
+def test_fp8_small_matches_oracle():
+    check_fp8(synth.custom(24, 9, 64, 3, 2, 128, "bf16", "sigmoid", True))
+
+
+FP8_RAGGED = [
+    # n_text, T, N, C, H, anchors: partial 128-key tiles, no text, anchors off, one frame,
+    # one frame per chunk, a single chunk, more than one workgroup per frame
+    (5, 7, 48, 2, 1, True),
+    (0, 6, 80, 2, 2, True),
+    (13, 8, 32, 3, 1, False),
+    (3, 1, 64, 5, 1, True),
+    (9, 5, 16, 1, 1, True),
+    (40, 4, 96, 5, 1, True),
+    (2, 3, 400, 2, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", FP8_RAGGED, ids=lambda c: "x".join(str(x) for x in c))
+def test_fp8_ragged_shapes(case):
+    n_text, T, N, C, H, anchors = case
+    check_fp8(synth.custom(n_text, T, N, C, H, 128, "bf16", "sigmoid", anchors), seed=2)
+
+
+def test_fp8_decay_and_joint():
+    w = synth.custom(12, 7, 48, 2, 2, 128, "bf16", "sigmoid", True)
+    check_fp8(w, seed=3, decay=True, n_audio=21, ctx_rows=True)
+
+
+def test_fp8_row_maximum_offset():
+    """Queries scaled by 64 on every other row, so that the bound c |q| kmax (8.2) exceeds 4 there:
+    those rows take the exact row maximum as the offset (the second launch), the others keep the
+    bound, inside the same workgroups.
+
+    These rows attend sharply (the weights span four binades and their sum is small), so one
+    weight that rounds to the neighbouring E4M3 value moves o by up to ~4 % of the output's RMS.
+    That happens when a weight's exponent lies within the score error of an E4M3 midpoint: the
+    matrix cores' fp32 score sums are not exact (one measured weight: 2^-17.6 relative), which
+    shifts the exponent by up to c 2^-16 sum|Q8 K8| / (s_q s_k).  The bar per row is the bf16 bar
+    plus the effect of every weight that close to a midpoint (``ambiguous_rounding_effect``; zero
+    on most rows)."""
+    w = synth.custom(10, 6, 64, 2, 2, 128, "bf16", "sigmoid", True)
+    scale = np.where(np.arange(w.T * w.N) % 2 == 0, 64.0, 1.0)
+    inp = synth.make_inputs(w, seed=4)
+    q = torch.from_numpy((inp["q"] * scale[:, None, None]).astype(np.float32))
+    inp["q"] = q.to(torch.bfloat16).float().numpy()
+    plan = fp8_plan(w)
+    dev = to_device(inp, w.dtype)
+    forward(plan, dev)
+    got = softmax_out(plan)
+    plan.close()
+    ref = f8.softmax_branch_fp8(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], w.T, w.N, w.C,
+                                w.anchors)
+    rms = np.sqrt(np.mean(ref ** 2))
+    allow = np.zeros((w.T * w.N, w.H))
+    for h in range(w.H):
+        keys_all = np.concatenate([inp["text_k"][:, h], inp["k"][:, h]])
+        vals_all = np.concatenate([inp["text_v"][:, h], inp["v"][:, h]])
+        scales = f8.head_scales(keys_all, vals_all)
+        for t in range(w.T):
+            kf = orc.key_frames(t, w.T, w.C, w.anchors)
+            idx = np.concatenate([np.arange(f * w.N, (f + 1) * w.N) for f in kf])
+            keys = np.concatenate([inp["text_k"][:, h], inp["k"][idx, h]])
+            vals = np.concatenate([inp["text_v"][:, h], inp["v"][idx, h]])
+            rows = slice(t * w.N, (t + 1) * w.N)
+            allow[rows, h] = f8.ambiguous_rounding_effect(inp["q"][rows, h], keys, vals, *scales)
+    err = np.abs(got - ref).max(axis=2)
+    bar = TOL["bf16"] * rms + allow
+    print(f"row-maximum offset: max err {err.max() / rms:.2e} RMS, plain bar exceeded on "
+          f"{int((err > TOL['bf16'] * rms).sum())} of {err.size} rows, max err/bar {np.max(err / bar):.2f}", flush=True)
+    assert np.all(err <= bar)
+    # the bound rows of the same workgroups keep the plain bar
+    assert err[1::2].max() <= TOL["bf16"] * rms
+
+
+def test_fp8_close_to_exact_layer():
+    """The FP8 layer against the exact oracle: the E4M3 roundings move o_s by a few percent of its
+    RMS (each rounding at most 2^-4 relative), far less than the branch itself."""
+    w = synth.custom(24, 9, 64, 3, 2, 128, "bf16", "sigmoid", True)
+    inp, got_os, _ = check_fp8(w, seed=5)
+    exact = orc.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], w.T, w.N, w.C, w.anchors)
+    err = got_os - exact
+    rms = np.sqrt(np.mean(exact.astype(np.float64) ** 2))
+    assert np.sqrt(np.mean(err ** 2)) <= 0.08 * rms
+    assert np.abs(err).max() <= 0.5 * rms
+
+
+def test_fp8_768p_sampled_rows():
+    """768p in the benchmark's launch configuration: sampled rows of out against the FP8 oracle."""
+    w = synth.WORKLOADS["768p"]
+    inp = synth.make_inputs(w, seed=0)
+    plan = fp8_plan(w)
+    dev = to_device(inp, w.dtype)
+    out = forward(plan, dev)
+    rows = synth.sample_rows(w)
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    del dev, out
+    ref = f8.vdn_forward_fp8(inp, w.T, w.N, w.C, w.anchors, rows=rows)
+    e = rel_err(got, ref)
+    print(f"768p fp8: out err {e:.2e} ({len(rows)} rows)", flush=True)
+    assert e <= TOL["bf16"]
+    plan.close()
+
+
+def test_fp8_backward_unsupported():
+    from linear_video_attention_amd import vdn
+    w = synth.custom(4, 3, 32, 2, 1, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w)
+    dev = to_device(inp, w.dtype)
+    plan = fp8_plan(w)
+    with pytest.raises(vdn.VdnError) as ei:
+        plan.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
+                      torch.zeros_like(dev["q"]))
+    assert ei.value.status == -2
+    plan.close()

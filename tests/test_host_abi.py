@@ -59,11 +59,24 @@ def test_invalid_plans_rejected_on_host(vdn, args, status):
     assert h.value is None
 
 
-@pytest.mark.parametrize("flags", [2 | 4, 8, 1 << 31])
+@pytest.mark.parametrize("flags", [2 | 4, 16, 1 << 31, 1 | 8])
 def test_invalid_plan_flags_rejected_on_host(vdn, flags):
-    """Serial and overlapped order together, or an unknown flag bit, are argument errors."""
+    """Serial and overlapped order together, an unknown flag bit, or the FP8 softmax with the
+    generic kernels are argument errors."""
     h = ctypes.c_void_p(1234)
-    assert vdn.lib().vdn_plan_create_ex(4, 16, 2, 1, 1, 16, 1, 0, flags, ctypes.byref(h)) == -1
+    assert vdn.lib().vdn_plan_create_ex(4, 16, 2, 1, 1, 128, 1, 1, flags, ctypes.byref(h)) == -1
+    assert h.value is None
+
+
+@pytest.mark.parametrize("args", [
+    (4, 16, 2, 1, 1, 128, 1, 0),     # fp32 plan
+    (4, 16, 2, 1, 1, 64, 1, 1),      # d = 64
+    (4, 24, 2, 1, 1, 128, 1, 1),     # N not a multiple of 16
+])
+def test_fp8_plan_limits_rejected_on_host(vdn, args):
+    """The FP8 softmax takes bf16 plans with d = 128 and N a multiple of 16 only."""
+    h = ctypes.c_void_p(1234)
+    assert vdn.lib().vdn_plan_create_ex(*args, 8, ctypes.byref(h)) == -2
     assert h.value is None
 
 
