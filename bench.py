@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 matrix peak
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 
 
@@ -240,6 +241,24 @@ def main():
     del dout
     plan.close()
 
+    # the FP8 (E4M3) softmax variant of the same layer (context: the headline value is bf16)
+    fplan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, fp8=True)
+    for _ in range(2):
+        forward(fplan)
+    torch.cuda.synchronize()
+    n_f8 = max(3, min(args.steps, 10))
+    fplan.profile_enable(n_f8)
+    f8_steps = timed_steps(lambda: forward(fplan), n_f8)
+    f8_ms, f8_calls = fplan.profile_read()
+    sm8 = f8_ms["softmax"] / f8_calls
+    f8_med = float(np.median(f8_steps))
+    fp8_info = {"ms_per_step_median": f8_med, "tokens_per_s": tokens / (f8_med * 1e-3),
+                "stages_ms": {k: v / f8_calls for k, v in f8_ms.items()},
+                "softmax_kernel": "softmax_fp8_kernel", "softmax_achieved_TFLOPs": flops / (sm8 * 1e-3) / 1e12,
+                "softmax_frac_fp8_peak": flops / (sm8 * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+                "fp8_peak_TFLOPs": MFMA_FP8_PEAK_TFLOPS}
+    fplan.close()
+
     overlapped = None
     if args.with_overlap:
         # the linear branch on a side stream next to the softmax branch (context only)
@@ -284,6 +303,7 @@ def main():
     decay["vda_frac_hbm"] = (vb + 4 * w.T * w.H * w.d) / (decay["vda_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
     result["decay_gate"] = decay
     result["backward"] = backward_info
+    result["fp8_softmax"] = fp8_info
     if overlapped is not None:
         result["overlapped_branches"] = overlapped
     del dev, beta, text_kv, alpha, out, ref

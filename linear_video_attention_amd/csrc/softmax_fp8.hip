@@ -16,7 +16,7 @@
 //     (a constant all-ones A operand next to the V^T tiles), and o_s is stored in bf16.
 //
 // Work decomposition (as the bf16 kernel, with 128-key tiles: one k-step of the P.V product):
-//   * one workgroup = 384 queries of one frame and head, 8 waves x 48 queries (three 16-query
+//   * one workgroup = 256 queries of one frame and head, 8 waves x 32 queries (two 16-query
 //     tiles), two waves per SIMD;
 //   * K [128 keys][128 B] and V^T [128 channels][128 B] tiles go global -> LDS by
 //     global_load_lds (16-byte chunks XOR-swizzled so each 8-lane group of a fragment read hits
@@ -41,9 +41,19 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 constexpr int D = 128;
 constexpr int kBK = 128;            // keys per tile
 constexpr int kWaves = 8;
-constexpr int kQT = 2;              // 16-query tiles per wave
+// Build parameters (defaults measured best at 768p; the alternatives are kept for measurement):
+//   VDN_FP8_QT   16-query tiles per wave (2; 3 exceeds the register budget of two waves per SIMD)
+//   VDN_FP8_UG   16-key score tiles formed per step before their weights (1, 2, 4)
+#ifndef VDN_FP8_QT
+#define VDN_FP8_QT 2
+#endif
+#ifndef VDN_FP8_UG
+#define VDN_FP8_UG 2
+#endif
+constexpr int kQT = VDN_FP8_QT;     // 16-query tiles per wave
+constexpr int kUG = VDN_FP8_UG;
 constexpr int kQW = 16 * kQT;
-constexpr int kBQ = kWaves * kQW;   // 384 queries per workgroup
+constexpr int kBQ = kWaves * kQW;   // queries per workgroup
 constexpr int kStages = 2;
 constexpr int K_BYTES = kBK * D;    // 16 KB
 constexpr int V_BYTES = D * kBK;    // 16 KB
@@ -355,19 +365,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
     VDN_FP8_NEXT_TILE(it, cur, valid, valid_next, kb)
     const unsigned char* vb = kb + K_BYTES;
     i32x8 pf[kQT];
-    // scores and weights, two 16-key tiles at a time
+    // scores and weights, kUG 16-key tiles at a time
 #pragma unroll
-    for (int up = 0; up < 4; ++up) {
-      const i32x8 kf0 = kfrag(kb, 2 * up), kf1 = kfrag(kb, 2 * up + 1);
-      f32x4 s[2][kQT];
+    for (int up = 0; up < 8 / kUG; ++up) {
+      i32x8 kf[kUG];
 #pragma unroll
-      for (int j = 0; j < kQT; ++j) {
-        s[0][j] = mfma8(kf0, qf[j], f32x4{0.f, 0.f, 0.f, 0.f});
-        s[1][j] = mfma8(kf1, qf[j], f32x4{0.f, 0.f, 0.f, 0.f});
-      }
+      for (int uu = 0; uu < kUG; ++uu) kf[uu] = kfrag(kb, kUG * up + uu);
+      f32x4 s[kUG][kQT];
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const int u = 2 * up + uu;
+      for (int uu = 0; uu < kUG; ++uu)
+#pragma unroll
+        for (int j = 0; j < kQT; ++j) s[uu][j] = mfma8(kf[uu], qf[j], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int uu = 0; uu < kUG; ++uu) {
+        const int u = kUG * up + uu;
         if (valid < kBK) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
