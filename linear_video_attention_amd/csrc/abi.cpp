@@ -82,7 +82,7 @@ vdn::Shape make_shape(int T, int N, int C, int n_text, int n_audio, int H, int d
   s.Nc = (T + C - 1) / C;
   s.ctx_pad = (int)vdn::round_up(s.n_ctx, vdn::kTextPad);
   s.Lk = (int64_t)s.ctx_pad + (int64_t)T * N;
-  s.Ls = s.Lk + 64;
+  s.Ls = s.Lk + 128;
   s.Ls8 = s.Lk + 128;
   return s;
 }

@@ -7,7 +7,7 @@
 //   Kp [H][Ls][d]   keys, bf16, row per key
 //   Vt [H][d][Ls]   values transposed, bf16, so that the P.V contraction (over keys) reads
 //                   key-contiguous 16-byte fragments
-// Ls = Lk + 64: one tile of zero keys past the end (zeroed at plan creation, never written here)
+// Ls = Lk + 128: a tile of zero keys past the end (zeroed at plan creation, never written here)
 // so that a tile load never leaves the buffer.  Padding keys (n_ctx <= j < ctx_pad) are zero;
 // the softmax kernel masks them.
 // The same pass records the largest key norm of each 64-key block; a second tiny kernel reduces

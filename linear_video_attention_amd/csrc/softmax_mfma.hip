@@ -37,18 +37,21 @@ namespace vdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-constexpr int kBK = 64;             // keys per tile
 // Build parameters (defaults measured best at 768p; the alternatives are kept for measurement):
 //   VDN_SOFTMAX_WAVES   waves per workgroup (8; 4 gives two 192-query workgroups per CU, ~4 % slower)
 //   VDN_SOFTMAX_STAGES  LDS stages of the tile pipeline (2; 3 and 4 keep more tiles in flight,
 //                       1-2 % slower since the key tiles mostly hit in L2 / Infinity Cache)
 //   VDN_SOFTMAX_SCHED   1: order each half as K reads, score MFMAs | V reads, exponentials, P.V
 //                       MFMAs (about 3 % faster than the compiler's own interleaving)
+//   VDN_SOFTMAX_BK      keys per LDS tile (64; 128 halves the barriers but is 3 % slower)
+//   VDN_SOFTMAX_DOT2SUM 1: the normaliser from the bf16-rounded weights by v_dot2c_f32_bf16 instead
+//                       of fp32 adds (4 % slower: the sums wait for the conversions)
 #ifndef VDN_SOFTMAX_WAVES
 #define VDN_SOFTMAX_WAVES 8
 #endif
@@ -58,6 +61,14 @@ constexpr int kBK = 64;             // keys per tile
 #ifndef VDN_SOFTMAX_SCHED
 #define VDN_SOFTMAX_SCHED 1
 #endif
+#ifndef VDN_SOFTMAX_BK
+#define VDN_SOFTMAX_BK 64
+#endif
+#ifndef VDN_SOFTMAX_DOT2SUM
+#define VDN_SOFTMAX_DOT2SUM 0
+#endif
+constexpr int kBK = VDN_SOFTMAX_BK;  // keys per tile (64 or 128)
+static_assert(kBK == 64 || kBK == 128, "key tile");
 constexpr int kWaves = VDN_SOFTMAX_WAVES;       // waves per workgroup; 8 / kWaves workgroups per CU
 constexpr int kQT = 3;              // 16-query column tiles per wave
 constexpr int kQW = 16 * kQT;       // queries per wave
@@ -256,8 +267,9 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
   }
 #pragma unroll
   for (int i = 0; i < V_INSTR; ++i) {
-    const int row = (i * kWaves + wave) * 8 + lane / 8;
-    const int c = (lane % 8) ^ v_swz(row);
+    constexpr int VCH = kBK / 8;                        // 16-byte chunks per V^T row
+    const int row = (i * kWaves + wave) * (64 / VCH) + lane / VCH;
+    const int c = (lane % VCH) ^ v_swz(row);
     voff[i] = (uint32_t)((int64_t)row * Ls + c * 8) * 2u;
   }
   auto issue_tile = [&](int key0, int stage) {
@@ -367,9 +379,17 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
           // raw v_exp_f32: results below 2^-126 flush to zero, harmless since the largest term of
           // every query is >= 2^-96 (fixed reference) or 1 (online maximum)
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][j][i], c_log2, -mref[j]));
+#if !VDN_SOFTMAX_DOT2SUM
           ls += p;
+#endif
           pf[j][4 * u + i] = (__bf16)p;
         }
+#if VDN_SOFTMAX_DOT2SUM
+      // the normaliser from the rounded weights, two per v_dot2c_f32_bf16
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[j][2 * e], pf[j][2 * e + 1]}, one2, ls, false);
+#endif
       lsum[j] += ls;
     }
   };
@@ -418,15 +438,19 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
     tile_at(it, key0, valid);
     const unsigned char* kb = smem + (it % kStages) * SM::STAGE;
     const unsigned char* vb = kb + SM::K_BYTES;
+#pragma unroll 1
+    for (int hp = 0; hp < kBK / 64; ++hp) {     // 64 keys per pass, as two 32-key halves
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 sacc[2][kQT];
-      bf16x8 pf[kQT];
-      scores(kb, half, sacc);
-      if (valid < kBK) mask(half, valid, sacc);
-      if constexpr (FALLBACK) online_max(sacc);
-      probs(sacc, pf);
-      accumulate(vb, half, pf);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int half = 2 * hp + hh;
+        f32x4 sacc[2][kQT];
+        bf16x8 pf[kQT];
+        scores(kb, half, sacc);
+        if (valid < kBK) mask(half, valid, sacc);
+        if constexpr (FALLBACK) online_max(sacc);
+        probs(sacc, pf);
+        accumulate(vb, half, pf);
+      }
     }
   }
 

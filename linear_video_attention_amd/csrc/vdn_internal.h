@@ -24,7 +24,7 @@ struct Shape {
   int Nc;            // number of chunks
   int ctx_pad;       // n_ctx rounded up to kTextPad
   int64_t Lk;        // key-space length per head: ctx_pad + T*N
-  int64_t Ls;        // allocated key stride of the packed K/V: Lk + one zero tile of padding
+  int64_t Ls;        // allocated key stride of the packed K/V: Lk + 128 zero keys of padding
   int64_t Ls8;       // key stride of the FP8 packed K/V: Lk + one zero 128-key tile
 };
 
