@@ -71,12 +71,13 @@ def stage_rooflines(w, ms):
     return out
 
 
-def recorded_traffic():
-    """HBM bytes per softmax launch from the committed rocprofv3 byte-counter summary, if it was
-    taken on the current source of the softmax kernel (else None)."""
+def recorded_traffic(name="softmax_mfma"):
+    """HBM bytes per launch of a softmax kernel (``softmax_mfma`` or ``softmax_fp8``) from the
+    committed rocprofv3 byte-counter summary, if it was taken on the kernel's current source
+    (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "softmax_mfma_768p_traffic.txt")
-    src = os.path.join(ROOT, "linear_video_attention_amd", "csrc", "softmax_mfma.hip")
+    path = os.path.join(ROOT, "profiles", f"{name}_768p_traffic.txt")
+    src = os.path.join(ROOT, "linear_video_attention_amd", "csrc", f"{name}.hip")
     try:
         rec = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -256,7 +257,7 @@ def main():
                 "stages_ms": {k: v / f8_calls for k, v in f8_ms.items()},
                 "softmax_kernel": "softmax_fp8_kernel", "softmax_achieved_TFLOPs": flops / (sm8 * 1e-3) / 1e12,
                 "softmax_frac_fp8_peak": flops / (sm8 * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
-                "fp8_peak_TFLOPs": MFMA_FP8_PEAK_TFLOPS}
+                "fp8_peak_TFLOPs": MFMA_FP8_PEAK_TFLOPS, "softmax_traffic": recorded_traffic("softmax_fp8")}
     fplan.close()
 
     overlapped = None
