@@ -29,6 +29,10 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kWaves = 8;
+// VDN_DKV_WIDE 1: the dK/dV kernel with 4 waves x 32 keys (see softmax_dkv_wide_kernel)
+#ifndef VDN_DKV_WIDE
+#define VDN_DKV_WIDE 1
+#endif
 constexpr int kVmcntZero = 0x0F70;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -241,6 +245,200 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
       f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
       *a = *a + dkt[dt];
       *b = *b + dvt[dt];
+    }
+  }
+}
+
+// Wide variant: 4 waves x 32 keys (two 16-key tiles per wave), one wave per SIMD.  Every Q, dO,
+// Q^T and dO^T fragment a wave reads from LDS feeds two MFMAs (one per key tile), which halves
+// the LDS reads per MFMA of the 16-key layout, and the tile's normalisers and D values come
+// through LDS with the tile instead of per-element global loads.
+constexpr int kDkvWaves = 4;
+#ifndef VDN_DKV_MINBLOCKS
+#define VDN_DKV_MINBLOCKS 1
+#endif
+
+template <int D>
+struct DkvWideSmem {
+  static constexpr int ROW = 64 * D * 2;
+  static constexpr int STAGE = 4 * ROW + 512;     // Q, dO, Q^T, dO^T, then lse[64], dsum[64]
+};
+
+template <int D>
+__global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv_wide_kernel(DkvParams P) {
+  using SM = DkvWideSmem<D>;
+  constexpr int KS = D / 32, DT = D / 16, KCH = D / 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int2 blk = P.blocks[blockIdx.x];
+  const int slot = blk.x, h = blockIdx.y;
+  const int N = P.N, H = P.H;
+  const int U = slot == 0 ? P.n_text : N;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  bf16x8 kf[2][KS], vf[2][KS];
+  int keyk[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = blk.y + 32 * wave + 16 * kt + l16;        // this lane's key of tile kt
+    keyk[kt] = key;
+    const int kc = key < U ? key : U - 1;
+    const bf16_t* kbase = slot == 0 ? P.text_kv + ((int64_t)kc * H + h) * D
+                                    : P.k + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
+    const bf16_t* vbase = slot == 0 ? P.text_kv + (((int64_t)P.n_text + kc) * H + h) * D
+                                    : P.v + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
+      vf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
+    }
+  }
+  f32x4 dvt[2][DT], dkt[2][DT];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dvt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dkt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int* qr = P.qranges + slot * 2 * kMaxRanges;
+  const int nr = uniform(P.nqranges[slot]);
+  const int tpf = (N + 63) / 64;
+  int nfr = 0;
+  for (int r = 0; r < nr; ++r) nfr += qr[2 * r + 1] - qr[2 * r];
+  const int ntiles = uniform(nfr * tpf);
+  constexpr int R_ROWS_PER_KB = 1024 / (D * 2);
+  constexpr int R_INSTR = SM::ROW / 1024 / kDkvWaves;
+  constexpr int T_INSTR = SM::ROW / 1024 / kDkvWaves;
+
+  const float c = P.c, tau = P.tau;
+  int t_next = 0, q_next = 0;
+#define VDN_DKV_TILE_AT(it_, t_, q0_)                                  \
+  {                                                                    \
+    int fi_ = (it_) / tpf;                                             \
+    q0_ = ((it_) % tpf) * 64;                                          \
+    t_ = 0;                                                            \
+    for (int r_ = 0; r_ < nr; ++r_) {                                  \
+      const int len_ = qr[2 * r_ + 1] - qr[2 * r_];                    \
+      if (fi_ < len_) { t_ = qr[2 * r_] + fi_; break; }                \
+      fi_ -= len_;                                                     \
+    }                                                                  \
+  }
+#define VDN_DKV_ISSUE(t_, q0_, stage_)                                                                      \
+  {                                                                                                         \
+    unsigned char* base_ = smem + (stage_) * SM::STAGE;                                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < R_INSTR; ++i_) {                                                \
+      const int blkid_ = i_ * kDkvWaves + wave;                                                             \
+      const int row_ = blkid_ * R_ROWS_PER_KB + lane / KCH;                                                 \
+      const int c_ = (lane % KCH) ^ r_swz(row_);                                                            \
+      const int qrow_ = min((q0_) + row_, N - 1);                                                           \
+      const int64_t off_ = (((int64_t)(t_) * N + qrow_) * H + h) * D + c_ * 8;                              \
+      __builtin_amdgcn_global_load_lds((gptr_t)(P.q + off_), (lptr_t)(base_ + blkid_ * 1024), 16, 0, 0);   \
+      __builtin_amdgcn_global_load_lds((gptr_t)(P.dout + off_), (lptr_t)(base_ + SM::ROW + blkid_ * 1024), \
+                                       16, 0, 0);                                                           \
+    }                                                                                                       \
+    _Pragma("unroll") for (int i_ = 0; i_ < T_INSTR; ++i_) {                                                \
+      const int blkid_ = i_ * kDkvWaves + wave;                                                             \
+      const int row_ = blkid_ * 8 + lane / 8;                                                               \
+      const int c_ = (lane % 8) ^ t_swz(row_);                                                              \
+      const int64_t off_ = ((int64_t)h * D + row_) * P.Lq + (int64_t)(t_) * N + (q0_) + c_ * 8;           \
+      __builtin_amdgcn_global_load_lds((gptr_t)(P.qt + off_), (lptr_t)(base_ + 2 * SM::ROW + blkid_ * 1024), \
+                                       16, 0, 0);                                                           \
+      __builtin_amdgcn_global_load_lds((gptr_t)(P.dot + off_), (lptr_t)(base_ + 3 * SM::ROW + blkid_ * 1024), \
+                                       16, 0, 0);                                                           \
+    }                                                                                                       \
+    if (wave < 2) {                                                                                         \
+      const int64_t rr_ = ((int64_t)(t_) * N + min((q0_) + lane, N - 1)) * H + h;                           \
+      __builtin_amdgcn_global_load_lds((gptr_t)((wave == 0 ? P.lse : P.dsum) + rr_),                        \
+                                       (lptr_t)(base_ + 4 * SM::ROW + wave * 256), 4, 0, 0);                \
+    }                                                                                                       \
+  }
+  if (ntiles > 0) {
+    VDN_DKV_TILE_AT(0, t_next, q_next)
+    VDN_DKV_ISSUE(t_next, q_next, 0)
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+    int t, q0;
+    VDN_DKV_TILE_AT(it, t, q0)
+    if (it + 1 < ntiles) {
+      VDN_DKV_TILE_AT(it + 1, t_next, q_next)
+      VDN_DKV_ISSUE(t_next, q_next, (it + 1) & 1)
+    }
+    const unsigned char* qs = smem + (it & 1) * SM::STAGE;
+    const unsigned char* os = qs + SM::ROW;
+    const unsigned char* qts = qs + 2 * SM::ROW;
+    const unsigned char* ots = qs + 3 * SM::ROW;
+    const float* lse_s = reinterpret_cast<const float*>(qs + 4 * SM::ROW);
+    const float* dsum_s = lse_s + 64;
+    bf16x8 pj[2][2], sj[2][2];                               // [key tile][32-query k-step]
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 sc[2], dp[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const int row = perm_row(u, l16);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = ks * 4 + g;
+        const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
+        const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + boff));
+        const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(os + boff));
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kt][ks], sc[kt], 0, 0, 0);
+          dp[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kt][ks], dp[kt], 0, 0, 0);
+        }
+      }
+      // lane holds rows 4 g + i of tile u = queries 32 (u/2) + 8 g + 4 (u%2) + i, key l16 of tile kt
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
+        const bool ok = q0 + qi < N;
+        const float l = lse_s[qi], dd = dsum_s[qi];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[kt][i], c, -l)) : 0.f;
+          const float ds = p * (dp[kt][i] - dd) * tau;
+          pj[kt][u >> 1][4 * (u & 1) + i] = (__bf16)p;
+          sj[kt][u >> 1][4 * (u & 1) + i] = (__bf16)ds;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int trow = dt * 16 + l16;
+        const int ch = j * 4 + g;
+        const int boff = trow * 128 + ((ch ^ t_swz(trow)) * 16);
+        const bf16x8 ot = as_bf16x8(*reinterpret_cast<const u32x4*>(ots + boff));
+        const bf16x8 qtv = as_bf16x8(*reinterpret_cast<const u32x4*>(qts + boff));
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          dvt[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ot, pj[kt][j], dvt[kt][dt], 0, 0, 0);
+          dkt[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtv, sj[kt][j], dkt[kt][dt], 0, 0, 0);
+        }
+      }
+  }
+#undef VDN_DKV_TILE_AT
+#undef VDN_DKV_ISSUE
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = keyk[kt];
+    if (key >= U) continue;
+    float* dkp = slot == 0 ? P.dtext + ((int64_t)key * H + h) * D : P.dk + (((int64_t)(slot - 1) * N + key) * H + h) * D;
+    float* dvp = slot == 0 ? P.dtext + (((int64_t)P.n_text + key) * H + h) * D
+                           : P.dv + (((int64_t)(slot - 1) * N + key) * H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
+      f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
+      *a = *a + dkt[kt][dt];
+      *b = *b + dvt[kt][dt];
     }
   }
 }
@@ -489,10 +687,17 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.Lq = w.Lq;
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
+#if VDN_DKV_WIDE
+    const size_t sm = 2 * DkvWideSmem<D>::STAGE;
+    (void)hipFuncSetAttribute((const void*)softmax_dkv_wide_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sm);
+    hipLaunchKernelGGL(softmax_dkv_wide_kernel<D>, dim3(w.nkblocks, H), dim3(kDkvWaves * 64), sm, st, p);
+#else
     const size_t sm = 2 * DkvSmem<D>::STAGE;
     (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sm);
     hipLaunchKernelGGL(softmax_dkv_mfma_kernel<D>, dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+#endif
   }
   // dQ
   {
