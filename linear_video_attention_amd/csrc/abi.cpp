@@ -399,6 +399,7 @@ vdn_status ensure_backward(vdn_plan* p) {
   const size_t o_part = take((size_t)std::max<int64_t>(splits_all, (int64_t)nslots * H * splits_read) * dd * 4);
   const size_t o_dread = take((size_t)nslots * H * dd * 4);
   const size_t o_z = take((size_t)3 * 2 * T * H * dd * 4);
+  const size_t o_g = take((size_t)2 * (T + 1) * H * dd * 4);
   const size_t o_dal = take((size_t)2 * T * H * d * 4);
   const size_t o_ds0 = take((size_t)2 * H * dd * 4);
   const size_t o_order = take(std::max<size_t>(1, order.size()) * 4), o_ms = take(mslot.size() * 4);
@@ -440,6 +441,8 @@ vdn_status ensure_backward(vdn_plan* p) {
   w.zin = z;
   w.dmf = z + 2 * (int64_t)T * H * dd;
   w.dbf = z + 4 * (int64_t)T * H * dd;
+  w.gsym = reinterpret_cast<float*>(ws + o_g);
+  w.gdb = w.gsym + (int64_t)(T + 1) * H * dd;
   w.dalf = reinterpret_cast<float*>(ws + o_dal);
   w.ds0 = reinterpret_cast<float*>(ws + o_ds0);
   w.order = reinterpret_cast<const int*>(ws + o_order);

@@ -16,9 +16,9 @@
 //   3. frame_states     per (head, direction): the state entering every scanned frame
 //   4. scan_bwd         per (head, direction), frames in reverse scan order: adjoint of each frame
 //                       step -> dM_f, dB_f, dalpha_f and the adjoint of the text state
-//   5. frame_grads      per (frame or text, head): dA = -M dM M, then the token gradients
-//                       dk = beta (dA + dA^T) k + beta dB^T v, dv = beta dB k,
-//                       dbeta = k^T dA k + v^T dB k (text at beta/2)
+//   5. frame_mats       per (frame or text, head): dA = -M^T dM M^T; writes dA + dA^T and dB
+//      token_grads      per (64 tokens, frame or text, head): dk = beta (dA + dA^T) k + beta dB^T v,
+//                       dv = beta dB k, dbeta = k^T dA k + v^T dB k (text at beta/2), as row-block products
 //   6. softmax_dq       per query: P from the saved normaliser, dS = P (dP - D), dq += tau dS K
 //   7. softmax_dkv      per key: over every query row that sees it, dV += P^T do_s, dK += tau dS^T q
 // All gradients are accumulated in fp32 into the caller's fp32 buffers.
@@ -51,6 +51,76 @@ __device__ __forceinline__ void mm_block(FA a, FB b, float (&c)[D / 16][D / 16],
     for (int ii = 0; ii < R; ++ii)
 #pragma unroll
       for (int jj = 0; jj < R; ++jj) c[ii][jj] = fmaf(av[ii], bv[jj], c[ii][jj]);
+  }
+}
+
+// The same product with the right-hand operand b read from global memory (g, d x d row-major)
+// through LDS, 16 rows of k at a time (coalesced loads instead of per-thread strided reads):
+// b(k, j) = g[k d + j], or g[j d + k] when BT.  Every thread of the block must call it; wst holds
+// 16 x D floats.
+template <int D, bool BT, class FA>
+__device__ __forceinline__ void mm_gstage(FA a, const float* __restrict__ g, float (*wst)[D], float (&c)[D / 16][D / 16],
+                                          int ty, int tx) {
+  constexpr int R = D / 16;
+  const int tid = ty * 16 + tx;
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) c[ii][jj] = 0.f;
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += kThreads) {
+      if (BT) {
+        const int kk = e % 16, j = e / 16;
+        wst[kk][j] = g[(int64_t)j * D + k0 + kk];
+      } else {
+        const int kk = e / D, j = e % D;
+        wst[kk][j] = g[(int64_t)(k0 + kk) * D + j];
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[R], bv[R];
+#pragma unroll
+      for (int ii = 0; ii < R; ++ii) av[ii] = a(ty * R + ii, k0 + kk);
+#pragma unroll
+      for (int jj = 0; jj < R; ++jj) bv[jj] = wst[kk][tx * R + jj];
+#pragma unroll
+      for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < R; ++jj) c[ii][jj] = fmaf(av[ii], bv[jj], c[ii][jj]);
+    }
+  }
+}
+
+// c = A b with the left-hand operand from global memory stored transposed: a(i, k) = g[k d + i]
+// (rows of k staged through LDS as above).
+template <int D, class FB>
+__device__ __forceinline__ void mm_gstage_at(const float* __restrict__ g, FB b, float (*wst)[D],
+                                             float (&c)[D / 16][D / 16], int ty, int tx) {
+  constexpr int R = D / 16;
+  const int tid = ty * 16 + tx;
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) c[ii][jj] = 0.f;
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += kThreads) wst[e / D][e % D] = g[(int64_t)(k0 + e / D) * D + e % D];
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[R], bv[R];
+#pragma unroll
+      for (int ii = 0; ii < R; ++ii) av[ii] = wst[kk][ty * R + ii];
+#pragma unroll
+      for (int jj = 0; jj < R; ++jj) bv[jj] = b(k0 + kk, tx * R + jj);
+#pragma unroll
+      for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < R; ++jj) c[ii][jj] = fmaf(av[ii], bv[jj], c[ii][jj]);
+    }
   }
 }
 
@@ -325,6 +395,7 @@ __global__ __launch_bounds__(kThreads) void frame_states_kernel(const float* __r
   constexpr int64_t DD = (int64_t)D * D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float(*z)[D + 1] = reinterpret_cast<float(*)[D + 1]>(smem_raw);                 // current state (rhs)
+  float(*wst)[D] = reinterpret_cast<float(*)[D]>(z + D);                          // staged rows of M_f
   const int h = blockIdx.x, dir = blockIdx.y;
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const float* s0 = states + ((int64_t)Nc * H + h) * DD;
@@ -345,8 +416,7 @@ __global__ __launch_bounds__(kThreads) void frame_states_kernel(const float* __r
     }
     __syncthreads();
     float c[R][R];
-    mm_block<D>([&](int i, int k) { return z[i][k]; }, [&](int k, int j) { return mf[(int64_t)k * D + j]; }, c, ty,
-                tx);
+    mm_gstage<D, false>([&](int i, int k) { return z[i][k]; }, mf, wst, c, ty, tx);
     __syncthreads();
 #pragma unroll
     for (int ii = 0; ii < R; ++ii)
@@ -370,6 +440,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float(*adj)[D + 1] = reinterpret_cast<float(*)[D + 1]>(smem_raw);
   float(*rhs)[D + 1] = adj + D;
+  float(*wst)[D] = reinterpret_cast<float(*)[D]>(rhs + D);                        // staged rows of M_f^T
   const int h = blockIdx.x, dir = blockIdx.y;
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const int* ms = mslot + dir * (Nc + 2);
@@ -398,8 +469,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     // dM = rhs^T adj ;  dR = adj M^T
     float dm[R][R], dr[R][R];
     mm_block<D>([&](int i, int k) { return rhs[k][i]; }, [&](int k, int j) { return adj[k][j]; }, dm, ty, tx);
-    mm_block<D>([&](int i, int k) { return adj[i][k]; }, [&](int k, int j) { return mf[(int64_t)j * D + k]; }, dr,
-                ty, tx);
+    mm_gstage<D, true>([&](int i, int k) { return adj[i][k]; }, mf, wst, dr, ty, tx);
     float* dmo = dmf + (((int64_t)dir * T + f) * H + h) * DD;
     float* dbo = dbf + (((int64_t)dir * T + f) * H + h) * DD;
 #pragma unroll
@@ -433,19 +503,20 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
   for (int e = tid; e < D * D; e += kThreads) o[e] = adj[e / D][e % D];
 }
 
-// ---- 5. per (frame or text, head): dA = -M dM M and the token gradients ----
-template <typename Tin, int D>
-__global__ __launch_bounds__(kThreads) void frame_grads_kernel(
-    const Tin* __restrict__ k, const Tin* __restrict__ v, const float* __restrict__ beta,
-    const Tin* __restrict__ text_kv, const float* __restrict__ minv, const float* __restrict__ bw,
-    const float* __restrict__ dmf, const float* __restrict__ dbf, const float* __restrict__ ds0, int T, int N, int H,
-    int n_text, int anchors, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
-    float* __restrict__ dtext_kv) {
+// ---- 5a. per (frame or text, head): dA + dA^T and dB, with dA = -M^T dM M^T ----
+template <int D>
+__global__ __launch_bounds__(kThreads) void frame_mats_kernel(const float* __restrict__ minv, const float* __restrict__ bw,
+                                                              const float* __restrict__ dmf,
+                                                              const float* __restrict__ dbf,
+                                                              const float* __restrict__ ds0, int T, int H, int n_text,
+                                                              int anchors, float* __restrict__ gsym,
+                                                              float* __restrict__ gdb) {
   constexpr int R = D / 16;
   constexpr int64_t DD = (int64_t)D * D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float(*ga)[D + 1] = reinterpret_cast<float(*)[D + 1]>(smem_raw);   // dM, then dA, then dA + dA^T
   float(*gb)[D + 1] = ga + D;                                         // dB
+  float(*wst)[D] = reinterpret_cast<float(*)[D]>(gb + D);
   const int slot = blockIdx.x, h = blockIdx.y;
   if (slot > 0 && anchors && (slot - 1 == 0 || slot - 1 == T - 1)) return;
   if (slot == 0 && n_text == 0) return;
@@ -478,10 +549,8 @@ __global__ __launch_bounds__(kThreads) void frame_grads_kernel(
     __syncthreads();
     const float* b0 = bw + (int64_t)h * DD;
     float c2[R][R];
-    mm_block<D>([&](int i, int kk) { return ga[i][kk]; }, [&](int kk, int j) { return m[(int64_t)j * D + kk]; }, c,
-                ty, tx);
-    mm_block<D>([&](int i, int kk) { return b0[(int64_t)kk * D + i]; }, [&](int kk, int j) { return ga[kk][j]; }, c2,
-                ty, tx);
+    mm_gstage<D, true>([&](int i, int kk) { return ga[i][kk]; }, m, wst, c, ty, tx);      // dS0 M0^T
+    mm_gstage_at<D>(b0, [&](int kk, int j) { return ga[kk][j]; }, wst, c2, ty, tx);        // B0^T dS0
     __syncthreads();
     put(gb, 1.f);                                       // dB0
 #pragma unroll
@@ -492,13 +561,10 @@ __global__ __launch_bounds__(kThreads) void frame_grads_kernel(
     __syncthreads();
   }
   // dA = -M^T dM M^T, then ga <- dA + dA^T
-  mm_block<D>([&](int i, int kk) { return m[(int64_t)kk * D + i]; }, [&](int kk, int j) { return ga[kk][j]; }, c, ty,
-              tx);
+  mm_gstage_at<D>(m, [&](int kk, int j) { return ga[kk][j]; }, wst, c, ty, tx);
   __syncthreads();
   put(ga, 1.f);
-  __syncthreads();
-  mm_block<D>([&](int i, int kk) { return ga[i][kk]; }, [&](int kk, int j) { return m[(int64_t)j * D + kk]; }, c, ty,
-              tx);
+  mm_gstage<D, true>([&](int i, int kk) { return ga[i][kk]; }, m, wst, c, ty, tx);
   __syncthreads();
   put(ga, -1.f);
   __syncthreads();
@@ -506,11 +572,41 @@ __global__ __launch_bounds__(kThreads) void frame_grads_kernel(
   for (int ii = 0; ii < R; ++ii)
 #pragma unroll
     for (int jj = 0; jj < R; ++jj) c[ii][jj] = ga[ty * R + ii][tx * R + jj] + ga[tx * R + jj][ty * R + ii];
-  __syncthreads();
-  put(ga, 1.f);
-  __syncthreads();
-  // token gradients: one wave per token at a time, lane covers output channels
+  float* gs = gsym + ((int64_t)slot * H + h) * DD;
+  float* gd = gdb + ((int64_t)slot * H + h) * DD;
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) gs[(int64_t)(ty * R + ii) * D + tx * R + jj] = c[ii][jj];
+  for (int e = tid; e < D * D; e += kThreads) gd[e] = gb[e / D][e % D];
+}
+
+// ---- 5b. token gradients, per (64 tokens, frame or text, head), as row-block products ----
+// With G = dA + dA^T:  dk = w (K G + V dB),  dv = w K dB^T,  dbeta = w' (k^T G k / 2 + v^T dB k)
+// (w = beta, or beta/2 for the text; w' = 1 or 1/2), each a 64 x d by d x d product.
+template <int D>
+struct TokSmem {
+  float k[kRows][D + 1], v[kRows][D + 1];
+  float w[kWChunk][D];
+  float red[kRows][16];
+};
+
+template <typename Tin, int D>
+__global__ __launch_bounds__(kThreads) void token_grads_kernel(
+    const Tin* __restrict__ k, const Tin* __restrict__ v, const float* __restrict__ beta,
+    const Tin* __restrict__ text_kv, const float* __restrict__ gsym, const float* __restrict__ gdb, int T, int N,
+    int H, int n_text, int anchors, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
+    float* __restrict__ dtext_kv) {
+  constexpr int RR = kRows / 16, RC = D / 16;
+  constexpr int64_t DD = (int64_t)D * D;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  auto& S = *reinterpret_cast<TokSmem<D>*>(smem_raw);
+  const int slot = blockIdx.y, h = blockIdx.z;
+  if (slot > 0 && anchors && (slot - 1 == 0 || slot - 1 == T - 1)) return;
   const int U = slot == 0 ? n_text : N;
+  const int u0 = blockIdx.x * kRows;
+  if (u0 >= U) return;
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const float wscale = slot == 0 ? 0.5f : 1.0f;
   const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
   const Tin* kb = slot == 0 ? text_kv : k;
@@ -518,29 +614,46 @@ __global__ __launch_bounds__(kThreads) void frame_grads_kernel(
   float* dkb = slot == 0 ? dtext_kv : dk;
   float* dvb = slot == 0 ? dtext_kv + (int64_t)n_text * H * D : dv;
   const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int u = wave; u < U; u += kThreads / 64) {
-    const int64_t off = ((tok0 + u) * H + h) * D;
-    const float w = wscale * beta[(brow0 + u) * H + h];
-    float kdk = 0.f, vdbk = 0.f;
-    for (int i = lane; i < D; i += 64) {
-      float gk = 0.f, gv = 0.f, dsk = 0.f;
-      for (int j = 0; j < D; ++j) {
-        const float kj = to_f32(kb[off + j]), vj = to_f32(vb[off + j]);
-        dsk = fmaf(ga[i][j], kj, dsk);               // (dA + dA^T) k
-        gk = fmaf(gb[j][i], vj, gk);                 // dB^T v
-        gv = fmaf(gb[i][j], kj, gv);                 // dB k
+  auto row_off = [&](int r) { return ((tok0 + u0 + r) * H + h) * D; };
+  for (int e = tid; e < kRows * D; e += kThreads) {
+    const int r = e / D, cc = e % D;
+    const bool ok = u0 + r < U;
+    S.k[r][cc] = ok ? to_f32(kb[row_off(r) + cc]) : 0.f;
+    S.v[r][cc] = ok ? to_f32(vb[row_off(r) + cc]) : 0.f;
+  }
+  __syncthreads();
+  const float* gs = gsym + ((int64_t)slot * H + h) * DD;
+  const float* gd = gdb + ((int64_t)slot * H + h) * DD;
+  float g1[RR][RC], g2[RR][RC], gv[RR][RC];
+  rows_mm<D>(S.k, [&](int kk, int j) { return gs[(int64_t)kk * D + j]; }, S.w, g1, ty, tx);   // K G
+  rows_mm<D>(S.v, [&](int kk, int j) { return gd[(int64_t)kk * D + j]; }, S.w, g2, ty, tx);   // V dB
+  rows_mm<D>(S.k, [&](int kk, int j) { return gd[(int64_t)j * D + kk]; }, S.w, gv, ty, tx);   // K dB^T
+  float part[RR];
+#pragma unroll
+  for (int i = 0; i < RR; ++i) {
+    const int r = ty * RR + i;
+    const bool ok = u0 + r < U;
+    const float wr = ok ? wscale * beta[(brow0 + u0 + r) * H + h] : 0.f;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < RC; ++j) {
+      const int cc = tx * RC + j;
+      acc += 0.5f * S.k[r][cc] * g1[i][j] + S.v[r][cc] * gv[i][j];
+      if (ok) {
+        dkb[row_off(r) + cc] += wr * (g1[i][j] + g2[i][j]);
+        dvb[row_off(r) + cc] += wr * gv[i][j];
       }
-      gk += dsk;
-      const float ki = to_f32(kb[off + i]), vi = to_f32(vb[off + i]);
-      kdk += 0.5f * ki * dsk;                        // k^T dA k = k^T (dA + dA^T) k / 2
-      vdbk += vi * gv;
-      dkb[off + i] += w * gk;
-      dvb[off + i] += w * gv;
     }
-    float s = kdk + vdbk;
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) dbeta[(brow0 + u) * H + h] += wscale * s;
+    part[i] = acc;
+  }
+#pragma unroll
+  for (int i = 0; i < RR; ++i) S.red[ty * RR + i][tx] = part[i];
+  __syncthreads();
+  if (tid < kRows && u0 + tid < U) {
+    float sum = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) sum += S.red[tid][cc];
+    dbeta[(brow0 + u0 + tid) * H + h] += wscale * sum;
   }
 }
 
@@ -709,13 +822,13 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   }
   // 3.-5. linear branch
   if (w.nscan > 0) {
-    const size_t sm1 = (size_t)D * (D + 1) * 4;
+    const size_t sm1 = (size_t)D * (D + 1) * 4 + (size_t)16 * D * 4;
     (void)hipFuncSetAttribute((const void*)frame_states_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm1);
     frame_states_kernel<D><<<dim3(H, 2), kThreads, sm1, st>>>(b.states, b.minv, b.bw, in.alpha, w.order, w.nscan, T, H,
                                                              Nc, w.zin);
   }
   {
-    const size_t sm2 = (size_t)2 * D * (D + 1) * 4;
+    const size_t sm2 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;
     (void)hipFuncSetAttribute((const void*)scan_bwd_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
     scan_bwd_kernel<D><<<dim3(H, 2), kThreads, sm2, st>>>(w.zin, b.minv, b.bw, in.alpha, w.dread, w.mslot, w.order,
                                                          w.nscan, T, H, Nc, w.dmf, w.dbf, w.dalf, w.ds0);
@@ -735,12 +848,16 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
       w.qranges, w.nqranges, T, N, H, s.n_text, tau, o.dk, o.dv, o.dtext_kv);
   }
   {
-    const size_t sm3 = (size_t)2 * D * (D + 1) * 4;
-    (void)hipFuncSetAttribute((const void*)frame_grads_kernel<Tin, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sm3);
-    frame_grads_kernel<Tin, D><<<dim3(T + 1, H), kThreads, sm3, st>>>(
-        (const Tin*)in.k, (const Tin*)in.v, in.beta, (const Tin*)in.text_kv, b.minv, b.bw, w.dmf, w.dbf, w.ds0, T, N, H,
-        s.n_text, s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
+    const size_t sm3 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;
+    (void)hipFuncSetAttribute((const void*)frame_mats_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm3);
+    frame_mats_kernel<D><<<dim3(T + 1, H), kThreads, sm3, st>>>(b.minv, b.bw, w.dmf, w.dbf, w.ds0, T, H, s.n_text,
+                                                               s.anchors, w.gsym, w.gdb);
+    const size_t sm4 = sizeof(TokSmem<D>);
+    (void)hipFuncSetAttribute((const void*)token_grads_kernel<Tin, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sm4);
+    token_grads_kernel<Tin, D><<<dim3((max(N, s.n_text) + kRows - 1) / kRows, T + 1, H), kThreads, sm4, st>>>(
+        (const Tin*)in.k, (const Tin*)in.v, in.beta, (const Tin*)in.text_kv, w.gsym, w.gdb, T, N, H, s.n_text,
+        s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
   }
   // dalpha: sum of both directions
   if (o.dalpha) {

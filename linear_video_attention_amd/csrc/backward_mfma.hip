@@ -463,11 +463,20 @@ struct DqSmem {
   static constexpr int STAGE = 3 * TILE;          // K, V (key-major), K^T
 };
 
-constexpr int kDqQT = 2;                          // 16-query column tiles per wave
-constexpr int kDqBQ = kWaves * 16 * kDqQT;        // queries per workgroup
+// VDN_DQ_WAVES, VDN_DQ_QT: waves per workgroup and 16-query column tiles per wave (8 x 2: two waves
+// per SIMD; 4 x 4: one wave per SIMD, each K, V and K^T fragment read feeding four MFMAs)
+#ifndef VDN_DQ_WAVES
+#define VDN_DQ_WAVES 8
+#endif
+#ifndef VDN_DQ_QT
+#define VDN_DQ_QT 2
+#endif
+constexpr int kDqWaves = VDN_DQ_WAVES;
+constexpr int kDqQT = VDN_DQ_QT;                  // 16-query column tiles per wave
+constexpr int kDqBQ = kDqWaves * 16 * kDqQT;      // queries per workgroup
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 1) void softmax_dq_mfma_kernel(DqParams P) {
+__global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqParams P) {
   using SM = DqSmem<D>;
   constexpr int KS = D / 32, DT = D / 16, KCH = D / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -537,12 +546,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dq_mfma_kernel(DqParam
   const unsigned char* vh = reinterpret_cast<const unsigned char*>(P.vp + (int64_t)h * Ls * D);
   const unsigned char* th = reinterpret_cast<const unsigned char*>(P.kt + (int64_t)h * D * Ls);
   constexpr int R_ROWS_PER_KB = 1024 / (D * 2);
-  constexpr int R_INSTR = SM::TILE / 1024 / kWaves;
+  constexpr int R_INSTR = SM::TILE / 1024 / kDqWaves;
   auto issue_tile = [&](int key0, int stage) {
     unsigned char* base = smem + stage * SM::STAGE;
 #pragma unroll
     for (int i = 0; i < R_INSTR; ++i) {
-      const int blkid = i * kWaves + wave;
+      const int blkid = i * kDqWaves + wave;
       const int row = blkid * R_ROWS_PER_KB + lane / KCH;
       const int c = (lane % KCH) ^ r_swz(row);
       const int64_t off = ((int64_t)(key0 + row) * D + c * 8) * 2;
@@ -551,7 +560,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dq_mfma_kernel(DqParam
     }
 #pragma unroll
     for (int i = 0; i < R_INSTR; ++i) {
-      const int blkid = i * kWaves + wave;
+      const int blkid = i * kDqWaves + wave;
       const int row = blkid * 8 + lane / 8;                    // d row
       const int c = (lane % 8) ^ t_swz(row);
       const int64_t off = ((int64_t)row * Ls + key0 + c * 8) * 2;
@@ -722,7 +731,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     const size_t sm = 2 * DqSmem<D>::STAGE;
     (void)hipFuncSetAttribute((const void*)softmax_dq_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sm);
-    hipLaunchKernelGGL(softmax_dq_mfma_kernel<D>, dim3(p.QT * T * H), dim3(kWaves * 64), sm, st, p);
+    hipLaunchKernelGGL(softmax_dq_mfma_kernel<D>, dim3(p.QT * T * H), dim3(kDqWaves * 64), sm, st, p);
   }
   return hipGetLastError();
 }

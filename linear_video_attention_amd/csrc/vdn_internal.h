@@ -119,6 +119,7 @@ struct BwdBuffers {
   float* partial;                       // [segments][splits][d][d]
   float* dread;                         // [Nc+2][H][d][d] readout adjoints (slots Nc, Nc+1: frames 0, T-1)
   float *zin, *dmf, *dbf;               // [2][T][H][d][d]
+  float *gsym, *gdb;                    // [T+1][H][d][d]: dA + dA^T and dB per slot (0: text)
   float* dalf;                          // [2][T][H][d]
   float* ds0;                           // [2][H][d][d]
   const int* order;                     // [T] scanned frames, forward order
