@@ -13,7 +13,7 @@
 //                       of the weight gradients, and D = rowsum(do_s * o_s)
 //   2. xty_reduce       X^T Y over row segments: the weight gradients (all rows of all heads) and,
 //                       per chunk and head, the readout adjoint sum_i do_l_i q_i^T
-//   3. frame_states     per (head, direction): the state entering every scanned frame
+//   3. frame_states     per (chunk, head, direction): the state entering every scanned frame
 //   4. scan_bwd         per (head, direction), frames in reverse scan order: adjoint of each frame
 //                       step -> dM_f, dB_f, dalpha_f and the adjoint of the text state
 //   5. frame_mats       per (frame or text, head): dA = -M^T dM M^T; writes dA + dA^T and dB
@@ -381,48 +381,66 @@ __global__ __launch_bounds__(kThreads) void xty_reduce_kernel(const float* __res
   out[(int64_t)s * D * D + e] = acc * scale;
 }
 
-// ---- 3. states entering every scanned frame, per (head, direction) ----
-// zin[dir][f][h] = state before frame f is written in direction dir; frames in scan order from
-// `order` (forward order; direction 1 walks it backwards).  S0 = states slot Nc.
+// ---- 3. states entering every scanned frame, per (chunk, head, direction) ----
+// zin[dir][f][h] = state before frame f is written in direction dir.  The forward's chunk states
+// give each chunk its entering state: S_fwd[j] has absorbed the chunks <= j - 2 and S_rev[j] the
+// chunks >= j + 2 (slot Nc: S0), so chunk c starts from S_fwd[c + 1] (forward) or S_rev[c - 1]
+// (reverse); the outermost chunk starts one chunk earlier and walks two.  Boundary frames (anchors
+// on) are never written.
 template <int D>
 __global__ __launch_bounds__(kThreads) void frame_states_kernel(const float* __restrict__ states,
                                                                 const float* __restrict__ minv,
                                                                 const float* __restrict__ bw,
-                                                                const float* __restrict__ alpha,
-                                                                const int* __restrict__ order, int nscan, int T,
-                                                                int H, int Nc, float* __restrict__ zin) {
+                                                                const float* __restrict__ alpha, int T, int C,
+                                                                int anchors, int H, int Nc, float* __restrict__ zin) {
   constexpr int R = D / 16;
   constexpr int64_t DD = (int64_t)D * D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float(*z)[D + 1] = reinterpret_cast<float(*)[D + 1]>(smem_raw);                 // current state (rhs)
   float(*wst)[D] = reinterpret_cast<float(*)[D]>(z + D);                          // staged rows of M_f
-  const int h = blockIdx.x, dir = blockIdx.y;
+  const int c = blockIdx.x, h = blockIdx.y, dir = blockIdx.z;
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  const float* s0 = states + ((int64_t)Nc * H + h) * DD;
+  // start slot and the frames to walk, [f_first, f_last] in walking order
+  int slot, f_first, f_last;
+  if (dir == 0) {
+    slot = min(c + 1, Nc - 1);
+    f_first = max(slot - 1, 0) * C;
+    f_last = min((c + 1) * C, T) - 1;
+  } else {
+    slot = max(c - 1, 0);
+    f_first = min((slot + 2) * C, T) - 1;
+    f_last = c * C;
+  }
+  const float* s0 = states + ((int64_t)(dir * (Nc + 1) + slot) * H + h) * DD;
   for (int e = tid; e < D * D; e += kThreads) z[e / D][e % D] = s0[e];
   __syncthreads();
-  for (int m = 0; m < nscan; ++m) {
-    const int f = order[dir == 0 ? m : nscan - 1 - m];
-    float* zo = zin + (((int64_t)dir * T + f) * H + h) * DD;
-    for (int e = tid; e < D * D; e += kThreads) zo[e] = z[e / D][e % D];
-    // rhs = Z Diag(alpha_f) + B_f, then Z <- rhs M_f
-    const float* af = alpha ? alpha + ((int64_t)f * H + h) * D : nullptr;
-    const float* bf = bw + ((int64_t)(1 + f) * H + h) * DD;
-    const float* mf = minv + ((int64_t)(1 + f) * H + h) * DD;
-    __syncthreads();
-    for (int e = tid; e < D * D; e += kThreads) {
-      const int r = e / D, c = e % D;
-      z[r][c] = z[r][c] * (af ? af[c] : 1.f) + bf[e];
+  const int step = dir == 0 ? 1 : -1;
+  for (int f = f_first;; f += step) {
+    const bool bnd = anchors && (f == 0 || f == T - 1);
+    if (!bnd) {
+      if (f / C == c) {
+        float* zo = zin + (((int64_t)dir * T + f) * H + h) * DD;
+        for (int e = tid; e < D * D; e += kThreads) zo[e] = z[e / D][e % D];
+      }
+      // rhs = Z Diag(alpha_f) + B_f, then Z <- rhs M_f
+      const float* af = alpha ? alpha + ((int64_t)f * H + h) * D : nullptr;
+      const float* bf = bw + ((int64_t)(1 + f) * H + h) * DD;
+      const float* mf = minv + ((int64_t)(1 + f) * H + h) * DD;
+      __syncthreads();
+      for (int e = tid; e < D * D; e += kThreads) {
+        const int r = e / D, cc = e % D;
+        z[r][cc] = z[r][cc] * (af ? af[cc] : 1.f) + bf[e];
+      }
+      float cm[R][R];
+      mm_gstage<D, false>([&](int i, int k) { return z[i][k]; }, mf, wst, cm, ty, tx);
+      __syncthreads();
+#pragma unroll
+      for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < R; ++jj) z[ty * R + ii][tx * R + jj] = cm[ii][jj];
+      __syncthreads();
     }
-    __syncthreads();
-    float c[R][R];
-    mm_gstage<D, false>([&](int i, int k) { return z[i][k]; }, mf, wst, c, ty, tx);
-    __syncthreads();
-#pragma unroll
-    for (int ii = 0; ii < R; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < R; ++jj) z[ty * R + ii][tx * R + jj] = c[ii][jj];
-    __syncthreads();
+    if (f == f_last) break;
   }
 }
 
@@ -824,8 +842,8 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   if (w.nscan > 0) {
     const size_t sm1 = (size_t)D * (D + 1) * 4 + (size_t)16 * D * 4;
     (void)hipFuncSetAttribute((const void*)frame_states_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm1);
-    frame_states_kernel<D><<<dim3(H, 2), kThreads, sm1, st>>>(b.states, b.minv, b.bw, in.alpha, w.order, w.nscan, T, H,
-                                                             Nc, w.zin);
+    frame_states_kernel<D><<<dim3(Nc, H, 2), kThreads, sm1, st>>>(b.states, b.minv, b.bw, in.alpha, T, s.C, s.anchors,
+                                                                 H, Nc, w.zin);
   }
   {
     const size_t sm2 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;
