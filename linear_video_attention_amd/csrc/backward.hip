@@ -15,7 +15,8 @@
 //                       per chunk and head, the readout adjoint sum_i do_l_i q_i^T
 //   3. frame_states     per (chunk, head, direction): the state entering every scanned frame
 //   4. scan_bwd         per (head, direction), frames in reverse scan order: adjoint of each frame
-//                       step -> dM_f, dB_f, dalpha_f and the adjoint of the text state
+//                       step -> dB_f and the adjoint after the write, and the text state's adjoint
+//      frame_dm         per (scanned frame, head, direction): dM_f and dalpha_f from that adjoint
 //   5. frame_mats       per (frame or text, head): dA = -M^T dM M^T; writes dA + dA^T and dB
 //      token_grads      per (64 tokens, frame or text, head): dk = beta (dA + dA^T) k + beta dB^T v,
 //                       dv = beta dB k, dbeta = k^T dA k + v^T dB k (text at beta/2), as row-block products
@@ -476,49 +477,72 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     add_reads(m);
     const int f = order[dir == 0 ? m - 1 : nscan - m];
     const float* af = alpha ? alpha + ((int64_t)f * H + h) * D : nullptr;
-    const float* zf = zin + (((int64_t)dir * T + f) * H + h) * DD;
-    const float* bf = bw + ((int64_t)(1 + f) * H + h) * DD;
     const float* mf = minv + ((int64_t)(1 + f) * H + h) * DD;
-    for (int e = tid; e < D * D; e += kThreads) {
-      const int r = e / D, c = e % D;
-      rhs[r][c] = zf[e] * (af ? af[c] : 1.f) + bf[e];
-    }
-    __syncthreads();
-    // dM = rhs^T adj ;  dR = adj M^T
-    float dm[R][R], dr[R][R];
-    mm_block<D>([&](int i, int k) { return rhs[k][i]; }, [&](int k, int j) { return adj[k][j]; }, dm, ty, tx);
+    // dR = adj M^T (dB_f = dR); the adjoint after the write is kept for frame_dm (dM, dalpha)
+    float dr[R][R];
     mm_gstage<D, true>([&](int i, int k) { return adj[i][k]; }, mf, wst, dr, ty, tx);
     float* dmo = dmf + (((int64_t)dir * T + f) * H + h) * DD;
     float* dbo = dbf + (((int64_t)dir * T + f) * H + h) * DD;
+    for (int e = tid; e < D * D; e += kThreads) dmo[e] = adj[e / D][e % D];
+#pragma unroll
+    for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < R; ++jj) dbo[(int64_t)(ty * R + ii) * D + tx * R + jj] = dr[ii][jj];
+    __syncthreads();                               // everyone is done with adj
+    // adj <- dR Diag(alpha)
 #pragma unroll
     for (int ii = 0; ii < R; ++ii)
 #pragma unroll
       for (int jj = 0; jj < R; ++jj) {
-        const int64_t e = (int64_t)(ty * R + ii) * D + tx * R + jj;
-        dmo[e] = dm[ii][jj];
-        dbo[e] = dr[ii][jj];
+        const int cc = tx * R + jj;
+        adj[ty * R + ii][cc] = dr[ii][jj] * (af ? af[cc] : 1.f);
       }
-    __syncthreads();                               // everyone is done with adj and rhs
-    // adj <- dR Diag(alpha); rhs <- Z * dR for the alpha gradient (column sums)
-#pragma unroll
-    for (int ii = 0; ii < R; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < R; ++jj) {
-        const int r = ty * R + ii, c = tx * R + jj;
-        adj[r][c] = dr[ii][jj] * (af ? af[c] : 1.f);
-        rhs[r][c] = zf[(int64_t)r * D + c] * dr[ii][jj];
-      }
-    __syncthreads();
-    if (dalf && tid < D) {
-      float s = 0.f;
-      for (int r = 0; r < D; ++r) s += rhs[r][tid];
-      dalf[(((int64_t)dir * T + f) * H + h) * D + tid] = s;
-    }
     __syncthreads();
   }
   add_reads(0);
   float* o = ds0 + ((int64_t)dir * H + h) * DD;
   for (int e = tid; e < D * D; e += kThreads) o[e] = adj[e / D][e % D];
+}
+
+// ---- 4b. per (scanned frame, head, direction): dM = R^T adj and dalpha = diag(Z^T dR) ----
+// R = Z Diag(alpha_f) + B_f with Z the state entering the frame; adj (the adjoint after the write,
+// left in dmf by scan_bwd) is replaced by dM.
+template <int D>
+__global__ __launch_bounds__(kThreads) void frame_dm_kernel(const float* __restrict__ zin, const float* __restrict__ bw,
+                                                            const float* __restrict__ alpha, int T, int H, int anchors,
+                                                            float* __restrict__ dmf, const float* __restrict__ dbf,
+                                                            float* __restrict__ dalf) {
+  constexpr int R = D / 16;
+  constexpr int64_t DD = (int64_t)D * D;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  float(*adj)[D + 1] = reinterpret_cast<float(*)[D + 1]>(smem_raw);
+  float(*rhs)[D + 1] = adj + D;
+  const int f = blockIdx.x, h = blockIdx.y, dir = blockIdx.z;
+  if (anchors && (f == 0 || f == T - 1)) return;
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const float* af = alpha ? alpha + ((int64_t)f * H + h) * D : nullptr;
+  const int64_t slot = ((int64_t)dir * T + f) * H + h;
+  const float* zf = zin + slot * DD;
+  const float* bf = bw + ((int64_t)(1 + f) * H + h) * DD;
+  float* dmo = dmf + slot * DD;
+  for (int e = tid; e < D * D; e += kThreads) {
+    const int r = e / D, cc = e % D;
+    adj[r][cc] = dmo[e];
+    rhs[r][cc] = zf[e] * (af ? af[cc] : 1.f) + bf[e];
+  }
+  __syncthreads();
+  float dm[R][R];
+  mm_block<D>([&](int i, int k) { return rhs[k][i]; }, [&](int k, int j) { return adj[k][j]; }, dm, ty, tx);
+#pragma unroll
+  for (int ii = 0; ii < R; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < R; ++jj) dmo[(int64_t)(ty * R + ii) * D + tx * R + jj] = dm[ii][jj];
+  if (dalf && tid < D) {
+    const float* dr = dbf + slot * DD;
+    float acc = 0.f;
+    for (int r = 0; r < D; ++r) acc = fmaf(zf[(int64_t)r * D + tid], dr[(int64_t)r * D + tid], acc);
+    dalf[slot * D + tid] = acc;
+  }
 }
 
 // ---- 5a. per (frame or text, head): dA + dA^T and dB, with dA = -M^T dM M^T ----
@@ -811,6 +835,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   zero(o.dv, (int64_t)T * N * H * D);
   zero(o.dbeta, ((int64_t)s.n_text + (int64_t)T * N) * H);
   zero(o.dtext_kv, (int64_t)2 * s.n_text * H * D);
+  if (o.dalpha) zero(w.dalf, (int64_t)2 * T * H * D);   // frames never written (boundary) keep zero
   // 1. merge backward
   {
     const size_t sm = merge_smem<D>();
@@ -850,6 +875,12 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     (void)hipFuncSetAttribute((const void*)scan_bwd_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
     scan_bwd_kernel<D><<<dim3(H, 2), kThreads, sm2, st>>>(w.zin, b.minv, b.bw, in.alpha, w.dread, w.mslot, w.order,
                                                          w.nscan, T, H, Nc, w.dmf, w.dbf, w.dalf, w.ds0);
+    if (w.nscan > 0) {
+      const size_t smd = (size_t)2 * D * (D + 1) * 4;
+      (void)hipFuncSetAttribute((const void*)frame_dm_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smd);
+      frame_dm_kernel<D><<<dim3(T, H, 2), kThreads, smd, st>>>(w.zin, b.bw, in.alpha, T, H, s.anchors, w.dmf, w.dbf,
+                                                               w.dalf);
+    }
   }
   // 6.-7. softmax branch (dq adds to the merge part, dk/dv/dtext start from zero)
   if (mfma_softmax) {
