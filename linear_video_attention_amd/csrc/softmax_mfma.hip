@@ -52,6 +52,11 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 //   VDN_SOFTMAX_BK      keys per LDS tile (64; 128 halves the barriers but is 3 % slower)
 //   VDN_SOFTMAX_DOT2SUM 1: the normaliser from the bf16-rounded weights by v_dot2c_f32_bf16 instead
 //                       of fp32 adds (4 % slower: the sums wait for the conversions)
+//   VDN_SOFTMAX_PRESCALE 1: the first launch takes the queries as bf16(c q) (c = log2(e)/sqrt(d)) and
+//                       starts each score accumulator at -mref, so a weight is exp2 of the
+//                       accumulator with no multiply-add; the extra rounding of c q moves a score by
+//                       at most 2^-9 |c q.k| <= 2^-9 mref, so rows whose bound mref exceeds 4 (log2
+//                       units) are left to the second launch, which keeps the unscaled arithmetic
 #ifndef VDN_SOFTMAX_WAVES
 #define VDN_SOFTMAX_WAVES 8
 #endif
@@ -67,6 +72,9 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 #ifndef VDN_SOFTMAX_DOT2SUM
 #define VDN_SOFTMAX_DOT2SUM 0
 #endif
+#ifndef VDN_SOFTMAX_PRESCALE
+#define VDN_SOFTMAX_PRESCALE 1
+#endif
 constexpr int kBK = VDN_SOFTMAX_BK;  // keys per tile (64 or 128)
 static_assert(kBK == 64 || kBK == 128, "key tile");
 constexpr int kWaves = VDN_SOFTMAX_WAVES;       // waves per workgroup; 8 / kWaves workgroups per CU
@@ -75,7 +83,7 @@ constexpr int kQW = 16 * kQT;       // queries per wave
 constexpr int kBQ = kWaves * kQW;   // queries per workgroup
 constexpr int kStages = VDN_SOFTMAX_STAGES;     // LDS stages: up to kStages - 1 tiles in flight
 static_assert(kStages >= 2 && kStages <= 4, "LDS stages");
-constexpr float kMaxRef = 48.0f;            // log2 units; beyond it the fallback kernel runs
+constexpr float kMaxRef = VDN_SOFTMAX_PRESCALE ? 4.0f : 48.0f;   // log2 units; beyond it the fallback kernel runs
 constexpr float kRescaleThreshold = 8.0f;   // fallback: log2 units of growth before a rescale
 constexpr float kMasked = -1.0e30f;
 constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
@@ -201,6 +209,14 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
       mref[j] = sqrtf(s2) * kmax * c_log2;
       unsafe |= !(mref[j] <= kMaxRef);
     }
+    if constexpr (!FALLBACK && VDN_SOFTMAX_PRESCALE) {
+#pragma unroll
+      for (int j = 0; j < kQT; ++j)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[j][ks][e] = (__bf16)((float)qf[j][ks][e] * c_log2);
+    }
     if constexpr (!FALLBACK) {
       if (tid == 0) unsafe_any = 0;
       __syncthreads();
@@ -310,10 +326,12 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
         kf[u][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz(row)) * 16)));
       }
     }
+    constexpr bool kPre = !FALLBACK && VDN_SOFTMAX_PRESCALE;   // accumulators start at -mref
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < kQT; ++j) sacc[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kQT; ++j)
+        sacc[u][j] = kPre ? f32x4{-mref[j], -mref[j], -mref[j], -mref[j]} : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -378,7 +396,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(P
         for (int i = 0; i < 4; ++i) {
           // raw v_exp_f32: results below 2^-126 flush to zero, harmless since the largest term of
           // every query is >= 2^-96 (fixed reference) or 1 (online maximum)
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[u][j][i], c_log2, -mref[j]));
+          const float p = (!FALLBACK && VDN_SOFTMAX_PRESCALE) ? __builtin_amdgcn_exp2f(sacc[u][j][i])
+                                                              : __builtin_amdgcn_exp2f(fmaf(sacc[u][j][i], c_log2, -mref[j]));
 #if !VDN_SOFTMAX_DOT2SUM
           ls += p;
 #endif
