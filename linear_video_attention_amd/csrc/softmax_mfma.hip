@@ -24,9 +24,10 @@
 //     taken straight from the score registers;
 //   * exponent reference: softmax is invariant to the offset subtracted from the scores, and
 //     |q.k| <= |q| max|k| bounds every score of the query, so p = 2^(s c - |q| kmax c) never
-//     exceeds 1 and needs no running maximum or accumulator rescale.  Workgroups whose bound could
-//     underflow (|q| kmax c > 48 in log2 units) flag themselves and a second launch of the same
-//     kernel with the classic online maximum redoes just those;
+//     exceeds 1 and needs no running maximum or accumulator rescale.  Workgroups holding a row
+//     whose bound |q| kmax c exceeds 4 log2 units (the limit of the query prescale below; 48 without
+//     it, against underflow) flag themselves and a second launch of the same kernel with the
+//     classic online maximum and unscaled queries redoes just those;
 //   * workgroup order: context query rows (every key) first, then the boundary frames, then the
 //     interior frames remapped so that consecutive query tiles -- which share their key window --
 //     land on the same XCD (workgroups are dispatched round-robin over the 8 XCDs).
