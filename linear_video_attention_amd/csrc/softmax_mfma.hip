@@ -53,6 +53,9 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 //   VDN_SOFTMAX_BK      keys per LDS tile (64; 128 halves the barriers but is 3 % slower)
 //   VDN_SOFTMAX_DOT2SUM 1: the normaliser from the bf16-rounded weights by v_dot2c_f32_bf16 instead
 //                       of fp32 adds (4 % slower: the sums wait for the conversions)
+//   VDN_SOFTMAX_QT, VDN_SOFTMAX_WG_PER_CU: query tiles per wave and the occupancy hint (3 and
+//                       8 / waves; 4 waves x 4 or 5 tiles at one wave per SIMD, 404 / 492 registers,
+//                       measured 27-33 % slower: the lone wave cannot hide its own exponentials)
 //   VDN_SOFTMAX_PRESCALE 1: the first launch takes the queries as bf16(c q) (c = log2(e)/sqrt(d)) and
 //                       starts each score accumulator at -mref, so a weight is exp2 of the
 //                       accumulator with no multiply-add; the extra rounding of c q moves a score by
@@ -79,7 +82,13 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 constexpr int kBK = VDN_SOFTMAX_BK;  // keys per tile (64 or 128)
 static_assert(kBK == 64 || kBK == 128, "key tile");
 constexpr int kWaves = VDN_SOFTMAX_WAVES;       // waves per workgroup; 8 / kWaves workgroups per CU
-constexpr int kQT = 3;              // 16-query column tiles per wave
+#ifndef VDN_SOFTMAX_QT
+#define VDN_SOFTMAX_QT 3
+#endif
+#ifndef VDN_SOFTMAX_WG_PER_CU
+#define VDN_SOFTMAX_WG_PER_CU (8 / VDN_SOFTMAX_WAVES)
+#endif
+constexpr int kQT = VDN_SOFTMAX_QT; // 16-query column tiles per wave
 constexpr int kQW = 16 * kQT;       // queries per wave
 constexpr int kBQ = kWaves * kQW;   // queries per workgroup
 constexpr int kStages = VDN_SOFTMAX_STAGES;     // LDS stages: up to kStages - 1 tiles in flight
@@ -129,7 +138,7 @@ struct Params {
 // FALLBACK = false: fixed exponent reference, writes its workgroup's flag (1 = redo).
 // FALLBACK = true : online maximum; runs only the workgroups flagged by the first launch.
 template <int D, bool FALLBACK>
-__global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void softmax_mfma_kernel(Params P) {
+__global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mfma_kernel(Params P) {
   using SM = Smem<D>;
   constexpr int KS = D / 32;          // k-steps of the QK^T contraction
   constexpr int DT = D / 16;          // 16-row d tiles of O^T
