@@ -254,6 +254,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
 // the LDS reads per MFMA of the 16-key layout, and the tile's normalisers and D values come
 // through LDS with the tile instead of per-element global loads.
 constexpr int kDkvWaves = 4;
+// VDN_DKV_FOLD 1: keys enter as bf16(c k) and the score and dP accumulators start at -lse and -D
+#ifndef VDN_DKV_FOLD
+#define VDN_DKV_FOLD 1
+#endif
 #ifndef VDN_DKV_MINBLOCKS
 #define VDN_DKV_MINBLOCKS 1
 #endif
@@ -289,6 +293,10 @@ __global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv
     for (int ks = 0; ks < KS; ++ks) {
       kf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
       vf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
+#if VDN_DKV_FOLD
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[kt][ks][e] = (__bf16)((float)kf[kt][ks][e] * P.c);
+#endif
     }
   }
   f32x4 dvt[2][DT], dkt[2][DT];
@@ -375,10 +383,25 @@ __global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       f32x4 sc[2], dp[2];
+#if VDN_DKV_FOLD
+      // accumulators start at -lse and -D of the lane's four query rows
+      f32x4 l0, d0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
+        l0[i] = -lse_s[qi];
+        d0[i] = -dsum_s[qi];
+      }
+#endif
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+#if VDN_DKV_FOLD
+        sc[kt] = l0;
+        dp[kt] = d0;
+#else
         sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#endif
       }
       const int row = perm_row(u, l16);
 #pragma unroll
@@ -398,11 +421,18 @@ __global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv
       for (int i = 0; i < 4; ++i) {
         const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
         const bool ok = q0 + qi < N;
+#if !VDN_DKV_FOLD
         const float l = lse_s[qi], dd = dsum_s[qi];
+#endif
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
+#if VDN_DKV_FOLD
+          const float p = ok ? __builtin_amdgcn_exp2f(sc[kt][i]) : 0.f;
+          const float ds = p * dp[kt][i];                       // tau applied to dK at the end
+#else
           const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[kt][i], c, -l)) : 0.f;
           const float ds = p * (dp[kt][i] - dd) * tau;
+#endif
           pj[kt][u >> 1][4 * (u & 1) + i] = (__bf16)p;
           sj[kt][u >> 1][4 * (u & 1) + i] = (__bf16)ds;
         }
@@ -437,7 +467,11 @@ __global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv
     for (int dt = 0; dt < DT; ++dt) {
       f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
       f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
+#if VDN_DKV_FOLD
+      *a = *a + dkt[kt][dt] * tau;
+#else
       *a = *a + dkt[kt][dt];
+#endif
       *b = *b + dvt[kt][dt];
     }
   }
@@ -467,6 +501,11 @@ struct DqSmem {
 // per SIMD; 4 x 4: one wave per SIMD, each K, V and K^T fragment read feeding four MFMAs)
 #ifndef VDN_DQ_WAVES
 #define VDN_DQ_WAVES 8
+#endif
+// VDN_DQ_FOLD 1: queries enter as bf16(c q) and the score and dP accumulators start at -lse and -D,
+// so dS = exp2(S') dP' needs no multiply-adds (tau is applied once to dQ)
+#ifndef VDN_DQ_FOLD
+#define VDN_DQ_FOLD 1
 #endif
 #ifndef VDN_DQ_QT
 #define VDN_DQ_QT 2
@@ -498,6 +537,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     for (int ks = 0; ks < KS; ++ks) {
       qf[j][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q + rr * D + ks * 32 + g * 8));
       of[j][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.dout + rr * D + ks * 32 + g * 8));
+#if VDN_DQ_FOLD
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[j][ks][e] = (__bf16)((float)qf[j][ks][e] * P.c);
+#endif
     }
     lse[j] = P.lse[rr];
     dsm[j] = P.dsum[rr];
@@ -597,8 +640,13 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
         f32x4 s[kDqQT], dp[kDqQT];
 #pragma unroll
         for (int j = 0; j < kDqQT; ++j) {
+#if VDN_DQ_FOLD
+          s[j] = f32x4{-lse[j], -lse[j], -lse[j], -lse[j]};
+          dp[j] = f32x4{-dsm[j], -dsm[j], -dsm[j], -dsm[j]};
+#else
           s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#endif
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -620,8 +668,12 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
             const int kl = half * 32 + 8 * g + 4 * u + i;
             float ds = 0.f;
             if (kl < valid && qv[j]) {
+#if VDN_DQ_FOLD
+              ds = __builtin_amdgcn_exp2f(s[j][i]) * dp[j][i];     // tau applied to dQ at the end
+#else
               const float p = exp2f(s[j][i] * c - lse[j]);
               ds = p * (dp[j][i] - dsm[j]) * tau;
+#endif
             }
             dsf[j][4 * u + i] = (__bf16)ds;
           }
@@ -645,7 +697,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       f32x4* a = reinterpret_cast<f32x4*>(dqp + dt * 16 + g * 4);
+#if VDN_DQ_FOLD
+      *a = *a + dqt[dt][j] * tau;
+#else
       *a = *a + dqt[dt][j];
+#endif
     }
   }
 }
