@@ -6,12 +6,14 @@
 // pages run their production kernels with FP8 (section "Adapting the Pretrained H3 backbone") but
 // do not fix its roundings.  The roundings made here, each a deterministic step:
 //   * operands: K8 = e4m3(s_k k), V8 = e4m3(s_v v) (power-of-two scales per head, packed by
-//     prep_fp8.hip), Q8 = e4m3(s_q q) with s_q = 2^(8 - e) from the query's own largest |q_i|;
-//   * scores x = <Q8, K8> / (s_q s_k) on v_mfma_f32_16x16x128_f8f6f4 (fp32 accumulate);
-//   * weights P8 = e4m3(2^(8 + c x - m)), c = log2(e)/sqrt(d), with the offset m = c |q| kmax when
-//     that bound is <= 4 (then the largest weight of every row is >= 1, far above E4M3's
-//     underflow), else the row's exact maximum c max x (a second launch of this kernel, for the
-//     workgroups that hold such rows, first scans the row's scores for it);
+//     prep_fp8.hip), Q8 = e4m3(s_q c q) with c = log2(e)/sqrt(d) and s_q = 2^(8 - e) from the
+//     largest |c q_i| of the query;
+//   * scores x = <Q8, K8> / (s_q s_k), already in log2 units, on v_mfma_scale_f32_16x16x128_f8f6f4
+//     (the E8M0 block scales divide by s_k and s_q; fp32 accumulate, started at 8 - m);
+//   * weights P8 = e4m3(2^(8 + x - m)) with the offset m = c |q| kmax when that bound is <= 4
+//     (then the largest weight of every row is >= 1, far above E4M3's underflow), else the row's
+//     exact maximum max x (a second launch of this kernel, for the workgroups that hold such rows,
+//     first scans the row's scores for it); a weight is exp2 of the accumulator;
 //   * o = sum P8 V8 / (s_v sum P8): the normaliser sums the rounded weights, on the matrix cores
 //     (a constant all-ones A operand next to the V^T tiles), and o_s is stored in bf16.
 //
@@ -77,6 +79,11 @@ __device__ __forceinline__ float pow2_scale(float m) {
 
 __device__ __forceinline__ f32x4 mfma8(const i32x8& a, const i32x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// scores of the c-scaled query in log2 units: (K8 . Q8) 2^(ea - 127) 2^(eb - 127) + c0
+__device__ __forceinline__ f32x4 mfma8_scaled(const i32x8& a, const i32x8& b, const f32x4& c0, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c0, 0, 0, 0, ea, 0, eb);
 }
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
@@ -181,6 +188,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
   const bf16_t* qsrc = ctx ? P.qc + (int64_t)h * D : P.q + ((int64_t)t * P.N * H + h) * D;
   bf16_t* odst = ctx ? P.oc + (int64_t)h * D : P.o_s + ((int64_t)t * P.N * H + h) * D;
   const float sk = P.scale[2 * h], sv = P.scale[2 * h + 1];
+  const int ekey = 127 - ilogbf(sk);              // E8M0 exponent dividing the scores by s_k
   const float kmax = P.kmax[h];
 
   const int tid = threadIdx.x;
@@ -189,7 +197,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
 
   // ---- Q8 fragments: query l16 of tile j, channels 32 g .. 32 g + 31 ----
   i32x8 qf[kQT];
-  float cq[kQT], moff[kQT];      // per query: score multiplier and exponent offset (minus the shift)
+  int escale[kQT];               // per query: E8M0 exponent dividing the scores by s_q
+  float moff[kQT];               // per query: exponent offset minus the shift
   bool over[kQT];                // the query's bound exceeds the limit
   const int n_base = qt * kBQ + wave * kQW;
   bool unsafe = false;
@@ -213,8 +222,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
       }
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      amax = fmaxf(amax, fabsf(x[i]));
       ss += x[i] * x[i];
+      x[i] *= P.c_log2;                          // the query enters as c q
+      amax = fmaxf(amax, fabsf(x[i]));
     }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
@@ -227,7 +237,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
       wv = __builtin_amdgcn_cvt_pk_fp8_f32(sq * x[4 * i + 2], sq * x[4 * i + 3], wv, true);
       qf[j][i] = wv;
     }
-    cq[j] = P.c_log2 / (sq * sk);
+    escale[j] = 127 - ilogbf(sq);
     const float bound = sqrtf(ss) * kmax * P.c_log2;
     over[j] = !(bound <= kBoundLimit);
     unsafe |= over[j];
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
         const i32x8 kf = kfrag(kb, u);
 #pragma unroll
         for (int j = 0; j < kQT; ++j) {
-          const f32x4 s = mfma8(kf, qf[j], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 s = mfma8_scaled(kf, qf[j], f32x4{0.f, 0.f, 0.f, 0.f}, ekey, escale[j]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (32 * g + 4 * u + i < valid) mx[j] = fmaxf(mx[j], s[i]);
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
     for (int j = 0; j < kQT; ++j) {
       float m = fmaxf(mx[j], __shfl_xor(mx[j], 16));
       m = fmaxf(m, __shfl_xor(m, 32));
-      if (over[j]) moff[j] = m * cq[j] - kShift;
+      if (over[j]) moff[j] = m - kShift;
     }
   }
 
@@ -375,7 +385,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
 #pragma unroll
       for (int uu = 0; uu < kUG; ++uu)
 #pragma unroll
-        for (int j = 0; j < kQT; ++j) s[uu][j] = mfma8(kf[uu], qf[j], f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int j = 0; j < kQT; ++j)
+          s[uu][j] = mfma8_scaled(kf[uu], qf[j], f32x4{-moff[j], -moff[j], -moff[j], -moff[j]}, ekey, escale[j]);
 #pragma unroll
       for (int uu = 0; uu < kUG; ++uu) {
         const int u = kUG * up + uu;
@@ -390,7 +401,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
         for (int j = 0; j < kQT; ++j) {
           float p[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[uu][j][i], cq[j], -moff[j]));
+          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[uu][j][i]);
           int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
           pf[j][u] = wv;

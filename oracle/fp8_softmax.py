@@ -18,15 +18,15 @@ Definition, per head h, for a video query row q with key set J (global keys, win
 
 * power-of-two scales: scale(m) = 2^(8 - e) for a largest magnitude m = f 2^e, f in [0.5, 1)
   (scale(0) = 1), so the scaled values stay below 256.  s_k = scale(max |k|) and s_v =
-  scale(max |v|) over every key and value of the head (global and video), s_q = scale(max |q|)
-  per query row;
-* K8 = e4m3(s_k k), V8 = e4m3(s_v v), Q8 = e4m3(s_q q);
+  scale(max |v|) over every key and value of the head (global and video);
+* the query enters multiplied by c = log2(e) / sqrt(d), so that scores come out in log2 units:
+  s_q = scale(max |c q|) per query row, Q8 = e4m3(s_q c q); K8 = e4m3(s_k k), V8 = e4m3(s_v v);
 * scores x_j = <Q8, K8_j> / (s_q s_k) (exact);
-* exponent offset: with c = log2(e) / sqrt(d) and the bound b = c |q| kmax (kmax the largest key
-  norm of the head, |q| the query's norm), m = b when b <= 4, else m = c max_{j in J} x_j.  (Any
-  offset gives the exact softmax; after rounding it matters, so it is part of the definition.
-  With b <= 4 every row's largest term 2^(8 + c x - m) is at least 1.)
-* P8_j = e4m3(2^(8 + c x_j - m));
+* exponent offset: with the bound b = c |q| kmax (kmax the largest key norm of the head, |q| the
+  query's norm), m = b when b <= 4, else m = max_{j in J} x_j.  (Any offset gives the exact
+  softmax; after rounding it matters, so it is part of the definition.  With b <= 4 every row's
+  largest term 2^(8 + x - m) is at least 1.)
+* P8_j = e4m3(2^(8 + x_j - m));
 * o = sum_j P8_j V8_j / (s_v sum_j P8_j).
 
 The normaliser sums the same rounded weights that multiply the values, so o is a convex
@@ -90,19 +90,19 @@ def softmax_rows_rounded(qr, k8, v8, s_k, s_v, kmax) -> np.ndarray:
     c = math.log2(math.e) / math.sqrt(d)
     out = np.zeros(qr.shape)
     for i, q in enumerate(qr):
-        s_q = pow2_scale(np.abs(q).max())
-        x = (k8 @ e4m3(s_q * q)) / (s_q * s_k)
+        s_q = pow2_scale(np.abs(c * q).max())
+        x = (k8 @ e4m3(s_q * c * q)) / (s_q * s_k)
         b = c * math.sqrt(float(q @ q)) * kmax
-        m = b if b <= OFFSET_BOUND_LIMIT else c * x.max()
-        p8 = e4m3(np.exp2(P_SHIFT + c * x - m))
+        m = b if b <= OFFSET_BOUND_LIMIT else x.max()
+        p8 = e4m3(np.exp2(P_SHIFT + x - m))
         out[i] = (p8 @ v8) / (s_v * p8.sum())
     return out
 
 
 def ambiguous_rounding_effect(qr, keys, vals, s_k, s_v, kmax, rel_score_err=2.0 ** -16) -> np.ndarray:
     """Per query row, how far o may move when the scores carry a relative error: a weight P8_j can
-    round to the other side of an E4M3 midpoint only if its exponent 8 + c x_j - m lies within
-    delta_j = c rel_score_err sum_i |Q8_i K8_ji| / (s_q s_k) (+ a float32 rounding of the
+    round to the other side of an E4M3 midpoint only if its exponent 8 + x_j - m lies within
+    delta_j = rel_score_err sum_i |Q8_i K8_ji| / (s_q s_k) (+ a float32 rounding of the
     exponent) of the midpoint's exponent; each such weight moves o by at most one E4M3 step times
     max |V8_j / s_v - o| / sum P8.  Returns the sum over those weights (zero for most rows).  Used
     to compare with hardware whose fp32 score sums are not exact."""
@@ -113,17 +113,17 @@ def ambiguous_rounding_effect(qr, keys, vals, s_k, s_v, kmax, rel_score_err=2.0 
     v8 = e4m3(s_v * np.asarray(vals, np.float64)) / s_v
     res = np.zeros(len(qr))
     for i, q in enumerate(qr):
-        s_q = pow2_scale(np.abs(q).max())
-        q8 = e4m3(s_q * q)
+        s_q = pow2_scale(np.abs(c * q).max())
+        q8 = e4m3(s_q * c * q)
         x = (k8 @ q8) / (s_q * s_k)
         b = c * math.sqrt(float(q @ q)) * kmax
-        m = b if b <= OFFSET_BOUND_LIMIT else c * x.max()
-        arg = P_SHIFT + c * x - m
+        m = b if b <= OFFSET_BOUND_LIMIT else x.max()
+        arg = P_SHIFT + x - m
         p8 = e4m3(np.exp2(arg))
         o = (p8 @ v8) / p8.sum()
-        delta = c * rel_score_err * (np.abs(k8) @ np.abs(q8)) / (s_q * s_k) + 2.0 ** -20 * (np.abs(arg) + P_SHIFT)
+        delta = rel_score_err * (np.abs(k8) @ np.abs(q8)) / (s_q * s_k) + 2.0 ** -20 * (np.abs(arg) + P_SHIFT)
         if m != b:
-            delta = delta + c * rel_score_err * np.max(np.abs(k8) @ np.abs(q8)) / (s_q * s_k)  # the row maximum too
+            delta = delta + rel_score_err * np.max(np.abs(k8) @ np.abs(q8)) / (s_q * s_k)  # the row maximum too
         p = np.exp2(arg)
         _, ex = np.frexp(p)
         e = np.maximum(ex - 1, -6)

@@ -61,11 +61,12 @@ def _two_key_case():
 
 
 def pin_hand_bound_offset(f8):
-    """d = 16, c = log2(e)/4 = 0.3607; q = e1, k1 = e1/2, k2 = -e1, v1 = e1, v2 = e2.
-    Scales: s_q = s_k = 2^(8-1) = 128 (max |.| = 1 = 0.5 * 2^1), s_v = 128; all operands exact, so
-    x = (0.5, -1).  kmax = 1, bound b = c <= 4 is the offset.  Weights: 2^(8 - c/2) = 225.92 lies
-    in [128, 256) where E4M3 steps by 16 -> 224; 2^(8 - 2c) = 155.27 -> 160.  o = (224, 160) / 384
-    in the first two channels."""
+    """d = 16, c = log2(e)/4 = 0.36067; q = e1, k1 = e1/2, k2 = -e1, v1 = e1, v2 = e2.
+    Scales: s_k = 2^(8-1) = 128 (max |k| = 1 = 0.5 * 2^1), so K8 = (64, -128) exactly, s_v = 128;
+    c q = 0.36067 e1 = 0.7213 * 2^-1, so s_q = 2^9 and Q8 = e4m3(184.67) = 192 (step 16 in
+    [128, 256)).  x = 192 (64, -128) / (512 * 128) = (0.1875, -0.375).  kmax = 1, bound b = c <= 4 is
+    the offset.  Weights: 2^(8 + 0.1875 - c) = 227.0 -> 224; 2^(8 - 0.375 - c) = 153.8 -> 160.
+    o = (224, 160) / 384 in the first two channels."""
     q, keys, vals = _two_key_case()
     o = f8.softmax_rows_fp8(q, keys, vals, *f8.head_scales(keys, vals))[0]
     expect = np.zeros(16)
@@ -74,16 +75,16 @@ def pin_hand_bound_offset(f8):
 
 
 def pin_hand_rowmax_offset(f8):
-    """As above with q = 20 e1: s_q = 2^(8-5) = 8, q8 = 160 exact, x = (10, -20); the bound
-    c * 20 = 7.21 > 4, so the offset is c * max x = 10 c.  Weights: 2^8 = 256 (exact) and
-    2^(8 - 30 c) = 2^-2.82 = 0.1416, in [2^-3, 2^-2) where E4M3 steps by 2^-6 -> 9/64.
-    o = (256, 9/64) / (256 + 9/64)."""
+    """As above with q = 20 e1: c q = 7.2135 e1 = 0.9017 * 2^3, so s_q = 2^5 and Q8 = e4m3(230.8) =
+    224; x = 224 (64, -128) / (32 * 128) = (3.5, -7); the bound c * 20 = 7.21 > 4, so the offset is
+    max x = 3.5.  Weights: 2^8 = 256 (exact) and 2^(8 - 10.5) = 0.1768, in [2^-3, 2^-2) where E4M3
+    steps by 2^-6 -> 11/64.  o = (256, 11/64) / (256 + 11/64)."""
     q, keys, vals = _two_key_case()
     q = q * 20.0
     o = f8.softmax_rows_fp8(q, keys, vals, *f8.head_scales(keys, vals))[0]
-    tot = 256 + 9 / 64
+    tot = 256 + 11 / 64
     assert math.isclose(o[0], 256 / tot, rel_tol=0, abs_tol=1e-12), o[0]
-    assert math.isclose(o[1], (9 / 64) / tot, rel_tol=0, abs_tol=1e-15), o[1]
+    assert math.isclose(o[1], (11 / 64) / tot, rel_tol=0, abs_tol=1e-15), o[1]
 
 
 def pin_uniform_visibility_fp8(f8):
@@ -182,11 +183,11 @@ def m_unrounded_denominator(f8):
         k8, v8 = f8.e4m3(s_k * keys), f8.e4m3(s_v * vals)
         out = np.zeros(qr.shape)
         for i, q in enumerate(qr):
-            s_q = f8.pow2_scale(np.abs(q).max())
-            x = (k8 @ f8.e4m3(s_q * q)) / (s_q * s_k)
+            s_q = f8.pow2_scale(np.abs(c * q).max())
+            x = (k8 @ f8.e4m3(s_q * c * q)) / (s_q * s_k)
             b = c * math.sqrt(float(q @ q)) * kmax
-            m = b if b <= 4 else c * x.max()
-            p = np.exp2(8 + c * x - m)
+            m = b if b <= 4 else x.max()
+            p = np.exp2(8 + x - m)
             out[i] = (f8.e4m3(p) @ v8) / (s_v * p.sum())
         return out
     f8.softmax_rows_fp8 = softmax_rows_fp8
@@ -217,11 +218,11 @@ def m_query_scale_dropped(f8):
         k8, v8 = f8.e4m3(s_k * keys), f8.e4m3(s_v * vals)
         out = np.zeros(qr.shape)
         for i, q in enumerate(qr):
-            s_q = orig(np.abs(q).max())
-            x = (k8 @ f8.e4m3(s_q * q)) / s_k                 # wrong: s_q not divided out
+            s_q = orig(np.abs(c * q).max())
+            x = (k8 @ f8.e4m3(s_q * c * q)) / s_k             # wrong: s_q not divided out
             b = c * math.sqrt(float(q @ q)) * kmax
-            m = b if b <= 4 else c * x.max()
-            p8 = f8.e4m3(np.exp2(8 + c * x - m))
+            m = b if b <= 4 else x.max()
+            p8 = f8.e4m3(np.exp2(8 + x - m))
             out[i] = (p8 @ v8) / (s_v * p8.sum())
         return out
     f8.softmax_rows_fp8 = softmax_rows_fp8
