@@ -102,10 +102,10 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
  * Models", section "Adapting the Pretrained H3 backbone", reports the production layer with FP8
  * arithmetic but not its roundings; the ones made here are: power-of-two scales 2^(8 - e) (e the
  * binary exponent of the largest magnitude) for the keys and for the values of each head and for
- * each query row; operands rounded to E4M3 (nearest, ties to even); scores from the rounded
- * operands in fp32; weights P8 = e4m3(2^(8 + c x - m)) with c = log2(e)/sqrt(d) and the offset
- * m = c |q| max|k| when that is <= 4, else the row's exact maximum c max x; o = sum P8 V8 /
- * (s_v sum P8).  Inputs and outputs are unchanged (bf16); the linear branch and the merge are the
+ * each query row taken as c q (c = log2(e)/sqrt(d)); operands rounded to E4M3 (nearest, ties to
+ * even); scores x (in log2 units) from the rounded operands in fp32; weights
+ * P8 = e4m3(2^(8 + x - m)) with the offset m = c |q| max|k| when that is <= 4, else the row's
+ * exact maximum max x; o = sum P8 V8 / (s_v sum P8).  Inputs and outputs are unchanged (bf16); the linear branch and the merge are the
  * bf16 plan's.  Requires VDN_BF16, d = 128 and N a multiple of 16 (else VDN_ERR_UNSUPPORTED);
  * with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward rejects such plans
  * (VDN_ERR_UNSUPPORTED). */
