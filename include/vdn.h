@@ -1,6 +1,6 @@
 /*
- * vdn.h -- C ABI of the MI355X (gfx950) forward pass of the Video DeltaNet (VDN) hybrid
- * video-video attention layer.
+ * vdn.h -- C ABI of the MI355X (gfx950) forward pass (bf16, fp32 or with an FP8 softmax branch)
+ * and backward pass of the Video DeltaNet (VDN) hybrid video-video attention layer.
  *
  * Source of every operation below: "Video DeltaNet: Near-Lossless Hybrid Attention for Video
  * Models" (openvdn.github.io), cited as [VDN] with the section name, and "Faster Than It Plays:
@@ -74,7 +74,8 @@ typedef struct vdn_plan vdn_plan;
 typedef enum {
   VDN_OK = 0,
   VDN_ERR_INVALID_ARG = -1,   /* NULL pointer, dimension <= 0, anchors not 0/1, misalignment */
-  VDN_ERR_UNSUPPORTED = -2,   /* d not in {16, 32, 64, 128}, unknown dtype, size overflow      */
+  VDN_ERR_UNSUPPORTED = -2,   /* d not in {16, 32, 64, 128}, unknown dtype, size overflow,
+                                 a shape outside a requested variant's limits                 */
   VDN_ERR_OUT_OF_MEMORY = -3, /* workspace allocation failed                                   */
   VDN_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed                    */
 } vdn_status;
