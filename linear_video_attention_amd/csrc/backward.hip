@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(
     const float* __restrict__ zin, const float* __restrict__ minv, const float* __restrict__ bw,
     const float* __restrict__ alpha, const float* __restrict__ dread, const int* __restrict__ mslot,
     const int* __restrict__ order, int nscan, int T, int H, int Nc, float* __restrict__ dmf,
-    float* __restrict__ dbf, float* __restrict__ dalf, float* __restrict__ ds0) {
+    float* __restrict__ dbf, float* __restrict__ ds0) {
   constexpr int R = D / 16;
   constexpr int64_t DD = (int64_t)D * D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -874,12 +874,12 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     const size_t sm2 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;
     (void)hipFuncSetAttribute((const void*)scan_bwd_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
     scan_bwd_kernel<D><<<dim3(H, 2), kThreads, sm2, st>>>(w.zin, b.minv, b.bw, in.alpha, w.dread, w.mslot, w.order,
-                                                         w.nscan, T, H, Nc, w.dmf, w.dbf, w.dalf, w.ds0);
+                                                         w.nscan, T, H, Nc, w.dmf, w.dbf, w.ds0);
     if (w.nscan > 0) {
       const size_t smd = (size_t)2 * D * (D + 1) * 4;
       (void)hipFuncSetAttribute((const void*)frame_dm_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smd);
       frame_dm_kernel<D><<<dim3(T, H, 2), kThreads, smd, st>>>(w.zin, b.bw, in.alpha, T, H, s.anchors, w.dmf, w.dbf,
-                                                               w.dalf);
+                                                               in.alpha ? w.dalf : nullptr);
     }
   }
   // 6.-7. softmax branch (dq adds to the merge part, dk/dv/dtext start from zero)
