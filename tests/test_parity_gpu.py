@@ -177,6 +177,28 @@ def test_softmax_fallback_for_large_scores():
     plan.close()
 
 
+
+def test_softmax_moderate_bound_rows():
+    """Rows whose exponent bound c |q| max|k| lies between the first launch's limit (4 log2 units,
+    where its prescaled queries stay accurate) and the underflow limit: every other row is scaled
+    by 36 (bound 4.6), so every workgroup holds both kinds and is redone by the second launch with
+    unscaled queries."""
+    import torch as _t
+    w = synth.custom(8, 6, 256, 2, 2, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, seed=6)
+    scale = np.where(np.arange(w.T * w.N) % 2 == 0, 36.0, 1.0).astype(np.float32)
+    inp["q"] = _t.from_numpy(inp["q"] * scale[:, None, None]).to(_t.bfloat16).float().numpy()
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
+    run_layer(plan, dev)
+    ref = orc.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], w.T, w.N, w.C, w.anchors)
+    got = softmax_out(plan).astype(np.float64)
+    e = rel_err(got, ref)
+    print(f"moderate-bound rows: o_s err {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
+    plan.close()
+
+
 # --- channel-wise decay gate of the linear branch (vdn_forward_decay) ---
 
 def test_decay_tiny_fp32_matches_oracle_and_bruteforce():
