@@ -128,7 +128,10 @@ __device__ __forceinline__ void mm_gstage_at(const float* __restrict__ g, FB b, 
 // ---- 1. merge backward ----
 // Rows are (token, head) pairs of one frame and head, kRows per block; threads 16 (row groups of
 // kRows/16) x 16 (column groups of D/16).
-constexpr int kRows = 64;
+#ifndef VDN_BWD_ROWS
+#define VDN_BWD_ROWS 64
+#endif
+constexpr int kRows = VDN_BWD_ROWS;   // rows per block of the merge and token-gradient products (32: within 1 %)
 
 constexpr int kWChunk = 16;            // rows of the right-hand matrix staged in LDS at a time
 
