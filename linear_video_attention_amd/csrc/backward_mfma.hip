@@ -29,9 +29,11 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kWaves = 8;
-// VDN_DKV_WIDE 1: the dK/dV kernel with 4 waves x 32 keys (see softmax_dkv_wide_kernel)
+// VDN_DKV_WIDE 1: the dK/dV kernel with 4 waves x 32 keys (softmax_dkv_wide_kernel); 0 (default):
+// 8 waves x 16 keys, two waves per SIMD (2.5 % faster at 768p once both stage the tile's
+// normalisers in LDS and fold the offsets into the accumulators)
 #ifndef VDN_DKV_WIDE
-#define VDN_DKV_WIDE 1
+#define VDN_DKV_WIDE 0
 #endif
 constexpr int kVmcntZero = 0x0F70;
 
@@ -95,7 +97,7 @@ struct DkvParams {
 template <int D>
 struct DkvSmem {
   static constexpr int ROW = 64 * D * 2;          // one 64-query row-major tile (Q or dO)
-  static constexpr int STAGE = 4 * ROW;           // Q, dO, Q^T, dO^T
+  static constexpr int STAGE = 4 * ROW + 512;     // Q, dO, Q^T, dO^T, then lse[64], dsum[64]
 };
 
 template <int D>
@@ -120,6 +122,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
     vf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[ks][e] = (__bf16)((float)kf[ks][e] * P.c);   // scores in log2 units
   }
   f32x4 dvt[DT], dkt[DT];
 #pragma unroll
@@ -170,6 +174,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
       __builtin_amdgcn_global_load_lds((gptr_t)(P.qt + off), (lptr_t)(base + 2 * SM::ROW + blkid * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gptr_t)(P.dot + off), (lptr_t)(base + 3 * SM::ROW + blkid * 1024), 16, 0, 0);
     }
+    if (wave < 2) {                              // the tile's normalisers (wave 0) and D values (wave 1)
+      const int64_t rr = ((int64_t)t * N + min(q0 + lane, N - 1)) * H + h;
+      __builtin_amdgcn_global_load_lds((gptr_t)((wave == 0 ? P.lse : P.dsum) + rr),
+                                       (lptr_t)(base + 4 * SM::ROW + wave * 256), 4, 0, 0);
+    }
   };
 
   const float c = P.c, tau = P.tau;
@@ -192,11 +201,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     const unsigned char* os = qs + SM::ROW;
     const unsigned char* qts = qs + 2 * SM::ROW;
     const unsigned char* ots = qs + 3 * SM::ROW;
-    const int64_t rowbase = (int64_t)t * N + q0;
+    const float* lse_s = reinterpret_cast<const float*>(qs + 4 * SM::ROW);
+    const float* dsum_s = lse_s + 64;
     bf16x8 pj[2], sj[2];                                     // P and dS of the two 32-query k-steps
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      // accumulators start at -lse and -D of the lane's four query rows
+      f32x4 s, dp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
+        s[i] = -lse_s[qi];
+        dp[i] = -dsum_s[qi];
+      }
       const int row = perm_row(u, l16);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -213,9 +230,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
         const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
         float p = 0.f, ds = 0.f;
         if (q0 + qi < N) {
-          const int64_t rr = (rowbase + qi) * H + h;
-          p = exp2f(s[i] * c - P.lse[rr]);
-          ds = p * (dp[i] - P.dsum[rr]) * tau;
+          p = __builtin_amdgcn_exp2f(s[i]);
+          ds = p * dp[i];                          // tau applied to dK at the end
         }
         pj[u >> 1][4 * (u & 1) + i] = (__bf16)p;
         sj[u >> 1][4 * (u & 1) + i] = (__bf16)ds;
@@ -243,7 +259,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     for (int dt = 0; dt < DT; ++dt) {
       f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
       f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
-      *a = *a + dkt[dt];
+      *a = *a + dkt[dt] * tau;
       *b = *b + dvt[dt];
     }
   }
