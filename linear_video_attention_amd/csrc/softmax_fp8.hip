@@ -56,7 +56,11 @@ constexpr int kQT = VDN_FP8_QT;     // 16-query tiles per wave
 constexpr int kUG = VDN_FP8_UG;
 constexpr int kQW = 16 * kQT;
 constexpr int kBQ = kWaves * kQW;   // queries per workgroup
-constexpr int kStages = 2;
+#ifndef VDN_FP8_STAGES
+#define VDN_FP8_STAGES 2
+#endif
+constexpr int kStages = VDN_FP8_STAGES;   // LDS stages (2; 3 keeps two tiles in flight, 2 % slower)
+static_assert(kStages == 2 || kStages == 3, "stages");
 constexpr int K_BYTES = kBK * D;    // 16 KB
 constexpr int V_BYTES = D * kBK;    // 16 KB
 constexpr int STAGE = K_BYTES + V_BYTES;
@@ -303,28 +307,36 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
     return join(lo, hi);
   };
 
-  // Tile pipeline: tile it + 1 is loaded while tile it is computed.  With two stages the only loads
-  // in flight at the top of an iteration are the current tile's; after the barrier the other
-  // stage is free in every wave and takes the next tile.
-#define VDN_FP8_FIRST_TILE(cursor, valid_next)                                          \
-  {                                                                                      \
-    int key0_;                                                                           \
-    if (ntiles > 0) {                                                                    \
-      cursor.pop(key0_, valid_next);                                                     \
-      issue_tile(kh, vh, koff, voff, smem, key0_, wave);                                 \
-    }                                                                                    \
+  // Tile pipeline: tiles are loaded kStages - 1 ahead of the one being computed.  At the top of an
+  // iteration a wave waits until only the younger tiles' loads are in flight; after the barrier
+  // the stage of tile it - 1 is free in every wave and takes tile it + kStages - 1.  va / vb hold
+  // the key counts of the tiles in flight (oldest first).
+  constexpr int kVmcntOneTile = 0x0F70 | (K_INSTR + V_INSTR);
+#define VDN_FP8_FIRST_TILE(cursor, va, vb)                                                   \
+  {                                                                                          \
+    int key0_;                                                                               \
+    if (ntiles > 0) {                                                                        \
+      cursor.pop(key0_, va);                                                                 \
+      issue_tile(kh, vh, koff, voff, smem, key0_, wave);                                     \
+    }                                                                                        \
+    if (kStages == 3 && ntiles > 1) {                                                        \
+      cursor.pop(key0_, vb);                                                                 \
+      issue_tile(kh, vh, koff, voff, smem + STAGE, key0_, wave);                             \
+    }                                                                                        \
   }
-#define VDN_FP8_NEXT_TILE(it, cursor, valid, valid_next, kb)                             \
-  {                                                                                      \
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);                                              \
-    __syncthreads();                                                                     \
-    valid = valid_next;                                                                  \
-    if (it + 1 < ntiles) {                                                               \
-      int key0_;                                                                         \
-      cursor.pop(key0_, valid_next);                                                     \
-      issue_tile(kh, vh, koff, voff, smem + ((it + 1) % kStages) * STAGE, key0_, wave); \
-    }                                                                                    \
-    kb = smem + (it % kStages) * STAGE;                                                  \
+#define VDN_FP8_NEXT_TILE(it, cursor, valid, va, vb, kb)                                     \
+  {                                                                                          \
+    if (kStages == 3 && it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntOneTile);          \
+    else __builtin_amdgcn_s_waitcnt(kVmcntZero);                                             \
+    __syncthreads();                                                                         \
+    valid = va;                                                                              \
+    if (kStages == 3) va = vb;                                                               \
+    if (it + kStages - 1 < ntiles) {                                                         \
+      int key0_;                                                                             \
+      cursor.pop(key0_, kStages == 3 ? vb : va);                                             \
+      issue_tile(kh, vh, koff, voff, smem + ((it + kStages - 1) % kStages) * STAGE, key0_, wave); \
+    }                                                                                        \
+    kb = smem + (it % kStages) * STAGE;                                                      \
   }
 
   if constexpr (FALLBACK) {
@@ -333,11 +345,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
 #pragma unroll
     for (int j = 0; j < kQT; ++j) mx[j] = kMasked;
     TileCursor c1 = cur;
-    int valid, valid_next = 0;
+    int valid, va = 0, vb = 0;
     const unsigned char* kb;
-    VDN_FP8_FIRST_TILE(c1, valid_next)
+    VDN_FP8_FIRST_TILE(c1, va, vb)
     for (int it = 0; it < ntiles; ++it) {
-      VDN_FP8_NEXT_TILE(it, c1, valid, valid_next, kb)
+      VDN_FP8_NEXT_TILE(it, c1, valid, va, vb, kb)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const i32x8 kf = kfrag(kb, u);
@@ -368,11 +380,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_fp8_kernel(Params P) {
   }
   const i32x8 ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
 
-  int valid, valid_next = 0;
+  int valid, va = 0, vb = 0;
   const unsigned char* kb;
-  VDN_FP8_FIRST_TILE(cur, valid_next)
+  VDN_FP8_FIRST_TILE(cur, va, vb)
   for (int it = 0; it < ntiles; ++it) {
-    VDN_FP8_NEXT_TILE(it, cur, valid, valid_next, kb)
+    VDN_FP8_NEXT_TILE(it, cur, valid, va, vb, kb)
     const unsigned char* vb = kb + K_BYTES;
     i32x8 pf[kQT];
     // scores and weights, kUG 16-key tiles at a time
