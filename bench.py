@@ -88,7 +88,7 @@ def recorded_traffic(name="softmax_mfma"):
         return None
 
 
-def cpu_baseline(w, inp, budget_rows=8192):
+def cpu_baseline(w, inp, budget_rows=32768):
     """Time the CPU oracle on a bounded sample of the workload and scale it to video tokens/s.
 
     Sample: the full linear-branch state computation (all frames, all heads; a fixed cost of the
