@@ -236,8 +236,16 @@ def main():
     n_bwd = max(2, min(args.steps, 5))
     bwd_ms = timed_steps(backward, n_bwd)
     bwd_med = float(np.median(bwd_ms))
+    # a training step that reuses the forward's intermediates: forward, then vdn_backward_after_forward
+    train = lambda: (forward(plan), plan.backward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"],
+                                                  dev["proj_w"], dout, after_forward=True))
+    train()
+    torch.cuda.synchronize()
+    train_med = float(np.median(timed_steps(train, n_bwd)))
     backward_info = {"ms_per_call_median": bwd_med, "calls": n_bwd,
                      "train_step_tokens_per_s": tokens / ((float(np.median(per_step)) + bwd_med) * 1e-3),
+                     "train_step_after_forward_ms_median": train_med,
+                     "train_step_after_forward_tokens_per_s": tokens / (train_med * 1e-3),
                      "softmax_backward_algorithmic_tflop": 3.5 * flops / 1e12}
     del dout
     plan.close()

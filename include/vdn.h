@@ -172,6 +172,21 @@ vdn_status vdn_backward(vdn_plan *plan, const void *q, const void *k, const void
                         float *dk, float *dv, float *dbeta, float *dtext_kv, float *dgate_w,
                         float *dproj_w, float *dalpha, void *stream);
 
+/* As vdn_backward, reusing the intermediates the plan's most recent call left in its workspace
+ * (linear-branch statistics and states, packed keys, the softmax output and its normalisers)
+ * instead of recomputing them: for a training step that runs the forward and then the backward on
+ * the same inputs.  Preconditions: the most recent call on this plan was vdn_forward,
+ * vdn_forward_decay, vdn_forward_joint or vdn_backward with exactly these q, k, v, beta, text_kv,
+ * alpha and weights, ordered before this call on the stream.  The library checks only that such a
+ * call succeeded and that alpha was given to both or to neither (else VDN_ERR_INVALID_ARG); other
+ * mismatched inputs give wrong gradients.  Results are identical to vdn_backward's. */
+vdn_status vdn_backward_after_forward(vdn_plan *plan, const void *q, const void *k, const void *v,
+                                      const float *beta, const void *text_kv, const float *alpha,
+                                      const void *gate_w, const void *proj_w, const void *dout,
+                                      float *dq, float *dk, float *dv, float *dbeta,
+                                      float *dtext_kv, float *dgate_w, float *dproj_w,
+                                      float *dalpha, void *stream);
+
 /* Free the plan's workspace, stream and events.  The caller must have synchronised the streams
  * the plan was used on.  NULL is a no-op. */
 void vdn_plan_destroy(vdn_plan *plan);

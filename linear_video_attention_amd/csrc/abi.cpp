@@ -20,6 +20,9 @@ struct vdn_plan {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // stage timing (mutable: recording events does not change the plan's meaning)
   bool overlap = false;                          // linear branch on the side stream
+  // the most recent call was a successful forward (its intermediates are in the workspace), with or
+  // without the decay gate
+  mutable bool fwd_valid = false, fwd_alpha = false;
   mutable int prof_max = 0, prof_count = 0;
   mutable std::vector<hipEvent_t> prof_events;   // [prof_max][VDN_NUM_STAGES][2]
   // backward workspace and tables, allocated by the first vdn_backward call
@@ -53,6 +56,7 @@ vdn::Buffers buffers_of(const vdn_plan* p) {
   b.v8 = p->kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + p->lay.v8) : nullptr;
   b.part8 = p->kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + p->lay.part8) : nullptr;
   b.scale8 = p->kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + p->lay.scale8) : nullptr;
+  b.lse = p->kinds.softmax_fp8 ? nullptr : reinterpret_cast<float*>(ws + p->lay.lse);
   b.ranges = reinterpret_cast<const int*>(ws + p->lay.ranges);
   b.nranges = b.ranges + (size_t)(p->s.T + 1) * 2 * vdn::kMaxRanges;
   return b;
@@ -249,6 +253,7 @@ vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, cons
   };
 #define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
 
+  plan->fwd_valid = false;                       // until every stage is enqueued
   mark(VDN_STAGE_TOTAL, 0, main);
   // linear branch: on the caller's stream, or for overlapped plans on the side stream, forked from
   // the caller's stream
@@ -283,6 +288,8 @@ vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, cons
   mark(VDN_STAGE_EPILOGUE, 1, main);
   mark(VDN_STAGE_TOTAL, 1, main);
 #undef VDN_TRY
+  plan->fwd_valid = true;
+  plan->fwd_alpha = alpha != nullptr;
   return VDN_OK;
 }
 
@@ -395,7 +402,7 @@ vdn_status ensure_backward(vdn_plan* p) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (size_t)vdn::round_up((int64_t)bytes, 256); return o; };
   const size_t o_rows6 = take((size_t)6 * rows * d * 4);
-  const size_t o_dsum = take((size_t)rows * 4), o_lse = take((size_t)rows * 4);
+  const size_t o_dsum = take((size_t)rows * 4);
   const size_t o_part = take((size_t)std::max<int64_t>(splits_all, (int64_t)nslots * H * splits_read) * dd * 4);
   const size_t o_dread = take((size_t)nslots * H * dd * 4);
   const size_t o_z = take((size_t)3 * 2 * T * H * dd * 4);
@@ -434,7 +441,6 @@ vdn_status ensure_backward(vdn_plan* p) {
   w.dz_s = r6 + 4 * rows * d;
   w.dz_l = r6 + 5 * rows * d;
   w.dsum = reinterpret_cast<float*>(ws + o_dsum);
-  w.lse = reinterpret_cast<float*>(ws + o_lse);
   w.partial = reinterpret_cast<float*>(ws + o_part);
   w.dread = reinterpret_cast<float*>(ws + o_dread);
   float* z = reinterpret_cast<float*>(ws + o_z);
@@ -471,10 +477,12 @@ vdn_status ensure_backward(vdn_plan* p) {
 
 }  // namespace
 
-vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
-                        const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
-                        const void* dout, float* dq, float* dk, float* dv, float* dbeta, float* dtext_kv,
-                        float* dgate_w, float* dproj_w, float* dalpha, void* stream) {
+namespace {
+
+vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                         const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
+                         const void* dout, float* dq, float* dk, float* dv, float* dbeta, float* dtext_kv,
+                         float* dgate_w, float* dproj_w, float* dalpha, void* stream, bool recompute) {
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !dout || !dq || !dk || !dv || !dbeta || !dgate_w ||
       !dproj_w)
     return VDN_ERR_INVALID_ARG;
@@ -493,6 +501,7 @@ vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
   if (dev != plan->device) return VDN_ERR_INVALID_ARG;
+  if (!recompute && (!plan->fwd_valid || plan->fwd_alpha != (alpha != nullptr))) return VDN_ERR_INVALID_ARG;
   vdn_status st = ensure_backward(plan);
   if (st != VDN_OK) return st;
 
@@ -500,23 +509,46 @@ vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void
   hipStream_t main = reinterpret_cast<hipStream_t>(stream);
   vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, nullptr, alpha, nullptr, nullptr};
   vdn::Buffers b = buffers_of(plan);
-  b.lse = plan->bw.lse;
   vdn::BwdBuffers w = plan->bw;
   w.dout = dout;
+  w.lse = b.lse;
   vdn::BwdOutputs o{dq, dk, dv, dbeta, dtext_kv, dgate_w, dproj_w, dalpha};
 #define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
-  // forward recomputation: linear-branch states, softmax output and its normalisers
-  VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, main));
-  VDN_TRY(vdn::launch_vda_scan(s, in, b, plan->kinds.scan_mfma, main));
-  if (plan->kinds.softmax_mfma) {
-    VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
-    VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
-  } else {
-    VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
+  if (recompute) {
+    // forward recomputation: linear-branch states, softmax output and its normalisers
+    VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, main));
+    VDN_TRY(vdn::launch_vda_scan(s, in, b, plan->kinds.scan_mfma, main));
+    if (plan->kinds.softmax_mfma) {
+      VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
+      VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
+    } else {
+      VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
+    }
+    plan->fwd_valid = true;                      // the workspace now holds this forward's intermediates
+    plan->fwd_alpha = alpha != nullptr;
   }
   VDN_TRY(vdn::launch_backward(s, in, b, w, o, plan->kinds.softmax_mfma, main));
 #undef VDN_TRY
   return VDN_OK;
+}
+
+}  // namespace
+
+vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                        const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
+                        const void* dout, float* dq, float* dk, float* dv, float* dbeta, float* dtext_kv,
+                        float* dgate_w, float* dproj_w, float* dalpha, void* stream) {
+  return backward_impl(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, dout, dq, dk, dv, dbeta, dtext_kv,
+                       dgate_w, dproj_w, dalpha, stream, true);
+}
+
+vdn_status vdn_backward_after_forward(vdn_plan* plan, const void* q, const void* k, const void* v,
+                                      const float* beta, const void* text_kv, const float* alpha,
+                                      const void* gate_w, const void* proj_w, const void* dout, float* dq,
+                                      float* dk, float* dv, float* dbeta, float* dtext_kv, float* dgate_w,
+                                      float* dproj_w, float* dalpha, void* stream) {
+  return backward_impl(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, dout, dq, dk, dv, dbeta, dtext_kv,
+                       dgate_w, dproj_w, dalpha, stream, false);
 }
 
 vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes) {

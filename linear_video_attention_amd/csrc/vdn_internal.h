@@ -55,6 +55,7 @@ struct Layout {
   size_t v8;
   size_t part8;     // FP8 softmax: per 64-key block and head max |k|, max |v|, max key norm [H][Lk/64][3] f32
   size_t scale8;    // FP8 softmax: per head key and value scales [H][2] f32
+  size_t lse;       // base-2 log of each video row's softmax normaliser [T*N][H] f32 (not FP8 plans)
   size_t ranges;    // int32 [T+1][2*kMaxRanges] + int32 [T+1] counts (row T: context query rows)
   size_t total;
 };

@@ -33,6 +33,7 @@ SIGNATURES = [
     ("vdn_forward_decay", _c_int, [_vp] * 11),
     ("vdn_forward_joint", _c_int, [_vp] * 13),
     ("vdn_backward", _c_int, [_vp] * 19),
+    ("vdn_backward_after_forward", _c_int, [_vp] * 19),
     ("vdn_plan_destroy", None, [_vp]),
     ("vdn_status_str", ctypes.c_char_p, [_c_int]),
     ("vdn_plan_workspace_bytes", _c_size, [_vp]),
@@ -246,9 +247,12 @@ class Plan:
             vdn_forward_decay(self.handle, q, k, v, beta, tkv, alpha, gate_w, proj_w, out, stream)
         return out
 
-    def backward(self, q, k, v, beta, text_kv, gate_w, proj_w, dout, alpha=None, stream=None):
+    def backward(self, q, k, v, beta, text_kv, gate_w, proj_w, dout, alpha=None, stream=None,
+                 after_forward=False):
         """Input gradients of the layer for the output gradient ``dout``; returns a dict of float32
-        device tensors (q, k, v, beta, text_kv, gate_w, proj_w and, with ``alpha``, alpha)."""
+        device tensors (q, k, v, beta, text_kv, gate_w, proj_w and, with ``alpha``, alpha).
+        ``after_forward=True`` reuses the intermediates of the plan's most recent forward on the
+        same inputs (vdn_backward_after_forward) instead of recomputing them."""
         import torch
         TN, H, d = self.T * self.N, self.H, self.d
         dt = self.torch_dtype
@@ -268,11 +272,12 @@ class Plan:
                  gate_w=torch.empty((2, d, d), **f32), proj_w=torch.empty((2, d, d), **f32),
                  alpha=torch.empty((self.T, H, d), **f32) if alpha is not None else None)
         ptr = lambda x: None if x is None else x.data_ptr()
-        _check(lib().vdn_backward(self.handle, ptr(q), ptr(k), ptr(v), ptr(beta),
-                                  ptr(text_kv if self.n_text > 0 else None), ptr(alpha), ptr(gate_w),
-                                  ptr(proj_w), ptr(dout), ptr(g["q"]), ptr(g["k"]), ptr(g["v"]),
-                                  ptr(g["beta"]), ptr(g["text_kv"]), ptr(g["gate_w"]), ptr(g["proj_w"]),
-                                  ptr(g["alpha"]), _stream_ptr(stream)), "vdn_backward")
+        name = "vdn_backward_after_forward" if after_forward else "vdn_backward"
+        _check(getattr(lib(), name)(self.handle, ptr(q), ptr(k), ptr(v), ptr(beta),
+                                    ptr(text_kv if self.n_text > 0 else None), ptr(alpha), ptr(gate_w),
+                                    ptr(proj_w), ptr(dout), ptr(g["q"]), ptr(g["k"]), ptr(g["v"]),
+                                    ptr(g["beta"]), ptr(g["text_kv"]), ptr(g["gate_w"]), ptr(g["proj_w"]),
+                                    ptr(g["alpha"]), _stream_ptr(stream)), name)
         return {key: val for key, val in g.items() if val is not None}
 
     def debug_buffer(self, which, stream=None):

@@ -95,3 +95,33 @@ def test_backward_768p_sampled_dq():
     assert finite
     assert e <= TOL[w.dtype]
     plan.close()
+
+
+@pytest.mark.parametrize("decay", [False, True])
+def test_backward_after_forward_matches(decay):
+    """vdn_backward_after_forward after a forward on the same inputs gives vdn_backward's gradients
+    bit for bit (same kernels on the same intermediates); without a preceding forward, or with
+    the decay gate given to only one of the two calls, it is an argument error."""
+    from linear_video_attention_amd import vdn
+    w = synth.custom(7, 11, 72, 3, 2, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, seed=8, decay=decay)
+    dev = to_device(inp, w.dtype)
+    dout = torch.from_numpy(np.random.default_rng(5).standard_normal((w.T * w.N, w.H, w.d)).astype(np.float32))
+    dout = dout.cuda().to(torch.bfloat16)
+    args = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"], dout)
+    plan = make_plan(w)
+    with pytest.raises(vdn.VdnError) as ei:
+        plan.backward(*args, alpha=dev["alpha"], after_forward=True)
+    assert ei.value.status == -1
+    ref = plan.backward(*args, alpha=dev["alpha"])
+    plan.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
+                 alpha=dev["alpha"])
+    got = plan.backward(*args, alpha=dev["alpha"], after_forward=True)
+    torch.cuda.synchronize()
+    for name in ref:
+        assert torch.equal(ref[name], got[name]), name
+    if decay:
+        with pytest.raises(vdn.VdnError) as ei:
+            plan.backward(*args, after_forward=True)          # the forward had a decay gate
+        assert ei.value.status == -1
+    plan.close()
