@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     }
   };
 
-  const float c = P.c, tau = P.tau;
+  [[maybe_unused]] const float c = P.c;
+  const float tau = P.tau;
   if (ntiles > 0) {
     int t, q0;
     tile_at(0, t, q0);
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv
   constexpr int R_INSTR = SM::ROW / 1024 / kDkvWaves;
   constexpr int T_INSTR = SM::ROW / 1024 / kDkvWaves;
 
-  const float c = P.c, tau = P.tau;
+  [[maybe_unused]] const float c = P.c;
+  const float tau = P.tau;
   int t_next = 0, q_next = 0;
 #define VDN_DKV_TILE_AT(it_, t_, q0_)                                  \
   {                                                                    \
@@ -383,7 +385,8 @@ __global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv
   for (int it = 0; it < ntiles; ++it) {
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
-    int t, q0;
+    [[maybe_unused]] int t;
+    int q0;
     VDN_DKV_TILE_AT(it, t, q0)
     if (it + 1 < ntiles) {
       VDN_DKV_TILE_AT(it + 1, t_next, q_next)
@@ -627,7 +630,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     }
   };
 
-  const float c = P.c, tau = P.tau;
+  [[maybe_unused]] const float c = P.c;
+  const float tau = P.tau;
   if (ntiles > 0) {
     int key0, valid;
     tile_at(0, key0, valid);

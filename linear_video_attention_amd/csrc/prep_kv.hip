@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void kmax_reduce_kernel(const float* __restric
   red[threadIdx.x] = m;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
     __syncthreads();
   }
   if (threadIdx.x == 0) kmax[h] = red[0];
