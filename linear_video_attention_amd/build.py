@@ -33,6 +33,7 @@ SOURCES = [
     "calibrate.hip",
     "backward.hip",
     "backward_mfma.hip",
+    "merge_bwd_mfma.hip",
 ]
 
 ARCH = "gfx950"

@@ -413,7 +413,9 @@ vdn_status ensure_backward(vdn_plan* p) {
   const size_t o_qr = take(qr.size() * 4), o_nqr = take(nqr.size() * 4);
   const size_t o_sa = take(seg_all.size() * sizeof(vdn::Segment)), o_sr = take(seg_read.size() * sizeof(vdn::Segment));
   const size_t o_kb = take(std::max<size_t>(1, kblocks.size()) * sizeof(int2));
-  const size_t pack_bytes = mfma_bwd ? (size_t)H * d * 2 * (2 * Lq + 2 * s.Ls) + (size_t)rows * d * 2 : 0;
+  const size_t mimg_bytes = (size_t)(6 + 4 * (s.Nc + 1) * H) * dd * 2;   // merge matrix images
+  const size_t pack_bytes =
+      mfma_bwd ? (size_t)H * d * 2 * (2 * Lq + 2 * s.Ls) + (size_t)rows * d * 2 + mimg_bytes : 0;
   const size_t o_pack = take(pack_bytes);
   char* ws = nullptr;
   if (hipMalloc(&ws, off) != hipSuccess) {
@@ -470,6 +472,7 @@ vdn_status ensure_backward(vdn_plan* p) {
     w.kt = pk + 2 * (int64_t)H * d * Lq;
     w.vp = w.kt + (int64_t)H * d * s.Ls;
     w.dos16 = w.vp + (int64_t)H * d * s.Ls;
+    w.mimg = w.dos16 + rows * d;
   }
   p->bws = ws;
   return VDN_OK;

@@ -839,8 +839,16 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   zero(o.dbeta, ((int64_t)s.n_text + (int64_t)T * N) * H);
   zero(o.dtext_kv, (int64_t)2 * s.n_text * H * D);
   if (o.dalpha) zero(w.dalf, (int64_t)2 * T * H * D);   // frames never written (boundary) keep zero
-  // 1. merge backward
-  {
+  // 1. merge backward (matrix cores for the plans whose softmax transpose runs on them)
+  bool merged = false;
+  if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128)) {
+    if (mfma_softmax) {
+      const hipError_t e = launch_merge_bwd_mfma(s, in, b, w, o, st);
+      if (e != hipSuccess) return e;
+      merged = true;
+    }
+  }
+  if (!merged) {
     const size_t sm = merge_smem<D>();
     (void)hipFuncSetAttribute((const void*)merge_bwd_kernel<Tin, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     merge_bwd_kernel<Tin, D><<<dim3((N + kRows - 1) / kRows, T, H), kThreads, sm, st>>>(

@@ -131,6 +131,7 @@ struct BwdBuffers {
   int splits_all, splits_read, nscan;
   // MFMA softmax backward (bf16 plans, d in {64, 128})
   uint16_t* dos16;                      // [T*N][H][d] do_s in bf16
+  uint16_t* mimg;                       // merge matrix images: 6 weights, then 4 per (slot, head)
   uint16_t *qt, *dot;                   // [H][d][Lq] transposed q, do_s (bf16); pad columns zero
   uint16_t *kt, *vp;                    // [H][d][Ls] transposed keys, [H][Ls][d] key-major values
   int64_t Lq;                           // T*N + 64
@@ -142,6 +143,8 @@ struct BwdOutputs {
 };
 hipError_t launch_backward(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                            const BwdOutputs& o, bool mfma_softmax, hipStream_t st);
+hipError_t launch_merge_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
+                                 const BwdOutputs& o, hipStream_t st);
 hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                         const BwdOutputs& o, hipStream_t st);
 
