@@ -34,6 +34,7 @@ SOURCES = [
     "backward.hip",
     "backward_mfma.hip",
     "merge_bwd_mfma.hip",
+    "xty_mfma.hip",
 ]
 
 ARCH = "gfx950"

@@ -860,7 +860,17 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     auto xty = [&](auto x, auto y, const Segment* segs, int nseg, int splits, float* out) {
       using TX = std::remove_cv_t<std::remove_pointer_t<decltype(x)>>;
       using TY = std::remove_cv_t<std::remove_pointer_t<decltype(y)>>;
-      xty_partial_kernel<D, TX, TY><<<dim3(nseg, splits), kThreads, 0, st>>>(x, y, segs, H, splits, w.partial);
+      bool on_mfma = false;   // matrix cores for the plans whose softmax transpose runs on them
+      if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128) &&
+                    std::is_same<TX, float>::value != std::is_same<TY, float>::value) {
+        if (mfma_softmax) {
+          (void)launch_xty_mfma(D, x, std::is_same<TX, float>::value, y, std::is_same<TY, float>::value, segs, nseg,
+                                splits, H, w.partial, st);
+          on_mfma = true;
+        }
+      }
+      if (!on_mfma)
+        xty_partial_kernel<D, TX, TY><<<dim3(nseg, splits), kThreads, 0, st>>>(x, y, segs, H, splits, w.partial);
       xty_reduce_kernel<D><<<dim3(nseg, (D * D + kThreads - 1) / kThreads), kThreads, 0, st>>>(w.partial, splits, out,
                                                                                                1.f);
     };
