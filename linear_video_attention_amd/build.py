@@ -35,6 +35,7 @@ SOURCES = [
     "backward_mfma.hip",
     "merge_bwd_mfma.hip",
     "xty_mfma.hip",
+    "scan_bwd_mfma.hip",
 ]
 
 ARCH = "gfx950"

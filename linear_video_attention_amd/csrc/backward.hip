@@ -894,8 +894,17 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   {
     const size_t sm2 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;
     (void)hipFuncSetAttribute((const void*)scan_bwd_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
-    scan_bwd_kernel<D><<<dim3(H, 2), kThreads, sm2, st>>>(w.zin, b.minv, b.bw, in.alpha, w.dread, w.mslot, w.order,
-                                                         w.nscan, T, H, Nc, w.dmf, w.dbf, w.ds0);
+    bool chained = false;   // matrix cores for the plans whose softmax transpose runs on them
+    if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128)) {
+      if (mfma_softmax) {
+        const hipError_t e = launch_scan_bwd_mfma(s, in, b, w, st);
+        if (e != hipSuccess) return e;
+        chained = true;
+      }
+    }
+    if (!chained)
+      scan_bwd_kernel<D><<<dim3(H, 2), kThreads, sm2, st>>>(w.zin, b.minv, b.bw, in.alpha, w.dread, w.mslot, w.order,
+                                                           w.nscan, T, H, Nc, w.dmf, w.dbf, w.ds0);
     if (w.nscan > 0) {
       const size_t smd = (size_t)2 * D * (D + 1) * 4;
       (void)hipFuncSetAttribute((const void*)frame_dm_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smd);

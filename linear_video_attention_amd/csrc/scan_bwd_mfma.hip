@@ -1,0 +1,137 @@
+// Adjoint chain of the frame scan on CDNA4 matrix cores (bf16 plans, d in {64, 128}).
+//
+// "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Video Delta
+// Attention: A Frame-Wise Solution": each scanned frame maps the state as
+// S <- (S Diag(alpha_f) + B_f) M_f.  Walking the frames of one direction in reverse scan order, the
+// adjoint G of the state after frame f (plus the readout adjoints of the chunks that read that
+// state) gives dB_f = dR = G M_f^T and the adjoint before the frame, dR Diag(alpha_f); the adjoint
+// after every write is kept for the per-frame dM_f and dalpha_f.  After the first frame, the
+// adjoint is that of the text state.
+//
+// The chain is sequential in the frames, so one workgroup per (head, direction) runs it; each step
+// is one d x d x d product on v_mfma_f32_16x16x32_bf16 with both fp32 operands as bf16 hi + lo parts
+// (three products, about 2^-16 relative per step).  G stays in LDS in fp32; 8 waves, wave w owns
+// output column tile w % (d / 16) and a share of the row tiles; its B fragments (rows of M_f, eight
+// consecutive k per lane) come straight from global memory and the next frame's are loaded while
+// the current product runs.
+#include "dev_common.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWaves = 8;
+
+__device__ __forceinline__ void split8(float4 a, float4 b, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 t = (__bf16)x[i];
+    hi[i] = t;
+    lo[i] = (__bf16)(x[i] - (float)t);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void scan_bwd_mfma_kernel(
+    const float* __restrict__ minv, const float* __restrict__ alpha, const float* __restrict__ dread,
+    const int* __restrict__ mslot, const int* __restrict__ order, int nscan, int T, int H, int Nc,
+    float* __restrict__ dmf, float* __restrict__ dbf, float* __restrict__ ds0) {
+  constexpr int KS = D / 32, TJ = D / 16, TI = D / 16;
+  constexpr int WPC = kWaves / TJ;             // waves per column tile
+  constexpr int NTI = TI / WPC;                // row tiles per wave
+  constexpr int LD = D + 4;                    // LDS row stride (floats)
+  constexpr int64_t DD = (int64_t)D * D;
+  extern __shared__ __attribute__((aligned(16))) float adj[];   // D x LD
+  const int h = blockIdx.x, dir = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int tj = wave % TJ, ti0 = (wave / TJ) * NTI;
+  const int* ms = mslot + dir * (Nc + 2);
+  for (int e = tid; e < D * D; e += kWaves * 64) adj[(e / D) * LD + e % D] = 0.f;
+  __syncthreads();
+  auto add_reads = [&](int m) {
+    for (int c = 0; c < Nc + 2; ++c)
+      if (ms[c] == m) {
+        const float* gr = dread + ((int64_t)c * H + h) * DD;
+        for (int e = tid; e < D * D; e += kWaves * 64) adj[(e / D) * LD + e % D] += gr[e];
+      }
+    __syncthreads();
+  };
+  auto frame_of = [&](int m) { return order[dir == 0 ? m - 1 : nscan - m]; };
+  // B fragment of k-step ks: row 16 tj + l16 of M_f, columns 32 ks + 8 g .. + 7
+  float4 mb[KS][2];
+  auto load_m = [&](int f) {
+    const float* mf = minv + ((int64_t)(1 + f) * H + h) * DD + (int64_t)(16 * tj + l16) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      mb[ks][0] = *reinterpret_cast<const float4*>(mf + 32 * ks);
+      mb[ks][1] = *reinterpret_cast<const float4*>(mf + 32 * ks + 4);
+    }
+  };
+  if (nscan >= 1) load_m(frame_of(nscan));
+  for (int m = nscan; m >= 1; --m) {
+    add_reads(m);
+    const int f = frame_of(m);
+    bf16x8 bh[KS], bl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) split8(mb[ks][0], mb[ks][1], bh[ks], bl[ks]);
+    if (m > 1) load_m(frame_of(m - 1));      // the next frame's fragments, in flight during this step
+    // dR = G M_f^T: dR[i][j] = sum_k G[i][k] M_f[j][k]
+    f32x4 acc[NTI];
+#pragma unroll
+    for (int t = 0; t < NTI; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t = 0; t < NTI; ++t) {
+        const float* ar = adj + (16 * (ti0 + t) + l16) * LD + 32 * ks + 8 * g;
+        bf16x8 ah, al;
+        split8(*reinterpret_cast<const float4*>(ar), *reinterpret_cast<const float4*>(ar + 4), ah, al);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[ks], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[ks], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[ks], acc[t], 0, 0, 0);
+      }
+    // keep the adjoint after the write (for dM_f, dalpha_f) and dB_f = dR
+    float* dmo = dmf + (((int64_t)dir * T + f) * H + h) * DD;
+    float* dbo = dbf + (((int64_t)dir * T + f) * H + h) * DD;
+    for (int e = tid; e < D * D; e += kWaves * 64) dmo[e] = adj[(e / D) * LD + e % D];
+    const int col = 16 * tj + l16;
+#pragma unroll
+    for (int t = 0; t < NTI; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dbo[(int64_t)(16 * (ti0 + t) + 4 * g + i) * D + col] = acc[t][i];
+    __syncthreads();                             // every wave is done reading G
+    const float a = alpha ? alpha[((int64_t)f * H + h) * D + col] : 1.f;
+#pragma unroll
+    for (int t = 0; t < NTI; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) adj[(16 * (ti0 + t) + 4 * g + i) * LD + col] = acc[t][i] * a;
+    __syncthreads();
+  }
+  add_reads(0);
+  float* o = ds0 + ((int64_t)dir * H + h) * DD;
+  for (int e = tid; e < D * D; e += kWaves * 64) o[e] = adj[(e / D) * LD + e % D];
+}
+
+}  // namespace
+
+template <int D>
+static hipError_t launch_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w, hipStream_t st) {
+  constexpr size_t sm = (size_t)D * (D + 4) * 4;
+  (void)hipFuncSetAttribute((const void*)scan_bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  scan_bwd_mfma_kernel<D><<<dim3(s.H, 2), kWaves * 64, sm, st>>>(b.minv, in.alpha, w.dread, w.mslot, w.order, w.nscan,
+                                                                 s.T, s.H, s.Nc, w.dmf, w.dbf, w.ds0);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
+                                hipStream_t st) {
+  if (s.d == 128) return launch_t<128>(s, in, b, w, st);
+  if (s.d == 64) return launch_t<64>(s, in, b, w, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vdn
