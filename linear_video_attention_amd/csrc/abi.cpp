@@ -413,7 +413,8 @@ vdn_status ensure_backward(vdn_plan* p) {
   const size_t o_qr = take(qr.size() * 4), o_nqr = take(nqr.size() * 4);
   const size_t o_sa = take(seg_all.size() * sizeof(vdn::Segment)), o_sr = take(seg_read.size() * sizeof(vdn::Segment));
   const size_t o_kb = take(std::max<size_t>(1, kblocks.size()) * sizeof(int2));
-  const size_t mimg_bytes = (size_t)(6 + 4 * (s.Nc + 1) * H) * dd * 2;   // merge matrix images
+  // matrix images: the merge's, then (reusing the space) the token gradients'
+  const size_t mimg_bytes = (size_t)std::max<int64_t>(6 + 4 * (int64_t)(s.Nc + 1) * H, 6 * (int64_t)(T + 1) * H) * dd * 2;
   const size_t pack_bytes =
       mfma_bwd ? (size_t)H * d * 2 * (2 * Lq + 2 * s.Ls) + (size_t)rows * d * 2 + mimg_bytes : 0;
   const size_t o_pack = take(pack_bytes);

@@ -931,12 +931,22 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     (void)hipFuncSetAttribute((const void*)frame_mats_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm3);
     frame_mats_kernel<D><<<dim3(T + 1, H), kThreads, sm3, st>>>(b.minv, b.bw, w.dmf, w.dbf, w.ds0, T, H, s.n_text,
                                                                s.anchors, w.gsym, w.gdb);
-    const size_t sm4 = sizeof(TokSmem<D>);
-    (void)hipFuncSetAttribute((const void*)token_grads_kernel<Tin, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sm4);
-    token_grads_kernel<Tin, D><<<dim3((max(N, s.n_text) + kRows - 1) / kRows, T + 1, H), kThreads, sm4, st>>>(
-        (const Tin*)in.k, (const Tin*)in.v, in.beta, (const Tin*)in.text_kv, w.gsym, w.gdb, T, N, H, s.n_text,
-        s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
+    bool tok_done = false;   // matrix cores for the plans whose softmax transpose runs on them
+    if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128)) {
+      if (mfma_softmax) {
+        const hipError_t e = launch_token_grads_mfma(s, in, w, o, st);
+        if (e != hipSuccess) return e;
+        tok_done = true;
+      }
+    }
+    if (!tok_done) {
+      const size_t sm4 = sizeof(TokSmem<D>);
+      (void)hipFuncSetAttribute((const void*)token_grads_kernel<Tin, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)sm4);
+      token_grads_kernel<Tin, D><<<dim3((max(N, s.n_text) + kRows - 1) / kRows, T + 1, H), kThreads, sm4, st>>>(
+          (const Tin*)in.k, (const Tin*)in.v, in.beta, (const Tin*)in.text_kv, w.gsym, w.gdb, T, N, H, s.n_text,
+          s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
+    }
   }
   // dalpha: sum of both directions
   if (o.dalpha) {

@@ -19,6 +19,11 @@
 // are written by a small kernel in that row order, XOR-swizzled by 16-byte chunk, and copied into
 // LDS with global_load_lds, four images at a time.
 //
+// The same machinery serves the token gradients of the linear branch (section "Video Delta
+// Attention: A Frame-Wise Solution"): per written token, with G = dA + dA^T and dB of its frame (or of
+// the text, at beta / 2), dk += beta (G k + dB^T v), dv += beta dB k, dbeta += k^T dA k + v^T dB k,
+// i.e. three d x d products per row with the images G, dB^T and dB.
+//
 // Precision: q, dout, o_s and the weights are bf16 inputs, exact as MFMA operands.  The fp32
 // operands (the state S, dz_s, dz_l, do_l) enter as bf16 hi + lo pairs, so every product is exact
 // to about 2^-16 relative; sums accumulate in fp32.
@@ -317,6 +322,146 @@ __global__ __launch_bounds__(kWaves * 64) void merge_bwd_mfma_kernel(
   if (ok) store_vec<D>(dq + row * D, acc, g);
 }
 
+// Token-gradient images: per (slot, head) six images, G hi, G lo, dB^T hi, dB^T lo, dB hi, dB lo
+// (G = dA + dA^T is symmetric).  Boundary frames are never written and get no images.
+constexpr int kTokImages = 6;
+
+template <int D>
+__global__ __launch_bounds__(256) void token_images_kernel(const float* __restrict__ gsym, const float* __restrict__ gdb,
+                                                           int T, int H, int anchors, uint16_t* __restrict__ img) {
+  constexpr int64_t DD = (int64_t)D * D;
+  const int m = blockIdx.x % kTokImages, idx = blockIdx.x / kTokImages;   // idx = slot * H + head
+  const int slot = idx / H;
+  if (slot > 0 && anchors && (slot - 1 == 0 || slot - 1 == T - 1)) return;
+  const float* src = (m < 2 ? gsym : gdb) + (int64_t)idx * DD;
+  unsigned char* dst = reinterpret_cast<unsigned char*>(img + (int64_t)blockIdx.x * DD);
+  for (int e = threadIdx.x; e < D * (D / 8); e += 256) {
+    const int p = e / (D / 8), c = e % (D / 8);
+    const int j = perm_row(p);
+    uint16_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * c + i;
+      const float x = (m == 2 || m == 3) ? src[(int64_t)k * D + j] : src[(int64_t)j * D + k];   // dB^T or G, dB
+      const uint16_t hi = bf16_bits(x);
+      v[i] = (m & 1) ? bf16_bits(x - to_f32(hi)) : hi;
+    }
+    *reinterpret_cast<uint4*>(dst + img_off<D>(p, c)) = *reinterpret_cast<const uint4*>(v);
+  }
+}
+
+// one workgroup = 128 tokens of one slot (0: text, f + 1: frame f) and head, 8 waves x 16 tokens
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void token_grads_mfma_kernel(
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ beta,
+    const bf16_t* __restrict__ text_kv, const uint16_t* __restrict__ img, int T, int N, int H, int n_text,
+    int anchors, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
+    float* __restrict__ dtext_kv) {
+  constexpr int KS = D / 32, CT = D / 16;
+  constexpr int64_t DD = (int64_t)D * D;
+  constexpr int IMG = D * D * 2;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];   // four images
+  const int slot = blockIdx.y, h = blockIdx.z;
+  if (slot > 0 && anchors && (slot - 1 == 0 || slot - 1 == T - 1)) return;
+  const int U = slot == 0 ? n_text : N;
+  if ((int)blockIdx.x * kTok >= U) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int u = blockIdx.x * kTok + wave * 16 + l16;
+  const bool ok = u < U;
+  const float wscale = slot == 0 ? 0.5f : 1.0f;
+  const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
+  const bf16_t* kb = slot == 0 ? text_kv : k;
+  const bf16_t* vb = slot == 0 ? text_kv + (int64_t)n_text * H * D : v;
+  float* dkb = slot == 0 ? dtext_kv : dk;
+  float* dvb = slot == 0 ? dtext_kv + (int64_t)n_text * H * D : dv;
+  const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
+  const int64_t off = ((tok0 + (ok ? u : 0)) * H + h) * D;
+  const unsigned char* timg = reinterpret_cast<const unsigned char*>(img + (int64_t)kTokImages * ((int64_t)slot * H + h) * DD);
+
+  dma_image<D>(timg, smem, 0, wave, lane);            // G hi
+  dma_image<D>(timg + IMG, smem, 1, wave, lane);      // G lo
+  dma_image<D>(timg + 2 * IMG, smem, 2, wave, lane);  // dB^T hi
+  dma_image<D>(timg + 3 * IMG, smem, 3, wave, lane);  // dB^T lo
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 z = {};
+    kf[ks] = ok ? *reinterpret_cast<const bf16x8*>(kb + off + 32 * ks + 8 * g) : z;
+    vf[ks] = ok ? *reinterpret_cast<const bf16x8*>(vb + off + 32 * ks + 8 * g) : z;
+  }
+  const float wr = ok ? wscale * beta[(brow0 + u) * H + h] : 0.f;
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  f32x4 g1[CT], g2[CT];
+  zero_acc<D>(g1);
+  zero_acc<D>(g2);
+  product<D>(smem, 0, kf, g1, l16, g);                // G k
+  product<D>(smem, 1, kf, g1, l16, g);
+  product<D>(smem, 2, vf, g2, l16, g);                // dB^T v
+  product<D>(smem, 3, vf, g2, l16, g);
+  __syncthreads();                                    // every wave is done with buffers 0-3
+  dma_image<D>(timg + 4 * IMG, smem, 0, wave, lane);  // dB hi
+  dma_image<D>(timg + 5 * IMG, smem, 1, wave, lane);  // dB lo
+  // dk += beta (G k + dB^T v); the k^T dA k part of dbeta is k . (G k) / 2
+  float part = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ct = 2 * ks + (e >> 2), i = e & 3;
+      part += 0.5f * (float)kf[ks][e] * g1[ct][i];
+      g1[ct][i] = wr * (g1[ct][i] + g2[ct][i]);
+    }
+  if (ok) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        f32x4* p = reinterpret_cast<f32x4*>(dkb + off + 32 * ks + 8 * g + 4 * hlf);
+        *p += g1[2 * ks + hlf];
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  f32x4 gv[CT];
+  zero_acc<D>(gv);
+  product<D>(smem, 0, kf, gv, l16, g);                // dB k
+  product<D>(smem, 1, kf, gv, l16, g);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ct = 2 * ks + (e >> 2), i = e & 3;
+      part += (float)vf[ks][e] * gv[ct][i];
+      gv[ct][i] *= wr;
+    }
+  if (ok) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        f32x4* p = reinterpret_cast<f32x4*>(dvb + off + 32 * ks + 8 * g + 4 * hlf);
+        *p += gv[2 * ks + hlf];
+      }
+  }
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  if (ok && g == 0) dbeta[(brow0 + u) * H + h] += wscale * part;
+}
+
+template <int D>
+hipError_t launch_tok_t(const Shape& s, const Inputs& in, const BwdBuffers& w, const BwdOutputs& o, hipStream_t st) {
+  token_images_kernel<D><<<kTokImages * (s.T + 1) * s.H, 256, 0, st>>>(w.gsym, w.gdb, s.T, s.H, s.anchors, w.mimg);
+  constexpr size_t sm = (size_t)4 * D * D * 2;
+  (void)hipFuncSetAttribute((const void*)token_grads_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sm);
+  const int U = s.N > s.n_text ? s.N : s.n_text;
+  token_grads_mfma_kernel<D><<<dim3((U + kTok - 1) / kTok, s.T + 1, s.H), kWaves * 64, sm, st>>>(
+      (const bf16_t*)in.k, (const bf16_t*)in.v, in.beta, (const bf16_t*)in.text_kv, w.mimg, s.T, s.N, s.H, s.n_text,
+      s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w, const BwdOutputs& o,
                     hipStream_t st) {
@@ -332,6 +477,13 @@ hipError_t launch_t(const Shape& s, const Inputs& in, const Buffers& b, const Bw
 }
 
 }  // namespace
+
+hipError_t launch_token_grads_mfma(const Shape& s, const Inputs& in, const BwdBuffers& w, const BwdOutputs& o,
+                                   hipStream_t st) {
+  if (s.d == 128) return launch_tok_t<128>(s, in, w, o, st);
+  if (s.d == 64) return launch_tok_t<64>(s, in, w, o, st);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_merge_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                  const BwdOutputs& o, hipStream_t st) {

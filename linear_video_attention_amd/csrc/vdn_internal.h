@@ -131,7 +131,8 @@ struct BwdBuffers {
   int splits_all, splits_read, nscan;
   // MFMA softmax backward (bf16 plans, d in {64, 128})
   uint16_t* dos16;                      // [T*N][H][d] do_s in bf16
-  uint16_t* mimg;                       // merge matrix images: 6 weights, then 4 per (slot, head)
+  uint16_t* mimg;                       // matrix images of the merge (6 weights, 4 per chunk slot and head),
+                                        // later of the token gradients (6 per frame slot and head)
   uint16_t *qt, *dot;                   // [H][d][Lq] transposed q, do_s (bf16); pad columns zero
   uint16_t *kt, *vp;                    // [H][d][Ls] transposed keys, [H][Ls][d] key-major values
   int64_t Lq;                           // T*N + 64
@@ -148,6 +149,8 @@ hipError_t launch_xty_mfma(int d, const void* x, bool x_f32, const void* y, bool
                            int splits, int H, float* partial, hipStream_t st);
 hipError_t launch_scan_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                 hipStream_t st);
+hipError_t launch_token_grads_mfma(const Shape& s, const Inputs& in, const BwdBuffers& w, const BwdOutputs& o,
+                                   hipStream_t st);
 hipError_t launch_merge_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                  const BwdOutputs& o, hipStream_t st);
 hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
