@@ -864,9 +864,8 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
       if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128) &&
                     std::is_same<TX, float>::value != std::is_same<TY, float>::value) {
         if (mfma_softmax) {
-          (void)launch_xty_mfma(D, x, std::is_same<TX, float>::value, y, std::is_same<TY, float>::value, segs, nseg,
-                                splits, H, w.partial, st);
-          on_mfma = true;
+          on_mfma = launch_xty_mfma(D, x, std::is_same<TX, float>::value, y, std::is_same<TY, float>::value, segs,
+                                    nseg, splits, H, w.partial, st) == hipSuccess;   // else the generic kernel
         }
       }
       if (!on_mfma)
