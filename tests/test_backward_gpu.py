@@ -63,6 +63,8 @@ BWD_RAGGED = [
     (3, 1, 16, 5, 1, 64, "fp32", True, False),
     (7, 11, 72, 3, 2, 128, "bf16", True, True),
     (2, 6, 64, 1, 1, 128, "bf16", False, False),
+    # more than one 128-row block per frame and of text rows, both ragged, on the d = 64 kernels
+    (150, 6, 130, 2, 1, 64, "bf16", True, True),
 ]
 
 
