@@ -46,6 +46,13 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-source flags.  The window-softmax kernel is scheduled by LLVM's instruction-level-parallelism
+# strategy: its matrix and vector instruction streams interleave better (about 4 % faster at 768p,
+# identical results).
+FILE_FLAGS = {
+    "softmax_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -56,7 +63,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool, out_dir: str, extra: list) -> str:
     obj = os.path.join(out_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), "-x", "hip", *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
