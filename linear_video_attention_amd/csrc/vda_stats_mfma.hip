@@ -9,7 +9,7 @@
 //
 // [A; B] = [K V]^T Diag(beta) K is one (2d x d) product with the tokens as the reduction
 // dimension, run on v_mfma_f32_32x32x16_bf16:
-//   * tokens stream through LDS 64 at a time, copied straight from global memory in their natural
+//   * tokens stream through LDS 32 (d = 128) or 64 at a time, copied straight from global memory in their natural
 //     token-major layout (global_load_lds, three stages: two tiles in flight while one is used),
 //     16-byte chunks XOR-swizzled per row; beta comes along the same way;
 //   * Y = Diag(beta) K is formed once per tile in LDS as two bf16 parts, beta k = Yh + Yl to
@@ -33,7 +33,14 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
 
-constexpr int kTU = 64;             // tokens per tile
+// tokens per tile: 32 at d = 128 (70 KB of LDS, two workgroups per CU, so every frame of a 768p
+// layer is resident at once: 0.207 -> 0.180 ms with the inverse), 64 at d = 64 (a DMA instruction
+// per wave needs 8 KB tiles)
+#ifndef VDN_GRAM_TU
+#define VDN_GRAM_TU 32
+#endif
+template <int D>
+constexpr int tile_tokens() { return D == 128 ? VDN_GRAM_TU : 64; }
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
@@ -50,6 +57,7 @@ constexpr int kStages = 3;
 template <int D>
 struct GramSmem {
   static constexpr int ROW = 2 * D;                    // bytes per token row
+  static constexpr int kTU = tile_tokens<D>();
   static constexpr int TILE = kTU * ROW;               // one matrix, one tile
   static constexpr int BETA = 2 * TILE;                // beta: wave w's 256 bytes hold tokens 8w..8w+7
   static constexpr int STAGE = BETA + kWaves * 256;    // K, V, beta
@@ -78,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* _
   constexpr int CH = D / 8;                 // 16-byte chunks per token row
   constexpr int ROWS_PER_KB = 1024 / SM::ROW;
   constexpr int DMA = SM::TILE / 1024 / kWaves;   // DMA instructions per wave per matrix and tile
+  constexpr int kTU = SM::kTU;
   constexpr int YCH = kTU * CH / kThreads;        // Y chunks per thread per tile
   constexpr int MT = D / 64, NT = D / 64;
   constexpr int kVmcntTile = 0x0F70 | (2 * DMA + 1);   // s_waitcnt vmcnt(one tile's loads of a wave)
