@@ -887,8 +887,17 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   if (w.nscan > 0) {
     const size_t sm1 = (size_t)D * (D + 1) * 4 + (size_t)16 * D * 4;
     (void)hipFuncSetAttribute((const void*)frame_states_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm1);
-    frame_states_kernel<D><<<dim3(Nc, H, 2), kThreads, sm1, st>>>(b.states, b.minv, b.bw, in.alpha, T, s.C, s.anchors,
-                                                                 H, Nc, w.zin);
+    bool walked = false;   // matrix cores for the plans whose softmax transpose runs on them
+    if constexpr (std::is_same<Tin, bf16_t>::value && (D == 64 || D == 128)) {
+      if (mfma_softmax) {
+        const hipError_t e = launch_frame_states_mfma(s, in, b, w, st);
+        if (e != hipSuccess) return e;
+        walked = true;
+      }
+    }
+    if (!walked)
+      frame_states_kernel<D><<<dim3(Nc, H, 2), kThreads, sm1, st>>>(b.states, b.minv, b.bw, in.alpha, T, s.C,
+                                                                   s.anchors, H, Nc, w.zin);
   }
   {
     const size_t sm2 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;

@@ -1,4 +1,5 @@
-// Adjoint chain of the frame scan on CDNA4 matrix cores (bf16 plans, d in {64, 128}).
+// Adjoint chain of the frame scan, and the states entering each scanned frame, on CDNA4 matrix
+// cores (bf16 plans, d in {64, 128}).
 //
 // "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Video Delta
 // Attention: A Frame-Wise Solution": each scanned frame maps the state as
@@ -116,6 +117,82 @@ __global__ __launch_bounds__(kWaves * 64) void scan_bwd_mfma_kernel(
   for (int e = tid; e < D * D; e += kWaves * 64) o[e] = adj[(e / D) * LD + e % D];
 }
 
+// States entering the scanned frames, walked per (chunk, head, direction) from the forward's chunk
+// state like the generic frame_states_kernel: Z <- (Z Diag(alpha_f) + B_f) M_f frame by frame (M_f
+// symmetric, so row j of M_f is column j), storing Z before every frame of the chunk.  Same product
+// layout as the chain above; Z lives in LDS in fp32.
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void frame_states_mfma_kernel(
+    const float* __restrict__ states, const float* __restrict__ minv, const float* __restrict__ bw,
+    const float* __restrict__ alpha, int T, int C, int anchors, int H, int Nc, float* __restrict__ zin) {
+  constexpr int KS = D / 32, TJ = D / 16, TI = D / 16;
+  constexpr int WPC = kWaves / TJ, NTI = TI / WPC;
+  constexpr int LD = D + 4;
+  constexpr int64_t DD = (int64_t)D * D;
+  extern __shared__ __attribute__((aligned(16))) float z[];   // D x LD
+  const int c = blockIdx.x, h = blockIdx.y, dir = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int tj = wave % TJ, ti0 = (wave / TJ) * NTI;
+  int slot, f_first, f_last;
+  if (dir == 0) {
+    slot = min(c + 1, Nc - 1);
+    f_first = max(slot - 1, 0) * C;
+    f_last = min((c + 1) * C, T) - 1;
+  } else {
+    slot = max(c - 1, 0);
+    f_first = min((slot + 2) * C, T) - 1;
+    f_last = c * C;
+  }
+  const float* s0 = states + ((int64_t)(dir * (Nc + 1) + slot) * H + h) * DD;
+  for (int e = tid; e < D * D; e += kWaves * 64) z[(e / D) * LD + e % D] = s0[e];
+  __syncthreads();
+  const int step = dir == 0 ? 1 : -1;
+  const int col = 16 * tj + l16;
+  for (int f = f_first;; f += step) {
+    if (!(anchors && (f == 0 || f == T - 1))) {
+      if (f / C == c) {
+        float* zo = zin + (((int64_t)dir * T + f) * H + h) * DD;
+        for (int e = tid; e < D * D; e += kWaves * 64) zo[e] = z[(e / D) * LD + e % D];
+      }
+      const float* af = alpha ? alpha + ((int64_t)f * H + h) * D : nullptr;
+      const float* bf = bw + ((int64_t)(1 + f) * H + h) * DD;
+      const float* mf = minv + ((int64_t)(1 + f) * H + h) * DD + (int64_t)col * D + 8 * g;
+      bf16x8 bh[KS], bl[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        split8(*reinterpret_cast<const float4*>(mf + 32 * ks), *reinterpret_cast<const float4*>(mf + 32 * ks + 4),
+               bh[ks], bl[ks]);
+      __syncthreads();                           // the copy-out of Z is done
+      for (int e = tid; e < D * D; e += kWaves * 64) {
+        const int r = e / D, cc = e % D;
+        z[r * LD + cc] = z[r * LD + cc] * (af ? af[cc] : 1.f) + bf[e];
+      }
+      __syncthreads();
+      f32x4 acc[NTI];
+#pragma unroll
+      for (int t = 0; t < NTI; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < NTI; ++t) {
+          const float* ar = z + (16 * (ti0 + t) + l16) * LD + 32 * ks + 8 * g;
+          bf16x8 ah, al;
+          split8(*reinterpret_cast<const float4*>(ar), *reinterpret_cast<const float4*>(ar + 4), ah, al);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[ks], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[ks], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[ks], acc[t], 0, 0, 0);
+        }
+      __syncthreads();                           // every wave is done reading the right-hand side
+#pragma unroll
+      for (int t = 0; t < NTI; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[(16 * (ti0 + t) + 4 * g + i) * LD + col] = acc[t][i];
+      __syncthreads();
+    }
+    if (f == f_last) break;
+  }
+}
+
 }  // namespace
 
 template <int D>
@@ -125,6 +202,23 @@ static hipError_t launch_t(const Shape& s, const Inputs& in, const Buffers& b, c
   scan_bwd_mfma_kernel<D><<<dim3(s.H, 2), kWaves * 64, sm, st>>>(b.minv, in.alpha, w.dread, w.mslot, w.order, w.nscan,
                                                                  s.T, s.H, s.Nc, w.dmf, w.dbf, w.ds0);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fs(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w, hipStream_t st) {
+  constexpr size_t sm = (size_t)D * (D + 4) * 4;
+  (void)hipFuncSetAttribute((const void*)frame_states_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sm);
+  frame_states_mfma_kernel<D><<<dim3(s.Nc, s.H, 2), kWaves * 64, sm, st>>>(b.states, b.minv, b.bw, in.alpha, s.T, s.C,
+                                                                          s.anchors, s.H, s.Nc, w.zin);
+  return hipGetLastError();
+}
+
+hipError_t launch_frame_states_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
+                                   hipStream_t st) {
+  if (s.d == 128) return launch_fs<128>(s, in, b, w, st);
+  if (s.d == 64) return launch_fs<64>(s, in, b, w, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_scan_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,

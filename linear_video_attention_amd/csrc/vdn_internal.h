@@ -147,6 +147,8 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const Buffers& b, c
 // partial[seg][split] = sum over the split's rows of x^T y (one of x, y fp32, the other bf16)
 hipError_t launch_xty_mfma(int d, const void* x, bool x_f32, const void* y, bool y_f32, const Segment* segs, int nseg,
                            int splits, int H, float* partial, hipStream_t st);
+hipError_t launch_frame_states_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
+                                   hipStream_t st);
 hipError_t launch_scan_bwd_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                 hipStream_t st);
 hipError_t launch_token_grads_mfma(const Shape& s, const Inputs& in, const BwdBuffers& w, const BwdOutputs& o,
