@@ -373,16 +373,23 @@ __global__ __launch_bounds__(kThreads) void xty_partial_kernel(const TX* __restr
     for (int jj = 0; jj < R; ++jj) out[(int64_t)(ty * R + ii) * D + tx * R + jj] = c[ii][jj];
 }
 
-// grid (segments, D*D / 256): one thread per output element, summing the splits in order
+// grid (segments, D*D / 256): one thread per output element, summing the splits as eight
+// interleaved partial sums (eight loads in flight), then those pairwise
 template <int D>
 __global__ __launch_bounds__(kThreads) void xty_reduce_kernel(const float* __restrict__ partial, int splits,
                                                               float* __restrict__ out, float scale) {
   const int s = blockIdx.x;
   const int e = blockIdx.y * kThreads + threadIdx.x;
   if (e >= D * D) return;
-  float acc = 0.f;
-  for (int k = 0; k < splits; ++k) acc += partial[((int64_t)s * splits + k) * D * D + e];
-  out[(int64_t)s * D * D + e] = acc * scale;
+  const float* p = partial + (int64_t)s * splits * D * D + e;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 8 <= splits; k += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += p[(int64_t)(k + u) * D * D];
+  for (; k < splits; ++k) acc[0] += p[(int64_t)k * D * D];
+  const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  out[(int64_t)s * D * D + e] = sum * scale;
 }
 
 // ---- 3. states entering every scanned frame, per (chunk, head, direction) ----
