@@ -66,11 +66,6 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ x, bf16_t* __restrict__ y, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) y[i] = __builtin_bit_cast(bf16_t, (__bf16)x[i]);
-}
-
 __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
                                                         int64_t rows, int H, int D, int64_t ld, int64_t row0) {
   const int64_t r = (int64_t)blockIdx.x;
@@ -732,10 +727,8 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   const int T = s.T, N = s.N, H = s.H;
   const int64_t TN = (int64_t)T * N;
   const float tau = 1.0f / sqrtf((float)D);
-  // packing: the softmax output gradient do_s in bf16; Q^T, dO_s^T [H][D][Lq]; K^T [H][D][Ls]; V
+  // packing (do_s arrives in bf16 from the merge): Q^T, dO_s^T [H][D][Lq]; K^T [H][D][Ls]; V
   // key-major [H][Ls][D]
-  const int64_t nel = TN * H * D;
-  to_bf16_kernel<<<(int)((nel + 255) / 256), 256, 0, st>>>(w.do_s, w.dos16, nel);
   pack_t_kernel<<<dim3((int)((TN + 63) / 64), H, D / 64), 256, 0, st>>>((const bf16_t*)in.q, w.qt, TN, H, D, w.Lq, 0);
   pack_t_kernel<<<dim3((int)((TN + 63) / 64), H, D / 64), 256, 0, st>>>(w.dos16, w.dot, TN, H, D, w.Lq, 0);
   if (s.n_text > 0) {

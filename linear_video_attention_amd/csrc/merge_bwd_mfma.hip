@@ -173,7 +173,7 @@ __device__ __forceinline__ void store_vec(float* __restrict__ dst, const f32x4 (
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void merge_bwd_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ o_s, const bf16_t* __restrict__ dout,
-    const uint16_t* __restrict__ img, float* __restrict__ dq, float* __restrict__ do_s, float* __restrict__ do_l,
+    const uint16_t* __restrict__ img, float* __restrict__ dq, bf16_t* __restrict__ dos16, float* __restrict__ do_l,
     float* __restrict__ x_s, float* __restrict__ x_l, float* __restrict__ dz_s, float* __restrict__ dz_l,
     float* __restrict__ dsum, int T, int N, int C, int Nc, int H, int anchors) {
   constexpr int KS = D / 32, CT = D / 16;
@@ -229,7 +229,13 @@ __global__ __launch_bounds__(kWaves * 64) void merge_bwd_mfma_kernel(
         ga[ct][i] = s_ * os;
       }
     if (ok) {
-      store_vec<D>(do_s + row * D, dx, g);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {             // do_s in bf16 (the softmax transpose's operand)
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)at<D>(dx, ks, e);
+        *reinterpret_cast<bf16x8*>(dos16 + row * D + 32 * ks + 8 * g) = v;
+      }
       store_vec<D>(x_s + row * D, ga, g);
       store_vec<D>(dz_s + row * D, zs, g);
     }
@@ -471,7 +477,7 @@ hipError_t launch_t(const Shape& s, const Inputs& in, const Buffers& b, const Bw
   constexpr size_t sm = (size_t)4 * D * D * 2;
   (void)hipFuncSetAttribute((const void*)merge_bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   merge_bwd_mfma_kernel<D><<<dim3((s.N + kTok - 1) / kTok, s.T, s.H), kWaves * 64, sm, st>>>(
-      (const bf16_t*)in.q, (const bf16_t*)b.os, (const bf16_t*)w.dout, w.mimg, o.dq, w.do_s, w.do_l, w.x_s, w.x_l,
+      (const bf16_t*)in.q, (const bf16_t*)b.os, (const bf16_t*)w.dout, w.mimg, o.dq, w.dos16, w.do_l, w.x_s, w.x_l,
       w.dz_s, w.dz_l, w.dsum, s.T, s.N, s.C, s.Nc, s.H, s.anchors);
   return hipGetLastError();
 }

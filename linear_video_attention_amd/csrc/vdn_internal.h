@@ -115,7 +115,7 @@ struct Segment {
 // Backward workspace (device) and host-built tables.
 struct BwdBuffers {
   const void* dout;                     // [T*N][H][d] plan dtype (the caller's)
-  float *do_s, *do_l, *x_s, *x_l, *dz_s, *dz_l;   // [T*N][H][d]
+  float *do_s, *do_l, *x_s, *x_l, *dz_s, *dz_l;   // [T*N][H][d] (do_s: generic kernels only)
   float *dsum, *lse;                    // [T*N][H]
   float* partial;                       // [segments][splits][d][d]
   float* dread;                         // [Nc+2][H][d][d] readout adjoints (slots Nc, Nc+1: frames 0, T-1)
