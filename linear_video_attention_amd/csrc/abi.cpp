@@ -10,6 +10,163 @@
 
 #include "vdn_internal.h"
 
+namespace vdn {
+
+Buffers make_buffers(char* ws, const Layout& lay, const Kinds& kinds, const Shape& s) {
+  Buffers b{};
+  b.os = ws + lay.os;
+  b.kp = kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + lay.kp) : nullptr;
+  b.vt = kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + lay.vt) : nullptr;
+  b.minv = reinterpret_cast<float*>(ws + lay.minv);
+  b.bw = reinterpret_cast<float*>(ws + lay.bw);
+  b.mhl = kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + lay.mhl) : nullptr;
+  b.cw = kinds.scan_mfma ? reinterpret_cast<float*>(ws + lay.cw) : nullptr;
+  b.pp = kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + lay.pp) : nullptr;
+  b.qq = kinds.scan_mfma ? reinterpret_cast<float*>(ws + lay.qq) : nullptr;
+  b.states = reinterpret_cast<float*>(ws + lay.states);
+  b.wt = kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + lay.wt) : nullptr;
+  const bool packed = kinds.softmax_mfma || kinds.softmax_fp8;
+  b.kmax_part = kinds.softmax_mfma ? reinterpret_cast<float*>(ws + lay.kmax_part) : nullptr;
+  b.kmax = packed ? reinterpret_cast<float*>(ws + lay.kmax) : nullptr;
+  b.flags = packed ? reinterpret_cast<int*>(ws + lay.flags) : nullptr;
+  b.k8 = kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + lay.k8) : nullptr;
+  b.v8 = kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + lay.v8) : nullptr;
+  b.part8 = kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + lay.part8) : nullptr;
+  b.scale8 = kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + lay.scale8) : nullptr;
+  b.lse = kinds.softmax_fp8 ? nullptr : reinterpret_cast<float*>(ws + lay.lse);
+  b.ranges = reinterpret_cast<const int*>(ws + lay.ranges);
+  b.nranges = b.ranges + (size_t)(s.T + 1) * 2 * kMaxRanges;
+  return b;
+}
+
+Shape make_shape(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors, vdn_dtype dt) {
+  Shape s{};
+  s.T = T; s.N = N; s.C = C; s.n_text = n_text; s.H = H; s.d = d; s.anchors = anchors; s.dtype = dt;
+  s.n_audio = n_audio;
+  s.n_ctx = n_text + n_audio;
+  s.Nc = (T + C - 1) / C;
+  s.ctx_pad = (int)round_up(s.n_ctx, kTextPad);
+  s.Lk = (int64_t)s.ctx_pad + (int64_t)T * N;
+  s.Ls = s.Lk + 128;
+  s.Ls8 = s.Lk + 128;
+  return s;
+}
+
+bool shape_ok(int T, int N, int C, int n_text, int H, int d, int anchors) {
+  return T > 0 && N > 0 && C > 0 && n_text >= 0 && H > 0 && d > 0 && (anchors == 0 || anchors == 1);
+}
+
+vdn_status check_plan_args(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors,
+                           vdn_dtype dtype, unsigned flags) {
+  if (!shape_ok(T, N, C, n_text, H, d, anchors) || n_audio < 0) return VDN_ERR_INVALID_ARG;
+  const int64_t n_ctx = (int64_t)n_text + n_audio;
+  if (dtype != VDN_F32 && dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return VDN_ERR_UNSUPPORTED;
+  // keep every index well inside 63 bits and grid dimensions inside their limits
+  const int64_t tokens = (int64_t)T * N;
+  if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || n_ctx * H * d > (int64_t(1) << 40))
+    return VDN_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP | VDN_FLAG_FP8_SOFTMAX))
+    return VDN_ERR_INVALID_ARG;
+  if ((flags & VDN_FLAG_SERIAL) && (flags & VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
+  const bool fp8 = (flags & VDN_FLAG_FP8_SOFTMAX) != 0;
+  if (fp8 && (flags & VDN_FLAG_GENERIC_KERNELS)) return VDN_ERR_INVALID_ARG;
+  // FP8 softmax: bf16 inputs, d = 128, key tiles 16-key aligned, 32-bit lane offsets into V8
+  if (fp8 && (dtype != VDN_BF16 || d != 128 || N % 16 != 0 ||
+              (int64_t)d * (round_up(n_ctx, kTextPad) + tokens + 128) >= (int64_t(1) << 31)))
+    return VDN_ERR_UNSUPPORTED;
+  if (round_up(n_ctx, kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
+  return VDN_OK;
+}
+
+namespace {
+
+bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool spans_overlap(const Span& x, const Span& y) {
+  if (!x.p || !y.p || x.n == 0 || y.n == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(x.p), b = reinterpret_cast<uintptr_t>(y.p);
+  return a < b + y.n && b < a + x.n;
+}
+
+vdn_status check_forward_args(const Shape& s, const Inputs& in) {
+  if (!in.q || !in.k || !in.v || !in.beta || !in.gate_w || !in.proj_w || !in.out) return VDN_ERR_INVALID_ARG;
+  if (s.n_ctx > 0 && !in.text_kv) return VDN_ERR_INVALID_ARG;
+  if (!in.ctx_q != !in.ctx_out) return VDN_ERR_INVALID_ARG;          // context rows: both or neither
+  const void* ptrs[] = {in.q, in.k, in.v, in.beta, in.gate_w, in.proj_w, in.out};
+  for (const void* ptr : ptrs) if (!is_aligned16(ptr)) return VDN_ERR_INVALID_ARG;
+  const void* opt[] = {in.text_kv, in.alpha, in.ctx_q, in.ctx_out};
+  for (const void* ptr : opt) if (ptr && !is_aligned16(ptr)) return VDN_ERR_INVALID_ARG;
+  // the outputs' bytes are disjoint from every input's and from each other's
+  const size_t elt = s.dtype == VDN_BF16 ? 2 : 4;
+  const size_t tok = (size_t)s.T * s.N * s.H * s.d * elt;
+  const size_t ctx = (size_t)s.n_ctx * s.H * s.d * elt;
+  const size_t dd2 = (size_t)2 * s.d * s.d * elt;
+  const Span ins[] = {{in.q, tok},
+                      {in.k, tok},
+                      {in.v, tok},
+                      {in.beta, ((size_t)s.n_text + (size_t)s.T * s.N) * s.H * 4},
+                      {s.n_ctx > 0 ? in.text_kv : nullptr, 2 * ctx},
+                      {in.gate_w, dd2},
+                      {in.proj_w, dd2},
+                      {in.alpha, (size_t)s.T * s.H * s.d * 4},
+                      {in.ctx_q, ctx}};
+  const Span outs[] = {{in.out, tok}, {in.ctx_out, ctx}};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (spans_overlap(o, i)) return VDN_ERR_INVALID_ARG;
+  if (spans_overlap(outs[0], outs[1])) return VDN_ERR_INVALID_ARG;
+  return VDN_OK;
+}
+
+hipError_t enqueue_forward(const Shape& s, const Kinds& kinds, const Buffers& b, const Inputs& in, hipStream_t main,
+                           hipStream_t side, hipEvent_t ev_fork, hipEvent_t ev_join, hipEvent_t* ev) {
+  auto mark = [&](int stage, int end, hipStream_t st) {
+    if (ev) (void)hipEventRecord(ev[stage * 2 + end], st);
+  };
+  hipError_t e = hipSuccess;
+#define VDN_TRY(x) do { if ((e = (x)) != hipSuccess) return e; } while (0)
+  mark(VDN_STAGE_TOTAL, 0, main);
+  // linear branch: on the caller's stream, or for overlapped plans on the side stream, forked from
+  // the caller's stream
+  hipStream_t lin = side ? side : main;
+  if (side) {
+    VDN_TRY(hipEventRecord(ev_fork, main));
+    VDN_TRY(hipStreamWaitEvent(side, ev_fork, 0));
+  }
+  mark(VDN_STAGE_VDA_STATS, 0, lin);
+  VDN_TRY(launch_vda_stats(s, in, b, kinds.stats_mfma, lin));
+  mark(VDN_STAGE_VDA_STATS, 1, lin);
+  mark(VDN_STAGE_VDA_SCAN, 0, lin);
+  VDN_TRY(launch_vda_scan(s, in, b, kinds.scan_mfma, lin));
+  mark(VDN_STAGE_VDA_SCAN, 1, lin);
+  if (side) VDN_TRY(hipEventRecord(ev_join, side));
+  // softmax branch on the caller's stream
+  mark(VDN_STAGE_PREP, 0, main);
+  if (kinds.softmax_mfma) VDN_TRY(launch_prep_kv(s, in, b, main));
+  if (kinds.softmax_fp8) VDN_TRY(launch_prep_fp8(s, in, b, main));
+  if (kinds.epilogue_mfma) VDN_TRY(launch_prep_weights(s, in, b, main));
+  mark(VDN_STAGE_PREP, 1, main);
+  mark(VDN_STAGE_SOFTMAX, 0, main);
+  if (kinds.softmax_fp8) VDN_TRY(launch_softmax_fp8(s, in, b, main));
+  else if (kinds.softmax_mfma) VDN_TRY(launch_softmax_mfma(s, in, b, main));
+  else VDN_TRY(launch_softmax_simt(s, in, b, main));
+  mark(VDN_STAGE_SOFTMAX, 1, main);
+  // join, then readout + gates + projections
+  if (side) VDN_TRY(hipStreamWaitEvent(main, ev_join, 0));
+  mark(VDN_STAGE_EPILOGUE, 0, main);
+  if (kinds.epilogue_mfma) VDN_TRY(launch_epilogue_mfma(s, in, b, main));
+  else VDN_TRY(launch_epilogue(s, in, b, false, main));
+  mark(VDN_STAGE_EPILOGUE, 1, main);
+  mark(VDN_STAGE_TOTAL, 1, main);
+#undef VDN_TRY
+  return hipSuccess;
+}
+
+}  // namespace vdn
+
 struct vdn_plan {
   vdn::Shape s;
   vdn::Layout lay;
@@ -34,33 +191,7 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-vdn::Buffers buffers_of(const vdn_plan* p) {
-  vdn::Buffers b{};
-  char* ws = p->ws;
-  b.os = ws + p->lay.os;
-  b.kp = p->kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.kp) : nullptr;
-  b.vt = p->kinds.softmax_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.vt) : nullptr;
-  b.minv = reinterpret_cast<float*>(ws + p->lay.minv);
-  b.bw = reinterpret_cast<float*>(ws + p->lay.bw);
-  b.mhl = p->kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.mhl) : nullptr;
-  b.cw = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.cw) : nullptr;
-  b.pp = p->kinds.scan_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.pp) : nullptr;
-  b.qq = p->kinds.scan_mfma ? reinterpret_cast<float*>(ws + p->lay.qq) : nullptr;
-  b.states = reinterpret_cast<float*>(ws + p->lay.states);
-  b.wt = p->kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + p->lay.wt) : nullptr;
-  const bool packed = p->kinds.softmax_mfma || p->kinds.softmax_fp8;
-  b.kmax_part = p->kinds.softmax_mfma ? reinterpret_cast<float*>(ws + p->lay.kmax_part) : nullptr;
-  b.kmax = packed ? reinterpret_cast<float*>(ws + p->lay.kmax) : nullptr;
-  b.flags = packed ? reinterpret_cast<int*>(ws + p->lay.flags) : nullptr;
-  b.k8 = p->kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + p->lay.k8) : nullptr;
-  b.v8 = p->kinds.softmax_fp8 ? reinterpret_cast<uint8_t*>(ws + p->lay.v8) : nullptr;
-  b.part8 = p->kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + p->lay.part8) : nullptr;
-  b.scale8 = p->kinds.softmax_fp8 ? reinterpret_cast<float*>(ws + p->lay.scale8) : nullptr;
-  b.lse = p->kinds.softmax_fp8 ? nullptr : reinterpret_cast<float*>(ws + p->lay.lse);
-  b.ranges = reinterpret_cast<const int*>(ws + p->lay.ranges);
-  b.nranges = b.ranges + (size_t)(p->s.T + 1) * 2 * vdn::kMaxRanges;
-  return b;
-}
+vdn::Buffers buffers_of(const vdn_plan* p) { return vdn::make_buffers(p->ws, p->lay, p->kinds, p->s); }
 
 void free_plan(vdn_plan* p) {
   if (!p) return;
@@ -72,23 +203,6 @@ void free_plan(vdn_plan* p) {
   if (p->ws) (void)hipFree(p->ws);
   if (p->bws) (void)hipFree(p->bws);
   delete p;
-}
-
-bool shape_ok(int T, int N, int C, int n_text, int H, int d, int anchors) {
-  return T > 0 && N > 0 && C > 0 && n_text >= 0 && H > 0 && d > 0 && (anchors == 0 || anchors == 1);
-}
-
-vdn::Shape make_shape(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors, vdn_dtype dt) {
-  vdn::Shape s{};
-  s.T = T; s.N = N; s.C = C; s.n_text = n_text; s.H = H; s.d = d; s.anchors = anchors; s.dtype = dt;
-  s.n_audio = n_audio;
-  s.n_ctx = n_text + n_audio;
-  s.Nc = (T + C - 1) / C;
-  s.ctx_pad = (int)vdn::round_up(s.n_ctx, vdn::kTextPad);
-  s.Lk = (int64_t)s.ctx_pad + (int64_t)T * N;
-  s.Ls = s.Lk + 128;
-  s.Ls8 = s.Lk + 128;
-  return s;
 }
 
 }  // namespace
@@ -107,17 +221,17 @@ const char* vdn_status_str(vdn_status s) {
 }
 
 int vdn_key_ranges(int T, int N, int C, int n_text, int anchors, int t, int64_t* ranges, int max_ranges) {
-  if (!shape_ok(T, N, C, n_text, 1, 1, anchors) || t < 0 || t >= T || (max_ranges > 0 && !ranges) || max_ranges < 0)
+  if (!vdn::shape_ok(T, N, C, n_text, 1, 1, anchors) || t < 0 || t >= T || (max_ranges > 0 && !ranges) || max_ranges < 0)
     return -1;
-  vdn::Shape s = make_shape(T, N, C, n_text, 0, 1, 1, anchors, VDN_F32);
+  vdn::Shape s = vdn::make_shape(T, N, C, n_text, 0, 1, 1, anchors, VDN_F32);
   return vdn::key_ranges(s, t, ranges, max_ranges);
 }
 
 int vdn_scan_frames(int T, int C, int anchors, int t, int dir, int* frames, int max_frames) {
-  if (!shape_ok(T, 1, C, 0, 1, 1, anchors) || t < 0 || t >= T || (dir != 0 && dir != 1) ||
+  if (!vdn::shape_ok(T, 1, C, 0, 1, 1, anchors) || t < 0 || t >= T || (dir != 0 && dir != 1) ||
       (max_frames > 0 && !frames) || max_frames < 0)
     return -1;
-  vdn::Shape s = make_shape(T, 1, C, 0, 0, 1, 1, anchors, VDN_F32);
+  vdn::Shape s = vdn::make_shape(T, 1, C, 0, 0, 1, 1, anchors, VDN_F32);
   return vdn::scan_frames(s, t, dir, frames, max_frames);
 }
 
@@ -135,28 +249,13 @@ vdn_status vdn_plan_create_joint(int T, int N, int C, int n_text, int n_audio, i
                                  vdn_dtype dtype, unsigned flags, vdn_plan** plan_out) {
   if (!plan_out) return VDN_ERR_INVALID_ARG;
   *plan_out = nullptr;
-  if (!shape_ok(T, N, C, n_text, H, d, anchors) || n_audio < 0) return VDN_ERR_INVALID_ARG;
-  const int64_t n_ctx = (int64_t)n_text + n_audio;
-  if (dtype != VDN_F32 && dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
-  if (d != 16 && d != 32 && d != 64 && d != 128) return VDN_ERR_UNSUPPORTED;
-  // keep every index well inside 63 bits and grid dimensions inside their limits
-  const int64_t tokens = (int64_t)T * N;
-  if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || n_ctx * H * d > (int64_t(1) << 40))
-    return VDN_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP | VDN_FLAG_FP8_SOFTMAX))
-    return VDN_ERR_INVALID_ARG;
-  if ((flags & VDN_FLAG_SERIAL) && (flags & VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
+  const vdn_status chk = vdn::check_plan_args(T, N, C, n_text, n_audio, H, d, anchors, dtype, flags);
+  if (chk != VDN_OK) return chk;
   const bool fp8 = (flags & VDN_FLAG_FP8_SOFTMAX) != 0;
-  if (fp8 && (flags & VDN_FLAG_GENERIC_KERNELS)) return VDN_ERR_INVALID_ARG;
-  // FP8 softmax: bf16 inputs, d = 128, key tiles 16-key aligned, 32-bit lane offsets into V8
-  if (fp8 && (dtype != VDN_BF16 || d != 128 || N % 16 != 0 ||
-              (int64_t)d * (vdn::round_up(n_ctx, vdn::kTextPad) + tokens + 128) >= (int64_t(1) << 31)))
-    return VDN_ERR_UNSUPPORTED;
-  if (vdn::round_up(n_ctx, vdn::kTextPad) + tokens > INT32_MAX) return VDN_ERR_UNSUPPORTED;
 
   vdn_plan* p = new (std::nothrow) vdn_plan();
   if (!p) return VDN_ERR_OUT_OF_MEMORY;
-  p->s = make_shape(T, N, C, n_text, n_audio, H, d, anchors, dtype);
+  p->s = vdn::make_shape(T, N, C, n_text, n_audio, H, d, anchors, dtype);
   p->kinds = (flags & VDN_FLAG_GENERIC_KERNELS) ? vdn::Kinds{} : vdn::choose_kinds(p->s);
   if (fp8) {
     p->kinds.softmax_mfma = false;
@@ -219,75 +318,27 @@ namespace {
 vdn_status forward_impl(const vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
                         const void* ctx_q, const void* text_kv, const float* alpha, const void* gate_w,
                         const void* proj_w, void* out, void* ctx_out, void* stream) {
-  if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !out) return VDN_ERR_INVALID_ARG;
-  if (plan->s.n_ctx > 0 && !text_kv) return VDN_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, out};
-  for (const void* ptr : ptrs) if (!aligned16(ptr)) return VDN_ERR_INVALID_ARG;
-  if (text_kv && !aligned16(text_kv)) return VDN_ERR_INVALID_ARG;
-  if (out == q || out == k || out == v || out == text_kv) return VDN_ERR_INVALID_ARG;
-  if (alpha && (!aligned16(alpha) || alpha == out)) return VDN_ERR_INVALID_ARG;
+  if (!plan) return VDN_ERR_INVALID_ARG;
   if (!ctx_q != !ctx_out) return VDN_ERR_INVALID_ARG;          // context rows: both or neither
   if (plan->s.n_ctx == 0) ctx_q = ctx_out = nullptr;
-  if (ctx_out) {
-    if (!aligned16(ctx_q) || !aligned16(ctx_out)) return VDN_ERR_INVALID_ARG;
-    const void* inputs[] = {q, k, v, beta, ctx_q, text_kv, alpha, gate_w, proj_w};
-    for (const void* ptr : inputs) if (ctx_out == ptr) return VDN_ERR_INVALID_ARG;
-    if (ctx_out == out) return VDN_ERR_INVALID_ARG;
-  }
+  const vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out, alpha, ctx_q, ctx_out};
+  const vdn_status chk = vdn::check_forward_args(plan->s, in);
+  if (chk != VDN_OK) return chk;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
   if (dev != plan->device) return VDN_ERR_INVALID_ARG;
-
-  const vdn::Shape& s = plan->s;
-  hipStream_t main = reinterpret_cast<hipStream_t>(stream);
-  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, out, alpha, ctx_q, ctx_out};
-  vdn::Buffers b = buffers_of(plan);
 
   hipEvent_t* ev = nullptr;
   if (plan->prof_count < plan->prof_max) {
     ev = &plan->prof_events[(size_t)plan->prof_count * VDN_NUM_STAGES * 2];
     ++plan->prof_count;
   }
-  auto mark = [&](int stage, int end, hipStream_t st) {
-    if (ev) (void)hipEventRecord(ev[stage * 2 + end], st);
-  };
-#define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
-
   plan->fwd_valid = false;                       // until every stage is enqueued
-  mark(VDN_STAGE_TOTAL, 0, main);
-  // linear branch: on the caller's stream, or for overlapped plans on the side stream, forked from
-  // the caller's stream
-  hipStream_t lin = plan->overlap ? plan->side : main;
-  if (plan->overlap) {
-    VDN_TRY(hipEventRecord(plan->ev_fork, main));
-    VDN_TRY(hipStreamWaitEvent(plan->side, plan->ev_fork, 0));
+  if (vdn::enqueue_forward(plan->s, plan->kinds, buffers_of(plan), in, reinterpret_cast<hipStream_t>(stream),
+                           plan->overlap ? plan->side : nullptr, plan->ev_fork, plan->ev_join, ev) != hipSuccess) {
+    (void)hipGetLastError();
+    return VDN_ERR_HIP;
   }
-  mark(VDN_STAGE_VDA_STATS, 0, lin);
-  VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, lin));
-  mark(VDN_STAGE_VDA_STATS, 1, lin);
-  mark(VDN_STAGE_VDA_SCAN, 0, lin);
-  VDN_TRY(vdn::launch_vda_scan(s, in, b, plan->kinds.scan_mfma, lin));
-  mark(VDN_STAGE_VDA_SCAN, 1, lin);
-  if (plan->overlap) VDN_TRY(hipEventRecord(plan->ev_join, plan->side));
-  // softmax branch on the caller's stream
-  mark(VDN_STAGE_PREP, 0, main);
-  if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_prep_kv(s, in, b, main));
-  if (plan->kinds.softmax_fp8) VDN_TRY(vdn::launch_prep_fp8(s, in, b, main));
-  if (plan->kinds.epilogue_mfma) VDN_TRY(vdn::launch_prep_weights(s, in, b, main));
-  mark(VDN_STAGE_PREP, 1, main);
-  mark(VDN_STAGE_SOFTMAX, 0, main);
-  if (plan->kinds.softmax_fp8) VDN_TRY(vdn::launch_softmax_fp8(s, in, b, main));
-  else if (plan->kinds.softmax_mfma) VDN_TRY(vdn::launch_softmax_mfma(s, in, b, main));
-  else VDN_TRY(vdn::launch_softmax_simt(s, in, b, main));
-  mark(VDN_STAGE_SOFTMAX, 1, main);
-  // join, then readout + gates + projections
-  if (plan->overlap) VDN_TRY(hipStreamWaitEvent(main, plan->ev_join, 0));
-  mark(VDN_STAGE_EPILOGUE, 0, main);
-  if (plan->kinds.epilogue_mfma) VDN_TRY(vdn::launch_epilogue_mfma(s, in, b, main));
-  else VDN_TRY(vdn::launch_epilogue(s, in, b, false, main));
-  mark(VDN_STAGE_EPILOGUE, 1, main);
-  mark(VDN_STAGE_TOTAL, 1, main);
-#undef VDN_TRY
   plan->fwd_valid = true;
   plan->fwd_alpha = alpha != nullptr;
   return VDN_OK;
@@ -497,11 +548,27 @@ vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const voi
   for (const void* ptr : ptrs) if (!aligned16(ptr)) return VDN_ERR_INVALID_ARG;
   const void* opt[] = {text_kv, dtext_kv, alpha, dalpha};
   for (const void* ptr : opt) if (ptr && !aligned16(ptr)) return VDN_ERR_INVALID_ARG;
-  const void* outs[] = {dq, dk, dv, dbeta, dtext_kv, dgate_w, dproj_w, dalpha};
-  const void* ins[] = {q, k, v, beta, text_kv, alpha, gate_w, proj_w, dout};
-  for (const void* o : outs)
-    for (const void* i : ins)
-      if (o && o == i) return VDN_ERR_INVALID_ARG;
+  {
+    // every output's bytes are disjoint from every input's and from the other outputs'
+    const vdn::Shape& s = plan->s;
+    const size_t elt = s.dtype == VDN_BF16 ? 2 : 4;
+    const size_t tokn = (size_t)s.T * s.N * s.H * s.d;
+    const size_t brow = ((size_t)s.n_text + (size_t)s.T * s.N) * s.H;
+    const size_t tkv = (size_t)2 * s.n_text * s.H * s.d, dd2 = (size_t)2 * s.d * s.d;
+    const size_t al = (size_t)s.T * s.H * s.d;
+    const vdn::Span outs[] = {{dq, tokn * 4}, {dk, tokn * 4}, {dv, tokn * 4}, {dbeta, brow * 4},
+                              {s.n_text > 0 ? dtext_kv : nullptr, tkv * 4}, {dgate_w, dd2 * 4},
+                              {dproj_w, dd2 * 4}, {dalpha, al * 4}};
+    const vdn::Span ins[] = {{q, tokn * elt}, {k, tokn * elt}, {v, tokn * elt}, {beta, brow * 4},
+                             {s.n_text > 0 ? text_kv : nullptr, tkv * elt}, {alpha, al * 4},
+                             {gate_w, dd2 * elt}, {proj_w, dd2 * elt}, {dout, tokn * elt}};
+    for (const vdn::Span& o : outs) {
+      for (const vdn::Span& i : ins)
+        if (vdn::spans_overlap(o, i)) return VDN_ERR_INVALID_ARG;
+      for (const vdn::Span& o2 : outs)
+        if (&o2 != &o && vdn::spans_overlap(o, o2)) return VDN_ERR_INVALID_ARG;
+    }
+  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
   if (dev != plan->device) return VDN_ERR_INVALID_ARG;

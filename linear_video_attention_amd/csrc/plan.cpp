@@ -1,40 +1,14 @@
-// Host-side plan logic of the VDN layer: key ranges of the softmax branch, scan order of the
-// linear branch, workspace layout and kernel selection.  No GPU calls.
+// Host-side plan logic of the VDN layer: scan order of the linear branch, workspace layout and
+// kernel selection (the key ranges of the softmax branch are in vdn_internal.h).  No GPU calls.
 //
 // Frame rules from "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section
-// "Local Softmax and Long-Range Linear Memory": chunks of C consecutive frames; a chunk attends to
-// itself and its two neighbours; the first and last frames are anchors seen by every frame and
-// seeing every frame; the forward state covers the frames before the window and the reverse state
-// those after it, neither covering window or boundary frames.
+// "Local Softmax and Long-Range Linear Memory": the forward state covers the non-boundary frames
+// before the window and the reverse state those after it.
 #include "vdn_internal.h"
 
 #include <algorithm>
 
 namespace vdn {
-
-bool is_boundary(const Shape& s, int t) { return s.anchors && (t == 0 || t == s.T - 1); }
-
-int key_ranges(const Shape& s, int t, int64_t* r, int max_ranges) {
-  int64_t tmp[2 * kMaxRanges];
-  int n = 0;
-  auto add = [&](int64_t a, int64_t b) {
-    if (b > a) { tmp[2 * n] = a; tmp[2 * n + 1] = b; ++n; }
-  };
-  const int64_t base = s.ctx_pad, N = s.N;
-  add(0, s.n_ctx);
-  if (t == s.T || is_boundary(s, t)) {                                  // context rows, boundary frames
-    add(base, base + (int64_t)s.T * N);
-  } else {
-    const int c = t / s.C;
-    const int lo = std::max(0, (c - 1) * s.C);
-    const int hi = std::min(s.T, (c + 2) * s.C);
-    if (s.anchors && lo > 0) add(base, base + N);                        // frame 0
-    add(base + lo * N, base + hi * N);                                   // window
-    if (s.anchors && s.T - 1 >= hi) add(base + (int64_t)(s.T - 1) * N, base + (int64_t)s.T * N);  // frame T-1
-  }
-  for (int i = 0; i < n && i < max_ranges; ++i) { r[2 * i] = tmp[2 * i]; r[2 * i + 1] = tmp[2 * i + 1]; }
-  return n;
-}
 
 int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames) {
   int n = 0;

@@ -28,12 +28,41 @@ struct Shape {
   int64_t Ls8;       // key stride of the FP8 packed K/V: Lk + one zero 128-key tile
 };
 
+// Frame rules of "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models", section "Local
+// Softmax and Long-Range Linear Memory": chunks of C consecutive frames; a chunk attends to itself
+// and its two neighbours; the first and last frames are anchors seen by every frame and seeing every
+// frame; the forward state covers the frames before the window and the reverse state those after
+// it, neither covering window or boundary frames.  Host and device (the allocation-free forward
+// builds its key-range table on the device).
+__host__ __device__ inline bool is_boundary(const Shape& s, int t) { return s.anchors && (t == 0 || t == s.T - 1); }
+
 // Key ranges of query frame t in a head's key space (see vdn_key_ranges); t == T gives the ranges
-// of the context (text and audio) query rows: every key.  Returns the count.
-int key_ranges(const Shape& s, int t, int64_t* ranges, int max_ranges);
+// of the context (text and audio) query rows: every key.  Writes min(count, max_ranges) ranges and
+// returns the count.
+__host__ __device__ inline int key_ranges(const Shape& s, int t, int64_t* r, int max_ranges) {
+  int64_t tmp[2 * kMaxRanges];
+  int n = 0;
+  auto add = [&](int64_t a, int64_t b) {
+    if (b > a) { tmp[2 * n] = a; tmp[2 * n + 1] = b; ++n; }
+  };
+  const int64_t base = s.ctx_pad, N = s.N;
+  add(0, s.n_ctx);
+  if (t == s.T || is_boundary(s, t)) {                                  // context rows, boundary frames
+    add(base, base + (int64_t)s.T * N);
+  } else {
+    const int c = t / s.C;
+    const int lo = c >= 1 ? (c - 1) * s.C : 0;
+    const int hi = (c + 2) * s.C < s.T ? (c + 2) * s.C : s.T;
+    if (s.anchors && lo > 0) add(base, base + N);                        // frame 0
+    add(base + lo * N, base + hi * N);                                   // window
+    if (s.anchors && s.T - 1 >= hi) add(base + (int64_t)(s.T - 1) * N, base + (int64_t)s.T * N);  // frame T-1
+  }
+  for (int i = 0; i < n && i < max_ranges; ++i) { r[2 * i] = tmp[2 * i]; r[2 * i + 1] = tmp[2 * i + 1]; }
+  return n;
+}
+
 // Frames written into the forward (dir 0) / reverse (dir 1) state of query frame t, in order.
 int scan_frames(const Shape& s, int t, int dir, int* frames, int max_frames);
-bool is_boundary(const Shape& s, int t);
 
 // Device workspace layout (byte offsets from the workspace base).
 struct Layout {
@@ -104,6 +133,29 @@ struct Inputs {
   const void* ctx_q;   // [n_ctx][H][d] text and audio query rows, or nullptr (not computed)
   void* ctx_out;       // [n_ctx][H][d] their attention output (with ctx_q)
 };
+
+// Host-side helpers of the C ABI (abi.cpp).
+Shape make_shape(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors, vdn_dtype dt);
+bool shape_ok(int T, int N, int C, int n_text, int H, int d, int anchors);
+// Validation of a plan's shape, dtype and flags (VDN_OK or the status vdn_plan_create_* returns).
+vdn_status check_plan_args(int T, int N, int C, int n_text, int n_audio, int H, int d, int anchors,
+                           vdn_dtype dtype, unsigned flags);
+// Validation of a forward's pointers: presence, 16-byte alignment, and outputs disjoint (by byte
+// range) from every input and from each other.
+vdn_status check_forward_args(const Shape& s, const Inputs& in);
+// Device buffers of a workspace laid out by make_layout at base ws.
+Buffers make_buffers(char* ws, const Layout& lay, const Kinds& kinds, const Shape& s);
+// Enqueue every stage of the forward on `main` (the linear branch on `side`, forked and joined
+// through the two events, when side is not null); ev, if not null, receives the stage events
+// [VDN_NUM_STAGES][2].  Returns the first launch error.
+hipError_t enqueue_forward(const Shape& s, const Kinds& kinds, const Buffers& b, const Inputs& in, hipStream_t main,
+                           hipStream_t side, hipEvent_t ev_fork, hipEvent_t ev_join, hipEvent_t* ev);
+// A byte range [p, p + n) of caller memory; two ranges overlap when they share a byte.
+struct Span {
+  const void* p;
+  size_t n;
+};
+bool spans_overlap(const Span& x, const Span& y);
 
 // Backward pass.  Row segment for X^T Y reductions: rows [row0, row0 + nrows) of head `head`
 // (head < 0: every head) of [rows][H][d] arrays.

@@ -139,6 +139,15 @@ def test_forward_argument_errors():
     bad[0] += 2                                               # misaligned q
     assert L.vdn_forward(plan.handle, *bad, ptr(out), stream) == -1
     assert L.vdn_forward(plan.handle, *args, args[0], stream) == -1   # out aliases q
+    # out overlaps any byte of any input: beta, text_kv, the weights, or a q shifted by one row
+    for i in range(len(args)):
+        assert L.vdn_forward(plan.handle, *args, args[i], stream) == -1, i
+    assert L.vdn_forward(plan.handle, *args, args[0] + w.H * w.d * 2, stream) == -1
+    gw = torch.empty(4 * w.d * w.d + 64, dtype=torch.bfloat16, device="cuda")
+    # out starting inside the (short) gate weights and running over them
+    assert L.vdn_forward(plan.handle, *args[:5], ptr(gw), args[6], ptr(gw) - 16 * 64, stream) == -1
+    out2 = torch.empty(out.numel() + 64, dtype=out.dtype, device="cuda")
+    assert L.vdn_forward(plan.handle, *args, ptr(out2) + 64, stream) == 0       # disjoint: fine
     nul = list(args)
     nul[4] = None                                             # text_kv missing with n_text > 0
     assert L.vdn_forward(plan.handle, *nul, ptr(out), stream) == -1
