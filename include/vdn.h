@@ -77,7 +77,9 @@ typedef enum {
   VDN_ERR_UNSUPPORTED = -2,   /* d not in {16, 32, 64, 128}, unknown dtype, size overflow,
                                  a shape outside a requested variant's limits                 */
   VDN_ERR_OUT_OF_MEMORY = -3, /* workspace allocation failed                                   */
-  VDN_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed                    */
+  VDN_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed                    */
+  VDN_ERR_TOO_LARGE = -5      /* vdn_forward_noalloc: the shape's workspace exceeds its static
+                                 scratch                                                       */
 } vdn_status;
 
 typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype;
@@ -186,6 +188,23 @@ vdn_status vdn_backward_after_forward(vdn_plan *plan, const void *q, const void 
                                       float *dq, float *dk, float *dv, float *dbeta,
                                       float *dtext_kv, float *dgate_w, float *dproj_w,
                                       float *dalpha, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc): the layer forward of vdn_forward for the plan vdn_plan_create(T, N, C,
+ * n_text, H, d, anchors, dtype) would build, without a plan.  The workspace is a static device
+ * array of 32 MiB that the library holds on each GPU it runs on until the process ends; the call
+ * allocates nothing (no hipMalloc, hipFree or other allocating routine).  A shape whose workspace
+ * (vdn_plan_workspace_bytes of that plan) exceeds 32 MiB is rejected with VDN_ERR_TOO_LARGE before
+ * anything is enqueued (the 20-frame x 256-token, 4 x 64 workload needs about 15 MiB; the 768p head
+ * share needs 0.63 GB and takes a plan).  Arguments, layouts, kernels and results as vdn_forward
+ * (the same bits), with the argument errors of vdn_plan_create and vdn_forward.  All calls on one
+ * GPU share its array, which keeps the previous call's contents (each call rebuilds what it reads
+ * before writing): calls that overlap on one GPU (other streams, other threads) race; serialise
+ * them. */
+vdn_status vdn_forward_noalloc(int T, int N, int C, int n_text, int H, int d, int anchors, vdn_dtype dtype,
+                               const void *q, const void *k, const void *v, const float *beta,
+                               const void *text_kv, const void *gate_w, const void *proj_w, void *out,
+                               void *stream);
 
 /* Free the plan's workspace, stream and events.  The caller must have synchronised the streams
  * the plan was used on.  NULL is a no-op. */

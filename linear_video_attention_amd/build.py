@@ -36,6 +36,7 @@ SOURCES = [
     "merge_bwd_mfma.hip",
     "xty_mfma.hip",
     "scan_bwd_mfma.hip",
+    "noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -216,6 +216,7 @@ const char* vdn_status_str(vdn_status s) {
     case VDN_ERR_UNSUPPORTED: return "unsupported configuration";
     case VDN_ERR_OUT_OF_MEMORY: return "out of device memory";
     case VDN_ERR_HIP: return "HIP runtime error";
+    case VDN_ERR_TOO_LARGE: return "workspace exceeds the static scratch of vdn_forward_noalloc";
   }
   return "unknown status";
 }

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libvdn.so")
 
 VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_OUT_OF_MEMORY, VDN_ERR_HIP = 0, -1, -2, -3, -4
+VDN_ERR_TOO_LARGE = -5
 VDN_F32, VDN_BF16 = 0, 1
 VDN_FLAG_GENERIC_KERNELS = 1
 VDN_FLAG_SERIAL = 2
@@ -32,6 +33,7 @@ SIGNATURES = [
     ("vdn_forward", _c_int, [_vp] * 10),
     ("vdn_forward_decay", _c_int, [_vp] * 11),
     ("vdn_forward_joint", _c_int, [_vp] * 13),
+    ("vdn_forward_noalloc", _c_int, [_c_int] * 8 + [_vp] * 9),
     ("vdn_backward", _c_int, [_vp] * 19),
     ("vdn_backward_after_forward", _c_int, [_vp] * 19),
     ("vdn_plan_destroy", None, [_vp]),
@@ -167,6 +169,24 @@ def vdn_forward_joint(plan, q, k, v, beta, ctx_q, ctx_kv, alpha, gate_w, proj_w,
     _check(lib().vdn_forward_joint(plan, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(ctx_q), ptr(ctx_kv),
                                    ptr(alpha), ptr(gate_w), ptr(proj_w), ptr(out), ptr(ctx_out),
                                    _stream_ptr(stream)), "vdn_forward_joint")
+
+
+def vdn_forward_noalloc(T, N, C, n_text, H, d, anchors, dtype, q, k, v, beta, text_kv, gate_w, proj_w, out,
+                        stream=None):
+    """The layer forward without a plan, on the library's static device scratch (allocates nothing;
+    shapes whose workspace exceeds the scratch raise VDN_ERR_TOO_LARGE).  ``dtype`` is "bf16" or
+    "fp32"; tensors as ``vdn_forward``; ``out`` is written."""
+    dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
+    ptr = lambda x: None if x is None else x.data_ptr()
+    _check(lib().vdn_forward_noalloc(T, N, C, n_text, H, d, int(anchors), dt, ptr(q), ptr(k), ptr(v), ptr(beta),
+                                     ptr(text_kv), ptr(gate_w), ptr(proj_w), ptr(out),
+                                     None if stream is None and not _has_gpu() else _stream_ptr(stream)),
+           "vdn_forward_noalloc")
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.is_available()
 
 
 class Plan:

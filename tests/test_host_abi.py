@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(vdn):
 
 
 def test_status_strings(vdn):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert vdn.status_str(s)
 
 
@@ -146,3 +146,50 @@ def test_key_ranges_at_768p_workload(vdn):
     ranges = vdn.vdn_key_ranges(75, 1536, 5, 512, True, 74)
     assert sum(b - a for a, b in ranges) == 512 + 75 * 1536
 
+
+
+# ---- the allocation-free forward: every check runs on the host before any GPU call ----
+
+def _fake_spans(T, N, n_text, H, d, elt):
+    """Disjoint, 256-byte aligned fake device addresses for q, k, v, beta, text_kv, gate_w,
+    proj_w, out (never dereferenced: the calls below return before anything is enqueued, or fail
+    at the first HIP call on a machine without a GPU)."""
+    tok = T * N * H * d * elt
+    sizes = [tok, tok, tok, (n_text + T * N) * H * 4, 2 * n_text * H * d * elt, 2 * d * d * elt, 2 * d * d * elt,
+             tok]
+    addr, out = 1 << 40, []
+    for sz in sizes:
+        out.append(addr)
+        addr += (sz + 4095) // 4096 * 4096
+    return out
+
+
+def test_noalloc_rejects_before_touching_the_gpu(vdn):
+    L = vdn.lib()
+    # the 768p head share needs 0.63 GB of workspace: beyond the static scratch
+    p = _fake_spans(75, 1536, 512, 5, 128, 2)
+    assert L.vdn_forward_noalloc(75, 1536, 5, 512, 5, 128, 1, vdn.VDN_BF16, *p, None) == vdn.VDN_ERR_TOO_LARGE
+    assert vdn.status_str(vdn.VDN_ERR_TOO_LARGE)
+    p = _fake_spans(4, 64, 4, 1, 64, 2)
+    assert L.vdn_forward_noalloc(4, 64, 2, 4, 1, 48, 1, vdn.VDN_BF16, *p, None) == vdn.VDN_ERR_UNSUPPORTED
+    assert L.vdn_forward_noalloc(0, 64, 2, 4, 1, 64, 1, vdn.VDN_BF16, *p, None) == vdn.VDN_ERR_INVALID_ARG
+    # out overlapping any input (here each input's first or last byte) is an argument error
+    elt, tok = 2, 4 * 64 * 1 * 64 * 2
+    for i in range(7):
+        bad = list(p)
+        bad[7] = p[i]
+        assert L.vdn_forward_noalloc(4, 64, 2, 4, 1, 64, 1, vdn.VDN_BF16, *bad, None) == vdn.VDN_ERR_INVALID_ARG, i
+    bad = list(p)
+    bad[7] = p[5] - tok + 16                      # out's last 16 bytes are gate_w's first
+    assert L.vdn_forward_noalloc(4, 64, 2, 4, 1, 64, 1, vdn.VDN_BF16, *bad, None) == vdn.VDN_ERR_INVALID_ARG
+    bad = list(p)
+    bad[0] += 8                                   # misaligned q
+    assert L.vdn_forward_noalloc(4, 64, 2, 4, 1, 64, 1, vdn.VDN_BF16, *bad, None) == vdn.VDN_ERR_INVALID_ARG
+    # valid arguments pass every host check; without a GPU the first HIP call fails
+    try:
+        import torch
+        gpu = torch.cuda.is_available()
+    except Exception:
+        gpu = False
+    if not gpu:
+        assert L.vdn_forward_noalloc(4, 64, 2, 4, 1, 64, 1, vdn.VDN_BF16, *p, None) == vdn.VDN_ERR_HIP
