@@ -187,3 +187,130 @@ def vdn_forward_fp8(inp: dict, T, N, C, anchors=True, rows=None, with_intermedia
     if with_intermediates:
         return out, {"o_s": o_s, "o_l": o_l}
     return out
+
+
+# ----------------------------------------------------------------------------------------------
+# How far the FP8 definition may lie from the exact softmax ([VDN] "Local Softmax and Long-Range
+# Linear Memory"; ``vdn_oracle.softmax_rows``), from nothing but its rounding steps.  Used to hold
+# the FP8 kernel to the pages' exact branch as well as to the definition above.
+# ----------------------------------------------------------------------------------------------
+
+E4M3_REL = 2.0 ** -4          # a rounding to E4M3 moves a normal value by at most 2^-4 of itself
+E4M3_ABS = 2.0 ** -10         # ... and a value below 2^-6 by at most half the spacing 2^-9
+
+
+def e4m3_half_step(y) -> np.ndarray:
+    """The largest move of a rounding to E4M3 near |y|: half the spacing, 2^(e-4) in the binade
+    [2^e, 2^(e+1)) for |y| >= 2^-6, 2^-10 below."""
+    a = np.abs(np.asarray(y, np.float64))
+    _, ex = np.frexp(a)
+    hs = np.ldexp(1.0, (ex - 1 - 4).astype(np.int64))
+    return np.where(a < 2.0 ** -6, E4M3_ABS, hs)
+
+
+def exact_deviation_bounds(qr, keys, vals, s_k, s_v, kmax, tail=1e-12, block=128):
+    """Per query row and channel: the exact softmax o (float64) and three envelopes of
+    |o_fp8 - o|, where o_fp8 is any result computed with the roundings of this module's
+    definition -- query, keys, values and weights rounded to E4M3 with the scales above, scores
+    summed from the rounded operands, one normaliser over the rounded weights -- whatever the
+    order of the sums.  Returns ``(o, det, prob, rms)``, each ``[m, d]``.
+
+    Derivation (per row; x_j = c <q, k_j> in log2 units, c = log2(e)/sqrt(d), p_j = 2^(8 + x_j - m)):
+
+    * scores: Q8_i = s_q c q_i + e_i, K8_ji = s_k k_ji + f_ji with |e_i| <= E_i = h(s_q c q_i),
+      |f_ji| <= F_ji = h(s_k k_ji) (h = ``e4m3_half_step``), so |x~_j - x_j| <= eta_j =
+      sum_i E_i |k_ji| / s_q + |c q_i| F_ji / s_k + E_i F_ji / (s_q s_k), plus 2^-17 sum_i
+      |Q8_i K8_ji| / (s_q s_k) for the float32 sums and 2^-18 (|m| + 8) for the exponent's
+      float32 arithmetic;
+    * weights: P8_j = e4m3(2^(8 + x~_j - m)) lies in [p_j r_j - 2^-10, p_j u_j + 2^-10] with
+      u_j = 2^eta_j (1 + 2^-4), r_j = 2^-eta_j - 2^-4 2^eta_j, so |P8_j - p_j| <= p_j a_j + 2^-10
+      with a_j = u_j - 1;
+    * values: |V8_jc / s_v - v_jc| <= g_jc = h(s_v v_jc) / s_v;
+    * since sum_j p_j (v_j - o) = 0,
+      o_fp8 - o = [sum_j (P8_j - p_j)(v_j - o) + sum_j P8_j (V8_j / s_v - v_j)] / sum_j P8_j,
+      with sum_j P8_j >= Z = sum_j (p_j r_j - 2^-10).
+
+    ``det`` = [sum_j (p_j a_j + 2^-10)(|v_jc| + |o_c|) + sum_j (p_j u_j + 2^-10) g_jc] / Z holds
+    for every input (worst case: every move aligned).  The offset m only scales p; the bound is
+    largest for the largest offset the row can take (m = c |q| kmax when that is <= 4, else
+    max x + max eta), which is the one used.
+
+    ``rms`` is the predicted root-mean-square deviation when each rounding error is uniform over
+    its half step and independent of the others (keys and values drawn independently), to first
+    order in the score error: the score error has variance sum_i [(c q_i)^2 F_ji^2 / s_k^2 +
+    k_ji^2 E_i^2 / s_q^2] / 3 (log2 units), each weight the relative variance
+    (ln 2)^2 var(x~_j) + (h(p_j) / p_j)^2 / 3, each value the variance g_jc^2 / 3, combined as
+    [sum_j p_j^2 var_w (v_jc - o_c)^2 + sum_j p_j^2 g_jc^2 / 3] / (sum_j p_j)^2.
+
+    ``prob`` = sqrt(6 ln(2 / tail)) rms: under the same model the deviation is a sum of independent
+    zero-mean terms, each confined to +-sqrt(3) times its standard deviation, so Hoeffding's
+    inequality bounds it by ``prob`` except with probability ``tail``.
+    """
+    qr = np.asarray(qr, np.float64)
+    keys = np.asarray(keys, np.float64)
+    vals = np.asarray(vals, np.float64)
+    m_rows, d = qr.shape
+    c = math.log2(math.e) / math.sqrt(d)
+    ln2 = math.log(2.0)
+    ak = np.abs(keys)
+    F = e4m3_half_step(s_k * keys)                     # [n, d], scaled units
+    g = e4m3_half_step(s_v * vals) / s_v               # [n, d], value units
+    V, V2 = vals, vals * vals
+    lam = math.sqrt(6.0 * math.log(2.0 / tail))
+    o_all, det_all, prob_all, rms_all = (np.zeros((m_rows, d)) for _ in range(4))
+    for r0 in range(0, m_rows, block):
+        q = qr[r0:r0 + block]
+        cq = c * q
+        s_q = np.array([pow2_scale(np.abs(row).max()) for row in cq])[:, None]
+        E = e4m3_half_step(s_q * cq)                   # [b, d]
+        acq = np.abs(cq)
+        eta = (E @ ak.T) / s_q + (acq @ F.T) / s_k + (E @ F.T) / (s_q * s_k)
+        eta += 2.0 ** -17 * (((s_q * acq + E) @ (s_k * ak + F).T) / (s_q * s_k))
+        x = cq @ keys.T                                # exact scores, log2 units
+        b = c * np.sqrt((q * q).sum(axis=1)) * kmax
+        m = np.where(b <= OFFSET_BOUND_LIMIT, b, x.max(axis=1) + eta.max(axis=1))[:, None]
+        eta += 2.0 ** -18 * (np.abs(m) + P_SHIFT)
+        p = np.exp2(P_SHIFT + x - m)
+        u = np.exp2(eta) * (1.0 + E4M3_REL)
+        r = np.exp2(-eta) - E4M3_REL * np.exp2(eta)
+        W1 = p * (u - 1.0) + E4M3_ABS
+        W2 = p * u + E4M3_ABS
+        Z = (p * r - E4M3_ABS).sum(axis=1, keepdims=True)
+        assert np.all(Z > 0), "rounding envelope of the normaliser reaches zero"
+        o = (p @ V) / p.sum(axis=1, keepdims=True)
+        det = (W1 @ np.abs(V) + np.abs(o) * W1.sum(axis=1, keepdims=True) + W2 @ g) / Z
+        var_x = ((acq * acq) @ (F * F).T / s_k ** 2 + (E * E) @ (keys * keys).T / s_q ** 2) / 3.0
+        var_w = ln2 * ln2 * var_x + (e4m3_half_step(p) / p) ** 2 / 3.0
+        P2w = p * p * var_w
+        dev2w = P2w @ V2 - 2.0 * o * (P2w @ V) + o * o * P2w.sum(axis=1, keepdims=True)
+        var = (np.maximum(dev2w, 0.0) + (p * p) @ (g * g) / 3.0) / p.sum(axis=1, keepdims=True) ** 2
+        sl = slice(r0, r0 + len(q))
+        o_all[sl], det_all[sl], prob_all[sl], rms_all[sl] = o, det, lam * np.sqrt(var), np.sqrt(var)
+    return o_all, det_all, prob_all, rms_all
+
+
+def softmax_branch_bounds(q, k, v, text_k, text_v, T, N, C, anchors, rows=None, audio_k=None, audio_v=None,
+                          tail=1e-12):
+    """``exact_deviation_bounds`` for the video rows of the softmax branch (every row, or the given
+    token indices), with each head's scales; returns ``(o, det, prob, rms)`` shaped
+    ``[len(rows), H, d]``."""
+    if audio_k is not None:
+        text_k = np.concatenate([text_k, audio_k], axis=0)
+        text_v = np.concatenate([text_v, audio_v], axis=0)
+    TN, H, d = q.shape
+    rows = np.arange(TN) if rows is None else np.asarray(rows)
+    res = [np.zeros((len(rows), H, d)) for _ in range(4)]
+    frames_of_rows = rows // N
+    for h in range(H):
+        keys_all = np.concatenate([text_k[:, h], k[:, h]]).astype(np.float64)
+        vals_all = np.concatenate([text_v[:, h], v[:, h]]).astype(np.float64)
+        s_k, s_v, kmax = head_scales(keys_all, vals_all)
+        n_g = text_k.shape[0]
+        for t in np.unique(frames_of_rows):
+            sel = np.nonzero(frames_of_rows == t)[0]
+            kf = orc.key_frames(int(t), T, C, anchors)
+            idx = np.concatenate([np.arange(n_g)] + [n_g + np.arange(f * N, (f + 1) * N) for f in kf])
+            out = exact_deviation_bounds(q[rows[sel], h], keys_all[idx], vals_all[idx], s_k, s_v, kmax, tail)
+            for a, b in zip(res, out):
+                a[sel, h] = b
+    return tuple(res)

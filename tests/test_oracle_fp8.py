@@ -7,7 +7,10 @@
   with a weight in the subnormal range), whose rounded weights are worked out in the comments;
 * uniform attention: identical keys give every visible key the same weight, so a frame-indicator
   value reveals each query's key set (text, window, anchors), exactly;
-* closeness to the exact softmax within the error the rounding allows;
+* closeness to the exact softmax within the error the rounding allows, and the envelopes of that
+  error derived from the rounding steps alone (worst case, probabilistic, predicted RMS);
+* the per-row allowance for scores that land near an E4M3 midpoint, by a hand-worked row and by
+  brute-force perturbation of the scores;
 * planted mistakes, each caught by one of the pins above.
 """
 
@@ -136,8 +139,108 @@ def pin_close_to_exact(f8, seed=3):
         assert np.abs(err).max() <= 0.30 * rms
 
 
+def _bound_inputs(seed=7):
+    """Rows over many keys with N(0,1) values: diffuse (unit queries), sharp (queries x64, so the
+    bound exceeds 4 and the row maximum is the offset), very sharp over few keys, d = 64, and
+    values small enough that some round in E4M3's subnormal range."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for d, n, qscale, vscale in ((128, 3000, 1.0, 1.0), (128, 3000, 64.0, 1.0), (128, 200, 200.0, 1.0),
+                                 (64, 800, 8.0, 1.0), (128, 1000, 1.0, 1e-3)):
+        q = pins._unit(rng.standard_normal((48, d))) * qscale
+        k = pins._unit(rng.standard_normal((n, d)))
+        v = rng.standard_normal((n, d)) * vscale
+        cases.append((q, k, v))
+    return cases
+
+
+def pin_exact_envelopes(f8):
+    """The definition against the exact softmax (``exact_deviation_bounds``): its o is the exact
+    softmax of ``vdn_oracle`` (float64); the definition's result lies inside the worst-case
+    envelope and inside the probabilistic one at every element; and the RMS deviation predicted
+    from the rounding steps matches the measured one within 0.8-1.25x on every input kind (so a
+    change in the precision of any rounding step shows up)."""
+    from oracle import vdn_oracle
+    for q, k, v in _bound_inputs():
+        sc = f8.head_scales(k, v)
+        o, det, prob, rms = f8.exact_deviation_bounds(q, k, v, *sc)
+        assert np.allclose(o, vdn_oracle.softmax_rows(q, k, v, np.float64), rtol=0, atol=1e-12)
+        err = np.abs(f8.softmax_rows_fp8(q, k, v, *sc) - o)
+        assert np.all(err <= det), float(np.max(err / det))
+        assert np.all(err <= prob), float(np.max(err / prob))
+        ratio = math.sqrt(float((err ** 2).mean()) / float((rms ** 2).mean()))
+        assert 0.8 <= ratio <= 1.25, ratio
+
+
+def pin_envelopes_have_teeth(f8):
+    """On diffuse rows the probabilistic envelope stays below RMS(o) (the check is not vacuous);
+    the worst-case one is the width of the value spread only when every rounding aligns."""
+    q, k, v = _bound_inputs()[0]
+    o, det, prob, rms = f8.exact_deviation_bounds(q, k, v, *f8.head_scales(k, v))
+    r = float(np.sqrt((o ** 2).mean()))
+    assert float(np.median(prob)) <= 0.6 * r
+    assert float(np.median(rms)) <= 0.06 * r
+
+
+def pin_allowance_hand(f8):
+    """``ambiguous_rounding_effect`` on the two-key row-maximum case (q = 20 e1; weights 256 and
+    2^-2.5 -> 11/64, see ``pin_hand_rowmax_offset``).  The small weight's exponent lies
+    0.02356 log2 units from the E4M3 midpoint 11.5/64 above it; the large one 0.0875 from 272.
+    Score-sum sizes sum|Q8 K8| / (s_q s_k): 3.5 (key 1), 7 (key 2), and the row maximum's 7 is
+    added since the offset is the row maximum, so delta_1 = 10.5 r, delta_2 = 14 r (+ 2^-20
+    (|exponent| + 8)).  r = 2^-12: nothing flagged, effect 0.  r = 2^-9 and 2^-7: key 2 only,
+    effect 2 (1/64) max|v2 - o| / sum P8 = 2 (1/64) (256 / 256.171875) / 256.171875 = 1.21907e-4.
+    r = 2^-6: both keys, + 2 * 32 * (11/64 / 256.171875) / 256.171875 = 1.67622e-4."""
+    q, keys, vals = _two_key_case()
+    q = q * 20.0
+    sc = f8.head_scales(keys, vals)
+    tot = 256 + 11 / 64
+    e2 = 2 * (1 / 64) * (256 / tot) / tot
+    e1 = 2 * 32 * ((11 / 64) / tot) / tot
+    for r, want in ((2.0 ** -12, 0.0), (2.0 ** -9, e2), (2.0 ** -7, e2), (2.0 ** -6, e1 + e2)):
+        got = f8.ambiguous_rounding_effect(q, keys, vals, *sc, rel_score_err=r)[0]
+        assert math.isclose(got, want, rel_tol=1e-12, abs_tol=1e-18), (r, got, want)
+
+
+def pin_allowance_brute_force(f8, seed=11, trials=40):
+    """The allowance covers what it claims to: every score of a row is perturbed by an independent
+    error of up to rel sum_i |Q8_i K8_ji| / (s_q s_k) (the row maximum with it, when it is the
+    offset), the definition's remaining steps are redone from the perturbed scores, and the
+    result moves by no more than ``ambiguous_rounding_effect`` with that rel.  Sharp rows over
+    few keys, rel = 2^-9, so that weights do cross midpoints (counted, must be > 0)."""
+    rng = np.random.default_rng(seed)
+    d, n = 32, 60
+    rel = 2.0 ** -9
+    q = pins._unit(rng.standard_normal((24, d))) * rng.uniform(4.0, 40.0, (24, 1))
+    k = pins._unit(rng.standard_normal((n, d)))
+    v = rng.standard_normal((n, d))
+    s_k, s_v, kmax = f8.head_scales(k, v)
+    c = math.log2(math.e) / math.sqrt(d)
+    k8, v8 = f8.e4m3(s_k * k), f8.e4m3(s_v * v)
+    allow = f8.ambiguous_rounding_effect(q, k, v, s_k, s_v, kmax, rel_score_err=rel)
+    flips = 0
+    for i, qi in enumerate(q):
+        s_q = f8.pow2_scale(np.abs(c * qi).max())
+        q8 = f8.e4m3(s_q * c * qi)
+        x = (k8 @ q8) / (s_q * s_k)
+        size = (np.abs(k8) @ np.abs(q8)) / (s_q * s_k)
+        b = c * math.sqrt(float(qi @ qi)) * kmax
+        base_m = b if b <= f8.OFFSET_BOUND_LIMIT else x.max()
+        p0 = f8.e4m3(np.exp2(f8.P_SHIFT + x - base_m))
+        o0 = (p0 @ v8) / (s_v * p0.sum())
+        for _ in range(trials):
+            xp = x + rel * size * rng.uniform(-1.0, 1.0, n)
+            m = b if b <= f8.OFFSET_BOUND_LIMIT else xp.max()
+            p = f8.e4m3(np.exp2(f8.P_SHIFT + xp - m))
+            o = (p @ v8) / (s_v * p.sum())
+            flips += int(np.any(p != p0 * np.exp2(base_m - m)))
+            assert np.abs(o - o0).max() <= allow[i] + 1e-12, (i, np.abs(o - o0).max(), allow[i])
+    assert flips > 0
+
+
 PINS = [pin_e4m3_library, pin_hand_bound_offset, pin_hand_rowmax_offset, pin_uniform_visibility_fp8,
-        pin_close_to_exact]
+        pin_close_to_exact, pin_exact_envelopes, pin_envelopes_have_teeth, pin_allowance_hand,
+        pin_allowance_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -243,7 +346,47 @@ def m_window_without_anchors(f8):
     assert orig is orc.key_frames
 
 
+def m_two_mantissa_bits(f8):
+    """The definition rounds to two mantissa bits (E5M2-like spacing) instead of three."""
+    def e4m3(x):
+        x = np.asarray(x, np.float64)
+        a = np.abs(x)
+        _, ex = np.frexp(a)
+        step = np.ldexp(1.0, (np.maximum(ex - 1, -6) - 2).astype(np.int64))
+        return np.copysign(np.minimum(np.round(a / step) * step, 448.0), x)
+    f8.e4m3 = e4m3
+
+
+def m_envelope_without_value_rounding(f8):
+    """The envelopes forget that the values are rounded too."""
+    orig = f8.e4m3_half_step
+
+    def e4m3_half_step(y):
+        return orig(y) * 1e-9
+    f8.e4m3_half_step = e4m3_half_step
+
+
+def m_allowance_window_quartered(f8):
+    orig = f8.ambiguous_rounding_effect
+
+    def ambiguous_rounding_effect(qr, keys, vals, s_k, s_v, kmax, rel_score_err=2.0 ** -16):
+        return orig(qr, keys, vals, s_k, s_v, kmax, rel_score_err / 4)
+    f8.ambiguous_rounding_effect = ambiguous_rounding_effect
+
+
+def m_allowance_one_quarter_step(f8):
+    orig = f8.ambiguous_rounding_effect
+
+    def ambiguous_rounding_effect(*args, **kw):
+        return orig(*args, **kw) * 0.125
+    f8.ambiguous_rounding_effect = ambiguous_rounding_effect
+
+
 MUTANTS = [
+    (m_two_mantissa_bits, pin_exact_envelopes),
+    (m_envelope_without_value_rounding, pin_exact_envelopes),
+    (m_allowance_window_quartered, pin_allowance_hand),
+    (m_allowance_one_quarter_step, pin_allowance_brute_force),
     (m_truncating_round, pin_e4m3_library),
     (m_ties_away, pin_e4m3_library),
     (m_no_subnormals, pin_e4m3_library),
