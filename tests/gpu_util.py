@@ -73,3 +73,55 @@ def combined_states(plan: Plan) -> np.ndarray:
 
 def softmax_out(plan: Plan) -> np.ndarray:
     return plan.debug_buffer(VDN_BUF_OS).float().cpu().numpy()
+
+
+def oracle_layer_rows(inp: dict, w, rows=None, workers: int = 8, softmax_fn=None):
+    """The oracle's layer output (and o_s) for the given video rows (every row when None).
+
+    The same functions as ``vdn_oracle.vdn_forward``: the softmax branch frame by frame, here
+    spread over a thread pool (numpy releases the GIL in its matrix products and exponentials, and
+    each worker's BLAS is held to two threads), then the linear branch and the merge.
+    ``softmax_fn(rows)`` replaces the exact softmax branch (the FP8 definition)."""
+    import concurrent.futures
+
+    import threadpoolctl
+
+    from oracle import vdn_oracle as orc
+    rows = np.arange(w.T * w.N) if rows is None else np.asarray(rows)
+    frames = rows // w.N
+    groups = [np.nonzero(frames == t)[0] for t in np.unique(frames)]
+    if softmax_fn is None:
+        def softmax_fn(r):
+            return orc.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], w.T, w.N, w.C,
+                                      w.anchors, r, inp.get("audio_k"), inp.get("audio_v"))
+    o_s = np.zeros((len(rows), w.H, w.d))
+    with threadpoolctl.threadpool_limits(2):
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            for sel, res in zip(groups, ex.map(lambda g: softmax_fn(rows[g]), groups)):
+                o_s[sel] = res
+        o_l = orc.linear_branch(inp["q"], inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"], w.T, w.N,
+                                w.C, w.anchors, rows, alpha=inp.get("alpha"))
+    out = orc.merge(inp["q"][rows], o_s, o_l, inp["gate_w"], inp["proj_w"])
+    return out, o_s
+
+
+def describe_error(got, ref) -> str:
+    """Max |got - ref| / RMS(ref), where it occurs (|ref| / RMS there), and the largest error left
+    after subtracting half a bf16 unit of |ref| (the rounding of a stored bf16 value)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    err = np.abs(got - ref)
+    i = int(np.argmax(err))
+    ax = np.abs(ref)
+    half_ulp = np.where(ax > 0, 2.0 ** (np.floor(np.log2(np.maximum(ax, 1e-30))) - 8), 0.0)
+    return (f"max err {err.flat[i] / rms:.3e} RMS at |ref| = {ax.flat[i] / rms:.2f} RMS; max |ref| "
+            f"{ax.max() / rms:.2f} RMS; beyond bf16 storage {np.max(err - half_ulp) / rms:.3e} RMS")
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place of |x| (8 significant bits): the largest move of storing
+    x in bf16 (round to nearest)."""
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 1e-30)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)

@@ -14,7 +14,10 @@ from oracle import vdn_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import TOL, combined_states, make_plan, rel_err, run_joint, run_layer, softmax_out, to_device  # noqa: E402
+from linear_video_attention_amd.vdn import Plan  # noqa: E402
+
+from gpu_util import (TOL, bf16_half_ulp, combined_states, describe_error, make_plan,  # noqa: E402
+                      oracle_layer_rows, rel_err, run_joint, run_layer, softmax_out, to_device)
 
 
 def check_full(w, generic=False, seed=0, stress=False, decay=False):
@@ -63,6 +66,7 @@ RAGGED = [
     (4, 3, 800, 2, 1, 128, "bf16", True),        # two epilogue workgroups per frame, short last one
     (9, 11, 37, 3, 2, 64, "fp32", True),         # fp32, ragged everything
     (1, 6, 5, 2, 1, 128, "fp32", False),         # fp32, d = 128, anchors off
+    (5, 9, 100, 3, 2, 128, "bf16", True),        # N % 8 != 0: generic softmax, MFMA linear branch and epilogue
 ]
 
 
@@ -73,6 +77,14 @@ def test_ragged_shapes_match_oracle(case):
     check_full(w, seed=3)
 
 
+def test_stress_keys_crowded_gram_full_frames():
+    """Crowded keys at the 768p frame size (1536 tokens, d = 128): sum beta per frame is about 768,
+    so the top eigenvalue of I + A is in the hundreds; the fp32 inverse (no pivoting) and the bf16
+    hi/lo planes of M are held to the bar on the states and the output."""
+    w = synth.custom(16, 8, 1536, 2, 2, 128, "bf16", "sigmoid", True)
+    check_full(w, seed=9, stress=True)
+
+
 def test_stress_keys_crowded_gram():
     """Keys of each frame crowd one direction (lambda_max(A) near sum beta): exercises the fp32
     inverse of I + A at a condition number in the hundreds."""
@@ -80,23 +92,67 @@ def test_stress_keys_crowded_gram():
     check_full(w, seed=5, stress=True)
 
 
-@pytest.mark.parametrize("name", ["medium", "768p", "long"])
-def test_full_size_sampled_rows(name):
-    """Full-size workloads in the launch configuration the benchmark times: every frame's first
-    and last token plus two random tokens per frame, all heads, against the oracle."""
+@pytest.mark.parametrize("name", ["medium", "768p"])
+def test_full_size_every_row(name):
+    """Full-size workloads in the launch configuration the benchmark times: every row of every
+    head against the oracle (its softmax branch spread over the host's cores frame by frame)."""
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w, seed=0)
     plan = make_plan(w)
     dev = to_device(inp, w.dtype)
+    out = run_layer(plan, dev).float().cpu().numpy()
+    del dev
+    plan.close()
+    ref, _ = oracle_layer_rows(inp, w)
+    e = rel_err(out, ref)
+    print(f"{name}: every row ({w.T * w.N} tokens x {w.H} heads): out err {e:.3e}; {describe_error(out, ref)}",
+          flush=True)
+    assert e <= TOL[w.dtype]
+
+
+def test_long_every_row_of_selected_frames():
+    """The long workload (180 frames): every row of the two boundary frames, of frame 1 (the first
+    chunk, whose reverse state absorbs the most frames) and of frame 89 (mid-sequence), plus the
+    first, last and two random rows of every other frame, all heads."""
+    w = synth.WORKLOADS["long"]
+    inp = synth.make_inputs(w, seed=0)
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
     out = run_layer(plan, dev)
-    rows = synth.sample_rows(w)
+    full = np.concatenate([np.arange(f * w.N, (f + 1) * w.N) for f in (0, 1, 89, w.T - 1)])
+    rows = np.union1d(full, synth.sample_rows(w))
     got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
     del dev, out
-    ref = orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors, rows=rows)
-    e = rel_err(got, ref)
-    print(f"{name}: sampled {len(rows)} rows, out err {e:.2e}", flush=True)
-    assert e <= TOL[w.dtype]
     plan.close()
+    ref, _ = oracle_layer_rows(inp, w, rows)
+    e = rel_err(got, ref)
+    print(f"long: {len(rows)} rows: out err {e:.3e}; {describe_error(got, ref)}", flush=True)
+    assert e <= TOL[w.dtype]
+
+
+def test_overlapped_branches_match_serial():
+    """VDN_FLAG_OVERLAP (linear branch on the plan's side stream): two forwards in a row give the
+    serial plan's bits, and the backward reusing the overlapped forward equals the serial one's."""
+    w = synth.custom(32, 10, 256, 5, 2, 128, "bf16", "sigmoid", True)
+    inp = synth.make_inputs(w, seed=12)
+    dev = to_device(inp, w.dtype)
+    ser = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype)
+    ovl = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, overlap=True)
+    want = run_layer(ser, dev).clone()
+    a = run_layer(ovl, dev).clone()
+    b = run_layer(ovl, dev).clone()
+    assert torch.equal(a, want) and torch.equal(b, want)
+    assert rel_err(a.float().cpu().numpy(), orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors)) <= TOL["bf16"]
+    dout = torch.from_numpy(np.random.default_rng(3).standard_normal(dev["q"].shape).astype(np.float32)).cuda()
+    dout = dout.to(torch.bfloat16)
+    args = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"], dout)
+    g_ser = ser.backward(*args, after_forward=True)
+    g_ovl = ovl.backward(*args, after_forward=True)
+    torch.cuda.synchronize()
+    for key in g_ser:
+        assert torch.equal(g_ser[key], g_ovl[key]), key
+    ser.close()
+    ovl.close()
 
 
 def test_two_runs_bit_identical():
@@ -155,34 +211,34 @@ def test_forward_argument_errors():
     plan.close()
 
 
-def bf16_half_ulp(x):
-    """Half a bf16 unit in the last place of |x| (8 significant bits)."""
-    ax = np.abs(np.asarray(x, np.float64))
-    e = np.floor(np.log2(np.maximum(ax, 1e-30)))
-    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
-
-
 def test_softmax_fallback_for_large_scores():
     """Queries scaled far beyond unit norm make the fixed exponent reference unsafe; those
     workgroups must be redone by the online-maximum kernel and still match the oracle.
 
     The softmax is then nearly one-hot: o_s is close to single value rows, max|o_s| / RMS ~ 7.6,
-    so rounding the stored o_s to bf16 alone moves an element by up to 2^-8 |o_s| ~ 2.8e-2 RMS.
+    so rounding the stored o_s to bf16 alone moves an element by up to 2^-8 |o_s|: storing the
+    exact result already costs 1.88e-2 RMS of the 2e-2 bar.
     The bar is therefore applied to the error beyond that half-ulp storage rounding of each
-    element: max(|gpu - oracle| - half_ulp_bf16(oracle)) <= 2e-2 RMS."""
+    element: max(|gpu - oracle| - half_ulp_bf16(oracle)) <= 2e-2 RMS (the CPU test
+    ``test_fallback_storage_allowance`` shows that the stored exact result needs that allowance and
+    no more).  The layer output of the same call is held to the plain bar."""
     import torch as _t
     w = synth.custom(8, 6, 256, 2, 2, 128, "bf16", "sigmoid", True)
     inp = synth.make_inputs(w, seed=4)
     inp["q"] = _t.from_numpy(inp["q"] * np.float32(600.0)).to(_t.bfloat16).float().numpy()
     plan = make_plan(w)
     dev = to_device(inp, w.dtype)
-    run_layer(plan, dev)
+    plan_out = run_layer(plan, dev)
     ref = orc.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], w.T, w.N, w.C, w.anchors)
     got = softmax_out(plan).astype(np.float64)
     rms = np.sqrt(np.mean(ref.astype(np.float64) ** 2))
     excess = np.max(np.abs(got - ref) - bf16_half_ulp(ref)) / rms
-    print(f"fallback o_s: plain err {rel_err(got, ref):.2e}, beyond bf16 storage rounding {excess:.2e}", flush=True)
+    out = plan_out.float().cpu().numpy()
+    e_out = rel_err(out, orc.vdn_forward(inp, w.T, w.N, w.C, w.anchors))
+    print(f"fallback o_s: plain err {rel_err(got, ref):.2e}, beyond bf16 storage rounding {excess:.2e}; "
+          f"out err {e_out:.2e}", flush=True)
     assert excess <= TOL["bf16"]
+    assert e_out <= TOL["bf16"]
     plan.close()
 
 
