@@ -17,15 +17,17 @@
 //   S<_c = S<_{c+1} P<_{c+2} + Q<_{c+2}.
 //
 // Two kernels, both built on the same row-chain step: row r of X M + Q depends only on row r of X,
-// so a workgroup owns 16 RT rows and walks its steps; each of its D/16 waves produces 16 output
-// columns with v_mfma_f32_16x16x32_bf16, both operands as bf16 high and low parts,
-// x M ~ xh Mh + xh Ml + xl Mh (relative error ~2^-16).  The right-hand matrix arrives split (two
-// bf16 planes holding its transpose row by row, so a lane's k-run is contiguous); the running rows
-// are kept in LDS as their two bf16 planes (double buffered: one barrier per step) and the fp32
-// accumulator is what gets stored.
-//   * vda_compose_kernel: every (chunk, head, map part) in parallel: P>, Q>, Q< (fp32), and P<
-//     with a decay gate; the maps are written as the planes of their transposes (the scan's
-//     operand layout), P> also as its own planes (= P<^T) without decay.  At most C-1 steps each.
+// so a workgroup owns 16 RT rows (the compose kernel: all D of them) and walks its steps; each of
+// its D/16 waves produces 16 output columns with v_mfma_f32_16x16x32_bf16, both operands as bf16
+// high and low parts, x M ~ xh Mh + xh Ml + xl Mh (relative error ~2^-16).  The right-hand matrix
+// arrives split (two bf16 planes holding its transpose row by row, so a lane's k-run is
+// contiguous); the running rows are kept in LDS as their two bf16 planes (double buffered: one
+// barrier per step) and the fp32 accumulator is what gets stored.
+//   * vda_compose_kernel: every (chunk, head, map part) in parallel, one workgroup over all D rows
+//     (each frame's step planes are loaded once, the next frame's during the current step): P>,
+//     Q>, Q< (fp32), and P< with a decay gate; the maps are written as the planes of their
+//     transposes (the scan's operand layout), P> also as its own planes (= P<^T) without decay.
+//     At most C-1 steps each.
 //   * vda_chunk_scan_kernel: one workgroup per (head, direction, 16 rows) walks the Nc-2 chunk
 //     steps with the operands of the next two steps in flight, storing one state slot per step.
 //     Slot Nc of each direction receives S0 (read by boundary query frames).
@@ -107,10 +109,9 @@ __device__ __forceinline__ void step_product(const RowPlanes<D, RT>& s, int buf,
   }
 }
 
-constexpr int kComposeRT = 2;      // 32 rows per compose workgroup
-
-// blockIdx.x = part * RB + rb (part 0: P>, 1: Q>, 2: Q<, 3: P< (decay only)), blockIdx.y = chunk,
-// blockIdx.z = head.  mhl holds each frame's step planes (G_f^T by rows, see the inverse kernel).
+// blockIdx.x = part (0: P>, 1: Q>, 2: Q<, 3: P< (decay only)), blockIdx.y = chunk, blockIdx.z =
+// head; the workgroup computes the whole D x D map, so each frame's step planes are loaded once per
+// (chunk, head, part).  mhl holds each frame's step planes (G_f^T by rows, see the inverse kernel).
 template <int D>
 __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restrict__ minv,
                                                             const bf16_t* __restrict__ mhl,
@@ -118,11 +119,9 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
                                                             const float* __restrict__ alpha,
                                                             bf16_t* __restrict__ pp, float* __restrict__ qq, int T,
                                                             int C, int Nc, int H, int anchors) {
-  constexpr int RT = kComposeRT;
-  constexpr int RB = D / (16 * RT);
+  constexpr int RT = D / 16;                         // every row of the map: D / 16 row tiles per wave
   __shared__ __attribute__((aligned(16))) RowPlanes<D, RT> s;
-  const int part = blockIdx.x / RB, rb = blockIdx.x % RB, j = blockIdx.y, h = blockIdx.z;
-  const int row0 = rb * 16 * RT;
+  const int part = blockIdx.x, j = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int col = wave * 16 + l16;
   const int64_t DD = (int64_t)D * D;
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rt][i] = (is_p && row0 + 16 * rt + 4 * lg + i == col) ? 1.f : 0.f;
+      for (int i = 0; i < 4; ++i) acc[rt][i] = (is_p && 16 * rt + 4 * lg + i == col) ? 1.f : 0.f;
   } else {
     // first frame's map: rows of G = Diag(alpha) M (row r of M times alpha[r]) or of C
     const int f1 = frame_at(0);
@@ -155,24 +154,28 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + 16 * rt + 4 * lg + i;
+        const int r = 16 * rt + 4 * lg + i;
         acc[rt][i] = x0[(int64_t)r * D + col] * (a1 ? a1[r] : 1.f);
       }
   }
   int buf = 0;
   put_rows<D, RT>(s, buf, acc, col, lg);
-  for (int a = 1; a < m; ++a) {
-    StepOps<D, RT> op;
+  StepOps<D, RT> op;
+  auto load_step = [&](int a) {                      // operands of frame a of the chain
     const int64_t slot = (int64_t)(1 + frame_at(a)) * H + h;
     load_mat<D, RT>(op, mhl + slot * 2 * DD, col, lg);
     if (is_p) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) op.c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
-      load_add<D, RT>(op, cw + slot * DD, row0, col, lg);
+      load_add<D, RT>(op, cw + slot * DD, 0, col, lg);
     }
+  };
+  if (m > 1) load_step(1);
+  for (int a = 1; a < m; ++a) {
     __syncthreads();                                 // rows of s[buf] complete
     step_product<D, RT>(s, buf, op, acc, l16, lg);
+    if (a + 1 < m) load_step(a + 1);                 // the next frame's operands during the stores
     buf ^= 1;
     put_rows<D, RT>(s, buf, acc, col, lg);
   }
@@ -180,30 +183,41 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
   const int64_t ph = (int64_t)j * H + h;
   if (is_p) {
     // pp[chunk][head][layout][plane][D][D]: layout 1 = P>^T (operand of the forward scan),
-    // layout 0 = P<^T (reverse scan); without decay P<^T = P>, written by the P> chain directly
+    // layout 0 = P<^T (reverse scan).  The transposed planes come straight from the accumulators
+    // (a lane's four rows are consecutive elements of one transposed row); without decay
+    // P<^T = P> is layout 0, copied row by row from the planes of the last step in LDS.
     bf16_t* p = pp + ph * 4 * DD;
+    bf16_t* t = p + (part == 0 ? 2 * DD : 0);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      ushort4 hv, lv;
+      uint16_t* hp = reinterpret_cast<uint16_t*>(&hv);
+      uint16_t* lp = reinterpret_cast<uint16_t*>(&lv);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + 16 * rt + 4 * lg + i;
         const __bf16 xh = (__bf16)acc[rt][i];
-        const bf16_t hb = __builtin_bit_cast(bf16_t, xh);
-        const bf16_t lb = __builtin_bit_cast(bf16_t, (__bf16)(acc[rt][i] - (float)xh));
-        if (part == 0 && !alpha) {
-          p[(int64_t)r * D + col] = hb;
-          p[DD + (int64_t)r * D + col] = lb;
-        }
-        bf16_t* t = p + (part == 0 ? 2 * DD : 0);      // transposed planes of this map
-        t[(int64_t)col * D + r] = hb;
-        t[DD + (int64_t)col * D + r] = lb;
+        hp[i] = __builtin_bit_cast(bf16_t, xh);
+        lp[i] = __builtin_bit_cast(bf16_t, (__bf16)(acc[rt][i] - (float)xh));
       }
+      const int64_t off = (int64_t)col * D + 16 * rt + 4 * lg;
+      *reinterpret_cast<ushort4*>(t + off) = hv;
+      *reinterpret_cast<ushort4*>(t + DD + off) = lv;
+    }
+    if (part == 0 && !alpha) {
+      __syncthreads();                               // the last planes of s[buf] complete
+      for (int e = tid; e < 2 * D * D / 8; e += D * 4) {
+        const int plane = e / (D * D / 8), rem = e % (D * D / 8);
+        const int row = rem / (D / 8), c8 = rem % (D / 8);
+        const bf16_t* src = plane ? &s.lo[buf][row][c8 * 8] : &s.hi[buf][row][c8 * 8];
+        *reinterpret_cast<uint4*>(p + plane * DD + (int64_t)row * D + c8 * 8) = *reinterpret_cast<const uint4*>(src);
+      }
+    }
   } else {
     float* q = qq + ((int64_t)(part - 1) * Nc * H + ph) * DD;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[(int64_t)(row0 + 16 * rt + 4 * lg + i) * D + col] = acc[rt][i];
+      for (int i = 0; i < 4; ++i) q[(int64_t)(16 * rt + 4 * lg + i) * D + col] = acc[rt][i];
   }
 }
 
@@ -294,10 +308,9 @@ __global__ __launch_bounds__(D * 4) void vda_chunk_scan_kernel(const float* __re
 
 template <int D>
 void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
-  constexpr int RB = D / (16 * kComposeRT);
   const int parts = in.alpha ? 4 : 3;
-  vda_compose_kernel<D><<<dim3(parts * RB, s.Nc, s.H), D * 4, 0, st>>>(b.minv, b.mhl, b.cw, in.alpha, b.pp, b.qq, s.T,
-                                                                      s.C, s.Nc, s.H, s.anchors);
+  vda_compose_kernel<D><<<dim3(parts, s.Nc, s.H), D * 4, 0, st>>>(b.minv, b.mhl, b.cw, in.alpha, b.pp, b.qq, s.T,
+                                                                 s.C, s.Nc, s.H, s.anchors);
   // the row blocks of one (head, direction) stay on one XCD: per_xcd is a multiple of D / 16
   const int n_chains = 2 * s.H;
   const int per_xcd = (n_chains + 7) / 8 * (D / 16);
