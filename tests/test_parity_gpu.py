@@ -211,6 +211,18 @@ def test_forward_argument_errors():
     plan.close()
 
 
+def test_plan_out_of_memory():
+    """A shape that passes every check but whose workspace (over 1 TB) exceeds the GPU's memory:
+    vdn_plan_create reports VDN_ERR_OUT_OF_MEMORY, returns no plan, and the device keeps working."""
+    import ctypes
+
+    from linear_video_attention_amd import vdn
+    h = ctypes.c_void_p(1234)
+    st = vdn.lib().vdn_plan_create(10000, 100000, 5, 0, 4, 128, 1, vdn.VDN_BF16, ctypes.byref(h))
+    assert st == vdn.VDN_ERR_OUT_OF_MEMORY and h.value is None
+    check_full(synth.custom(4, 5, 64, 2, 1, 64, "bf16", "sigmoid", True), seed=1)
+
+
 def test_softmax_fallback_for_large_scores():
     """Queries scaled far beyond unit norm make the fixed exponent reference unsafe; those
     workgroups must be redone by the online-maximum kernel and still match the oracle.
