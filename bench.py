@@ -6,6 +6,15 @@ HBM.  Prints one JSON line.  Default workload: one GPU's head share of a 768p cl
 tokens, 75 latent frames x 1536 tokens, chunks of 5 frames, 5 heads of 128, bf16, anchors on).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 768p] [--no-cpu-baseline]
+    python bench.py --forward-only ...         # only the timed forwards (for profiler runs)
+    python bench.py --summarize-trace DIR --warmup W --steps K
+    python bench.py --summarize-counters DIR [DIR ...] [--copy-counters DIR [DIR ...]]
+
+The summaries read rocprofv3 CSV output (``--output-format csv``) of a ``--forward-only`` run: the
+kernel trace gives each kernel's mean duration and, for the softmax, the mean of the K timed
+dispatches (those after the W warm-up forwards) and the bf16 MFMA fraction it implies; the
+counters give per-dispatch averages, the MFMA busy share and the HBM bytes per launch (scaled by
+what FETCH_SIZE / WRITE_SIZE read for a plain copy of known size, from ``--copy-calibration``).
 """
 
 from __future__ import annotations
@@ -88,6 +97,87 @@ def recorded_traffic(name="softmax_mfma"):
         return None
 
 
+def _csv_rows(dirs, suffix):
+    import csv
+    import glob
+    rows = []
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+            with open(f, newline="") as fh:
+                rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def summarize_trace(d, warmup, steps, workload):
+    """Markdown summary of a rocprofv3 kernel trace of ``bench.py --forward-only``."""
+    rows = _csv_rows([d], "kernel_trace.csv")
+    if not rows:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    disp = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"])) for r in rows))
+    per = {}
+    for a, z, k in disp:
+        per.setdefault(k, []).append((z - a) / 1e3)
+    total = sum(sum(v) for v in per.values())
+    lines = ["| kernel | calls | mean us | min us | total us | % of kernel time |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {len(v)} | {np.mean(v):.1f} | {np.min(v):.1f} | {sum(v):.1f} | {100 * sum(v) / total:.2f} |")
+    w = __import__("synth").WORKLOADS[workload]
+    flops = softmax_flops(w)
+    out = ["\n".join(lines), ""]
+    for k in sorted(per):
+        if k.startswith("vdn::softmax_mfma_kernel<") and k.endswith("false>"):
+            v = per[k]
+            timed = v[warmup:warmup + steps]
+            if len(timed) != steps:
+                raise SystemExit(f"{k}: {len(v)} dispatches, expected at least {warmup + steps}")
+            m = float(np.mean(timed))
+            out.append(f"{k}: timed dispatches {warmup + 1}..{warmup + steps} of {len(v)}: mean {m:.1f} us, "
+                       f"min {min(timed):.1f} us, max {max(timed):.1f} us; {flops / 1e12:.4f} TFLOP per launch "
+                       f"-> {flops / (m * 1e-6) / 1e12:.1f} TFLOP/s = {flops / (m * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.4f} "
+                       f"of the {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s bf16 dense peak")
+    return "\n".join(out)
+
+
+def summarize_counters(dirs, copy_dirs=()):
+    """Markdown summary of rocprofv3 counter collections: per-kernel averages per dispatch, the MFMA
+    busy share (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) and HBM
+    KiB per dispatch scaled by the copy calibration."""
+    acc = {}
+    for r in _csv_rows(dirs, "counter_collection.csv"):
+        acc.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    scale = {}
+    if copy_dirs:
+        cal = {}
+        for r in _csv_rows(copy_dirs, "counter_collection.csv"):
+            if "copy" in r["Kernel_Name"].lower() and r["Counter_Name"] in ("FETCH_SIZE", "WRITE_SIZE"):
+                cal.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        # the calibration copies 1 GiB: ideal FETCH = WRITE = 2^20 KiB per dispatch
+        for c, v in cal.items():
+            scale[c] = (1 << 20) / max(v)
+    lines = []
+    for k, cs in sorted(acc.items()):
+        if not k.startswith("vdn::"):
+            continue
+        avg = {c: float(np.mean(v)) for c, v in cs.items()}
+        parts = [f"{c} {v:.4g}" for c, v in sorted(avg.items())]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+            parts.append(f"MFMA busy {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * avg['GRBM_GUI_ACTIVE'] / 8):.4f}")
+        if "SQ_ACTIVE_INST_VALU" in avg and "GRBM_GUI_ACTIVE" in avg:
+            parts.append(f"VALU busy {4 * avg['SQ_ACTIVE_INST_VALU'] / (1024 * avg['GRBM_GUI_ACTIVE'] / 8):.4f}")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in avg and c in scale:
+                parts.append(f"{c} scaled {avg[c] * scale[c] * 1024 / 1e9:.4f} GB")
+        lines.append(f"- {k}: " + "; ".join(parts))
+    if scale:
+        lines.append("- copy calibration factors: " + ", ".join(f"{c} x{v:.4f}" for c, v in sorted(scale.items())))
+    return "\n".join(lines)
+
+
 def cpu_baseline(w, inp, budget_rows=32768):
     """Time the CPU oracle on a bounded sample of the workload and scale it to video tokens/s.
 
@@ -152,7 +242,20 @@ def main():
                     help="also time a plan that runs the linear branch on a side stream (context)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only warm-up and timed forwards of the bf16 plan (for profiler runs)")
+    ap.add_argument("--fp8", action="store_true", help="with --forward-only: time the FP8 softmax plan instead")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="summarise a rocprofv3 kernel trace (CPU only)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", help="summarise rocprofv3 counters (CPU only)")
+    ap.add_argument("--copy-counters", nargs="+", default=(), metavar="DIR",
+                    help="counters of a --copy-calibration 1024 run, to scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.warmup, args.steps, args.workload))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.copy_counters))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer's head share runs on one device); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -180,7 +283,7 @@ def main():
     text_kv = torch.from_numpy(np.stack([inp["text_k"], inp["text_v"]])).to("cuda").to(tdt).contiguous()
     alpha = torch.from_numpy(inp["alpha"]).to("cuda").contiguous()
     out = torch.empty_like(dev["q"])
-    plan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype)
+    plan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, fp8=args.forward_only and args.fp8)
 
     def forward(p, gate=None):
         p.forward(dev["q"], dev["k"], dev["v"], beta, text_kv, dev["gate_w"], dev["proj_w"], out, alpha=gate)
@@ -201,10 +304,28 @@ def main():
     ref = out.clone()
     tokens = w.T * w.N
 
-    sm_ms = stages["softmax"]
+    sm_ms = stages["softmax_first"]      # the fixed-reference launch alone (the dominant kernel)
     flops = softmax_flops(w)
     achieved = flops / (sm_ms * 1e-3) / 1e12
     vda_ms = stages["vda_stats"] + stages["vda_scan"]
+    roofline = {"bound": "mfma", "kernel": "softmax_mfma_kernel", "achieved": achieved,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": recorded_traffic(), "algorithmic_tflop_per_launch": flops / 1e12,
+                "avg_launch_ms": sm_ms,
+                "timing": "mean over the timed steps of HIP events recorded by the library on the softmax "
+                          "stream around the fixed-reference launch of softmax_mfma_kernel alone",
+                "softmax_stage_ms": stages["softmax"]}
+    if args.forward_only:
+        if args.fp8:
+            roofline = {"kernel": "softmax_fp8_kernel", "avg_launch_ms": sm_ms,
+                        "achieved": achieved, "unit": "TFLOP/s", "peak": MFMA_FP8_PEAK_TFLOPS,
+                        "frac": achieved / MFMA_FP8_PEAK_TFLOPS}
+        print(json.dumps({"metric": "VDN layer fwd: video tokens/sec (forward-only profiler run)",
+                          "value": tokens / (ms_step * 1e-3), "unit": "video tokens/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+                          "stages_ms": stages, "roofline": roofline}), flush=True)
+        plan.close()
+        return
 
     # the linear-branch stages after a 1 GB write (cold Infinity Cache), three forwards
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -259,7 +380,7 @@ def main():
     fplan.profile_enable(n_f8)
     f8_steps = timed_steps(lambda: forward(fplan), n_f8)
     f8_ms, f8_calls = fplan.profile_read()
-    sm8 = f8_ms["softmax"] / f8_calls
+    sm8 = f8_ms["softmax_first"] / f8_calls
     f8_med = float(np.median(f8_steps))
     fp8_info = {"ms_per_step_median": f8_med, "tokens_per_s": tokens / (f8_med * 1e-3),
                 "stages_ms": {k: v / f8_calls for k, v in f8_ms.items()},
@@ -296,10 +417,7 @@ def main():
         "data": "synthetic (seeded; q/k L2-normalised N(0,1), v N(0,1), beta sigmoid(N(0,1)), weights N(0,1/d))",
         "config": {"workload": f"{w.name}: n_text={w.n_text} T={w.T} N={w.N} C={w.C} H={w.H} d={w.d} anchors={int(w.anchors)}",
                    "n_text": w.n_text, "T": w.T, "N": w.N, "C": w.C, "H": w.H, "d": w.d},
-        "roofline": {"bound": "mfma", "kernel": "softmax_mfma_kernel", "achieved": achieved,
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": recorded_traffic(), "algorithmic_tflop_per_launch": flops / 1e12,
-                     "avg_launch_ms": sm_ms, "onbox_peak": mfma_onbox, "frac_onbox": achieved / mfma_onbox},
+        "roofline": dict(roofline, onbox_peak=mfma_onbox, frac_onbox=achieved / mfma_onbox),
         "step_ms": {"median": float(np.median(per_step)), "min": float(np.min(per_step))},
         "stages_ms": stages,
         "stage_rooflines": stage_rooflines(w, stages),

@@ -251,7 +251,11 @@ vdn_status vdn_debug_copy(const vdn_plan *plan, int which, void *dst, size_t byt
  * synchronising the events) into ms[VDN_STAGE_*] for n_stages entries and reports the number of
  * forwards recorded.  Stages: */
 enum { VDN_STAGE_SOFTMAX = 0, VDN_STAGE_PREP = 1, VDN_STAGE_VDA_STATS = 2, VDN_STAGE_VDA_SCAN = 3,
-       VDN_STAGE_EPILOGUE = 4, VDN_STAGE_TOTAL = 5, VDN_NUM_STAGES = 6 };
+       VDN_STAGE_EPILOGUE = 4, VDN_STAGE_TOTAL = 5, VDN_STAGE_SOFTMAX_FIRST = 6, VDN_NUM_STAGES = 7 };
+/* VDN_STAGE_SOFTMAX covers both launches of the MFMA and FP8 softmax kernels: the fixed-reference
+ * launch and the online-maximum launch that redoes the workgroups it flagged.
+ * VDN_STAGE_SOFTMAX_FIRST starts with it and ends after the first launch alone (the single launch
+ * of the generic kernel). */
 vdn_status vdn_profile_enable(vdn_plan *plan, int max_calls);
 vdn_status vdn_profile_read(vdn_plan *plan, float *ms, int n_stages, int *calls);
 

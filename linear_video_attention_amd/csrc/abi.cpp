@@ -150,9 +150,16 @@ hipError_t enqueue_forward(const Shape& s, const Kinds& kinds, const Buffers& b,
   if (kinds.epilogue_mfma) VDN_TRY(launch_prep_weights(s, in, b, main));
   mark(VDN_STAGE_PREP, 1, main);
   mark(VDN_STAGE_SOFTMAX, 0, main);
-  if (kinds.softmax_fp8) VDN_TRY(launch_softmax_fp8(s, in, b, main));
-  else if (kinds.softmax_mfma) VDN_TRY(launch_softmax_mfma(s, in, b, main));
-  else VDN_TRY(launch_softmax_simt(s, in, b, main));
+  mark(VDN_STAGE_SOFTMAX_FIRST, 0, main);
+  hipEvent_t first_end = ev ? ev[VDN_STAGE_SOFTMAX_FIRST * 2 + 1] : nullptr;
+  if (kinds.softmax_fp8) {
+    VDN_TRY(launch_softmax_fp8(s, in, b, main, first_end));
+  } else if (kinds.softmax_mfma) {
+    VDN_TRY(launch_softmax_mfma(s, in, b, main, first_end));
+  } else {
+    VDN_TRY(launch_softmax_simt(s, in, b, main));
+    mark(VDN_STAGE_SOFTMAX_FIRST, 1, main);
+  }
   mark(VDN_STAGE_SOFTMAX, 1, main);
   // join, then readout + gates + projections
   if (side) VDN_TRY(hipStreamWaitEvent(main, ev_join, 0));
@@ -304,7 +311,8 @@ size_t vdn_plan_workspace_bytes(const vdn_plan* plan) { return plan ? plan->lay.
 vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
   if (!plan || !kind) return VDN_ERR_INVALID_ARG;
   switch (stage) {
-    case VDN_STAGE_SOFTMAX: *kind = plan->kinds.softmax_fp8 ? 2 : plan->kinds.softmax_mfma; break;
+    case VDN_STAGE_SOFTMAX:
+    case VDN_STAGE_SOFTMAX_FIRST: *kind = plan->kinds.softmax_fp8 ? 2 : plan->kinds.softmax_mfma; break;
     case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma || plan->kinds.softmax_fp8 || plan->kinds.epilogue_mfma; break;
     case VDN_STAGE_VDA_STATS: *kind = plan->kinds.stats_mfma; break;
     case VDN_STAGE_VDA_SCAN: *kind = plan->kinds.scan_mfma; break;

@@ -459,7 +459,8 @@ int softmax_fp8_grid(const Shape& s, bool with_ctx) {
   return n_ctx_wg + n_bnd_wg + 8 * ((n_int_wg + 7) / 8);
 }
 
-hipError_t launch_softmax_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
+hipError_t launch_softmax_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st,
+                              hipEvent_t after_first) {
   if (s.d != D) return hipErrorInvalidValue;
   Params P{};
   P.q = (const bf16_t*)in.q;
@@ -494,6 +495,7 @@ hipError_t launch_softmax_fp8(const Shape& s, const Inputs& in, const Buffers& b
   (void)hipFuncSetAttribute((const void*)softmax_fp8_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   (void)hipFuncSetAttribute((const void*)softmax_fp8_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipLaunchKernelGGL(softmax_fp8_kernel<false>, dim3(grid), dim3(kWaves * 64), smem, st, P);
+  if (after_first) (void)hipEventRecord(after_first, st);
   hipLaunchKernelGGL(softmax_fp8_kernel<true>, dim3(grid), dim3(kWaves * 64), smem, st, P);
   return hipGetLastError();
 }

@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
 }
 
 template <int D>
-void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
+void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st, hipEvent_t after_first) {
   Params P{};
   P.q = (const bf16_t*)in.q;
   P.qc = (const bf16_t*)in.ctx_q;
@@ -541,6 +541,7 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   (void)hipFuncSetAttribute((const void*)softmax_mfma_kernel<D, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipLaunchKernelGGL((softmax_mfma_kernel<D, false>), dim3(grid), dim3(kWaves * 64), smem, st, P);
+  if (after_first) (void)hipEventRecord(after_first, st);
   hipLaunchKernelGGL((softmax_mfma_kernel<D, true>), dim3(grid), dim3(kWaves * 64), smem, st, P);
 }
 
@@ -555,9 +556,10 @@ int softmax_grid(const Shape& s, bool with_ctx) {
   return n_ctx_wg + n_bnd_wg + 8 * ((n_int_wg + 7) / 8);
 }
 
-hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
-  if (s.d == 128) launch_t<128>(s, in, b, st);
-  else launch_t<64>(s, in, b, st);
+hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st,
+                               hipEvent_t after_first) {
+  if (s.d == 128) launch_t<128>(s, in, b, st, after_first);
+  else launch_t<64>(s, in, b, st, after_first);
   return hipGetLastError();
 }
 

@@ -218,9 +218,12 @@ int softmax_fp8_grid(const Shape& s, bool with_ctx);
 // Launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_prep_kv(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_softmax_simt(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
-hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+// after_first: if not null, recorded on st between the fixed-reference and the online-maximum launch
+hipError_t launch_softmax_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st,
+                               hipEvent_t after_first = nullptr);
 hipError_t launch_prep_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
-hipError_t launch_softmax_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_softmax_fp8(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st,
+                              hipEvent_t after_first = nullptr);
 hipError_t launch_vda_stats(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_vda_stats_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_vda_invert_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);

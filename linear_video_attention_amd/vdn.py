@@ -22,7 +22,7 @@ VDN_FLAG_OVERLAP = 4
 VDN_FLAG_FP8_SOFTMAX = 8
 VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV, VDN_BUF_BW = 0, 1, 2, 3
 VDN_BUF_K8, VDN_BUF_V8, VDN_BUF_SCALES8 = 4, 5, 6
-STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total")
+STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total", "softmax_first")
 
 # every symbol include/vdn.h declares: (name, restype, argtypes)
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
