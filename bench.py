@@ -389,6 +389,22 @@ def main():
                 "fp8_peak_TFLOPs": MFMA_FP8_PEAK_TFLOPS, "softmax_traffic": recorded_traffic("softmax_fp8")}
     fplan.close()
 
+    # the MXFP8 epilogue variant (gate and projection products in MXFP8), alone and with the FP8
+    # softmax (context)
+    mx_info = {}
+    for name, kw in (("fp8_epilogue", {"fp8_epilogue": True}), ("fp8_softmax_and_epilogue", {"fp8": True, "fp8_epilogue": True})):
+        mplan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, **kw)
+        for _ in range(2):
+            forward(mplan)
+        torch.cuda.synchronize()
+        mplan.profile_enable(n_f8)
+        m_steps = timed_steps(lambda: forward(mplan), n_f8)
+        m_ms, m_calls = mplan.profile_read()
+        mx_info[name] = {"ms_per_step_median": float(np.median(m_steps)),
+                         "tokens_per_s": tokens / (float(np.median(m_steps)) * 1e-3),
+                         "stages_ms": {k: v / m_calls for k, v in m_ms.items()}}
+        mplan.close()
+
     overlapped = None
     if args.with_overlap:
         # the linear branch on a side stream next to the softmax branch (context only)
@@ -431,6 +447,7 @@ def main():
     result["decay_gate"] = decay
     result["backward"] = backward_info
     result["fp8_softmax"] = fp8_info
+    result.update(mx_info)
     if overlapped is not None:
         result["overlapped_branches"] = overlapped
     del dev, beta, text_kv, alpha, out, ref

@@ -111,8 +111,23 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
  * exact maximum max x; o = sum P8 V8 / (s_v sum P8).  Inputs and outputs are unchanged (bf16); the linear branch and the merge are the
  * bf16 plan's.  Requires VDN_BF16, d = 128 and N a multiple of 16 (else VDN_ERR_UNSUPPORTED);
  * with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward rejects such plans
- * (VDN_ERR_UNSUPPORTED). */
-enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4, VDN_FLAG_FP8_SOFTMAX = 8 };
+ * (VDN_ERR_UNSUPPORTED).
+ *
+ * VDN_FLAG_FP8_EPILOGUE computes the epilogue's four d x d products -- the two sigmoid gates
+ * q Wg_m and the two output projections of "Gating the Softmax and Linear Branch Outputs" -- in
+ * MXFP8 on the matrix cores (the same page's "Adapting the Pretrained H3 backbone" runs FP8
+ * linear layers without fixing their roundings).  The roundings made here: each operand is cut
+ * into blocks of 32 consecutive elements along the contraction axis (q and the gated branch
+ * outputs per token, each weight column along its input index); a block with largest magnitude
+ * f 2^e (f in [0.5, 1)) is scaled by 2^-(e - 8) (X = e - 8 at least -127, 0 for a zero block) and
+ * its elements rounded to E4M3 (nearest, ties to even); the products of the dequantised operands
+ * accumulate in fp32.  The gated linear-branch output sigmoid(q Wg1) * o_l is quantised before
+ * the RMSNorm factor is applied; the readout S q, the RMSNorm, the sigmoids and the gating stay
+ * as in the bf16 plan.  Combines with VDN_FLAG_FP8_SOFTMAX.  Requires VDN_BF16 and d = 128 (else
+ * VDN_ERR_UNSUPPORTED); with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward
+ * rejects such plans (VDN_ERR_UNSUPPORTED). */
+enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4, VDN_FLAG_FP8_SOFTMAX = 8,
+       VDN_FLAG_FP8_EPILOGUE = 16 };
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,
                               vdn_dtype dtype, unsigned flags, vdn_plan **plan_out);
 
@@ -246,6 +261,18 @@ enum { VDN_BUF_OS = 0, VDN_BUF_STATES = 1, VDN_BUF_MINV = 2, VDN_BUF_BW = 3, VDN
 vdn_status vdn_debug_buffer_bytes(const vdn_plan *plan, int which, size_t *bytes);
 vdn_status vdn_debug_copy(const vdn_plan *plan, int which, void *dst, size_t bytes, void *stream);
 
+/* Runs the plan's epilogue alone ("Gating the Softmax and Linear Branch Outputs": readout, RMSNorm,
+ * gates, projections; MXFP8 products for VDN_FLAG_FP8_EPILOGUE plans) on a caller-supplied softmax
+ * output o_s [T*N][H][d] bf16 and chunk-state buffer in the VDN_BUF_STATES layout
+ * ([2][Nc+1][H][d][d] float32: forward slots, then reverse slots; slot Nc is read by the boundary
+ * frames), with q, gate_w, proj_w and out as in vdn_forward.  Both are copied into the plan's
+ * workspace on `stream` first, so a later vdn_backward_after_forward is rejected until the next
+ * forward.  For testing the epilogue in isolation.  MFMA-epilogue plans only (else
+ * VDN_ERR_UNSUPPORTED); device pointers, 16-byte aligned; out must not overlap an input
+ * (VDN_ERR_INVALID_ARG). */
+vdn_status vdn_debug_epilogue(vdn_plan *plan, const void *q, const void *o_s, const float *states,
+                              const void *gate_w, const void *proj_w, void *out, void *stream);
+
 /* Kernel timing.  vdn_profile_enable(plan, n) makes the next n forwards record HIP events around
  * each stage on the stream it runs on; vdn_profile_read sums the recorded times (milliseconds,
  * synchronising the events) into ms[VDN_STAGE_*] for n_stages entries and reports the number of
@@ -260,7 +287,8 @@ vdn_status vdn_profile_enable(vdn_plan *plan, int max_calls);
 vdn_status vdn_profile_read(vdn_plan *plan, float *ms, int n_stages, int *calls);
 
 /* Which kernel family a plan selected for each stage (0 = generic SIMT kernel, 1 = MFMA kernel,
- * 2 = FP8 MFMA kernel: the softmax stage of VDN_FLAG_FP8_SOFTMAX plans). */
+ * 2 = FP8 MFMA kernel: the softmax stage of VDN_FLAG_FP8_SOFTMAX plans, the epilogue stage of
+ * VDN_FLAG_FP8_EPILOGUE plans). */
 vdn_status vdn_plan_kernel_kind(const vdn_plan *plan, int stage, int *kind);
 
 /* On-box reference rates for rooflines (measurement helpers; synchronous, on the current device's

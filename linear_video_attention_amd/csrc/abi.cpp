@@ -25,6 +25,8 @@ Buffers make_buffers(char* ws, const Layout& lay, const Kinds& kinds, const Shap
   b.qq = kinds.scan_mfma ? reinterpret_cast<float*>(ws + lay.qq) : nullptr;
   b.states = reinterpret_cast<float*>(ws + lay.states);
   b.wt = kinds.epilogue_mfma ? reinterpret_cast<uint16_t*>(ws + lay.wt) : nullptr;
+  b.wt8 = kinds.epilogue_mx ? reinterpret_cast<uint8_t*>(ws + lay.wt8) : nullptr;
+  b.wsc8 = kinds.epilogue_mx ? reinterpret_cast<uint8_t*>(ws + lay.wsc8) : nullptr;
   const bool packed = kinds.softmax_mfma || kinds.softmax_fp8;
   b.kmax_part = kinds.softmax_mfma ? reinterpret_cast<float*>(ws + lay.kmax_part) : nullptr;
   b.kmax = packed ? reinterpret_cast<float*>(ws + lay.kmax) : nullptr;
@@ -66,8 +68,12 @@ vdn_status check_plan_args(int T, int N, int C, int n_text, int n_audio, int H, 
   const int64_t tokens = (int64_t)T * N;
   if (tokens > (int64_t(1) << 31) || tokens * H * d > (int64_t(1) << 40) || n_ctx * H * d > (int64_t(1) << 40))
     return VDN_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP | VDN_FLAG_FP8_SOFTMAX))
+  if (flags & ~(unsigned)(VDN_FLAG_GENERIC_KERNELS | VDN_FLAG_SERIAL | VDN_FLAG_OVERLAP | VDN_FLAG_FP8_SOFTMAX |
+                          VDN_FLAG_FP8_EPILOGUE))
     return VDN_ERR_INVALID_ARG;
+  // MXFP8 epilogue: bf16, d = 128 (one readout wave per 32-channel block), matrix-core kernels
+  if ((flags & VDN_FLAG_FP8_EPILOGUE) && (flags & VDN_FLAG_GENERIC_KERNELS)) return VDN_ERR_INVALID_ARG;
+  if ((flags & VDN_FLAG_FP8_EPILOGUE) && (dtype != VDN_BF16 || d != 128)) return VDN_ERR_UNSUPPORTED;
   if ((flags & VDN_FLAG_SERIAL) && (flags & VDN_FLAG_OVERLAP)) return VDN_ERR_INVALID_ARG;
   const bool fp8 = (flags & VDN_FLAG_FP8_SOFTMAX) != 0;
   if (fp8 && (flags & VDN_FLAG_GENERIC_KERNELS)) return VDN_ERR_INVALID_ARG;
@@ -147,7 +153,8 @@ hipError_t enqueue_forward(const Shape& s, const Kinds& kinds, const Buffers& b,
   mark(VDN_STAGE_PREP, 0, main);
   if (kinds.softmax_mfma) VDN_TRY(launch_prep_kv(s, in, b, main));
   if (kinds.softmax_fp8) VDN_TRY(launch_prep_fp8(s, in, b, main));
-  if (kinds.epilogue_mfma) VDN_TRY(launch_prep_weights(s, in, b, main));
+  if (kinds.epilogue_mx) VDN_TRY(launch_prep_weights_mx(s, in, b, main));
+  else if (kinds.epilogue_mfma) VDN_TRY(launch_prep_weights(s, in, b, main));
   mark(VDN_STAGE_PREP, 1, main);
   mark(VDN_STAGE_SOFTMAX, 0, main);
   mark(VDN_STAGE_SOFTMAX_FIRST, 0, main);
@@ -164,7 +171,7 @@ hipError_t enqueue_forward(const Shape& s, const Kinds& kinds, const Buffers& b,
   // join, then readout + gates + projections
   if (side) VDN_TRY(hipStreamWaitEvent(main, ev_join, 0));
   mark(VDN_STAGE_EPILOGUE, 0, main);
-  if (kinds.epilogue_mfma) VDN_TRY(launch_epilogue_mfma(s, in, b, main));
+  if (kinds.epilogue_mfma) VDN_TRY(launch_epilogue_mfma(s, in, b, kinds.epilogue_mx, main));
   else VDN_TRY(launch_epilogue(s, in, b, false, main));
   mark(VDN_STAGE_EPILOGUE, 1, main);
   mark(VDN_STAGE_TOTAL, 1, main);
@@ -269,6 +276,10 @@ vdn_status vdn_plan_create_joint(int T, int N, int C, int n_text, int n_audio, i
     p->kinds.softmax_mfma = false;
     p->kinds.softmax_fp8 = true;
   }
+  if (flags & VDN_FLAG_FP8_EPILOGUE) {
+    p->kinds.epilogue_mfma = true;
+    p->kinds.epilogue_mx = true;
+  }
   p->overlap = (flags & VDN_FLAG_OVERLAP) != 0;
   p->lay = vdn::make_layout(p->s, p->kinds);
   if (hipGetDevice(&p->device) != hipSuccess) { free_plan(p); return VDN_ERR_HIP; }
@@ -316,7 +327,7 @@ vdn_status vdn_plan_kernel_kind(const vdn_plan* plan, int stage, int* kind) {
     case VDN_STAGE_PREP: *kind = plan->kinds.softmax_mfma || plan->kinds.softmax_fp8 || plan->kinds.epilogue_mfma; break;
     case VDN_STAGE_VDA_STATS: *kind = plan->kinds.stats_mfma; break;
     case VDN_STAGE_VDA_SCAN: *kind = plan->kinds.scan_mfma; break;
-    case VDN_STAGE_EPILOGUE: *kind = plan->kinds.epilogue_mfma; break;
+    case VDN_STAGE_EPILOGUE: *kind = plan->kinds.epilogue_mx ? 2 : plan->kinds.epilogue_mfma; break;
     default: return VDN_ERR_INVALID_ARG;
   }
   return VDN_OK;
@@ -550,7 +561,7 @@ vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const voi
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !dout || !dq || !dk || !dv || !dbeta || !dgate_w ||
       !dproj_w)
     return VDN_ERR_INVALID_ARG;
-  if (plan->s.n_audio > 0 || plan->kinds.softmax_fp8) return VDN_ERR_UNSUPPORTED;
+  if (plan->s.n_audio > 0 || plan->kinds.softmax_fp8 || plan->kinds.epilogue_mx) return VDN_ERR_UNSUPPORTED;
   if (plan->s.n_text > 0 && (!text_kv || !dtext_kv)) return VDN_ERR_INVALID_ARG;
   if (dalpha && !alpha) return VDN_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, dout, dq, dk, dv, dbeta, dgate_w, dproj_w};
@@ -667,6 +678,40 @@ vdn_status vdn_debug_copy(const vdn_plan* plan, int which, void* dst, size_t byt
                : which == VDN_BUF_V8 ? plan->lay.v8
                                      : plan->lay.scale8;
   if (hipMemcpyAsync(dst, plan->ws + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return VDN_ERR_HIP;
+  }
+  return VDN_OK;
+}
+
+vdn_status vdn_debug_epilogue(vdn_plan* plan, const void* q, const void* o_s, const float* states, const void* gate_w,
+                              const void* proj_w, void* out, void* stream) {
+  if (!plan || !q || !o_s || !states || !gate_w || !proj_w || !out) return VDN_ERR_INVALID_ARG;
+  if (!plan->kinds.epilogue_mfma) return VDN_ERR_UNSUPPORTED;
+  const vdn::Shape& s = plan->s;
+  const size_t tok = (size_t)s.T * s.N * s.H * s.d * 2;
+  const size_t st_bytes = (size_t)2 * (s.Nc + 1) * s.H * s.d * s.d * 4;
+  const size_t w_bytes = (size_t)2 * s.d * s.d * 2;
+  const vdn::Span ins[] = {{q, tok}, {o_s, tok}, {states, st_bytes}, {gate_w, w_bytes}, {proj_w, w_bytes}};
+  for (const vdn::Span& i : ins)
+    if (vdn::spans_overlap({out, tok}, i) || (reinterpret_cast<uintptr_t>(i.p) & 15u)) return VDN_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(out) & 15u) return VDN_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return VDN_ERR_HIP;
+  if (dev != plan->device) return VDN_ERR_INVALID_ARG;
+  plan->fwd_valid = false;                       // the workspace no longer holds a forward's intermediates
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const vdn::Buffers b = buffers_of(plan);
+  vdn::Inputs in{};
+  in.q = q;
+  in.gate_w = gate_w;
+  in.proj_w = proj_w;
+  in.out = out;
+  if (hipMemcpyAsync(b.os, o_s, tok, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(b.states, states, st_bytes, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+      (plan->kinds.epilogue_mx ? vdn::launch_prep_weights_mx(s, in, b, st) : vdn::launch_prep_weights(s, in, b, st)) !=
+          hipSuccess ||
+      vdn::launch_epilogue_mfma(s, in, b, plan->kinds.epilogue_mx, st) != hipSuccess) {
     (void)hipGetLastError();
     return VDN_ERR_HIP;
   }

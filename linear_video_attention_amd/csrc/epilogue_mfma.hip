@@ -21,6 +21,17 @@
 // channels.  q tiles are copied straight into LDS (global_load_lds, three buffers, issued two
 // tiles ahead by the readout waves, which are their only readers); all LDS tiles are token rows
 // with 16-byte chunks XOR-swizzled so the 16-lane fragment reads are bank-conflict free.
+//
+// MXFP8 variant (MX = true, d = 128): the four d x d products take E4M3 operands in blocks of 32
+// along the contraction axis, each block with a power-of-two scale 2^X, X = max(e - 8, -127) for
+// a largest magnitude f 2^e (f in [0.5, 1)), on v_mfma_scale_f32_16x16x128_f8f6f4 (the whole
+// contraction in one instruction; the block scales are its E8M0 scale operands).  The readout
+// stays split bf16.  In that instruction lane group g (lanes 16g .. 16g+15) holds k = 16g .. +15
+// in its first 16 bytes and k = 64 + 16g .. +15 in its last 16, and supplies the scale of k block
+// g: each readout lane quantises its own two q half-blocks (block maxima from the partner lane
+// group) and fetches the scale it must supply from the lane group that holds that block's first
+// half.  x_s and z_l are quantised per token and 32-channel block -- exactly one readout wave's
+// channels -- and handed over as two E4M3 planes plus one scale byte per token and block.
 #include "dev_common.h"
 #include "vdn_internal.h"
 
@@ -31,6 +42,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -50,15 +62,66 @@ __device__ __forceinline__ int swz(int r) {
   else return (r >> 1) & 7;
 }
 
-template <int D>
+template <int D, bool MX>
 struct EpiSmem {
   static constexpr int ROW = 2 * D;                          // bytes per token row
   static constexpr int PLANE = kTileTok * ROW;
+  static constexpr int PLANE8 = kTileTok * D;                // E4M3 planes (MX)
   static constexpr int Q_OFF = 0;                            // kQBufs q tiles
   static constexpr int X_OFF = kQBufs * PLANE;               // [2][3] planes: x_s, z_l hi, z_l lo
-  static constexpr int P_OFF = X_OFF + 6 * PLANE;            // [2][4 waves][kTileTok] floats
+                                                             // (MX: [2][2] E4M3 planes x_s, z_l)
+  static constexpr int SC_OFF = X_OFF + (MX ? 4 * PLANE8 : 6 * PLANE);  // MX: [2][2][kTileTok][4] scale bytes
+  static constexpr int P_OFF = SC_OFF + (MX ? 2 * 2 * kTileTok * 4 : 0);  // [2][4 waves][kTileTok] floats
   static constexpr int TOTAL = P_OFF + 2 * 4 * kTileTok * 4;
 };
+
+// Block exponent of the MX format: X = max(e - 8, -127) for m = f 2^e (f in [0.5, 1)), 0 for
+// m = 0 (m >= 0; every subnormal m gives -127).
+__device__ __forceinline__ int mx_exponent(float m) {
+  const int E = (int)((__float_as_uint(m) >> 23) & 0xFFu);
+  if (E == 0) return m > 0.f ? -127 : 0;
+  return max(E - 134, -127);
+}
+
+// 2^x for -126 <= x <= 127
+__device__ __forceinline__ float exp2i(int x) { return __uint_as_float((uint32_t)(x + 127) << 23); }
+
+// four floats, already scaled into the block's range, as E4M3 codes (nearest, ties to even)
+__device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// MX weights: wt8[m][j][i] = E4M3 code of W_m[i][j] / 2^X and wsc8[m][j][b] = X + 127, X the
+// exponent of block b = i / 32 of column j (gate_w[0], gate_w[1], proj_w[0], proj_w[1])
+__global__ __launch_bounds__(512) void prep_weights_mx_kernel(const bf16_t* __restrict__ gate_w,
+                                                              const bf16_t* __restrict__ proj_w,
+                                                              uint8_t* __restrict__ wt8, uint8_t* __restrict__ wsc8,
+                                                              int D) {
+  const int m = blockIdx.y;
+  const bf16_t* src = m < 2 ? gate_w + (int64_t)m * D * D : proj_w + (int64_t)(m - 2) * D * D;
+  const int nb = D / 32;
+  for (int e = blockIdx.x * 512 + threadIdx.x; e < D * nb; e += gridDim.x * 512) {
+    const int j = e % D, b = e / D;           // consecutive threads: consecutive columns (coalesced reads)
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      v[t] = __uint_as_float((uint32_t)src[(int64_t)(32 * b + t) * D + j] << 16);
+      amax = fmaxf(amax, fabsf(v[t]));
+    }
+    const int X = mx_exponent(amax);
+    const float sc = exp2i(-X);
+    uint8_t* dst = wt8 + ((int64_t)m * D + j) * D + 32 * b;
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4)
+      reinterpret_cast<int*>(dst)[i4] = pack4_e4m3(v[4 * i4] * sc, v[4 * i4 + 1] * sc, v[4 * i4 + 2] * sc, v[4 * i4 + 3] * sc);
+    wsc8[((int64_t)m * D + j) * nb + b] = (uint8_t)(X + 127);
+  }
+}
 
 // W^T for gate_w[0], gate_w[1], proj_w[0], proj_w[1]: wt[m][j][i] = W_m[i][j]
 __global__ __launch_bounds__(256) void prep_weights_kernel(const bf16_t* __restrict__ gate_w,
@@ -74,14 +137,17 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(const bf16_t* __restr
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-template <int D>
+template <int D, bool MX>
 __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __restrict__ q,
                                                             const bf16_t* __restrict__ o_s,
                                                             const float* __restrict__ states,
-                                                            const bf16_t* __restrict__ wt, bf16_t* __restrict__ out,
+                                                            const bf16_t* __restrict__ wt,
+                                                            const uint8_t* __restrict__ wt8,
+                                                            const uint8_t* __restrict__ wsc8, bf16_t* __restrict__ out,
                                                             int T, int N, int H, int C, int Nc, int anchors,
                                                             int wg_per_frame) {
-  using SM = EpiSmem<D>;
+  using SM = EpiSmem<D, MX>;
+  static_assert(!MX || D == 128, "MX epilogue: d = 128 (one readout wave per 32-channel block)");
   constexpr int CT = D / 64;              // 16-channel tiles per wave (4 waves per stage cover D)
   constexpr int KS = D / 32;              // k-steps of 32
   constexpr int CH = D / 8;               // 16-byte chunks per token row
@@ -105,6 +171,16 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
 
   // fragment byte offset of (token row r, channels k0 .. k0+7) in a swizzled tile
   auto frag_off = [&](int r, int k0) { return r * SM::ROW + (((k0 >> 3) ^ swz<D>(r)) << 4); };
+  // byte offset of (token row r, channels 16 c .. 16 c + 15) in an E4M3 plane (MX)
+  auto off8 = [&](int r, int c) { return r * D + ((c ^ (r & 7)) << 4); };
+  // MX weight fragment (A operand) of matrix m, row j, for this lane's group, and its scale
+  auto wfrag8 = [&](int m, int j, i32x8& a, int& sc) {
+    const uint8_t* row = wt8 + ((int64_t)m * D + j) * D;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 16 * lg);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 64 + 16 * lg);
+    a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    sc = wsc8[((int64_t)m * D + j) * (D / 32) + lg];
+  };
 
   // q DMA (readout waves): instruction i of stage wave sw fills token rows
   // (i*4 + sw)*ROWS_PER_KB + lane / CH; the lane fetches chunk (lane % CH) ^ swz(row).  Rows past the
@@ -144,9 +220,11 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
     const int slot = bnd ? Nc : t / C;
     const float* sf = states + ((int64_t)slot * H + h) * DD;
     const float* sr = states + (((int64_t)(Nc + 1) + slot) * H + h) * DD;
-    bf16x8 s_hi[CT][KS], s_lo[CT][KS], wg0[CT][KS], wg1[CT][KS];
+    bf16x8 s_hi[CT][KS], s_lo[CT][KS], wg0[MX ? 1 : CT][MX ? 1 : KS], wg1[MX ? 1 : CT][MX ? 1 : KS];
+    i32x8 wg8[2][CT];                       // MX gate weights and their block scales
+    int wgs[2][CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int j = (sw * CT + ct) * 16 + l16, i0 = ks * 32 + lg * 8;
@@ -160,9 +238,17 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
           s_hi[ct][ks][e] = hi;
           s_lo[ct][ks][e] = (__bf16)(sv - (float)hi);
         }
-        wg0[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 0 * DD + (int64_t)j * D + i0));
-        wg1[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 1 * DD + (int64_t)j * D + i0));
+        if constexpr (!MX) {
+          wg0[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 0 * DD + (int64_t)j * D + i0));
+          wg1[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 1 * DD + (int64_t)j * D + i0));
+        }
       }
+      if constexpr (MX) {
+        const int j = (sw * CT + ct) * 16 + l16;
+        wfrag8(0, j, wg8[0][ct], wgs[0][ct]);
+        wfrag8(1, j, wg8[1][ct], wgs[1][ct]);
+      }
+    }
     // Issue order per tile: the o_s loads of the next tile, then the q DMA of the tile after; the
     // wait for those o_s loads (before their registers are used) then leaves the DMA in flight.
     __builtin_amdgcn_s_waitcnt(0x0F70);                // q tiles 0 (and 1) landed
@@ -172,7 +258,7 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
         if (it + 1 < ntiles) fetch_os(it + 1, osb);
         if (it + 2 < ntiles) issue_q(it + 2);          // its buffer held tile it-1, read in the last iteration
         const unsigned char* qb = smem + SM::Q_OFF + (it % kQBufs) * SM::PLANE;
-        unsigned char* xb = smem + SM::X_OFF + (it & 1) * 3 * SM::PLANE;
+        unsigned char* xb = smem + SM::X_OFF + (it & 1) * (MX ? 2 * SM::PLANE8 : 3 * SM::PLANE);
         float* part = reinterpret_cast<float*>(smem + SM::P_OFF) + (it & 1) * 4 * kTileTok + sw * kTileTok;
 #pragma unroll
         for (int sub = 0; sub < kSub; ++sub) {
@@ -187,32 +273,117 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
             for (int ct = 0; ct < CT; ++ct) {
               ol[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_hi[ct][ks], qf, ol[ct], 0, 0, 0);
               ol[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s_lo[ct][ks], qf, ol[ct], 0, 0, 0);
-              gs[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg0[ct][ks], qf, gs[ct], 0, 0, 0);
-              gl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg1[ct][ks], qf, gl[ct], 0, 0, 0);
+              if constexpr (!MX) {
+                gs[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg0[ct][ks], qf, gs[ct], 0, 0, 0);
+                gl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg1[ct][ks], qf, gl[ct], 0, 0, 0);
+              }
+            }
+          }
+          if constexpr (MX) {
+            // q of token r as the B operand: k = 16 lg .. +15 (half A, block lg / 2) and
+            // k = 64 + 16 lg .. +15 (half B, block 2 + lg / 2), each half quantised with its block
+            uint32_t h[2][8];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const u32x4 c0 = *reinterpret_cast<const u32x4*>(qb + frag_off(r, 64 * hf + 16 * lg));
+              const u32x4 c1 = *reinterpret_cast<const u32x4*>(qb + frag_off(r, 64 * hf + 16 * lg + 8));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                h[hf][i] = c0[i];
+                h[hf][4 + i] = c1[i];
+              }
+            }
+            float am[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              float m = 0.f;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(h[hf][i])), fabsf(bf16_hi(h[hf][i]))));
+              am[hf] = fmaxf(m, __shfl_xor(m, 16));          // both halves of the block
+            }
+            const int xa = mx_exponent(am[0]), xb = mx_exponent(am[1]);
+            // lane group g supplies block g's scale: block 0 and 2 sit in group 0, block 1 in
+            // group 2 (half A), block 3 in group 3 (half B)
+            const int both = (xa + 127) | ((xb + 127) << 8);
+            const int got = __shfl(both, l16 + 16 * ((0xC8 >> (2 * lg)) & 3));
+            const int qsc = lg < 2 ? (got & 0xFF) : ((got >> 8) & 0xFF);
+            i32x8 q8;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const float sc = exp2i(-(hf ? xb : xa));
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                q8[4 * hf + i] = pack4_e4m3(bf16_lo(h[hf][2 * i]) * sc, bf16_hi(h[hf][2 * i]) * sc,
+                                            bf16_lo(h[hf][2 * i + 1]) * sc, bf16_hi(h[hf][2 * i + 1]) * sc);
+            }
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              gs[ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wg8[0][ct], q8, z, 0, 0, 0, wgs[0][ct], 0, qsc);
+              gl[ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wg8[1][ct], q8, z, 0, 0, 0, wgs[1][ct], 0, qsc);
             }
           }
           // outputs: channel 16 (sw CT + ct) + 4 lg + e, token row r
           float ss = 0.f;
+          float xsv[CT][4], zlv[CT][4];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const uint32_t o01 = osa[ct][sub].x, o23 = osa[ct][sub].y;
-            const float osv[4] = {__uint_as_float(o01 << 16), __uint_as_float(o01 & 0xFFFF0000u),
-                                  __uint_as_float(o23 << 16), __uint_as_float(o23 & 0xFFFF0000u)};
-            bf16x4 xs, zh, zl;
+            const float osv[4] = {bf16_lo(o01), bf16_hi(o01), bf16_lo(o23), bf16_hi(o23)};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               ss += ol[ct][e] * ol[ct][e];
-              const float xsv = fast_sigmoid(gs[ct][e]) * osv[e];
-              const float zlv = fast_sigmoid(gl[ct][e]) * ol[ct][e];
-              xs[e] = (__bf16)xsv;
-              zh[e] = (__bf16)zlv;
-              zl[e] = (__bf16)(zlv - (float)zh[e]);
+              xsv[ct][e] = fast_sigmoid(gs[ct][e]) * osv[e];
+              zlv[ct][e] = fast_sigmoid(gl[ct][e]) * ol[ct][e];
             }
-            const int ch = (sw * CT + ct) * 16 + lg * 4;
-            const int off = frag_off(r, ch) + (ch & 4) * 2;
-            *reinterpret_cast<bf16x4*>(xb + off) = xs;
-            *reinterpret_cast<bf16x4*>(xb + SM::PLANE + off) = zh;
-            *reinterpret_cast<bf16x4*>(xb + 2 * SM::PLANE + off) = zl;
+          }
+          if constexpr (MX) {
+            // this wave's 32 channels are block sw of token r: maxima over the lane's 8 values and
+            // the four lane groups, then E4M3 codes and the block's scale byte
+            float mx = 0.f, mz = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                mx = fmaxf(mx, fabsf(xsv[ct][e]));
+                mz = fmaxf(mz, fabsf(zlv[ct][e]));
+              }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mz = fmaxf(mz, __shfl_xor(mz, 16));
+            mz = fmaxf(mz, __shfl_xor(mz, 32));
+            const int ex = mx_exponent(mx), ez = mx_exponent(mz);
+            const float sx = exp2i(-ex), sz = exp2i(-ez);
+            unsigned char* x8 = xb;                      // [2][PLANE8]: x_s, z_l
+            uint8_t* scb = reinterpret_cast<uint8_t*>(smem + SM::SC_OFF) + (it & 1) * 2 * kTileTok * 4;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              const int off = off8(r, sw * CT + ct) + 4 * lg;
+              *reinterpret_cast<int*>(x8 + off) =
+                  pack4_e4m3(xsv[ct][0] * sx, xsv[ct][1] * sx, xsv[ct][2] * sx, xsv[ct][3] * sx);
+              *reinterpret_cast<int*>(x8 + SM::PLANE8 + off) =
+                  pack4_e4m3(zlv[ct][0] * sz, zlv[ct][1] * sz, zlv[ct][2] * sz, zlv[ct][3] * sz);
+            }
+            if (lg == 0) {
+              scb[r * 4 + sw] = (uint8_t)(ex + 127);
+              scb[kTileTok * 4 + r * 4 + sw] = (uint8_t)(ez + 127);
+            }
+          } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              bf16x4 xs, zh, zl;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                xs[e] = (__bf16)xsv[ct][e];
+                zh[e] = (__bf16)zlv[ct][e];
+                zl[e] = (__bf16)(zlv[ct][e] - (float)zh[e]);
+              }
+              const int ch = (sw * CT + ct) * 16 + lg * 4;
+              const int off = frag_off(r, ch) + (ch & 4) * 2;
+              *reinterpret_cast<bf16x4*>(xb + off) = xs;
+              *reinterpret_cast<bf16x4*>(xb + SM::PLANE + off) = zh;
+              *reinterpret_cast<bf16x4*>(xb + 2 * SM::PLANE + off) = zl;
+            }
           }
           ss += __shfl_xor(ss, 16);
           ss += __shfl_xor(ss, 32);
@@ -229,20 +400,30 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
     }
   } else {
     // ---- projection waves: channels [16 CT sw, +16 CT) ----
-    bf16x8 wp0[CT][KS], wp1[CT][KS];
+    bf16x8 wp0[MX ? 1 : CT][MX ? 1 : KS], wp1[MX ? 1 : CT][MX ? 1 : KS];
+    i32x8 wp8[2][CT];                       // MX projection weights and their block scales
+    int wps[2][CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int ct = 0; ct < CT; ++ct) {
+      const int j = (sw * CT + ct) * 16 + l16;
+      if constexpr (MX) {
+        wfrag8(2, j, wp8[0][ct], wps[0][ct]);
+        wfrag8(3, j, wp8[1][ct], wps[1][ct]);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int j = (sw * CT + ct) * 16 + l16, i0 = ks * 32 + lg * 8;
-        wp0[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 2 * DD + (int64_t)j * D + i0));
-        wp1[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 3 * DD + (int64_t)j * D + i0));
+        for (int ks = 0; ks < KS; ++ks) {
+          const int i0 = ks * 32 + lg * 8;
+          wp0[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 2 * DD + (int64_t)j * D + i0));
+          wp1[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(wt + 3 * DD + (int64_t)j * D + i0));
+        }
       }
+    }
     __syncthreads();
     for (int it = 0; it <= ntiles; ++it) {
       if (it >= 1) {
         const int pt = it - 1;                         // the tile handed over at the last barrier
-        const unsigned char* xb = smem + SM::X_OFF + (pt & 1) * 3 * SM::PLANE;
+        const unsigned char* xb = smem + SM::X_OFF + (pt & 1) * (MX ? 2 * SM::PLANE8 : 3 * SM::PLANE);
+        const uint8_t* scb = reinterpret_cast<const uint8_t*>(smem + SM::SC_OFF) + (pt & 1) * 2 * kTileTok * 4;
         const float* part = reinterpret_cast<const float*>(smem + SM::P_OFF) + (pt & 1) * 4 * kTileTok;
         const int tok0 = tok_begin + pt * kTileTok;
 #pragma unroll
@@ -251,17 +432,35 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
           f32x4 as[CT], al[CT];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) as[ct] = al[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (MX) {
+            // B operands: token r, channels 16 lg .. +15 and 64 + 16 lg .. +15; scale of block lg
+            i32x8 x8[2];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int off = frag_off(r, ks * 32 + lg * 8);
-            const bf16x8 xs = *reinterpret_cast<const bf16x8*>(xb + off);
-            const bf16x8 zh = *reinterpret_cast<const bf16x8*>(xb + SM::PLANE + off);
-            const bf16x8 zl = *reinterpret_cast<const bf16x8*>(xb + 2 * SM::PLANE + off);
+            for (int pl = 0; pl < 2; ++pl) {
+              const unsigned char* pb = xb + pl * SM::PLANE8;
+              const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + off8(r, lg));
+              const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + off8(r, 4 + lg));
+              x8[pl] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+            const int sx = scb[r * 4 + lg], sz = scb[kTileTok * 4 + r * 4 + lg];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-              as[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp0[ct][ks], xs, as[ct], 0, 0, 0);
-              al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ct][ks], zh, al[ct], 0, 0, 0);
-              al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ct][ks], zl, al[ct], 0, 0, 0);
+              as[ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wp8[0][ct], x8[0], as[ct], 0, 0, 0, wps[0][ct], 0, sx);
+              al[ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wp8[1][ct], x8[1], al[ct], 0, 0, 0, wps[1][ct], 0, sz);
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              const int off = frag_off(r, ks * 32 + lg * 8);
+              const bf16x8 xs = *reinterpret_cast<const bf16x8*>(xb + off);
+              const bf16x8 zh = *reinterpret_cast<const bf16x8*>(xb + SM::PLANE + off);
+              const bf16x8 zl = *reinterpret_cast<const bf16x8*>(xb + 2 * SM::PLANE + off);
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct) {
+                as[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp0[ct][ks], xs, as[ct], 0, 0, 0);
+                al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ct][ks], zh, al[ct], 0, 0, 0);
+                al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wp1[ct][ks], zl, al[ct], 0, 0, 0);
+              }
             }
           }
           const float ss = part[r] + part[kTileTok + r] + part[2 * kTileTok + r] + part[3 * kTileTok + r];
@@ -283,15 +482,15 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
   }
 }
 
-template <int D>
+template <int D, bool MX>
 void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
   const int wg_per_frame = (s.N + kTokPerWG - 1) / kTokPerWG;
-  const size_t smem = EpiSmem<D>::TOTAL;
-  (void)hipFuncSetAttribute((const void*)epilogue_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  const size_t smem = EpiSmem<D, MX>::TOTAL;
+  (void)hipFuncSetAttribute((const void*)epilogue_mfma_kernel<D, MX>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)smem);
-  hipLaunchKernelGGL(epilogue_mfma_kernel<D>, dim3(s.T * wg_per_frame, s.H), dim3(512), smem, st,
-                     (const bf16_t*)in.q, (const bf16_t*)b.os, b.states, b.wt, (bf16_t*)in.out, s.T, s.N, s.H, s.C,
-                     s.Nc, s.anchors, wg_per_frame);
+  hipLaunchKernelGGL((epilogue_mfma_kernel<D, MX>), dim3(s.T * wg_per_frame, s.H), dim3(512), smem, st,
+                     (const bf16_t*)in.q, (const bf16_t*)b.os, b.states, b.wt, b.wt8, b.wsc8, (bf16_t*)in.out, s.T,
+                     s.N, s.H, s.C, s.Nc, s.anchors, wg_per_frame);
 }
 
 }  // namespace
@@ -302,9 +501,22 @@ hipError_t launch_prep_weights(const Shape& s, const Inputs& in, const Buffers& 
   return hipGetLastError();
 }
 
-hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
-  if (s.d == 128) launch_t<128>(s, in, b, st);
-  else launch_t<64>(s, in, b, st);
+hipError_t launch_prep_weights_mx(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st) {
+  if (s.d != 128 || !b.wt8 || !b.wsc8) return hipErrorInvalidValue;
+  prep_weights_mx_kernel<<<dim3(1, 4), 512, 0, st>>>((const bf16_t*)in.gate_w, (const bf16_t*)in.proj_w, b.wt8, b.wsc8,
+                                                     s.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, bool mx, hipStream_t st) {
+  if (mx) {
+    if (s.d != 128 || !b.wt8 || !b.wsc8) return hipErrorInvalidValue;
+    launch_t<128, true>(s, in, b, st);
+  } else if (s.d == 128) {
+    launch_t<128, false>(s, in, b, st);
+  } else {
+    launch_t<64, false>(s, in, b, st);
+  }
   return hipGetLastError();
 }
 

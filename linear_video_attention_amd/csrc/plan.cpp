@@ -43,6 +43,8 @@ Layout make_layout(const Shape& s, const Kinds& k) {
   L.qq = k.scan_mfma ? take((size_t)2 * s.Nc * s.H * dd * 4) : 0;
   L.states = take((size_t)2 * (s.Nc + 1) * s.H * dd * 4);
   L.wt = mfma_epilogue ? take((size_t)4 * dd * 2) : 0;
+  L.wt8 = k.epilogue_mx ? take((size_t)4 * dd) : 0;
+  L.wsc8 = k.epilogue_mx ? take((size_t)4 * dd / 32) : 0;
   L.kmax_part = mfma_softmax ? take((size_t)s.H * ((s.Lk + 63) / 64) * 4) : 0;
   L.kmax = (mfma_softmax || k.softmax_fp8) ? take((size_t)s.H * 4) : 0;
   L.flags = mfma_softmax ? take((size_t)softmax_grid(s, true) * 4) : k.softmax_fp8 ? take((size_t)softmax_fp8_grid(s, true) * 4) : 0;

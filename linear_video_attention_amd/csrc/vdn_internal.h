@@ -77,6 +77,8 @@ struct Layout {
   size_t qq;        // chunk maps Q_fwd, Q_rev [2][Nc][H][d][d] f32 (MFMA scan only)
   size_t states;    // S_fwd, S_rev  [2][Nc+1][H][d][d] f32
   size_t wt;        // transposed weights [4][d][d] bf16: Wg0^T, Wg1^T, Wp0^T, Wp1^T (MFMA epilogue)
+  size_t wt8;       // MX epilogue: the same as E4M3 codes [4][d][d] bytes
+  size_t wsc8;      // MX epilogue: their block scales (E8M0) [4][d][d/32] bytes
   size_t kmax_part; // largest key norm per 64-key block [H][Lk/64] f32  (MFMA softmax path only)
   size_t kmax;      // largest key norm per head [H] f32
   size_t flags;     // per-workgroup fallback flags of the MFMA softmax [softmax_grid] int32
@@ -95,6 +97,7 @@ struct Kinds {
   bool stats_mfma;
   bool scan_mfma;
   bool epilogue_mfma;
+  bool epilogue_mx;   // MXFP8 gate and projection products (with epilogue_mfma, d = 128)
 };
 Kinds choose_kinds(const Shape& s);
 Layout make_layout(const Shape& s, const Kinds& k);
@@ -111,6 +114,8 @@ struct Buffers {
   float* qq;
   float* states;
   uint16_t* wt;
+  uint8_t* wt8;        // MX epilogue weights and block scales, or nullptr
+  uint8_t* wsc8;
   float* kmax_part;
   float* kmax;
   int* flags;
@@ -231,6 +236,7 @@ hipError_t launch_vda_scan(const Shape& s, const Inputs& in, const Buffers& b, b
 hipError_t launch_vda_scan_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
 hipError_t launch_epilogue(const Shape& s, const Inputs& in, const Buffers& b, bool mfma, hipStream_t st);
 hipError_t launch_prep_weights(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
-hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_prep_weights_mx(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st);
+hipError_t launch_epilogue_mfma(const Shape& s, const Inputs& in, const Buffers& b, bool mx, hipStream_t st);
 
 }  // namespace vdn

@@ -20,9 +20,12 @@ VDN_FLAG_GENERIC_KERNELS = 1
 VDN_FLAG_SERIAL = 2
 VDN_FLAG_OVERLAP = 4
 VDN_FLAG_FP8_SOFTMAX = 8
+VDN_FLAG_FP8_EPILOGUE = 16
 VDN_BUF_OS, VDN_BUF_STATES, VDN_BUF_MINV, VDN_BUF_BW = 0, 1, 2, 3
 VDN_BUF_K8, VDN_BUF_V8, VDN_BUF_SCALES8 = 4, 5, 6
 STAGES = ("softmax", "prep", "vda_stats", "vda_scan", "epilogue", "total", "softmax_first")
+(VDN_STAGE_SOFTMAX, VDN_STAGE_PREP, VDN_STAGE_VDA_STATS, VDN_STAGE_VDA_SCAN, VDN_STAGE_EPILOGUE, VDN_STAGE_TOTAL,
+ VDN_STAGE_SOFTMAX_FIRST) = range(7)
 
 # every symbol include/vdn.h declares: (name, restype, argtypes)
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -43,6 +46,7 @@ SIGNATURES = [
     ("vdn_scan_frames", _c_int, [_c_int] * 5 + [ctypes.POINTER(_c_int), _c_int]),
     ("vdn_debug_buffer_bytes", _c_int, [_vp, _c_int, ctypes.POINTER(_c_size)]),
     ("vdn_debug_copy", _c_int, [_vp, _c_int, _vp, _c_size, _vp]),
+    ("vdn_debug_epilogue", _c_int, [_vp] * 8),
     ("vdn_profile_enable", _c_int, [_vp, _c_int]),
     ("vdn_profile_read", _c_int, [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]),
     ("vdn_plan_kernel_kind", _c_int, [_vp, _c_int, ctypes.POINTER(_c_int)]),
@@ -118,13 +122,15 @@ def measure_copy_gbs(nbytes=1 << 30):
 # ---- plan ----
 
 def vdn_plan_create(T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
-                    overlap=False, n_audio=0, fp8=False):
+                    overlap=False, n_audio=0, fp8=False, fp8_epilogue=False):
     """Create a plan; returns an opaque handle (int).  ``dtype`` is "bf16" or "fp32"; ``n_audio``
-    audio tokens follow the text tokens (a joint plan); ``fp8`` selects the FP8 softmax branch."""
+    audio tokens follow the text tokens (a joint plan); ``fp8`` selects the FP8 softmax branch,
+    ``fp8_epilogue`` the MXFP8 gate and projection products."""
     dt = {"bf16": VDN_BF16, "fp32": VDN_F32}[dtype]
     h = _vp()
     flags = ((VDN_FLAG_GENERIC_KERNELS if generic else 0) | (VDN_FLAG_SERIAL if serial else 0)
-             | (VDN_FLAG_OVERLAP if overlap else 0) | (VDN_FLAG_FP8_SOFTMAX if fp8 else 0))
+             | (VDN_FLAG_OVERLAP if overlap else 0) | (VDN_FLAG_FP8_SOFTMAX if fp8 else 0)
+             | (VDN_FLAG_FP8_EPILOGUE if fp8_epilogue else 0))
     if n_audio:
         _check(lib().vdn_plan_create_joint(T, N, C, n_text, n_audio, H, d, int(anchors), dt, flags,
                                            ctypes.byref(h)), "vdn_plan_create_joint")
@@ -193,7 +199,7 @@ class Plan:
     """Owning wrapper of a plan with argument checks on torch tensors."""
 
     def __init__(self, T, N, C, n_text, H, d, anchors=True, dtype="bf16", generic=False, serial=False,
-                 overlap=False, n_audio=0, fp8=False):
+                 overlap=False, n_audio=0, fp8=False, fp8_epilogue=False):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("no GPU visible: the VDN layer runs only on the GPU")
@@ -206,7 +212,9 @@ class Plan:
         self.Nc = (T + C - 1) // C
         self.fp8 = bool(fp8)
         self.Ls8 = (self.n_ctx + 63) // 64 * 64 + T * N + 128
-        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap, n_audio, fp8)
+        self.fp8_epilogue = bool(fp8_epilogue)
+        self.handle = vdn_plan_create(T, N, C, n_text, H, d, anchors, dtype, generic, serial, overlap, n_audio, fp8,
+                                      fp8_epilogue)
 
     def close(self):
         if self.handle:
@@ -321,6 +329,23 @@ class Plan:
         _check(lib().vdn_debug_copy(self.handle, which, dst.data_ptr(), nbytes.value, _stream_ptr(stream)),
                "vdn_debug_copy")
         return dst
+
+    def debug_epilogue(self, q, o_s, states, gate_w, proj_w, out=None, stream=None):
+        """The plan's epilogue alone on a given softmax output o_s [T*N, H, d] and chunk-state
+        buffer states [2, Nc+1, H, d, d] (float32); returns out [T*N, H, d]."""
+        import torch
+        shp = (self.T * self.N, self.H, self.d)
+        for name, t, dt, want in (("q", q, self.torch_dtype, shp), ("o_s", o_s, self.torch_dtype, shp),
+                                  ("states", states, torch.float32, (2, self.Nc + 1, self.H, self.d, self.d)),
+                                  ("gate_w", gate_w, self.torch_dtype, (2, self.d, self.d)),
+                                  ("proj_w", proj_w, self.torch_dtype, (2, self.d, self.d))):
+            if t.dtype != dt or tuple(t.shape) != want or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name}: expected a contiguous CUDA {dt} tensor of shape {want}")
+        if out is None:
+            out = torch.empty(shp, dtype=self.torch_dtype, device="cuda")
+        _check(lib().vdn_debug_epilogue(self.handle, q.data_ptr(), o_s.data_ptr(), states.data_ptr(), gate_w.data_ptr(),
+                                        proj_w.data_ptr(), out.data_ptr(), _stream_ptr(stream)), "vdn_debug_epilogue")
+        return out
 
     def workspace_bytes(self):
         return lib().vdn_plan_workspace_bytes(self.handle)
