@@ -9,6 +9,7 @@ import torch
 
 import synth
 from oracle import vdn_backward as bwd
+from oracle import vdn_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
@@ -76,8 +77,11 @@ def test_backward_ragged(case):
 
 def test_backward_768p_sampled_dq():
     """768p in the benchmark's configuration: dq of sampled rows (every frame's first and last
-    token plus two random tokens per frame, all heads) against the row-wise oracle; every other
-    gradient is checked for finiteness here and against the full oracle at the smaller shapes."""
+    token plus two random tokens per frame, all heads) against the row-wise oracle; every element
+    of dbeta, dgate_w[1] and dproj_w[1] (the gradients that do not pass through the softmax
+    branch: the merge's linear half and the linear branch's backward) against the full oracle;
+    dk, dv and the softmax half of the weight gradients are checked for finiteness here and
+    against the full oracle at the smaller shapes."""
     w = synth.WORKLOADS["768p"]
     inp = synth.make_inputs(w, seed=0)
     dout = np.random.default_rng(7).standard_normal((w.T * w.N, w.H, w.d)).astype(np.float32)
@@ -89,14 +93,32 @@ def test_backward_768p_sampled_dq():
     torch.cuda.synchronize()
     rows = synth.sample_rows(w)
     got = g["q"][torch.from_numpy(rows).cuda()].cpu().numpy()
+    got_beta = g["beta"].cpu().numpy()
+    got_gw1 = g["gate_w"][1].cpu().numpy()
+    got_pw1 = g["proj_w"][1].cpu().numpy()
     finite = all(bool(torch.isfinite(x).all()) for x in g.values())
     del dev, g
+    plan.close()
     ref = bwd.dq_rows(inp, dout.astype(np.float64), w.T, w.N, w.C, w.anchors, rows)
     e = rel_err(got, ref)
     print(f"768p backward: dq of {len(rows)} sampled rows, err {e:.2e}", flush=True)
     assert finite
     assert e <= TOL[w.dtype]
-    plan.close()
+    # linear half: do_l, dgate_w[1] and dproj_w[1] do not depend on o_s (zero here)
+    print("768p backward: oracle linear branch ...", flush=True)
+    o_l = orc.linear_branch(inp["q"], inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"],
+                            w.T, w.N, w.C, w.anchors)
+    print("768p backward: oracle merge backward ...", flush=True)
+    _, _, do_l, dgate, dproj = bwd.merge_backward(inp["q"], np.zeros_like(o_l), o_l, inp["gate_w"], inp["proj_w"],
+                                                  dout.astype(np.float64))
+    print("768p backward: oracle linear-branch backward ...", flush=True)
+    dbeta = bwd.linear_backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["text_k"], inp["text_v"],
+                                w.T, w.N, w.C, w.anchors, do_l)[3]
+    errs = {"beta": rel_err(got_beta, dbeta), "gate_w[1]": rel_err(got_gw1, dgate[1]),
+            "proj_w[1]": rel_err(got_pw1, dproj[1])}
+    print("768p backward, linear half: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for name, err in errs.items():
+        assert err <= TOL[w.dtype], (name, err)
 
 
 @pytest.mark.parametrize("decay", [False, True])
