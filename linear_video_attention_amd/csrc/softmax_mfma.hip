@@ -356,11 +356,16 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
   };
   // lane's score i of row tile u is key half*32 + 8 g + 4 u + i
   auto mask = [&](int half, int valid, f32x4 (&sacc)[2][kQT]) {
+    // an opaque copy of g: with it the compiler cannot prove the key offset below 64, so the
+    // caller's "valid < kBK" test stays a real branch that full tiles skip (else it becomes an
+    // unconditional select on every score of every tile)
+    int gl = g;
+    asm volatile("" : "+v"(gl));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (half * 32 + 8 * g + 4 * u + i >= valid) {
+        if (half * 32 + 8 * gl + 4 * u + i >= valid) {
 #pragma unroll
           for (int j = 0; j < kQT; ++j) sacc[u][j][i] = kMasked;
         }
