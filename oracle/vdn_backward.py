@@ -23,8 +23,13 @@ below is the transpose of the corresponding step of the forward definition in ``
 
 [VDN] = "Video DeltaNet: Near-Lossless Hybrid Attention for Video Models" (openvdn.github.io);
 [FTP] = "Faster Than It Plays: Video DeltaNet Generates 14 Seconds of 768p Video in 11 Seconds"
-(ai-blog.deepmagic.app).  Audio tokens and context query rows are not covered here (their
-gradients are those of plain softmax attention).
+(ai-blog.deepmagic.app).
+
+Joint sequences ([GLN] = "Video DeltaNet speeds MiniMax H3 video generation 14.5x", summary: every
+interaction with a text or audio token keeps the full softmax attention): audio keys are global
+softmax keys of the video rows beside the text keys, so their gradients come from the same softmax
+transpose; the text and audio query rows are one plain softmax over every key, whose transpose is
+the same three products (``context_rows_backward``).  Audio tokens never enter the linear memory.
 """
 
 from __future__ import annotations
@@ -65,8 +70,14 @@ def merge_backward(q, o_s, o_l, gate_w, proj_w, dout, eps=orc.RMS_EPS):
     return dq, do_s, do_l, dgate, dproj
 
 
-def softmax_backward(q, k, v, text_k, text_v, T, N, C, anchors, do_s):
-    """Gradients of the softmax branch: (dq, dk, dv, dtext_k, dtext_v), float64."""
+def softmax_backward(q, k, v, text_k, text_v, T, N, C, anchors, do_s, audio_k=None, audio_v=None):
+    """Gradients of the video rows' softmax branch: (dq, dk, dv, dglobal_k, dglobal_v), float64.
+
+    The global keys are the text tokens followed, when given, by the audio tokens (as in
+    ``vdn_oracle.softmax_branch``); dglobal_k and dglobal_v are ordered the same way."""
+    if audio_k is not None:
+        text_k = np.concatenate([text_k, audio_k], axis=0)
+        text_v = np.concatenate([text_v, audio_v], axis=0)
     TN, H, d = q.shape
     tau = 1.0 / math.sqrt(d)
     n_text = text_k.shape[0]
@@ -97,6 +108,34 @@ def softmax_backward(q, k, v, text_k, text_v, T, N, C, anchors, do_s):
             dk[idx, h] += dkeys[n_text:]
             dv[idx, h] += dvals[n_text:]
     return dq, dk, dv, dtk, dtv
+
+
+def context_rows_backward(ctx_q, keys, vals, do_ctx):
+    """Gradients of the text and audio query rows: (dctx_q, dkeys, dvals), float64.
+
+    Each context row is one plain softmax over every key of the sequence ([GLN]), o = P V with
+    P = softmax(tau q K^T); its transpose is dS = P (dP - rowsum(P dP)) with dP = do V^T, and
+    dq = tau dS K, dK = tau dS^T q, dV = P^T do.  ``keys``, ``vals`` are [L, H, d] in the
+    sequence's order (text, audio, video)."""
+    n_ctx, H, d = ctx_q.shape
+    tau = 1.0 / math.sqrt(d)
+    dq = np.zeros((n_ctx, H, d))
+    dkeys = np.zeros(keys.shape)
+    dvals = np.zeros(vals.shape)
+    for h in range(H):
+        qh = np.asarray(ctx_q[:, h], np.float64)
+        kh = np.asarray(keys[:, h], np.float64)
+        vh = np.asarray(vals[:, h], np.float64)
+        s = tau * (qh @ kh.T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        do = np.asarray(do_ctx[:, h], np.float64)
+        dp = do @ vh.T
+        ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        dq[:, h] = tau * (ds @ kh)
+        dkeys[:, h] = tau * (ds.T @ qh)
+        dvals[:, h] = p.T @ do
+    return dq, dkeys, dvals
 
 
 def frame_stats_backward(kf, vf, bf, da, db, weight_scale=1.0):
@@ -195,24 +234,48 @@ def linear_backward(q, k, v, beta, text_k, text_v, T, N, C, anchors, do_l, alpha
     return dq, dk, dv, dbeta, dtk, dtv, dalpha
 
 
-def vdn_backward(inp: dict, dout, T, N, C, anchors=True):
+def vdn_backward(inp: dict, dout, T, N, C, anchors=True, dctx_out=None):
     """All input gradients of the layer for the output gradient ``dout`` [T*N, H, d] (float64).
 
     Returns a dict with q, k, v, beta, text_k, text_v, gate_w, proj_w and, when ``inp`` has a decay
-    gate, alpha."""
+    gate, alpha.  With audio tokens (``audio_k``, ``audio_v`` in ``inp``) it also holds audio_k and
+    audio_v.  ``dctx_out`` [n_text + n_audio, H, d] is the gradient of the text and audio query
+    rows' output (``vdn_oracle.context_rows`` of ``inp["ctx_q"]``); when given, their transpose is
+    added and the dict also holds ctx_q."""
     q, k, v = inp["q"], inp["k"], inp["v"]
     tk, tv, beta = inp["text_k"], inp["text_v"], inp["beta"]
     alpha = inp.get("alpha")
-    o_s = orc.softmax_branch(q, k, v, tk, tv, T, N, C, anchors, dtype=np.float64)
+    n_text = tk.shape[0]
+    audio = {}
+    if inp.get("audio_k") is not None:
+        audio = dict(audio_k=inp["audio_k"], audio_v=inp["audio_v"])
+    o_s = orc.softmax_branch(q, k, v, tk, tv, T, N, C, anchors, dtype=np.float64, **audio)
     o_l = orc.linear_branch(q, k, v, beta, tk, tv, T, N, C, anchors, alpha=alpha)
     dq_m, do_s, do_l, dgate, dproj = merge_backward(q, o_s, o_l, inp["gate_w"], inp["proj_w"], dout)
-    dq_s, dk_s, dv_s, dtk_s, dtv_s = softmax_backward(q, k, v, tk, tv, T, N, C, anchors, do_s)
+    dq_s, dk_s, dv_s, dgk_s, dgv_s = softmax_backward(q, k, v, tk, tv, T, N, C, anchors, do_s, **audio)
     dq_l, dk_l, dv_l, dbeta, dtk_l, dtv_l, dalpha = linear_backward(q, k, v, beta, tk, tv, T, N, C, anchors,
                                                                    do_l, alpha)
-    grads = dict(q=dq_m + dq_s + dq_l, k=dk_s + dk_l, v=dv_s + dv_l, beta=dbeta, text_k=dtk_s + dtk_l,
-                 text_v=dtv_s + dtv_l, gate_w=dgate, proj_w=dproj)
+    grads = dict(q=dq_m + dq_s + dq_l, k=dk_s + dk_l, v=dv_s + dv_l, beta=dbeta, text_k=dgk_s[:n_text] + dtk_l,
+                 text_v=dgv_s[:n_text] + dtv_l, gate_w=dgate, proj_w=dproj)
+    if audio:
+        grads["audio_k"] = dgk_s[n_text:]
+        grads["audio_v"] = dgv_s[n_text:]
     if alpha is not None:
         grads["alpha"] = dalpha
+    if dctx_out is not None:
+        parts_k = [tk] + ([audio["audio_k"]] if audio else []) + [k]
+        parts_v = [tv] + ([audio["audio_v"]] if audio else []) + [v]
+        dcq, dka, dva = context_rows_backward(inp["ctx_q"], np.concatenate(parts_k), np.concatenate(parts_v),
+                                              dctx_out)
+        n_ctx = dcq.shape[0]
+        grads["ctx_q"] = dcq
+        grads["text_k"] = grads["text_k"] + dka[:n_text]
+        grads["text_v"] = grads["text_v"] + dva[:n_text]
+        if audio:
+            grads["audio_k"] = grads["audio_k"] + dka[n_text:n_ctx]
+            grads["audio_v"] = grads["audio_v"] + dva[n_text:n_ctx]
+        grads["k"] = grads["k"] + dka[n_ctx:]
+        grads["v"] = grads["v"] + dva[n_ctx:]
     return grads
 
 
@@ -222,6 +285,11 @@ def dq_rows(inp: dict, dout, T, N, C, anchors, rows):
     two states of its frame), so that it stays cheap at full size."""
     q, k, v = inp["q"], inp["k"], inp["v"]
     tk, tv, beta = inp["text_k"], inp["text_v"], inp["beta"]
+    if inp.get("audio_k") is not None:          # global softmax keys: text, then audio
+        gk = np.concatenate([tk, inp["audio_k"]])
+        gv = np.concatenate([tv, inp["audio_v"]])
+    else:
+        gk, gv = tk, tv
     TN, H, d = q.shape
     tau = 1.0 / math.sqrt(d)
     rows = np.asarray(rows)
@@ -232,8 +300,8 @@ def dq_rows(inp: dict, dout, T, N, C, anchors, rows):
             t = int(i) // N
             kf = orc.key_frames(t, T, C, anchors)
             idx = np.concatenate([np.arange(f * N, (f + 1) * N) for f in kf])
-            keys = np.concatenate([tk[:, h], k[idx, h]]).astype(np.float64)
-            vals = np.concatenate([tv[:, h], v[idx, h]]).astype(np.float64)
+            keys = np.concatenate([gk[:, h], k[idx, h]]).astype(np.float64)
+            vals = np.concatenate([gv[:, h], v[idx, h]]).astype(np.float64)
             qi = np.asarray(q[i, h], np.float64)
             s = tau * (keys @ qi)
             p = np.exp(s - s.max())

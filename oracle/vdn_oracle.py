@@ -303,8 +303,9 @@ def vdn_forward(inp: dict, T, N, C, anchors=True, rows=None, text_mode="half_bet
     return out
 
 
-def context_rows(inp: dict, T, N) -> np.ndarray:
-    """Text and audio query rows ``[n_text + n_audio, H, d]`` (float32).
+def context_rows(inp: dict, T, N, dtype=np.float32) -> np.ndarray:
+    """Text and audio query rows ``[n_text + n_audio, H, d]`` (in ``dtype``: fp32 by default, fp64
+    for derivative checks).
 
     [GLN]: interactions that involve a text or audio token keep the full softmax attention, so a
     text or audio query attends to every token of the sequence (text, audio and every video
@@ -315,11 +316,11 @@ def context_rows(inp: dict, T, N) -> np.ndarray:
     parts_k = [inp["text_k"]] + ([inp["audio_k"]] if inp.get("audio_k") is not None else []) + [inp["k"]]
     parts_v = [inp["text_v"]] + ([inp["audio_v"]] if inp.get("audio_v") is not None else []) + [inp["v"]]
     assert inp["k"].shape[0] == T * N
-    out = np.zeros(cq.shape, np.float32)
+    out = np.zeros(cq.shape, dtype)
     for h in range(H):
         keys = np.concatenate([p[:, h] for p in parts_k], axis=0)
         vals = np.concatenate([p[:, h] for p in parts_v], axis=0)
-        out[:, h] = softmax_rows(cq[:, h], keys, vals)
+        out[:, h] = softmax_rows(cq[:, h], keys, vals, dtype)
     return out
 
 

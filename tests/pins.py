@@ -671,14 +671,17 @@ def torch_layer_forward(x, T, N, C, anchors, eps=1e-6):
     alpha = x.get("alpha")
     TN, H, d = q.shape
     n_text = tk.shape[0]
+    # global softmax keys: the text and, when present, the audio tokens (never in the linear memory)
+    gk = torch.cat([tk, x["audio_k"]]) if x.get("audio_k") is not None else tk
+    gv = torch.cat([tv, x["audio_v"]]) if x.get("audio_v") is not None else tv
     bset = (0, T - 1) if anchors else ()
     tau = 1.0 / math.sqrt(d)
-    mask = torch.tensor(bruteforce.dense_mask(T, N, n_text, C, anchors))
+    mask = torch.tensor(bruteforce.dense_mask(T, N, gk.shape[0], C, anchors))
     eye = torch.eye(d, dtype=torch.float64)
     outs = []
     for h in range(H):
-        keys = torch.cat([tk[:, h], k[:, h]])
-        vals = torch.cat([tv[:, h], v[:, h]])
+        keys = torch.cat([gk[:, h], k[:, h]])
+        vals = torch.cat([gv[:, h], v[:, h]])
         s = (q[:, h] @ keys.T) * tau
         s = s.masked_fill(~mask, float("-inf"))
         o_s = torch.softmax(s, dim=1) @ vals
@@ -710,6 +713,20 @@ def torch_layer_forward(x, T, N, C, anchors, eps=1e-6):
         gl = torch.sigmoid(q[:, h] @ x["gate_w"][1])
         r = o_l / torch.sqrt(torch.mean(o_l * o_l, dim=1, keepdim=True) + eps)
         outs.append((gs * o_s) @ x["proj_w"][0] + (gl * r) @ x["proj_w"][1])
+    return torch.stack(outs, dim=1)
+
+
+def torch_context_rows(x):
+    """Dense float64 text and audio query rows in torch: one softmax over [text, audio, video]."""
+    import torch
+    parts_k = [x["text_k"]] + ([x["audio_k"]] if x.get("audio_k") is not None else []) + [x["k"]]
+    parts_v = [x["text_v"]] + ([x["audio_v"]] if x.get("audio_v") is not None else []) + [x["v"]]
+    keys, vals = torch.cat(parts_k), torch.cat(parts_v)
+    d = keys.shape[-1]
+    outs = []
+    for h in range(keys.shape[1]):
+        p = torch.softmax((x["ctx_q"][:, h] @ keys[:, h].T) / math.sqrt(d), dim=1)
+        outs.append(p @ vals[:, h])
     return torch.stack(outs, dim=1)
 
 
@@ -756,6 +773,72 @@ def pin_backward_finite_differences(bwd, seed=50):
         dout = _rng(seed + 200 + ci).standard_normal((T * N, H, d))
         got = bwd.vdn_backward(inp, dout, T, N, C, anchors)
         loss = lambda x: float(np.sum(dout * orc.vdn_forward(x, T, N, C, anchors, softmax_dtype=np.float64)))
+        rng = _rng(seed + 300 + ci)
+        for name in got:
+            delta = rng.standard_normal(inp[name].shape)
+            eps = 1e-5
+            plus = dict(inp)
+            minus = dict(inp)
+            plus[name] = inp[name] + eps * delta
+            minus[name] = inp[name] - eps * delta
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            an = float(np.sum(got[name] * delta))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (ci, name, fd, an)
+
+
+JOINT_BWD_CASES = [
+    # T, N, C, n_text, n_audio, H, d, anchors, decay
+    (7, 3, 2, 2, 3, 2, 4, True, False),
+    (6, 2, 1, 0, 2, 1, 5, False, False),
+    (9, 2, 2, 1, 1, 1, 4, True, True),
+    (5, 3, 5, 2, 0, 1, 4, True, False),
+]
+
+
+def _joint_bwd_inputs(T, N, n_text, n_audio, H, d, decay, seed):
+    inp = {key: val.astype(np.float64) for key, val in joint_inputs(T, N, n_text, n_audio, H, d, seed).items()}
+    if n_audio == 0:
+        del inp["audio_k"], inp["audio_v"]
+    if decay:
+        inp["alpha"] = 0.5 + 0.5 * _rng(seed + 7).random((T, H, d))
+    return inp
+
+
+def pin_joint_backward_autograd(bwd, seed=70):
+    """With audio keys and the text/audio query rows, the reverse-mode oracle equals torch autograd
+    of <dout, out> + <dctx_out, ctx_out> through the dense joint forward."""
+    import torch
+    for ci, (T, N, C, n_text, n_audio, H, d, anchors, decay) in enumerate(JOINT_BWD_CASES):
+        inp = _joint_bwd_inputs(T, N, n_text, n_audio, H, d, decay, seed + ci)
+        dout = _rng(seed + 100 + ci).standard_normal((T * N, H, d))
+        dctx = _rng(seed + 150 + ci).standard_normal((n_text + n_audio, H, d))
+        x = {key: torch.tensor(val, requires_grad=True) for key, val in inp.items()}
+        loss = torch.sum(torch_layer_forward(x, T, N, C, anchors) * torch.tensor(dout)) + \
+            torch.sum(torch_context_rows(x) * torch.tensor(dctx))
+        names = list(x)
+        auto = dict(zip(names, torch.autograd.grad(loss, [x[n] for n in names])))
+        got = bwd.vdn_backward(inp, dout, T, N, C, anchors, dctx_out=dctx)
+        assert set(got) == set(names), (ci, sorted(got), sorted(names))
+        for name in names:
+            ref = auto[name].numpy()
+            scale = max(1.0, float(np.abs(ref).max())) if ref.size else 1.0
+            assert np.allclose(got[name], ref, rtol=1e-8, atol=1e-9 * scale), (ci, name, np.abs(got[name] - ref).max())
+
+
+def pin_joint_backward_finite_differences(bwd, seed=80):
+    """Directional derivatives of <dout, out> + <dctx_out, ctx_out> by central differences of the
+    numpy forward oracle (float64 softmax, float64 context rows) equal <gradient, direction> for
+    every input of a joint sequence, one random direction each."""
+    from oracle import vdn_oracle as orc
+    for ci, (T, N, C, n_text, n_audio, H, d, anchors, decay) in enumerate(JOINT_BWD_CASES[:2]):
+        inp = _joint_bwd_inputs(T, N, n_text, n_audio, H, d, decay, seed + ci)
+        dout = _rng(seed + 200 + ci).standard_normal((T * N, H, d))
+        dctx = _rng(seed + 250 + ci).standard_normal((n_text + n_audio, H, d))
+        got = bwd.vdn_backward(inp, dout, T, N, C, anchors, dctx_out=dctx)
+
+        def loss(x):
+            out = orc.vdn_forward(x, T, N, C, anchors, softmax_dtype=np.float64)
+            return float(np.sum(dout * out) + np.sum(dctx * orc.context_rows(x, T, N, dtype=np.float64)))
         rng = _rng(seed + 300 + ci)
         for name in got:
             delta = rng.standard_normal(inp[name].shape)

@@ -6,13 +6,15 @@ import pins
 from oracle import vdn_backward as bwd
 
 
-@pytest.mark.parametrize("pin", [pins.pin_backward_autograd, pins.pin_backward_finite_differences],
+@pytest.mark.parametrize("pin", [pins.pin_backward_autograd, pins.pin_backward_finite_differences,
+                                 pins.pin_joint_backward_autograd, pins.pin_joint_backward_finite_differences],
                          ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(bwd)
 
 
 import importlib.util
+import math
 import os
 
 import numpy as np
@@ -85,7 +87,53 @@ def m_rms_no_projection(b):
     b.merge_backward = merge_backward
 
 
+def m_context_rows_no_rowsum(b):
+    """The context rows' softmax Jacobian without its rowsum(P dP) term."""
+    import math
+
+    def context_rows_backward(ctx_q, keys, vals, do_ctx):
+        n_ctx, H, d = ctx_q.shape
+        tau = 1.0 / math.sqrt(d)
+        dq = np.zeros((n_ctx, H, d)); dkeys = np.zeros(keys.shape); dvals = np.zeros(vals.shape)
+        for h in range(H):
+            s = tau * (ctx_q[:, h] @ keys[:, h].T)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            ds = p * (do_ctx[:, h] @ vals[:, h].T)
+            dq[:, h] = tau * (ds @ keys[:, h])
+            dkeys[:, h] = tau * (ds.T @ ctx_q[:, h])
+            dvals[:, h] = p.T @ do_ctx[:, h]
+        return dq, dkeys, dvals
+    b.context_rows_backward = context_rows_backward
+
+
+def m_context_key_grad_unscaled(b):
+    """The context rows' key gradient taken without the softmax scale tau."""
+    orig = b.context_rows_backward
+
+    def context_rows_backward(ctx_q, keys, vals, do_ctx):
+        dq, dkeys, dvals = orig(ctx_q, keys, vals, do_ctx)
+        return dq, dkeys * math.sqrt(ctx_q.shape[-1]), dvals
+    b.context_rows_backward = context_rows_backward
+
+
+def m_audio_keys_left_out(b):
+    """The video rows' softmax transpose run over the text keys only (audio keys forgotten)."""
+    orig = b.softmax_backward
+
+    def softmax_backward(q, k, v, text_k, text_v, T, N, C, anchors, do_s, audio_k=None, audio_v=None):
+        dq, dk, dv, dgk, dgv = orig(q, k, v, text_k, text_v, T, N, C, anchors, do_s)
+        if audio_k is not None:
+            dgk = np.concatenate([dgk, np.zeros(audio_k.shape)])
+            dgv = np.concatenate([dgv, np.zeros(audio_v.shape)])
+        return dq, dk, dv, dgk, dgv
+    b.softmax_backward = softmax_backward
+
+
 BWD_MUTANTS = [
+    (m_context_rows_no_rowsum, pins.pin_joint_backward_autograd),
+    (m_context_key_grad_unscaled, pins.pin_joint_backward_finite_differences),
+    (m_audio_keys_left_out, pins.pin_joint_backward_autograd),
     (m_softmax_no_rowsum, pins.pin_backward_autograd),
     (m_text_full_weight, pins.pin_backward_autograd),
     (m_gram_gradient_sign, pins.pin_backward_finite_differences),
