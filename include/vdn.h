@@ -177,24 +177,45 @@ vdn_status vdn_forward_joint(const vdn_plan *plan, const void *q, const void *k,
  * both frame scans with the text initialisation and, when alpha is given, the decay gate ("Video
  * Delta Attention: A Frame-Wise Solution").  Inputs as vdn_forward / vdn_forward_decay (alpha may
  * be NULL: no decay).  Outputs, all float32 device buffers owned by the caller and overwritten:
- * dq, dk, dv [T*N][H][d]; dbeta [n_text + T*N][H]; dtext_kv [2][n_text][H][d] (NULL iff
- * n_text == 0); dgate_w, dproj_w [2][d][d]; dalpha [T][H][d] or NULL (requires alpha).  The call
+ * dq, dk, dv [T*N][H][d]; dbeta [n_text + T*N][H]; dtext_kv [2][n_ctx][H][d] with n_ctx =
+ * n_text + n_audio (the gradient of text_kv, whose layout it shares; NULL iff n_ctx == 0);
+ * dgate_w, dproj_w [2][d][d]; dalpha [T][H][d] or NULL (requires alpha).  For a plan with audio
+ * tokens, text_kv holds the text and audio keys and values as in vdn_forward_joint, and the audio
+ * keys' gradients come from the video rows' softmax alone (they are not in the linear memory); the
+ * text and audio query rows are not part of this call (see vdn_backward_joint).  The call
  * recomputes the forward quantities it needs on `stream`.  The first call on a plan allocates a
  * backward workspace (about 6 T N H d float32 plus per-frame d x d matrices) that the plan keeps.
- * Plans with audio tokens are VDN_ERR_UNSUPPORTED; other errors as vdn_forward, plus
- * VDN_ERR_INVALID_ARG when an output aliases an input. */
+ * Errors as vdn_forward, plus VDN_ERR_INVALID_ARG when an output aliases an input. */
 vdn_status vdn_backward(vdn_plan *plan, const void *q, const void *k, const void *v,
                         const float *beta, const void *text_kv, const float *alpha,
                         const void *gate_w, const void *proj_w, const void *dout, float *dq,
                         float *dk, float *dv, float *dbeta, float *dtext_kv, float *dgate_w,
                         float *dproj_w, float *dalpha, void *stream);
 
+/* Backward pass of the whole joint sequence, the transpose of vdn_forward_joint: vdn_backward for
+ * the video rows plus, when ctx_q, dctx_out and dctx_q are all non-NULL, the text and audio query
+ * rows, each one plain softmax over every key of the sequence ("Video DeltaNet speeds MiniMax H3
+ * video generation 14.5x", summary), with output gradient dctx_out ([n_ctx][H][d], plan dtype):
+ * dctx_q ([n_ctx][H][d] float32) receives their query gradient and their key and value gradients
+ * are added to dk, dv and dctx_kv.  All three NULL leaves the context rows out (vdn_backward);
+ * one or two NULL is VDN_ERR_INVALID_ARG; with n_ctx = 0 they are ignored.  ctx_kv and dctx_kv are
+ * vdn_backward's text_kv and dtext_kv ([2][n_ctx][H][d]).  Ownership, alignment, aliasing and the
+ * other arguments and errors as vdn_backward; the context rows' output and normalisers are
+ * recomputed on `stream` with the rest. */
+vdn_status vdn_backward_joint(vdn_plan *plan, const void *q, const void *k, const void *v,
+                              const float *beta, const void *ctx_q, const void *ctx_kv,
+                              const float *alpha, const void *gate_w, const void *proj_w,
+                              const void *dout, const void *dctx_out, float *dq, float *dk,
+                              float *dv, float *dbeta, float *dctx_q, float *dctx_kv,
+                              float *dgate_w, float *dproj_w, float *dalpha, void *stream);
+
 /* As vdn_backward, reusing the intermediates the plan's most recent call left in its workspace
  * (linear-branch statistics and states, packed keys, the softmax output and its normalisers)
  * instead of recomputing them: for a training step that runs the forward and then the backward on
  * the same inputs.  Preconditions: the most recent call on this plan was vdn_forward,
- * vdn_forward_decay, vdn_forward_joint or vdn_backward with exactly these q, k, v, beta, text_kv,
- * alpha and weights, ordered before this call on the stream.  The library checks only that such a
+ * vdn_forward_decay, vdn_forward_joint, vdn_backward or vdn_backward_joint with exactly these q,
+ * k, v, beta, text_kv, alpha and weights, ordered before this call on the stream (the text and
+ * audio query rows are not part of this call).  The library checks only that such a
  * call succeeded and that alpha was given to both or to neither (else VDN_ERR_INVALID_ARG); other
  * mismatched inputs give wrong gradients.  Results are identical to vdn_backward's. */
 vdn_status vdn_backward_after_forward(vdn_plan *plan, const void *q, const void *k, const void *v,

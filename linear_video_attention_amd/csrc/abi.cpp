@@ -409,7 +409,8 @@ vdn_status ensure_backward(vdn_plan* p) {
     mslot[c] = mf;
     mslot[nslots + c] = mr;
   }
-  // query-frame ranges for each key slot (0 = text: every frame; 1 + f = frame f)
+  // query-frame ranges for each key slot (0 = the global text and audio keys: every frame; 1 + f =
+  // frame f); the context query rows, when a backward includes them, see every slot
   std::vector<int> qr((size_t)(T + 1) * 2 * vdn::kMaxRanges, 0), nqr(T + 1, 0);
   for (int slot = 0; slot <= T; ++slot) {
     int n = 0, start = -1;
@@ -455,25 +456,30 @@ vdn_status ensure_backward(vdn_plan* p) {
       seg_read.push_back({(int64_t)f0 * N, (f1 - f0) * N, h});
     }
   // dK/dV workgroups of the MFMA softmax backward: 128 keys of one slot each, the slots seen by
-  // every query frame (text, boundary frames) first
+  // every query frame (global keys, boundary frames) first
   std::vector<int2> kblocks;
   auto add_slot = [&](int slot) {
-    const int U = slot == 0 ? s.n_text : N;
+    const int U = slot == 0 ? s.n_ctx : N;
     for (int k0 = 0; k0 < U; k0 += 128) kblocks.push_back(make_int2(slot, k0));
   };
-  if (s.n_text > 0) add_slot(0);
+  if (s.n_ctx > 0) add_slot(0);
   for (int f = 0; f < T; ++f)
     if (vdn::is_boundary(s, f)) add_slot(1 + f);
   for (int f = 0; f < T; ++f)
     if (!vdn::is_boundary(s, f)) add_slot(1 + f);
   const bool mfma_bwd = p->kinds.softmax_mfma;
-  const int64_t Lq = (int64_t)T * N + 64;
+  // transposed query rows: the video rows, then the context rows from column T N, then a tile of
+  // zero padding for the last partial tile
+  const int64_t Lq = (int64_t)T * N + vdn::round_up(s.n_ctx, 64) + 64;
+  const size_t elt = s.dtype == VDN_BF16 ? 2 : 4;
+  const int64_t ctx_elems = (int64_t)s.n_ctx * H * d;
   const int splits_all = 512, splits_read = 8;
   // layout
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (size_t)vdn::round_up((int64_t)bytes, 256); return o; };
   const size_t o_rows6 = take((size_t)6 * rows * d * 4);
-  const size_t o_dsum = take((size_t)rows * 4);
+  const size_t o_dsum = take((size_t)(rows + (int64_t)s.n_ctx * H) * 4);
+  const size_t o_octx = take((size_t)ctx_elems * elt), o_doctx = take((size_t)ctx_elems * 4);
   const size_t o_part = take((size_t)std::max<int64_t>(splits_all, (int64_t)nslots * H * splits_read) * dd * 4);
   const size_t o_dread = take((size_t)nslots * H * dd * 4);
   const size_t o_z = take((size_t)3 * 2 * T * H * dd * 4);
@@ -515,6 +521,9 @@ vdn_status ensure_backward(vdn_plan* p) {
   w.dz_s = r6 + 4 * rows * d;
   w.dz_l = r6 + 5 * rows * d;
   w.dsum = reinterpret_cast<float*>(ws + o_dsum);
+  w.octx = ws + o_octx;
+  w.do_ctx = reinterpret_cast<float*>(ws + o_doctx);
+  w.dctx_out = nullptr;
   w.partial = reinterpret_cast<float*>(ws + o_part);
   w.dread = reinterpret_cast<float*>(ws + o_dread);
   float* z = reinterpret_cast<float*>(ws + o_z);
@@ -555,18 +564,24 @@ vdn_status ensure_backward(vdn_plan* p) {
 namespace {
 
 vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
-                         const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
-                         const void* dout, float* dq, float* dk, float* dv, float* dbeta, float* dtext_kv,
-                         float* dgate_w, float* dproj_w, float* dalpha, void* stream, bool recompute) {
+                         const void* text_kv, const void* ctx_q, const float* alpha, const void* gate_w,
+                         const void* proj_w, const void* dout, const void* dctx_out, float* dq, float* dk, float* dv,
+                         float* dbeta, float* dtext_kv, float* dctx_q, float* dgate_w, float* dproj_w, float* dalpha,
+                         void* stream, bool recompute) {
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !dout || !dq || !dk || !dv || !dbeta || !dgate_w ||
       !dproj_w)
     return VDN_ERR_INVALID_ARG;
-  if (plan->s.n_audio > 0 || plan->kinds.softmax_fp8 || plan->kinds.epilogue_mx) return VDN_ERR_UNSUPPORTED;
-  if (plan->s.n_text > 0 && (!text_kv || !dtext_kv)) return VDN_ERR_INVALID_ARG;
+  if (plan->kinds.softmax_fp8 || plan->kinds.epilogue_mx) return VDN_ERR_UNSUPPORTED;
+  if (plan->s.n_ctx > 0 && (!text_kv || !dtext_kv)) return VDN_ERR_INVALID_ARG;
   if (dalpha && !alpha) return VDN_ERR_INVALID_ARG;
+  // the context query rows: all three pointers or none; ignored without context tokens
+  const int nset = (ctx_q != nullptr) + (dctx_out != nullptr) + (dctx_q != nullptr);
+  if (nset != 0 && nset != 3) return VDN_ERR_INVALID_ARG;
+  if (plan->s.n_ctx == 0) ctx_q = dctx_out = dctx_q = nullptr;
+  const bool ctx_rows = ctx_q != nullptr;
   const void* ptrs[] = {q, k, v, beta, gate_w, proj_w, dout, dq, dk, dv, dbeta, dgate_w, dproj_w};
   for (const void* ptr : ptrs) if (!aligned16(ptr)) return VDN_ERR_INVALID_ARG;
-  const void* opt[] = {text_kv, dtext_kv, alpha, dalpha};
+  const void* opt[] = {text_kv, dtext_kv, alpha, dalpha, ctx_q, dctx_out, dctx_q};
   for (const void* ptr : opt) if (ptr && !aligned16(ptr)) return VDN_ERR_INVALID_ARG;
   {
     // every output's bytes are disjoint from every input's and from the other outputs'
@@ -574,14 +589,15 @@ vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const voi
     const size_t elt = s.dtype == VDN_BF16 ? 2 : 4;
     const size_t tokn = (size_t)s.T * s.N * s.H * s.d;
     const size_t brow = ((size_t)s.n_text + (size_t)s.T * s.N) * s.H;
-    const size_t tkv = (size_t)2 * s.n_text * s.H * s.d, dd2 = (size_t)2 * s.d * s.d;
+    const size_t ctx = (size_t)s.n_ctx * s.H * s.d, dd2 = (size_t)2 * s.d * s.d;
     const size_t al = (size_t)s.T * s.H * s.d;
     const vdn::Span outs[] = {{dq, tokn * 4}, {dk, tokn * 4}, {dv, tokn * 4}, {dbeta, brow * 4},
-                              {s.n_text > 0 ? dtext_kv : nullptr, tkv * 4}, {dgate_w, dd2 * 4},
-                              {dproj_w, dd2 * 4}, {dalpha, al * 4}};
+                              {s.n_ctx > 0 ? dtext_kv : nullptr, 2 * ctx * 4}, {dgate_w, dd2 * 4},
+                              {dproj_w, dd2 * 4}, {dalpha, al * 4}, {dctx_q, ctx * 4}};
     const vdn::Span ins[] = {{q, tokn * elt}, {k, tokn * elt}, {v, tokn * elt}, {beta, brow * 4},
-                             {s.n_text > 0 ? text_kv : nullptr, tkv * elt}, {alpha, al * 4},
-                             {gate_w, dd2 * elt}, {proj_w, dd2 * elt}, {dout, tokn * elt}};
+                             {s.n_ctx > 0 ? text_kv : nullptr, 2 * ctx * elt}, {alpha, al * 4},
+                             {gate_w, dd2 * elt}, {proj_w, dd2 * elt}, {dout, tokn * elt},
+                             {ctx_q, ctx * elt}, {dctx_out, ctx * elt}};
     for (const vdn::Span& o : outs) {
       for (const vdn::Span& i : ins)
         if (vdn::spans_overlap(o, i)) return VDN_ERR_INVALID_ARG;
@@ -598,15 +614,18 @@ vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const voi
 
   const vdn::Shape& s = plan->s;
   hipStream_t main = reinterpret_cast<hipStream_t>(stream);
-  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, nullptr, alpha, nullptr, nullptr};
-  vdn::Buffers b = buffers_of(plan);
   vdn::BwdBuffers w = plan->bw;
+  // the context rows' output is recomputed into the backward workspace
+  vdn::Inputs in{q, k, v, beta, text_kv, gate_w, proj_w, nullptr, alpha, ctx_q, ctx_rows ? w.octx : nullptr};
+  vdn::Buffers b = buffers_of(plan);
   w.dout = dout;
   w.lse = b.lse;
-  vdn::BwdOutputs o{dq, dk, dv, dbeta, dtext_kv, dgate_w, dproj_w, dalpha};
+  w.dctx_out = dctx_out;
+  vdn::BwdOutputs o{dq, dk, dv, dbeta, dtext_kv, dgate_w, dproj_w, dalpha, dctx_q};
 #define VDN_TRY(x) do { if ((x) != hipSuccess) { (void)hipGetLastError(); return VDN_ERR_HIP; } } while (0)
   if (recompute) {
-    // forward recomputation: linear-branch states, softmax output and its normalisers
+    // forward recomputation: linear-branch states, softmax output and its normalisers (with the
+    // context rows' output and normalisers when they are part of this backward)
     VDN_TRY(vdn::launch_vda_stats(s, in, b, plan->kinds.stats_mfma, main));
     VDN_TRY(vdn::launch_vda_scan(s, in, b, plan->kinds.scan_mfma, main));
     if (plan->kinds.softmax_mfma) {
@@ -629,8 +648,17 @@ vdn_status vdn_backward(vdn_plan* plan, const void* q, const void* k, const void
                         const void* text_kv, const float* alpha, const void* gate_w, const void* proj_w,
                         const void* dout, float* dq, float* dk, float* dv, float* dbeta, float* dtext_kv,
                         float* dgate_w, float* dproj_w, float* dalpha, void* stream) {
-  return backward_impl(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, dout, dq, dk, dv, dbeta, dtext_kv,
-                       dgate_w, dproj_w, dalpha, stream, true);
+  return backward_impl(plan, q, k, v, beta, text_kv, nullptr, alpha, gate_w, proj_w, dout, nullptr, dq, dk, dv, dbeta,
+                       dtext_kv, nullptr, dgate_w, dproj_w, dalpha, stream, true);
+}
+
+vdn_status vdn_backward_joint(vdn_plan* plan, const void* q, const void* k, const void* v, const float* beta,
+                              const void* ctx_q, const void* ctx_kv, const float* alpha, const void* gate_w,
+                              const void* proj_w, const void* dout, const void* dctx_out, float* dq, float* dk,
+                              float* dv, float* dbeta, float* dctx_q, float* dctx_kv, float* dgate_w, float* dproj_w,
+                              float* dalpha, void* stream) {
+  return backward_impl(plan, q, k, v, beta, ctx_kv, ctx_q, alpha, gate_w, proj_w, dout, dctx_out, dq, dk, dv, dbeta,
+                       dctx_kv, dctx_q, dgate_w, dproj_w, dalpha, stream, true);
 }
 
 vdn_status vdn_backward_after_forward(vdn_plan* plan, const void* q, const void* k, const void* v,
@@ -638,8 +666,8 @@ vdn_status vdn_backward_after_forward(vdn_plan* plan, const void* q, const void*
                                       const void* gate_w, const void* proj_w, const void* dout, float* dq,
                                       float* dk, float* dv, float* dbeta, float* dtext_kv, float* dgate_w,
                                       float* dproj_w, float* dalpha, void* stream) {
-  return backward_impl(plan, q, k, v, beta, text_kv, alpha, gate_w, proj_w, dout, dq, dk, dv, dbeta, dtext_kv,
-                       dgate_w, dproj_w, dalpha, stream, false);
+  return backward_impl(plan, q, k, v, beta, text_kv, nullptr, alpha, gate_w, proj_w, dout, nullptr, dq, dk, dv, dbeta,
+                       dtext_kv, nullptr, dgate_w, dproj_w, dalpha, stream, false);
 }
 
 vdn_status vdn_debug_buffer_bytes(const vdn_plan* plan, int which, size_t* bytes) {

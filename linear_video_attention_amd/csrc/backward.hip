@@ -647,8 +647,8 @@ template <typename Tin, int D>
 __global__ __launch_bounds__(kThreads) void token_grads_kernel(
     const Tin* __restrict__ k, const Tin* __restrict__ v, const float* __restrict__ beta,
     const Tin* __restrict__ text_kv, const float* __restrict__ gsym, const float* __restrict__ gdb, int T, int N,
-    int H, int n_text, int anchors, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
-    float* __restrict__ dtext_kv) {
+    int H, int n_text, int n_ctx, int anchors, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dbeta, float* __restrict__ dtext_kv) {
   constexpr int RR = kRows / 16, RC = D / 16;
   constexpr int64_t DD = (int64_t)D * D;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -662,9 +662,9 @@ __global__ __launch_bounds__(kThreads) void token_grads_kernel(
   const float wscale = slot == 0 ? 0.5f : 1.0f;
   const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
   const Tin* kb = slot == 0 ? text_kv : k;
-  const Tin* vb = slot == 0 ? text_kv + (int64_t)n_text * H * D : v;
+  const Tin* vb = slot == 0 ? text_kv + (int64_t)n_ctx * H * D : v;     // V half of [2][n_ctx][H][d]
   float* dkb = slot == 0 ? dtext_kv : dk;
-  float* dvb = slot == 0 ? dtext_kv + (int64_t)n_text * H * D : dv;
+  float* dvb = slot == 0 ? dtext_kv + (int64_t)n_ctx * H * D : dv;
   const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
   auto row_off = [&](int r) { return ((tok0 + u0 + r) * H + h) * D; };
   for (int e = tid; e < kRows * D; e += kThreads) {
@@ -709,17 +709,20 @@ __global__ __launch_bounds__(kThreads) void token_grads_kernel(
   }
 }
 
-// ---- 6. softmax dq: one thread per query row ----
+// ---- 6. softmax dq: one thread per query row.  Row group blockIdx.y holds nq rows (q, do_s, lse,
+// dsum, dq indexed [groups][nq][H](...)) and uses key-range row t0 + blockIdx.y: the video frames
+// (t0 = 0, nq = N) or the context rows (t0 = T, nq = n_ctx, one group).  Global keys: the n_ctx
+// context tokens at key index j < ctx_pad. ----
 template <typename Tin, int D>
 __global__ __launch_bounds__(64) void softmax_dq_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ text_kv,
     const float* __restrict__ do_s, const float* __restrict__ lse, const float* __restrict__ dsum,
-    const int* __restrict__ ranges, const int* __restrict__ nranges, int N, int H, int n_text, int text_pad,
+    const int* __restrict__ ranges, const int* __restrict__ nranges, int N, int t0, int H, int n_text, int text_pad,
     float tau, float* __restrict__ dq) {
-  const int t = blockIdx.y, h = blockIdx.z;
+  const int t = t0 + blockIdx.y, h = blockIdx.z;
   const int n = blockIdx.x * 64 + threadIdx.x;
   if (n >= N) return;
-  const int64_t row = ((int64_t)t * N + n) * H + h;
+  const int64_t row = ((int64_t)blockIdx.y * N + n) * H + h;
   float qr[D], dor[D], acc[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -765,9 +768,11 @@ __global__ __launch_bounds__(64) void softmax_dkv_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ text_kv,
     const float* __restrict__ do_s, const float* __restrict__ lse, const float* __restrict__ dsum,
     const int* __restrict__ qranges, const int* __restrict__ nqranges, int T, int N, int H, int n_text, float tau,
-    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtext_kv) {
-  // key index j: 0 .. n_text-1 text keys, then the video tokens; blockIdx.y = key frame slot
-  // (0 = text, 1 + f = frame f)
+    const Tin* __restrict__ cq, const float* __restrict__ cdo, int n_cq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dtext_kv) {
+  // key index j: 0 .. n_text-1 global (text, then audio) keys, then the video tokens; blockIdx.y =
+  // key frame slot (0 = global keys, 1 + f = frame f).  Every key is also seen by the n_cq context
+  // query rows cq (their do in cdo, lse and dsum after the T N video rows).
   const int slot = blockIdx.y, h = blockIdx.z;
   const int U = slot == 0 ? n_text : N;
   const int u = blockIdx.x * 64 + threadIdx.x;
@@ -807,6 +812,25 @@ __global__ __launch_bounds__(64) void softmax_dkv_kernel(
       }
     }
   }
+  for (int n = 0; n < n_cq; ++n) {
+    const int64_t crow = (int64_t)n * H + h;
+    const int64_t row = (int64_t)T * N * H + crow;
+    const Tin* qp = cq + crow * D;
+    const float* dp_ = cdo + crow * D;
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      s = fmaf(to_f32(qp[i]), kr[i], s);
+      dp = fmaf(dp_[i], vr[i], dp);
+    }
+    const float p = exp2f(s * c - lse[row]);
+    const float ds = p * (dp - dsum[row]) * tau;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      gv[i] = fmaf(p, dp_[i], gv[i]);
+      gk[i] = fmaf(ds, to_f32(qp[i]), gk[i]);
+    }
+  }
   float* dkp = slot == 0 ? dtext_kv + ((int64_t)u * H + h) * D : dk + (((int64_t)(slot - 1) * N + u) * H + h) * D;
   float* dvp = slot == 0 ? dtext_kv + (((int64_t)n_text + u) * H + h) * D
                          : dv + (((int64_t)(slot - 1) * N + u) * H + h) * D;
@@ -815,6 +839,22 @@ __global__ __launch_bounds__(64) void softmax_dkv_kernel(
     dkp[i] += gk[i];
     dvp[i] += gv[i];
   }
+}
+
+// Context query rows: do in fp32 and D = rowsum(do * o) of each row and head, stored after the T N
+// video rows' values.  One 64-thread group per (row, head).
+template <typename Tin, int D>
+__global__ __launch_bounds__(64) void ctx_rows_dsum_kernel(const Tin* __restrict__ dctx, const Tin* __restrict__ octx,
+                                                           float* __restrict__ do_ctx, float* __restrict__ dsum_ctx) {
+  const int64_t row = blockIdx.x;             // (context row) * H + head
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < D; i += 64) {
+    const float g = to_f32(dctx[row * D + i]);
+    do_ctx[row * D + i] = g;
+    acc = fmaf(g, to_f32(octx[row * D + i]), acc);
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (threadIdx.x == 0) dsum_ctx[row] = acc;
 }
 
 __global__ void sum2_kernel(const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ out,
@@ -844,7 +884,13 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   zero(o.dk, (int64_t)T * N * H * D);
   zero(o.dv, (int64_t)T * N * H * D);
   zero(o.dbeta, ((int64_t)s.n_text + (int64_t)T * N) * H);
-  zero(o.dtext_kv, (int64_t)2 * s.n_text * H * D);
+  zero(o.dtext_kv, (int64_t)2 * s.n_ctx * H * D);
+  const int n_cq = w.dctx_out ? s.n_ctx : 0;       // context query rows in this backward
+  if (n_cq > 0) {
+    zero(o.dctx_q, (int64_t)n_cq * H * D);
+    ctx_rows_dsum_kernel<Tin, D><<<dim3((unsigned)((int64_t)n_cq * H)), 64, 0, st>>>(
+        (const Tin*)w.dctx_out, (const Tin*)w.octx, w.do_ctx, w.dsum + (int64_t)T * N * H);
+  }
   if (o.dalpha) zero(w.dalf, (int64_t)2 * T * H * D);   // frames never written (boundary) keep zero
   // 1. merge backward (matrix cores for the plans whose softmax transpose runs on them)
   bool merged = false;
@@ -936,10 +982,16 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   } else {
   softmax_dq_kernel<Tin, D><<<dim3((N + 63) / 64, T, H), 64, 0, st>>>(
       (const Tin*)in.q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, w.do_s, w.lse, w.dsum, b.ranges,
-      b.nranges, N, H, s.n_text, s.ctx_pad, tau, o.dq);
-  softmax_dkv_kernel<Tin, D><<<dim3((max(N, s.n_text) + 63) / 64, T + 1, H), 64, 0, st>>>(
+      b.nranges, N, 0, H, s.n_ctx, s.ctx_pad, tau, o.dq);
+  if (n_cq > 0) {
+    const int64_t c0 = (int64_t)T * N * H;      // the context rows' lse and D follow the video rows'
+    softmax_dq_kernel<Tin, D><<<dim3((n_cq + 63) / 64, 1, H), 64, 0, st>>>(
+        (const Tin*)in.ctx_q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, w.do_ctx, w.lse + c0,
+        w.dsum + c0, b.ranges, b.nranges, n_cq, T, H, s.n_ctx, s.ctx_pad, tau, o.dctx_q);
+  }
+  softmax_dkv_kernel<Tin, D><<<dim3((max(N, s.n_ctx) + 63) / 64, T + 1, H), 64, 0, st>>>(
       (const Tin*)in.q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, w.do_s, w.lse, w.dsum,
-      w.qranges, w.nqranges, T, N, H, s.n_text, tau, o.dk, o.dv, o.dtext_kv);
+      w.qranges, w.nqranges, T, N, H, s.n_ctx, tau, (const Tin*)in.ctx_q, w.do_ctx, n_cq, o.dk, o.dv, o.dtext_kv);
   }
   {
     const size_t sm3 = (size_t)2 * D * (D + 1) * 4 + (size_t)16 * D * 4;
@@ -960,7 +1012,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
                                 (int)sm4);
       token_grads_kernel<Tin, D><<<dim3((max(N, s.n_text) + kRows - 1) / kRows, T + 1, H), kThreads, sm4, st>>>(
           (const Tin*)in.k, (const Tin*)in.v, in.beta, (const Tin*)in.text_kv, w.gsym, w.gdb, T, N, H, s.n_text,
-          s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
+          s.n_ctx, s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
     }
   }
   // dalpha: sum of both directions

@@ -7,13 +7,17 @@
 //   dS = P (dP - Dq) tau,  dP = do V^T,   dq = dS K,   dK = dS^T q,   dV = P^T do.
 // Two kernels, both on v_mfma_f32_16x16x32_bf16 with operand tiles staged in XOR-swizzled LDS by
 // global_load_lds (two stages):
-//   * softmax_dkv_mfma: one workgroup = 128 keys of one key slot (the text or one frame) and head,
-//     16 keys per wave; it walks every 64-query tile of the query frames that see the slot.  Keys
+//   * softmax_dkv_mfma: one workgroup = 128 keys of one key slot (the global text and audio keys,
+//     or one frame) and head, 16 keys per wave; it walks every 64-query tile of the query frames
+//     that see the slot, then the tiles of the text and audio query rows when the backward includes
+//     them (they see every key: "Video DeltaNet speeds MiniMax H3 video generation 14.5x",
+//     summary).  Keys
 //     stay in registers (K, V as B operands); per query tile it forms S = Q K^T and dP = dO V^T
 //     with the query rows permuted so that a lane's values of two 16-row tiles are 8 consecutive
 //     queries, which makes P and dS directly the B operands of dV^T += dO^T P and dK^T += Q^T dS
 //     (dO^T, Q^T tiles from transposed copies).
-//   * softmax_dq_mfma: one workgroup = 256 queries of one frame and head, 32 per wave, walking the
+//   * softmax_dq_mfma: one workgroup = 256 queries of one frame (or of the text and audio query
+//     rows, which walk every key and are dispatched first) and head, 32 per wave, walking the
 //     frame's key ranges like the forward; S^T = K Q^T and dP^T = V dO^T with the key rows
 //     permuted the same way, then dQ^T += K^T dS^T.
 #include "dev_common.h"
@@ -29,12 +33,6 @@ typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr int kWaves = 8;
-// VDN_DKV_WIDE 1: the dK/dV kernel with 4 waves x 32 keys (softmax_dkv_wide_kernel); 0 (default):
-// 8 waves x 16 keys, two waves per SIMD (2.5 % faster at 768p once both stage the tile's
-// normalisers in LDS and fold the offsets into the accumulators)
-#ifndef VDN_DKV_WIDE
-#define VDN_DKV_WIDE 0
-#endif
 constexpr int kVmcntZero = 0x0F70;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -78,13 +76,15 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t* __restrict
 // dK, dV
 // ---------------------------------------------------------------------------------------------
 struct DkvParams {
-  const bf16_t *q, *dout, *qt, *dot;    // q, do_s [TN][H][D]; their transposes [H][D][Lq]
-  const bf16_t *k, *v, *text_kv;        // [TN][H][D]; [2][n_text][H][D]
-  const float *lse, *dsum;              // [TN][H]
+  const bf16_t *q, *dout, *qt, *dot;    // q, do_s [TN][H][D]; their transposes [H][D][Lq] (context rows
+                                        // from column TN)
+  const bf16_t *cq, *cdout;             // context query rows and their do [n_cq][H][D] (n_cq > 0)
+  const bf16_t *k, *v, *text_kv;        // [TN][H][D]; [2][n_glob][H][D]
+  const float *lse, *dsum;              // [TN + n_cq][H]
   const int *qranges, *nqranges;        // per key slot: query-frame ranges
   const int2* blocks;                   // per workgroup: (key slot, first key of the slot)
   float *dk, *dv, *dtext;               // fp32 outputs (accumulated)
-  int T, N, H, n_text;
+  int T, N, H, n_glob, n_cq;            // n_glob global (text, audio) keys in slot 0; n_cq context rows
   int64_t Lq;
   float tau, c;
 };
@@ -103,14 +103,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   const int2 blk = P.blocks[blockIdx.x];
   const int slot = blk.x, h = blockIdx.y;
   const int N = P.N, H = P.H;
-  const int U = slot == 0 ? P.n_text : N;
+  const int U = slot == 0 ? P.n_glob : N;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int key = blk.y + 16 * wave + l16;                     // this lane's key within the slot
   const bool kvalid = key < U;
   const int kc = kvalid ? key : U - 1;
   const bf16_t* kbase = slot == 0 ? P.text_kv + ((int64_t)kc * H + h) * D
                                   : P.k + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
-  const bf16_t* vbase = slot == 0 ? P.text_kv + (((int64_t)P.n_text + kc) * H + h) * D
+  const bf16_t* vbase = slot == 0 ? P.text_kv + (((int64_t)P.n_glob + kc) * H + h) * D
                                   : P.v + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
   bf16x8 kf[KS], vf[KS];
 #pragma unroll
@@ -127,14 +127,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // query tiles: every 64-row tile of every frame in the slot's ranges
+  // query tiles: every 64-row tile of every frame in the slot's ranges, then the context rows
+  // (pseudo-frame T: they see every key)
   const int* qr = P.qranges + slot * 2 * kMaxRanges;
   const int nr = uniform(P.nqranges[slot]);
   const int tpf = (N + 63) / 64;
   int nfr = 0;
   for (int r = 0; r < nr; ++r) nfr += qr[2 * r + 1] - qr[2 * r];
-  const int ntiles = uniform(nfr * tpf);
+  const int nvt = uniform(nfr * tpf);
+  const int ntiles = uniform(nvt + (P.n_cq + 63) / 64);
   auto tile_at = [&](int it, int& t, int& q0) {
+    if (it >= nvt) {
+      t = P.T;
+      q0 = (it - nvt) * 64;
+      return;
+    }
     int fi = it / tpf;
     q0 = (it % tpf) * 64;
     t = 0;
@@ -150,15 +157,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   constexpr int T_INSTR = SM::ROW / 1024 / kWaves;           // per wave, per transposed tile
   auto issue_tile = [&](int t, int q0, int stage) {
     unsigned char* base = smem + stage * SM::STAGE;
+    const bool cx = t == P.T;                                  // the context rows
+    const int rows = cx ? P.n_cq : N;
+    const bf16_t* qsrc = cx ? P.cq : P.q + (int64_t)t * N * H * D;
+    const bf16_t* osrc = cx ? P.cdout : P.dout + (int64_t)t * N * H * D;
 #pragma unroll
     for (int i = 0; i < R_INSTR; ++i) {
       const int blkid = i * kWaves + wave;
       const int row = blkid * R_ROWS_PER_KB + lane / KCH;
       const int c = (lane % KCH) ^ r_swz(row);
-      const int qrow = min(q0 + row, N - 1);
-      const int64_t off = (((int64_t)t * N + qrow) * H + h) * D + c * 8;
-      __builtin_amdgcn_global_load_lds((gptr_t)(P.q + off), (lptr_t)(base + blkid * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr_t)(P.dout + off), (lptr_t)(base + SM::ROW + blkid * 1024), 16, 0, 0);
+      const int qrow = min(q0 + row, rows - 1);
+      const int64_t off = ((int64_t)qrow * H + h) * D + c * 8;
+      __builtin_amdgcn_global_load_lds((gptr_t)(qsrc + off), (lptr_t)(base + blkid * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(osrc + off), (lptr_t)(base + SM::ROW + blkid * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < T_INSTR; ++i) {
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
       __builtin_amdgcn_global_load_lds((gptr_t)(P.dot + off), (lptr_t)(base + 3 * SM::ROW + blkid * 1024), 16, 0, 0);
     }
     if (wave < 2) {                              // the tile's normalisers (wave 0) and D values (wave 1)
-      const int64_t rr = ((int64_t)t * N + min(q0 + lane, N - 1)) * H + h;
+      const int64_t rr = ((int64_t)t * N + min(q0 + lane, rows - 1)) * H + h;
       __builtin_amdgcn_global_load_lds((gptr_t)((wave == 0 ? P.lse : P.dsum) + rr),
                                        (lptr_t)(base + 4 * SM::ROW + wave * 256), 4, 0, 0);
     }
@@ -193,6 +204,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     }
     int t, q0;
     tile_at(it, t, q0);
+    const int rows = t == P.T ? P.n_cq : N;
     const unsigned char* qs = smem + (it & 1) * SM::STAGE;
     const unsigned char* os = qs + SM::ROW;
     const unsigned char* qts = qs + 2 * SM::ROW;
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
       for (int i = 0; i < 4; ++i) {
         const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
         float p = 0.f, ds = 0.f;
-        if (q0 + qi < N) {
+        if (q0 + qi < rows) {
           p = __builtin_amdgcn_exp2f(s[i]);
           ds = p * dp[i];                          // tau applied to dK at the end
         }
@@ -249,7 +261,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   // lane holds dV^T / dK^T rows d = 16 dt + 4 g + i of key l16
   if (kvalid) {
     float* dkp = slot == 0 ? P.dtext + ((int64_t)key * H + h) * D : P.dk + (((int64_t)(slot - 1) * N + key) * H + h) * D;
-    float* dvp = slot == 0 ? P.dtext + (((int64_t)P.n_text + key) * H + h) * D
+    float* dvp = slot == 0 ? P.dtext + (((int64_t)P.n_glob + key) * H + h) * D
                            : P.dv + (((int64_t)(slot - 1) * N + key) * H + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -261,246 +273,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   }
 }
 
-// Wide variant: 4 waves x 32 keys (two 16-key tiles per wave), one wave per SIMD.  Every Q, dO,
-// Q^T and dO^T fragment a wave reads from LDS feeds two MFMAs (one per key tile), which halves
-// the LDS reads per MFMA of the 16-key layout, and the tile's normalisers and D values come
-// through LDS with the tile instead of per-element global loads.
-constexpr int kDkvWaves = 4;
-// VDN_DKV_FOLD 1: keys enter as bf16(c k) and the score and dP accumulators start at -lse and -D
-#ifndef VDN_DKV_FOLD
-#define VDN_DKV_FOLD 1
-#endif
-#ifndef VDN_DKV_MINBLOCKS
-#define VDN_DKV_MINBLOCKS 1
-#endif
-
-template <int D>
-struct DkvWideSmem {
-  static constexpr int ROW = 64 * D * 2;
-  static constexpr int STAGE = 4 * ROW + 512;     // Q, dO, Q^T, dO^T, then lse[64], dsum[64]
-};
-
-template <int D>
-__global__ __launch_bounds__(kDkvWaves * 64, VDN_DKV_MINBLOCKS) void softmax_dkv_wide_kernel(DkvParams P) {
-  using SM = DkvWideSmem<D>;
-  constexpr int KS = D / 32, DT = D / 16, KCH = D / 8;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int2 blk = P.blocks[blockIdx.x];
-  const int slot = blk.x, h = blockIdx.y;
-  const int N = P.N, H = P.H;
-  const int U = slot == 0 ? P.n_text : N;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  bf16x8 kf[2][KS], vf[2][KS];
-  int keyk[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int key = blk.y + 32 * wave + 16 * kt + l16;        // this lane's key of tile kt
-    keyk[kt] = key;
-    const int kc = key < U ? key : U - 1;
-    const bf16_t* kbase = slot == 0 ? P.text_kv + ((int64_t)kc * H + h) * D
-                                    : P.k + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
-    const bf16_t* vbase = slot == 0 ? P.text_kv + (((int64_t)P.n_text + kc) * H + h) * D
-                                    : P.v + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
-      vf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
-#if VDN_DKV_FOLD
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[kt][ks][e] = (__bf16)((float)kf[kt][ks][e] * P.c);
-#endif
-    }
-  }
-  f32x4 dvt[2][DT], dkt[2][DT];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      dvt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dkt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-  const int* qr = P.qranges + slot * 2 * kMaxRanges;
-  const int nr = uniform(P.nqranges[slot]);
-  const int tpf = (N + 63) / 64;
-  int nfr = 0;
-  for (int r = 0; r < nr; ++r) nfr += qr[2 * r + 1] - qr[2 * r];
-  const int ntiles = uniform(nfr * tpf);
-  constexpr int R_ROWS_PER_KB = 1024 / (D * 2);
-  constexpr int R_INSTR = SM::ROW / 1024 / kDkvWaves;
-  constexpr int T_INSTR = SM::ROW / 1024 / kDkvWaves;
-
-  [[maybe_unused]] const float c = P.c;
-  const float tau = P.tau;
-  int t_next = 0, q_next = 0;
-#define VDN_DKV_TILE_AT(it_, t_, q0_)                                  \
-  {                                                                    \
-    int fi_ = (it_) / tpf;                                             \
-    q0_ = ((it_) % tpf) * 64;                                          \
-    t_ = 0;                                                            \
-    for (int r_ = 0; r_ < nr; ++r_) {                                  \
-      const int len_ = qr[2 * r_ + 1] - qr[2 * r_];                    \
-      if (fi_ < len_) { t_ = qr[2 * r_] + fi_; break; }                \
-      fi_ -= len_;                                                     \
-    }                                                                  \
-  }
-#define VDN_DKV_ISSUE(t_, q0_, stage_)                                                                      \
-  {                                                                                                         \
-    unsigned char* base_ = smem + (stage_) * SM::STAGE;                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < R_INSTR; ++i_) {                                                \
-      const int blkid_ = i_ * kDkvWaves + wave;                                                             \
-      const int row_ = blkid_ * R_ROWS_PER_KB + lane / KCH;                                                 \
-      const int c_ = (lane % KCH) ^ r_swz(row_);                                                            \
-      const int qrow_ = min((q0_) + row_, N - 1);                                                           \
-      const int64_t off_ = (((int64_t)(t_) * N + qrow_) * H + h) * D + c_ * 8;                              \
-      __builtin_amdgcn_global_load_lds((gptr_t)(P.q + off_), (lptr_t)(base_ + blkid_ * 1024), 16, 0, 0);   \
-      __builtin_amdgcn_global_load_lds((gptr_t)(P.dout + off_), (lptr_t)(base_ + SM::ROW + blkid_ * 1024), \
-                                       16, 0, 0);                                                           \
-    }                                                                                                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < T_INSTR; ++i_) {                                                \
-      const int blkid_ = i_ * kDkvWaves + wave;                                                             \
-      const int row_ = blkid_ * 8 + lane / 8;                                                               \
-      const int c_ = (lane % 8) ^ t_swz(row_);                                                              \
-      const int64_t off_ = ((int64_t)h * D + row_) * P.Lq + (int64_t)(t_) * N + (q0_) + c_ * 8;           \
-      __builtin_amdgcn_global_load_lds((gptr_t)(P.qt + off_), (lptr_t)(base_ + 2 * SM::ROW + blkid_ * 1024), \
-                                       16, 0, 0);                                                           \
-      __builtin_amdgcn_global_load_lds((gptr_t)(P.dot + off_), (lptr_t)(base_ + 3 * SM::ROW + blkid_ * 1024), \
-                                       16, 0, 0);                                                           \
-    }                                                                                                       \
-    if (wave < 2) {                                                                                         \
-      const int64_t rr_ = ((int64_t)(t_) * N + min((q0_) + lane, N - 1)) * H + h;                           \
-      __builtin_amdgcn_global_load_lds((gptr_t)((wave == 0 ? P.lse : P.dsum) + rr_),                        \
-                                       (lptr_t)(base_ + 4 * SM::ROW + wave * 256), 4, 0, 0);                \
-    }                                                                                                       \
-  }
-  if (ntiles > 0) {
-    VDN_DKV_TILE_AT(0, t_next, q_next)
-    VDN_DKV_ISSUE(t_next, q_next, 0)
-  }
-  for (int it = 0; it < ntiles; ++it) {
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
-    [[maybe_unused]] int t;
-    int q0;
-    VDN_DKV_TILE_AT(it, t, q0)
-    if (it + 1 < ntiles) {
-      VDN_DKV_TILE_AT(it + 1, t_next, q_next)
-      VDN_DKV_ISSUE(t_next, q_next, (it + 1) & 1)
-    }
-    const unsigned char* qs = smem + (it & 1) * SM::STAGE;
-    const unsigned char* os = qs + SM::ROW;
-    const unsigned char* qts = qs + 2 * SM::ROW;
-    const unsigned char* ots = qs + 3 * SM::ROW;
-    const float* lse_s = reinterpret_cast<const float*>(qs + 4 * SM::ROW);
-    const float* dsum_s = lse_s + 64;
-    bf16x8 pj[2][2], sj[2][2];                               // [key tile][32-query k-step]
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f32x4 sc[2], dp[2];
-#if VDN_DKV_FOLD
-      // accumulators start at -lse and -D of the lane's four query rows
-      f32x4 l0, d0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
-        l0[i] = -lse_s[qi];
-        d0[i] = -dsum_s[qi];
-      }
-#endif
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#if VDN_DKV_FOLD
-        sc[kt] = l0;
-        dp[kt] = d0;
-#else
-        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#endif
-      }
-      const int row = perm_row(u, l16);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = ks * 4 + g;
-        const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
-        const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + boff));
-        const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(os + boff));
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kt][ks], sc[kt], 0, 0, 0);
-          dp[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kt][ks], dp[kt], 0, 0, 0);
-        }
-      }
-      // lane holds rows 4 g + i of tile u = queries 32 (u/2) + 8 g + 4 (u%2) + i, key l16 of tile kt
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
-        const bool ok = q0 + qi < N;
-#if !VDN_DKV_FOLD
-        const float l = lse_s[qi], dd = dsum_s[qi];
-#endif
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#if VDN_DKV_FOLD
-          const float p = ok ? __builtin_amdgcn_exp2f(sc[kt][i]) : 0.f;
-          const float ds = p * dp[kt][i];                       // tau applied to dK at the end
-#else
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[kt][i], c, -l)) : 0.f;
-          const float ds = p * (dp[kt][i] - dd) * tau;
-#endif
-          pj[kt][u >> 1][4 * (u & 1) + i] = (__bf16)p;
-          sj[kt][u >> 1][4 * (u & 1) + i] = (__bf16)ds;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int trow = dt * 16 + l16;
-        const int ch = j * 4 + g;
-        const int boff = trow * 128 + ((ch ^ t_swz(trow)) * 16);
-        const bf16x8 ot = as_bf16x8(*reinterpret_cast<const u32x4*>(ots + boff));
-        const bf16x8 qtv = as_bf16x8(*reinterpret_cast<const u32x4*>(qts + boff));
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          dvt[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ot, pj[kt][j], dvt[kt][dt], 0, 0, 0);
-          dkt[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtv, sj[kt][j], dkt[kt][dt], 0, 0, 0);
-        }
-      }
-  }
-#undef VDN_DKV_TILE_AT
-#undef VDN_DKV_ISSUE
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int key = keyk[kt];
-    if (key >= U) continue;
-    float* dkp = slot == 0 ? P.dtext + ((int64_t)key * H + h) * D : P.dk + (((int64_t)(slot - 1) * N + key) * H + h) * D;
-    float* dvp = slot == 0 ? P.dtext + (((int64_t)P.n_text + key) * H + h) * D
-                           : P.dv + (((int64_t)(slot - 1) * N + key) * H + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
-      f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
-#if VDN_DKV_FOLD
-      *a = *a + dkt[kt][dt] * tau;
-#else
-      *a = *a + dkt[kt][dt];
-#endif
-      *b = *b + dvt[kt][dt];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------------------------
 struct DqParams {
   const bf16_t *q, *dout;               // q, do_s [TN][H][D]
+  const bf16_t *cq, *cdout;             // context query rows and their do [n_cq][H][D] (n_cq > 0)
   const bf16_t *kp, *vp, *kt;           // [H][Ls][D], [H][Ls][D], [H][D][Ls]
-  const float *lse, *dsum;
-  const int *ranges, *nranges;
-  float* dq;                            // fp32 [TN][H][D] (accumulated)
-  int T, N, H, QT;
+  const float *lse, *dsum;              // [TN + n_cq][H]
+  const int *ranges, *nranges;          // key ranges of each query frame; row T: the context rows
+  float *dq, *dcq;                      // fp32 [TN][H][D], [n_cq][H][D] (accumulated)
+  int T, N, H, QT, n_cq, QTc;           // QTc query tiles of the context rows (0 without them)
+  int ctx_split;                        // workgroups sharing one context query tile's key tiles
   int64_t Ls;
   float tau, c;
 };
@@ -533,9 +317,28 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
   using SM = DqSmem<D>;
   constexpr int KS = D / 32, DT = D / 16, KCH = D / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // workgroup -> (head, frame, query tile); the context rows (pseudo-frame T, every key: the
+  // longest workgroups, each query tile's key tiles split over ctx_split workgroups that add
+  // their parts atomically) come first
   const int w = blockIdx.x;
-  const int qt = w % P.QT, t = (w / P.QT) % P.T, h = w / (P.QT * P.T);
+  const int nctx_wg = P.QTc * P.H * P.ctx_split;
+  int qt, t, h, part = 0;
+  if (w < nctx_wg) {
+    qt = w % P.QTc;
+    part = (w / P.QTc) % P.ctx_split;
+    h = w / (P.QTc * P.ctx_split);
+    t = P.T;
+  } else {
+    const int wv = w - nctx_wg;
+    qt = wv % P.QT;
+    t = (wv / P.QT) % P.T;
+    h = wv / (P.QT * P.T);
+  }
+  const bool cx = t == P.T;
   const int N = P.N, H = P.H;
+  const int rows = cx ? P.n_cq : N;
+  const bf16_t* qsrc = cx ? P.cq : P.q + (int64_t)t * N * H * D;
+  const bf16_t* osrc = cx ? P.cdout : P.dout + (int64_t)t * N * H * D;
   const int64_t Ls = P.Ls;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int n_base = qt * kDqBQ + wave * 16 * kDqQT;
@@ -545,12 +348,14 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
 #pragma unroll
   for (int j = 0; j < kDqQT; ++j) {
     const int n = n_base + 16 * j + l16;
-    qv[j] = n < N;
-    const int64_t rr = ((int64_t)t * N + min(n, N - 1)) * H + h;
+    qv[j] = n < rows;
+    const int nc = min(n, rows - 1);
+    const int64_t rr = ((int64_t)t * N + nc) * H + h;      // lse, D: context rows after the video rows
+    const int64_t ro = ((int64_t)nc * H + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[j][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.q + rr * D + ks * 32 + g * 8));
-      of[j][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(P.dout + rr * D + ks * 32 + g * 8));
+      qf[j][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qsrc + ro + ks * 32 + g * 8));
+      of[j][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(osrc + ro + ks * 32 + g * 8));
 #if VDN_DQ_FOLD
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[j][ks][e] = (__bf16)((float)qf[j][ks][e] * P.c);
@@ -577,7 +382,9 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     nfull += rl[r] / 64;
     npart += (rl[r] % 64) != 0;
   }
-  const int ntiles = nfull + npart;
+  const int ntiles_all = nfull + npart;
+  const int it0 = cx ? ntiles_all * part / P.ctx_split : 0;
+  const int it1 = cx ? ntiles_all * (part + 1) / P.ctx_split : ntiles_all;
   auto tile_at = [&](int it, int& key0, int& valid) {
     if (it < nfull) {
       valid = 64;
@@ -627,22 +434,22 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
 
   [[maybe_unused]] const float c = P.c;
   const float tau = P.tau;
-  if (ntiles > 0) {
+  if (it1 > it0) {
     int key0, valid;
-    tile_at(0, key0, valid);
+    tile_at(it0, key0, valid);
     issue_tile(key0, 0);
   }
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = it0; it < it1; ++it) {
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
-    if (it + 1 < ntiles) {
+    if (it + 1 < it1) {
       int k1, v1;
       tile_at(it + 1, k1, v1);
-      issue_tile(k1, (it + 1) & 1);
+      issue_tile(k1, (it + 1 - it0) & 1);
     }
     int key0, valid;
     tile_at(it, key0, valid);
-    const unsigned char* ks_ = smem + (it & 1) * SM::STAGE;
+    const unsigned char* ks_ = smem + ((it - it0) & 1) * SM::STAGE;
     const unsigned char* vs_ = ks_ + SM::TILE;
     const unsigned char* ts_ = ks_ + 2 * SM::TILE;
 #pragma unroll
@@ -708,6 +515,15 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
 #pragma unroll
   for (int j = 0; j < kDqQT; ++j) {
     if (!qv[j]) continue;
+    if (cx) {                                   // parts of a context query tile: atomic adds
+      float* dqp = P.dcq + (((int64_t)n_base + 16 * j + l16) * H + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          atomicAdd(dqp + dt * 16 + g * 4 + i, VDN_DQ_FOLD ? dqt[dt][j][i] * tau : dqt[dt][j][i]);
+      continue;
+    }
     float* dqp = P.dq + (((int64_t)t * N + n_base + 16 * j + l16) * H + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -731,11 +547,18 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   // key-major [H][Ls][D]
   pack_t_kernel<<<dim3((int)((TN + 63) / 64), H, D / 64), 256, 0, st>>>((const bf16_t*)in.q, w.qt, TN, H, D, w.Lq, 0);
   pack_t_kernel<<<dim3((int)((TN + 63) / 64), H, D / 64), 256, 0, st>>>(w.dos16, w.dot, TN, H, D, w.Lq, 0);
-  if (s.n_text > 0) {
-    pack_t_kernel<<<dim3((s.n_text + 63) / 64, H, D / 64), 256, 0, st>>>((const bf16_t*)in.text_kv, w.kt, s.n_text, H,
-                                                                         D, s.Ls, 0);
-    pack_rows_kernel<<<dim3(s.n_text, H), 256, 0, st>>>((const bf16_t*)in.text_kv + (int64_t)s.n_text * H * D, w.vp,
-                                                        s.n_text, H, D, s.Ls, 0);
+  const int n_cq = w.dctx_out ? s.n_ctx : 0;       // context query rows: columns TN.. of the transposes
+  if (n_cq > 0) {
+    pack_t_kernel<<<dim3((n_cq + 63) / 64, H, D / 64), 256, 0, st>>>((const bf16_t*)in.ctx_q, w.qt, n_cq, H, D, w.Lq,
+                                                                     TN);
+    pack_t_kernel<<<dim3((n_cq + 63) / 64, H, D / 64), 256, 0, st>>>((const bf16_t*)w.dctx_out, w.dot, n_cq, H, D,
+                                                                     w.Lq, TN);
+  }
+  if (s.n_ctx > 0) {                               // the global (text, audio) keys
+    pack_t_kernel<<<dim3((s.n_ctx + 63) / 64, H, D / 64), 256, 0, st>>>((const bf16_t*)in.text_kv, w.kt, s.n_ctx, H,
+                                                                        D, s.Ls, 0);
+    pack_rows_kernel<<<dim3(s.n_ctx, H), 256, 0, st>>>((const bf16_t*)in.text_kv + (int64_t)s.n_ctx * H * D, w.vp,
+                                                       s.n_ctx, H, D, s.Ls, 0);
   }
   pack_t_kernel<<<dim3((int)((TN + 63) / 64), H, D / 64), 256, 0, st>>>((const bf16_t*)in.k, w.kt, TN, H, D, s.Ls,
                                                                        s.ctx_pad);
@@ -747,6 +570,8 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.dout = w.dos16;
     p.qt = w.qt;
     p.dot = w.dot;
+    p.cq = (const bf16_t*)in.ctx_q;
+    p.cdout = (const bf16_t*)w.dctx_out;
     p.k = (const bf16_t*)in.k;
     p.v = (const bf16_t*)in.v;
     p.text_kv = (const bf16_t*)in.text_kv;
@@ -761,27 +586,23 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.T = T;
     p.N = N;
     p.H = H;
-    p.n_text = s.n_text;
+    p.n_glob = s.n_ctx;
+    p.n_cq = n_cq;
     p.Lq = w.Lq;
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
-#if VDN_DKV_WIDE
-    const size_t sm = 2 * DkvWideSmem<D>::STAGE;
-    (void)hipFuncSetAttribute((const void*)softmax_dkv_wide_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sm);
-    hipLaunchKernelGGL(softmax_dkv_wide_kernel<D>, dim3(w.nkblocks, H), dim3(kDkvWaves * 64), sm, st, p);
-#else
     const size_t sm = 2 * DkvSmem<D>::STAGE;
     (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sm);
     hipLaunchKernelGGL(softmax_dkv_mfma_kernel<D>, dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
-#endif
   }
   // dQ
   {
     DqParams p{};
     p.q = (const bf16_t*)in.q;
     p.dout = w.dos16;
+    p.cq = (const bf16_t*)in.ctx_q;
+    p.cdout = (const bf16_t*)w.dctx_out;
     p.kp = b.kp;
     p.vp = w.vp;
     p.kt = w.kt;
@@ -790,17 +611,25 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.ranges = b.ranges;
     p.nranges = b.nranges;
     p.dq = o.dq;
+    p.dcq = o.dctx_q;
     p.T = T;
     p.N = N;
     p.H = H;
     p.QT = (N + kDqBQ - 1) / kDqBQ;
+    p.n_cq = n_cq;
+    p.QTc = (n_cq + kDqBQ - 1) / kDqBQ;
+    // split each context query tile's key tiles so that its workgroups take about as long as a
+    // frame's (whose key set is its window: ctx_pad + up to 3 C + 2 frames)
+    const int64_t ctx_keys = (int64_t)s.n_ctx + TN, frame_keys = (int64_t)s.ctx_pad + (int64_t)(3 * s.C + 2) * N;
+    p.ctx_split = n_cq > 0 ? (int)std::min<int64_t>(64, std::max<int64_t>(1, ctx_keys / frame_keys)) : 1;
     p.Ls = s.Ls;
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
     const size_t sm = 2 * DqSmem<D>::STAGE;
     (void)hipFuncSetAttribute((const void*)softmax_dq_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sm);
-    hipLaunchKernelGGL(softmax_dq_mfma_kernel<D>, dim3(p.QT * T * H), dim3(kDqWaves * 64), sm, st, p);
+    hipLaunchKernelGGL(softmax_dq_mfma_kernel<D>, dim3((p.QT * T + p.QTc * p.ctx_split) * H), dim3(kDqWaves * 64), sm,
+                       st, p);
   }
   return hipGetLastError();
 }

@@ -361,7 +361,7 @@ template <int D>
 __global__ __launch_bounds__(kWaves * 64) void token_grads_mfma_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ beta,
     const bf16_t* __restrict__ text_kv, const uint16_t* __restrict__ img, int T, int N, int H, int n_text,
-    int anchors, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
+    int n_ctx, int anchors, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
     float* __restrict__ dtext_kv) {
   constexpr int KS = D / 32, CT = D / 16;
   constexpr int64_t DD = (int64_t)D * D;
@@ -377,9 +377,9 @@ __global__ __launch_bounds__(kWaves * 64) void token_grads_mfma_kernel(
   const float wscale = slot == 0 ? 0.5f : 1.0f;
   const int64_t tok0 = slot == 0 ? 0 : (int64_t)(slot - 1) * N;
   const bf16_t* kb = slot == 0 ? text_kv : k;
-  const bf16_t* vb = slot == 0 ? text_kv + (int64_t)n_text * H * D : v;
+  const bf16_t* vb = slot == 0 ? text_kv + (int64_t)n_ctx * H * D : v;   // V half of [2][n_ctx][H][d]
   float* dkb = slot == 0 ? dtext_kv : dk;
-  float* dvb = slot == 0 ? dtext_kv + (int64_t)n_text * H * D : dv;
+  float* dvb = slot == 0 ? dtext_kv + (int64_t)n_ctx * H * D : dv;
   const int64_t brow0 = slot == 0 ? 0 : n_text + tok0;
   const int64_t off = ((tok0 + (ok ? u : 0)) * H + h) * D;
   const unsigned char* timg = reinterpret_cast<const unsigned char*>(img + (int64_t)kTokImages * ((int64_t)slot * H + h) * DD);
@@ -464,7 +464,7 @@ hipError_t launch_tok_t(const Shape& s, const Inputs& in, const BwdBuffers& w, c
   const int U = s.N > s.n_text ? s.N : s.n_text;
   token_grads_mfma_kernel<D><<<dim3((U + kTok - 1) / kTok, s.T + 1, s.H), kWaves * 64, sm, st>>>(
       (const bf16_t*)in.k, (const bf16_t*)in.v, in.beta, (const bf16_t*)in.text_kv, w.mimg, s.T, s.N, s.H, s.n_text,
-      s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
+      s.n_ctx, s.anchors, o.dk, o.dv, o.dbeta, o.dtext_kv);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ Layout make_layout(const Shape& s, const Kinds& k) {
   L.v8 = k.softmax_fp8 ? take((size_t)s.H * s.Ls8 * s.d) : 0;
   L.part8 = k.softmax_fp8 ? take((size_t)s.H * ((s.Lk + 63) / 64) * 3 * 4) : 0;
   L.scale8 = k.softmax_fp8 ? take((size_t)s.H * 2 * 4) : 0;
-  L.lse = k.softmax_fp8 ? 0 : take((size_t)s.T * s.N * s.H * 4);
+  L.lse = k.softmax_fp8 ? 0 : take(((size_t)s.T * s.N + s.n_ctx) * s.H * 4);
   L.ranges = take((size_t)(s.T + 1) * (2 * kMaxRanges + 1) * 4);
   L.total = off;
   return L;

@@ -53,6 +53,10 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 //   VDN_SOFTMAX_BK      keys per LDS tile (64; 128 halves the barriers but is 3 % slower)
 //   VDN_SOFTMAX_DOT2SUM 1: the normaliser from the bf16-rounded weights by v_dot2c_f32_bf16 instead
 //                       of fp32 adds (4 % slower: the sums wait for the conversions)
+//   VDN_SOFTMAX_MMASUM  1: the normaliser on the matrix cores, one more MFMA per query tile and
+//                       half with an all-ones A operand (sums the bf16-rounded weights); removes
+//                       27 of the ~70 vector instructions of a half but is 2 % slower at 768p
+//                       (6.80-6.82 against 6.64-6.71 ms): the matrix cores are the busier unit
 //   VDN_SOFTMAX_QT, VDN_SOFTMAX_WG_PER_CU: query tiles per wave and the occupancy hint (3 and
 //                       8 / waves; 4 waves x 4 or 5 tiles at one wave per SIMD, 404 / 492 registers,
 //                       measured 27-33 % slower: the lone wave cannot hide its own exponentials)
@@ -78,6 +82,9 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 #endif
 #ifndef VDN_SOFTMAX_PRESCALE
 #define VDN_SOFTMAX_PRESCALE 1
+#endif
+#ifndef VDN_SOFTMAX_MMASUM
+#define VDN_SOFTMAX_MMASUM 0
 #endif
 constexpr int kBK = VDN_SOFTMAX_BK;  // keys per tile (64 or 128)
 static_assert(kBK == 64 || kBK == 128, "key tile");
@@ -124,7 +131,7 @@ struct Params {
   const bf16_t* vt;
   bf16_t* o_s;
   bf16_t* oc;               // their output [n_ctx][H][D]
-  float* lse;               // video rows: log2 of the normaliser in scaled-score units, or nullptr
+  float* lse;               // [T*N + n_ctx][H]: log2 of each row's normaliser in scaled-score units, or nullptr
   const int* ranges;
   const int* nranges;
   const float* kmax;
@@ -319,6 +326,13 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
   float lsum[kQT];
 #pragma unroll
   for (int j = 0; j < kQT; ++j) lsum[j] = 0.f;
+#if VDN_SOFTMAX_MMASUM
+  f32x4 lacc[kQT];
+#pragma unroll
+  for (int j = 0; j < kQT; ++j) lacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+#endif
 
   // K row read by this lane for 16-key tile u of a half (see header): key 8 (l16 / 4) + 4 u + l16 % 4
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
@@ -395,6 +409,9 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
         const float alpha = exp2f(mref[j] - mnew);
         mref[j] = mnew;
         lsum[j] *= alpha;
+#if VDN_SOFTMAX_MMASUM
+        lacc[j] *= alpha;
+#endif
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt][j] *= alpha;
       }
@@ -413,7 +430,7 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
           // every query is >= 2^-96 (fixed reference) or 1 (online maximum)
           const float p = (!FALLBACK && VDN_SOFTMAX_PRESCALE) ? __builtin_amdgcn_exp2f(sacc[u][j][i])
                                                               : __builtin_amdgcn_exp2f(fmaf(sacc[u][j][i], c_log2, -mref[j]));
-#if !VDN_SOFTMAX_DOT2SUM
+#if !VDN_SOFTMAX_DOT2SUM && !VDN_SOFTMAX_MMASUM
           ls += p;
 #endif
           pf[j][4 * u + i] = (__bf16)p;
@@ -424,7 +441,9 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
 #pragma unroll
       for (int e = 0; e < 4; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[j][2 * e], pf[j][2 * e + 1]}, one2, ls, false);
 #endif
+#if !VDN_SOFTMAX_MMASUM
       lsum[j] += ls;
+#endif
     }
   };
   auto accumulate = [&](const unsigned char* vb, int half, const bf16x8 (&pf)[kQT]) {
@@ -440,10 +459,15 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
 #pragma unroll
       for (int j = 0; j < kQT; ++j)
         oacc[dt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[j], oacc[dt][j], 0, 0, 0);
+#if VDN_SOFTMAX_MMASUM
+    // every row of the product is the query's sum of the half's 32 rounded weights
+#pragma unroll
+    for (int j = 0; j < kQT; ++j) lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[j], lacc[j], 0, 0, 0);
+#endif
 #if VDN_SOFTMAX_SCHED
     __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);        // V fragment reads first,
     __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);       // then the probabilities (VALU),
-    __builtin_amdgcn_sched_group_barrier(0x008, DT * kQT, 0);  // then the P.V MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, (DT + VDN_SOFTMAX_MMASUM) * kQT, 0);  // then the MFMAs
 #endif
   };
 
@@ -491,11 +515,16 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
   // ---- normalise and store (bf16): lane holds d rows 16 dt + 4 g + i of query l16 of tile j ----
 #pragma unroll
   for (int j = 0; j < kQT; ++j) {
+#if VDN_SOFTMAX_MMASUM
+    const float tot = lacc[j][0];
+#else
     float tot = lsum[j] + __shfl_xor(lsum[j], 16);
     tot += __shfl_xor(tot, 32);
+#endif
     const float inv = 1.0f / tot;
     const int n = n_base + 16 * j + l16;
-    if (P.lse && !ctx && n < nrows && g == 0) P.lse[((int64_t)t * P.N + n) * H + h] = mref[j] + __log2f(tot);
+    // video rows at t N + n, context rows (t = T) after them
+    if (P.lse && n < nrows && g == 0) P.lse[((int64_t)t * P.N + n) * H + h] = mref[j] + __log2f(tot);
     if (n < nrows) {
       bf16_t* op = odst + (int64_t)n * H * D;
 #pragma unroll

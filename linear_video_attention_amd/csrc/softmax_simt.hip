@@ -80,7 +80,8 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   if (in.ctx_out)
     softmax_simt_kernel<Tin, D><<<dim3((s.n_ctx + 63) / 64, 1, s.H), 64, 0, st>>>(
         (const Tin*)in.ctx_q, (const Tin*)in.k, (const Tin*)in.v, (const Tin*)in.text_kv, (Tin*)in.ctx_out,
-        b.ranges, b.nranges, s.n_ctx, s.T, s.H, s.n_ctx, s.ctx_pad, scale_log2, nullptr);
+        b.ranges, b.nranges, s.n_ctx, s.T, s.H, s.n_ctx, s.ctx_pad, scale_log2,
+        b.lse ? b.lse + (int64_t)s.T * s.N * s.H : nullptr);   // context rows after the video rows
 }
 
 template <typename Tin>

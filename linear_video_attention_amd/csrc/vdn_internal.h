@@ -86,7 +86,8 @@ struct Layout {
   size_t v8;
   size_t part8;     // FP8 softmax: per 64-key block and head max |k|, max |v|, max key norm [H][Lk/64][3] f32
   size_t scale8;    // FP8 softmax: per head key and value scales [H][2] f32
-  size_t lse;       // base-2 log of each video row's softmax normaliser [T*N][H] f32 (not FP8 plans)
+  size_t lse;       // base-2 log of each softmax row's normaliser [T*N + n_ctx][H] f32, video rows then the
+                    // context rows (not FP8 plans)
   size_t ranges;    // int32 [T+1][2*kMaxRanges] + int32 [T+1] counts (row T: context query rows)
   size_t total;
 };
@@ -125,7 +126,8 @@ struct Buffers {
   uint8_t* v8;
   float* part8;
   float* scale8;
-  float* lse;          // [T*N][H] base-2 log of each video row's softmax normaliser, or nullptr
+  float* lse;          // [T*N + n_ctx][H] base-2 log of each row's softmax normaliser (video rows, then the
+                       // context rows when they are computed), or nullptr
 };
 
 struct Inputs {
@@ -173,7 +175,7 @@ struct Segment {
 struct BwdBuffers {
   const void* dout;                     // [T*N][H][d] plan dtype (the caller's)
   float *do_s, *do_l, *x_s, *x_l, *dz_s, *dz_l;   // [T*N][H][d] (do_s: generic kernels only)
-  float *dsum, *lse;                    // [T*N][H]
+  float *dsum, *lse;                    // [T*N + n_ctx][H]: video rows, then the context query rows
   float* partial;                       // [segments][splits][d][d]
   float* dread;                         // [Nc+2][H][d][d] readout adjoints (slots Nc, Nc+1: frames 0, T-1)
   float *zin, *dmf, *dbf;               // [2][T][H][d][d]
@@ -192,12 +194,17 @@ struct BwdBuffers {
                                         // later of the token gradients (6 per frame slot and head)
   uint16_t *qt, *dot;                   // [H][d][Lq] transposed q, do_s (bf16); pad columns zero
   uint16_t *kt, *vp;                    // [H][d][Ls] transposed keys, [H][Ls][d] key-major values
-  int64_t Lq;                           // T*N + 64
+  int64_t Lq;                           // T*N + round_up(n_ctx, 64) + 64 (context rows from column T*N)
   const int2* kblocks;                  // dK/dV workgroups: (key slot, first key)
   int nkblocks;
+  // text and audio query rows (the joint backward with context rows)
+  const void* dctx_out;                 // [n_ctx][H][d] plan dtype (the caller's), or nullptr: no context rows
+  void* octx;                           // [n_ctx][H][d] plan dtype: their recomputed output
+  float* do_ctx;                        // [n_ctx][H][d] dctx_out in fp32 (generic kernels)
 };
 struct BwdOutputs {
   float *dq, *dk, *dv, *dbeta, *dtext_kv, *dgate_w, *dproj_w, *dalpha;
+  float* dctx_q;                        // [n_ctx][H][d] or nullptr (no context rows)
 };
 hipError_t launch_backward(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                            const BwdOutputs& o, bool mfma_softmax, hipStream_t st);

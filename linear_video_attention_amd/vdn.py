@@ -39,6 +39,7 @@ SIGNATURES = [
     ("vdn_forward_noalloc", _c_int, [_c_int] * 8 + [_vp] * 9),
     ("vdn_backward", _c_int, [_vp] * 19),
     ("vdn_backward_after_forward", _c_int, [_vp] * 19),
+    ("vdn_backward_joint", _c_int, [_vp] * 22),
     ("vdn_plan_destroy", None, [_vp]),
     ("vdn_status_str", ctypes.c_char_p, [_c_int]),
     ("vdn_plan_workspace_bytes", _c_size, [_vp]),
@@ -276,36 +277,53 @@ class Plan:
         return out
 
     def backward(self, q, k, v, beta, text_kv, gate_w, proj_w, dout, alpha=None, stream=None,
-                 after_forward=False):
+                 after_forward=False, ctx_q=None, dctx_out=None):
         """Input gradients of the layer for the output gradient ``dout``; returns a dict of float32
         device tensors (q, k, v, beta, text_kv, gate_w, proj_w and, with ``alpha``, alpha).
+        ``text_kv`` and its gradient hold the context tokens ([2, n_text + n_audio, H, d]).
         ``after_forward=True`` reuses the intermediates of the plan's most recent forward on the
-        same inputs (vdn_backward_after_forward) instead of recomputing them."""
+        same inputs (vdn_backward_after_forward) instead of recomputing them.  With ``ctx_q`` and
+        ``dctx_out`` ([n_ctx, H, d]) the text and audio query rows are included
+        (vdn_backward_joint) and the dict also holds their gradient ctx_q."""
         import torch
         TN, H, d = self.T * self.N, self.H, self.d
         dt = self.torch_dtype
         for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
             self._expect(name, x, (TN, H, d), dt)
         self._expect("beta", beta, (self.n_text + TN, H), torch.float32)
-        if self.n_text > 0:
-            self._expect("text_kv", text_kv, (2, self.n_text, H, d), dt)
+        if self.n_ctx > 0:
+            self._expect("text_kv", text_kv, (2, self.n_ctx, H, d), dt)
         self._expect("gate_w", gate_w, (2, d, d), dt)
         self._expect("proj_w", proj_w, (2, d, d), dt)
         if alpha is not None:
             self._expect("alpha", alpha, (self.T, H, d), torch.float32)
+        joint = ctx_q is not None or dctx_out is not None
+        if joint:
+            if after_forward:
+                raise ValueError("the context rows are recomputed: after_forward does not take them")
+            self._expect("ctx_q", ctx_q, (self.n_ctx, H, d), dt)
+            self._expect("dctx_out", dctx_out, (self.n_ctx, H, d), dt)
         f32 = dict(dtype=torch.float32, device=q.device)
         g = dict(q=torch.empty((TN, H, d), **f32), k=torch.empty((TN, H, d), **f32),
                  v=torch.empty((TN, H, d), **f32), beta=torch.empty((self.n_text + TN, H), **f32),
-                 text_kv=torch.empty((2, self.n_text, H, d), **f32) if self.n_text > 0 else None,
+                 text_kv=torch.empty((2, self.n_ctx, H, d), **f32) if self.n_ctx > 0 else None,
                  gate_w=torch.empty((2, d, d), **f32), proj_w=torch.empty((2, d, d), **f32),
-                 alpha=torch.empty((self.T, H, d), **f32) if alpha is not None else None)
+                 alpha=torch.empty((self.T, H, d), **f32) if alpha is not None else None,
+                 ctx_q=torch.empty((self.n_ctx, H, d), **f32) if joint and self.n_ctx > 0 else None)
         ptr = lambda x: None if x is None else x.data_ptr()
-        name = "vdn_backward_after_forward" if after_forward else "vdn_backward"
-        _check(getattr(lib(), name)(self.handle, ptr(q), ptr(k), ptr(v), ptr(beta),
-                                    ptr(text_kv if self.n_text > 0 else None), ptr(alpha), ptr(gate_w),
-                                    ptr(proj_w), ptr(dout), ptr(g["q"]), ptr(g["k"]), ptr(g["v"]),
-                                    ptr(g["beta"]), ptr(g["text_kv"]), ptr(g["gate_w"]), ptr(g["proj_w"]),
-                                    ptr(g["alpha"]), _stream_ptr(stream)), name)
+        tkv = text_kv if self.n_ctx > 0 else None
+        if joint:
+            _check(lib().vdn_backward_joint(self.handle, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(ctx_q), ptr(tkv),
+                                            ptr(alpha), ptr(gate_w), ptr(proj_w), ptr(dout), ptr(dctx_out),
+                                            ptr(g["q"]), ptr(g["k"]), ptr(g["v"]), ptr(g["beta"]), ptr(g["ctx_q"]),
+                                            ptr(g["text_kv"]), ptr(g["gate_w"]), ptr(g["proj_w"]), ptr(g["alpha"]),
+                                            _stream_ptr(stream)), "vdn_backward_joint")
+        else:
+            name = "vdn_backward_after_forward" if after_forward else "vdn_backward"
+            _check(getattr(lib(), name)(self.handle, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(tkv), ptr(alpha),
+                                        ptr(gate_w), ptr(proj_w), ptr(dout), ptr(g["q"]), ptr(g["k"]), ptr(g["v"]),
+                                        ptr(g["beta"]), ptr(g["text_kv"]), ptr(g["gate_w"]), ptr(g["proj_w"]),
+                                        ptr(g["alpha"]), _stream_ptr(stream)), name)
         return {key: val for key, val in g.items() if val is not None}
 
     def debug_buffer(self, which, stream=None):

@@ -117,6 +117,9 @@ def test_null_arguments_rejected(vdn):
     assert L.vdn_plan_create(4, 16, 2, 1, 1, 16, 1, 0, None) == -1
     assert L.vdn_forward(None, *([None] * 9)) == -1
     assert L.vdn_forward_decay(None, *([None] * 10)) == -1
+    assert L.vdn_backward(None, *([None] * 18)) == -1
+    assert L.vdn_backward_joint(None, *([None] * 21)) == -1
+    assert L.vdn_backward_after_forward(None, *([None] * 18)) == -1
     L.vdn_plan_destroy(None)                       # no-op
     assert L.vdn_plan_workspace_bytes(None) == 0
     assert L.vdn_profile_enable(None, 4) == -1
