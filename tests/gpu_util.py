@@ -125,3 +125,26 @@ def bf16_half_ulp(x):
     ax = np.abs(np.asarray(x, np.float64))
     e = np.floor(np.log2(np.maximum(ax, 1e-30)))
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def weight_grad_storage_error(inp: dict, dout, w) -> dict:
+    """The part of the softmax-half weight gradients (gate_w[0], proj_w[0]) that storing o_s in bf16
+    alone makes, as a fraction of each one's RMS: the oracle's merge backward with o_s rounded to
+    bf16 against the same with o_s exact.  Both gradients sum x_s = sigmoid(q Wg0) * o_s over
+    every row, so where the attention is near uniform (rows of a frame with nearly the same o_s)
+    the storage roundings add up coherently."""
+    from oracle import vdn_backward as bwd
+    from oracle import vdn_oracle as orc
+    x = {k: np.asarray(v, np.float64) for k, v in inp.items() if v is not None}
+    audio = {}
+    if x.get("audio_k") is not None and x["audio_k"].shape[0] > 0:
+        audio = dict(audio_k=x["audio_k"], audio_v=x["audio_v"])
+    o_s = orc.softmax_branch(x["q"], x["k"], x["v"], x["text_k"], x["text_v"], w.T, w.N, w.C, w.anchors,
+                             dtype=np.float64, **audio)
+    o_l = orc.linear_branch(x["q"], x["k"], x["v"], x["beta"], x["text_k"], x["text_v"], w.T, w.N, w.C,
+                            w.anchors, alpha=x.get("alpha"))
+    stored = torch.from_numpy(o_s.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    dout = np.asarray(dout, np.float64)
+    _, _, _, dg, dp = bwd.merge_backward(x["q"], o_s, o_l, x["gate_w"], x["proj_w"], dout)
+    _, _, _, dg16, dp16 = bwd.merge_backward(x["q"], stored, o_l, x["gate_w"], x["proj_w"], dout)
+    return {"gate_w[0]": rel_err(dg16[0], dg[0]), "proj_w[0]": rel_err(dp16[0], dp[0])}

@@ -13,7 +13,7 @@ from oracle import vdn_backward as bwd
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import TOL, make_plan, rel_err, to_device  # noqa: E402
+from gpu_util import TOL, make_plan, rel_err, to_device, weight_grad_storage_error  # noqa: E402
 
 
 def _round(x, dtype):
@@ -65,10 +65,14 @@ def check_joint_backward(w, n_audio, ctx_rows=True, seed=0, decay=False, generic
             continue
         # an all-zero reference (no frame reaches the linear memory) is compared absolutely
         errs[name] = rel_err(got[name], r) if np.any(r) else float(np.abs(got[name]).max())
-    print("   " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+    # bf16 plans store o_s in bf16: the softmax-half weight gradients may differ by what that
+    # storage alone makes (computed by the oracle) on top of the bar
+    allow = weight_grad_storage_error(x, dout, w) if w.dtype == "bf16" else {}
+    print("   " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()) +
+          "   storage " + "  ".join(f"{k} {v:.1e}" for k, v in allow.items()), flush=True)
     assert set(ref) - {"audio_k", "audio_v"} <= set(got)
     for name, e in errs.items():
-        assert e <= TOL[w.dtype], (name, e)
+        assert e <= TOL[w.dtype] + allow.get(name, 0.0), (name, e)
 
 
 JOINT_BWD = [
@@ -120,7 +124,7 @@ def test_joint_backward_after_forward_matches():
 
 
 def test_joint_backward_argument_errors():
-    """Context-row pointers all or none; the FP8 plans' backward stays unsupported."""
+    """Context-row pointers all or none."""
     from linear_video_attention_amd import vdn
     w = synth.custom(3, 4, 16, 2, 1, 128, "bf16", "sigmoid", True)
     n_audio = 2
@@ -149,11 +153,6 @@ def test_joint_backward_argument_errors():
     assert call(None, None, None) == 0
     torch.cuda.synchronize()
     plan.close()
-    fp8 = vdn.Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, fp8=True, n_audio=n_audio)
-    with pytest.raises(vdn.VdnError) as ei:
-        fp8.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"], dout)
-    assert ei.value.status == -2
-    fp8.close()
 
 
 def test_joint_backward_768p_sampled():
