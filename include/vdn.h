@@ -110,8 +110,12 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
  * P8 = e4m3(2^(8 + x - m)) with the offset m = c |q| max|k| when that is <= 4, else the row's
  * exact maximum max x; o = sum P8 V8 / (s_v sum P8).  Inputs and outputs are unchanged (bf16); the linear branch and the merge are the
  * bf16 plan's.  Requires VDN_BF16, d = 128 and N a multiple of 16 (else VDN_ERR_UNSUPPORTED);
- * with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward rejects such plans
- * (VDN_ERR_UNSUPPORTED).
+ * with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward and vdn_backward_joint on
+ * such a plan return the gradient of the exact (bf16) layer at the same inputs: the roundings,
+ * whose derivative is zero almost everywhere, are passed straight through.  The plan computes it
+ * with a bf16 plan of the same shape that it creates at its first backward call and keeps (its
+ * workspace is not counted by vdn_plan_workspace_bytes); vdn_backward_after_forward rejects FP8
+ * plans (VDN_ERR_UNSUPPORTED), since their forward leaves none of the exact intermediates.
  *
  * VDN_FLAG_FP8_EPILOGUE computes the epilogue's four d x d products -- the two sigmoid gates
  * q Wg_m and the two output projections of "Gating the Softmax and Linear Branch Outputs" -- in
@@ -124,8 +128,8 @@ vdn_status vdn_plan_create(int T, int N, int C, int n_text, int H, int d, int an
  * accumulate in fp32.  The gated linear-branch output sigmoid(q Wg1) * o_l is quantised before
  * the RMSNorm factor is applied; the readout S q, the RMSNorm, the sigmoids and the gating stay
  * as in the bf16 plan.  Combines with VDN_FLAG_FP8_SOFTMAX.  Requires VDN_BF16 and d = 128 (else
- * VDN_ERR_UNSUPPORTED); with VDN_FLAG_GENERIC_KERNELS it is an argument error.  vdn_backward
- * rejects such plans (VDN_ERR_UNSUPPORTED). */
+ * VDN_ERR_UNSUPPORTED); with VDN_FLAG_GENERIC_KERNELS it is an argument error.  The backward of
+ * such plans is the exact layer's, as for VDN_FLAG_FP8_SOFTMAX. */
 enum { VDN_FLAG_GENERIC_KERNELS = 1, VDN_FLAG_SERIAL = 2, VDN_FLAG_OVERLAP = 4, VDN_FLAG_FP8_SOFTMAX = 8,
        VDN_FLAG_FP8_EPILOGUE = 16 };
 vdn_status vdn_plan_create_ex(int T, int N, int C, int n_text, int H, int d, int anchors,

@@ -199,6 +199,8 @@ struct vdn_plan {
   // backward workspace and tables, allocated by the first vdn_backward call
   char* bws = nullptr;
   vdn::BwdBuffers bw{};
+  // FP8 plans: the bf16 plan of the same shape whose backward theirs runs (created on first use)
+  vdn_plan* exact = nullptr;
 };
 
 namespace {
@@ -216,6 +218,7 @@ void free_plan(vdn_plan* p) {
   if (p->side) (void)hipStreamDestroy(p->side);
   if (p->ws) (void)hipFree(p->ws);
   if (p->bws) (void)hipFree(p->bws);
+  if (p->exact) free_plan(p->exact);
   delete p;
 }
 
@@ -571,7 +574,22 @@ vdn_status backward_impl(vdn_plan* plan, const void* q, const void* k, const voi
   if (!plan || !q || !k || !v || !beta || !gate_w || !proj_w || !dout || !dq || !dk || !dv || !dbeta || !dgate_w ||
       !dproj_w)
     return VDN_ERR_INVALID_ARG;
-  if (plan->kinds.softmax_fp8 || plan->kinds.epilogue_mx) return VDN_ERR_UNSUPPORTED;
+  if (plan->kinds.softmax_fp8 || plan->kinds.epilogue_mx) {
+    // FP8 plans: the gradient of the exact layer at the same inputs (their roundings are passed
+    // straight through), computed by a bf16 plan of the same shape; the FP8 forward leaves none of
+    // the exact intermediates the after-forward variant reuses
+    if (!recompute) return VDN_ERR_UNSUPPORTED;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return VDN_ERR_HIP;
+    if (cur != plan->device) return VDN_ERR_INVALID_ARG;
+    if (!plan->exact) {
+      const vdn::Shape& s = plan->s;
+      const vdn_status cs = vdn_plan_create_joint(s.T, s.N, s.C, s.n_text, s.n_audio, s.H, s.d, s.anchors, s.dtype,
+                                                  0, &plan->exact);
+      if (cs != VDN_OK) return cs;
+    }
+    plan = plan->exact;
+  }
   if (plan->s.n_ctx > 0 && (!text_kv || !dtext_kv)) return VDN_ERR_INVALID_ARG;
   if (dalpha && !alpha) return VDN_ERR_INVALID_ARG;
   // the context query rows: all three pointers or none; ignored without context tokens

@@ -231,14 +231,36 @@ def test_fp8_768p_sampled_rows():
     plan.close()
 
 
-def test_fp8_backward_unsupported():
+@pytest.mark.parametrize("kind", ["fp8_softmax", "fp8_epilogue", "both"])
+def test_fp8_backward_is_the_exact_layers(kind):
+    """The backward of an FP8 plan (straight through its roundings) is the bf16 plan's backward at
+    the same inputs, bit for bit (same kernels), for vdn_backward and, on a joint plan, for
+    vdn_backward_joint; vdn_backward_after_forward rejects FP8 plans (VDN_ERR_UNSUPPORTED)."""
     from linear_video_attention_amd import vdn
-    w = synth.custom(4, 3, 32, 2, 1, 128, "bf16", "sigmoid", True)
-    inp = synth.make_inputs(w)
+    w = synth.custom(4, 5, 32, 2, 1, 128, "bf16", "sigmoid", True)
+    n_audio = 3
+    inp = synth.make_inputs(w, seed=6, n_audio=n_audio, ctx_rows=True)
     dev = to_device(inp, w.dtype)
-    plan = fp8_plan(w)
+    rng = np.random.default_rng(8)
+    dout = torch.from_numpy(rng.standard_normal((w.T * w.N, w.H, w.d)).astype(np.float32)).cuda().to(torch.bfloat16)
+    dctx = torch.from_numpy(rng.standard_normal((w.n_text + n_audio, w.H, w.d)).astype(np.float32))
+    dctx = dctx.cuda().to(torch.bfloat16)
+    args = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"], dout)
+    exact = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, n_audio=n_audio)
+    ref = exact.backward(*args)
+    ref_j = exact.backward(*args, ctx_q=dev["ctx_q"], dctx_out=dctx)
+    plan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, n_audio=n_audio,
+                fp8=kind != "fp8_epilogue", fp8_epilogue=kind != "fp8_softmax")
+    plan.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"])
     with pytest.raises(vdn.VdnError) as ei:
-        plan.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
-                      torch.zeros_like(dev["q"]))
+        plan.backward(*args, after_forward=True)
     assert ei.value.status == -2
+    got = plan.backward(*args)
+    got_j = plan.backward(*args, ctx_q=dev["ctx_q"], dctx_out=dctx)
+    torch.cuda.synchronize()
+    for r, g in ((ref, got), (ref_j, got_j)):
+        assert set(r) == set(g)
+        for name in r:
+            assert torch.equal(r[name], g[name]), (kind, name)
     plan.close()
+    exact.close()
