@@ -458,12 +458,13 @@ vdn_status ensure_backward(vdn_plan* p) {
       }
       seg_read.push_back({(int64_t)f0 * N, (f1 - f0) * N, h});
     }
-  // dK/dV workgroups of the MFMA softmax backward: 128 keys of one slot each, the slots seen by
-  // every query frame (global keys, boundary frames) first
+  // dK/dV workgroups of the MFMA softmax backward: a block of keys of one slot each, the slots
+  // seen by every query frame (global keys, boundary frames) first
   std::vector<int2> kblocks;
+  const int bkeys = vdn::softmax_dkv_block_keys();
   auto add_slot = [&](int slot) {
     const int U = slot == 0 ? s.n_ctx : N;
-    for (int k0 = 0; k0 < U; k0 += 128) kblocks.push_back(make_int2(slot, k0));
+    for (int k0 = 0; k0 < U; k0 += bkeys) kblocks.push_back(make_int2(slot, k0));
   };
   if (s.n_ctx > 0) add_slot(0);
   for (int f = 0; f < T; ++f)

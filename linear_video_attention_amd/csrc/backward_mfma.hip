@@ -95,37 +95,51 @@ struct DkvSmem {
   static constexpr int STAGE = 4 * ROW + 512;     // Q, dO, Q^T, dO^T, then lse[64], dsum[64]
 };
 
+// KT 16-key tiles per wave (VDN_DKV_KT): with KT = 2 every Q, dO, Q^T and dO^T fragment a wave
+// reads from LDS feeds two MFMAs, halving the LDS reads per MFMA of KT = 1; P and dS are formed
+// and consumed one 32-query k-step at a time so that the accumulators of both key tiles, their K
+// and V fragments and the k-step's operands fit the 256 registers of two waves per SIMD.
+#ifndef VDN_DKV_KT
+#define VDN_DKV_KT 2
+#endif
+constexpr int kDkvKT = VDN_DKV_KT;
+constexpr int kDkvKeys = kWaves * 16 * kDkvKT;   // keys per workgroup
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvParams P) {
   using SM = DkvSmem<D>;
-  constexpr int KS = D / 32, DT = D / 16, KCH = D / 8;
+  constexpr int KS = D / 32, DT = D / 16, KCH = D / 8, KT = kDkvKT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int2 blk = P.blocks[blockIdx.x];
   const int slot = blk.x, h = blockIdx.y;
   const int N = P.N, H = P.H;
   const int U = slot == 0 ? P.n_glob : N;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int key = blk.y + 16 * wave + l16;                     // this lane's key within the slot
-  const bool kvalid = key < U;
-  const int kc = kvalid ? key : U - 1;
-  const bf16_t* kbase = slot == 0 ? P.text_kv + ((int64_t)kc * H + h) * D
-                                  : P.k + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
-  const bf16_t* vbase = slot == 0 ? P.text_kv + (((int64_t)P.n_glob + kc) * H + h) * D
-                                  : P.v + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 kf[KT][KS], vf[KT][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
-    vf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
+  for (int kt = 0; kt < KT; ++kt) {
+    const int key = blk.y + 16 * (KT * wave + kt) + l16;       // this lane's key of tile kt
+    const int kc = key < U ? key : U - 1;
+    const bf16_t* kbase = slot == 0 ? P.text_kv + ((int64_t)kc * H + h) * D
+                                    : P.k + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
+    const bf16_t* vbase = slot == 0 ? P.text_kv + (((int64_t)P.n_glob + kc) * H + h) * D
+                                    : P.v + (((int64_t)(slot - 1) * N + kc) * H + h) * D;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kf[ks][e] = (__bf16)((float)kf[ks][e] * P.c);   // scores in log2 units
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
+      vf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[kt][ks][e] = (__bf16)((float)kf[kt][ks][e] * P.c);   // scores in log2 units
+    }
   }
-  f32x4 dvt[DT], dkt[DT];
+  f32x4 dvt[KT][DT], dkt[KT][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dvt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dvt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dkt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   // query tiles: every 64-row tile of every frame in the slot's ranges, then the context rows
   // (pseudo-frame T: they see every key)
@@ -211,42 +225,50 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     const unsigned char* ots = qs + 3 * SM::ROW;
     const float* lse_s = reinterpret_cast<const float*>(qs + 4 * SM::ROW);
     const float* dsum_s = lse_s + 64;
-    bf16x8 pj[2], sj[2];                                     // P and dS of the two 32-query k-steps
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // accumulators start at -lse and -D of the lane's four query rows
-      f32x4 s, dp;
+    for (int j = 0; j < 2; ++j) {                            // 32-query k-steps
+      bf16x8 pj[KT], sj[KT];                                 // P and dS of this k-step, per key tile
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
-        s[i] = -lse_s[qi];
-        dp[i] = -dsum_s[qi];
-      }
-      const int row = perm_row(u, l16);
+      for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = 2 * j + u2;
+        // accumulators start at -lse and -D of the lane's four query rows
+        f32x4 s[KT], dp[KT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = ks * 4 + g;
-        const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
-        const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + boff));
-        const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(os + boff));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[ks], dp, 0, 0, 0);
-      }
-      // lane holds rows 4 g + i of tile u = queries 32 (u/2) + 8 g + 4 (u%2) + i, key l16
+        for (int i = 0; i < 4; ++i) {
+          const int qi = 32 * j + 8 * g + 4 * u2 + i;
+          const float l = -lse_s[qi], dd = -dsum_s[qi];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = 32 * (u >> 1) + 8 * g + 4 * (u & 1) + i;
-        float p = 0.f, ds = 0.f;
-        if (q0 + qi < rows) {
-          p = __builtin_amdgcn_exp2f(s[i]);
-          ds = p * dp[i];                          // tau applied to dK at the end
+          for (int kt = 0; kt < KT; ++kt) {
+            s[kt][i] = l;
+            dp[kt][i] = dd;
+          }
         }
-        pj[u >> 1][4 * (u & 1) + i] = (__bf16)p;
-        sj[u >> 1][4 * (u & 1) + i] = (__bf16)ds;
-      }
-    }
+        const int row = perm_row(u, l16);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = ks * 4 + g;
+          const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
+          const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + boff));
+          const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(os + boff));
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kt][ks], s[kt], 0, 0, 0);
+            dp[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kt][ks], dp[kt], 0, 0, 0);
+          }
+        }
+        // lane holds rows 4 g + i of tile u = queries 32 j + 8 g + 4 u2 + i, key l16 of tile kt
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = q0 + 32 * j + 8 * g + 4 * u2 + i < rows;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const float p = ok ? __builtin_amdgcn_exp2f(s[kt][i]) : 0.f;
+            const float ds = p * dp[kt][i];          // tau applied to dK at the end
+            pj[kt][4 * u2 + i] = (__bf16)p;
+            sj[kt][4 * u2 + i] = (__bf16)ds;
+          }
+        }
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int trow = dt * 16 + l16;
@@ -254,12 +276,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
         const int boff = trow * 128 + ((ch ^ t_swz(trow)) * 16);
         const bf16x8 ot = as_bf16x8(*reinterpret_cast<const u32x4*>(ots + boff));
         const bf16x8 qtv = as_bf16x8(*reinterpret_cast<const u32x4*>(qts + boff));
-        dvt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ot, pj[j], dvt[dt], 0, 0, 0);
-        dkt[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtv, sj[j], dkt[dt], 0, 0, 0);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          dvt[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ot, pj[kt], dvt[kt][dt], 0, 0, 0);
+          dkt[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtv, sj[kt], dkt[kt][dt], 0, 0, 0);
+        }
       }
+    }
   }
-  // lane holds dV^T / dK^T rows d = 16 dt + 4 g + i of key l16
-  if (kvalid) {
+  // lane holds dV^T / dK^T rows d = 16 dt + 4 g + i of key l16 of tile kt
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int key = blk.y + 16 * (KT * wave + kt) + l16;
+    if (key >= U) continue;
     float* dkp = slot == 0 ? P.dtext + ((int64_t)key * H + h) * D : P.dk + (((int64_t)(slot - 1) * N + key) * H + h) * D;
     float* dvp = slot == 0 ? P.dtext + (((int64_t)P.n_glob + key) * H + h) * D
                            : P.dv + (((int64_t)(slot - 1) * N + key) * H + h) * D;
@@ -267,8 +296,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     for (int dt = 0; dt < DT; ++dt) {
       f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
       f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
-      *a = *a + dkt[dt] * tau;
-      *b = *b + dvt[dt];
+      *a = *a + dkt[kt][dt] * tau;
+      *b = *b + dvt[kt][dt];
     }
   }
 }
@@ -635,6 +664,8 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
 }
 
 }  // namespace
+
+int softmax_dkv_block_keys() { return kDkvKeys; }
 
 hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                         const BwdOutputs& o, hipStream_t st) {

@@ -221,6 +221,8 @@ hipError_t launch_merge_bwd_mfma(const Shape& s, const Inputs& in, const Buffers
                                  const BwdOutputs& o, hipStream_t st);
 hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                         const BwdOutputs& o, hipStream_t st);
+// keys of one key slot that a workgroup of the MFMA dK/dV kernel covers (the host's block table)
+int softmax_dkv_block_keys();
 
 // Number of workgroups of the MFMA softmax launch.
 // with_ctx: including the workgroups of the context query rows.
