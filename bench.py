@@ -371,6 +371,37 @@ def main():
     del dout
     plan.close()
 
+    # the joint sequence (context): 576 audio tokens after the text (14.4 s at 40 audio latents per
+    # second) and the text and audio query rows; forward (vdn_forward_joint) and backward
+    # (vdn_backward_joint, which recomputes the forward), seeded extras of the same distributions
+    n_audio = 576
+    n_ctx = w.n_text + n_audio
+    jr = np.random.default_rng(1)
+    unit = lambda x: (x / np.linalg.norm(x.astype(np.float64), axis=-1, keepdims=True)).astype(np.float32)
+    audio_k = unit(jr.standard_normal((n_audio, w.H, w.d), dtype=np.float32))
+    audio_v = jr.standard_normal((n_audio, w.H, w.d), dtype=np.float32)
+    ctx_q = torch.from_numpy(unit(jr.standard_normal((n_ctx, w.H, w.d), dtype=np.float32))).to("cuda").to(tdt)
+    ctx_kv = torch.from_numpy(np.stack([np.concatenate([inp["text_k"], audio_k]),
+                                        np.concatenate([inp["text_v"], audio_v])])).to("cuda").to(tdt).contiguous()
+    dctx = torch.from_numpy(jr.standard_normal((n_ctx, w.H, w.d), dtype=np.float32)).to("cuda").to(tdt)
+    dout = torch.from_numpy(np.random.default_rng(7).standard_normal(out.shape, dtype=np.float32)).to("cuda").to(tdt)
+    jplan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, n_audio=n_audio)
+    ctx_out = torch.empty_like(ctx_q)
+    jfwd = lambda: jplan.forward(dev["q"], dev["k"], dev["v"], beta, ctx_kv, dev["gate_w"], dev["proj_w"], out,
+                                 ctx_q=ctx_q, ctx_out=ctx_out)
+    jbwd = lambda: jplan.backward(dev["q"], dev["k"], dev["v"], beta, ctx_kv, dev["gate_w"], dev["proj_w"], dout,
+                                  ctx_q=ctx_q, dctx_out=dctx)
+    jfwd()
+    jbwd()
+    torch.cuda.synchronize()
+    jf_med = float(np.median(timed_steps(jfwd, max(3, min(args.steps, 10)))))
+    jb_med = float(np.median(timed_steps(jbwd, n_bwd)))
+    joint_info = {"n_audio": n_audio, "context_query_rows": n_ctx, "forward_ms_median": jf_med,
+                  "forward_tokens_per_s": (tokens + n_ctx) / (jf_med * 1e-3),
+                  "backward_ms_median": jb_med, "backward_calls": n_bwd}
+    del dout, dctx, ctx_q, ctx_kv, ctx_out
+    jplan.close()
+
     # the FP8 (E4M3) softmax variant of the same layer (context: the headline value is bf16)
     fplan = Plan(w.T, w.N, w.C, w.n_text, w.H, w.d, w.anchors, w.dtype, fp8=True)
     for _ in range(2):
@@ -446,6 +477,7 @@ def main():
     decay["vda_frac_hbm"] = (vb + 4 * w.T * w.H * w.d) / (decay["vda_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
     result["decay_gate"] = decay
     result["backward"] = backward_info
+    result["joint"] = joint_info
     result["fp8_softmax"] = fp8_info
     result.update(mx_info)
     if overlapped is not None:
