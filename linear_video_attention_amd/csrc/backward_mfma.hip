@@ -105,7 +105,9 @@ struct DkvSmem {
 constexpr int kDkvKT = VDN_DKV_KT;
 constexpr int kDkvKeys = kWaves * 16 * kDkvKT;   // keys per workgroup
 
-template <int D>
+// CTX: whether the backward includes the context query rows (a compile-time switch, so the plain
+// path carries none of their selects)
+template <int D, bool CTX>
 __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvParams P) {
   using SM = DkvSmem<D>;
   constexpr int KS = D / 32, DT = D / 16, KCH = D / 8, KT = kDkvKT;
@@ -149,9 +151,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   int nfr = 0;
   for (int r = 0; r < nr; ++r) nfr += qr[2 * r + 1] - qr[2 * r];
   const int nvt = uniform(nfr * tpf);
-  const int ntiles = uniform(nvt + (P.n_cq + 63) / 64);
+  const int ntiles = CTX ? uniform(nvt + (P.n_cq + 63) / 64) : nvt;
   auto tile_at = [&](int it, int& t, int& q0) {
-    if (it >= nvt) {
+    if (CTX && it >= nvt) {
       t = P.T;
       q0 = (it - nvt) * 64;
       return;
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   constexpr int T_INSTR = SM::ROW / 1024 / kWaves;           // per wave, per transposed tile
   auto issue_tile = [&](int t, int q0, int stage) {
     unsigned char* base = smem + stage * SM::STAGE;
-    const bool cx = t == P.T;                                  // the context rows
+    const bool cx = CTX && t == P.T;                           // the context rows
     const int rows = cx ? P.n_cq : N;
     const bf16_t* qsrc = cx ? P.cq : P.q + (int64_t)t * N * H * D;
     const bf16_t* osrc = cx ? P.cdout : P.dout + (int64_t)t * N * H * D;
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     }
     int t, q0;
     tile_at(it, t, q0);
-    const int rows = t == P.T ? P.n_cq : N;
+    const int rows = (CTX && t == P.T) ? P.n_cq : N;
     const unsigned char* qs = smem + (it & 1) * SM::STAGE;
     const unsigned char* os = qs + SM::ROW;
     const unsigned char* qts = qs + 2 * SM::ROW;
@@ -341,29 +343,27 @@ constexpr int kDqWaves = VDN_DQ_WAVES;
 constexpr int kDqQT = VDN_DQ_QT;                  // 16-query column tiles per wave
 constexpr int kDqBQ = kDqWaves * 16 * kDqQT;      // queries per workgroup
 
-template <int D>
+// CTX = false: one workgroup per (head, frame, query tile) of the video rows.  CTX = true: the
+// context rows (pseudo-frame T, every key), each query tile's key tiles split over ctx_split
+// workgroups that add their parts atomically; a launch of their own, before the video rows'.
+template <int D, bool CTX>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqParams P) {
   using SM = DqSmem<D>;
   constexpr int KS = D / 32, DT = D / 16, KCH = D / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // workgroup -> (head, frame, query tile); the context rows (pseudo-frame T, every key: the
-  // longest workgroups, each query tile's key tiles split over ctx_split workgroups that add
-  // their parts atomically) come first
   const int w = blockIdx.x;
-  const int nctx_wg = P.QTc * P.H * P.ctx_split;
   int qt, t, h, part = 0;
-  if (w < nctx_wg) {
+  if constexpr (CTX) {
     qt = w % P.QTc;
     part = (w / P.QTc) % P.ctx_split;
     h = w / (P.QTc * P.ctx_split);
     t = P.T;
   } else {
-    const int wv = w - nctx_wg;
-    qt = wv % P.QT;
-    t = (wv / P.QT) % P.T;
-    h = wv / (P.QT * P.T);
+    qt = w % P.QT;
+    t = (w / P.QT) % P.T;
+    h = w / (P.QT * P.T);
   }
-  const bool cx = t == P.T;
+  constexpr bool cx = CTX;
   const int N = P.N, H = P.H;
   const int rows = cx ? P.n_cq : N;
   const bf16_t* qsrc = cx ? P.cq : P.q + (int64_t)t * N * H * D;
@@ -412,8 +412,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     npart += (rl[r] % 64) != 0;
   }
   const int ntiles_all = nfull + npart;
-  const int it0 = cx ? ntiles_all * part / P.ctx_split : 0;
-  const int it1 = cx ? ntiles_all * (part + 1) / P.ctx_split : ntiles_all;
+  const int it0 = CTX ? ntiles_all * part / P.ctx_split : 0;
+  const int it1 = CTX ? ntiles_all * (part + 1) / P.ctx_split : ntiles_all;
   auto tile_at = [&](int it, int& key0, int& valid) {
     if (it < nfull) {
       valid = 64;
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
 #pragma unroll
   for (int j = 0; j < kDqQT; ++j) {
     if (!qv[j]) continue;
-    if (cx) {                                   // parts of a context query tile: atomic adds
+    if constexpr (CTX) {                        // parts of a context query tile: atomic adds
       float* dqp = P.dcq + (((int64_t)n_base + 16 * j + l16) * H + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -621,9 +621,15 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
     const size_t sm = 2 * DkvSmem<D>::STAGE;
-    (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sm);
-    hipLaunchKernelGGL(softmax_dkv_mfma_kernel<D>, dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+    if (n_cq > 0) {
+      (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, true>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+    } else {
+      (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+    }
   }
   // dQ
   {
@@ -655,10 +661,15 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
     const size_t sm = 2 * DqSmem<D>::STAGE;
-    (void)hipFuncSetAttribute((const void*)softmax_dq_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (n_cq > 0) {                              // the context rows first: their walks are the longest
+      (void)hipFuncSetAttribute((const void*)softmax_dq_mfma_kernel<D, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+      hipLaunchKernelGGL((softmax_dq_mfma_kernel<D, true>), dim3(p.QTc * p.ctx_split * H), dim3(kDqWaves * 64), sm,
+                         st, p);
+    }
+    (void)hipFuncSetAttribute((const void*)softmax_dq_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sm);
-    hipLaunchKernelGGL(softmax_dq_mfma_kernel<D>, dim3((p.QT * T + p.QTc * p.ctx_split) * H), dim3(kDqWaves * 64), sm,
-                       st, p);
+    hipLaunchKernelGGL((softmax_dq_mfma_kernel<D, false>), dim3(p.QT * T * H), dim3(kDqWaves * 64), sm, st, p);
   }
   return hipGetLastError();
 }
