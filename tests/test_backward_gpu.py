@@ -121,6 +121,33 @@ def test_backward_768p_sampled_dq():
         assert err <= TOL[w.dtype], (name, err)
 
 
+def test_backward_long_sampled_dq():
+    """The long workload (180 frames of 1536 tokens, 5 heads) in the benchmark's launch
+    configuration: dq of sampled rows (every frame's first and last token plus two random tokens
+    per frame, all heads) against the row-wise oracle, and every gradient finite."""
+    w = synth.WORKLOADS["long"]
+    inp = synth.make_inputs(w, seed=0)
+    dout = np.random.default_rng(9).standard_normal((w.T * w.N, w.H, w.d)).astype(np.float32)
+    dout = torch.from_numpy(dout).to(torch.bfloat16).float().numpy()
+    plan = make_plan(w)
+    dev = to_device(inp, w.dtype)
+    print("long backward on the GPU ...", flush=True)
+    g = plan.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["text_kv"], dev["gate_w"], dev["proj_w"],
+                      torch.from_numpy(dout).cuda().to(torch.bfloat16))
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w)
+    got = g["q"][torch.from_numpy(rows).cuda()].cpu().numpy()
+    finite = all(bool(torch.isfinite(x).all()) for x in g.values())
+    del dev, g
+    plan.close()
+    print("long backward: oracle dq rows ...", flush=True)
+    ref = bwd.dq_rows(inp, dout.astype(np.float64), w.T, w.N, w.C, w.anchors, rows)
+    e = rel_err(got, ref)
+    print(f"long backward: dq of {len(rows)} sampled rows, err {e:.2e}", flush=True)
+    assert finite
+    assert e <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("decay", [False, True])
 def test_backward_after_forward_matches(decay):
     """vdn_backward_after_forward after a forward on the same inputs gives vdn_backward's gradients
