@@ -105,8 +105,9 @@ struct DkvSmem {
 constexpr int kDkvKT = VDN_DKV_KT;
 constexpr int kDkvKeys = kWaves * 16 * kDkvKT;   // keys per workgroup
 
-// CTX: whether the backward includes the context query rows (a compile-time switch, so the plain
-// path carries none of their selects)
+// CTX = false: the query tiles of the video frames that see the slot.  CTX = true: only the context
+// query rows' tiles (they see every slot), a second pass that adds to the first one's dK, dV (a
+// compile-time switch, so neither pass carries the other's selects)
 template <int D, bool CTX>
 __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvParams P) {
   using SM = DkvSmem<D>;
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   const int tpf = (N + 63) / 64;
   int nfr = 0;
   for (int r = 0; r < nr; ++r) nfr += qr[2 * r + 1] - qr[2 * r];
-  const int nvt = uniform(nfr * tpf);
-  const int ntiles = CTX ? uniform(nvt + (P.n_cq + 63) / 64) : nvt;
+  const int nvt = CTX ? 0 : uniform(nfr * tpf);
+  const int ntiles = CTX ? (P.n_cq + 63) / 64 : nvt;
   auto tile_at = [&](int it, int& t, int& q0) {
     if (CTX && it >= nvt) {
       t = P.T;
@@ -626,14 +627,13 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
     const size_t sm = 2 * DkvSmem<D>::STAGE;
-    if (n_cq > 0) {
+    (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+    if (n_cq > 0) {                              // then the context rows' part, added on the same stream
       (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
       hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, true>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
-    } else {
-      (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
     }
   }
   // dQ
