@@ -658,10 +658,15 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.QT = (N + kDqBQ - 1) / kDqBQ;
     p.n_cq = n_cq;
     p.QTc = (n_cq + kDqBQ - 1) / kDqBQ;
-    // split each context query tile's key tiles so that its workgroups take about as long as a
-    // frame's (whose key set is its window: ctx_pad + up to 3 C + 2 frames)
-    const int64_t ctx_keys = (int64_t)s.n_ctx + TN, frame_keys = (int64_t)s.ctx_pad + (int64_t)(3 * s.C + 2) * N;
-    p.ctx_split = n_cq > 0 ? (int)std::min<int64_t>(64, std::max<int64_t>(1, ctx_keys / frame_keys)) : 1;
+    // split each context query tile's key walk so that their own launch fills the GPU (two
+    // workgroups per compute unit), each part at least an eighth of a frame's key walk
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || cus <= 0)
+      cus = 256;
+    const int64_t ctx_tiles = ((int64_t)s.n_ctx + TN + 63) / 64, frame_tiles = (int64_t)(3 * s.C + 2) * N / 64 + 1;
+    const int64_t fill = (2 * (int64_t)cus + (int64_t)p.QTc * H - 1) / std::max<int64_t>(1, (int64_t)p.QTc * H);
+    p.ctx_split = n_cq > 0 ? (int)std::max<int64_t>(1, std::min<int64_t>({64, fill, ctx_tiles / frame_tiles * 8})) : 1;
     p.Ls = s.Ls;
     p.tau = tau;
     p.c = tau * 1.4426950408889634f;
