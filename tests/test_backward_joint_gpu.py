@@ -27,7 +27,37 @@ def split_context(got, n_text):
     got["audio_k"], got["audio_v"] = ckv[0][n_text:], ckv[1][n_text:]
 
 
-def check_joint_backward(w, n_audio, ctx_rows=True, seed=0, decay=False, generic=False):
+def split_weights(g):
+    """gate_w and proj_w as their two matrices each, compared one by one."""
+    for name in ("gate_w", "proj_w"):
+        for m in range(2):
+            g[f"{name}[{m}]"] = g[name][m]
+        del g[name]
+    return g
+
+
+def rounding_sensitivity(x, dout, dctx, w, ctx_rows, trials=2, seed=5):
+    """Largest relative change (max abs over the RMS) of every oracle gradient when every input is
+    perturbed by up to 2^-24 of itself (the rounding of an fp32 input), over ``trials`` random
+    perturbations: how much of an fp32 bar the problem's own conditioning already takes."""
+    ref = split_weights(bwd.vdn_backward(x, dout, w.T, w.N, w.C, w.anchors, dctx_out=dctx if ctx_rows else None))
+    rng = np.random.default_rng(seed)
+    out = {name: 0.0 for name in ref}
+    for _ in range(trials):
+        xp = {k: v * (1.0 + 2.0 ** -24 * rng.uniform(-1.0, 1.0, v.shape)) for k, v in x.items()}
+        g = split_weights(bwd.vdn_backward(xp, dout, w.T, w.N, w.C, w.anchors, dctx_out=dctx if ctx_rows else None))
+        for name, r in ref.items():
+            if r.size and np.any(r):
+                out[name] = max(out[name], rel_err(g[name], r))
+    return out
+
+
+def check_joint_backward(w, n_audio, ctx_rows=True, seed=0, decay=False, generic=False, conditioning=False):
+    """GPU gradients against the oracle's.  With ``conditioning`` (fp32 plans), each gradient may
+    also differ by sqrt(2 d) times its sensitivity to rounding the inputs to fp32
+    (``rounding_sensitivity``): fp32 sums of d terms gather rounding errors that grow like
+    sqrt(d) 2^-24 in the random-rounding model, and an ill-conditioned step (the RMSNorm of a
+    nearly empty linear memory's readout) amplifies them exactly as it amplifies input rounding."""
     inp = synth.make_inputs(w, seed=seed, decay=decay, n_audio=n_audio, ctx_rows=ctx_rows)
     n_ctx = w.n_text + n_audio
     rng = np.random.default_rng(seed + 99)
@@ -54,23 +84,27 @@ def check_joint_backward(w, n_audio, ctx_rows=True, seed=0, decay=False, generic
     ref = bwd.vdn_backward(x, dout.astype(np.float64), w.T, w.N, w.C, w.anchors,
                            dctx_out=dctx.astype(np.float64) if ctx_rows else None)
     # the two gates' and the two projections' weight gradients are compared matrix by matrix
-    for name in ("gate_w", "proj_w"):
-        for m in range(2):
-            ref[f"{name}[{m}]"] = ref[name][m]
-            got[f"{name}[{m}]"] = got[name][m]
-        del ref[name], got[name]
+    split_weights(ref)
+    split_weights(got)
     errs = {}
     for name, r in ref.items():
         if r.size == 0:
             continue
-        # an all-zero reference (no frame reaches the linear memory) is compared absolutely
-        errs[name] = rel_err(got[name], r) if np.any(r) else float(np.abs(got[name]).max())
+        # rows (tokens) whose reference gradient is exactly zero -- tokens that never reach the linear
+        # memory, or a whole gradient when nothing does -- must be zero on the GPU too; the others
+        # are held to the bar relative to their own RMS
+        live = np.abs(r.reshape(r.shape[0], -1)).max(axis=1) > 0
+        dead_err = float(np.abs(got[name][~live]).max()) if (~live).any() else 0.0
+        errs[name] = max(rel_err(got[name][live], r[live]) if live.any() else 0.0, dead_err)
     # bf16 plans store o_s in bf16: the softmax-half weight gradients may differ by what that
     # storage alone makes (computed by the oracle) on top of the bar
     allow = weight_grad_storage_error(x, dout, w) if w.dtype == "bf16" else {}
+    if conditioning and w.dtype == "fp32":
+        sens = rounding_sensitivity(x, dout.astype(np.float64), dctx.astype(np.float64), w, ctx_rows)
+        allow = {name: np.sqrt(2.0 * w.d) * v for name, v in sens.items()}
     print("   " + "  ".join(f"{k} {v:.1e}" for k, v in errs.items()) +
-          "   storage " + "  ".join(f"{k} {v:.1e}" for k, v in allow.items()), flush=True)
-    assert set(ref) - {"audio_k", "audio_v"} <= set(got)
+          "   allowance " + "  ".join(f"{k} {v:.1e}" for k, v in allow.items()), flush=True)
+    assert {n for n, r in ref.items() if r.size} - {"audio_k", "audio_v"} <= set(got)
     for name, e in errs.items():
         assert e <= TOL[w.dtype] + allow.get(name, 0.0), (name, e)
 
