@@ -471,6 +471,17 @@ vdn_status ensure_backward(vdn_plan* p) {
     if (vdn::is_boundary(s, f)) add_slot(1 + f);
   for (int f = 0; f < T; ++f)
     if (!vdn::is_boundary(s, f)) add_slot(1 + f);
+  // dQ workgroups: the query frames with the most keys (the boundary frames) first, so that their
+  // longer walks start with the launch instead of trailing it
+  std::vector<int> qframes(T);
+  std::vector<int64_t> nkeys(T, 0);
+  for (int t = 0; t < T; ++t) {
+    qframes[t] = t;
+    int64_t r[2 * vdn::kMaxRanges];
+    const int nr = vdn::key_ranges(s, t, r, vdn::kMaxRanges);
+    for (int i = 0; i < nr; ++i) nkeys[t] += r[2 * i + 1] - r[2 * i];
+  }
+  std::stable_sort(qframes.begin(), qframes.end(), [&](int a, int b) { return nkeys[a] > nkeys[b]; });
   const bool mfma_bwd = p->kinds.softmax_mfma;
   // transposed query rows: the video rows, then the context rows from column T N, then a tile of
   // zero padding for the last partial tile
@@ -494,6 +505,7 @@ vdn_status ensure_backward(vdn_plan* p) {
   const size_t o_qr = take(qr.size() * 4), o_nqr = take(nqr.size() * 4);
   const size_t o_sa = take(seg_all.size() * sizeof(vdn::Segment)), o_sr = take(seg_read.size() * sizeof(vdn::Segment));
   const size_t o_kb = take(std::max<size_t>(1, kblocks.size()) * sizeof(int2));
+  const size_t o_qf = take(qframes.size() * 4);
   // matrix images: the merge's, then (reusing the space) the token gradients'
   const size_t mimg_bytes = (size_t)std::max<int64_t>(6 + 4 * (int64_t)(s.Nc + 1) * H, 6 * (int64_t)(T + 1) * H) * dd * 2;
   const size_t pack_bytes =
@@ -511,7 +523,7 @@ vdn_status ensure_backward(vdn_plan* p) {
       !up(o_qr, qr.data(), qr.size() * 4) || !up(o_nqr, nqr.data(), nqr.size() * 4) ||
       !up(o_sa, seg_all.data(), seg_all.size() * sizeof(vdn::Segment)) ||
       !up(o_sr, seg_read.data(), seg_read.size() * sizeof(vdn::Segment)) ||
-      !up(o_kb, kblocks.data(), kblocks.size() * sizeof(int2)) ||
+      !up(o_kb, kblocks.data(), kblocks.size() * sizeof(int2)) || !up(o_qf, qframes.data(), qframes.size() * 4) ||
       (pack_bytes && hipMemset(ws + o_pack, 0, pack_bytes) != hipSuccess)) {
     (void)hipFree(ws);
     return VDN_ERR_HIP;
@@ -549,6 +561,7 @@ vdn_status ensure_backward(vdn_plan* p) {
   w.nscan = (int)order.size();
   w.kblocks = reinterpret_cast<const int2*>(ws + o_kb);
   w.nkblocks = (int)kblocks.size();
+  w.qframes = reinterpret_cast<const int*>(ws + o_qf);
   w.Lq = Lq;
   if (mfma_bwd) {
     uint16_t* pk = reinterpret_cast<uint16_t*>(ws + o_pack);

@@ -12,19 +12,29 @@
 //     that see the slot, then the tiles of the text and audio query rows when the backward includes
 //     them (they see every key: "Video DeltaNet speeds MiniMax H3 video generation 14.5x",
 //     summary).  Keys
-//     stay in registers (K, V as B operands); per query tile it forms S = Q K^T and dP = dO V^T
-//     with the query rows permuted so that a lane's values of two 16-row tiles are 8 consecutive
-//     queries, which makes P and dS directly the B operands of dV^T += dO^T P and dK^T += Q^T dS
-//     (dO^T, Q^T tiles from transposed copies).
+//     stay in registers (K, V as B operands, both negated: the accumulators start at +lse and +D
+//     read straight from LDS and hold lse - S and D - dP, whose exponential takes the sign as a
+//     source modifier); per query tile it forms S = Q K^T and dP = dO V^T with the query rows
+//     permuted so that a lane's values of two 16-row tiles are 8 consecutive queries, which makes
+//     P and -dS directly the B operands of dV^T += dO^T P and dK^T -= Q^T dS (dO^T, Q^T tiles from
+//     transposed copies).  Query rows past the end of their frame read an infinite lse, so their
+//     P and dS are exactly zero without a select.
 //   * softmax_dq_mfma: one workgroup = 256 queries of one frame (or of the text and audio query
 //     rows, which walk every key and are dispatched first) and head, 32 per wave, walking the
 //     frame's key ranges like the forward; S^T = K Q^T and dP^T = V dO^T with the key rows
-//     permuted the same way, then dQ^T += K^T dS^T.
+//     permuted the same way, then dQ^T += K^T dS^T.  Queries past the end of the rows take an
+//     infinite lse (zero P and dS); only a range's last, partial key tile masks keys (a
+//     compile-time variant of the tile body, so full tiles carry no selects).
+#include <type_traits>
+
 #include "dev_common.h"
 #include "vdn_internal.h"
 
 namespace vdn {
 namespace {
+
+// the normaliser DMA'd for query rows past the end of their frame: exp2(-inf) = 0 exactly
+__device__ float kInfRow = __builtin_inff();
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -82,7 +92,9 @@ struct DkvParams {
   const bf16_t *k, *v, *text_kv;        // [TN][H][D]; [2][n_glob][H][D]
   const float *lse, *dsum;              // [TN + n_cq][H]
   const int *qranges, *nqranges;        // per key slot: query-frame ranges
-  const int2* blocks;                   // per workgroup: (key slot, first key of the slot)
+  const int2* blocks;                   // per key block: (key slot, first key of the slot); workgroup
+                                        // b H + h takes block b of head h (the slots that every query
+                                        // frame sees come first, for every head)
   float *dk, *dv, *dtext;               // fp32 outputs (accumulated)
   int T, N, H, n_glob, n_cq;            // n_glob global (text, audio) keys in slot 0; n_cq context rows
   int64_t Lq;
@@ -113,9 +125,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   using SM = DkvSmem<D>;
   constexpr int KS = D / 32, DT = D / 16, KCH = D / 8, KT = kDkvKT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int2 blk = P.blocks[blockIdx.x];
-  const int slot = blk.x, h = blockIdx.y;
   const int N = P.N, H = P.H;
+  const int2 blk = P.blocks[blockIdx.x / H];
+  const int slot = blk.x, h = blockIdx.x % H;
   const int U = slot == 0 ? P.n_glob : N;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   bf16x8 kf[KT][KS], vf[KT][KS];
@@ -130,9 +142,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + ks * 32 + g * 8));
-      vf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8));
+      // -V: sign bits flipped once here (the opaque copy keeps the compiler from redoing the flip
+      // inside the tile loop)
+      u32x4 vr = *reinterpret_cast<const u32x4*>(vbase + ks * 32 + g * 8) ^ 0x80008000u;
+      asm volatile("" : "+v"(vr));
+      vf[kt][ks] = as_bf16x8(vr);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[kt][ks][e] = (__bf16)((float)kf[kt][ks][e] * P.c);   // scores in log2 units
+      for (int e = 0; e < 8; ++e) kf[kt][ks][e] = (__bf16)((float)kf[kt][ks][e] * -P.c);   // -scores in log2 units
     }
   }
   f32x4 dvt[KT][DT], dkt[KT][DT];
@@ -204,8 +220,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     }
     if (wave < 2) {                              // the tile's normalisers (wave 0) and D values (wave 1)
       const int64_t rr = ((int64_t)t * N + min(q0 + lane, rows - 1)) * H + h;
-      __builtin_amdgcn_global_load_lds((gptr_t)((wave == 0 ? P.lse : P.dsum) + rr),
-                                       (lptr_t)(base + 4 * SM::ROW + wave * 256), 4, 0, 0);
+      const float* src = wave == 1 ? P.dsum + rr : q0 + lane < rows ? P.lse + rr : &kInfRow;
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(base + 4 * SM::ROW + wave * 256), 4, 0, 0);
     }
   };
 
@@ -226,7 +242,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     }
     int t, q0;
     tile_at(it, t, q0);
-    const int rows = (CTX && t == P.T) ? P.n_cq : N;
     const unsigned char* qs = smem + (it & 1) * SM::STAGE;
     const unsigned char* os = qs + SM::ROW;
     const unsigned char* qts = qs + 2 * SM::ROW;
@@ -239,12 +254,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         const int u = 2 * j + u2;
-        // accumulators start at -lse and -D of the lane's four query rows
+        // accumulators start at lse and D of the lane's four query rows: they hold lse - S, D - dP
         f32x4 s[KT], dp[KT];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int qi = 32 * j + 8 * g + 4 * u2 + i;
-          const float l = -lse_s[qi], dd = -dsum_s[qi];
+          const float l = lse_s[qi], dd = dsum_s[qi];
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
             s[kt][i] = l;
@@ -267,11 +282,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
         // lane holds rows 4 g + i of tile u = queries 32 j + 8 g + 4 u2 + i, key l16 of tile kt
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = q0 + 32 * j + 8 * g + 4 * u2 + i < rows;
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
-            const float p = ok ? __builtin_amdgcn_exp2f(s[kt][i]) : 0.f;
-            const float ds = p * dp[kt][i];          // tau applied to dK at the end
+            const float p = __builtin_amdgcn_exp2f(-s[kt][i]);
+            const float ds = p * dp[kt][i];          // -dS / tau: -tau applied to dK at the end
             pj[kt][4 * u2 + i] = (__bf16)p;
             sj[kt][4 * u2 + i] = (__bf16)ds;
           }
@@ -304,7 +318,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     for (int dt = 0; dt < DT; ++dt) {
       f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
       f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
-      *a = *a + dkt[kt][dt] * tau;
+      *a = *a - dkt[kt][dt] * tau;
       *b = *b + dvt[kt][dt];
     }
   }
@@ -319,6 +333,7 @@ struct DqParams {
   const bf16_t *kp, *vp, *kt;           // [H][Ls][D], [H][Ls][D], [H][D][Ls]
   const float *lse, *dsum;              // [TN + n_cq][H]
   const int *ranges, *nranges;          // key ranges of each query frame; row T: the context rows
+  const int* qframes;                   // [T] query frames in dispatch order (most keys first)
   float *dq, *dcq;                      // fp32 [TN][H][D], [n_cq][H][D] (accumulated)
   int T, N, H, QT, n_cq, QTc;           // QTc query tiles of the context rows (0 without them)
   int ctx_split;                        // workgroups sharing one context query tile's key tiles
@@ -365,9 +380,9 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     h = w / (P.QTc * P.ctx_split);
     t = P.T;
   } else {
-    qt = w % P.QT;
-    t = (w / P.QT) % P.T;
-    h = w / (P.QT * P.T);
+    qt = w % P.QT;                              // frame-major: every head of the longest walks first
+    h = (w / P.QT) % P.H;
+    t = P.qframes[w / (P.QT * P.H)];
   }
   constexpr bool cx = CTX;
   const int N = P.N, H = P.H;
@@ -396,7 +411,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
       for (int e = 0; e < 8; ++e) qf[j][ks][e] = (__bf16)((float)qf[j][ks][e] * P.c);
 #endif
     }
-    lse[j] = P.lse[rr];
+    lse[j] = qv[j] ? P.lse[rr] : __builtin_inff();
     dsm[j] = P.dsum[rr];
   }
   f32x4 dqt[DT][kDqQT];
@@ -474,7 +489,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     tile_at(it0, key0, valid);
     issue_tile(key0, 0);
   }
-  for (int it = it0; it < it1; ++it) {
+  // the full key tiles come first in the walk, then each range's partial tile: two loops, the
+  // second with the key mask compiled in
+  auto step = [&](int it, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;       // keys valid..63 of the tile lie outside
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     __syncthreads();
     if (it + 1 < it1) {
@@ -487,65 +505,70 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     const unsigned char* ks_ = smem + ((it - it0) & 1) * SM::STAGE;
     const unsigned char* vs_ = ks_ + SM::TILE;
     const unsigned char* ts_ = ks_ + 2 * SM::TILE;
+    {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      bf16x8 dsf[kDqQT];
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 dsf[kDqQT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // S^T and dP^T of 16-key row tile u: key rows 8 (l16/4) + 4 u + l16%4 of the half
-        const int row = half * 32 + 8 * (l16 >> 2) + 4 * u + (l16 & 3);
-        f32x4 s[kDqQT], dp[kDqQT];
-#pragma unroll
-        for (int j = 0; j < kDqQT; ++j) {
-#if VDN_DQ_FOLD
-          s[j] = f32x4{-lse[j], -lse[j], -lse[j], -lse[j]};
-          dp[j] = f32x4{-dsm[j], -dsm[j], -dsm[j], -dsm[j]};
-#else
-          s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#endif
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = ks * 4 + g;
-          const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
-          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks_ + boff));
-          const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vs_ + boff));
+        for (int u = 0; u < 2; ++u) {
+          // S^T and dP^T of 16-key row tile u: key rows 8 (l16/4) + 4 u + l16%4 of the half
+          const int row = half * 32 + 8 * (l16 >> 2) + 4 * u + (l16 & 3);
+          f32x4 s[kDqQT], dp[kDqQT];
 #pragma unroll
           for (int j = 0; j < kDqQT; ++j) {
-            s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j][ks], s[j], 0, 0, 0);
-            dp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, of[j][ks], dp[j], 0, 0, 0);
-          }
-        }
-        // lane holds keys half*32 + 8 g + 4 u + i of query l16 (column tile j)
-#pragma unroll
-        for (int j = 0; j < kDqQT; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kl = half * 32 + 8 * g + 4 * u + i;
-            float ds = 0.f;
-            if (kl < valid && qv[j]) {
 #if VDN_DQ_FOLD
-              ds = __builtin_amdgcn_exp2f(s[j][i]) * dp[j][i];     // tau applied to dQ at the end
+            s[j] = f32x4{-lse[j], -lse[j], -lse[j], -lse[j]};
+            dp[j] = f32x4{-dsm[j], -dsm[j], -dsm[j], -dsm[j]};
+#else
+            s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#endif
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int ch = ks * 4 + g;
+            const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
+            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks_ + boff));
+            const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vs_ + boff));
+#pragma unroll
+            for (int j = 0; j < kDqQT; ++j) {
+              s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j][ks], s[j], 0, 0, 0);
+              dp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, of[j][ks], dp[j], 0, 0, 0);
+            }
+          }
+          // lane holds keys half*32 + 8 g + 4 u + i of query l16 (column tile j); a query past
+          // the rows has lse = inf, so its P and dS are zero
+#pragma unroll
+          for (int j = 0; j < kDqQT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#if VDN_DQ_FOLD
+              float ds = __builtin_amdgcn_exp2f(s[j][i]) * dp[j][i];     // tau applied to dQ at the end
 #else
               const float p = exp2f(s[j][i] * c - lse[j]);
-              ds = p * (dp[j][i] - dsm[j]) * tau;
+              float ds = p * (dp[j][i] - dsm[j]) * tau;
 #endif
+              if constexpr (MASKED) {
+                if (half * 32 + 8 * g + 4 * u + i >= valid) ds = 0.f;
+              }
+              dsf[j][4 * u + i] = (__bf16)ds;
             }
-            dsf[j][4 * u + i] = (__bf16)ds;
-          }
-      }
-      // dQ^T += K^T dS^T: K^T rows d = 16 dt + l16, keys half*32 + 8 g .. +8
+        }
+        // dQ^T += K^T dS^T: K^T rows d = 16 dt + l16, keys half*32 + 8 g .. +8
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int trow = dt * 16 + l16;
-        const int ch = half * 4 + g;
-        const bf16x8 kt = as_bf16x8(*reinterpret_cast<const u32x4*>(ts_ + trow * 128 + ((ch ^ t_swz(trow)) * 16)));
+        for (int dt = 0; dt < DT; ++dt) {
+          const int trow = dt * 16 + l16;
+          const int ch = half * 4 + g;
+          const bf16x8 kt = as_bf16x8(*reinterpret_cast<const u32x4*>(ts_ + trow * 128 + ((ch ^ t_swz(trow)) * 16)));
 #pragma unroll
-        for (int j = 0; j < kDqQT; ++j) dqt[dt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, dsf[j], dqt[dt][j], 0, 0, 0);
+          for (int j = 0; j < kDqQT; ++j) dqt[dt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, dsf[j], dqt[dt][j], 0, 0, 0);
+        }
       }
     }
-  }
+  };
+  const int split = min(max(nfull, it0), it1);
+  for (int it = it0; it < split; ++it) step(it, std::false_type{});
+  for (int it = split; it < it1; ++it) step(it, std::true_type{});
   // lane holds dQ^T rows d = 16 dt + 4 g + i of query l16 of tile j
 #pragma unroll
   for (int j = 0; j < kDqQT; ++j) {
@@ -629,11 +652,11 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     const size_t sm = 2 * DkvSmem<D>::STAGE;
     (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+    hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkblocks * H), dim3(kWaves * 64), sm, st, p);
     if (n_cq > 0) {                              // then the context rows' part, added on the same stream
       (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, true>), dim3(w.nkblocks, H), dim3(kWaves * 64), sm, st, p);
+      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, true>), dim3(w.nkblocks * H), dim3(kWaves * 64), sm, st, p);
     }
   }
   // dQ
@@ -650,6 +673,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.dsum = w.dsum;
     p.ranges = b.ranges;
     p.nranges = b.nranges;
+    p.qframes = w.qframes;
     p.dq = o.dq;
     p.dcq = o.dctx_q;
     p.T = T;

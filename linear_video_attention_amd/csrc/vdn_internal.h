@@ -197,6 +197,7 @@ struct BwdBuffers {
   int64_t Lq;                           // T*N + round_up(n_ctx, 64) + 64 (context rows from column T*N)
   const int2* kblocks;                  // dK/dV workgroups: (key slot, first key)
   int nkblocks;
+  const int* qframes;                   // [T] query frames by decreasing key count (dQ dispatch order)
   // text and audio query rows (the joint backward with context rows)
   const void* dctx_out;                 // [n_ctx][H][d] plan dtype (the caller's), or nullptr: no context rows
   void* octx;                           // [n_ctx][H][d] plan dtype: their recomputed output
