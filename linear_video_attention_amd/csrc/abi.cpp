@@ -458,21 +458,53 @@ vdn_status ensure_backward(vdn_plan* p) {
       }
       seg_read.push_back({(int64_t)f0 * N, (f1 - f0) * N, h});
     }
-  // dK/dV workgroups of the MFMA softmax backward: a block of keys of one slot each, the slots
-  // seen by every query frame (global keys, boundary frames) first
-  std::vector<int2> kblocks;
+  // Workgroup tables of the MFMA softmax transposes.  Workgroups are dispatched round-robin over
+  // the 8 XCDs, so entry w runs on XCD w % 8.  A group of workgroups that stream the same operand
+  // tiles (the key blocks of one slot and head; the query tiles of one frame and head) is placed on
+  // one XCD, whose L2 then serves them all; groups go in decreasing work (the slots every query
+  // frame sees, the frames that see every key: their walks are the longest and start with the
+  // launch), each to the XCD with the least work so far.
+  auto xcd_table = [](const auto& groups, const std::vector<int64_t>& work, auto noop) {
+    using E = decltype(noop);
+    constexpr int kXcds = 8;
+    std::vector<std::vector<E>> q(kXcds);
+    std::vector<int64_t> load(kXcds, 0);
+    for (size_t g = 0; g < groups.size(); ++g) {
+      const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      load[x] += work[g];
+      q[x].insert(q[x].end(), groups[g].begin(), groups[g].end());
+    }
+    size_t rounds = 0;
+    for (const auto& v : q) rounds = std::max(rounds, v.size());
+    std::vector<E> table(rounds * kXcds, noop);
+    for (int x = 0; x < kXcds; ++x)
+      for (size_t r = 0; r < q[x].size(); ++r) table[r * kXcds + x] = q[x][r];
+    return table;
+  };
+  // dK/dV: blocks of bkeys keys of one slot; the global keys and the boundary frames first
   const int bkeys = vdn::softmax_dkv_block_keys();
+  std::vector<std::vector<int4>> kgroups;
+  std::vector<int64_t> kgwork;
   auto add_slot = [&](int slot) {
     const int U = slot == 0 ? s.n_ctx : N;
-    for (int k0 = 0; k0 < U; k0 += bkeys) kblocks.push_back(make_int2(slot, k0));
+    int64_t frames = 0;
+    for (int r = 0; r < nqr[slot]; ++r)
+      frames += qr[(size_t)slot * 2 * vdn::kMaxRanges + 2 * r + 1] - qr[(size_t)slot * 2 * vdn::kMaxRanges + 2 * r];
+    for (int h = 0; h < H; ++h) {
+      std::vector<int4> g;
+      for (int k0 = 0; k0 < U; k0 += bkeys) g.push_back(make_int4(slot, k0, h, 0));
+      kgwork.push_back((int64_t)g.size() * frames);
+      kgroups.push_back(std::move(g));
+    }
   };
   if (s.n_ctx > 0) add_slot(0);
   for (int f = 0; f < T; ++f)
     if (vdn::is_boundary(s, f)) add_slot(1 + f);
   for (int f = 0; f < T; ++f)
     if (!vdn::is_boundary(s, f)) add_slot(1 + f);
-  // dQ workgroups: the query frames with the most keys (the boundary frames) first, so that their
-  // longer walks start with the launch instead of trailing it
+  const std::vector<int4> kwork = xcd_table(kgroups, kgwork, make_int4(-1, 0, 0, 0));
+  // dQ: the query tiles of one frame and head; frames by decreasing key count
+  const int QT = (N + vdn::softmax_dq_block_queries() - 1) / vdn::softmax_dq_block_queries();
   std::vector<int> qframes(T);
   std::vector<int64_t> nkeys(T, 0);
   for (int t = 0; t < T; ++t) {
@@ -482,6 +514,16 @@ vdn_status ensure_backward(vdn_plan* p) {
     for (int i = 0; i < nr; ++i) nkeys[t] += r[2 * i + 1] - r[2 * i];
   }
   std::stable_sort(qframes.begin(), qframes.end(), [&](int a, int b) { return nkeys[a] > nkeys[b]; });
+  std::vector<std::vector<int2>> qgroups;
+  std::vector<int64_t> qgwork;
+  for (int t : qframes)
+    for (int h = 0; h < H; ++h) {
+      std::vector<int2> g;
+      for (int qt = 0; qt < QT; ++qt) g.push_back(make_int2(t, qt + QT * h));
+      qgwork.push_back((int64_t)QT * nkeys[t]);
+      qgroups.push_back(std::move(g));
+    }
+  const std::vector<int2> qwork = xcd_table(qgroups, qgwork, make_int2(-1, 0));
   const bool mfma_bwd = p->kinds.softmax_mfma;
   // transposed query rows: the video rows, then the context rows from column T N, then a tile of
   // zero padding for the last partial tile
@@ -504,8 +546,8 @@ vdn_status ensure_backward(vdn_plan* p) {
   const size_t o_order = take(std::max<size_t>(1, order.size()) * 4), o_ms = take(mslot.size() * 4);
   const size_t o_qr = take(qr.size() * 4), o_nqr = take(nqr.size() * 4);
   const size_t o_sa = take(seg_all.size() * sizeof(vdn::Segment)), o_sr = take(seg_read.size() * sizeof(vdn::Segment));
-  const size_t o_kb = take(std::max<size_t>(1, kblocks.size()) * sizeof(int2));
-  const size_t o_qf = take(qframes.size() * 4);
+  const size_t o_kw = take(std::max<size_t>(1, kwork.size()) * sizeof(int4));
+  const size_t o_qw = take(std::max<size_t>(1, qwork.size()) * sizeof(int2));
   // matrix images: the merge's, then (reusing the space) the token gradients'
   const size_t mimg_bytes = (size_t)std::max<int64_t>(6 + 4 * (int64_t)(s.Nc + 1) * H, 6 * (int64_t)(T + 1) * H) * dd * 2;
   const size_t pack_bytes =
@@ -523,7 +565,7 @@ vdn_status ensure_backward(vdn_plan* p) {
       !up(o_qr, qr.data(), qr.size() * 4) || !up(o_nqr, nqr.data(), nqr.size() * 4) ||
       !up(o_sa, seg_all.data(), seg_all.size() * sizeof(vdn::Segment)) ||
       !up(o_sr, seg_read.data(), seg_read.size() * sizeof(vdn::Segment)) ||
-      !up(o_kb, kblocks.data(), kblocks.size() * sizeof(int2)) || !up(o_qf, qframes.data(), qframes.size() * 4) ||
+      !up(o_kw, kwork.data(), kwork.size() * sizeof(int4)) || !up(o_qw, qwork.data(), qwork.size() * sizeof(int2)) ||
       (pack_bytes && hipMemset(ws + o_pack, 0, pack_bytes) != hipSuccess)) {
     (void)hipFree(ws);
     return VDN_ERR_HIP;
@@ -559,9 +601,10 @@ vdn_status ensure_backward(vdn_plan* p) {
   w.splits_all = splits_all;
   w.splits_read = splits_read;
   w.nscan = (int)order.size();
-  w.kblocks = reinterpret_cast<const int2*>(ws + o_kb);
-  w.nkblocks = (int)kblocks.size();
-  w.qframes = reinterpret_cast<const int*>(ws + o_qf);
+  w.kwork = reinterpret_cast<const int4*>(ws + o_kw);
+  w.nkwork = (int)kwork.size();
+  w.qwork = reinterpret_cast<const int2*>(ws + o_qw);
+  w.nqwork = (int)qwork.size();
   w.Lq = Lq;
   if (mfma_bwd) {
     uint16_t* pk = reinterpret_cast<uint16_t*>(ws + o_pack);

@@ -92,9 +92,8 @@ struct DkvParams {
   const bf16_t *k, *v, *text_kv;        // [TN][H][D]; [2][n_glob][H][D]
   const float *lse, *dsum;              // [TN + n_cq][H]
   const int *qranges, *nqranges;        // per key slot: query-frame ranges
-  const int2* blocks;                   // per key block: (key slot, first key of the slot); workgroup
-                                        // b H + h takes block b of head h (the slots that every query
-                                        // frame sees come first, for every head)
+  const int4* work;                     // per workgroup: (key slot, first key of the slot, head, 0);
+                                        // a negative slot: no work (padding of the XCD placement)
   float *dk, *dv, *dtext;               // fp32 outputs (accumulated)
   int T, N, H, n_glob, n_cq;            // n_glob global (text, audio) keys in slot 0; n_cq context rows
   int64_t Lq;
@@ -126,8 +125,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   constexpr int KS = D / 32, DT = D / 16, KCH = D / 8, KT = kDkvKT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int N = P.N, H = P.H;
-  const int2 blk = P.blocks[blockIdx.x / H];
-  const int slot = blk.x, h = blockIdx.x % H;
+  const int4 blk = P.work[blockIdx.x];
+  if (blk.x < 0) return;
+  const int slot = blk.x, h = blk.z;
   const int U = slot == 0 ? P.n_glob : N;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   bf16x8 kf[KT][KS], vf[KT][KS];
@@ -333,7 +333,8 @@ struct DqParams {
   const bf16_t *kp, *vp, *kt;           // [H][Ls][D], [H][Ls][D], [H][D][Ls]
   const float *lse, *dsum;              // [TN + n_cq][H]
   const int *ranges, *nranges;          // key ranges of each query frame; row T: the context rows
-  const int* qframes;                   // [T] query frames in dispatch order (most keys first)
+  const int2* work;                     // per workgroup of the video rows: (query frame, query tile +
+                                        // QT head); a negative frame: no work
   float *dq, *dcq;                      // fp32 [TN][H][D], [n_cq][H][D] (accumulated)
   int T, N, H, QT, n_cq, QTc;           // QTc query tiles of the context rows (0 without them)
   int ctx_split;                        // workgroups sharing one context query tile's key tiles
@@ -380,9 +381,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     h = w / (P.QTc * P.ctx_split);
     t = P.T;
   } else {
-    qt = w % P.QT;                              // frame-major: every head of the longest walks first
-    h = (w / P.QT) % P.H;
-    t = P.qframes[w / (P.QT * P.H)];
+    const int2 e = P.work[w];
+    if (e.x < 0) return;
+    t = e.x;
+    qt = e.y % P.QT;
+    h = e.y / P.QT;
   }
   constexpr bool cx = CTX;
   const int N = P.N, H = P.H;
@@ -637,7 +640,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.dsum = w.dsum;
     p.qranges = w.qranges;
     p.nqranges = w.nqranges;
-    p.blocks = w.kblocks;
+    p.work = w.kwork;
     p.dk = o.dk;
     p.dv = o.dv;
     p.dtext = o.dtext_kv;
@@ -652,11 +655,11 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     const size_t sm = 2 * DkvSmem<D>::STAGE;
     (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkblocks * H), dim3(kWaves * 64), sm, st, p);
+    hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, false>), dim3(w.nkwork), dim3(kWaves * 64), sm, st, p);
     if (n_cq > 0) {                              // then the context rows' part, added on the same stream
       (void)hipFuncSetAttribute((const void*)softmax_dkv_mfma_kernel<D, true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, true>), dim3(w.nkblocks * H), dim3(kWaves * 64), sm, st, p);
+      hipLaunchKernelGGL((softmax_dkv_mfma_kernel<D, true>), dim3(w.nkwork), dim3(kWaves * 64), sm, st, p);
     }
   }
   // dQ
@@ -673,7 +676,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     p.dsum = w.dsum;
     p.ranges = b.ranges;
     p.nranges = b.nranges;
-    p.qframes = w.qframes;
+    p.work = w.qwork;
     p.dq = o.dq;
     p.dcq = o.dctx_q;
     p.T = T;
@@ -703,7 +706,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
     }
     (void)hipFuncSetAttribute((const void*)softmax_dq_mfma_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sm);
-    hipLaunchKernelGGL((softmax_dq_mfma_kernel<D, false>), dim3(p.QT * T * H), dim3(kDqWaves * 64), sm, st, p);
+    hipLaunchKernelGGL((softmax_dq_mfma_kernel<D, false>), dim3(w.nqwork), dim3(kDqWaves * 64), sm, st, p);
   }
   return hipGetLastError();
 }
@@ -711,6 +714,7 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
 }  // namespace
 
 int softmax_dkv_block_keys() { return kDkvKeys; }
+int softmax_dq_block_queries() { return kDqBQ; }
 
 hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const Buffers& b, const BwdBuffers& w,
                                         const BwdOutputs& o, hipStream_t st) {

@@ -195,9 +195,12 @@ struct BwdBuffers {
   uint16_t *qt, *dot;                   // [H][d][Lq] transposed q, do_s (bf16); pad columns zero
   uint16_t *kt, *vp;                    // [H][d][Ls] transposed keys, [H][Ls][d] key-major values
   int64_t Lq;                           // T*N + round_up(n_ctx, 64) + 64 (context rows from column T*N)
-  const int2* kblocks;                  // dK/dV workgroups: (key slot, first key)
-  int nkblocks;
-  const int* qframes;                   // [T] query frames by decreasing key count (dQ dispatch order)
+  // workgroup tables of the two softmax transposes: entry w runs on XCD w % 8; an entry with a
+  // negative first field is a workgroup without work
+  const int4* kwork;                    // dK/dV: (key slot, first key, head, 0)
+  int nkwork;
+  const int2* qwork;                    // dQ: (query frame, query tile + QT head)
+  int nqwork;
   // text and audio query rows (the joint backward with context rows)
   const void* dctx_out;                 // [n_ctx][H][d] plan dtype (the caller's), or nullptr: no context rows
   void* octx;                           // [n_ctx][H][d] plan dtype: their recomputed output
@@ -224,6 +227,7 @@ hipError_t launch_softmax_backward_mfma(const Shape& s, const Inputs& in, const 
                                         const BwdOutputs& o, hipStream_t st);
 // keys of one key slot that a workgroup of the MFMA dK/dV kernel covers (the host's block table)
 int softmax_dkv_block_keys();
+int softmax_dq_block_queries();
 
 // Number of workgroups of the MFMA softmax launch.
 // with_ctx: including the workgroups of the context query rows.
