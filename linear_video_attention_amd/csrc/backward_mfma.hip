@@ -47,10 +47,16 @@ constexpr int kVmcntZero = 0x0F70;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-// swizzles: rows read 8 lanes at a time as {8a + b : a in {0,1}, b in 0..3} + const (row-major
-// tiles) or 8 consecutive rows (transposed tiles)
-__device__ __forceinline__ int r_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int t_swz(int row) { return row & 7; }
+// LDS swizzles (XOR on the 16-byte chunk index of a row).  gfx950 serves a 16-byte LDS read 16
+// lanes per pass over 64 banks of 4 bytes, so the 16 rows one lane group reads must fall on 16
+// distinct 16-byte slots of the 256-byte bank period.  Row-major tiles: a group reads rows
+// {8a + b : a in 0..3, b in 0..3} + const of one chunk (rows of 2 D bytes); transposed tiles: 16
+// consecutive rows of 128 bytes.
+template <int D>
+__device__ __forceinline__ int r_swz(int row) {
+  return D == 128 ? (row & 3) | ((row >> 1) & 12) : ((row >> 1) & 1) | ((row >> 2) & 6);
+}
+__device__ __forceinline__ int t_swz(int row) { return (row >> 1) & 7; }
 // row of a 16-row tile u (of a 32-row k-step pair) that lane l16 addresses: 8 (l16/4) + 4 (u%2) + l16%4
 __device__ __forceinline__ int perm_row(int u, int l16) { return 32 * (u >> 1) + 8 * (l16 >> 2) + 4 * (u & 1) + (l16 & 3); }
 
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     for (int i = 0; i < R_INSTR; ++i) {
       const int blkid = i * kWaves + wave;
       const int row = blkid * R_ROWS_PER_KB + lane / KCH;
-      const int c = (lane % KCH) ^ r_swz(row);
+      const int c = (lane % KCH) ^ r_swz<D>(row);
       const int qrow = min(q0 + row, rows - 1);
       const int64_t off = ((int64_t)qrow * H + h) * D + c * 8;
       __builtin_amdgcn_global_load_lds((gptr_t)(qsrc + off), (lptr_t)(base + blkid * 1024), 16, 0, 0);
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int ch = ks * 4 + g;
-          const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
+          const int boff = row * (D * 2) + ((ch ^ r_swz<D>(row)) * 16);
           const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + boff));
           const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(os + boff));
 #pragma unroll
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
     for (int i = 0; i < R_INSTR; ++i) {
       const int blkid = i * kDqWaves + wave;
       const int row = blkid * R_ROWS_PER_KB + lane / KCH;
-      const int c = (lane % KCH) ^ r_swz(row);
+      const int c = (lane % KCH) ^ r_swz<D>(row);
       const int64_t off = ((int64_t)(key0 + row) * D + c * 8) * 2;
       __builtin_amdgcn_global_load_lds((gptr_t)(kh + off), (lptr_t)(base + blkid * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gptr_t)(vh + off), (lptr_t)(base + SM::TILE + blkid * 1024), 16, 0, 0);
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void softmax_dq_mfma_kernel(DqPar
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const int ch = ks * 4 + g;
-            const int boff = row * (D * 2) + ((ch ^ r_swz(row)) * 16);
+            const int boff = row * (D * 2) + ((ch ^ r_swz<D>(row)) * 16);
             const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks_ + boff));
             const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vs_ + boff));
 #pragma unroll

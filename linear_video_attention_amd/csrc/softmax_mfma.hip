@@ -16,7 +16,7 @@
 //     two waves per SIMD, whose interleaving hides each other's exponentials and LDS latency;
 //   * key tiles of 64 keys are loaded straight from global memory into LDS (global_load_lds,
 //     two stages by default: the next tile in flight; K as [key][d], V transposed as [d][key], both
-//     XOR-swizzled so that every group of eight lanes of a 16-byte fragment read hits distinct
+//     XOR-swizzled so that every group of sixteen lanes of a 16-byte fragment read hits distinct
 //     banks) and processed as two 32-key halves;
 //   * S^T = K Q^T with keys as rows: the K fragment rows of 16-key tile t are the keys
 //     8 (r / 4) + 4 t + (r % 4) of the half, so that a lane's four scores of tile 0 and four of
@@ -107,11 +107,15 @@ constexpr int kVmcntZero = 0x0F70;          // s_waitcnt vmcnt(0), other counter
 // s_waitcnt immediate for vmcnt(n), n < 64 (low four bits in [3:0], high two in [15:14])
 constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// LDS chunk swizzles (16-byte chunks).  One fragment read serves eight lanes per LDS cycle: lanes
-// 8j .. 8j+7 read K rows {8a + b : a in {0,1}, b in 0..3} + const (same chunk) and V^T rows
-// 8 consecutive rows (same chunk); the swizzles give those rows eight distinct chunk positions.
-__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int v_swz(int row) { return row & 7; }
+// LDS chunk swizzles (XOR on the 16-byte chunk index of a row).  gfx950 serves a 16-byte LDS read
+// 16 lanes per pass over 64 banks of 4 bytes: lanes 16j .. 16j+15 read K rows
+// {8a + b : a in 0..3, b in 0..3} + const of one chunk (rows of 2 D bytes) and 16 consecutive V^T
+// rows of 128 bytes, and the swizzles put those 16 rows on 16 distinct 16-byte bank slots.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 3) | ((row >> 1) & 12) : ((row >> 1) & 1) | ((row >> 2) & 6);
+}
+__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
 
 template <int D>
 struct Smem {
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
 #pragma unroll
   for (int i = 0; i < K_INSTR; ++i) {
     const int row = (i * kWaves + wave) * K_ROWS_PER_KB + lane / SM::KCH;
-    const int c = (lane % SM::KCH) ^ k_swz(row);
+    const int c = (lane % SM::KCH) ^ k_swz<D>(row);
     koff[i] = (uint32_t)(row * D + c * 8) * 2u;
   }
 #pragma unroll
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(kWaves * 64, VDN_SOFTMAX_WG_PER_CU) void softmax_mf
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int c = ks * 4 + g;
-        kf[u][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz(row)) * 16)));
+        kf[u][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)));
       }
     }
     constexpr bool kPre = !FALLBACK && VDN_SOFTMAX_PRESCALE;   // accumulators start at -mref
