@@ -70,8 +70,12 @@ constexpr float kMasked = -1.0e30f;
 constexpr int kVmcntZero = 0x0F70;
 constexpr uint32_t kOnes = 0x38383838u;   // four E4M3 ones
 
-__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 3) & 4); }
-__device__ __forceinline__ int v_swz(int row) { return row & 7; }
+// LDS swizzles (XOR on the 16-byte chunk index of a 128-byte row): a 16-byte LDS read is served
+// 16 lanes per pass over 64 banks of 4 bytes, and the 16 rows one lane group reads -- K rows
+// {32 a + b : a in 0..3, b in 0..3} + const, V^T rows 16 consecutive -- fall on 16 distinct
+// 16-byte slots of the 256-byte bank period
+__device__ __forceinline__ int k_swz(int row) { return ((row >> 1) & 1) | ((row >> 4) & 6); }
+__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ float pow2_scale(float m) {
