@@ -66,9 +66,27 @@ __device__ __forceinline__ int perm_row(int u, int l16) { return 32 * (u >> 1) +
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
                                                      int64_t rows, int H, int D, int64_t ld, int64_t col0) {
-  __shared__ bf16_t tile[64][64 + 2];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64][64 + 8];
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int h = blockIdx.y, d0 = blockIdx.z * 64;
+  if (r0 + 64 <= rows && ld % 8 == 0 && col0 % 8 == 0) {
+    // a full tile with 16-byte aligned destination rows: 16-byte loads and stores
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+      const int r = e / 8, c8 = e % 8;
+      *reinterpret_cast<u32x4*>(&tile[r][c8 * 8]) =
+          *reinterpret_cast<const u32x4*>(src + ((r0 + r) * H + h) * D + d0 + c8 * 8);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+      const int c = e / 8, r8 = e % 8;                 // output row d0 + c, input rows 8 r8 .. + 7
+      bf16_t o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = tile[8 * r8 + k][c];
+      *reinterpret_cast<u32x4*>(dst + ((int64_t)h * D + d0 + c) * ld + col0 + r0 + 8 * r8) =
+          *reinterpret_cast<const u32x4*>(o);
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int r = e / 64, c = e % 64;
     tile[r][c] = (r0 + r < rows) ? src[((r0 + r) * H + h) * D + d0 + c] : (bf16_t)0;
@@ -80,12 +98,18 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ 
   }
 }
 
+// one 16-byte chunk per thread: chunk e of src row (r, h) goes to dst row h ld + row0 + r
 __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
                                                         int64_t rows, int H, int D, int64_t ld, int64_t row0) {
-  const int64_t r = (int64_t)blockIdx.x;
-  const int h = blockIdx.y;
-  if (r >= rows) return;
-  for (int c = threadIdx.x; c < D; c += 256) dst[((int64_t)h * ld + row0 + r) * D + c] = src[(r * H + h) * D + c];
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = D / 8;
+  if (e >= rows * H * cpr) return;
+  const int c = (int)(e % cpr);
+  const int64_t rh = e / cpr;
+  const int h = (int)(rh % H);
+  const int64_t r = rh / H;
+  *reinterpret_cast<u32x4*>(dst + ((int64_t)h * ld + row0 + r) * D + c * 8) =
+      *reinterpret_cast<const u32x4*>(src + (r * H + h) * D + c * 8);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -624,12 +648,14 @@ hipError_t run_t(const Shape& s, const Inputs& in, const Buffers& b, const BwdBu
   if (s.n_ctx > 0) {                               // the global (text, audio) keys
     pack_t_kernel<<<dim3((s.n_ctx + 63) / 64, H, D / 64), 256, 0, st>>>((const bf16_t*)in.text_kv, w.kt, s.n_ctx, H,
                                                                         D, s.Ls, 0);
-    pack_rows_kernel<<<dim3(s.n_ctx, H), 256, 0, st>>>((const bf16_t*)in.text_kv + (int64_t)s.n_ctx * H * D, w.vp,
+    pack_rows_kernel<<<(unsigned)(((int64_t)s.n_ctx * H * (D / 8) + 255) / 256), 256, 0, st>>>(
+        (const bf16_t*)in.text_kv + (int64_t)s.n_ctx * H * D, w.vp,
                                                        s.n_ctx, H, D, s.Ls, 0);
   }
   pack_t_kernel<<<dim3((int)((TN + 63) / 64), H, D / 64), 256, 0, st>>>((const bf16_t*)in.k, w.kt, TN, H, D, s.Ls,
                                                                        s.ctx_pad);
-  pack_rows_kernel<<<dim3((unsigned)TN, H), 256, 0, st>>>((const bf16_t*)in.v, w.vp, TN, H, D, s.Ls, s.ctx_pad);
+  pack_rows_kernel<<<(unsigned)((TN * H * (D / 8) + 255) / 256), 256, 0, st>>>((const bf16_t*)in.v, w.vp, TN, H, D, s.Ls,
+                                                                               s.ctx_pad);
   // dK, dV
   {
     DkvParams p{};
