@@ -10,10 +10,14 @@ namespace vdn {
 // No pivoting: the callers invert I + A with A symmetric positive semi-definite, whose pivots are
 // all >= 1.  Pivot p maps a to
 //   a_ij - a_ip a_pj / a_pp (i, j != p),  a_pj / a_pp (row p),  -a_ip / a_pp (column p),  1 / a_pp;
-// every element takes the rank-one update a_ij - f_i r_j with r_j = a_pj / a_pp, and the owners of
-// row and column p then overwrite those with their own values (the same arithmetic as a
-// per-element select, at one FMA per element).  The pivot loop is split into (block, unrolled
-// offset) so that every register index is a compile-time constant.
+// every element takes the rank-one update a_ij - g_i a_pj with g_i = a_ip / a_pp, and the owners
+// of column p then store -g_i, the owners of row p a_pj / a_pp, the owner of a_pp 1 / a_pp.  The
+// kernel is bound by vector-ALU issue (366 eliminations at 768p, two per CU on part of the chip),
+// so the per-pivot work is kept to the FMAs of the update plus one multiply per owned row (g_i):
+// the row fix-up runs as a branch taken by the one wave that holds row p, 1 / a_pp is a
+// reciprocal refined by one Newton step, and the column fix-up is a sign-flipped copy of g.
+// The pivot loop is split into (block, unrolled offset) so that every register index is a
+// compile-time constant.
 template <int D>
 __device__ __forceinline__ void gauss_jordan_inverse(float (&a)[D / 16][D / 16], float* rowbuf, float* colbuf,
                                                      int ty, int tx) {
@@ -33,22 +37,26 @@ __device__ __forceinline__ void gauss_jordan_inverse(float (&a)[D / 16][D / 16],
         for (int ii = 0; ii < R; ++ii) cb[ty * R + ii] = a[ii][pr];
       }
       __syncthreads();
-      const float inv = 1.0f / rb[p];
-      float rj[R], fi[R];
+      const float piv = rb[p];
+      float inv = __builtin_amdgcn_rcpf(piv);
+      inv = __builtin_fmaf(__builtin_fmaf(-piv, inv, 1.0f), inv, inv);
+      float rj[R], gi[R];
 #pragma unroll
-      for (int jj = 0; jj < R; ++jj) rj[jj] = rb[tx * R + jj] * inv;
+      for (int jj = 0; jj < R; ++jj) rj[jj] = rb[tx * R + jj];
 #pragma unroll
-      for (int ii = 0; ii < R; ++ii) fi[ii] = cb[ty * R + ii];
+      for (int ii = 0; ii < R; ++ii) gi[ii] = cb[ty * R + ii] * inv;
 #pragma unroll
       for (int ii = 0; ii < R; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < R; ++jj) a[ii][jj] -= fi[ii] * rj[jj];
-      const bool own_row = ty == pb, own_col = tx == pb;
+        for (int jj = 0; jj < R; ++jj) a[ii][jj] = __builtin_fmaf(-gi[ii], rj[jj], a[ii][jj]);
+      if (ty == pb) {                      // the one wave holding row p
 #pragma unroll
-      for (int jj = 0; jj < R; ++jj) a[pr][jj] = own_row ? rj[jj] : a[pr][jj];
+        for (int jj = 0; jj < R; ++jj) a[pr][jj] = rj[jj] * inv;
+      }
+      const bool own_col = tx == pb;
 #pragma unroll
-      for (int ii = 0; ii < R; ++ii) a[ii][pr] = own_col ? -fi[ii] * inv : a[ii][pr];
-      a[pr][pr] = (own_row && own_col) ? inv : a[pr][pr];
+      for (int ii = 0; ii < R; ++ii) a[ii][pr] = own_col ? -gi[ii] : a[ii][pr];
+      a[pr][pr] = (ty == pb && own_col) ? inv : a[pr][pr];
     }
   }
 }
