@@ -27,4 +27,14 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global memory, which on
+// this target waits for every outstanding vector-memory operation of the wave (vmcnt(0)): the
+// global loads, stores and LDS DMA copies issued for later tiles or steps, so a multi-stage tile
+// pipeline drains at every barrier (an LDS-only fence does the same, since LDS DMA is counted by
+// vmcnt).  Here the wave waits only for its own LDS operations (lgkmcnt(0)) before s_barrier,
+// and the memory clobber keeps the compiler from moving memory accesses across it.  A tile copied
+// by LDS DMA must be waited for with an explicit vmcnt by every wave that issued part of it
+// before the barrier, and nothing written to global memory by another wave is visible after it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace vdn

@@ -14,7 +14,8 @@
 //     hi + lo parts), plus each wave's partial sum of o_l^2 per token;
 //   * projection waves (4-7): one tile behind, out^T = Wp0^T x_s^T + r (Wp1^T z_l^T), with r from
 //     the four partial sums, stored as bf16.
-// One barrier per tile hands the tile over (double-buffered x planes and partials).  Every product
+// One barrier per tile hands the tile over (double-buffered x planes and partials); it orders LDS
+// only, so the q copies, o_s loads and output stores in flight stay in flight across it.  Every product
 // is computed transposed (channels x tokens) with v_mfma_f32_16x16x32_bf16 so that the matrix
 // shared by all tokens -- S (as bf16 hi + lo, since the readout needs ~16 mantissa bits) and the
 // pre-transposed weights -- is the A operand and stays in registers: each wave owns 16 CT
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
     // Issue order per tile: the o_s loads of the next tile, then the q DMA of the tile after; the
     // wait for those o_s loads (before their registers are used) then leaves the DMA in flight.
     __builtin_amdgcn_s_waitcnt(0x0F70);                // q tiles 0 (and 1) landed
-    __syncthreads();                                   // q tile 0 complete for every wave
+    lds_barrier();                                     // q tile 0 complete for every wave
     for (int it = 0; it <= ntiles; ++it) {
       if (it < ntiles) {
         if (it + 1 < ntiles) fetch_os(it + 1, osb);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
       }
       if (it + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntTile);   // q tile it+1 landed
       else __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();                                 // tile it handed over; q tile it+1 complete
+      lds_barrier();                                   // tile it handed over; q tile it+1 complete
     }
   } else {
     // ---- projection waves: channels [16 CT sw, +16 CT) ----
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     for (int it = 0; it <= ntiles; ++it) {
       if (it >= 1) {
         const int pt = it - 1;                         // the tile handed over at the last barrier
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(512) void epilogue_mfma_kernel(const bf16_t* __rest
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 }

@@ -29,7 +29,8 @@
 //     transposes (the scan's operand layout), P> also as its own planes (= P<^T) without decay.
 //     At most C-1 steps each.
 //   * vda_chunk_scan_kernel: one workgroup per (head, direction, 16 rows) walks the Nc-2 chunk
-//     steps with the operands of the next two steps in flight, storing one state slot per step.
+//     steps, the next step's matrix copied into LDS (DMA, two stages) during the current step's
+//     product, storing one state slot per step.
 //     Slot Nc of each direction receives S0 (read by boundary query frames).
 #include "dev_common.h"
 #include "vdn_internal.h"
@@ -39,6 +40,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 __device__ __forceinline__ bool is_bnd(int f, int T, int anchors) { return anchors && (f == 0 || f == T - 1); }
 
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
   };
   if (m > 1) load_step(1);
   for (int a = 1; a < m; ++a) {
-    __syncthreads();                                 // rows of s[buf] complete
+    lds_barrier();                                   // rows of s[buf] complete (the next operands stay in flight)
     step_product<D, RT>(s, buf, op, acc, l16, lg);
     if (a + 1 < m) load_step(a + 1);                 // the next frame's operands during the stores
     buf ^= 1;
@@ -221,14 +224,39 @@ __global__ __launch_bounds__(D * 4) void vda_compose_kernel(const float* __restr
   }
 }
 
+// Chunk scan operand staging: the step matrix (two bf16 planes of its transpose, 2 D^2 bf16,
+// contiguous) is copied into LDS by DMA in whole 256-byte rows (the fragment loads straight from
+// global memory touched each 128-byte line with half a line per instruction, so twice the bytes
+// crossed into the CU; at 768p the scan spent most of its time there), 16-byte chunk c of row n
+// at chunk position c ^ scan_swz(n) so that the 16 rows a 16-lane fragment read covers land on
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int scan_swz(int n) {
+  if constexpr (D == 128) return n & 15;
+  else return (n >> 1) & 7;
+}
+template <int D>
+struct ScanSmem {
+  static constexpr int MAT = 2 * D * D * 2;            // bytes of one step matrix (hi, lo planes)
+  static constexpr int STAGES = 2;
+  static constexpr int ROWS_OFF = STAGES * MAT;
+  static constexpr int TOTAL = ROWS_OFF + (int)sizeof(RowPlanes<D, 1>);
+};
+
 template <int D>
 __global__ __launch_bounds__(D * 4) void vda_chunk_scan_kernel(const float* __restrict__ cw,
                                                                const bf16_t* __restrict__ pp,
                                                                const float* __restrict__ qq,
                                                                float* __restrict__ states, int Nc, int H,
                                                                int n_chains, int per_xcd) {
+  using SM = ScanSmem<D>;
   constexpr int RB = D / 16;                         // row blocks per (head, direction)
-  __shared__ __attribute__((aligned(16))) RowPlanes<D, 1> s;
+  constexpr int NW = D / 16;                         // waves
+  constexpr int CHR = D / 8;                         // 16-byte chunks per plane row
+  constexpr int ROWS_PER_KB = 1024 / (2 * D);
+  constexpr int DMA = SM::MAT / 1024 / NW;           // DMA instructions per wave and step
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  RowPlanes<D, 1>& s = *reinterpret_cast<RowPlanes<D, 1>*>(smem + SM::ROWS_OFF);
   // workgroup -> (head, direction, row block), the row blocks of one chain on one XCD
   const int w = blockIdx.x;
   const int L = (w & 7) * per_xcd + (w >> 3);
@@ -247,62 +275,80 @@ __global__ __launch_bounds__(D * 4) void vda_chunk_scan_kernel(const float* __re
   };
   // step k applies chunk j(k) and yields slot j(k) + 2 (forward) / j(k) - 2 (reverse)
   const int n_steps = max(Nc - 2, 0);
-  auto load = [&](StepOps<D, 1>& op, int k) {        // past the last step: a harmless reload of step 0
-    const int kk = k < n_steps ? k : 0;
-    const int j = dir == 0 ? kk : Nc - 1 - kk;
-    const int64_t ph = (int64_t)j * H + h;
-    // forward applies P> (planes of P>^T give its columns), reverse applies P< (planes of P<^T)
-    load_mat<D, 1>(op, pp + ph * 4 * DD + (dir == 0 ? 2 * DD : 0), col, lg);
-    load_add<D, 1>(op, qq + ((int64_t)dir * Nc * H + ph) * DD, row0, col, lg);
+  auto chunk_of = [&](int k) { return dir == 0 ? k : Nc - 1 - k; };
+  // forward applies P> (planes of P>^T give its columns), reverse applies P< (planes of P<^T)
+  auto issue_mat = [&](int k) {
+    const bf16_t* src = pp + ((int64_t)chunk_of(k) * H + h) * 4 * DD + (dir == 0 ? 2 * DD : 0);
+    unsigned char* stg = smem + (k & 1) * SM::MAT;
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const int blk = i * NW + wave;
+      const int row = blk * ROWS_PER_KB + lane / CHR;          // row of the [2 D][D] plane pair
+      const int c = (lane % CHR) ^ scan_swz<D>(row & (D - 1));
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + (int64_t)row * D + c * 8), (lptr_t)(stg + blk * 1024), 16,
+                                       0, 0);
+    }
+  };
+  auto load_c = [&](f32x4& c, int k) {
+    const float* a = qq + ((int64_t)dir * Nc * H + (int64_t)chunk_of(k) * H + h) * DD + (int64_t)(row0 + 4 * lg) * D + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = a[i * D];
   };
 
-  f32x4 acca[1], accb[1];
+  f32x4 acc;
   {
     const float* cp = cw + (int64_t)h * DD + (int64_t)(row0 + 4 * lg) * D + col;   // S0 = C_0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) accb[0][i] = cp[i * D];
+    for (int i = 0; i < 4; ++i) acc[i] = cp[i * D];
   }
   int buf = 0;
-  put_rows<D, 1>(s, buf, accb, col, lg);
-  for (int c = 0; c < min(Nc, 2); ++c) store(dir == 0 ? c : Nc - 1 - c, accb[0]);
-
-  // The steps run in pairs with the operands of the next two steps in flight.  Each step issues
-  // exactly one store, before the next operand loads, and results alternate between two
-  // accumulators (the store of one is never overwritten by the next step): the compiler can then
-  // keep the loads in flight across the following steps.  The prologue follows the same pattern
-  // (loads, one store, loads).
-  StepOps<D, 1> opa, opb;
-  load(opa, 0);
-  asm volatile("" ::: "memory");
-  store(Nc, accb[0]);
-  asm volatile("" ::: "memory");
-  load(opb, 1);
-  asm volatile("" ::: "memory");
-  auto apply = [&](const StepOps<D, 1>& op, f32x4 (&acc)[1]) {
-    __syncthreads();                                 // rows of s[buf] complete
-    step_product<D, 1>(s, buf, op, acc, l16, lg);
-    buf ^= 1;
-    put_rows<D, 1>(s, buf, acc, col, lg);
-  };
-  auto slot_after = [&](int k) { return dir == 0 ? k + 2 : Nc - 3 - k; };
-  int k = 0;
-  for (; k + 1 < n_steps; k += 2) {
-    apply(opa, acca);
-    asm volatile("" ::"v"(accb[0]));                 // the store of accb may still be reading it
-    store(slot_after(k), acca[0]);
-    asm volatile("" ::: "memory");
-    load(opa, k + 2);
-    asm volatile("" ::: "memory");
-    apply(opb, accb);
-    asm volatile("" ::"v"(acca[0]));
-    store(slot_after(k + 1), accb[0]);
-    asm volatile("" ::: "memory");
-    load(opb, k + 3);
-    asm volatile("" ::: "memory");
+  {
+    f32x4 a1[1] = {acc};
+    put_rows<D, 1>(s, buf, a1, col, lg);
   }
-  if (k < n_steps) {
-    apply(opa, acca);
-    store(slot_after(k), acca[0]);
+  for (int c = 0; c < min(Nc, 2); ++c) store(dir == 0 ? c : Nc - 1 - c, acc);
+  store(Nc, acc);
+  if (n_steps == 0) return;
+  // one step: wait for its matrix (DMA) and additive term, start the next step's copies into
+  // the other stage and registers, then the product; the loop runs in pairs so the additive terms
+  // alternate between two registers without a copy (a copy would make the compiler wait for the
+  // next step's loads too)
+  auto step = [&](int k, const f32x4& cur, f32x4& nxt) {
+    // only the 4 state stores of step k-1 may be newer than step k's loads (none at k = 0: the
+    // prologue's stores came first)
+    if (k == 0) __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0F74);                // vmcnt(4)
+    lds_barrier();                                          // stage k & 1 and the rows of s[buf] complete
+    if (k + 1 < n_steps) {                                  // stage (k+1) & 1 was last read in step k-1
+      issue_mat(k + 1);
+      load_c(nxt, k + 1);
+    }
+    asm volatile("" ::: "memory");                          // keep these loads ahead of this step's store
+    const unsigned char* stg = smem + (k & 1) * SM::MAT;
+    f32x4 a0 = cur, a1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const int ch = ks * 4 + lg;
+      const int off = col * (2 * D) + ((ch ^ scan_swz<D>(col)) << 4);
+      const bf16x8 mh = *reinterpret_cast<const bf16x8*>(stg + off);
+      const bf16x8 ml = *reinterpret_cast<const bf16x8*>(stg + D * D * 2 + off);
+      const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&s.hi[buf][l16][ks * 32 + lg * 8]);
+      const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&s.lo[buf][l16][ks * 32 + lg * 8]);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, mh, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, ml, a1, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, mh, a1, 0, 0, 0);
+    }
+    f32x4 r1[1] = {a0 + a1};
+    buf ^= 1;
+    put_rows<D, 1>(s, buf, r1, col, lg);
+    store(dir == 0 ? k + 2 : Nc - 3 - k, r1[0]);
+  };
+  f32x4 ca, cb;
+  issue_mat(0);
+  load_c(ca, 0);
+  for (int k = 0; k < n_steps; k += 2) {
+    step(k, ca, cb);
+    if (k + 1 < n_steps) step(k + 1, cb, ca);
   }
 }
 
@@ -314,7 +360,11 @@ void launch_t(const Shape& s, const Inputs& in, const Buffers& b, hipStream_t st
   // the row blocks of one (head, direction) stay on one XCD: per_xcd is a multiple of D / 16
   const int n_chains = 2 * s.H;
   const int per_xcd = (n_chains + 7) / 8 * (D / 16);
-  vda_chunk_scan_kernel<D><<<8 * per_xcd, D * 4, 0, st>>>(b.cw, b.pp, b.qq, b.states, s.Nc, s.H, n_chains, per_xcd);
+  const size_t smem = ScanSmem<D>::TOTAL;
+  (void)hipFuncSetAttribute((const void*)vda_chunk_scan_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+  vda_chunk_scan_kernel<D><<<8 * per_xcd, D * 4, smem, st>>>(b.cw, b.pp, b.qq, b.states, s.Nc, s.H, n_chains,
+                                                             per_xcd);
 }
 
 }  // namespace

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* _
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kVmcntTile);   // tile it landed, it+1 in flight
     else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
-    __syncthreads();                       // ... for every wave; Y and stage (it+2)%3 (tile it-1) are free
+    lds_barrier();                         // ... for every wave; Y and stage (it+2)%3 (tile it-1) are free
     if (it + 2 < ntiles) issue_tile((it + 2) * kTU, (it + 2) % kStages);
     const unsigned char* kb = smem + (it % kStages) * SM::STAGE;
     // Y = beta k as hi + lo, same chunk positions as K (chunk e = tid + s * kThreads, token e / CH)
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* _
       *reinterpret_cast<bf16x8*>(yb + e * 16) = yhv;
       *reinterpret_cast<bf16x8*>(yb + SM::TILE + e * 16) = ylv;
     }
-    __syncthreads();                                  // Y ready
+    lds_barrier();                                    // Y ready
 #pragma unroll
     for (int ks = 0; ks < kTU / 16; ++ks) {
       const int kbyte = ks * 16 * SM::ROW;
