@@ -20,6 +20,8 @@
 //   * 8 waves: wave w owns X rows [32 MT (w % 4), +32 MT) (K features for w % 4 < 2, V features
 //     otherwise) and Y columns [32 NT (w / 4), +32 NT), MT = NT = d / 64.
 // Every K/V/beta byte of the frame is read once.
+#include <type_traits>
+
 #include "dev_common.h"
 #include "vdn_internal.h"
 
@@ -69,9 +71,69 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-__device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                        (__attribute__((address_space(3))) lds_bf16x4*)(p)));
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) unsigned char*)p);
+}
+__device__ __forceinline__ bf16x8 cat2(u32x2 a, u32x2 b) {
+  return cat(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b));
+}
+
+// The transposed fragment reads of one k-step (ds_read_b64_tr_b16) as one asm block that waits for
+// its own reads.  Issued through the builtin, each such read gets a vmcnt(0) from the compiler
+// while any LDS DMA copy is in flight (it cannot tell the read from the stage being filled), which
+// completed the tiles in flight before every k-step and left the copies of later tiles no time to
+// overlap the products.  A fragment is two reads, rows r and r + 4 of the block (R4 bytes apart);
+// the Y operand has the high and low planes TILE bytes apart.
+//   d = 128 (two Y and two X fragments per wave): ya[nt], xa[mt] are the fragment base addresses
+//   without the k-step offset KB.
+template <int KB, int TILE, int R4>
+__device__ __forceinline__ void ks_frags(const uint32_t (&ya)[2], const uint32_t (&xa)[2], bf16x8 (&yf)[2][2],
+                                         bf16x8 (&xf)[2]) {
+  u32x2 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12 offset:%c16\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:%c17\n\t"
+      "ds_read_b64_tr_b16 %2, %12 offset:%c18\n\t"
+      "ds_read_b64_tr_b16 %3, %12 offset:%c19\n\t"
+      "ds_read_b64_tr_b16 %4, %13 offset:%c16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%c17\n\t"
+      "ds_read_b64_tr_b16 %6, %13 offset:%c18\n\t"
+      "ds_read_b64_tr_b16 %7, %13 offset:%c19\n\t"
+      "ds_read_b64_tr_b16 %8, %14 offset:%c16\n\t"
+      "ds_read_b64_tr_b16 %9, %14 offset:%c17\n\t"
+      "ds_read_b64_tr_b16 %10, %15 offset:%c16\n\t"
+      "ds_read_b64_tr_b16 %11, %15 offset:%c17\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7), "=&v"(r8),
+        "=&v"(r9), "=&v"(r10), "=&v"(r11)
+      : "v"(ya[0]), "v"(ya[1]), "v"(xa[0]), "v"(xa[1]), "i"(KB), "i"(KB + R4), "i"(TILE + KB), "i"(TILE + KB + R4));
+  yf[0][0] = cat2(r0, r1);
+  yf[0][1] = cat2(r2, r3);
+  yf[1][0] = cat2(r4, r5);
+  yf[1][1] = cat2(r6, r7);
+  xf[0] = cat2(r8, r9);
+  xf[1] = cat2(r10, r11);
+}
+//   d = 64 (one Y and one X fragment per wave)
+template <int KB, int TILE, int R4>
+__device__ __forceinline__ void ks_frags(const uint32_t (&ya)[1], const uint32_t (&xa)[1], bf16x8 (&yf)[1][2],
+                                         bf16x8 (&xf)[1]) {
+  u32x2 r0, r1, r2, r3, r4, r5;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %6 offset:%c8\n\t"
+      "ds_read_b64_tr_b16 %1, %6 offset:%c9\n\t"
+      "ds_read_b64_tr_b16 %2, %6 offset:%c10\n\t"
+      "ds_read_b64_tr_b16 %3, %6 offset:%c11\n\t"
+      "ds_read_b64_tr_b16 %4, %7 offset:%c8\n\t"
+      "ds_read_b64_tr_b16 %5, %7 offset:%c9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5)
+      : "v"(ya[0]), "v"(xa[0]), "i"(KB), "i"(KB + R4), "i"(TILE + KB), "i"(TILE + KB + R4));
+  yf[0][0] = cat2(r0, r1);
+  yf[0][1] = cat2(r2, r3);
+  xf[0] = cat2(r4, r5);
 }
 
 template <int D>
@@ -187,27 +249,28 @@ __global__ __launch_bounds__(kThreads) void vda_gram_mfma_kernel(const bf16_t* _
       *reinterpret_cast<bf16x8*>(yb + SM::TILE + e * 16) = ylv;
     }
     lds_barrier();                                    // Y ready
+    uint32_t ya[NT], xa[MT];
 #pragma unroll
-    for (int ks = 0; ks < kTU / 16; ++ks) {
-      const int kbyte = ks * 16 * SM::ROW;
-      bf16x8 yf[NT][2];
+    for (int nt = 0; nt < NT; ++nt) ya[nt] = lds_addr(yb) + yoff[nt];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int mt = 0; mt < MT; ++mt) xa[mt] = lds_addr(kb) + (xv[mt] ? SM::TILE : 0) + xoff[mt];
+    auto kstep = [&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      bf16x8 yf[NT][2], xf[MT];
+      ks_frags<ks * 16 * SM::ROW, SM::TILE, 4 * SM::ROW>(ya, xa, yf, xf);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const unsigned char* base = yb + p * SM::TILE + kbyte + yoff[nt];
-          yf[nt][p] = cat(tr_read(base), tr_read(base + 4 * SM::ROW));
-        }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const unsigned char* base = kb + (xv[mt] ? SM::TILE : 0) + kbyte + xoff[mt];
-        const bf16x8 xf = cat(tr_read(base), tr_read(base + 4 * SM::ROW));
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, yf[nt][0], acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, yf[nt][1], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[mt], yf[nt][0], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[mt], yf[nt][1], acc[mt][nt], 0, 0, 0);
         }
-      }
+    };
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+    if constexpr (kTU / 16 > 2) {
+      kstep(std::integral_constant<int, 2>{});
+      kstep(std::integral_constant<int, 3>{});
     }
   }
 
