@@ -218,6 +218,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
   constexpr int R_ROWS_PER_KB = 1024 / (D * 2);
   constexpr int R_INSTR = SM::ROW / 1024 / kWaves;           // per wave, per row-major tile
   constexpr int T_INSTR = SM::ROW / 1024 / kWaves;           // per wave, per transposed tile
+  // The normaliser and D-value arrays as values held in scalar registers: selected per wave in
+  // the tile copy below, a select between the two parameter fields became a load from the
+  // parameter block through a vector address, and its wait also completed the tile copies just
+  // issued (so every tile's copy latency was exposed).
+  const float* lse_p = P.lse;
+  const float* dsum_p = P.dsum;
+  asm volatile("" : "+s"(lse_p), "+s"(dsum_p));
   auto issue_tile = [&](int t, int q0, int stage) {
     unsigned char* base = smem + stage * SM::STAGE;
     // an opaque copy of the lane index: the per-lane DMA offsets are recomputed at each issue
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     }
     if (wave < 2) {                              // the tile's normalisers (wave 0) and D values (wave 1)
       const int64_t rr = ((int64_t)t * N + min(q0 + lane, rows - 1)) * H + h;
-      const float* src = wave == 1 ? P.dsum + rr : q0 + lane < rows ? P.lse + rr : &kInfRow;
+      const float* src = wave == 1 ? dsum_p + rr : q0 + lane < rows ? lse_p + rr : &kInfRow;
       __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(base + 4 * SM::ROW + wave * 256), 4, 0, 0);
     }
   };
