@@ -192,11 +192,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
 
   // query tiles: every 64-row tile of every frame in the slot's ranges, then the context rows
   // (pseudo-frame T: they see every key)
+  // (the frame ranges are read once into scalar registers: read from the table inside the tile
+  // walk, each tile's range lookup waited for a global load right before its tile copy)
   const int* qr = P.qranges + slot * 2 * kMaxRanges;
   const int nr = uniform(P.nqranges[slot]);
   const int tpf = (N + 63) / 64;
+  int qs[kMaxRanges], ql[kMaxRanges];
   int nfr = 0;
-  for (int r = 0; r < nr; ++r) nfr += qr[2 * r + 1] - qr[2 * r];
+#pragma unroll
+  for (int r = 0; r < kMaxRanges; ++r) {
+    qs[r] = r < nr ? uniform(qr[2 * r]) : 0;
+    ql[r] = r < nr ? uniform(qr[2 * r + 1]) - qs[r] : 0;
+    nfr += ql[r];
+  }
   const int nvt = CTX ? 0 : uniform(nfr * tpf);
   const int ntiles = CTX ? (P.n_cq + 63) / 64 : nvt;
   auto tile_at = [&](int it, int& t, int& q0) {
@@ -208,10 +216,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     int fi = it / tpf;
     q0 = (it % tpf) * 64;
     t = 0;
-    for (int r = 0; r < nr; ++r) {
-      const int len = qr[2 * r + 1] - qr[2 * r];
-      if (fi < len) { t = qr[2 * r] + fi; break; }
-      fi -= len;
+#pragma unroll
+    for (int r = 0; r < kMaxRanges; ++r) {
+      if (fi < ql[r]) { t = qs[r] + fi; return; }
+      fi -= ql[r];
     }
   };
   // DMA: Q and dO tiles [64][D] (row-major, rows clamped to the frame), Q^T and dO^T tiles [D][64]
@@ -351,12 +359,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void softmax_dkv_mfma_kernel(DkvPar
     float* dkp = slot == 0 ? P.dtext + ((int64_t)key * H + h) * D : P.dk + (((int64_t)(slot - 1) * N + key) * H + h) * D;
     float* dvp = slot == 0 ? P.dtext + (((int64_t)P.n_glob + key) * H + h) * D
                            : P.dv + (((int64_t)(slot - 1) * N + key) * H + h) * D;
+    // every load first, then every store (interleaved, each load waited for the stores before it)
+    f32x4 ka[DT], va[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      f32x4* a = reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4);
-      f32x4* b = reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4);
-      *a = *a - dkt[kt][dt] * tau;
-      *b = *b + dvt[kt][dt];
+      ka[dt] = *reinterpret_cast<const f32x4*>(dkp + dt * 16 + g * 4);
+      va[dt] = *reinterpret_cast<const f32x4*>(dvp + dt * 16 + g * 4);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      *reinterpret_cast<f32x4*>(dkp + dt * 16 + g * 4) = ka[dt] - dkt[kt][dt] * tau;
+      *reinterpret_cast<f32x4*>(dvp + dt * 16 + g * 4) = va[dt] + dvt[kt][dt];
     }
   }
 }
